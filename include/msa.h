@@ -1,0 +1,182 @@
+/*
+ * msa.h -- C ABI of the MiniMax Sparse Attention (MSA) forward path for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed (Sparse Attention Part II, mtreviso.github.io, section 3.2
+ * "MiniMax's MSA"; MiniMax Sparse Attention, api.staik.se blog): for every
+ * query and GQA group an index query is scored against one index key head
+ * shared by all groups, over the causally visible tokens.  Each block of
+ * `block_size` key tokens is scored by the maximum of its token scores.  A
+ * Top-k over the block scores keeps `topk` blocks per query and group, one of
+ * them always the query's own (local) block.  Every query head of the group
+ * then runs exact attention over the visible tokens of the kept blocks, with
+ * its own softmax normalised over that set only.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers, allocated and owned by the
+ *     caller.  The library never allocates, frees or synchronises; it keeps no
+ *     mutable global state, so calls on different streams may run
+ *     concurrently.  `stream` is a hipStream_t (NULL = the null stream).
+ *   - Layouts are dense, row-major, with no padding ("BSHD"):
+ *       q      [B][S_q][H_q][D]       bf16
+ *       k, v   [B][S_k][H_kv][D]      bf16
+ *       q_idx  [B][S_q][H_kv][D_idx]  bf16  (one index-query head per group)
+ *       k_idx  [B][S_k][D_idx]        bf16  (one index-key head, shared)
+ *       block_scores [B][H_kv][S_q][n_blk] fp32, n_blk = ceil(S_k / block_size)
+ *       block_idx    [B][H_kv][S_q][topk]  int32
+ *       out    [B][S_q][H_q][D]       bf16
+ *       lse    [B][H_q][S_q]          fp32 (natural log), optional
+ *   - Query i sits at absolute position t_i = i + S_k - S_q (the queries are
+ *     the last S_q positions of the key sequence; decode is S_q = 1).  Its
+ *     local block is l_i = floor(t_i / block_size).  Query head h belongs to
+ *     group g = floor(h / (H_q / H_kv)).
+ *   - All pointers must be 16-byte aligned.
+ *   - Argument checks run on the host before any HIP call; a failed check
+ *     returns its status and launches nothing.  A HIP launch error returns
+ *     MSA_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *     synchronisation, as for any asynchronous HIP work.
+ *   - Results are bit-identical from run to run.
+ *   - batch == 0 or seqlen_q == 0 is an empty problem: MSA_OK, no launch.
+ *
+ * Supported on this device path: causal = 1, head_dim = 128,
+ * index_dim in {64, 128}, block_size = 128, 1 <= topk <= 64,
+ * seqlen_k >= seqlen_q, num_heads_q a multiple of num_heads_kv with
+ * H_q / H_kv in {1, 2, 4, 8, 16, 32}.  Other values return
+ * MSA_ERR_UNSUPPORTED (or MSA_ERR_INVALID_DIMS when they are not meaningful).
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum msa_status {
+  MSA_OK = 0,
+  MSA_ERR_NULL_PTR = 1,           /* a required pointer is NULL */
+  MSA_ERR_INVALID_DIMS = 2,       /* negative sizes, S_k < S_q, H_q % H_kv != 0, ... */
+  MSA_ERR_UNSUPPORTED = 3,        /* meaningful, but outside the device path's set */
+  MSA_ERR_MISALIGNED = 4,         /* a pointer is not 16-byte aligned */
+  MSA_ERR_WORKSPACE_TOO_SMALL = 5,/* ws_bytes < msa_workspace_bytes(...) */
+  MSA_ERR_HIP = 6                 /* a HIP runtime call or launch failed */
+} msa_status;
+
+typedef struct msa_dims {
+  int32_t batch;         /* B */
+  int32_t seqlen_q;      /* S_q: new queries per sequence */
+  int32_t seqlen_k;      /* S_k: keys per sequence (prefix incl. the queries) */
+  int32_t num_heads_q;   /* H_q: main-branch query heads */
+  int32_t num_heads_kv;  /* H_kv: KV heads = GQA groups = index-query heads */
+  int32_t head_dim;      /* D */
+  int32_t index_dim;     /* D_idx: width of the index query / key */
+  int32_t block_size;    /* key tokens per block */
+  int32_t topk;          /* blocks kept per query and group, local block incl. */
+  int32_t causal;        /* must be 1 */
+  float softmax_scale;   /* main-branch logit scale; 0 selects 1/sqrt(D) */
+} msa_dims;
+
+/* Which call a workspace size is asked for. */
+typedef enum msa_entry {
+  MSA_ENTRY_INDEX_SCORES = 0,
+  MSA_ENTRY_BLOCK_TOPK = 1,
+  MSA_ENTRY_SPARSE_ATTN_FWD = 2,
+  MSA_ENTRY_FORWARD = 3
+} msa_entry;
+
+/*
+ * Index branch, scoring step (section 3.2 of Sparse Attention Part II: the
+ * index query scores the visible tokens against the shared index key head and
+ * each block is scored by its maximum token score; section 4.4 of the same
+ * page for keeping the token scores off HBM).
+ *
+ *   block_scores[b][g][i][j] = max over s in block j with s <= t_i of
+ *                              sum_c q_idx[b][i][g][c] * k_idx[b][s][c]
+ *   and -infinity for blocks j > l_i (nothing visible).
+ *
+ * The raw dot product is used: no scale and no activation.  Products are
+ * exact in fp32 and sums accumulate in fp32 on the matrix cores, so the
+ * result is exact whenever every partial sum is an integer below 2^24 (as
+ * with small integer-valued inputs).  Token scores are never written to
+ * memory.  Inputs: q_idx, k_idx (read only).  Output: block_scores (written
+ * in full, including the -infinity entries).
+ */
+msa_status msa_index_scores(const msa_dims* dims, const void* q_idx,
+                            const void* k_idx, float* block_scores,
+                            void* stream);
+
+/*
+ * Index branch, selection step (section 3.2 of Sparse Attention Part II: one
+ * of the k slots is reserved for the query's local block and the indexer
+ * picks the others; the MiniMax Sparse Attention blog: the Top-k works on raw
+ * scores, with no exponential; section 4.2 of Sparse Attention Part II: exact
+ * top-k needs one consistent rule for ties).
+ *
+ *   Sel_i = { l_i } united with the (topk - 1) best blocks among 0 .. l_i - 1,
+ *           ranked by block score (higher first) and, on equal scores, by
+ *           block index (lower first); all of 0 .. l_i - 1 when l_i < topk.
+ *
+ *   block_idx[b][g][i][0 .. n-1] = Sel_i in ascending order, n = min(topk, l_i + 1),
+ *   block_idx[b][g][i][n .. topk-1] = -1.
+ *
+ * The local block's own score is not ranked.  Input: block_scores as written
+ * by msa_index_scores (finite for j < l_i; NaN is not supported).  Output:
+ * block_idx (written in full).
+ */
+msa_status msa_block_topk(const msa_dims* dims, const float* block_scores,
+                          int32_t* block_idx, void* stream);
+
+/*
+ * Main branch (section 3.2 of Sparse Attention Part II: every query head of
+ * the group attends to the causally visible tokens of the selected blocks
+ * with its own weights; section 2 of the same page: the softmax is normalised
+ * within the selection; section 4.1: O = P V with P the softmax of the scaled
+ * scores, computed tile by tile without storing P).
+ *
+ *   T_i = { s : floor(s / block_size) in block_idx[b][g][i][:], s <= t_i }
+ *   out[b][i][h] = sum_{s in T_i} softmax_s(scale * q[b][i][h] . k[b][s][g]) v[b][s][g]
+ *   lse[b][h][i] = log sum_{s in T_i} exp(scale * q[b][i][h] . k[b][s][g])
+ *
+ * Entries of block_idx equal to -1 are ignored; the others must be distinct,
+ * lie in 0 .. l_i, and include l_i (as msa_block_topk writes them).  Inputs
+ * q, k, v, block_idx are read only.  `lse` may be NULL.  `ws` is scratch of at
+ * least msa_workspace_bytes(dims, MSA_ENTRY_SPARSE_ATTN_FWD) bytes, owned by
+ * the caller; its contents on entry do not matter and are clobbered.
+ */
+msa_status msa_sparse_attn_fwd(const msa_dims* dims, const void* q,
+                               const void* k, const void* v,
+                               const int32_t* block_idx, void* out, float* lse,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole forward path in the order the pages give it (The Architecture of
+ * Infinity, baystreetwire.com: index/proxy attention first, then the sparse
+ * main attention; Sparse Attention Part II, section 3.2 figure: hidden states,
+ * indexer scores, selected indices, main attention): msa_index_scores, then
+ * msa_block_topk, then msa_sparse_attn_fwd, all on `stream`, with the block
+ * scores kept in `ws`.  `block_idx_out` (may be NULL) receives the selection;
+ * `lse` may be NULL.  `ws` must hold msa_workspace_bytes(dims,
+ * MSA_ENTRY_FORWARD) bytes.
+ */
+msa_status msa_forward(const msa_dims* dims, const void* q, const void* k,
+                       const void* v, const void* q_idx, const void* k_idx,
+                       void* out, float* lse, int32_t* block_idx_out, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * Bytes of caller-provided workspace the given entry point needs for these
+ * dims (0 for entries that need none).  Returns (size_t)-1 when the dims are
+ * not valid for that entry point.
+ */
+size_t msa_workspace_bytes(const msa_dims* dims, int entry);
+
+/* Static, human-readable name of a status code. */
+const char* msa_status_str(msa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */
