@@ -1,0 +1,61 @@
+// Device-side helpers shared by the gfx950 kernels of the MSA library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// D = A * B + C on a 32x32 tile with K = 16 (v_mfma_f32_32x32x16_bf16).
+// Lane l supplies A[m = l % 32][k = 8 * (l / 32) + e] and
+// B[k = 8 * (l / 32) + e][n = l % 32] for e = 0..7; it receives
+// D[m = 8 * (r / 4) + 4 * (l / 32) + (r % 4)][n = l % 32] in register r.
+// Only the pairing of A and B along k matters for the result, so any
+// consistent assignment of k to (lane half, e) on both operands is valid.
+__device__ __forceinline__ f32x16 mfma32x32x16(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// 16-byte load that is not expected to be reused (streamed once).
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// Row index (within a 32x32 MFMA output tile) held by register r of lane l.
+__device__ __forceinline__ int mfma32_row(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+}
+
+// Value of `x` held by lane (l ^ 32).
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  // round-to-nearest-even of two fp32 values to bf16, packed low|high
+  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+  a += 0x7FFFu + ((a >> 16) & 1u);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (a >> 16) | (b & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+}  // namespace msa

@@ -1,0 +1,32 @@
+// Internal launch interface between the C-ABI layer (msa_api.cpp) and the
+// gfx950 kernels.  Shapes reaching these functions are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+// Block scores (see index_scan.hip).
+hipError_t launch_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, float* bm,
+                               int batch, int S_q, int S_k, int H_kv, int D_idx, int n_blk,
+                               hipStream_t stream);
+long index_scores_grid(int batch, int S_q, int H_kv, int n_blk);
+
+// Top-k selection (see block_topk.hip).
+hipError_t launch_block_topk(const float* bm, int32_t* idx, int batch, int S_q, int S_k,
+                             int H_kv, int n_blk, int topk, hipStream_t stream);
+
+// Sparse attention (see sparse_attn.hip).
+struct AttnShape {
+  int batch, S_q, S_k, H_q, H_kv, n_blk, topk;
+  float scale_log2;  // softmax scale * log2(e)
+  float scale;       // softmax scale
+};
+size_t sparse_attn_workspace(const AttnShape& s);
+hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, const int32_t* idx, uint16_t* out, float* lse,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+}  // namespace msa

@@ -1,0 +1,521 @@
+// Main branch: exact block-sparse causal GQA attention over the selected
+// blocks (Sparse Attention Part II, section 3.2: every query head of a group
+// attends to the visible tokens of the kept blocks with its own weights;
+// section 2: the softmax is normalised inside the selection; section 4.1:
+// scores and weights stay on chip, only statistics and the output leave).
+//
+// Schedule.  Neighbouring queries pick largely unrelated blocks, so a kernel
+// that walks each query's own 16 blocks re-reads every KV block once per
+// (query, group).  Here the edges (query i, group g, selected block j) are
+// bucketed by (b, g, j) instead: one workgroup loads K_j and V_j of group g
+// into LDS once and runs every query of its bucket against them, all G heads
+// of a query sharing the load (section 3.2: regular blocks let the group's
+// heads share KV loads).  Each edge leaves a partial result: the output
+// normalised over the block's visible keys and its log-sum-exp.  A merge
+// kernel then combines each query's partials, which is exactly the softmax
+// over the union of its blocks.  Decode (one query per sequence) is the same
+// computation with one query per bucket, i.e. split-KV.
+//
+// Work-list construction: counts per bucket, exclusive scans of edges and of
+// work items, edge scatter (atomics choose positions inside a bucket only;
+// every edge's arithmetic is independent of its position, so results do not
+// depend on that order), and one work item per up-to-QT edges of a bucket.
+#include <algorithm>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace msa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kD = 128;         // head dim
+constexpr int kBlock = 128;     // keys per block
+constexpr int kSubTiles = 4;    // 4-wave sub-tiles per work item
+constexpr int kScanPerWg = 1024;
+constexpr int kVStride = kBlock + 4;  // bf16 per row of the transposed V tile
+constexpr size_t kPartBudget = size_t(4) << 30;  // bytes of partials per chunk
+
+struct Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* idx;
+  uint16_t* out;
+  float* lse;
+  int B, S_q, S_k, H_q, H_kv, G, n_blk, topk;
+  int q0, Qc;            // this chunk's queries: [q0, q0 + Qc) clipped to S_q
+  int NB;                // buckets = B * H_kv * n_blk
+  int QT;                // edges per work item
+  float scale_log2;
+  int32_t* counts;
+  int32_t* cursor;
+  int32_t* offsets;      // NB + 1
+  int32_t* tile_off;     // NB + 1
+  int32_t* blk_sums;     // 2 * n_scan_wg
+  int32_t* edges;        // slot ids grouped by bucket
+  int2* work;            // (bucket, first edge in bucket)
+  float* part_lse;       // [slot][G], log2 units
+  float* part_o;         // [slot][G][D], normalised per block
+};
+
+// Slot of edge (b, g, il, e) inside the chunk.
+__device__ __forceinline__ long slot_of(const Params& p, int bg, int il, int e) {
+  return ((long)bg * p.Qc + il) * p.topk + e;
+}
+
+__global__ void zero_kernel(int32_t* a, long n) {
+  for (long x = (long)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (long)gridDim.x * blockDim.x)
+    a[x] = 0;
+}
+
+__global__ void count_kernel(Params p) {
+  const long n = (long)p.B * p.H_kv * p.Qc * p.topk;
+  for (long s = (long)blockIdx.x * blockDim.x + threadIdx.x; s < n; s += (long)gridDim.x * blockDim.x) {
+    const int e = (int)(s % p.topk);
+    const long r = s / p.topk;
+    const int il = (int)(r % p.Qc);
+    const int bg = (int)(r / p.Qc);
+    const int i = p.q0 + il;
+    if (i >= p.S_q) continue;
+    const int j = p.idx[((long)bg * p.S_q + i) * p.topk + e];
+    if (j >= 0 && j <= (i + p.S_k - p.S_q) / kBlock) atomicAdd(&p.counts[(long)bg * p.n_blk + j], 1);
+  }
+}
+
+// Exclusive scans of edges and work items per bucket, stage 1: per-workgroup.
+__global__ __launch_bounds__(256) void scan_local_kernel(Params p) {
+  __shared__ int32_t se[256], st[256];
+  const int tid = threadIdx.x;
+  const long base = (long)blockIdx.x * kScanPerWg + tid * 4;
+  int ce[4], ct[4], sum_e = 0, sum_t = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const long x = base + u;
+    const int c = x < p.NB ? p.counts[x] : 0;
+    ce[u] = sum_e;
+    ct[u] = sum_t;
+    sum_e += c;
+    sum_t += (c + p.QT - 1) / p.QT;
+  }
+  se[tid] = sum_e;
+  st[tid] = sum_t;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {  // Hillis-Steele inclusive scan
+    const int ae = tid >= d ? se[tid - d] : 0;
+    const int at = tid >= d ? st[tid - d] : 0;
+    __syncthreads();
+    se[tid] += ae;
+    st[tid] += at;
+    __syncthreads();
+  }
+  const int pe = se[tid] - sum_e, pt = st[tid] - sum_t;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const long x = base + u;
+    if (x < p.NB) {
+      p.offsets[x] = pe + ce[u];
+      p.tile_off[x] = pt + ct[u];
+    }
+  }
+  if (tid == 255) {
+    p.blk_sums[2 * blockIdx.x] = se[255];
+    p.blk_sums[2 * blockIdx.x + 1] = st[255];
+  }
+}
+
+// Stage 2: one workgroup scans the per-workgroup totals (exclusive, in place)
+// and writes the grand totals at offsets[NB], tile_off[NB].
+__global__ __launch_bounds__(256) void scan_blocks_kernel(Params p, int n_wg) {
+  __shared__ int32_t se[256], st[256];
+  __shared__ int32_t carry[2];
+  const int tid = threadIdx.x;
+  if (tid == 0) carry[0] = carry[1] = 0;
+  __syncthreads();
+  for (int base = 0; base < n_wg; base += 256) {
+    const int x = base + tid;
+    const int ve = x < n_wg ? p.blk_sums[2 * x] : 0;
+    const int vt = x < n_wg ? p.blk_sums[2 * x + 1] : 0;
+    se[tid] = ve;
+    st[tid] = vt;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const int ae = tid >= d ? se[tid - d] : 0;
+      const int at = tid >= d ? st[tid - d] : 0;
+      __syncthreads();
+      se[tid] += ae;
+      st[tid] += at;
+      __syncthreads();
+    }
+    const int ce = carry[0], ct = carry[1];
+    if (x < n_wg) {
+      p.blk_sums[2 * x] = ce + se[tid] - ve;
+      p.blk_sums[2 * x + 1] = ct + st[tid] - vt;
+    }
+    __syncthreads();
+    if (tid == 255) {
+      carry[0] = ce + se[255];
+      carry[1] = ct + st[255];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    p.offsets[p.NB] = carry[0];
+    p.tile_off[p.NB] = carry[1];
+  }
+}
+
+// Stage 3: add the workgroup prefix; also emits the work items of each bucket.
+__global__ __launch_bounds__(256) void scan_add_kernel(Params p) {
+  const long base = (long)blockIdx.x * kScanPerWg;
+  const int add_e = p.blk_sums[2 * blockIdx.x];
+  const int add_t = p.blk_sums[2 * blockIdx.x + 1];
+  for (int u = threadIdx.x; u < kScanPerWg; u += 256) {
+    const long x = base + u;
+    if (x >= p.NB) break;
+    const int oe = p.offsets[x] + add_e;
+    const int ot = p.tile_off[x] + add_t;
+    p.offsets[x] = oe;
+    p.tile_off[x] = ot;
+    const int c = p.counts[x];
+    for (int t = 0, s = 0; s < c; ++t, s += p.QT) p.work[ot + t] = make_int2((int)x, s);
+  }
+}
+
+__global__ void fill_kernel(Params p) {
+  const long n = (long)p.B * p.H_kv * p.Qc * p.topk;
+  for (long s = (long)blockIdx.x * blockDim.x + threadIdx.x; s < n; s += (long)gridDim.x * blockDim.x) {
+    const int e = (int)(s % p.topk);
+    const long r = s / p.topk;
+    const int il = (int)(r % p.Qc);
+    const int bg = (int)(r / p.Qc);
+    const int i = p.q0 + il;
+    if (i >= p.S_q) continue;
+    const int j = p.idx[((long)bg * p.S_q + i) * p.topk + e];
+    if (j >= 0 && j <= (i + p.S_k - p.S_q) / kBlock) {
+      const long bucket = (long)bg * p.n_blk + j;
+      const int pos = p.offsets[bucket] + atomicAdd(&p.cursor[bucket], 1);
+      p.edges[pos] = (int32_t)s;
+    }
+  }
+}
+
+// One work item: (bucket (b, g, j), up to QT of its edges).
+template <int G>
+__global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
+  constexpr int QW = 32 / G;  // queries per wave (32 MFMA rows = QW queries x G heads)
+  __shared__ uint4 ktile[kBlock * 16];                 // [key][16 chunks], swizzled
+  __shared__ uint32_t vt[kD * kVStride / 2];           // [d][key] bf16, padded rows
+
+  const int w = blockIdx.x;
+  if (w >= p.tile_off[p.NB]) return;  // uniform: past the last work item
+  const int2 item = p.work[w];
+  const int bucket = item.x;
+  const int start = item.y;
+  const int n_here = min(p.QT, p.counts[bucket] - start);
+  const int ebase = p.offsets[bucket] + start;
+  const int bg = bucket / p.n_blk;
+  const int j = bucket - bg * p.n_blk;
+  const int b = bg / p.H_kv;
+  const int g = bg - b * p.H_kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+
+  // K_j, V_j of group g into LDS (V transposed to [d][key]).
+  {
+    const size_t row_stride = (size_t)p.H_kv * kD;
+    const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+    const uint16_t* vb = p.v + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int qd = it * kThreads + tid;
+      const int row = qd >> 4, c = qd & 15;
+      const int s = j * kBlock + row;
+      const uint4 x = s < p.S_k ? *reinterpret_cast<const uint4*>(kb + (size_t)s * row_stride + 8 * c)
+                                : make_uint4(0, 0, 0, 0);
+      ktile[row * 16 + (c ^ (row & 15))] = x;
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int u = it * kThreads + tid;
+      const int kp = (u & 15) + 16 * ((u >> 6) & 3);
+      const int d0 = ((u >> 4) & 3) + 4 * ((u >> 8) & 3);
+      const int s = j * kBlock + 2 * kp;
+      const uint4 lo = s < p.S_k ? *reinterpret_cast<const uint4*>(vb + (size_t)s * row_stride + 8 * d0)
+                                 : make_uint4(0, 0, 0, 0);
+      const uint4 hi = s + 1 < p.S_k ? *reinterpret_cast<const uint4*>(vb + (size_t)(s + 1) * row_stride + 8 * d0)
+                                     : make_uint4(0, 0, 0, 0);
+      const uint32_t lw[4] = {lo.x, lo.y, lo.z, lo.w};
+      const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t a = (e & 1) ? (lw[e >> 1] >> 16) : (lw[e >> 1] & 0xFFFFu);
+        const uint32_t c2 = (e & 1) ? (hw[e >> 1] & 0xFFFF0000u) : (hw[e >> 1] << 16);
+        vt[((8 * d0 + e) * kVStride + 2 * kp) >> 1] = a | c2;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int off = p.S_k - p.S_q;
+  const int n = lane & 31;          // MFMA row of this lane
+  const int qi = n / G, hh = n - (n / G) * G;
+  for (int sub = 0; sub < n_here; sub += 4 * QW) {
+    const int qbase = sub + wave * QW;
+    if (qbase >= n_here) break;  // wave-uniform
+    const int qx = qbase + qi;
+    const bool valid = qx < n_here;
+    long slot = 0;
+    int i = 0, t = 0x7FFFFFFF;
+    if (valid) {
+      slot = p.edges[ebase + qx];
+      const int il = (int)((slot / p.topk) % p.Qc);
+      i = p.q0 + il;
+      t = i + off;
+    }
+    uint4 qb[8];
+    {
+      const uint16_t* qrow = p.q + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        qb[ks] = valid ? *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * h) : make_uint4(0, 0, 0, 0);
+    }
+    f32x16 sacc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
+      const int krow = mt * 32 + n;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        sacc[mt] = mfma32x32x16(ktile[krow * 16 + ((2 * ks + h) ^ (krow & 15))], qb[ks], sacc[mt]);
+    }
+    const bool need_mask = __builtin_amdgcn_ballot_w64(j * kBlock + kBlock - 1 > t) != 0;
+    float mx = neg_inf();
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = sacc[mt][r] * p.scale_log2;
+        if (need_mask && j * kBlock + mt * 32 + mfma32_row(r, lane) > t) x = neg_inf();
+        sacc[mt][r] = x;
+        mx = __builtin_fmaxf(mx, x);
+      }
+    mx = __builtin_fmaxf(mx, swap_halves(mx));
+    float l = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e2 = __builtin_amdgcn_exp2f(sacc[mt][r] - mx);
+        sacc[mt][r] = e2;
+        l += e2;
+      }
+    l += swap_halves(l);
+
+    f32x16 oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        uint4 pb;
+        pb.x = pack_bf16x2(sacc[mt][8 * qq + 0], sacc[mt][8 * qq + 1]);
+        pb.y = pack_bf16x2(sacc[mt][8 * qq + 2], sacc[mt][8 * qq + 3]);
+        pb.z = pack_bf16x2(sacc[mt][8 * qq + 4], sacc[mt][8 * qq + 5]);
+        pb.w = pack_bf16x2(sacc[mt][8 * qq + 6], sacc[mt][8 * qq + 7]);
+        const int key0 = mt * 32 + 16 * qq + 4 * h;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int d = dt * 32 + n;
+          const uint2 a0 = *reinterpret_cast<const uint2*>(&vt[(d * kVStride + key0) >> 1]);
+          const uint2 a1 = *reinterpret_cast<const uint2*>(&vt[(d * kVStride + key0 + 8) >> 1]);
+          oacc[dt] = mfma32x32x16(make_uint4(a0.x, a0.y, a1.x, a1.y), pb, oacc[dt]);
+        }
+      }
+    if (valid) {
+      const float inv_l = 1.f / l;
+      float* po = p.part_o + ((size_t)slot * G + hh) * kD;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          float4 v4;
+          v4.x = oacc[dt][4 * rq + 0] * inv_l;
+          v4.y = oacc[dt][4 * rq + 1] * inv_l;
+          v4.z = oacc[dt][4 * rq + 2] * inv_l;
+          v4.w = oacc[dt][4 * rq + 3] * inv_l;
+          *reinterpret_cast<float4*>(po + dt * 32 + 8 * rq + 4 * h) = v4;
+        }
+      if (h == 0) p.part_lse[(size_t)slot * G + hh] = mx + __builtin_amdgcn_logf(l);
+    }
+  }
+}
+
+// Combines the partials of each (query, group): one wave per row.
+template <int G>
+__global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse) {
+  constexpr int NF = G * kD / 4;            // float4s per partial
+  constexpr int F = (NF + 63) / 64;         // float4s per lane
+  const int lane = threadIdx.x & 63;
+  const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= (long)p.B * p.H_kv * p.Qc) return;
+  const int il = (int)(r % p.Qc);
+  const int bg = (int)(r / p.Qc);
+  const int i = p.q0 + il;
+  if (i >= p.S_q) return;
+  const int b = bg / p.H_kv, g = bg - (bg / p.H_kv) * p.H_kv;
+  const int32_t* sel = p.idx + ((long)bg * p.S_q + i) * p.topk;
+  const int local = (i + p.S_k - p.S_q) / kBlock;  // entries past it are ignored
+
+  float M[F], L[F];
+  float4 acc[F];
+#pragma unroll
+  for (int u = 0; u < F; ++u) {
+    M[u] = neg_inf();
+    L[u] = 0.f;
+    acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int e = 0; e < p.topk; ++e) {
+    if (sel[e] < 0 || sel[e] > local) continue;
+    const long slot = slot_of(p, bg, il, e);
+#pragma unroll
+    for (int u = 0; u < F; ++u) {
+      const int f = lane + 64 * u;
+      if (f < NF) M[u] = __builtin_fmaxf(M[u], p.part_lse[slot * G + f / (kD / 4)]);
+    }
+  }
+  for (int e = 0; e < p.topk; ++e) {
+    if (sel[e] < 0 || sel[e] > local) continue;
+    const long slot = slot_of(p, bg, il, e);
+#pragma unroll
+    for (int u = 0; u < F; ++u) {
+      const int f = lane + 64 * u;
+      if (f < NF) {
+        const float wgt = __builtin_amdgcn_exp2f(p.part_lse[slot * G + f / (kD / 4)] - M[u]);
+        const float4 x = reinterpret_cast<const float4*>(p.part_o + (size_t)slot * G * kD)[f];
+        L[u] += wgt;
+        acc[u].x += wgt * x.x;
+        acc[u].y += wgt * x.y;
+        acc[u].z += wgt * x.z;
+        acc[u].w += wgt * x.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < F; ++u) {
+    const int f = lane + 64 * u;
+    if (f >= NF) continue;
+    const int hh = f / (kD / 4);
+    const int d = (f - hh * (kD / 4)) * 4;
+    const float inv = 1.f / L[u];
+    uint2 o;
+    o.x = pack_bf16x2(acc[u].x * inv, acc[u].y * inv);
+    o.y = pack_bf16x2(acc[u].z * inv, acc[u].w * inv);
+    *reinterpret_cast<uint2*>(p.out + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + d) = o;
+    if (with_lse && d == 0)
+      p.lse[((size_t)b * p.H_q + g * G + hh) * p.S_q + i] =
+          (M[u] + __builtin_amdgcn_logf(L[u])) * 0.69314718055994530942f;
+  }
+}
+
+struct Layout {
+  int Qc, QT, n_scan_wg;
+  long NB, E, T;
+  size_t counts, cursor, offsets, tile_off, blk_sums, edges, work, part_lse, part_o, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Layout make_layout(const AttnShape& s) {
+  Layout L{};
+  const int G = s.H_q / s.H_kv;
+  L.QT = kSubTiles * 4 * (32 / G);
+  const size_t per_query = (size_t)s.batch * s.H_kv * s.topk * ((size_t)G * (kD + 1) * 4 + 8 + 4);
+  long qc = (long)(kPartBudget / per_query);
+  if (qc >= 128) qc -= qc % 128;
+  L.Qc = (int)std::max(1L, std::min<long>(qc, s.S_q));
+  L.NB = (long)s.batch * s.H_kv * s.n_blk;
+  L.E = (long)s.batch * s.H_kv * L.Qc * s.topk;
+  L.T = (L.E + L.QT - 1) / L.QT + std::min(L.NB, L.E);
+  L.n_scan_wg = (int)((L.NB + kScanPerWg - 1) / kScanPerWg);
+  size_t o = 0;
+  L.counts = o;   o = align256(o + L.NB * 4);
+  L.cursor = o;   o = align256(o + L.NB * 4);
+  L.offsets = o;  o = align256(o + (L.NB + 1) * 4);
+  L.tile_off = o; o = align256(o + (L.NB + 1) * 4);
+  L.blk_sums = o; o = align256(o + (size_t)L.n_scan_wg * 8);
+  L.edges = o;    o = align256(o + L.E * 4);
+  L.work = o;     o = align256(o + L.T * 8);
+  L.part_lse = o; o = align256(o + (size_t)L.E * G * 4);
+  L.part_o = o;   o = align256(o + (size_t)L.E * G * kD * 4);
+  L.total = o;
+  return L;
+}
+
+int grid_cap(long n, int per) {
+  long g = (n + per - 1) / per;
+  return (int)std::max(1L, std::min(g, 65536L));
+}
+
+}  // namespace
+
+size_t sparse_attn_workspace(const AttnShape& s) { return make_layout(s).total; }
+
+template <int G>
+static hipError_t launch_g(const AttnShape& s, const Layout& L, Params p, bool with_lse, hipStream_t st) {
+  for (int q0 = 0; q0 < s.S_q; q0 += L.Qc) {
+    p.q0 = q0;
+    const long slots = (long)s.batch * s.H_kv * L.Qc * s.topk;
+    hipLaunchKernelGGL(zero_kernel, dim3(grid_cap(L.NB, 256)), dim3(256), 0, st, p.counts, L.NB);
+    hipLaunchKernelGGL(zero_kernel, dim3(grid_cap(L.NB, 256)), dim3(256), 0, st, p.cursor, L.NB);
+    hipLaunchKernelGGL(count_kernel, dim3(grid_cap(slots, 256)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(scan_local_kernel, dim3(L.n_scan_wg), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(scan_blocks_kernel, dim3(1), dim3(256), 0, st, p, L.n_scan_wg);
+    hipLaunchKernelGGL(scan_add_kernel, dim3(L.n_scan_wg), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(fill_kernel, dim3(grid_cap(slots, 256)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(attn_partial_kernel<G>, dim3((unsigned)L.T), dim3(kThreads), 0, st, p);
+    const long rows = (long)s.batch * s.H_kv * L.Qc;
+    hipLaunchKernelGGL(merge_kernel<G>, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, st, p,
+                       with_lse ? 1 : 0);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* v, const int32_t* idx, uint16_t* out, float* lse,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  const Layout L = make_layout(s);
+  if (ws_bytes < L.total) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(ws);
+  Params p{};
+  p.q = q; p.k = k; p.v = v; p.idx = idx; p.out = out; p.lse = lse;
+  p.B = s.batch; p.S_q = s.S_q; p.S_k = s.S_k; p.H_q = s.H_q; p.H_kv = s.H_kv;
+  p.G = s.H_q / s.H_kv; p.n_blk = s.n_blk; p.topk = s.topk;
+  p.Qc = L.Qc; p.NB = (int)L.NB; p.QT = L.QT; p.scale_log2 = s.scale_log2;
+  p.counts = reinterpret_cast<int32_t*>(base + L.counts);
+  p.cursor = reinterpret_cast<int32_t*>(base + L.cursor);
+  p.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  p.tile_off = reinterpret_cast<int32_t*>(base + L.tile_off);
+  p.blk_sums = reinterpret_cast<int32_t*>(base + L.blk_sums);
+  p.edges = reinterpret_cast<int32_t*>(base + L.edges);
+  p.work = reinterpret_cast<int2*>(base + L.work);
+  p.part_lse = reinterpret_cast<float*>(base + L.part_lse);
+  p.part_o = reinterpret_cast<float*>(base + L.part_o);
+  const bool with_lse = lse != nullptr;
+  switch (p.G) {
+    case 1: return launch_g<1>(s, L, p, with_lse, stream);
+    case 2: return launch_g<2>(s, L, p, with_lse, stream);
+    case 4: return launch_g<4>(s, L, p, with_lse, stream);
+    case 8: return launch_g<8>(s, L, p, with_lse, stream);
+    case 16: return launch_g<16>(s, L, p, with_lse, stream);
+    case 32: return launch_g<32>(s, L, p, with_lse, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace msa

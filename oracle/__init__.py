@@ -48,7 +48,11 @@ def _load():
 
 
 def default_threads() -> int:
-    return _load().oracle_default_threads()
+    """Worker threads used when a call passes threads=0: every core, capped by
+    OMP_NUM_THREADS when that is set."""
+    n = _load().oracle_default_threads()
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(cap)) if cap.isdigit() and int(cap) > 0 else n
 
 
 class Problem:
@@ -114,7 +118,7 @@ def block_scores(p: Problem, q_idx, k_idx, rows=None, threads=0):
     bm = np.empty((len(rows), p.n_blk), dtype=np.float64)
     d = p._c()
     rc = _load().oracle_block_scores(ctypes.byref(d), _ptr(qi), _ptr(ki), _ptr(rows), len(rows),
-                                     _ptr(bm), threads)
+                                     _ptr(bm), threads or default_threads())
     if rc:
         raise ValueError("oracle_block_scores rejected its arguments")
     return bm
@@ -141,7 +145,7 @@ def attention(p: Problem, q, k, v, sel, rows=None, threads=0):
     lse = np.empty((len(rows), p.group), dtype=np.float64)
     d = p._c()
     rc = _load().oracle_attention(ctypes.byref(d), _ptr(qq), _ptr(kk), _ptr(vv), _ptr(rows),
-                                  len(rows), _ptr(sel), _ptr(out), _ptr(lse), threads)
+                                  len(rows), _ptr(sel), _ptr(out), _ptr(lse), threads or default_threads())
     if rc:
         raise ValueError("oracle_attention rejected its arguments")
     return out, lse
@@ -162,7 +166,7 @@ def forward(p: Problem, q, k, v, q_idx, k_idx, rows=None, threads=0):
     lse = np.empty((n, p.group), dtype=np.float64)
     d = p._c()
     rc = _load().oracle_forward(ctypes.byref(d), _ptr(qq), _ptr(kk), _ptr(vv), _ptr(qi), _ptr(ki),
-                                _ptr(rows), n, _ptr(bm), _ptr(sel), _ptr(out), _ptr(lse), threads)
+                                _ptr(rows), n, _ptr(bm), _ptr(sel), _ptr(out), _ptr(lse), threads or default_threads())
     if rc:
         raise ValueError("oracle_forward rejected its arguments")
     return {"bm": bm, "sel": sel, "out": out, "lse": lse, "rows": rows}

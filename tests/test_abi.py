@@ -1,0 +1,128 @@
+"""The C-ABI library loads, exports what include/msa.h declares, and rejects
+bad arguments on the host before any HIP call (no GPU needed: only error
+paths are exercised, nothing is launched).  Every call below must fail
+validation: the pointers are fake addresses that are never dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_gqa_scores_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = ctypes.c_void_p(0x10000)       # a 16-byte aligned, never dereferenced address
+MIS = ctypes.c_void_p(0x10008)     # misaligned
+NULL = None
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "msa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(msa_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    L = msa.lib()
+    names = declared_symbols()
+    assert set(names) == set(msa.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def dims(**kw):
+    base = dict(batch=1, seqlen_q=256, seqlen_k=512, num_heads_q=8, num_heads_kv=2, head_dim=128,
+                index_dim=128, block_size=128, topk=16, causal=1, softmax_scale=0.0)
+    base.update(kw)
+    return msa.Dims.make(**base)
+
+
+def fwd(d, q=A, k=A, v=A, qi=A, ki=A, out=A, lse=NULL, idx=NULL, ws=A, nbytes=None):
+    if nbytes is None:
+        nbytes = 1 << 40
+    return msa.lib().msa_forward(None if d is None else ctypes.byref(d), q, k, v, qi, ki, out, lse,
+                                 idx, ws, nbytes, None)
+
+
+def attn(d, q=A, k=A, v=A, idx=A, out=A, lse=NULL, ws=A, nbytes=1 << 40):
+    return msa.lib().msa_sparse_attn_fwd(ctypes.byref(d), q, k, v, idx, out, lse, ws, nbytes, None)
+
+
+def scores(d, qi=A, ki=A, bm=A):
+    return msa.lib().msa_index_scores(ctypes.byref(d), qi, ki, bm, None)
+
+
+def topk(d, bm=A, idx=A):
+    return msa.lib().msa_block_topk(ctypes.byref(d), bm, idx, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), 2), (dict(seqlen_q=600), 2), (dict(num_heads_q=7), 2), (dict(topk=0), 2),
+    (dict(block_size=0), 2), (dict(num_heads_kv=0), 2), (dict(head_dim=0), 2),
+    (dict(softmax_scale=float("nan")), 2),
+    (dict(causal=0), 3), (dict(head_dim=64), 3), (dict(block_size=64), 3), (dict(topk=65), 3),
+    (dict(index_dim=96), 3), (dict(num_heads_q=6, num_heads_kv=2), 3),
+])
+def test_forward_rejects_dims(kw, status):
+    assert fwd(dims(**kw)) == status
+
+
+def test_entry_specific_checks():
+    # index_dim only matters to the index branch; head_dim only to the main branch
+    assert scores(dims(index_dim=96)) == 3
+    assert topk(dims(block_size=64)) == 3 and topk(dims(topk=0)) == 2
+    assert attn(dims(index_dim=96, head_dim=64)) == 3
+    assert scores(dims(head_dim=64, index_dim=64, seqlen_q=600)) == 2
+
+
+def test_null_and_misaligned_pointers():
+    d = dims()
+    assert fwd(None) == 1
+    assert fwd(d, q=NULL) == 1
+    assert fwd(d, ki=NULL) == 1
+    assert fwd(d, ws=NULL, nbytes=0) == 1
+    assert fwd(d, v=MIS) == 4
+    assert fwd(d, lse=MIS) == 4
+    assert fwd(d, idx=MIS) == 4
+    assert attn(d, idx=NULL) == 1
+    assert attn(d, out=MIS) == 4
+    assert scores(d, bm=NULL) == 1
+    assert scores(d, qi=MIS) == 4
+    assert topk(d, idx=NULL) == 1
+    assert topk(d, bm=MIS) == 4
+
+
+def test_workspace_checks():
+    d = dims()
+    need = msa.msa_workspace_bytes(d, msa.ENTRY_FORWARD)
+    bm = d.batch * d.num_heads_kv * d.seqlen_q * d.n_blk * 4
+    assert need >= bm + msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_FWD)
+    assert fwd(d, nbytes=need - 1) == 5
+    need_a = msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_FWD)
+    assert need_a > 0 and attn(d, nbytes=need_a - 1) == 5
+    assert msa.msa_workspace_bytes(d, msa.ENTRY_INDEX_SCORES) == 0
+    assert msa.msa_workspace_bytes(d, msa.ENTRY_BLOCK_TOPK) == 0
+    with pytest.raises(msa.MsaError):
+        msa.msa_workspace_bytes(dims(causal=0), msa.ENTRY_FORWARD)
+    with pytest.raises(msa.MsaError):
+        msa.msa_workspace_bytes(d, 17)
+
+
+def test_empty_problems_are_ok_without_pointers():
+    for kw in (dict(batch=0), dict(seqlen_q=0)):
+        d = dims(**kw)
+        assert fwd(d, q=NULL, k=NULL, v=NULL, qi=NULL, ki=NULL, out=NULL, ws=NULL, nbytes=0) == 0
+        assert attn(d, q=NULL, k=NULL, v=NULL, idx=NULL, out=NULL, ws=NULL, nbytes=0) == 0
+        assert scores(d, qi=NULL, ki=NULL, bm=NULL) == 0
+        assert topk(d, bm=NULL, idx=NULL) == 0
+        assert msa.msa_workspace_bytes(d, msa.ENTRY_FORWARD) == 0
+
+
+def test_size_limits():
+    # rows * topk must stay below 2^31 (32-bit slot ids)
+    assert fwd(dims(batch=1 << 10, seqlen_q=1 << 17, seqlen_k=1 << 17, topk=16)) == 3
+
+
+def test_status_strings():
+    for code, name in msa.STATUS_NAMES.items():
+        assert msa.msa_status_str(code) == name
+    assert msa.msa_status_str(99) == "MSA_ERR_UNKNOWN"
