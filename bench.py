@@ -1,0 +1,233 @@
+"""Benchmark of the MSA forward path on one MI355X.
+
+One step = msa_forward over one batch of the workload: index scores fused with
+the block max-pool, the exp-free Top-k, and block-sparse attention.  Inputs
+are seeded synthetic tensors drawn on the device and resident in HBM before
+the timed region starts.
+
+Prints ONE JSON line.  ``value`` is tokens/s (queries of the batch per second)
+on the 32K prefill workload (B=1, S=32768, 64/8 heads, head dim 128, index dim
+128, block 128, k=16).  Alongside: algorithmic TFLOP/s and the fraction of the
+bf16 MFMA peak, per-entry-point times, the roofline of the dominant step, the
+CPU oracle timed on a bounded row sample, and the decode workload (64
+sequences against a 256K-token cache) as HBM GB/s and fraction of peak.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MSA fwd tokens/s + TFLOP/s (%MFMA peak) prefill; decode HBM GB/s (%peak)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+# ------------------------------------------------------------ work counts
+def positions(w):
+    return np.arange(w.seqlen_q, dtype=np.int64) + (w.seqlen_k - w.seqlen_q)
+
+
+def visible_tokens(w):
+    """|T_i| per query: every visible token while the local block index is
+    below k, else k-1 full blocks plus the visible part of the local block."""
+    t = positions(w)
+    local = t // w.block_size
+    sparse = (w.topk - 1) * w.block_size + (t % w.block_size) + 1
+    return np.where(local < w.topk, t + 1, sparse)
+
+
+def index_flops(w):
+    return 2.0 * w.index_dim * w.heads_kv * w.batch * float((positions(w) + 1).sum())
+
+
+def attn_flops(w):
+    return 4.0 * w.head_dim * w.heads_q * w.batch * float(visible_tokens(w).sum())
+
+
+def decode_bytes(w):
+    """Algorithmic HBM bytes of one decode step: the index-key scan, the
+    selected K/V blocks, Q, O, Q_idx and the selection."""
+    kidx = w.batch * w.seqlen_k * w.index_dim * 2
+    kv = w.batch * w.heads_kv * float(visible_tokens(w).sum()) * w.head_dim * 2 * 2
+    q = w.batch * w.seqlen_q * w.heads_q * w.head_dim * 2
+    qidx = w.batch * w.seqlen_q * w.heads_kv * w.index_dim * 2
+    idx = w.batch * w.heads_kv * w.seqlen_q * w.topk * 4
+    return kidx + kv + 2 * q + qidx + idx
+
+
+# ------------------------------------------------------------ timing
+def time_loop(fn, steps, stream):
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def run_workload(w, steps, warmup):
+    import torch
+
+    import block_sparse_gqa_scores_amd as msa
+    import synth
+
+    dev = torch.device("cuda", 0)
+    t = synth.device_tensors(w, dev)
+    d = msa.dims_of(t["q"], t["k"], t["q_idx"], t["k_idx"], topk=w.topk)
+    ws = torch.empty(msa.msa_workspace_bytes(d, msa.ENTRY_FORWARD), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(t["q"])
+    idx = torch.empty((w.batch, w.heads_kv, w.seqlen_q, w.topk), dtype=torch.int32, device=dev)
+    bm = torch.empty((w.batch, w.heads_kv, w.seqlen_q, w.n_blk), dtype=torch.float32, device=dev)
+    attn_ws = torch.empty(msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_FWD), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk, out=out,
+                        workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_loop(step, steps, stream)
+    wall = time.perf_counter() - t0
+    # Per entry point, each timed over the same number of launches.
+    per = {
+        "msa_index_scores": time_loop(lambda: msa.msa_index_scores(t["q_idx"], t["k_idx"], topk=w.topk,
+                                                                  block_scores=bm), steps, stream),
+        "msa_block_topk": time_loop(lambda: msa.msa_block_topk(bm, seqlen_k=w.seqlen_k, topk=w.topk,
+                                                              block_idx=idx), steps, stream),
+        "msa_sparse_attn_fwd": time_loop(lambda: msa.msa_sparse_attn_fwd(t["q"], t["k"], t["v"], idx, out=out,
+                                                                        workspace=attn_ws), steps, stream),
+    }
+    return t, ms, wall, per
+
+
+# ------------------------------------------------------------ CPU baseline
+def sample_rows(w, n_random, seed=1):
+    """Stratified (b, i, g) rows: first/last query of random query blocks, the
+    dense/sparse boundary (t = 2047, 2048), t = 0 or 127 mod 128, and random
+    rows."""
+    rng = np.random.default_rng(seed)
+    off = w.seqlen_k - w.seqlen_q
+    qs = set()
+    nqb = -(-w.seqlen_q // 128)
+    for qb in rng.choice(nqb, size=min(nqb, 64), replace=False):
+        qs.update({int(qb) * 128, min(w.seqlen_q - 1, int(qb) * 128 + 127)})
+    qs.update(t - off for t in (2047, 2048) if 0 <= t - off < w.seqlen_q)
+    qs.update(int(x) for x in rng.integers(0, w.seqlen_q, size=n_random))
+    rows = [(int(rng.integers(0, w.batch)), q, g) for q in sorted(qs) for g in range(w.heads_kv)]
+    return np.array(rows, dtype=np.int64)
+
+
+def cpu_baseline(w, t, budget_s):
+    import oracle
+    import torch
+
+    h = {k: v.contiguous().view(torch.int16).cpu().numpy().view(np.uint16) for k, v in t.items()}
+    p = oracle.Problem.of(w)
+    threads = oracle.default_threads()
+    # Calibrate on a small sample, then size the sample to the time budget.
+    probe = sample_rows(w, 8, seed=2)[: max(threads, 16)]
+    t0 = time.perf_counter()
+    oracle.forward(p, h["q"], h["k"], h["v"], h["q_idx"], h["k_idx"], rows=probe, threads=threads)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    n_random = int(max(16, budget_s / max(per_row, 1e-6) / w.heads_kv - 140))
+    rows = sample_rows(w, n_random)
+    t0 = time.perf_counter()
+    oracle.forward(p, h["q"], h["k"], h["v"], h["q_idx"], h["k_idx"], rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    rows_per_s = len(rows) / dt
+    return {"value": rows_per_s / w.heads_kv, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} (query, group) rows of {w.name} (stratified, seed 1) in {dt:.1f} s; "
+                      f"{rows_per_s:.1f} rows/s; a token is one query with all {w.heads_kv} groups"}
+
+
+# ------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_32k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(this path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    print(f"[bench] workload {w.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+    t, ms, wall, per = run_workload(w, args.steps, args.warmup)
+    fi, fa = index_flops(w), attn_flops(w)
+    tokens = w.batch * w.seqlen_q
+    tflops = (fi + fa) / (ms * 1e-3) / 1e12
+    kernels = {
+        "msa_index_scores": {"ms": per["msa_index_scores"], "tflops": fi / (per["msa_index_scores"] * 1e-3) / 1e12},
+        "msa_block_topk": {"ms": per["msa_block_topk"]},
+        "msa_sparse_attn_fwd": {"ms": per["msa_sparse_attn_fwd"],
+                                "tflops": fa / (per["msa_sparse_attn_fwd"] * 1e-3) / 1e12},
+    }
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    if dom == "msa_block_topk":
+        nbytes = w.batch * w.heads_kv * w.seqlen_q * (w.n_blk * 4 + w.topk * 4)
+        ach = nbytes / (per[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS, "traffic": None, "step": dom}
+    else:
+        ach = kernels[dom]["tflops"]
+        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "step": dom}
+    print(f"[bench] {ms:.3f} ms/step; per entry {json.dumps(per)}", file=sys.stderr, flush=True)
+
+    res = {
+        "metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen_q": w.seqlen_q, "seqlen_k": w.seqlen_k,
+                   "heads_q": w.heads_q, "heads_kv": w.heads_kv, "head_dim": w.head_dim,
+                   "index_dim": w.index_dim, "block_size": w.block_size, "topk": w.topk,
+                   "parallelism": "single GPU"},
+        "tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+        "algorithmic_flops": {"index": fi, "attention": fa},
+        "kernels": kernels, "roofline": roof, "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
+    del t
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        wd = synth.WORKLOADS["decode_64x256k"]
+        print(f"[bench] decode workload {wd.name}", file=sys.stderr, flush=True)
+        td, msd, _, perd = run_workload(wd, args.steps, args.warmup)
+        nbytes = decode_bytes(wd)
+        gbs = nbytes / (msd * 1e-3) / 1e9
+        res["decode"] = {"workload": wd.name, "ms_per_step": msd, "algorithmic_bytes": nbytes,
+                         "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+                         "tokens/s": wd.batch * wd.seqlen_q / (msd * 1e-3),
+                         "kernels_ms": perd}
+        del td
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
