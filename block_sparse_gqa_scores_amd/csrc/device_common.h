@@ -25,6 +25,12 @@ __device__ __forceinline__ f32x16 mfma32x32x16(uint4 a, uint4 b, f32x16 c) {
                                                  0, 0, 0);
 }
 
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
 // 16-byte load that is not expected to be reused (streamed once).
 __device__ __forceinline__ uint4 load_nt16(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -38,8 +44,27 @@ __device__ __forceinline__ int mfma32_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
+// max(a, b, c) in one v_max3_f32 (operands are never NaN where it is used:
+// scores are finite or -inf, so no NaN canonicalisation is needed).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
-  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Max of the 16 values of an MFMA 32x32 output register block and `m`.
+__device__ __forceinline__ float max16(float m, const f32x16& x) {
+  const float a = max3f(x[0], x[1], x[2]);
+  const float b = max3f(x[3], x[4], x[5]);
+  const float c = max3f(x[6], x[7], x[8]);
+  const float d = max3f(x[9], x[10], x[11]);
+  const float e = max3f(x[12], x[13], x[14]);
+  return max3f(max3f(a, b, c), max3f(d, e, x[15]), m);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z = {};
+  return z;
 }
 
 // Value of `x` held by lane (l ^ 32).
@@ -53,6 +78,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   a += 0x7FFFu + ((a >> 16) & 1u);
   b += 0x7FFFu + ((b >> 16) & 1u);
   return (a >> 16) | (b & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  // round-to-nearest-even of two fp32 values to fp16, packed low|high
+  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

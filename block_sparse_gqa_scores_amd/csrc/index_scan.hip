@@ -19,16 +19,15 @@ namespace {
 
 constexpr int kBlock = 128;        // keys per block (the pages' block size)
 constexpr int kThreads = 256;      // 4 waves
-constexpr int kRowsPerWave = 64;   // two 32-row MFMA N tiles
-constexpr int kRowsPerWg = 256;
 constexpr int kChunk = 16;         // key blocks per workgroup
+constexpr int kStageStride = kChunk + 1;  // padded: conflict-free stage writes
 
 struct ScanArgs {
   const uint16_t* q_idx;
   const uint16_t* k_idx;
   float* bm;
   int S_q, S_k, H_kv, n_blk;
-  int n_qtiles;   // ceil(S_q * H_kv / 256)
+  int n_qtiles;   // ceil(S_q * H_kv / rows per workgroup)
   int batch;
 };
 
@@ -41,14 +40,19 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   else return chunk ^ ((row >> 1) & 7);
 }
 
-template <int DIDX>
-__global__ __launch_bounds__(kThreads, 2) void index_scan_prefill(ScanArgs a) {
+// NT 32-row MFMA N tiles per wave: every 16-byte key fragment read from LDS
+// feeds NT matrix instructions.
+template <int DIDX, int NT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) {
+  constexpr int kThreads = 64 * WAVES;
   constexpr int KS = DIDX / 16;           // MFMA k-steps
   constexpr int CPR = DIDX / 8;           // 16-byte chunks per key row
   constexpr int TILE_CHUNKS = kBlock * CPR;
   constexpr int LOADS = TILE_CHUNKS / kThreads;  // 16-byte loads per thread
-  __shared__ uint4 ktile[2][TILE_CHUNKS];
-  __shared__ float stage[kRowsPerWg * kChunk];
+  constexpr int ROWS_W = 32 * NT;
+  constexpr int ROWS_WG = WAVES * ROWS_W;
+  __shared__ u32x4 ktile[2][TILE_CHUNKS];
+  __shared__ float stage[ROWS_WG * kStageStride];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -61,95 +65,103 @@ __global__ __launch_bounds__(kThreads, 2) void index_scan_prefill(ScanArgs a) {
 
   const int R = a.S_q * a.H_kv;
   const int off = a.S_k - a.S_q;        // position of query i is i + off
-  const int wg_r0 = qt * kRowsPerWg;
-  const int wg_r1 = min(wg_r0 + kRowsPerWg, R) - 1;  // last valid row
+  const int wg_r0 = qt * ROWS_WG;
+  const int wg_r1 = min(wg_r0 + ROWS_WG, R) - 1;  // last valid row
   const int j0 = chunk * kChunk;
   const int nj = min(kChunk, a.n_blk - j0);
   const int wg_lmax = (wg_r1 / a.H_kv + off) / kBlock;  // largest local block
   const int nj_live = max(0, min(nj, wg_lmax - j0 + 1));
 
   // The wave's rows and their causal positions.
-  const int w_r0 = wg_r0 + wave * kRowsPerWave;
+  const int w_r0 = wg_r0 + wave * ROWS_W;
   const int w_t_min = (min(w_r0, R - 1) / a.H_kv) + off;
-  const int w_t_max = (min(w_r0 + kRowsPerWave - 1, R - 1) / a.H_kv) + off;
-  int t_col[2];
+  const int w_t_max = (min(w_r0 + ROWS_W - 1, R - 1) / a.H_kv) + off;
+  int t_col[NT];
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
+  for (int n = 0; n < NT; ++n) {
     const int r = w_r0 + 32 * n + (lane & 31);
     t_col[n] = r < R ? r / a.H_kv + off : -1;
   }
 
-  // Stationary B operand: this wave's 64 index-query rows.
-  uint4 qb[2][KS];
+  // Stationary B operand: this wave's index-query rows.
+  u32x4 qb[NT][KS];
   {
     const uint16_t* qbase = a.q_idx + (size_t)b * R * DIDX;
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int r = w_r0 + 32 * n + (lane & 31);
+    for (int n = 0; n < NT; ++n) {
+      const int r = min(w_r0 + 32 * n + (lane & 31), R - 1);  // rows past R are never stored
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (r < R)
-          qb[n][ks] = *reinterpret_cast<const uint4*>(qbase + (size_t)r * DIDX + 16 * ks + 8 * (lane >> 5));
-        else
-          qb[n][ks] = make_uint4(0, 0, 0, 0);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        qb[n][ks] = *reinterpret_cast<const u32x4*>(qbase + (size_t)r * DIDX + 16 * ks + 8 * (lane >> 5));
     }
   }
 
   const uint16_t* kbase = a.k_idx + (size_t)b * a.S_k * DIDX;
-  uint4 pre[LOADS];
-  auto load_tile = [&](int j) {
+  // Tile geometry of this thread's LOADS 16-byte pieces: key row and LDS slot.
+  int t_row[LOADS], t_lds[LOADS];
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int q = it * kThreads + tid;
-      const int row = q / CPR, c = q % CPR;
-      const int s = j * kBlock + row;
-      pre[it] = s < a.S_k ? *reinterpret_cast<const uint4*>(kbase + (size_t)s * DIDX + 8 * c)
-                          : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int q = it * kThreads + tid;
-      const int row = q / CPR, c = q % CPR;
-      ktile[buf][row * CPR + swz<DIDX>(row, c)] = pre[it];
-    }
-  };
+  for (int it = 0; it < LOADS; ++it) {
+    const int q = it * kThreads + tid;
+    const int row = q / CPR, c = q % CPR;
+    t_row[it] = row;
+    t_lds[it] = row * CPR + swz<DIDX>(row, c);
+  }
+  const int t_col16 = 8 * ((tid) % CPR);  // same column for every piece (kThreads % CPR == 0)
+  u32x4 pre[LOADS];  // native vectors: stay in registers
+  // Rows past S_k are causally masked for every query; reading a clamped row
+  // instead keeps the loads unconditional (a fixed count in flight).
+#define MSA_LOAD_TILE(J)                                                                   \
+  _Pragma("unroll") for (int it = 0; it < LOADS; ++it) {                                   \
+    const int s_ = min((J) * kBlock + t_row[it], a.S_k - 1);                               \
+    pre[it] = *reinterpret_cast<const u32x4*>(kbase + (size_t)s_ * DIDX + t_col16);        \
+  }
+#define MSA_STORE_TILE(BUF) \
+  _Pragma("unroll") for (int it = 0; it < LOADS; ++it) ktile[BUF][t_lds[it]] = pre[it];
 
   if (nj_live > 0) {
-    load_tile(j0);
-    store_tile(0);
+    MSA_LOAD_TILE(j0)
+    MSA_STORE_TILE(0)
   }
+  // Everything loaded so far (index queries, first tile) has landed; saying so
+  // explicitly keeps the loop's MFMAs from waiting on the next tile's loads.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  const bool lo = lane < 32;
   for (int jj = 0; jj < nj_live; ++jj) {
     const int j = j0 + jj;
-    if (jj + 1 < nj_live) load_tile(j + 1);
-    const int buf = jj & 1;
-    float best;
+    if (jj + 1 < nj_live) { MSA_LOAD_TILE(j + 1) }
+    // Compiler-only fences: keep the next tile's global loads before the
+    // compute and its LDS stores after it, so the loads fly during the MFMAs.
+    asm volatile("" ::: "memory");
+    const u32x4* kt = ktile[jj & 1];
+    float best[NT / 2];
     if (j * kBlock > w_t_max) {
-      best = neg_inf();  // nothing visible to any row of this wave
+#pragma unroll
+      for (int p2 = 0; p2 < NT / 2; ++p2) best[p2] = neg_inf();  // nothing visible to this wave
     } else {
       const bool need_mask = j * kBlock + kBlock - 1 > w_t_min;
-      float m[2] = {neg_inf(), neg_inf()};
+      float m[NT];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) m[n] = neg_inf();
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        f32x16 acc[2];
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
         const int krow = mt * 32 + (lane & 31);
+        f32x16 acc[NT];
+        {
+          const u32x4 av = kt[krow * CPR + swz<DIDX>(krow, lane >> 5)];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const uint4 av = ktile[buf][krow * CPR + swz<DIDX>(krow, 2 * ks + (lane >> 5))];
-          acc[0] = mfma32x32x16(av, qb[0][ks], acc[0]);
-          acc[1] = mfma32x32x16(av, qb[1][ks], acc[1]);
+          for (int n = 0; n < NT; ++n) acc[n] = mfma32x32x16(av, qb[n][0], zero16());
+        }
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks) {
+          const u32x4 av = kt[krow * CPR + swz<DIDX>(krow, 2 * ks + (lane >> 5))];
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[n] = mfma32x32x16(av, qb[n][ks], acc[n]);
         }
         if (need_mask) {
 #pragma unroll
-          for (int n = 0; n < 2; ++n)
+          for (int n = 0; n < NT; ++n)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int s = j * kBlock + mt * 32 + mfma32_row(r, lane);
@@ -157,30 +169,35 @@ __global__ __launch_bounds__(kThreads, 2) void index_scan_prefill(ScanArgs a) {
             }
         }
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          float x = m[n];
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) x = max3f(x, acc[n][r], acc[n][r + 1]);
-          m[n] = x;
-        }
+        for (int n = 0; n < NT; ++n) m[n] = max16(m[n], acc[n]);
       }
-      // Lanes < 32 finish rows of tile 0, lanes >= 32 rows of tile 1.
-      const bool lo = lane < 32;
-      const float give = lo ? m[1] : m[0];
-      const float got = swap_halves(give);
-      best = __builtin_fmaxf(lo ? m[0] : m[1], got);
+      // Tile pair (2p, 2p+1): lanes < 32 finish tile 2p, lanes >= 32 tile 2p+1,
+      // so lane l ends with row w_r0 + 64 p + l.
+#pragma unroll
+      for (int p2 = 0; p2 < NT / 2; ++p2) {
+        const float give = lo ? m[2 * p2 + 1] : m[2 * p2];
+        const float got = swap_halves(give);
+        best[p2] = __builtin_fmaxf(lo ? m[2 * p2] : m[2 * p2 + 1], got);
+      }
     }
-    stage[(wave * kRowsPerWave + lane) * kChunk + jj] = best;
-    if (jj + 1 < nj_live) store_tile(buf ^ 1);
+#pragma unroll
+    for (int p2 = 0; p2 < NT / 2; ++p2)
+      stage[(wave * ROWS_W + 64 * p2 + lane) * kStageStride + jj] = best[p2];
+    asm volatile("" ::: "memory");
+    if (jj + 1 < nj_live) { MSA_STORE_TILE((jj & 1) ^ 1) }
     __syncthreads();
   }
 
-  // Each thread writes one row's nj block scores (contiguous in memory).
-  const int r = wg_r0 + tid;
-  if (r < R && nj > 0) {
+#undef MSA_LOAD_TILE
+#undef MSA_STORE_TILE
+
+  // Each row's nj block scores are contiguous in memory.
+  for (int rr = tid; rr < ROWS_WG; rr += kThreads) {
+    const int r = wg_r0 + rr;
+    if (r >= R || nj <= 0) continue;
     const int i = r / a.H_kv, g = r - (r / a.H_kv) * a.H_kv;
     float* dst = a.bm + (((size_t)b * a.H_kv + g) * a.S_q + i) * a.n_blk + j0;
-    const float* src = stage + tid * kChunk;
+    const float* src = stage + rr * kStageStride;
     if ((a.n_blk & 3) == 0) {
       for (int q = 0; q < nj; q += 4) {
         float4 v;
@@ -221,10 +238,10 @@ __global__ __launch_bounds__(kThreads, 2) void index_scan_decode(ScanArgs a) {
   uint4 qb[KS];
   {
     const uint16_t* qbase = a.q_idx + (size_t)b * R * DIDX;
+    const int rc = min(r, R - 1);  // rows past R are never stored
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qb[ks] = r < R ? *reinterpret_cast<const uint4*>(qbase + (size_t)r * DIDX + 16 * ks + 8 * (lane >> 5))
-                     : make_uint4(0, 0, 0, 0);
+      qb[ks] = *reinterpret_cast<const uint4*>(qbase + (size_t)rc * DIDX + 16 * ks + 8 * (lane >> 5));
   }
   const uint16_t* kbase = a.k_idx + (size_t)b * a.S_k * DIDX;
 
@@ -239,21 +256,18 @@ __global__ __launch_bounds__(kThreads, 2) void index_scan_decode(ScanArgs a) {
       uint4 av[4][KS];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const int s = j * kBlock + mt * 32 + (lane & 31);
+        const int s = min(j * kBlock + mt * 32 + (lane & 31), a.S_k - 1);  // masked past S_k
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          av[mt][ks] = s < a.S_k ? load_nt16(kbase + (size_t)s * DIDX + 16 * ks + 8 * (lane >> 5))
-                                 : make_uint4(0, 0, 0, 0);
+          av[mt][ks] = load_nt16(kbase + (size_t)s * DIDX + 16 * ks + 8 * (lane >> 5));
       }
       const bool need_mask = j * kBlock + kBlock - 1 > t_min;
       float m = neg_inf();
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        f32x16 acc;
+        f32x16 acc = mfma32x32x16(av[mt][0], qb[0], zero16());
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) acc[rr] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma32x32x16(av[mt][ks], qb[ks], acc);
+        for (int ks = 1; ks < KS; ++ks) acc = mfma32x32x16(av[mt][ks], qb[ks], acc);
         if (need_mask) {
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
@@ -261,8 +275,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_scan_decode(ScanArgs a) {
             if (s > t_col) acc[rr] = neg_inf();
           }
         }
-#pragma unroll
-        for (int rr = 0; rr < 16; rr += 2) m = max3f(m, acc[rr], acc[rr + 1]);
+        m = max16(m, acc);
       }
       best = __builtin_fmaxf(m, swap_halves(m));
     }
@@ -274,6 +287,17 @@ __global__ __launch_bounds__(kThreads, 2) void index_scan_decode(ScanArgs a) {
 }
 
 }  // namespace
+
+// N tiles per wave and waves per workgroup of the prefill kernel.
+#ifndef MSA_SCAN_NT
+#define MSA_SCAN_NT 2
+#endif
+#ifndef MSA_SCAN_WAVES
+#define MSA_SCAN_WAVES 8
+#endif
+constexpr int kNT = MSA_SCAN_NT;
+constexpr int kWaves = MSA_SCAN_WAVES;
+constexpr int kRowsPerWg = kWaves * 32 * kNT;
 
 hipError_t launch_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, float* bm,
                                int batch, int S_q, int S_k, int H_kv, int D_idx, int n_blk,
@@ -293,16 +317,10 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, flo
   const long n_chunks = (n_blk + kChunk - 1) / kChunk;
   const long grid = n_chunks * batch * a.n_qtiles;
   if (D_idx == 128)
-    hipLaunchKernelGGL(index_scan_prefill<128>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((index_scan_prefill<128, kNT, kWaves>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
   else
-    hipLaunchKernelGGL(index_scan_prefill<64>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((index_scan_prefill<64, kNT, kWaves>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
-}
-
-long index_scores_grid(int batch, int S_q, int H_kv, int n_blk) {
-  const int R = S_q * H_kv;
-  if (R <= 32) return (long)batch * ((n_blk + 4 * kDecodeBlocksPerWave - 1) / (4 * kDecodeBlocksPerWave));
-  return (long)((n_blk + kChunk - 1) / kChunk) * batch * ((R + kRowsPerWg - 1) / kRowsPerWg);
 }
 
 }  // namespace msa

@@ -12,7 +12,6 @@ namespace msa {
 hipError_t launch_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, float* bm,
                                int batch, int S_q, int S_k, int H_kv, int D_idx, int n_blk,
                                hipStream_t stream);
-long index_scores_grid(int batch, int S_q, int H_kv, int n_blk);
 
 // Top-k selection (see block_topk.hip).
 hipError_t launch_block_topk(const float* bm, int32_t* idx, int batch, int S_q, int S_k,

@@ -35,6 +35,8 @@ constexpr int kSubTiles = 4;    // 4-wave sub-tiles per work item
 constexpr int kScanPerWg = 1024;
 constexpr int kVStride = kBlock + 4;  // bf16 per row of the transposed V tile
 constexpr size_t kPartBudget = size_t(4) << 30;  // bytes of partials per chunk
+constexpr int kBuildQueries = 256;   // queries per bucket-build workgroup
+constexpr int kHistBins = 8192;      // widest row whose histogram lives in LDS
 
 struct Params {
   const uint16_t* q;
@@ -55,8 +57,9 @@ struct Params {
   int32_t* blk_sums;     // 2 * n_scan_wg
   int32_t* edges;        // slot ids grouped by bucket
   int2* work;            // (bucket, first edge in bucket)
-  float* part_lse;       // [slot][G], log2 units
-  float* part_o;         // [slot][G][D], normalised per block
+  float* part_lse;       // [slot][G]: log2-sum-exp of the block's visible logits
+  float* part_sc;        // [slot][G]: max |O_e| of the row
+  uint16_t* part_o;      // [slot][G][D] fp16: O_e / max |O_e|, O_e normalised per block
 };
 
 // Slot of edge (b, g, il, e) inside the chunk.
@@ -67,6 +70,67 @@ __device__ __forceinline__ long slot_of(const Params& p, int bg, int il, int e) 
 __global__ void zero_kernel(int32_t* a, long n) {
   for (long x = (long)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (long)gridDim.x * blockDim.x)
     a[x] = 0;
+}
+
+// Bucket build with per-workgroup LDS histograms: a workgroup takes
+// kBuildQueries queries of one (b, g), counts their edges per block in LDS and
+// touches global memory once per distinct block.  Used when the histogram of
+// n_blk bins fits in LDS; count_kernel / fill_kernel below cover wider rows.
+__device__ __forceinline__ bool edge_ok(const Params& p, int i, int j) {
+  return j >= 0 && j <= (i + p.S_k - p.S_q) / kBlock;
+}
+
+__global__ __launch_bounds__(256) void bucket_count_kernel(Params p) {
+  extern __shared__ int32_t hist[];  // n_blk
+  const int tiles = (p.Qc + kBuildQueries - 1) / kBuildQueries;
+  const int bg = blockIdx.x / tiles;
+  const int il0 = (blockIdx.x - bg * tiles) * kBuildQueries;
+  const int nq = min(min(kBuildQueries, p.Qc - il0), p.S_q - (p.q0 + il0));
+  if (nq <= 0) return;  // uniform
+  for (int x = threadIdx.x; x < p.n_blk; x += 256) hist[x] = 0;
+  __syncthreads();
+  const int32_t* sel = p.idx + ((long)bg * p.S_q + p.q0 + il0) * p.topk;
+  for (int s = threadIdx.x; s < nq * p.topk; s += 256) {
+    const int j = sel[s];
+    if (edge_ok(p, p.q0 + il0 + s / p.topk, j)) atomicAdd(&hist[j], 1);
+  }
+  __syncthreads();
+  int32_t* cnt = p.counts + (long)bg * p.n_blk;
+  for (int x = threadIdx.x; x < p.n_blk; x += 256)
+    if (hist[x]) atomicAdd(&cnt[x], hist[x]);
+}
+
+__global__ __launch_bounds__(256) void bucket_fill_kernel(Params p) {
+  extern __shared__ int32_t lds[];  // hist[n_blk], base[n_blk]
+  int32_t* hist = lds;
+  int32_t* base = lds + p.n_blk;
+  const int tiles = (p.Qc + kBuildQueries - 1) / kBuildQueries;
+  const int bg = blockIdx.x / tiles;
+  const int il0 = (blockIdx.x - bg * tiles) * kBuildQueries;
+  const int nq = min(min(kBuildQueries, p.Qc - il0), p.S_q - (p.q0 + il0));
+  if (nq <= 0) return;  // uniform
+  for (int x = threadIdx.x; x < p.n_blk; x += 256) hist[x] = 0;
+  __syncthreads();
+  const int32_t* sel = p.idx + ((long)bg * p.S_q + p.q0 + il0) * p.topk;
+  for (int s = threadIdx.x; s < nq * p.topk; s += 256) {
+    const int j = sel[s];
+    if (edge_ok(p, p.q0 + il0 + s / p.topk, j)) atomicAdd(&hist[j], 1);
+  }
+  __syncthreads();
+  const long b0 = (long)bg * p.n_blk;
+  for (int x = threadIdx.x; x < p.n_blk; x += 256) {
+    const int c = hist[x];
+    if (c) base[x] = p.offsets[b0 + x] + atomicAdd(&p.cursor[b0 + x], c);
+    hist[x] = 0;
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < nq * p.topk; s += 256) {
+    const int j = sel[s];
+    if (edge_ok(p, p.q0 + il0 + s / p.topk, j)) {
+      const int pos = base[j] + atomicAdd(&hist[j], 1);
+      p.edges[pos] = (int32_t)slot_of(p, bg, il0 + s / p.topk, s % p.topk);
+    }
+  }
 }
 
 __global__ void count_kernel(Params p) {
@@ -229,9 +293,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
     for (int it = 0; it < 8; ++it) {
       const int qd = it * kThreads + tid;
       const int row = qd >> 4, c = qd & 15;
-      const int s = j * kBlock + row;
-      const uint4 x = s < p.S_k ? *reinterpret_cast<const uint4*>(kb + (size_t)s * row_stride + 8 * c)
-                                : make_uint4(0, 0, 0, 0);
+      // Keys past S_k are causally masked for every query (their weight is
+      // exactly 0), so a clamped row is read instead of branching.
+      const int s = min(j * kBlock + row, p.S_k - 1);
+      const uint4 x = *reinterpret_cast<const uint4*>(kb + (size_t)s * row_stride + 8 * c);
       ktile[row * 16 + (c ^ (row & 15))] = x;
     }
 #pragma unroll
@@ -239,11 +304,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
       const int u = it * kThreads + tid;
       const int kp = (u & 15) + 16 * ((u >> 6) & 3);
       const int d0 = ((u >> 4) & 3) + 4 * ((u >> 8) & 3);
-      const int s = j * kBlock + 2 * kp;
-      const uint4 lo = s < p.S_k ? *reinterpret_cast<const uint4*>(vb + (size_t)s * row_stride + 8 * d0)
-                                 : make_uint4(0, 0, 0, 0);
-      const uint4 hi = s + 1 < p.S_k ? *reinterpret_cast<const uint4*>(vb + (size_t)(s + 1) * row_stride + 8 * d0)
-                                     : make_uint4(0, 0, 0, 0);
+      const int s0 = min(j * kBlock + 2 * kp, p.S_k - 1);
+      const int s1 = min(j * kBlock + 2 * kp + 1, p.S_k - 1);
+      const uint4 lo = *reinterpret_cast<const uint4*>(vb + (size_t)s0 * row_stride + 8 * d0);
+      const uint4 hi = *reinterpret_cast<const uint4*>(vb + (size_t)s1 * row_stride + 8 * d0);
       const uint32_t lw[4] = {lo.x, lo.y, lo.z, lo.w};
       const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
@@ -335,30 +399,38 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
           oacc[dt] = mfma32x32x16(make_uint4(a0.x, a0.y, a1.x, a1.y), pb, oacc[dt]);
         }
       }
+    float amax = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) amax = __builtin_fmaxf(amax, __builtin_fabsf(oacc[dt][r]));
+    amax = __builtin_fmaxf(amax, swap_halves(amax));
     if (valid) {
-      const float inv_l = 1.f / l;
-      float* po = p.part_o + ((size_t)slot * G + hh) * kD;
+      const float inv = amax > 0.f ? 1.f / amax : 0.f;
+      uint16_t* po = p.part_o + ((size_t)slot * G + hh) * kD;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          float4 v4;
-          v4.x = oacc[dt][4 * rq + 0] * inv_l;
-          v4.y = oacc[dt][4 * rq + 1] * inv_l;
-          v4.z = oacc[dt][4 * rq + 2] * inv_l;
-          v4.w = oacc[dt][4 * rq + 3] * inv_l;
-          *reinterpret_cast<float4*>(po + dt * 32 + 8 * rq + 4 * h) = v4;
+          uint2 v2;
+          v2.x = pack_f16x2(oacc[dt][4 * rq + 0] * inv, oacc[dt][4 * rq + 1] * inv);
+          v2.y = pack_f16x2(oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
+          *reinterpret_cast<uint2*>(po + dt * 32 + 8 * rq + 4 * h) = v2;
         }
-      if (h == 0) p.part_lse[(size_t)slot * G + hh] = mx + __builtin_amdgcn_logf(l);
+      if (h == 0) {
+        p.part_lse[(size_t)slot * G + hh] = mx + __builtin_amdgcn_logf(l);
+        p.part_sc[(size_t)slot * G + hh] = amax / l;
+      }
     }
   }
 }
 
 // Combines the partials of each (query, group): one wave per row.
+// O = sum_e 2^(lse_e - M) sc_e x_e / sum_e 2^(lse_e - M), LSE = M + log2(sum).
 template <int G>
 __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse) {
-  constexpr int NF = G * kD / 4;            // float4s per partial
-  constexpr int F = (NF + 63) / 64;         // float4s per lane
+  constexpr int NF = G * kD / 8;            // 16-byte pieces (8 halves) per record
+  constexpr int F = (NF + 63) / 64;         // pieces per lane
   const int lane = threadIdx.x & 63;
   const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= (long)p.B * p.H_kv * p.Qc) return;
@@ -370,13 +442,13 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse)
   const int32_t* sel = p.idx + ((long)bg * p.S_q + i) * p.topk;
   const int local = (i + p.S_k - p.S_q) / kBlock;  // entries past it are ignored
 
-  float M[F], L[F];
-  float4 acc[F];
+  float M[F], L[F], acc[F][8];
 #pragma unroll
   for (int u = 0; u < F; ++u) {
     M[u] = neg_inf();
     L[u] = 0.f;
-    acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[u][c] = 0.f;
   }
   for (int e = 0; e < p.topk; ++e) {
     if (sel[e] < 0 || sel[e] > local) continue;
@@ -384,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse)
 #pragma unroll
     for (int u = 0; u < F; ++u) {
       const int f = lane + 64 * u;
-      if (f < NF) M[u] = __builtin_fmaxf(M[u], p.part_lse[slot * G + f / (kD / 4)]);
+      if (f < NF) M[u] = __builtin_fmaxf(M[u], p.part_lse[slot * G + f / (kD / 8)]);
     }
   }
   for (int e = 0; e < p.topk; ++e) {
@@ -394,13 +466,17 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse)
     for (int u = 0; u < F; ++u) {
       const int f = lane + 64 * u;
       if (f < NF) {
-        const float wgt = __builtin_amdgcn_exp2f(p.part_lse[slot * G + f / (kD / 4)] - M[u]);
-        const float4 x = reinterpret_cast<const float4*>(p.part_o + (size_t)slot * G * kD)[f];
-        L[u] += wgt;
-        acc[u].x += wgt * x.x;
-        acc[u].y += wgt * x.y;
-        acc[u].z += wgt * x.z;
-        acc[u].w += wgt * x.w;
+        const int hh = f / (kD / 8);
+        const float wl = __builtin_amdgcn_exp2f(p.part_lse[slot * G + hh] - M[u]);
+        const float wx = wl * p.part_sc[slot * G + hh];
+        const uint4 x = reinterpret_cast<const uint4*>(p.part_o + (size_t)slot * G * kD)[f];
+        L[u] += wl;
+        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[u][2 * c] += wx * f16_lo(xw[c]);
+          acc[u][2 * c + 1] += wx * f16_hi(xw[c]);
+        }
       }
     }
   }
@@ -408,13 +484,15 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse)
   for (int u = 0; u < F; ++u) {
     const int f = lane + 64 * u;
     if (f >= NF) continue;
-    const int hh = f / (kD / 4);
-    const int d = (f - hh * (kD / 4)) * 4;
+    const int hh = f / (kD / 8);
+    const int d = (f - hh * (kD / 8)) * 8;
     const float inv = 1.f / L[u];
-    uint2 o;
-    o.x = pack_bf16x2(acc[u].x * inv, acc[u].y * inv);
-    o.y = pack_bf16x2(acc[u].z * inv, acc[u].w * inv);
-    *reinterpret_cast<uint2*>(p.out + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + d) = o;
+    uint4 o;
+    o.x = pack_bf16x2(acc[u][0] * inv, acc[u][1] * inv);
+    o.y = pack_bf16x2(acc[u][2] * inv, acc[u][3] * inv);
+    o.z = pack_bf16x2(acc[u][4] * inv, acc[u][5] * inv);
+    o.w = pack_bf16x2(acc[u][6] * inv, acc[u][7] * inv);
+    *reinterpret_cast<uint4*>(p.out + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + d) = o;
     if (with_lse && d == 0)
       p.lse[((size_t)b * p.H_q + g * G + hh) * p.S_q + i] =
           (M[u] + __builtin_amdgcn_logf(L[u])) * 0.69314718055994530942f;
@@ -424,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse)
 struct Layout {
   int Qc, QT, n_scan_wg;
   long NB, E, T;
-  size_t counts, cursor, offsets, tile_off, blk_sums, edges, work, part_lse, part_o, total;
+  size_t counts, cursor, offsets, tile_off, blk_sums, edges, work, part_lse, part_sc, part_o, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -433,7 +511,7 @@ Layout make_layout(const AttnShape& s) {
   Layout L{};
   const int G = s.H_q / s.H_kv;
   L.QT = kSubTiles * 4 * (32 / G);
-  const size_t per_query = (size_t)s.batch * s.H_kv * s.topk * ((size_t)G * (kD + 1) * 4 + 8 + 4);
+  const size_t per_query = (size_t)s.batch * s.H_kv * s.topk * ((size_t)G * (kD * 2 + 8) + 8 + 4);
   long qc = (long)(kPartBudget / per_query);
   if (qc >= 128) qc -= qc % 128;
   L.Qc = (int)std::max(1L, std::min<long>(qc, s.S_q));
@@ -450,7 +528,8 @@ Layout make_layout(const AttnShape& s) {
   L.edges = o;    o = align256(o + L.E * 4);
   L.work = o;     o = align256(o + L.T * 8);
   L.part_lse = o; o = align256(o + (size_t)L.E * G * 4);
-  L.part_o = o;   o = align256(o + (size_t)L.E * G * kD * 4);
+  L.part_sc = o;  o = align256(o + (size_t)L.E * G * 4);
+  L.part_o = o;   o = align256(o + (size_t)L.E * G * kD * 2);
   L.total = o;
   return L;
 }
@@ -471,11 +550,19 @@ static hipError_t launch_g(const AttnShape& s, const Layout& L, Params p, bool w
     const long slots = (long)s.batch * s.H_kv * L.Qc * s.topk;
     hipLaunchKernelGGL(zero_kernel, dim3(grid_cap(L.NB, 256)), dim3(256), 0, st, p.counts, L.NB);
     hipLaunchKernelGGL(zero_kernel, dim3(grid_cap(L.NB, 256)), dim3(256), 0, st, p.cursor, L.NB);
-    hipLaunchKernelGGL(count_kernel, dim3(grid_cap(slots, 256)), dim3(256), 0, st, p);
+    const bool lds_hist = s.n_blk <= kHistBins;
+    const long build_grid = (long)s.batch * s.H_kv * ((L.Qc + kBuildQueries - 1) / kBuildQueries);
+    if (lds_hist)
+      hipLaunchKernelGGL(bucket_count_kernel, dim3((unsigned)build_grid), dim3(256), s.n_blk * 4, st, p);
+    else
+      hipLaunchKernelGGL(count_kernel, dim3(grid_cap(slots, 256)), dim3(256), 0, st, p);
     hipLaunchKernelGGL(scan_local_kernel, dim3(L.n_scan_wg), dim3(256), 0, st, p);
     hipLaunchKernelGGL(scan_blocks_kernel, dim3(1), dim3(256), 0, st, p, L.n_scan_wg);
     hipLaunchKernelGGL(scan_add_kernel, dim3(L.n_scan_wg), dim3(256), 0, st, p);
-    hipLaunchKernelGGL(fill_kernel, dim3(grid_cap(slots, 256)), dim3(256), 0, st, p);
+    if (lds_hist)
+      hipLaunchKernelGGL(bucket_fill_kernel, dim3((unsigned)build_grid), dim3(256), s.n_blk * 8, st, p);
+    else
+      hipLaunchKernelGGL(fill_kernel, dim3(grid_cap(slots, 256)), dim3(256), 0, st, p);
     hipLaunchKernelGGL(attn_partial_kernel<G>, dim3((unsigned)L.T), dim3(kThreads), 0, st, p);
     const long rows = (long)s.batch * s.H_kv * L.Qc;
     hipLaunchKernelGGL(merge_kernel<G>, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, st, p,
@@ -505,7 +592,8 @@ hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint1
   p.edges = reinterpret_cast<int32_t*>(base + L.edges);
   p.work = reinterpret_cast<int2*>(base + L.work);
   p.part_lse = reinterpret_cast<float*>(base + L.part_lse);
-  p.part_o = reinterpret_cast<float*>(base + L.part_o);
+  p.part_sc = reinterpret_cast<float*>(base + L.part_sc);
+  p.part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
   const bool with_lse = lse != nullptr;
   switch (p.G) {
     case 1: return launch_g<1>(s, L, p, with_lse, stream);
