@@ -37,6 +37,7 @@ constexpr int kVStride = kBlock + 4;  // bf16 per row of the transposed V tile
 constexpr size_t kPartBudget = size_t(4) << 30;  // bytes of partials per chunk
 constexpr int kBuildQueries = 256;   // queries per bucket-build workgroup
 constexpr int kHistBins = 8192;      // widest row whose histogram lives in LDS
+constexpr int kMaxQT = kSubTiles * 4 * 32;  // edges per work item at G = 1
 
 struct Params {
   const uint16_t* q;
@@ -265,11 +266,18 @@ __global__ void fill_kernel(Params p) {
 }
 
 // One work item: (bucket (b, g, j), up to QT of its edges).
+//
+// Each wave takes QW queries x G heads = 32 MFMA rows per sub-tile.  Rows past
+// the item's last edge are clamped onto that edge: they recompute and rewrite
+// exactly the same values, which keeps every load and store unconditional (a
+// fixed number of memory operations in flight, no exec-skip branches).  The Q
+// rows of the next sub-tile are loaded while the current one computes.
 template <int G>
 __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
   constexpr int QW = 32 / G;  // queries per wave (32 MFMA rows = QW queries x G heads)
-  __shared__ uint4 ktile[kBlock * 16];                 // [key][16 chunks], swizzled
+  __shared__ u32x4 ktile[kBlock * 16];                 // [key][16 chunks], swizzled
   __shared__ uint32_t vt[kD * kVStride / 2];           // [d][key] bf16, padded rows
+  __shared__ int32_t s_slot[kMaxQT];                   // this item's edge slots
 
   const int w = blockIdx.x;
   if (w >= p.tile_off[p.NB]) return;  // uniform: past the last work item
@@ -284,6 +292,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
   const int g = bg - b * p.H_kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
 
+  for (int x = tid; x < n_here; x += kThreads) s_slot[x] = p.edges[ebase + x];
   // K_j, V_j of group g into LDS (V transposed to [d][key]).
   {
     const size_t row_stride = (size_t)p.H_kv * kD;
@@ -296,8 +305,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
       // Keys past S_k are causally masked for every query (their weight is
       // exactly 0), so a clamped row is read instead of branching.
       const int s = min(j * kBlock + row, p.S_k - 1);
-      const uint4 x = *reinterpret_cast<const uint4*>(kb + (size_t)s * row_stride + 8 * c);
-      ktile[row * 16 + (c ^ (row & 15))] = x;
+      ktile[row * 16 + (c ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * c);
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -306,52 +314,57 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
       const int d0 = ((u >> 4) & 3) + 4 * ((u >> 8) & 3);
       const int s0 = min(j * kBlock + 2 * kp, p.S_k - 1);
       const int s1 = min(j * kBlock + 2 * kp + 1, p.S_k - 1);
-      const uint4 lo = *reinterpret_cast<const uint4*>(vb + (size_t)s0 * row_stride + 8 * d0);
-      const uint4 hi = *reinterpret_cast<const uint4*>(vb + (size_t)s1 * row_stride + 8 * d0);
-      const uint32_t lw[4] = {lo.x, lo.y, lo.z, lo.w};
-      const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w};
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(vb + (size_t)s0 * row_stride + 8 * d0);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(vb + (size_t)s1 * row_stride + 8 * d0);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t a = (e & 1) ? (lw[e >> 1] >> 16) : (lw[e >> 1] & 0xFFFFu);
-        const uint32_t c2 = (e & 1) ? (hw[e >> 1] & 0xFFFF0000u) : (hw[e >> 1] << 16);
+        const uint32_t a = (e & 1) ? (lo[e >> 1] >> 16) : (lo[e >> 1] & 0xFFFFu);
+        const uint32_t c2 = (e & 1) ? (hi[e >> 1] & 0xFFFF0000u) : (hi[e >> 1] << 16);
         vt[((8 * d0 + e) * kVStride + 2 * kp) >> 1] = a | c2;
       }
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   const int off = p.S_k - p.S_q;
   const int n = lane & 31;          // MFMA row of this lane
   const int qi = n / G, hh = n - (n / G) * G;
-  for (int sub = 0; sub < n_here; sub += 4 * QW) {
-    const int qbase = sub + wave * QW;
-    if (qbase >= n_here) break;  // wave-uniform
-    const int qx = qbase + qi;
-    const bool valid = qx < n_here;
-    long slot = 0;
-    int i = 0, t = 0x7FFFFFFF;
-    if (valid) {
-      slot = p.edges[ebase + qx];
-      const int il = (int)((slot / p.topk) % p.Qc);
-      i = p.q0 + il;
-      t = i + off;
-    }
-    uint4 qb[8];
-    {
-      const uint16_t* qrow = p.q + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD;
+  const size_t q_head_off = (size_t)(g * G + hh) * kD + 8 * h;
+
+  // Row geometry of sub-tile `sub` for this lane (clamped onto the last edge).
+  auto row_slot = [&](int sub) { return s_slot[min(sub + wave * QW + qi, n_here - 1)]; };
+  auto q_of_slot = [&](int slot) { return p.q0 + (int)((slot / p.topk) % p.Qc); };
+  auto load_q = [&](u32x4* dst, int i) {
+    const uint16_t* qrow = p.q + ((size_t)b * p.S_q + i) * p.H_q * kD + q_head_off;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        qb[ks] = valid ? *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * h) : make_uint4(0, 0, 0, 0);
-    }
+    for (int ks = 0; ks < 8; ++ks) dst[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
+  };
+
+  int slot = row_slot(0);
+  int i = q_of_slot(slot);
+  u32x4 qb[8];
+  load_q(qb, i);
+  for (int sub = 0; sub < n_here; sub += 4 * QW) {
+    if (sub + wave * QW >= n_here) break;  // wave-uniform
+    // Next sub-tile's Q rows fly while this one computes.
+    const int slot_n = row_slot(sub + 4 * QW);
+    const int i_n = q_of_slot(slot_n);
+    u32x4 qn[8];
+    load_q(qn, i_n);
+    asm volatile("" ::: "memory");
+
+    const int t = i + off;
     f32x16 sacc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
       const int krow = mt * 32 + n;
+      u32x4 ka[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        sacc[mt] = mfma32x32x16(ktile[krow * 16 + ((2 * ks + h) ^ (krow & 15))], qb[ks], sacc[mt]);
+      for (int ks = 0; ks < 8; ++ks) ka[ks] = ktile[krow * 16 + ((2 * ks + h) ^ (krow & 15))];
+      sacc[mt] = mfma32x32x16(ka[0], qb[0], zero16());
+#pragma unroll
+      for (int ks = 1; ks < 8; ++ks) sacc[mt] = mfma32x32x16(ka[ks], qb[ks], sacc[mt]);
     }
     const bool need_mask = __builtin_amdgcn_ballot_w64(j * kBlock + kBlock - 1 > t) != 0;
     float mx = neg_inf();
@@ -362,41 +375,44 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
         float x = sacc[mt][r] * p.scale_log2;
         if (need_mask && j * kBlock + mt * 32 + mfma32_row(r, lane) > t) x = neg_inf();
         sacc[mt][r] = x;
-        mx = __builtin_fmaxf(mx, x);
       }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) mx = max16(mx, sacc[mt]);
     mx = __builtin_fmaxf(mx, swap_halves(mx));
     float l = 0.f;
+    u32x4 pb[4][2];  // P in bf16, packed as the B operand of O^T = V^T P^T
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float e2 = __builtin_amdgcn_exp2f(sacc[mt][r] - mx);
         sacc[mt][r] = e2;
         l += e2;
       }
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        pb[mt][qq][0] = pack_bf16x2(sacc[mt][8 * qq + 0], sacc[mt][8 * qq + 1]);
+        pb[mt][qq][1] = pack_bf16x2(sacc[mt][8 * qq + 2], sacc[mt][8 * qq + 3]);
+        pb[mt][qq][2] = pack_bf16x2(sacc[mt][8 * qq + 4], sacc[mt][8 * qq + 5]);
+        pb[mt][qq][3] = pack_bf16x2(sacc[mt][8 * qq + 6], sacc[mt][8 * qq + 7]);
+      }
+    }
     l += swap_halves(l);
 
     f32x16 oacc[4];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-#pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
-        uint4 pb;
-        pb.x = pack_bf16x2(sacc[mt][8 * qq + 0], sacc[mt][8 * qq + 1]);
-        pb.y = pack_bf16x2(sacc[mt][8 * qq + 2], sacc[mt][8 * qq + 3]);
-        pb.z = pack_bf16x2(sacc[mt][8 * qq + 4], sacc[mt][8 * qq + 5]);
-        pb.w = pack_bf16x2(sacc[mt][8 * qq + 6], sacc[mt][8 * qq + 7]);
         const int key0 = mt * 32 + 16 * qq + 4 * h;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const int d = dt * 32 + n;
           const uint2 a0 = *reinterpret_cast<const uint2*>(&vt[(d * kVStride + key0) >> 1]);
           const uint2 a1 = *reinterpret_cast<const uint2*>(&vt[(d * kVStride + key0 + 8) >> 1]);
-          oacc[dt] = mfma32x32x16(make_uint4(a0.x, a0.y, a1.x, a1.y), pb, oacc[dt]);
+          const u32x4 av = {a0.x, a0.y, a1.x, a1.y};
+          oacc[dt] = (mt == 0 && qq == 0) ? mfma32x32x16(av, pb[mt][qq], zero16())
+                                          : mfma32x32x16(av, pb[mt][qq], oacc[dt]);
         }
       }
     float amax = 0.f;
@@ -405,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) amax = __builtin_fmaxf(amax, __builtin_fabsf(oacc[dt][r]));
     amax = __builtin_fmaxf(amax, swap_halves(amax));
-    if (valid) {
+    {
       const float inv = amax > 0.f ? 1.f / amax : 0.f;
       uint16_t* po = p.part_o + ((size_t)slot * G + hh) * kD;
 #pragma unroll
@@ -417,11 +433,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
           v2.y = pack_f16x2(oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
           *reinterpret_cast<uint2*>(po + dt * 32 + 8 * rq + 4 * h) = v2;
         }
-      if (h == 0) {
-        p.part_lse[(size_t)slot * G + hh] = mx + __builtin_amdgcn_logf(l);
-        p.part_sc[(size_t)slot * G + hh] = amax / l;
-      }
+      // Both wave halves hold the same row statistics; both store them.
+      p.part_lse[(size_t)slot * G + hh] = mx + __builtin_amdgcn_logf(l);
+      p.part_sc[(size_t)slot * G + hh] = amax / l;
     }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qb[ks] = qn[ks];
+    slot = slot_n;
+    i = i_n;
   }
 }
 
