@@ -77,6 +77,8 @@ def time_loop(fn, steps, stream):
 
 
 def run_workload(w, steps, warmup):
+    """Warm up, time `steps` forward steps, then time each internal stage over
+    another `steps` steps with events recorded on the launch stream."""
     import torch
 
     import block_sparse_gqa_scores_amd as msa
@@ -87,14 +89,11 @@ def run_workload(w, steps, warmup):
     d = msa.dims_of(t["q"], t["k"], t["q_idx"], t["k_idx"], topk=w.topk)
     ws = torch.empty(msa.msa_workspace_bytes(d, msa.ENTRY_FORWARD), dtype=torch.uint8, device=dev)
     out = torch.empty_like(t["q"])
-    idx = torch.empty((w.batch, w.heads_kv, w.seqlen_q, w.topk), dtype=torch.int32, device=dev)
-    bm = torch.empty((w.batch, w.heads_kv, w.seqlen_q, w.n_blk), dtype=torch.float32, device=dev)
-    attn_ws = torch.empty(msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_FWD), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def step(events=None):
         msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk, out=out,
-                        workspace=ws)
+                        workspace=ws, stage_events=events)
 
     for _ in range(warmup):
         step()
@@ -102,16 +101,60 @@ def run_workload(w, steps, warmup):
     t0 = time.perf_counter()
     ms = time_loop(step, steps, stream)
     wall = time.perf_counter() - t0
-    # Per entry point, each timed over the same number of launches.
-    per = {
-        "msa_index_scores": time_loop(lambda: msa.msa_index_scores(t["q_idx"], t["k_idx"], topk=w.topk,
-                                                                  block_scores=bm), steps, stream),
-        "msa_block_topk": time_loop(lambda: msa.msa_block_topk(bm, seqlen_k=w.seqlen_k, topk=w.topk,
-                                                              block_idx=idx), steps, stream),
-        "msa_sparse_attn_fwd": time_loop(lambda: msa.msa_sparse_attn_fwd(t["q"], t["k"], t["v"], idx, out=out,
-                                                                        workspace=attn_ws), steps, stream),
+
+    n_st = len(msa.STAGES)
+    evs = []
+    for _ in range(steps):
+        pair = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_st)]
+        for e in pair:
+            e.record(stream)  # creates the underlying event
+        evs.append(pair)
+    torch.cuda.synchronize()
+    for pair in evs:
+        step([e.cuda_event for e in pair])
+    torch.cuda.synchronize()
+    stage_ms = {name: sum(p[2 * s].elapsed_time(p[2 * s + 1]) for p in evs) / steps
+                for s, name in enumerate(msa.STAGES)}
+    return t, ms, wall, stage_ms, msa.msa_attn_chunks(d)
+
+
+def stage_work(w, chunks):
+    """Algorithmic work of each stage per launch: (bound, amount, unit)."""
+    rows = w.batch * w.heads_kv * w.seqlen_q
+    edges = w.batch * w.heads_kv * float(np.minimum(positions(w) // w.block_size + 1, w.topk).sum())
+    G = w.group
+    return {
+        "index_scores": ("mfma", index_flops(w), "FLOP"),
+        "block_topk": ("hbm", rows * (w.n_blk + w.topk) * 4.0, "B"),
+        "attn_build": ("hbm", (rows * w.topk * 4.0 * 2 + edges * 4.0) / chunks, "B"),
+        "attn_partial": ("mfma", attn_flops(w) / chunks, "FLOP"),
+        "attn_merge": ("hbm", (edges * G * (2 * w.head_dim + 8) + rows * G * w.head_dim * 2.0) / chunks, "B"),
     }
-    return t, ms, wall, per
+
+
+def roofline(w, stage_ms, chunks):
+    work = stage_work(w, chunks)
+    dom = max(stage_ms, key=stage_ms.get)
+    bound, amount, _ = work[dom]
+    per_launch_ms = stage_ms[dom] / chunks
+    if bound == "mfma":
+        ach = amount / (per_launch_ms * 1e-3) / 1e12
+        r = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        ach = amount / (per_launch_ms * 1e-3) / 1e9
+        r = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    r.update(frac=r["achieved"] / r["peak"], traffic=None, kernel=KERNEL_OF_STAGE[dom],
+             launches_per_step=chunks, avg_launch_ms=per_launch_ms)
+    return r
+
+
+KERNEL_OF_STAGE = {
+    "index_scores": "index_scan_prefill (index_scan_decode when S_q * H_kv <= 32)",
+    "block_topk": "block_topk_kernel",
+    "attn_build": "zero/bucket_count/scan/bucket_fill kernels",
+    "attn_partial": "attn_partial_kernel<G>",
+    "attn_merge": "merge_kernel<G>",
+}
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -176,27 +219,18 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     print(f"[bench] workload {w.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
-    t, ms, wall, per = run_workload(w, args.steps, args.warmup)
+    t, ms, wall, stage_ms, chunks = run_workload(w, args.steps, args.warmup)
     fi, fa = index_flops(w), attn_flops(w)
     tokens = w.batch * w.seqlen_q
     tflops = (fi + fa) / (ms * 1e-3) / 1e12
-    kernels = {
-        "msa_index_scores": {"ms": per["msa_index_scores"], "tflops": fi / (per["msa_index_scores"] * 1e-3) / 1e12},
-        "msa_block_topk": {"ms": per["msa_block_topk"]},
-        "msa_sparse_attn_fwd": {"ms": per["msa_sparse_attn_fwd"],
-                                "tflops": fa / (per["msa_sparse_attn_fwd"] * 1e-3) / 1e12},
-    }
-    dom = max(kernels, key=lambda k: kernels[k]["ms"])
-    if dom == "msa_block_topk":
-        nbytes = w.batch * w.heads_kv * w.seqlen_q * (w.n_blk * 4 + w.topk * 4)
-        ach = nbytes / (per[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": ach / PEAK_HBM_GBS, "traffic": None, "step": dom}
-    else:
-        ach = kernels[dom]["tflops"]
-        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "step": dom}
-    print(f"[bench] {ms:.3f} ms/step; per entry {json.dumps(per)}", file=sys.stderr, flush=True)
+    roof = roofline(w, stage_ms, chunks)
+    stages = {}
+    for name, (bound, amount, unit) in stage_work(w, chunks).items():
+        per = stage_ms[name] / chunks
+        rate = amount / (per * 1e-3)
+        stages[name] = {"ms_per_step": stage_ms[name], "bound": bound,
+                        ("TFLOP/s" if unit == "FLOP" else "GB/s"): rate / (1e12 if unit == "FLOP" else 1e9)}
+    print(f"[bench] {ms:.3f} ms/step; stages {json.dumps(stage_ms)}", file=sys.stderr, flush=True)
 
     res = {
         "metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -208,7 +242,7 @@ def main():
                    "parallelism": "single GPU"},
         "tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
         "algorithmic_flops": {"index": fi, "attention": fa},
-        "kernels": kernels, "roofline": roof, "wall_s_timed": wall,
+        "stages": stages, "attn_chunks": chunks, "roofline": roof, "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
@@ -218,13 +252,13 @@ def main():
     if not args.no_decode:
         wd = synth.WORKLOADS["decode_64x256k"]
         print(f"[bench] decode workload {wd.name}", file=sys.stderr, flush=True)
-        td, msd, _, perd = run_workload(wd, args.steps, args.warmup)
+        td, msd, _, stage_d, chunks_d = run_workload(wd, args.steps, args.warmup)
         nbytes = decode_bytes(wd)
         gbs = nbytes / (msd * 1e-3) / 1e9
         res["decode"] = {"workload": wd.name, "ms_per_step": msd, "algorithmic_bytes": nbytes,
                          "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
                          "tokens/s": wd.batch * wd.seqlen_q / (msd * 1e-3),
-                         "kernels_ms": perd}
+                         "stages_ms": stage_d, "roofline": roofline(wd, stage_d, chunks_d)}
         del td
     print(json.dumps(res), flush=True)
 

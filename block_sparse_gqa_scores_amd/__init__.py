@@ -20,7 +20,8 @@ STATUS_NAMES = {0: "MSA_OK", 1: "MSA_ERR_NULL_PTR", 2: "MSA_ERR_INVALID_DIMS", 3
                 4: "MSA_ERR_MISALIGNED", 5: "MSA_ERR_WORKSPACE_TOO_SMALL", 6: "MSA_ERR_HIP"}
 ENTRY_INDEX_SCORES, ENTRY_BLOCK_TOPK, ENTRY_SPARSE_ATTN_FWD, ENTRY_FORWARD = 0, 1, 2, 3
 EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
-            "msa_workspace_bytes", "msa_status_str")
+            "msa_forward_profiled", "msa_attn_chunks", "msa_workspace_bytes", "msa_status_str")
+STAGES = ("index_scores", "block_topk", "attn_build", "attn_partial", "attn_merge")
 
 
 class MsaError(RuntimeError):
@@ -63,8 +64,13 @@ def lib():
         L.msa_block_topk.argtypes = [D, P, P, P]
         L.msa_sparse_attn_fwd.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_forward.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        for f in (L.msa_index_scores, L.msa_block_topk, L.msa_sparse_attn_fwd, L.msa_forward):
+        L.msa_forward_profiled.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
+                                           ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+        for f in (L.msa_index_scores, L.msa_block_topk, L.msa_sparse_attn_fwd, L.msa_forward,
+                  L.msa_forward_profiled):
             f.restype = ctypes.c_int
+        L.msa_attn_chunks.argtypes = [D]
+        L.msa_attn_chunks.restype = ctypes.c_int
         L.msa_workspace_bytes.argtypes = [D, ctypes.c_int]
         L.msa_workspace_bytes.restype = ctypes.c_size_t
         L.msa_status_str.argtypes = [ctypes.c_int]
@@ -173,8 +179,13 @@ def msa_sparse_attn_fwd(q, k, v, block_idx, *, block_size=128, softmax_scale=0.0
     return (out, lse) if return_lse else out
 
 
+def msa_attn_chunks(dims: Dims) -> int:
+    """Query chunks the attention stages run in for these dims."""
+    return lib().msa_attn_chunks(ctypes.byref(dims))
+
+
 def msa_forward(q, k, v, q_idx, k_idx, *, topk=16, block_size=128, softmax_scale=0.0, out=None,
-                return_lse=False, return_idx=False, workspace=None):
+                return_lse=False, return_idx=False, workspace=None, stage_events=None):
     """Index scores -> Top-k -> sparse attention.  Returns out, plus lse and
     block_idx when asked."""
     import torch
@@ -188,9 +199,16 @@ def msa_forward(q, k, v, q_idx, k_idx, *, topk=16, block_size=128, softmax_scale
     idx = torch.empty((d.batch, d.num_heads_kv, d.seqlen_q, topk), dtype=torch.int32, device=q.device) \
         if return_idx else None
     ws, nbytes = _workspace(d, ENTRY_FORWARD, workspace, q.device)
-    rc = lib().msa_forward(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx),
-                           _ptr(out), _ptr(lse), _ptr(idx), _ptr(ws), nbytes, _stream(q.device))
-    _check(rc, "msa_forward")
+    args = (ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx), _ptr(out), _ptr(lse),
+            _ptr(idx), _ptr(ws), nbytes, _stream(q.device))
+    if stage_events is None:
+        rc = lib().msa_forward(*args)
+        _check(rc, "msa_forward")
+    else:
+        # stage_events: 2 * len(STAGES) raw hipEvent_t handles (msa_forward_profiled).
+        arr = (ctypes.c_void_p * len(stage_events))(*stage_events)
+        rc = lib().msa_forward_profiled(*args, arr, len(stage_events))
+        _check(rc, "msa_forward_profiled")
     res = [out]
     if return_lse:
         res.append(lse)

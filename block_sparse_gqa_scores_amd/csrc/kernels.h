@@ -24,8 +24,16 @@ struct AttnShape {
   float scale;       // softmax scale
 };
 size_t sparse_attn_workspace(const AttnShape& s);
+int sparse_attn_chunks(const AttnShape& s);
+
+// Optional stage events: ev[2 s] before the first launch of stage s,
+// ev[2 s + 1] after its last launch (stages 2, 3, 4 of msa_stage here).
+struct StageEvents {
+  hipEvent_t ev[10];
+};
 hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int32_t* idx, uint16_t* out, float* lse,
-                              void* ws, size_t ws_bytes, hipStream_t stream);
+                              void* ws, size_t ws_bytes, hipStream_t stream,
+                              const StageEvents* events = nullptr);
 
 }  // namespace msa

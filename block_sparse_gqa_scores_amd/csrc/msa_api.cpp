@@ -156,9 +156,12 @@ msa_status msa_sparse_attn_fwd(const msa_dims* d, const void* q, const void* k, 
       static_cast<hipStream_t>(stream)));
 }
 
-msa_status msa_forward(const msa_dims* d, const void* q, const void* k, const void* v,
-                       const void* q_idx, const void* k_idx, void* out, float* lse,
-                       int32_t* block_idx_out, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+msa_status forward_impl(const msa_dims* d, const void* q, const void* k, const void* v,
+                        const void* q_idx, const void* k_idx, void* out, float* lse,
+                        int32_t* block_idx_out, void* ws, size_t ws_bytes, void* stream,
+                        const msa::StageEvents* ev) {
   msa_status st = check_dims(d, true, true);
   if (st != MSA_OK || is_empty(*d)) return st;
   if (!q || !k || !v || !q_idx || !k_idx || !out) return MSA_ERR_NULL_PTR;
@@ -177,18 +180,51 @@ msa_status msa_forward(const msa_dims* d, const void* q, const void* k, const vo
   int32_t* idx = block_idx_out ? block_idx_out : reinterpret_cast<int32_t*>(base + bm_sz);
   void* attn_ws = base + bm_sz + idx_sz;
   hipStream_t strm = static_cast<hipStream_t>(stream);
+  if (ev) hipEventRecord(ev->ev[2 * MSA_STAGE_INDEX_SCORES], strm);
   hipError_t e = msa::launch_index_scores(static_cast<const uint16_t*>(q_idx),
                                           static_cast<const uint16_t*>(k_idx), bm, d->batch,
                                           d->seqlen_q, d->seqlen_k, d->num_heads_kv, d->index_dim,
                                           s.n_blk, strm);
   if (e != hipSuccess) return MSA_ERR_HIP;
+  if (ev) hipEventRecord(ev->ev[2 * MSA_STAGE_INDEX_SCORES + 1], strm);
+  if (ev) hipEventRecord(ev->ev[2 * MSA_STAGE_BLOCK_TOPK], strm);
   e = msa::launch_block_topk(bm, idx, d->batch, d->seqlen_q, d->seqlen_k, d->num_heads_kv,
                              s.n_blk, d->topk, strm);
   if (e != hipSuccess) return MSA_ERR_HIP;
+  if (ev) hipEventRecord(ev->ev[2 * MSA_STAGE_BLOCK_TOPK + 1], strm);
   e = msa::launch_sparse_attn(s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                               static_cast<const uint16_t*>(v), idx, static_cast<uint16_t*>(out),
-                              lse, attn_ws, attn_sz, strm);
+                              lse, attn_ws, attn_sz, strm, ev);
   return from_hip(e);
+}
+
+}  // namespace
+
+msa_status msa_forward(const msa_dims* d, const void* q, const void* k, const void* v,
+                       const void* q_idx, const void* k_idx, void* out, float* lse,
+                       int32_t* block_idx_out, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(d, q, k, v, q_idx, k_idx, out, lse, block_idx_out, ws, ws_bytes, stream,
+                      nullptr);
+}
+
+msa_status msa_forward_profiled(const msa_dims* d, const void* q, const void* k, const void* v,
+                                const void* q_idx, const void* k_idx, void* out, float* lse,
+                                int32_t* block_idx_out, void* ws, size_t ws_bytes, void* stream,
+                                void* const* events, int n_events) {
+  if (!events) return MSA_ERR_NULL_PTR;
+  if (n_events < 2 * MSA_N_STAGES) return MSA_ERR_INVALID_DIMS;
+  msa::StageEvents ev;
+  for (int x = 0; x < 2 * MSA_N_STAGES; ++x) {
+    if (!events[x]) return MSA_ERR_NULL_PTR;
+    ev.ev[x] = static_cast<hipEvent_t>(events[x]);
+  }
+  return forward_impl(d, q, k, v, q_idx, k_idx, out, lse, block_idx_out, ws, ws_bytes, stream, &ev);
+}
+
+int msa_attn_chunks(const msa_dims* d) {
+  if (check_dims(d, false, true) != MSA_OK) return 0;
+  if (is_empty(*d)) return 0;
+  return msa::sparse_attn_chunks(attn_shape(*d));
 }
 
 }  // extern "C"

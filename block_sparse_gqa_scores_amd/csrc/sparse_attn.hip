@@ -34,7 +34,7 @@ constexpr int kBlock = 128;     // keys per block
 constexpr int kSubTiles = 4;    // 4-wave sub-tiles per work item
 constexpr int kScanPerWg = 1024;
 constexpr int kVStride = kBlock + 4;  // bf16 per row of the transposed V tile
-constexpr size_t kPartBudget = size_t(4) << 30;  // bytes of partials per chunk
+constexpr size_t kPartBudget = size_t(16) << 30;  // bytes of partials per chunk
 constexpr int kBuildQueries = 256;   // queries per bucket-build workgroup
 constexpr int kHistBins = 8192;      // widest row whose histogram lives in LDS
 constexpr int kMaxQT = kSubTiles * 4 * 32;  // edges per work item at G = 1
@@ -563,10 +563,22 @@ int grid_cap(long n, int per) {
 
 size_t sparse_attn_workspace(const AttnShape& s) { return make_layout(s).total; }
 
+int sparse_attn_chunks(const AttnShape& s) {
+  const Layout L = make_layout(s);
+  return (s.S_q + L.Qc - 1) / L.Qc;
+}
+
 template <int G>
-static hipError_t launch_g(const AttnShape& s, const Layout& L, Params p, bool with_lse, hipStream_t st) {
+static hipError_t launch_g(const AttnShape& s, const Layout& L, Params p, bool with_lse, hipStream_t st,
+                           const StageEvents* ev) {
+  // Stage s of msa_stage: 2 = build, 3 = partial, 4 = merge.
+  auto mark = [&](int stage, bool after, bool first, bool last) {
+    if (ev && ((!after && first) || (after && last))) hipEventRecord(ev->ev[2 * stage + (after ? 1 : 0)], st);
+  };
   for (int q0 = 0; q0 < s.S_q; q0 += L.Qc) {
     p.q0 = q0;
+    const bool first = q0 == 0, last = q0 + L.Qc >= s.S_q;
+    mark(2, false, first, last);
     const long slots = (long)s.batch * s.H_kv * L.Qc * s.topk;
     hipLaunchKernelGGL(zero_kernel, dim3(grid_cap(L.NB, 256)), dim3(256), 0, st, p.counts, L.NB);
     hipLaunchKernelGGL(zero_kernel, dim3(grid_cap(L.NB, 256)), dim3(256), 0, st, p.cursor, L.NB);
@@ -583,10 +595,15 @@ static hipError_t launch_g(const AttnShape& s, const Layout& L, Params p, bool w
       hipLaunchKernelGGL(bucket_fill_kernel, dim3((unsigned)build_grid), dim3(256), s.n_blk * 8, st, p);
     else
       hipLaunchKernelGGL(fill_kernel, dim3(grid_cap(slots, 256)), dim3(256), 0, st, p);
+    mark(2, true, first, last);
+    mark(3, false, first, last);
     hipLaunchKernelGGL(attn_partial_kernel<G>, dim3((unsigned)L.T), dim3(kThreads), 0, st, p);
+    mark(3, true, first, last);
     const long rows = (long)s.batch * s.H_kv * L.Qc;
+    mark(4, false, first, last);
     hipLaunchKernelGGL(merge_kernel<G>, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, st, p,
                        with_lse ? 1 : 0);
+    mark(4, true, first, last);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -595,7 +612,8 @@ static hipError_t launch_g(const AttnShape& s, const Layout& L, Params p, bool w
 
 hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int32_t* idx, uint16_t* out, float* lse,
-                              void* ws, size_t ws_bytes, hipStream_t stream) {
+                              void* ws, size_t ws_bytes, hipStream_t stream,
+                              const StageEvents* events) {
   const Layout L = make_layout(s);
   if (ws_bytes < L.total) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
@@ -616,12 +634,12 @@ hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint1
   p.part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
   const bool with_lse = lse != nullptr;
   switch (p.G) {
-    case 1: return launch_g<1>(s, L, p, with_lse, stream);
-    case 2: return launch_g<2>(s, L, p, with_lse, stream);
-    case 4: return launch_g<4>(s, L, p, with_lse, stream);
-    case 8: return launch_g<8>(s, L, p, with_lse, stream);
-    case 16: return launch_g<16>(s, L, p, with_lse, stream);
-    case 32: return launch_g<32>(s, L, p, with_lse, stream);
+    case 1: return launch_g<1>(s, L, p, with_lse, stream, events);
+    case 2: return launch_g<2>(s, L, p, with_lse, stream, events);
+    case 4: return launch_g<4>(s, L, p, with_lse, stream, events);
+    case 8: return launch_g<8>(s, L, p, with_lse, stream, events);
+    case 16: return launch_g<16>(s, L, p, with_lse, stream, events);
+    case 32: return launch_g<32>(s, L, p, with_lse, stream, events);
     default: return hipErrorInvalidValue;
   }
 }

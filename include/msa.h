@@ -165,6 +165,39 @@ msa_status msa_forward(const msa_dims* dims, const void* q, const void* k,
                        void* out, float* lse, int32_t* block_idx_out, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* Internal stages of msa_forward, in launch order (for msa_forward_profiled). */
+typedef enum msa_stage {
+  MSA_STAGE_INDEX_SCORES = 0,  /* index scores fused with the block max-pool */
+  MSA_STAGE_BLOCK_TOPK = 1,    /* exp-free Top-k */
+  MSA_STAGE_ATTN_BUILD = 2,    /* edges grouped by (batch, group, block) */
+  MSA_STAGE_ATTN_PARTIAL = 3,  /* attention of each edge over its block */
+  MSA_STAGE_ATTN_MERGE = 4,    /* per-query merge of the partial results */
+  MSA_N_STAGES = 5
+} msa_stage;
+
+/*
+ * msa_forward with timing instrumentation, for profilers and benchmarks (the
+ * tracing hooks of the forward path; same arguments, same results).  `events`
+ * holds 2 * MSA_N_STAGES caller-created hipEvent_t handles: events[2 s] is
+ * recorded on `stream` before the first launch of stage s and events[2 s + 1]
+ * after its last launch.  When the attention runs in several query chunks
+ * (see msa_attn_chunks), each stage is launched once per chunk and the pair
+ * spans all of them.  Returns MSA_ERR_NULL_PTR if events is NULL or holds a
+ * NULL handle, MSA_ERR_INVALID_DIMS if n_events < 2 * MSA_N_STAGES.
+ */
+msa_status msa_forward_profiled(const msa_dims* dims, const void* q, const void* k,
+                                const void* v, const void* q_idx, const void* k_idx,
+                                void* out, float* lse, int32_t* block_idx_out,
+                                void* ws, size_t ws_bytes, void* stream,
+                                void* const* events, int n_events);
+
+/*
+ * Number of query chunks the attention stages run in for these dims (the
+ * per-edge partial results of one chunk must fit the workspace budget of at
+ * most 16 GiB); 0 for invalid dims.
+ */
+int msa_attn_chunks(const msa_dims* dims);
+
 /*
  * Bytes of caller-provided workspace the given entry point needs for these
  * dims (0 for entries that need none).  Returns (size_t)-1 when the dims are

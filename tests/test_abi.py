@@ -126,3 +126,25 @@ def test_status_strings():
     for code, name in msa.STATUS_NAMES.items():
         assert msa.msa_status_str(code) == name
     assert msa.msa_status_str(99) == "MSA_ERR_UNKNOWN"
+
+
+def test_profiled_entry_rejects_bad_events():
+    d = dims()
+    L = msa.lib()
+    ev = (ctypes.c_void_p * 10)(*([0x20000] * 10))
+    args = (ctypes.byref(d), A, A, A, A, A, A, NULL, NULL, A, 1 << 40, None)
+    assert L.msa_forward_profiled(*args, None, 10) == 1
+    assert L.msa_forward_profiled(*args, ev, 9) == 2
+    holes = (ctypes.c_void_p * 10)(*([0x20000] * 9 + [0]))
+    assert L.msa_forward_profiled(*args, holes, 10) == 1
+    bad = dims(causal=0)
+    assert L.msa_forward_profiled(ctypes.byref(bad), *args[1:], ev, 10) == 3
+
+
+def test_attn_chunks():
+    assert msa.msa_attn_chunks(dims()) == 1
+    assert msa.msa_attn_chunks(dims(causal=0)) == 0
+    assert msa.msa_attn_chunks(dims(batch=0)) == 0
+    # partials of 131072 queries x 8 groups x 16 blocks exceed one chunk's budget
+    big = dims(seqlen_q=131072, seqlen_k=131072, num_heads_q=64, num_heads_kv=8)
+    assert msa.msa_attn_chunks(big) >= 2

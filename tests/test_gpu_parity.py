@@ -159,3 +159,20 @@ def test_deterministic():
 def test_empty_problem_launches_nothing():
     d = msa.Dims.make(0, 0, 0, 8, 2)
     assert msa.lib().msa_forward(d, None, None, None, None, None, None, None, None, None, 0, None) == 0
+
+
+def test_profiled_forward_matches_forward():
+    """msa_forward_profiled only adds event records: identical results."""
+    w = W("profiled", 1, 700, 3000, 16, 2, topk=8)
+    t = inputs_for(w)
+    a = run_device(w, t)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(msa.STAGES))]
+    for e in evs:
+        e.record()
+    out, lse, idx = msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=8,
+                                    return_lse=True, return_idx=True,
+                                    stage_events=[e.cuda_event for e in evs])
+    torch.cuda.synchronize()
+    assert torch.equal(out, a["out"]) and torch.equal(lse, a["lse"]) and torch.equal(idx, a["idx"])
+    for s in range(len(msa.STAGES)):
+        assert evs[2 * s].elapsed_time(evs[2 * s + 1]) >= 0.0
