@@ -123,8 +123,11 @@ def stage_work(w, chunks):
     rows = w.batch * w.heads_kv * w.seqlen_q
     edges = w.batch * w.heads_kv * float(np.minimum(positions(w) // w.block_size + 1, w.topk).sum())
     G = w.group
+    index = ("mfma", index_flops(w), "FLOP")
+    if w.seqlen_q * w.heads_kv <= 32:  # decode: the index-key cache stream bounds the scan
+        index = ("hbm", w.batch * (w.seqlen_k * w.index_dim * 2.0 + rows / w.batch * (w.index_dim * 2.0 + w.n_blk * 4.0)), "B")
     return {
-        "index_scores": ("mfma", index_flops(w), "FLOP"),
+        "index_scores": index,
         "block_topk": ("hbm", rows * (w.n_blk + w.topk) * 4.0, "B"),
         "attn_build": ("hbm", (rows * w.topk * 4.0 * 2 + edges * 4.0) / chunks, "B"),
         "attn_partial": ("mfma", attn_flops(w) / chunks, "FLOP"),
@@ -143,9 +146,37 @@ def roofline(w, stage_ms, chunks):
     else:
         ach = amount / (per_launch_ms * 1e-3) / 1e9
         r = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    r.update(frac=r["achieved"] / r["peak"], traffic=None, kernel=KERNEL_OF_STAGE[dom],
-             launches_per_step=chunks, avg_launch_ms=per_launch_ms)
+    r.update(frac=r["achieved"] / r["peak"], traffic=measured_traffic(w, dom),
+             kernel=KERNEL_OF_STAGE[dom], launches_per_step=chunks, avg_launch_ms=per_launch_ms)
     return r
+
+
+TRAFFIC_FILES = {("prefill_32k", "attn_partial"): ("attn_partial_prefill_32k_traffic.txt",
+                                                   ("sparse_attn.hip", "device_common.h"))}
+
+
+def measured_traffic(w, stage):
+    """HBM bytes per launch from the committed counter summary of this kernel
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel calibration), or
+    None when there is none or the kernel's source changed since."""
+    import hashlib
+
+    key = TRAFFIC_FILES.get((w.name, stage))
+    if key is None:
+        return None
+    path = os.path.join(ROOT, "profiles", key[0])
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    csrc = os.path.join(ROOT, "block_sparse_gqa_scores_amd", "csrc")
+    digest = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in key[1])).hexdigest()
+    if digest != fields.get("source_sha256"):
+        return None
+    return float(fields["hbm_bytes_per_launch"])
 
 
 KERNEL_OF_STAGE = {
@@ -207,6 +238,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="run one plain device copy of this many bytes first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -218,6 +251,8 @@ def main():
     import synth
 
     w = synth.WORKLOADS[args.workload]
+    if args.copy_probe:
+        synth.copy_probe(args.copy_probe)
     print(f"[bench] workload {w.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
     t, ms, wall, stage_ms, chunks = run_workload(w, args.steps, args.warmup)
     fi, fa = index_flops(w), attn_flops(w)

@@ -191,8 +191,25 @@ def _load():
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32,
                            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        lib.synth_copy_bytes.restype = ctypes.c_int
+        lib.synth_copy_bytes.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         _lib = lib
     return _lib
+
+
+def copy_probe(nbytes: int, device="cuda") -> None:
+    """Run one plain device copy of ``nbytes`` (reads and writes exactly that
+    many bytes): the known-size reference for traffic counters."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(src.device).cuda_stream
+    rc = _load().synth_copy_bytes(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                  nbytes, ctypes.c_void_p(stream))
+    if rc != 0:
+        raise RuntimeError(f"copy probe failed ({rc})")
+    torch.cuda.synchronize()
 
 
 def fill_device(w: Workload, name: str, tensor) -> None:

@@ -93,6 +93,14 @@ __global__ void fill_int_kernel(uint16_t* __restrict__ dst, int64_t n,
   }
 }
 
+// Plain copy of n16 16-byte words (a known-size memory stream used to
+// calibrate hardware traffic counters).
+__global__ void copy16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t n16) {
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n16; e += stride)
+    dst[e] = src[e];
+}
+
 int grid_for(int64_t n) {
   int64_t g = (n + 255) / 256;
   if (g > 65536) g = 65536;
@@ -132,6 +140,16 @@ int synth_fill_int_bf16(void* dst, int64_t n, uint64_t seed, uint32_t tensor_id,
   hipLaunchKernelGGL(fill_int_kernel, dim3(grid_for(n)), dim3(256), 0,
                      (hipStream_t)stream, (uint16_t*)dst, n, seed, tensor_id,
                      geo);
+  return (int)hipGetLastError();
+}
+
+// Copy `bytes` (a multiple of 16) from src to dst on `stream`: a plain
+// streaming kernel that reads and writes exactly `bytes` each.
+int synth_copy_bytes(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes <= 0 || (bytes & 15)) return bytes == 0 ? 0 : -1;
+  const int64_t n16 = bytes / 16;
+  hipLaunchKernelGGL(copy16_kernel, dim3(grid_for(n16)), dim3(256), 0, (hipStream_t)stream,
+                     (const uint4*)src, (uint4*)dst, n16);
   return (int)hipGetLastError();
 }
 
