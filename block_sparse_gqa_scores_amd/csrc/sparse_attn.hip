@@ -9,7 +9,7 @@
 // (query, group).  Here the edges (query i, group g, selected block j) are
 // bucketed by (b, g, j) instead: one workgroup loads K_j and V_j of group g
 // into LDS once and runs every query of its bucket against them, all G heads
-// of a query sharing the load (section 3.2: regular blocks let the group's
+// of a query sharing the load (section 3.2: fixed-size blocks allow the group's
 // heads share KV loads).  Each edge leaves a partial result: the output
 // normalised over the block's visible keys and its log-sum-exp.  A merge
 // kernel then combines each query's partials, which is exactly the softmax

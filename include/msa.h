@@ -88,7 +88,8 @@ typedef enum msa_entry {
 
 /*
  * Index branch, scoring step (section 3.2 of Sparse Attention Part II: the
- * index query scores the visible tokens against the shared index key head and
+ * index query is dotted with the one index key all groups share, over the
+ * causally visible keys, and
  * each block is scored by its maximum token score; section 4.4 of the same
  * page for keeping the token scores off HBM).
  *
@@ -112,7 +113,7 @@ msa_status msa_index_scores(const msa_dims* dims, const void* q_idx,
  * of the k slots is reserved for the query's local block and the indexer
  * picks the others; the MiniMax Sparse Attention blog: the Top-k works on raw
  * scores, with no exponential; section 4.2 of Sparse Attention Part II: exact
- * top-k needs one consistent rule for ties).
+ * top-k must break equal scores in one fixed way).
  *
  *   Sel_i = { l_i } united with the (topk - 1) best blocks among 0 .. l_i - 1,
  *           ranked by block score (higher first) and, on equal scores, by

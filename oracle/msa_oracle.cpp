@@ -6,16 +6,16 @@
 // It restates the method from its description, one step at a time, in fp64:
 //
 //   Sparse Attention Part II (mtreviso.github.io), section 3.2 "MiniMax's MSA":
-//     per query and GQA group, an index query scores the visible tokens
-//     against one shared index key head; a block's score is the maximum token
-//     score inside it; Top-k keeps 16 blocks of 128 tokens per group, one slot
-//     reserved for the query's own block, the indexer choosing the rest; every
-//     query head of the group then attends to the causally visible tokens of
-//     the kept blocks with its own weights.
+//     for each query and group, the index query is dotted with the single
+//     index key that all groups share, over causally visible keys; a block's
+//     score is the largest token score inside it; Top-k keeps 16 blocks of 128
+//     tokens per group, the block holding the query always among them and the
+//     other 15 picked by score; each query head of the group then runs its own
+//     attention over the causally visible tokens of those blocks.
 //   Same page, section 2: sparse-trained models normalise the softmax inside
 //     the selection; exactness means reproducing that operator.
 //   Same page, section 4.1: P = softmax(Q K^T / sqrt(d)), O = P V.
-//   Same page, section 4.2: exact top-k needs a consistent rule for ties
+//   Same page, section 4.2: an exact top-k must break equal scores one fixed way
 //     (here: higher score first, then lower block index).
 //   MiniMax Sparse Attention (api.staik.se blog): the Top-k selects on raw
 //     scores (exp-free), per GQA group.

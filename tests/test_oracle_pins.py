@@ -137,7 +137,7 @@ def test_select_all_equal_scores_keeps_lowest_indices(oracle_mod):
 
 def test_select_local_block_never_competes(oracle_mod):
     """The local block's own score, high or low, does not change which
-    earlier blocks are chosen (section 3.2: one slot is reserved for it)."""
+    earlier blocks are chosen (section 3.2: the local block has a slot of its own)."""
     p = oracle.Problem(1, 64, 64, 1, 1, 8, 8, block_size=4, topk=4)
     rng = np.random.default_rng(4)
     bm = rng.normal(size=(64, 16))
@@ -153,7 +153,7 @@ def test_select_local_block_never_competes(oracle_mod):
 
 def test_select_invariants_on_a_workload_shape(oracle_mod):
     """Local block kept; count = min(k, l+1); ascending, unique; at most
-    k * block_size tokens (section 3.2: at most 2048 tokens per query and group)."""
+    k * block_size tokens (section 3.2: 16 blocks of 128 cap the tokens per query and group)."""
     w = synth.WORKLOADS["prefill_4k"].with_(seqlen_q=512, seqlen_k=2304)
     p = oracle.Problem.of(w)
     rows = p.all_rows()[::7]
