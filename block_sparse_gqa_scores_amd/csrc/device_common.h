@@ -62,6 +62,13 @@ __device__ __forceinline__ float max16(float m, const f32x16& x) {
   return max3f(max3f(a, b, c), max3f(d, e, x[15]), m);
 }
 
+// max(|a|, |b|, c) in one v_max3_f32 with abs source modifiers.
+__device__ __forceinline__ float max3abs(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z = {};
   return z;
@@ -72,18 +79,22 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest-even bf16, packed low|high
+// (one v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  // round-to-nearest-even of two fp32 values to bf16, packed low|high
-  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-  a += 0x7FFFu + ((a >> 16) & 1u);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return (a >> 16) | (b & 0xFFFF0000u);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// Two fp32 values rounded to nearest-even fp16, packed low|high
+// (one v_cvt_pk_f16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  // round-to-nearest-even of two fp32 values to fp16, packed low|high
-  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 __device__ __forceinline__ float f16_lo(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));

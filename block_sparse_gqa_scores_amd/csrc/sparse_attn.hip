@@ -31,13 +31,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kD = 128;         // head dim
 constexpr int kBlock = 128;     // keys per block
-constexpr int kSubTiles = 4;    // 4-wave sub-tiles per work item
+constexpr int kSubTiles = 16;   // 4-wave sub-tiles per work item
 constexpr int kScanPerWg = 1024;
 constexpr int kVStride = kBlock + 4;  // bf16 per row of the transposed V tile
 constexpr size_t kPartBudget = size_t(16) << 30;  // bytes of partials per chunk
 constexpr int kBuildQueries = 256;   // queries per bucket-build workgroup
 constexpr int kHistBins = 8192;      // widest row whose histogram lives in LDS
-constexpr int kMaxQT = kSubTiles * 4 * 32;  // edges per work item at G = 1
 
 struct Params {
   const uint16_t* q;
@@ -60,8 +59,20 @@ struct Params {
   int2* work;            // (bucket, first edge in bucket)
   float* part_lse;       // [slot][G]: log2-sum-exp of the block's visible logits
   float* part_sc;        // [slot][G]: max |O_e| of the row
-  uint16_t* part_o;      // [slot][G][D] fp16: O_e / max |O_e|, O_e normalised per block
+  uint16_t* part_o;      // [slot][G * D] fp16: O_e / max |O_e|, in record order (below)
 };
+
+// Record order of one slot's G x D partial outputs.  The MFMA output puts
+// O[hh][d] of a query in lane (row hh, half h) at register 4 * rq + c of tile
+// dt, with d = 32 dt + 8 rq + 4 h + c.  Unit u (4 fp16, 8 bytes) holds
+// c = 0..3 of (dt, rq, hh, h) at u = ((dt * 4 + rq) * G + hh) * 2 + h, so the
+// 2 G lanes of one query write 16 G contiguous bytes per store instruction
+// (a full 128-byte line at G = 8).  Two consecutive units are the 8
+// consecutive d = 32 dt + 8 rq + 0..7 of head hh.
+template <int G>
+__device__ __forceinline__ int record_unit(int dt, int rq, int hh, int h) {
+  return ((dt * 4 + rq) * G + hh) * 2 + h;
+}
 
 // Slot of edge (b, g, il, e) inside the chunk.
 __device__ __forceinline__ long slot_of(const Params& p, int bg, int il, int e) {
@@ -275,9 +286,10 @@ __global__ void fill_kernel(Params p) {
 template <int G>
 __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
   constexpr int QW = 32 / G;  // queries per wave (32 MFMA rows = QW queries x G heads)
+  constexpr int QT = kSubTiles * 4 * QW;               // edges per work item
   __shared__ u32x4 ktile[kBlock * 16];                 // [key][16 chunks], swizzled
   __shared__ uint32_t vt[kD * kVStride / 2];           // [d][key] bf16, padded rows
-  __shared__ int32_t s_slot[kMaxQT];                   // this item's edge slots
+  __shared__ int32_t s_slot[QT];                       // this item's edge slots
 
   const int w = blockIdx.x;
   if (w >= p.tile_off[p.NB]) return;  // uniform: past the last work item
@@ -366,26 +378,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
 #pragma unroll
       for (int ks = 1; ks < 8; ++ks) sacc[mt] = mfma32x32x16(ka[ks], qb[ks], sacc[mt]);
     }
-    const bool need_mask = __builtin_amdgcn_ballot_w64(j * kBlock + kBlock - 1 > t) != 0;
+    // Causal mask only where the block reaches past some row's position (the
+    // query's own block); raw scores are ranked, the scale is applied inside
+    // the exponent: p = 2^(s * c - m * c) with c = scale * log2(e).
+    if (__builtin_amdgcn_ballot_w64(j * kBlock + kBlock - 1 > t) != 0) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (j * kBlock + mt * 32 + mfma32_row(r, lane) > t) sacc[mt][r] = neg_inf();
+    }
     float mx = neg_inf();
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[mt][r] * p.scale_log2;
-        if (need_mask && j * kBlock + mt * 32 + mfma32_row(r, lane) > t) x = neg_inf();
-        sacc[mt][r] = x;
-      }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) mx = max16(mx, sacc[mt]);
     mx = __builtin_fmaxf(mx, swap_halves(mx));
+    const float c = p.scale_log2;
+    const float bias = -mx * c;
     float l = 0.f;
     u32x4 pb[4][2];  // P in bf16, packed as the B operand of O^T = V^T P^T
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e2 = __builtin_amdgcn_exp2f(sacc[mt][r] - mx);
+        const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][r], c, bias));
         sacc[mt][r] = e2;
         l += e2;
       }
@@ -419,11 +434,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) amax = __builtin_fmaxf(amax, __builtin_fabsf(oacc[dt][r]));
+      for (int r = 0; r < 16; r += 2) amax = max3abs(oacc[dt][r], oacc[dt][r + 1], amax);
     amax = __builtin_fmaxf(amax, swap_halves(amax));
     {
       const float inv = amax > 0.f ? 1.f / amax : 0.f;
-      uint16_t* po = p.part_o + ((size_t)slot * G + hh) * kD;
+      uint2* po = reinterpret_cast<uint2*>(p.part_o + (size_t)slot * G * kD);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -431,10 +446,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
           uint2 v2;
           v2.x = pack_f16x2(oacc[dt][4 * rq + 0] * inv, oacc[dt][4 * rq + 1] * inv);
           v2.y = pack_f16x2(oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
-          *reinterpret_cast<uint2*>(po + dt * 32 + 8 * rq + 4 * h) = v2;
+          po[record_unit<G>(dt, rq, hh, h)] = v2;
         }
       // Both wave halves hold the same row statistics; both store them.
-      p.part_lse[(size_t)slot * G + hh] = mx + __builtin_amdgcn_logf(l);
+      p.part_lse[(size_t)slot * G + hh] = mx * c + __builtin_amdgcn_logf(l);
       p.part_sc[(size_t)slot * G + hh] = amax / l;
     }
     asm volatile("" ::: "memory");
@@ -447,6 +462,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
 
 // Combines the partials of each (query, group): one wave per row.
 // O = sum_e 2^(lse_e - M) sc_e x_e / sum_e 2^(lse_e - M), LSE = M + log2(sum).
+// Every record shares one element order, so the sums run in record order and
+// the order is undone once, when O is written.
 template <int G>
 __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse) {
   constexpr int NF = G * kD / 8;            // 16-byte pieces (8 halves) per record
@@ -476,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse)
 #pragma unroll
     for (int u = 0; u < F; ++u) {
       const int f = lane + 64 * u;
-      if (f < NF) M[u] = __builtin_fmaxf(M[u], p.part_lse[slot * G + f / (kD / 8)]);
+      if (f < NF) M[u] = __builtin_fmaxf(M[u], p.part_lse[slot * G + f % G]);
     }
   }
   for (int e = 0; e < p.topk; ++e) {
@@ -486,7 +503,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse)
     for (int u = 0; u < F; ++u) {
       const int f = lane + 64 * u;
       if (f < NF) {
-        const int hh = f / (kD / 8);
+        const int hh = f % G;
         const float wl = __builtin_amdgcn_exp2f(p.part_lse[slot * G + hh] - M[u]);
         const float wx = wl * p.part_sc[slot * G + hh];
         const uint4 x = reinterpret_cast<const uint4*>(p.part_o + (size_t)slot * G * kD)[f];
@@ -504,8 +521,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse)
   for (int u = 0; u < F; ++u) {
     const int f = lane + 64 * u;
     if (f >= NF) continue;
-    const int hh = f / (kD / 8);
-    const int d = (f - hh * (kD / 8)) * 8;
+    // 16-byte piece f holds d = 32 dt + 8 rq + 0..7 of head hh, f = (dt * 4 + rq) * G + hh.
+    const int hh = f % G;
+    const int d = (f / G) * 8;
     const float inv = 1.f / L[u];
     uint4 o;
     o.x = pack_bf16x2(acc[u][0] * inv, acc[u][1] * inv);
