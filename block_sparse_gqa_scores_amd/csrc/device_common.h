@@ -31,12 +31,6 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                  0, 0, 0);
 }
 
-// 16-byte load that is not expected to be reused (streamed once).
-__device__ __forceinline__ uint4 load_nt16(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 // Row index (within a 32x32 MFMA output tile) held by register r of lane l.

@@ -215,7 +215,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
 
 // Few rows per sequence (decode): one wave covers every row of a sequence
 // (at most 32), so the waves of a workgroup split the key blocks between them
-// and read their key tiles straight from memory into MFMA operands.
+// and read their key tiles straight from memory into MFMA operands.  Each
+// load instruction covers 32 bytes of 32 key rows and the 8 loads of a row
+// share its cache lines, so the loads are ordinary cached loads (a streaming
+// hint that skips cache reuse makes every line arrive several times).
 constexpr int kDecodeBlocksPerWave = 4;
 
 template <int DIDX>
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_scan_decode(ScanArgs a) {
         const int s = min(j * kBlock + mt * 32 + (lane & 31), a.S_k - 1);  // masked past S_k
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          av[mt][ks] = load_nt16(kbase + (size_t)s * DIDX + 16 * ks + 8 * (lane >> 5));
+          av[mt][ks] = *reinterpret_cast<const uint4*>(kbase + (size_t)s * DIDX + 16 * ks + 8 * (lane >> 5));
       }
       const bool need_mask = j * kBlock + kBlock - 1 > t_min;
       float m = neg_inf();
