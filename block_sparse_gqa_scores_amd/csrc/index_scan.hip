@@ -19,7 +19,7 @@ namespace {
 
 constexpr int kBlock = 128;        // keys per block (the pages' block size)
 constexpr int kThreads = 256;      // 4 waves
-constexpr int kChunk = 16;         // key blocks per workgroup
+constexpr int kChunk = 32;         // key blocks per workgroup
 constexpr int kStageStride = kChunk + 1;  // padded: conflict-free stage writes
 
 struct ScanArgs {
@@ -144,20 +144,30 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
       float m[NT];
 #pragma unroll
       for (int n = 0; n < NT; ++n) m[n] = neg_inf();
+      // Operand fragments of tile row mt + 1 are read from LDS while the MFMAs
+      // of tile row mt run.
+      u32x4 ka[KS], kn[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int krow = (lane & 31);
+        ka[ks] = kt[krow * CPR + swz<DIDX>(krow, 2 * ks + (lane >> 5))];
+      }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const int krow = mt * 32 + (lane & 31);
-        f32x16 acc[NT];
-        {
-          const u32x4 av = kt[krow * CPR + swz<DIDX>(krow, lane >> 5)];
+        if (mt < 3) {
 #pragma unroll
-          for (int n = 0; n < NT; ++n) acc[n] = mfma32x32x16(av, qb[n][0], zero16());
+          for (int ks = 0; ks < KS; ++ks) {
+            const int krow = (mt + 1) * 32 + (lane & 31);
+            kn[ks] = kt[krow * CPR + swz<DIDX>(krow, 2 * ks + (lane >> 5))];
+          }
         }
+        f32x16 acc[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[n] = mfma32x32x16(ka[0], qb[n][0], zero16());
 #pragma unroll
         for (int ks = 1; ks < KS; ++ks) {
-          const u32x4 av = kt[krow * CPR + swz<DIDX>(krow, 2 * ks + (lane >> 5))];
 #pragma unroll
-          for (int n = 0; n < NT; ++n) acc[n] = mfma32x32x16(av, qb[n][ks], acc[n]);
+          for (int n = 0; n < NT; ++n) acc[n] = mfma32x32x16(ka[ks], qb[n][ks], acc[n]);
         }
         if (need_mask) {
 #pragma unroll
@@ -170,6 +180,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
         }
 #pragma unroll
         for (int n = 0; n < NT; ++n) m[n] = max16(m[n], acc[n]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) ka[ks] = kn[ks];
       }
       // Tile pair (2p, 2p+1): lanes < 32 finish tile 2p, lanes >= 32 tile 2p+1,
       // so lane l ends with row w_r0 + 64 p + l.
