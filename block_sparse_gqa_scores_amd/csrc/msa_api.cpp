@@ -33,7 +33,7 @@ msa_status check_dims(const msa_dims* d, bool uses_index, bool uses_main) {
   if (uses_main) {
     if (d->num_heads_q <= 0 || d->head_dim <= 0) return MSA_ERR_INVALID_DIMS;
     if (d->num_heads_q % d->num_heads_kv != 0) return MSA_ERR_INVALID_DIMS;
-    if (!std::isfinite(d->softmax_scale)) return MSA_ERR_INVALID_DIMS;
+    if (!std::isfinite(d->softmax_scale) || d->softmax_scale < 0.f) return MSA_ERR_INVALID_DIMS;
   }
   if (uses_index && d->index_dim <= 0) return MSA_ERR_INVALID_DIMS;
   if (d->causal != 1) return MSA_ERR_UNSUPPORTED;
@@ -180,18 +180,18 @@ msa_status forward_impl(const msa_dims* d, const void* q, const void* k, const v
   int32_t* idx = block_idx_out ? block_idx_out : reinterpret_cast<int32_t*>(base + bm_sz);
   void* attn_ws = base + bm_sz + idx_sz;
   hipStream_t strm = static_cast<hipStream_t>(stream);
-  if (ev) hipEventRecord(ev->ev[2 * MSA_STAGE_INDEX_SCORES], strm);
+  if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_INDEX_SCORES], strm);
   hipError_t e = msa::launch_index_scores(static_cast<const uint16_t*>(q_idx),
                                           static_cast<const uint16_t*>(k_idx), bm, d->batch,
                                           d->seqlen_q, d->seqlen_k, d->num_heads_kv, d->index_dim,
                                           s.n_blk, strm);
   if (e != hipSuccess) return MSA_ERR_HIP;
-  if (ev) hipEventRecord(ev->ev[2 * MSA_STAGE_INDEX_SCORES + 1], strm);
-  if (ev) hipEventRecord(ev->ev[2 * MSA_STAGE_BLOCK_TOPK], strm);
+  if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_INDEX_SCORES + 1], strm);
+  if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_BLOCK_TOPK], strm);
   e = msa::launch_block_topk(bm, idx, d->batch, d->seqlen_q, d->seqlen_k, d->num_heads_kv,
                              s.n_blk, d->topk, strm);
   if (e != hipSuccess) return MSA_ERR_HIP;
-  if (ev) hipEventRecord(ev->ev[2 * MSA_STAGE_BLOCK_TOPK + 1], strm);
+  if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_BLOCK_TOPK + 1], strm);
   e = msa::launch_sparse_attn(s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                               static_cast<const uint16_t*>(v), idx, static_cast<uint16_t*>(out),
                               lse, attn_ws, attn_sz, strm, ev);

@@ -591,7 +591,7 @@ static hipError_t launch_g(const AttnShape& s, const Layout& L, Params p, bool w
                            const StageEvents* ev) {
   // Stage s of msa_stage: 2 = build, 3 = partial, 4 = merge.
   auto mark = [&](int stage, bool after, bool first, bool last) {
-    if (ev && ((!after && first) || (after && last))) hipEventRecord(ev->ev[2 * stage + (after ? 1 : 0)], st);
+    if (ev && ((!after && first) || (after && last))) (void)hipEventRecord(ev->ev[2 * stage + (after ? 1 : 0)], st);
   };
   for (int q0 = 0; q0 < s.S_q; q0 += L.Qc) {
     p.q0 = q0;

@@ -57,7 +57,7 @@ extern "C" {
 typedef enum msa_status {
   MSA_OK = 0,
   MSA_ERR_NULL_PTR = 1,           /* a required pointer is NULL */
-  MSA_ERR_INVALID_DIMS = 2,       /* negative sizes, S_k < S_q, H_q % H_kv != 0, ... */
+  MSA_ERR_INVALID_DIMS = 2,       /* negative sizes or scale, S_k < S_q, H_q % H_kv != 0, ... */
   MSA_ERR_UNSUPPORTED = 3,        /* meaningful, but outside the device path's set */
   MSA_ERR_MISALIGNED = 4,         /* a pointer is not 16-byte aligned */
   MSA_ERR_WORKSPACE_TOO_SMALL = 5,/* ws_bytes < msa_workspace_bytes(...) */
@@ -75,7 +75,7 @@ typedef struct msa_dims {
   int32_t block_size;    /* key tokens per block */
   int32_t topk;          /* blocks kept per query and group, local block incl. */
   int32_t causal;        /* must be 1 */
-  float softmax_scale;   /* main-branch logit scale; 0 selects 1/sqrt(D) */
+  float softmax_scale;   /* main-branch logit scale (>= 0); 0 selects 1/sqrt(D) */
 } msa_dims;
 
 /* Which call a workspace size is asked for. */

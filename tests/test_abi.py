@@ -58,7 +58,7 @@ def topk(d, bm=A, idx=A):
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=-1), 2), (dict(seqlen_q=600), 2), (dict(num_heads_q=7), 2), (dict(topk=0), 2),
     (dict(block_size=0), 2), (dict(num_heads_kv=0), 2), (dict(head_dim=0), 2),
-    (dict(softmax_scale=float("nan")), 2),
+    (dict(softmax_scale=float("nan")), 2), (dict(softmax_scale=-0.5), 2),
     (dict(causal=0), 3), (dict(head_dim=64), 3), (dict(block_size=64), 3), (dict(topk=65), 3),
     (dict(index_dim=96), 3), (dict(num_heads_q=6, num_heads_kv=2), 3),
 ])
