@@ -464,10 +464,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
 // O = sum_e 2^(lse_e - M) sc_e x_e / sum_e 2^(lse_e - M), LSE = M + log2(sum).
 // Every record shares one element order, so the sums run in record order and
 // the order is undone once, when O is written.
+//
+// The entries that count form a wave-uniform bit mask (one ballot).  M comes
+// from the row's topk x G statistics, read by all lanes at once and reduced
+// across the lanes of each head.  Records are then read kBatch at a time
+// with unconditional loads (an entry that does not count reads its own slot,
+// which lies inside the workspace, and is skipped after the load), so a lane
+// keeps kBatch x F 16-byte loads (16 at G <= 8) in flight.
 template <int G>
 __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse) {
   constexpr int NF = G * kD / 8;            // 16-byte pieces (8 halves) per record
   constexpr int F = (NF + 63) / 64;         // pieces per lane
+  constexpr int kBatch = F >= 8 ? 2 : (F >= 4 ? 4 : 8);  // records per batch of loads
   const int lane = threadIdx.x & 63;
   const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= (long)p.B * p.H_kv * p.Qc) return;
@@ -478,53 +486,59 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse)
   const int b = bg / p.H_kv, g = bg - (bg / p.H_kv) * p.H_kv;
   const int32_t* sel = p.idx + ((long)bg * p.S_q + i) * p.topk;
   const int local = (i + p.S_k - p.S_q) / kBlock;  // entries past it are ignored
+  const long slot0 = slot_of(p, bg, il, 0);        // the row's topk slots are consecutive
 
-  float M[F], L[F], acc[F][8];
+  const int je = lane < p.topk ? sel[lane] : -1;
+  const unsigned long long valid = __builtin_amdgcn_ballot_w64(je >= 0 && je <= local);
+
+  // M for head hh = lane % G (every piece f = lane + 64 u has f % G = lane % G).
+  float M = neg_inf();
+  for (int c = lane; c < p.topk * G; c += 64)
+    if ((valid >> (c / G)) & 1ull) M = __builtin_fmaxf(M, p.part_lse[slot0 * G + c]);
 #pragma unroll
-  for (int u = 0; u < F; ++u) {
-    M[u] = neg_inf();
-    L[u] = 0.f;
+  for (int o = G; o < 64; o <<= 1) M = __builtin_fmaxf(M, __shfl_xor(M, o, 64));
+
+  float L = 0.f, acc[F][8];
+#pragma unroll
+  for (int u = 0; u < F; ++u)
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[u][c] = 0.f;
-  }
-  for (int e = 0; e < p.topk; ++e) {
-    if (sel[e] < 0 || sel[e] > local) continue;
-    const long slot = slot_of(p, bg, il, e);
+  const int hh = lane % G;
+  for (int e0 = 0; e0 < p.topk; e0 += kBatch) {
+    u32x4 x[kBatch][F];
+    float lse[kBatch], sc[kBatch];
 #pragma unroll
-    for (int u = 0; u < F; ++u) {
-      const int f = lane + 64 * u;
-      if (f < NF) M[u] = __builtin_fmaxf(M[u], p.part_lse[slot * G + f % G]);
+    for (int k = 0; k < kBatch; ++k) {
+      const long slot = slot0 + min(e0 + k, p.topk - 1);
+      lse[k] = p.part_lse[slot * G + hh];
+      sc[k] = p.part_sc[slot * G + hh];
+      const u32x4* rec = reinterpret_cast<const u32x4*>(p.part_o + (size_t)slot * G * kD);
+#pragma unroll
+      for (int u = 0; u < F; ++u) x[k][u] = rec[min(lane + 64 * u, NF - 1)];
     }
-  }
-  for (int e = 0; e < p.topk; ++e) {
-    if (sel[e] < 0 || sel[e] > local) continue;
-    const long slot = slot_of(p, bg, il, e);
+    asm volatile("" ::: "memory");  // keep the loads above together
 #pragma unroll
-    for (int u = 0; u < F; ++u) {
-      const int f = lane + 64 * u;
-      if (f < NF) {
-        const int hh = f % G;
-        const float wl = __builtin_amdgcn_exp2f(p.part_lse[slot * G + hh] - M[u]);
-        const float wx = wl * p.part_sc[slot * G + hh];
-        const uint4 x = reinterpret_cast<const uint4*>(p.part_o + (size_t)slot * G * kD)[f];
-        L[u] += wl;
-        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+    for (int k = 0; k < kBatch; ++k) {
+      if (!((valid >> min(e0 + k, 63)) & 1ull) || e0 + k >= p.topk) continue;  // wave-uniform
+      const float wl = __builtin_amdgcn_exp2f(lse[k] - M);
+      const float wx = wl * sc[k];
+      L += wl;
+#pragma unroll
+      for (int u = 0; u < F; ++u)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          acc[u][2 * c] += wx * f16_lo(xw[c]);
-          acc[u][2 * c + 1] += wx * f16_hi(xw[c]);
+          acc[u][2 * c] += wx * f16_lo(x[k][u][c]);
+          acc[u][2 * c + 1] += wx * f16_hi(x[k][u][c]);
         }
-      }
     }
   }
+  const float inv = 1.f / L;
 #pragma unroll
   for (int u = 0; u < F; ++u) {
     const int f = lane + 64 * u;
     if (f >= NF) continue;
     // 16-byte piece f holds d = 32 dt + 8 rq + 0..7 of head hh, f = (dt * 4 + rq) * G + hh.
-    const int hh = f % G;
     const int d = (f / G) * 8;
-    const float inv = 1.f / L[u];
     uint4 o;
     o.x = pack_bf16x2(acc[u][0] * inv, acc[u][1] * inv);
     o.y = pack_bf16x2(acc[u][2] * inv, acc[u][3] * inv);
@@ -533,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse)
     *reinterpret_cast<uint4*>(p.out + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + d) = o;
     if (with_lse && d == 0)
       p.lse[((size_t)b * p.H_q + g * G + hh) * p.S_q + i] =
-          (M[u] + __builtin_amdgcn_logf(L[u])) * 0.69314718055994530942f;
+          (M + __builtin_amdgcn_logf(L)) * 0.69314718055994530942f;
   }
 }
 
