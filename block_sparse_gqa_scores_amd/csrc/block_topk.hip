@@ -6,13 +6,14 @@
 // Attention blog: the Top-k works on raw scores, with no exponential).
 //
 // One wavefront per row.  Scores are compared as order-preserving unsigned
-// keys.  The (k-1)-th largest key is found exactly by a most-significant-bit
-// first search whose counts are wave ballots.  To keep that search off long
-// rows, a cutoff is taken first: the (k-1)-th largest of the 64 per-lane
+// keys.  A cutoff is taken first: the (k-1)-th largest of the 64 per-lane
 // maxima.  It cannot exceed the row's (k-1)-th largest score (the conservative
 // filter of section 4.2), so every block of the answer passes it and the exact
-// search runs on the few survivors.  Rows whose survivors overflow the
-// buffer (massive ties) run the same search over the whole row instead.
+// threshold is found among the few survivors.  Both order statistics come
+// from a bitonic sort across the wave's 64 lanes (vector work only); when more
+// than 64 blocks survive, the threshold is found by a most-significant-bit
+// first search whose counts are wave ballots, over the survivor buffer or,
+// past its capacity (massive ties), over the whole row.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -28,6 +29,27 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// The wave's 64 values (one per lane) sorted in descending order: lane l
+// returns the l-th largest.  A bitonic network; every step is one cross-lane
+// exchange, a compare and a select.
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)v, j, 64);
+      const bool desc = (lane & k) == 0;  // direction of this lane's k-run
+      const bool low = (lane & j) == 0;   // lower lane of the exchanged pair
+      v = (low == desc) ? max(v, o) : min(v, o);
+    }
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
 
 // Largest T with #{x >= T} >= kk over the values the callback exposes.
 // count(cand) must return the wave-wide number of values >= cand.
@@ -60,15 +82,26 @@ __global__ __launch_bounds__(kThreads) void block_topk_kernel(const float* __res
   const float* x = bm + row * (long)n_blk;
   int32_t* out = out_idx + row * (long)topk;
 
+  if (kk == 0) {  // k = 1: the local block alone
+    if (lane == 0) out[0] = local;
+    return;
+  }
   if (n_c <= kk) {  // every earlier block fits: keep them all
     for (int e = lane; e < topk; e += 64) out[e] = e <= local ? e : -1;
     return;
   }
 
-  // Cutoff: the kk-th largest of the per-lane maxima.
+  // Cutoff: the kk-th largest of the per-lane maxima (kk <= 63).
   uint32_t lmax = 0;
-  for (int j = lane; j < n_c; j += 64) lmax = max(lmax, order_key(x[j]));
-  const uint32_t cut = kth_largest(kk, [&](uint32_t c) { return __popcll(ballot(lmax >= c)); });
+  {
+    int j = lane;
+    for (; j + 192 < n_c; j += 256) {  // four loads in flight
+      const float a0 = x[j], a1 = x[j + 64], a2 = x[j + 128], a3 = x[j + 192];
+      lmax = max(max(lmax, max(order_key(a0), order_key(a1))), max(order_key(a2), order_key(a3)));
+    }
+    for (; j < n_c; j += 64) lmax = max(lmax, order_key(x[j]));
+  }
+  const uint32_t cut = lane_value(wave_sort_desc(lmax, lane), kk - 1);
 
   // Survivors >= cut, compacted in index order.
   int total = 0;
@@ -90,7 +123,18 @@ __global__ __launch_bounds__(kThreads) void block_topk_kernel(const float* __res
   uint32_t T;
   int need_eq;
   int written = 0;
-  if (total <= kCap) {
+  if (total <= 64) {
+    // One survivor per lane: the threshold by sorting them.
+    const uint32_t key = lane < total ? cand_x[wave][lane] : 0u;
+    T = lane_value(wave_sort_desc(key, lane), kk - 1);
+    need_eq = kk - __popcll(ballot(lane < total && key > T));
+    const bool is_gt = lane < total && key > T;
+    const bool is_eq = lane < total && key == T;
+    const uint64_t em = ballot(is_eq);
+    const bool sel = is_gt || (is_eq && __popcll(em & lt) < need_eq);
+    const uint64_t sm = ballot(sel);
+    if (sel) out[__popcll(sm & lt)] = cand_j[wave][lane];
+  } else if (total <= kCap) {
     uint32_t reg[kCap / 64];
 #pragma unroll
     for (int q = 0; q < kCap / 64; ++q) {

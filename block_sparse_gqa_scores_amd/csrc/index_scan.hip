@@ -152,6 +152,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
         const int krow = (lane & 31);
         ka[ks] = kt[krow * CPR + swz<DIDX>(krow, 2 * ks + (lane >> 5))];
       }
+      // All eight first-row fragments land before the first MFMA (one LDS
+      // round trip instead of one per k-step).
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         if (mt < 3) {
