@@ -16,6 +16,12 @@
 // over the union of its blocks.  Decode (one query per sequence) is the same
 // computation with one query per bucket, i.e. split-KV.
 //
+// Buckets are further split by query window: bucket (b, g, w, j) holds the
+// edges of queries in window w of the chunk, and work items run in bucket
+// order, so the workgroups in flight at any time gather the Q rows of one or
+// two windows, which stay in L2, instead of Q rows from the whole sequence.
+// The window is sized so that a bucket still averages about QT edges.
+//
 // Work-list construction: counts per bucket, exclusive scans of edges and of
 // work items, edge scatter (atomics choose positions inside a bucket only;
 // every edge's arithmetic is independent of its position, so results do not
@@ -37,6 +43,7 @@ constexpr int kVStride = kBlock + 4;  // bf16 per row of the transposed V tile
 constexpr size_t kPartBudget = size_t(16) << 30;  // bytes of partials per chunk
 constexpr int kBuildQueries = 256;   // queries per bucket-build workgroup
 constexpr int kHistBins = 8192;      // widest row whose histogram lives in LDS
+constexpr int kMinWindow = 2048;     // smallest query window (a multiple of kBuildQueries)
 
 struct Params {
   const uint16_t* q;
@@ -47,7 +54,9 @@ struct Params {
   float* lse;
   int B, S_q, S_k, H_q, H_kv, G, n_blk, topk;
   int q0, Qc;            // this chunk's queries: [q0, q0 + Qc) clipped to S_q
-  int NB;                // buckets = B * H_kv * n_blk
+  int NB;                // buckets = B * H_kv * n_win * n_blk
+  int W, n_win;          // queries per window (a multiple of kBuildQueries unless
+                         // it is the whole chunk), windows per chunk
   int QT;                // edges per work item
   float scale_log2;
   int32_t* counts;
@@ -107,7 +116,7 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(Params p) {
     if (edge_ok(p, p.q0 + il0 + s / p.topk, j)) atomicAdd(&hist[j], 1);
   }
   __syncthreads();
-  int32_t* cnt = p.counts + (long)bg * p.n_blk;
+  int32_t* cnt = p.counts + ((long)bg * p.n_win + il0 / p.W) * p.n_blk;
   for (int x = threadIdx.x; x < p.n_blk; x += 256)
     if (hist[x]) atomicAdd(&cnt[x], hist[x]);
 }
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(Params p) {
     if (edge_ok(p, p.q0 + il0 + s / p.topk, j)) atomicAdd(&hist[j], 1);
   }
   __syncthreads();
-  const long b0 = (long)bg * p.n_blk;
+  const long b0 = ((long)bg * p.n_win + il0 / p.W) * p.n_blk;
   for (int x = threadIdx.x; x < p.n_blk; x += 256) {
     const int c = hist[x];
     if (c) base[x] = p.offsets[b0 + x] + atomicAdd(&p.cursor[b0 + x], c);
@@ -155,7 +164,8 @@ __global__ void count_kernel(Params p) {
     const int i = p.q0 + il;
     if (i >= p.S_q) continue;
     const int j = p.idx[((long)bg * p.S_q + i) * p.topk + e];
-    if (j >= 0 && j <= (i + p.S_k - p.S_q) / kBlock) atomicAdd(&p.counts[(long)bg * p.n_blk + j], 1);
+    if (j >= 0 && j <= (i + p.S_k - p.S_q) / kBlock)
+      atomicAdd(&p.counts[((long)bg * p.n_win + il / p.W) * p.n_blk + j], 1);
   }
 }
 
@@ -269,7 +279,7 @@ __global__ void fill_kernel(Params p) {
     if (i >= p.S_q) continue;
     const int j = p.idx[((long)bg * p.S_q + i) * p.topk + e];
     if (j >= 0 && j <= (i + p.S_k - p.S_q) / kBlock) {
-      const long bucket = (long)bg * p.n_blk + j;
+      const long bucket = ((long)bg * p.n_win + il / p.W) * p.n_blk + j;
       const int pos = p.offsets[bucket] + atomicAdd(&p.cursor[bucket], 1);
       p.edges[pos] = (int32_t)s;
     }
@@ -298,8 +308,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
   const int start = item.y;
   const int n_here = min(p.QT, p.counts[bucket] - start);
   const int ebase = p.offsets[bucket] + start;
-  const int bg = bucket / p.n_blk;
-  const int j = bucket - bg * p.n_blk;
+  const int bgw = bucket / p.n_blk;
+  const int j = bucket - bgw * p.n_blk;
+  const int bg = bgw / p.n_win;
   const int b = bg / p.H_kv;
   const int g = bg - b * p.H_kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
@@ -465,12 +476,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
 // Every record shares one element order, so the sums run in record order and
 // the order is undone once, when O is written.
 //
-// The entries that count form a wave-uniform bit mask (one ballot).  M comes
-// from the row's topk x G statistics, read by all lanes at once and reduced
-// across the lanes of each head.  Records are then read kBatch at a time
-// with unconditional loads (an entry that does not count reads its own slot,
-// which lies inside the workspace, and is skipped after the load), so a lane
-// keeps kBatch x F 16-byte loads (16 at G <= 8) in flight.
+// The entries that count form a wave-uniform bit mask (one ballot).  Records
+// are read kBatch at a time with unconditional loads (an entry that does not
+// count reads its own slot, which lies inside the workspace, and is skipped
+// after the load), so a lane keeps kBatch x F 16-byte loads (16 at G <= 8) in
+// flight.
 template <int G>
 __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse) {
   constexpr int NF = G * kD / 8;            // 16-byte pieces (8 halves) per record
@@ -488,22 +498,17 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse)
   const int local = (i + p.S_k - p.S_q) / kBlock;  // entries past it are ignored
   const long slot0 = slot_of(p, bg, il, 0);        // the row's topk slots are consecutive
 
+  // The validity mask, statistics and records of a batch are all requested
+  // before any of them is used; the softmax max is kept online, one rescale
+  // per batch, so no pass over the statistics precedes the records.
   const int je = lane < p.topk ? sel[lane] : -1;
-  const unsigned long long valid = __builtin_amdgcn_ballot_w64(je >= 0 && je <= local);
-
-  // M for head hh = lane % G (every piece f = lane + 64 u has f % G = lane % G).
-  float M = neg_inf();
-  for (int c = lane; c < p.topk * G; c += 64)
-    if ((valid >> (c / G)) & 1ull) M = __builtin_fmaxf(M, p.part_lse[slot0 * G + c]);
-#pragma unroll
-  for (int o = G; o < 64; o <<= 1) M = __builtin_fmaxf(M, __shfl_xor(M, o, 64));
-
-  float L = 0.f, acc[F][8];
+  const int hh = lane % G;
+  float M = neg_inf(), L = 0.f, acc[F][8];
 #pragma unroll
   for (int u = 0; u < F; ++u)
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[u][c] = 0.f;
-  const int hh = lane % G;
+  unsigned long long valid = 0;
   for (int e0 = 0; e0 < p.topk; e0 += kBatch) {
     u32x4 x[kBatch][F];
     float lse[kBatch], sc[kBatch];
@@ -517,9 +522,25 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse)
       for (int u = 0; u < F; ++u) x[k][u] = rec[min(lane + 64 * u, NF - 1)];
     }
     asm volatile("" ::: "memory");  // keep the loads above together
+    if (e0 == 0) valid = __builtin_amdgcn_ballot_w64(je >= 0 && je <= local);
+    // Entry e counts when its bit is set (wave-uniform); e past topk never is.
+    const unsigned bits = (unsigned)(valid >> e0) & ((1u << kBatch) - 1u);  // e0 < topk <= 64
+    if (bits == 0) continue;
+    float mb = neg_inf();
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if ((bits >> k) & 1u) mb = __builtin_fmaxf(mb, lse[k]);
+    const float m_new = __builtin_fmaxf(M, mb);
+    const float alpha = __builtin_amdgcn_exp2f(M - m_new);  // 0 while M = -inf
+    M = m_new;
+    L *= alpha;
+#pragma unroll
+    for (int u = 0; u < F; ++u)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[u][c] *= alpha;
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      if (!((valid >> min(e0 + k, 63)) & 1ull) || e0 + k >= p.topk) continue;  // wave-uniform
+      if (!((bits >> k) & 1u)) continue;  // wave-uniform
       const float wl = __builtin_amdgcn_exp2f(lse[k] - M);
       const float wx = wl * sc[k];
       L += wl;
@@ -554,6 +575,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse)
 struct Layout {
   int Qc, QT, n_scan_wg;
   long NB, E, T;
+  int W, n_win;
   size_t counts, cursor, offsets, tile_off, blk_sums, edges, work, part_lse, part_sc, part_o, total;
 };
 
@@ -567,7 +589,15 @@ Layout make_layout(const AttnShape& s) {
   long qc = (long)(kPartBudget / per_query);
   if (qc >= 128) qc -= qc % 128;
   L.Qc = (int)std::max(1L, std::min<long>(qc, s.S_q));
-  L.NB = (long)s.batch * s.H_kv * s.n_blk;
+  // Window: about QT edges per (window, block) bucket at the chunk's mean
+  // number of visible blocks, at least kMinWindow queries; the whole chunk
+  // when that exceeds it.
+  const long vis = std::max(1L, ((long)s.S_k - s.S_q + s.S_q / 2) / kBlock);
+  long w = ((long)L.QT * vis / std::max(1, s.topk) + kBuildQueries - 1) / kBuildQueries * kBuildQueries;
+  w = std::max<long>(w, kMinWindow);
+  L.W = w < L.Qc ? (int)w : L.Qc;
+  L.n_win = (L.Qc + L.W - 1) / L.W;
+  L.NB = (long)s.batch * s.H_kv * L.n_win * s.n_blk;
   L.E = (long)s.batch * s.H_kv * L.Qc * s.topk;
   L.T = (L.E + L.QT - 1) / L.QT + std::min(L.NB, L.E);
   L.n_scan_wg = (int)((L.NB + kScanPerWg - 1) / kScanPerWg);
@@ -654,6 +684,7 @@ hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint1
   p.B = s.batch; p.S_q = s.S_q; p.S_k = s.S_k; p.H_q = s.H_q; p.H_kv = s.H_kv;
   p.G = s.H_q / s.H_kv; p.n_blk = s.n_blk; p.topk = s.topk;
   p.Qc = L.Qc; p.NB = (int)L.NB; p.QT = L.QT; p.scale_log2 = s.scale_log2;
+  p.W = L.W; p.n_win = L.n_win;
   p.counts = reinterpret_cast<int32_t*>(base + L.counts);
   p.cursor = reinterpret_cast<int32_t*>(base + L.cursor);
   p.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
