@@ -240,6 +240,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run one plain device copy of this many bytes first (counter calibration)")
+    ap.add_argument("--no-copy-rate", action="store_true",
+                    help="skip the closing 1 GiB device copy that reports the plain copy rate")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -295,6 +297,12 @@ def main():
                          "tokens/s": wd.batch * wd.seqlen_q / (msd * 1e-3),
                          "stages_ms": stage_d, "roofline": roofline(wd, stage_d, chunks_d)}
         del td
+    if not args.no_copy_rate:
+        torch.cuda.empty_cache()
+        # Reference rate of the same HBM: a plain streaming copy (reads and
+        # writes 1 GiB each), for reading the GB/s figures above.
+        res["copy_rate"] = {"GB/s": synth.copy_probe(1 << 30, reps=11), "bytes": 1 << 30,
+                            "what": "plain device copy, bytes read + written per second"}
     print(json.dumps(res), flush=True)
 
 

@@ -197,19 +197,35 @@ def _load():
     return _lib
 
 
-def copy_probe(nbytes: int, device="cuda") -> None:
-    """Run one plain device copy of ``nbytes`` (reads and writes exactly that
-    many bytes): the known-size reference for traffic counters."""
+def copy_probe(nbytes: int, device="cuda", reps: int = 1) -> float:
+    """Run ``reps`` plain device copies of ``nbytes`` (each reads and writes
+    exactly that many bytes): the known-size reference for traffic counters.
+    Returns the copy rate in GB/s (bytes read + written per second) over the
+    reps after the first, or 0.0 when reps == 1."""
     import torch
 
     src = torch.empty(nbytes, dtype=torch.uint8, device=device)
     dst = torch.empty_like(src)
-    stream = torch.cuda.current_stream(src.device).cuda_stream
-    rc = _load().synth_copy_bytes(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
-                                  nbytes, ctypes.c_void_p(stream))
-    if rc != 0:
-        raise RuntimeError(f"copy probe failed ({rc})")
+    stream = torch.cuda.current_stream(src.device)
+    lib = _load()
+
+    def once():
+        rc = lib.synth_copy_bytes(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                  nbytes, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"copy probe failed ({rc})")
+
+    once()
+    if reps <= 1:
+        torch.cuda.synchronize()
+        return 0.0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps - 1):
+        once()
+    e1.record(stream)
     torch.cuda.synchronize()
+    return 2.0 * nbytes * (reps - 1) / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
 def fill_device(w: Workload, name: str, tensor) -> None:
