@@ -23,11 +23,6 @@ namespace {
 constexpr int kThreads = 256;  // 4 rows per workgroup
 constexpr int kCap = 256;      // survivor buffer per row (4 per lane)
 
-__device__ __forceinline__ uint32_t order_key(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // The wave's 64 values (one per lane) sorted in descending order: lane l

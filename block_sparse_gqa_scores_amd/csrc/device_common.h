@@ -38,12 +38,13 @@ __device__ __forceinline__ int mfma32_row(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
-// max(a, b, c) in one v_max3_f32 (operands are never NaN where it is used:
-// scores are finite or -inf, so no NaN canonicalisation is needed).
+// max(a, b, c): the compiler fuses the two maxima into one v_max3_f32.  This
+// is written with the compiler's max, not inline assembly: the compiler then
+// sees where the operands come from and inserts the wait states that a vector
+// ALU read of a fresh MFMA result requires (it cannot do so for an assembly
+// operand, and a read too early returns the register's previous contents).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 
 // Max of the 16 values of an MFMA 32x32 output register block and `m`.
@@ -56,11 +57,9 @@ __device__ __forceinline__ float max16(float m, const f32x16& x) {
   return max3f(max3f(a, b, c), max3f(d, e, x[15]), m);
 }
 
-// max(|a|, |b|, c) in one v_max3_f32 with abs source modifiers.
+// max(|a|, |b|, c): one v_max3_f32 with abs source modifiers (see max3f).
 __device__ __forceinline__ float max3abs(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(a), __builtin_fabsf(b)), c);
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -99,5 +98,11 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Order-preserving unsigned key of a float: a < b (non-NaN) iff key(a) < key(b).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
 }  // namespace msa

@@ -11,6 +11,17 @@
 // Rows are r = i * H_kv + g: q_idx[b] is one contiguous [S_q * H_kv][D_idx]
 // matrix, and 256 consecutive rows (32 queries when H_kv = 8) share one
 // 128-block window of causal positions.
+//
+// Selection mode (the forward path with k <= 16): one workgroup sweeps every
+// key block before its rows' local blocks and keeps, per row, the running best
+// k-1 blocks in registers, so neither the block scores nor a separate Top-k
+// pass touch memory (the streaming form of the exact top-k of Sparse
+// Attention Part II, sections 4.2 and 4.4).  Blocks arrive in ascending index
+// order, so a new block displaces the current worst kept block only when its
+// score is strictly higher: equal scores keep the lower index, as the
+// selection rule requires.
+#include <climits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -29,7 +40,11 @@ struct ScanArgs {
   int S_q, S_k, H_kv, n_blk;
   int n_qtiles;   // ceil(S_q * H_kv / rows per workgroup)
   int batch;
+  int32_t* sel;   // selection mode: [B][H_kv][S_q][topk] output
+  int topk;
 };
+
+constexpr int kKeep = 15;  // selection mode: earlier blocks kept per row (k <= 16)
 
 // 16-byte chunk position inside an LDS row of the key tile, XOR-swizzled so
 // that the 16 lanes reading one chunk column of 16 consecutive rows hit 16
@@ -41,9 +56,10 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 // NT 32-row MFMA N tiles per wave: every 16-byte key fragment read from LDS
-// feeds NT matrix instructions.
-template <int DIDX, int NT, int WAVES>
+// feeds NT matrix instructions.  SELECT: selection mode (above).
+template <int DIDX, int NT, int WAVES, bool SELECT>
 __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) {
+  static_assert(!SELECT || NT == 2, "selection mode keeps one row per lane");
   constexpr int kThreads = 64 * WAVES;
   constexpr int KS = DIDX / 16;           // MFMA k-steps
   constexpr int CPR = DIDX / 8;           // 16-byte chunks per key row
@@ -52,25 +68,33 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
   constexpr int ROWS_W = 32 * NT;
   constexpr int ROWS_WG = WAVES * ROWS_W;
   __shared__ u32x4 ktile[2][TILE_CHUNKS];
-  __shared__ float stage[ROWS_WG * kStageStride];
+  __shared__ float stage[SELECT ? 1 : ROWS_WG * kStageStride];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int per_chunk = a.batch * a.n_qtiles;
-  const int chunk = blockIdx.x / per_chunk;
-  const int rem = blockIdx.x - chunk * per_chunk;
-  const int b = rem / a.n_qtiles;
-  const int qt = rem - b * a.n_qtiles;
+  int chunk, b, qt;
+  if constexpr (SELECT) {  // one workgroup per row tile, longest rows first
+    chunk = 0;
+    b = blockIdx.x / a.n_qtiles;
+    qt = a.n_qtiles - 1 - (blockIdx.x - b * a.n_qtiles);
+  } else {
+    const int per_chunk = a.batch * a.n_qtiles;
+    chunk = blockIdx.x / per_chunk;
+    const int rem = blockIdx.x - chunk * per_chunk;
+    b = rem / a.n_qtiles;
+    qt = rem - b * a.n_qtiles;
+  }
 
   const int R = a.S_q * a.H_kv;
   const int off = a.S_k - a.S_q;        // position of query i is i + off
   const int wg_r0 = qt * ROWS_WG;
   const int wg_r1 = min(wg_r0 + ROWS_WG, R) - 1;  // last valid row
   const int j0 = chunk * kChunk;
-  const int nj = min(kChunk, a.n_blk - j0);
+  const int nj = SELECT ? a.n_blk : min(kChunk, a.n_blk - j0);
   const int wg_lmax = (wg_r1 / a.H_kv + off) / kBlock;  // largest local block
-  const int nj_live = max(0, min(nj, wg_lmax - j0 + 1));
+  // Selection ranks only blocks before a row's local block.
+  const int nj_live = max(0, min(nj, wg_lmax - j0 + (SELECT ? 0 : 1)));
 
   // The wave's rows and their causal positions.
   const int w_r0 = wg_r0 + wave * ROWS_W;
@@ -97,26 +121,32 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
   }
 
   const uint16_t* kbase = a.k_idx + (size_t)b * a.S_k * DIDX;
-  // Tile geometry of this thread's LOADS 16-byte pieces: key row and LDS slot.
-  int t_row[LOADS], t_lds[LOADS];
-#pragma unroll
-  for (int it = 0; it < LOADS; ++it) {
-    const int q = it * kThreads + tid;
-    const int row = q / CPR, c = q % CPR;
-    t_row[it] = row;
-    t_lds[it] = row * CPR + swz<DIDX>(row, c);
-  }
-  const int t_col16 = 8 * ((tid) % CPR);  // same column for every piece (kThreads % CPR == 0)
+  // Tile geometry of this thread's LOADS 16-byte pieces: piece q = it *
+  // kThreads + tid is key row q / CPR, chunk q % CPR (the same chunk for every
+  // piece, as kThreads % CPR == 0).  The indices are recomputed from an opaque
+  // copy of tid at each use instead of being held across the loop.
   u32x4 pre[LOADS];  // native vectors: stay in registers
+#define MSA_TILE_TID                                                                       \
+  int t_ = tid;                                                                            \
+  asm volatile("" : "+v"(t_));
   // Rows past S_k are causally masked for every query; reading a clamped row
   // instead keeps the loads unconditional (a fixed count in flight).
 #define MSA_LOAD_TILE(J)                                                                   \
-  _Pragma("unroll") for (int it = 0; it < LOADS; ++it) {                                   \
-    const int s_ = min((J) * kBlock + t_row[it], a.S_k - 1);                               \
-    pre[it] = *reinterpret_cast<const u32x4*>(kbase + (size_t)s_ * DIDX + t_col16);        \
+  {                                                                                        \
+    MSA_TILE_TID                                                                           \
+    _Pragma("unroll") for (int it = 0; it < LOADS; ++it) {                                 \
+      const int s_ = min((J) * kBlock + (it * kThreads + t_) / CPR, a.S_k - 1);            \
+      pre[it] = *reinterpret_cast<const u32x4*>(kbase + (size_t)s_ * DIDX + 8 * (t_ % CPR)); \
+    }                                                                                      \
   }
-#define MSA_STORE_TILE(BUF) \
-  _Pragma("unroll") for (int it = 0; it < LOADS; ++it) ktile[BUF][t_lds[it]] = pre[it];
+#define MSA_STORE_TILE(BUF)                                                                \
+  {                                                                                        \
+    MSA_TILE_TID                                                                           \
+    _Pragma("unroll") for (int it = 0; it < LOADS; ++it) {                                 \
+      const int row_ = (it * kThreads + t_) / CPR;                                         \
+      ktile[BUF][row_ * CPR + swz<DIDX>(row_, t_ % CPR)] = pre[it];                        \
+    }                                                                                      \
+  }
 
   if (nj_live > 0) {
     MSA_LOAD_TILE(j0)
@@ -127,6 +157,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  // Selection mode: this lane's row, its local block, and its kept blocks as
+  // 64-bit keys (order-preserving score << 32 | ~index: larger is better).
+  // Unused slots hold 0 (worse than any block); slots past k-1 hold ~0 (never
+  // the worst, never replaced).
+  const int my_r = w_r0 + lane;
+  const int my_l = my_r < R ? (my_r / a.H_kv + off) / kBlock : -1;
+  uint64_t keep[kKeep];
+#pragma unroll
+  for (int t = 0; t < kKeep; ++t) keep[t] = t < a.topk - 1 ? 0ull : ~0ull;
+  uint64_t worst = a.topk - 1 > 0 ? 0ull : ~0ull;
+  int wi = 0;
+
   const bool lo = lane < 32;
   for (int jj = 0; jj < nj_live; ++jj) {
     const int j = j0 + jj;
@@ -136,11 +178,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
     asm volatile("" ::: "memory");
     const u32x4* kt = ktile[jj & 1];
     float best[NT / 2];
-    if (j * kBlock > w_t_max) {
+    // Selection mode skips blocks at or past every local block of the wave.
+    if (SELECT ? j >= w_t_max / kBlock : j * kBlock > w_t_max) {
 #pragma unroll
       for (int p2 = 0; p2 < NT / 2; ++p2) best[p2] = neg_inf();  // nothing visible to this wave
     } else {
-      const bool need_mask = j * kBlock + kBlock - 1 > w_t_min;
+      // Selection mode ranks a block only for rows that see all of it.
+      const bool need_mask = !SELECT && j * kBlock + kBlock - 1 > w_t_min;
       float m[NT];
 #pragma unroll
       for (int n = 0; n < NT; ++n) m[n] = neg_inf();
@@ -183,6 +227,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
         }
 #pragma unroll
         for (int n = 0; n < NT; ++n) m[n] = max16(m[n], acc[n]);
+        // Keep each tile row's maxima ahead of the next row's MFMAs: letting
+        // them overlap keeps two rows of accumulators live and spills.
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) ka[ks] = kn[ks];
       }
@@ -195,17 +242,71 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
         best[p2] = __builtin_fmaxf(lo ? m[2 * p2] : m[2 * p2 + 1], got);
       }
     }
+    if constexpr (SELECT) {
+      const uint64_t x = ((uint64_t)order_key(best[0]) << 32) | (uint32_t)~(uint32_t)j;
+      const bool take = j < my_l && x > worst;
+      if (__builtin_amdgcn_ballot_w64(take) != 0) {
+        if (take) {
 #pragma unroll
-    for (int p2 = 0; p2 < NT / 2; ++p2)
-      stage[(wave * ROWS_W + 64 * p2 + lane) * kStageStride + jj] = best[p2];
+          for (int t = 0; t < kKeep; ++t)
+            if (t == wi) keep[t] = x;
+          worst = keep[0];
+          wi = 0;
+#pragma unroll
+          for (int t = 1; t < kKeep; ++t)
+            if (keep[t] < worst) {
+              worst = keep[t];
+              wi = t;
+            }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int p2 = 0; p2 < NT / 2; ++p2)
+        stage[(wave * ROWS_W + 64 * p2 + lane) * kStageStride + jj] = best[p2];
+    }
     asm volatile("" ::: "memory");
     if (jj + 1 < nj_live) { MSA_STORE_TILE((jj & 1) ^ 1) }
     __syncthreads();
   }
 
+#undef MSA_TILE_TID
 #undef MSA_LOAD_TILE
 #undef MSA_STORE_TILE
 
+  if constexpr (SELECT) {
+    // Kept blocks in ascending order, then the local block, then -1 padding.
+    if (my_r < R) {
+      int js[16];
+#pragma unroll
+      for (int t = 0; t < kKeep; ++t)
+        js[t] = (keep[t] != 0ull && keep[t] != ~0ull) ? (int)~(uint32_t)keep[t] : INT_MAX;
+      js[15] = INT_MAX;
+#pragma unroll
+      for (int k2 = 2; k2 <= 16; k2 <<= 1)
+#pragma unroll
+        for (int h2 = k2 >> 1; h2 > 0; h2 >>= 1)
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const int u = t ^ h2;
+            if (u > t) {
+              const int mn = min(js[t], js[u]), mx = max(js[t], js[u]);
+              const bool up = (t & k2) == 0;
+              js[t] = up ? mn : mx;
+              js[u] = up ? mx : mn;
+            }
+          }
+      int n = 0;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) n += js[t] != INT_MAX;
+      const int i = my_r / a.H_kv, g = my_r - (my_r / a.H_kv) * a.H_kv;
+      int32_t* out = a.sel + (((size_t)b * a.H_kv + g) * a.S_q + i) * a.topk;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (e < a.topk) out[e] = e < n ? js[e] : (e == n ? my_l : -1);
+    }
+    return;
+  }
   // Each row's nj block scores are contiguous in memory.
   for (int rr = tid; rr < ROWS_WG; rr += kThreads) {
     const int r = wg_r0 + rr;
@@ -320,7 +421,7 @@ constexpr int kRowsPerWg = kWaves * 32 * kNT;
 hipError_t launch_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, float* bm,
                                int batch, int S_q, int S_k, int H_kv, int D_idx, int n_blk,
                                hipStream_t stream) {
-  ScanArgs a{q_idx, k_idx, bm, S_q, S_k, H_kv, n_blk, 0, batch};
+  ScanArgs a{q_idx, k_idx, bm, S_q, S_k, H_kv, n_blk, 0, batch, nullptr, 0};
   const int R = S_q * H_kv;
   if (R <= 32) {
     const int blocks_per_wg = 4 * kDecodeBlocksPerWave;
@@ -335,9 +436,28 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, flo
   const long n_chunks = (n_blk + kChunk - 1) / kChunk;
   const long grid = n_chunks * batch * a.n_qtiles;
   if (D_idx == 128)
-    hipLaunchKernelGGL((index_scan_prefill<128, kNT, kWaves>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((index_scan_prefill<128, kNT, kWaves, false>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
   else
-    hipLaunchKernelGGL((index_scan_prefill<64, kNT, kWaves>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((index_scan_prefill<64, kNT, kWaves, false>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
+bool index_select_fused(int S_q, int H_kv, int topk) {
+  return S_q * H_kv > 32 && topk <= kKeep + 1;
+}
+
+hipError_t launch_index_select(const uint16_t* q_idx, const uint16_t* k_idx, int32_t* sel,
+                               int batch, int S_q, int S_k, int H_kv, int D_idx, int n_blk,
+                               int topk, hipStream_t stream) {
+  if (!index_select_fused(S_q, H_kv, topk)) return hipErrorInvalidValue;
+  ScanArgs a{q_idx, k_idx, nullptr, S_q, S_k, H_kv, n_blk, 0, batch, sel, topk};
+  const int R = S_q * H_kv;
+  a.n_qtiles = (R + kRowsPerWg - 1) / kRowsPerWg;
+  const long grid = (long)batch * a.n_qtiles;
+  if (D_idx == 128)
+    hipLaunchKernelGGL((index_scan_prefill<128, kNT, kWaves, true>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL((index_scan_prefill<64, kNT, kWaves, true>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 

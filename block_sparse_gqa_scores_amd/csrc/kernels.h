@@ -13,6 +13,13 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, flo
                                int batch, int S_q, int S_k, int H_kv, int D_idx, int n_blk,
                                hipStream_t stream);
 
+// Block scores and Top-k in one pass, no block scores in memory (see
+// index_scan.hip); only for the shapes index_select_fused accepts.
+bool index_select_fused(int S_q, int H_kv, int topk);
+hipError_t launch_index_select(const uint16_t* q_idx, const uint16_t* k_idx, int32_t* sel,
+                               int batch, int S_q, int S_k, int H_kv, int D_idx, int n_blk,
+                               int topk, hipStream_t stream);
+
 // Top-k selection (see block_topk.hip).
 hipError_t launch_block_topk(const float* bm, int32_t* idx, int batch, int S_q, int S_k,
                              int H_kv, int n_blk, int topk, hipStream_t stream);

@@ -75,6 +75,14 @@ size_t idx_bytes(const msa_dims& d) {
   return size_t(d.batch) * d.num_heads_kv * d.seqlen_q * d.topk * sizeof(int32_t);
 }
 
+// msa_forward scores and selects in one pass (no block scores in memory) when
+// the fused kernel covers the shape.
+bool fused_select(const msa_dims& d) {
+  return msa::index_select_fused(d.seqlen_q, d.num_heads_kv, d.topk);
+}
+
+size_t forward_bm_bytes(const msa_dims& d) { return fused_select(d) ? 0 : align256(bm_bytes(d)); }
+
 msa_status from_hip(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
 }  // namespace
@@ -107,7 +115,7 @@ size_t msa_workspace_bytes(const msa_dims* d, int entry) {
     case MSA_ENTRY_FORWARD:
       if (check_dims(d, true, true) != MSA_OK) return bad;
       if (is_empty(*d)) return 0;
-      return align256(bm_bytes(*d)) + align256(idx_bytes(*d)) +
+      return forward_bm_bytes(*d) + align256(idx_bytes(*d)) +
              msa::sparse_attn_workspace(attn_shape(*d));
     default:
       return bad;
@@ -169,7 +177,7 @@ msa_status forward_impl(const msa_dims* d, const void* q, const void* k, const v
       !aligned16(out) || (lse && !aligned16(lse)) || (block_idx_out && !aligned16(block_idx_out)))
     return MSA_ERR_MISALIGNED;
   const msa::AttnShape s = attn_shape(*d);
-  const size_t bm_sz = align256(bm_bytes(*d));
+  const size_t bm_sz = forward_bm_bytes(*d);
   const size_t idx_sz = align256(idx_bytes(*d));
   const size_t attn_sz = msa::sparse_attn_workspace(s);
   const size_t need = bm_sz + idx_sz + attn_sz;
@@ -180,17 +188,28 @@ msa_status forward_impl(const msa_dims* d, const void* q, const void* k, const v
   int32_t* idx = block_idx_out ? block_idx_out : reinterpret_cast<int32_t*>(base + bm_sz);
   void* attn_ws = base + bm_sz + idx_sz;
   hipStream_t strm = static_cast<hipStream_t>(stream);
+  hipError_t e;
   if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_INDEX_SCORES], strm);
-  hipError_t e = msa::launch_index_scores(static_cast<const uint16_t*>(q_idx),
-                                          static_cast<const uint16_t*>(k_idx), bm, d->batch,
-                                          d->seqlen_q, d->seqlen_k, d->num_heads_kv, d->index_dim,
-                                          s.n_blk, strm);
-  if (e != hipSuccess) return MSA_ERR_HIP;
-  if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_INDEX_SCORES + 1], strm);
-  if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_BLOCK_TOPK], strm);
-  e = msa::launch_block_topk(bm, idx, d->batch, d->seqlen_q, d->seqlen_k, d->num_heads_kv,
-                             s.n_blk, d->topk, strm);
-  if (e != hipSuccess) return MSA_ERR_HIP;
+  if (fused_select(*d)) {
+    // One kernel scores and selects; the Top-k stage is empty.
+    e = msa::launch_index_select(static_cast<const uint16_t*>(q_idx),
+                                 static_cast<const uint16_t*>(k_idx), idx, d->batch, d->seqlen_q,
+                                 d->seqlen_k, d->num_heads_kv, d->index_dim, s.n_blk, d->topk,
+                                 strm);
+    if (e != hipSuccess) return MSA_ERR_HIP;
+    if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_INDEX_SCORES + 1], strm);
+    if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_BLOCK_TOPK], strm);
+  } else {
+    e = msa::launch_index_scores(static_cast<const uint16_t*>(q_idx),
+                                 static_cast<const uint16_t*>(k_idx), bm, d->batch, d->seqlen_q,
+                                 d->seqlen_k, d->num_heads_kv, d->index_dim, s.n_blk, strm);
+    if (e != hipSuccess) return MSA_ERR_HIP;
+    if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_INDEX_SCORES + 1], strm);
+    if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_BLOCK_TOPK], strm);
+    e = msa::launch_block_topk(bm, idx, d->batch, d->seqlen_q, d->seqlen_k, d->num_heads_kv,
+                               s.n_blk, d->topk, strm);
+    if (e != hipSuccess) return MSA_ERR_HIP;
+  }
   if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_BLOCK_TOPK + 1], strm);
   e = msa::launch_sparse_attn(s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                               static_cast<const uint16_t*>(v), idx, static_cast<uint16_t*>(out),
