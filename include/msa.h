@@ -157,9 +157,11 @@ msa_status msa_sparse_attn_fwd(const msa_dims* dims, const void* q,
  * main attention; Sparse Attention Part II, section 3.2 figure: hidden states,
  * indexer scores, selected indices, main attention): msa_index_scores, then
  * msa_block_topk, then msa_sparse_attn_fwd, all on `stream`, with the block
- * scores kept in `ws`.  `block_idx_out` (may be NULL) receives the selection;
- * `lse` may be NULL.  `ws` must hold msa_workspace_bytes(dims,
- * MSA_ENTRY_FORWARD) bytes.
+ * scores kept in `ws`.  When topk <= 16 and seqlen_q * num_heads_kv > 32 the
+ * first two run as one kernel that keeps each row's running Top-k in
+ * registers and never writes the block scores (same selection, bit for bit).
+ * `block_idx_out` (may be NULL) receives the selection; `lse` may be NULL.
+ * `ws` must hold msa_workspace_bytes(dims, MSA_ENTRY_FORWARD) bytes.
  */
 msa_status msa_forward(const msa_dims* dims, const void* q, const void* k,
                        const void* v, const void* q_idx, const void* k_idx,

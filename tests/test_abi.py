@@ -91,11 +91,28 @@ def test_null_and_misaligned_pointers():
     assert topk(d, bm=MIS) == 4
 
 
+def _al(x):
+    return (x + 255) // 256 * 256
+
+
 def test_workspace_checks():
     d = dims()
     need = msa.msa_workspace_bytes(d, msa.ENTRY_FORWARD)
-    bm = d.batch * d.num_heads_kv * d.seqlen_q * d.n_blk * 4
-    assert need >= bm + msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_FWD)
+    rows = d.batch * d.num_heads_kv * d.seqlen_q
+    attn_ws = msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_FWD)
+    # k <= 16 with more than 32 rows: scores and selection are fused, so the
+    # forward workspace holds the selection and the attention scratch only.
+    assert need == _al(rows * d.topk * 4) + attn_ws
+    # A wider Top-k stages the block scores in the workspace first.
+    d2 = dims(topk=32)
+    attn2 = msa.msa_workspace_bytes(d2, msa.ENTRY_SPARSE_ATTN_FWD)
+    assert msa.msa_workspace_bytes(d2, msa.ENTRY_FORWARD) == (
+        _al(rows * d2.n_blk * 4) + _al(rows * 32 * 4) + attn2)
+    # So does decode (at most 32 rows), which scores with the decode kernel.
+    d3 = dims(seqlen_q=1, seqlen_k=4096)
+    attn3 = msa.msa_workspace_bytes(d3, msa.ENTRY_SPARSE_ATTN_FWD)
+    assert msa.msa_workspace_bytes(d3, msa.ENTRY_FORWARD) == (
+        _al(2 * d3.n_blk * 4) + _al(2 * 16 * 4) + attn3)
     assert fwd(d, nbytes=need - 1) == 5
     need_a = msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_FWD)
     assert need_a > 0 and attn(d, nbytes=need_a - 1) == 5
