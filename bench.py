@@ -118,8 +118,15 @@ def run_workload(w, steps, warmup):
     return t, ms, wall, stage_ms, msa.msa_attn_chunks(d)
 
 
+def fused_selection(w):
+    """msa_forward scores and selects in one kernel for these shapes (msa.h)."""
+    return w.seqlen_q * w.heads_kv > 32 and w.topk <= 16
+
+
 def stage_work(w, chunks):
-    """Algorithmic work of each stage per launch: (bound, amount, unit)."""
+    """Algorithmic work of each stage per launch: (bound, amount, unit).  With
+    the fused selection the Top-k runs inside the index stage and its own
+    stage is empty (bound "fused")."""
     rows = w.batch * w.heads_kv * w.seqlen_q
     edges = w.batch * w.heads_kv * float(np.minimum(positions(w) // w.block_size + 1, w.topk).sum())
     G = w.group
@@ -128,7 +135,7 @@ def stage_work(w, chunks):
         index = ("hbm", w.batch * (w.seqlen_k * w.index_dim * 2.0 + rows / w.batch * (w.index_dim * 2.0 + w.n_blk * 4.0)), "B")
     return {
         "index_scores": index,
-        "block_topk": ("hbm", rows * (w.n_blk + w.topk) * 4.0, "B"),
+        "block_topk": ("fused", 0.0, "B") if fused_selection(w) else ("hbm", rows * (w.n_blk + w.topk) * 4.0, "B"),
         "attn_build": ("hbm", (rows * w.topk * 4.0 * 2 + edges * 4.0) / chunks, "B"),
         "attn_partial": ("mfma", attn_flops(w) / chunks, "FLOP"),
         "attn_merge": ("hbm", (edges * G * (2 * w.head_dim + 8) + rows * G * w.head_dim * 2.0) / chunks, "B"),
@@ -180,7 +187,7 @@ def measured_traffic(w, stage):
 
 
 KERNEL_OF_STAGE = {
-    "index_scores": "index_scan_prefill (index_scan_decode when S_q * H_kv <= 32)",
+    "index_scores": "index_scan_prefill (selection mode with k <= 16; index_scan_decode when S_q * H_kv <= 32)",
     "block_topk": "block_topk_kernel",
     "attn_build": "zero/bucket_count/scan/bucket_fill kernels",
     "attn_partial": "attn_partial_kernel<G>",
@@ -263,10 +270,10 @@ def main():
     roof = roofline(w, stage_ms, chunks)
     stages = {}
     for name, (bound, amount, unit) in stage_work(w, chunks).items():
-        per = stage_ms[name] / chunks
-        rate = amount / (per * 1e-3)
-        stages[name] = {"ms_per_step": stage_ms[name], "bound": bound,
-                        ("TFLOP/s" if unit == "FLOP" else "GB/s"): rate / (1e12 if unit == "FLOP" else 1e9)}
+        stages[name] = {"ms_per_step": stage_ms[name], "bound": bound}
+        if bound != "fused":
+            rate = amount / (stage_ms[name] / chunks * 1e-3)
+            stages[name]["TFLOP/s" if unit == "FLOP" else "GB/s"] = rate / (1e12 if unit == "FLOP" else 1e9)
     print(f"[bench] {ms:.3f} ms/step; stages {json.dumps(stage_ms)}", file=sys.stderr, flush=True)
 
     res = {
