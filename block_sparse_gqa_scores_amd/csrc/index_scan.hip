@@ -67,7 +67,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
   constexpr int LOADS = TILE_CHUNKS / kThreads;  // 16-byte loads per thread
   constexpr int ROWS_W = 32 * NT;
   constexpr int ROWS_WG = WAVES * ROWS_W;
-  __shared__ u32x4 ktile[2][TILE_CHUNKS];
+  // Selection mode works on two key blocks per barrier: four tile buffers.
+  constexpr int NBUF = SELECT ? 4 : 2;
+  __shared__ u32x4 ktile[NBUF][TILE_CHUNKS];
   __shared__ float stage[SELECT ? 1 : ROWS_WG * kStageStride];
 
   const int tid = threadIdx.x;
@@ -125,32 +127,34 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
   // kThreads + tid is key row q / CPR, chunk q % CPR (the same chunk for every
   // piece, as kThreads % CPR == 0).  The indices are recomputed from an opaque
   // copy of tid at each use instead of being held across the loop.
-  u32x4 pre[LOADS];  // native vectors: stay in registers
+  u32x4 pre[LOADS], pre2[LOADS];  // native vectors: stay in registers
 #define MSA_TILE_TID                                                                       \
   int t_ = tid;                                                                            \
   asm volatile("" : "+v"(t_));
   // Rows past S_k are causally masked for every query; reading a clamped row
   // instead keeps the loads unconditional (a fixed count in flight).
-#define MSA_LOAD_TILE(J)                                                                   \
+#define MSA_LOAD_TILE(J, PRE)                                                              \
   {                                                                                        \
     MSA_TILE_TID                                                                           \
     _Pragma("unroll") for (int it = 0; it < LOADS; ++it) {                                 \
       const int s_ = min((J) * kBlock + (it * kThreads + t_) / CPR, a.S_k - 1);            \
-      pre[it] = *reinterpret_cast<const u32x4*>(kbase + (size_t)s_ * DIDX + 8 * (t_ % CPR)); \
+      PRE[it] = *reinterpret_cast<const u32x4*>(kbase + (size_t)s_ * DIDX + 8 * (t_ % CPR)); \
     }                                                                                      \
   }
-#define MSA_STORE_TILE(BUF)                                                                \
+#define MSA_STORE_TILE(BUF, PRE)                                                           \
   {                                                                                        \
     MSA_TILE_TID                                                                           \
     _Pragma("unroll") for (int it = 0; it < LOADS; ++it) {                                 \
       const int row_ = (it * kThreads + t_) / CPR;                                         \
-      ktile[BUF][row_ * CPR + swz<DIDX>(row_, t_ % CPR)] = pre[it];                        \
+      ktile[BUF][row_ * CPR + swz<DIDX>(row_, t_ % CPR)] = PRE[it];                        \
     }                                                                                      \
   }
 
   if (nj_live > 0) {
-    MSA_LOAD_TILE(j0)
-    MSA_STORE_TILE(0)
+    MSA_LOAD_TILE(j0, pre)
+    if constexpr (SELECT) { MSA_LOAD_TILE(j0 + min(1, nj_live - 1), pre2) }
+    MSA_STORE_TILE(0, pre)
+    if constexpr (SELECT) { MSA_STORE_TILE(1, pre2) }
   }
   // Everything loaded so far (index queries, first tile) has landed; saying so
   // explicitly keeps the loop's MFMAs from waiting on the next tile's loads.
@@ -170,14 +174,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
   int wi = 0;
 
   const bool lo = lane < 32;
-  for (int jj = 0; jj < nj_live; ++jj) {
-    const int j = j0 + jj;
-    if (jj + 1 < nj_live) { MSA_LOAD_TILE(j + 1) }
-    // Compiler-only fences: keep the next tile's global loads before the
-    // compute and its LDS stores after it, so the loads fly during the MFMAs.
-    asm volatile("" ::: "memory");
-    const u32x4* kt = ktile[jj & 1];
-    float best[NT / 2];
+  // Block max of block j for this lane's rows (tile kt in LDS).
+  auto block_max = [&](int j, const u32x4* kt, float (&best)[NT / 2]) {
     // Selection mode skips blocks at or past every local block of the wave.
     if (SELECT ? j >= w_t_max / kBlock : j * kBlock > w_t_max) {
 #pragma unroll
@@ -242,32 +240,70 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
         best[p2] = __builtin_fmaxf(lo ? m[2 * p2] : m[2 * p2 + 1], got);
       }
     }
-    if constexpr (SELECT) {
-      const uint64_t x = ((uint64_t)order_key(best[0]) << 32) | (uint32_t)~(uint32_t)j;
-      const bool take = j < my_l && x > worst;
-      if (__builtin_amdgcn_ballot_w64(take) != 0) {
-        if (take) {
+  };
+  // Selection mode: offer block j's max to this lane's row.
+  auto offer = [&](int j, float bmax) {
+    const uint64_t x = ((uint64_t)order_key(bmax) << 32) | (uint32_t)~(uint32_t)j;
+    const bool take = j < my_l && x > worst;
+    if (__builtin_amdgcn_ballot_w64(take) != 0) {
+      if (take) {
 #pragma unroll
-          for (int t = 0; t < kKeep; ++t)
-            if (t == wi) keep[t] = x;
-          worst = keep[0];
-          wi = 0;
+        for (int t = 0; t < kKeep; ++t)
+          if (t == wi) keep[t] = x;
+        worst = keep[0];
+        wi = 0;
 #pragma unroll
-          for (int t = 1; t < kKeep; ++t)
-            if (keep[t] < worst) {
-              worst = keep[t];
-              wi = t;
-            }
-        }
+        for (int t = 1; t < kKeep; ++t)
+          if (keep[t] < worst) {
+            worst = keep[t];
+            wi = t;
+          }
       }
-    } else {
+    }
+  };
+
+  if constexpr (SELECT) {
+    // Two blocks per barrier: blocks jj, jj + 1 in buffers 2 h, 2 h + 1 (h =
+    // pair parity); the next pair's tiles are loaded meanwhile and stored into
+    // the other half.
+    for (int jj = 0; jj < nj_live; jj += 2) {
+      const int h = (jj >> 1) & 1;
+      const bool more = jj + 2 < nj_live;
+      if (more) {
+        MSA_LOAD_TILE(j0 + jj + 2, pre)
+        MSA_LOAD_TILE(j0 + min(jj + 3, nj_live - 1), pre2)
+      }
+      asm volatile("" ::: "memory");
+      float best[NT / 2];
+      block_max(j0 + jj, ktile[2 * h], best);
+      offer(j0 + jj, best[0]);
+      if (jj + 1 < nj_live) {
+        block_max(j0 + jj + 1, ktile[2 * h + 1], best);
+        offer(j0 + jj + 1, best[0]);
+      }
+      asm volatile("" ::: "memory");
+      if (more) {
+        MSA_STORE_TILE(2 * (h ^ 1), pre)
+        MSA_STORE_TILE(2 * (h ^ 1) + 1, pre2)
+      }
+      __syncthreads();
+    }
+  } else {
+    for (int jj = 0; jj < nj_live; ++jj) {
+      const int j = j0 + jj;
+      if (jj + 1 < nj_live) { MSA_LOAD_TILE(j + 1, pre) }
+      // Compiler-only fences: keep the next tile's global loads before the
+      // compute and its LDS stores after it, so the loads fly during the MFMAs.
+      asm volatile("" ::: "memory");
+      float best[NT / 2];
+      block_max(j, ktile[jj & 1], best);
 #pragma unroll
       for (int p2 = 0; p2 < NT / 2; ++p2)
         stage[(wave * ROWS_W + 64 * p2 + lane) * kStageStride + jj] = best[p2];
+      asm volatile("" ::: "memory");
+      if (jj + 1 < nj_live) { MSA_STORE_TILE((jj & 1) ^ 1, pre) }
+      __syncthreads();
     }
-    asm volatile("" ::: "memory");
-    if (jj + 1 < nj_live) { MSA_STORE_TILE((jj & 1) ^ 1) }
-    __syncthreads();
   }
 
 #undef MSA_TILE_TID
