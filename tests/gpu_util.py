@@ -38,7 +38,10 @@ def inputs_for(w: synth.Workload, device="cuda"):
 def run_device(w, t, *, with_bm=True):
     res = {}
     if with_bm:
+        # The separate entry points: block scores, then the Top-k on them (the
+        # forward may fuse both into one kernel; both paths are compared).
         res["bm"] = msa.msa_index_scores(t["q_idx"], t["k_idx"], topk=w.topk)
+        res["idx_split"] = msa.msa_block_topk(res["bm"], seqlen_k=w.seqlen_k, topk=w.topk)
     out, lse, idx = msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk,
                                     return_lse=True, return_idx=True)
     res.update(out=out, lse=lse, idx=idx)
@@ -63,12 +66,15 @@ def compare(w, dev, ref, rows, *, check_bm=True, label=""):
             r = np.argwhere(bad)[0]
             msgs.append(f"{label} block scores differ at {int(bad.sum())} entries; first row {rows[r[0]]}"
                         f" block {r[1]}: {bm[r[0], r[1]]} vs {exp[r[0], r[1]]}")
-    idx = dev["idx"][torch.from_numpy(b), torch.from_numpy(g), torch.from_numpy(i)].cpu().numpy()
-    bad = (idx != ref["sel"]).any(axis=1)
-    if bad.any():
-        r = int(np.argwhere(bad)[0][0])
-        msgs.append(f"{label} selection differs on {int(bad.sum())} rows; first {rows[r]}: "
-                    f"{idx[r].tolist()} vs {ref['sel'][r].tolist()}")
+    for key, what in (("idx", "selection"), ("idx_split", "msa_block_topk selection")):
+        if key not in dev:
+            continue
+        idx = dev[key][torch.from_numpy(b), torch.from_numpy(g), torch.from_numpy(i)].cpu().numpy()
+        bad = (idx != ref["sel"]).any(axis=1)
+        if bad.any():
+            r = int(np.argwhere(bad)[0][0])
+            msgs.append(f"{label} {what} differs on {int(bad.sum())} rows; first {rows[r]}: "
+                        f"{idx[r].tolist()} vs {ref['sel'][r].tolist()}")
     out = dev["out"].float()
     heads = (g[:, None] * G + np.arange(G)[None, :])
     o = out[torch.from_numpy(b)[:, None], torch.from_numpy(i)[:, None], torch.from_numpy(heads)].cpu().numpy()

@@ -48,6 +48,10 @@ def test_prefill_workload_sampled_rows(name):
     t = inputs_for(w)
     print(f"[{name}] msa_forward", flush=True)
     dev = run_device(w, t)
+    # Every row: the forward's selection (fused with the scan here) equals the
+    # Top-k of the separately computed block scores.
+    n_diff = int((dev["idx"] != dev["idx_split"]).any(-1).sum())
+    assert n_diff == 0, f"{name}: fused and separate selections differ on {n_diff} rows"
     rows = stratified_rows(w)
     h = {k: to_u16(v) for k, v in t.items()}
     del t
