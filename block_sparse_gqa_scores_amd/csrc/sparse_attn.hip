@@ -44,6 +44,7 @@ constexpr size_t kPartBudget = size_t(16) << 30;  // bytes of partials per chunk
 constexpr int kBuildQueries = 256;   // queries per bucket-build workgroup
 constexpr int kHistBins = 8192;      // widest row whose histogram lives in LDS
 constexpr int kMinWindow = 2048;     // smallest query window (a multiple of kBuildQueries)
+constexpr long kMergePairRows = 1 << 16;  // from this many rows on, two merge rows per wave
 
 struct Params {
   const uint16_t* q;
@@ -482,93 +483,97 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
 // after the load), so a lane keeps kBatch x F 16-byte loads (16 at G <= 8) in
 // flight.
 template <int G>
-__global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse) {
+__global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse, int rows_per_wave) {
   constexpr int NF = G * kD / 8;            // 16-byte pieces (8 halves) per record
   constexpr int F = (NF + 63) / 64;         // pieces per lane
   constexpr int kBatch = F >= 8 ? 2 : (F >= 4 ? 4 : 8);  // records per batch of loads
   const int lane = threadIdx.x & 63;
-  const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= (long)p.B * p.H_kv * p.Qc) return;
-  const int il = (int)(r % p.Qc);
-  const int bg = (int)(r / p.Qc);
-  const int i = p.q0 + il;
-  if (i >= p.S_q) return;
-  const int b = bg / p.H_kv, g = bg - (bg / p.H_kv) * p.H_kv;
-  const int32_t* sel = p.idx + ((long)bg * p.S_q + i) * p.topk;
-  const int local = (i + p.S_k - p.S_q) / kBlock;  // entries past it are ignored
-  const long slot0 = slot_of(p, bg, il, 0);        // the row's topk slots are consecutive
+  // rows_per_wave consecutive rows per wave: the next row's loads start while
+  // the previous row's output stores drain.
+  for (int rk = 0; rk < rows_per_wave; ++rk) {
+    const long r = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * rows_per_wave + rk;
+    if (r >= (long)p.B * p.H_kv * p.Qc) break;
+    const int il = (int)(r % p.Qc);
+    const int bg = (int)(r / p.Qc);
+    const int i = p.q0 + il;
+    if (i >= p.S_q) continue;  // past the end of this (b, g); the next row may be valid
+    const int b = bg / p.H_kv, g = bg - (bg / p.H_kv) * p.H_kv;
+    const int32_t* sel = p.idx + ((long)bg * p.S_q + i) * p.topk;
+    const int local = (i + p.S_k - p.S_q) / kBlock;  // entries past it are ignored
+    const long slot0 = slot_of(p, bg, il, 0);        // the row's topk slots are consecutive
 
-  // The validity mask, statistics and records of a batch are all requested
-  // before any of them is used; the softmax max is kept online, one rescale
-  // per batch, so no pass over the statistics precedes the records.
-  const int je = lane < p.topk ? sel[lane] : -1;
-  const int hh = lane % G;
-  float M = neg_inf(), L = 0.f, acc[F][8];
-#pragma unroll
-  for (int u = 0; u < F; ++u)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[u][c] = 0.f;
-  unsigned long long valid = 0;
-  for (int e0 = 0; e0 < p.topk; e0 += kBatch) {
-    u32x4 x[kBatch][F];
-    float lse[kBatch], sc[kBatch];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const long slot = slot0 + min(e0 + k, p.topk - 1);
-      lse[k] = p.part_lse[slot * G + hh];
-      sc[k] = p.part_sc[slot * G + hh];
-      const u32x4* rec = reinterpret_cast<const u32x4*>(p.part_o + (size_t)slot * G * kD);
-#pragma unroll
-      for (int u = 0; u < F; ++u) x[k][u] = rec[min(lane + 64 * u, NF - 1)];
-    }
-    asm volatile("" ::: "memory");  // keep the loads above together
-    if (e0 == 0) valid = __builtin_amdgcn_ballot_w64(je >= 0 && je <= local);
-    // Entry e counts when its bit is set (wave-uniform); e past topk never is.
-    const unsigned bits = (unsigned)(valid >> e0) & ((1u << kBatch) - 1u);  // e0 < topk <= 64
-    if (bits == 0) continue;
-    float mb = neg_inf();
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k)
-      if ((bits >> k) & 1u) mb = __builtin_fmaxf(mb, lse[k]);
-    const float m_new = __builtin_fmaxf(M, mb);
-    const float alpha = __builtin_amdgcn_exp2f(M - m_new);  // 0 while M = -inf
-    M = m_new;
-    L *= alpha;
+    // The validity mask, statistics and records of a batch are all requested
+    // before any of them is used; the softmax max is kept online, one rescale
+    // per batch, so no pass over the statistics precedes the records.
+    const int je = lane < p.topk ? sel[lane] : -1;
+    const int hh = lane % G;
+    float M = neg_inf(), L = 0.f, acc[F][8];
 #pragma unroll
     for (int u = 0; u < F; ++u)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[u][c] *= alpha;
+      for (int c = 0; c < 8; ++c) acc[u][c] = 0.f;
+    unsigned long long valid = 0;
+    for (int e0 = 0; e0 < p.topk; e0 += kBatch) {
+      u32x4 x[kBatch][F];
+      float lse[kBatch], sc[kBatch];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      if (!((bits >> k) & 1u)) continue;  // wave-uniform
-      const float wl = __builtin_amdgcn_exp2f(lse[k] - M);
-      const float wx = wl * sc[k];
-      L += wl;
+      for (int k = 0; k < kBatch; ++k) {
+        const long slot = slot0 + min(e0 + k, p.topk - 1);
+        lse[k] = p.part_lse[slot * G + hh];
+        sc[k] = p.part_sc[slot * G + hh];
+        const u32x4* rec = reinterpret_cast<const u32x4*>(p.part_o + (size_t)slot * G * kD);
+#pragma unroll
+        for (int u = 0; u < F; ++u) x[k][u] = rec[min(lane + 64 * u, NF - 1)];
+      }
+      asm volatile("" ::: "memory");  // keep the loads above together
+      if (e0 == 0) valid = __builtin_amdgcn_ballot_w64(je >= 0 && je <= local);
+      // Entry e counts when its bit is set (wave-uniform); e past topk never is.
+      const unsigned bits = (unsigned)(valid >> e0) & ((1u << kBatch) - 1u);  // e0 < topk <= 64
+      if (bits == 0) continue;
+      float mb = neg_inf();
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if ((bits >> k) & 1u) mb = __builtin_fmaxf(mb, lse[k]);
+      const float m_new = __builtin_fmaxf(M, mb);
+      const float alpha = __builtin_amdgcn_exp2f(M - m_new);  // 0 while M = -inf
+      M = m_new;
+      L *= alpha;
 #pragma unroll
       for (int u = 0; u < F; ++u)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc[u][2 * c] += wx * f16_lo(x[k][u][c]);
-          acc[u][2 * c + 1] += wx * f16_hi(x[k][u][c]);
-        }
-    }
-  }
-  const float inv = 1.f / L;
+        for (int c = 0; c < 8; ++c) acc[u][c] *= alpha;
 #pragma unroll
-  for (int u = 0; u < F; ++u) {
-    const int f = lane + 64 * u;
-    if (f >= NF) continue;
-    // 16-byte piece f holds d = 32 dt + 8 rq + 0..7 of head hh, f = (dt * 4 + rq) * G + hh.
-    const int d = (f / G) * 8;
-    uint4 o;
-    o.x = pack_bf16x2(acc[u][0] * inv, acc[u][1] * inv);
-    o.y = pack_bf16x2(acc[u][2] * inv, acc[u][3] * inv);
-    o.z = pack_bf16x2(acc[u][4] * inv, acc[u][5] * inv);
-    o.w = pack_bf16x2(acc[u][6] * inv, acc[u][7] * inv);
-    *reinterpret_cast<uint4*>(p.out + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + d) = o;
-    if (with_lse && d == 0)
-      p.lse[((size_t)b * p.H_q + g * G + hh) * p.S_q + i] =
-          (M + __builtin_amdgcn_logf(L)) * 0.69314718055994530942f;
+      for (int k = 0; k < kBatch; ++k) {
+        if (!((bits >> k) & 1u)) continue;  // wave-uniform
+        const float wl = __builtin_amdgcn_exp2f(lse[k] - M);
+        const float wx = wl * sc[k];
+        L += wl;
+#pragma unroll
+        for (int u = 0; u < F; ++u)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            acc[u][2 * c] += wx * f16_lo(x[k][u][c]);
+            acc[u][2 * c + 1] += wx * f16_hi(x[k][u][c]);
+          }
+      }
+    }
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int u = 0; u < F; ++u) {
+      const int f = lane + 64 * u;
+      if (f >= NF) continue;
+      // 16-byte piece f holds d = 32 dt + 8 rq + 0..7 of head hh, f = (dt * 4 + rq) * G + hh.
+      const int d = (f / G) * 8;
+      uint4 o;
+      o.x = pack_bf16x2(acc[u][0] * inv, acc[u][1] * inv);
+      o.y = pack_bf16x2(acc[u][2] * inv, acc[u][3] * inv);
+      o.z = pack_bf16x2(acc[u][4] * inv, acc[u][5] * inv);
+      o.w = pack_bf16x2(acc[u][6] * inv, acc[u][7] * inv);
+      *reinterpret_cast<uint4*>(p.out + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + d) = o;
+      if (with_lse && d == 0)
+        p.lse[((size_t)b * p.H_q + g * G + hh) * p.S_q + i] =
+            (M + __builtin_amdgcn_logf(L)) * 0.69314718055994530942f;
+    }
   }
 }
 
@@ -663,8 +668,9 @@ static hipError_t launch_g(const AttnShape& s, const Layout& L, Params p, bool w
     mark(3, true, first, last);
     const long rows = (long)s.batch * s.H_kv * L.Qc;
     mark(4, false, first, last);
-    hipLaunchKernelGGL(merge_kernel<G>, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, st, p,
-                       with_lse ? 1 : 0);
+    const int rpw = rows >= kMergePairRows ? 2 : 1;
+    hipLaunchKernelGGL(merge_kernel<G>, dim3((unsigned)((rows + 4 * rpw - 1) / (4 * rpw))), dim3(kThreads), 0,
+                       st, p, with_lse ? 1 : 0, rpw);
     mark(4, true, first, last);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
