@@ -170,3 +170,73 @@ def forward(p: Problem, q, k, v, q_idx, k_idx, rows=None, threads=0):
     if rc:
         raise ValueError("oracle_forward rejected its arguments")
     return {"bm": bm, "sel": sel, "out": out, "lse": lse, "rows": rows}
+
+
+# ------------------------------------------------- block-mask selection format
+# Sparse Attention Part II, section 4.3: the blocks a query (block) visits are
+# flags packed 32 to an unsigned word; block j is bit j mod 32 of word
+# floor(j / 32), set by OR-ing 1 << (j mod 32) into that word.  A traversal
+# walks the words, takes each word's popcount as its number of active blocks
+# and the rank-th set bit (nth_set_bit) as the position of the rank-th one.
+# Bits past the last block stay zero.  Storage: 4 * ceil(n_blk / 32) bytes per
+# row, i.e. 4 T_r ceil(T_c / 32) per batch item and head for T_r row blocks.
+
+def mask_words(n_blk: int) -> int:
+    """32-bit words per row of a mask over n_blk blocks."""
+    return -(-n_blk // 32)
+
+
+def block_mask(sel, n_blk: int):
+    """Selections [..., k] (block indices, -1 = unused) -> masks
+    [..., ceil(n_blk / 32)] uint32, bit j mod 32 of word j // 32 per block j."""
+    sel = np.asarray(sel)
+    flat = sel.reshape(-1, sel.shape[-1]).astype(np.int64)
+    mask = np.zeros((flat.shape[0], mask_words(n_blk)), dtype=np.uint32)
+    r, e = np.nonzero((flat >= 0) & (flat < n_blk))
+    j = flat[r, e]
+    np.bitwise_or.at(mask, (r, j // 32), np.left_shift(np.uint32(1), (j % 32).astype(np.uint32)))
+    return mask.reshape(sel.shape[:-1] + (mask.shape[-1],))
+
+
+def popcount(word: int) -> int:
+    """Number of set bits of a 32-bit word."""
+    return sum((int(word) >> b) & 1 for b in range(32))
+
+
+def nth_set_bit(word: int, rank: int) -> int:
+    """Position of the rank-th (zero-based) set bit of a 32-bit word."""
+    seen = 0
+    for b in range(32):
+        if (int(word) >> b) & 1:
+            if seen == rank:
+                return b
+            seen += 1
+    raise ValueError("rank past the word's popcount")
+
+
+def mask_blocks(mask, cap: int):
+    """Masks [..., n_words] -> block lists [..., cap] int32: the set bits in
+    ascending block order (the traversal order), at most cap of them (the
+    lowest), padded with -1."""
+    mask = np.asarray(mask, dtype=np.uint32)
+    flat = mask.reshape(-1, mask.shape[-1])
+    n_rows, n_words = flat.shape
+    bits = (flat[:, :, None] >> np.arange(32, dtype=np.uint32)[None, None, :]) & 1  # [rows, words, 32]
+    on = bits.reshape(n_rows, n_words * 32).astype(bool)  # position 32 w + b, ascending
+    out = np.full((n_rows, cap), -1, dtype=np.int32)
+    r, j = np.nonzero(on)  # row-major: ascending j within each row
+    rank = np.arange(len(r)) - np.searchsorted(r, r)  # position of each set bit within its row
+    keep = rank < cap
+    out[r[keep], rank[keep]] = j[keep]
+    return out.reshape(mask.shape[:-1] + (cap,))
+
+
+def mask_blocks_by_traversal(mask_row, cap: int):
+    """One row, written as the section's loop: for each word, popcount, then
+    nth_set_bit for every rank.  Pure Python, for small cases."""
+    out = []
+    for w, word in enumerate(np.asarray(mask_row, dtype=np.uint32).tolist()):
+        for rank in range(popcount(word)):
+            out.append(32 * w + nth_set_bit(word, rank))
+    out = out[:cap]
+    return out + [-1] * (cap - len(out))
