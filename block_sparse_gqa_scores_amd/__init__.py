@@ -20,7 +20,8 @@ STATUS_NAMES = {0: "MSA_OK", 1: "MSA_ERR_NULL_PTR", 2: "MSA_ERR_INVALID_DIMS", 3
                 4: "MSA_ERR_MISALIGNED", 5: "MSA_ERR_WORKSPACE_TOO_SMALL", 6: "MSA_ERR_HIP"}
 ENTRY_INDEX_SCORES, ENTRY_BLOCK_TOPK, ENTRY_SPARSE_ATTN_FWD, ENTRY_FORWARD = 0, 1, 2, 3
 EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
-            "msa_forward_profiled", "msa_attn_chunks", "msa_workspace_bytes", "msa_status_str")
+            "msa_forward_profiled", "msa_attn_chunks", "msa_workspace_bytes", "msa_status_str",
+            "msa_block_mask", "msa_mask_blocks")
 STAGES = ("index_scores", "block_topk", "attn_build", "attn_partial", "attn_merge")
 
 
@@ -66,8 +67,10 @@ def lib():
         L.msa_forward.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_forward_profiled.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
                                            ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+        L.msa_block_mask.argtypes = [D, P, P, P]
+        L.msa_mask_blocks.argtypes = [D, P, P, P]
         for f in (L.msa_index_scores, L.msa_block_topk, L.msa_sparse_attn_fwd, L.msa_forward,
-                  L.msa_forward_profiled):
+                  L.msa_forward_profiled, L.msa_block_mask, L.msa_mask_blocks):
             f.restype = ctypes.c_int
         L.msa_attn_chunks.argtypes = [D]
         L.msa_attn_chunks.restype = ctypes.c_int
@@ -157,6 +160,38 @@ def msa_block_topk(block_scores, *, seqlen_k, topk=16, block_size=128, block_idx
     rc = lib().msa_block_topk(ctypes.byref(d), _ptr(block_scores), _ptr(block_idx),
                               _stream(block_scores.device))
     _check(rc, "msa_block_topk")
+    return block_idx
+
+
+def _selection_dims(B, Hkv, Sq, seqlen_k, topk, block_size):
+    return Dims.make(B, Sq, seqlen_k, Hkv, Hkv, 128, 128, block_size, topk, 1, 0.0)
+
+
+def msa_block_mask(block_idx, *, seqlen_k, block_size=128, mask=None):
+    """Block-mask form [B, H_kv, S_q, ceil(n_blk / 32)] (int32 tensor holding
+    uint32 words) of a selection [B, H_kv, S_q, topk]."""
+    import torch
+    B, Hkv, Sq, topk = block_idx.shape
+    d = _selection_dims(B, Hkv, Sq, seqlen_k, topk, block_size)
+    if mask is None:
+        mask = torch.empty((B, Hkv, Sq, -(-d.n_blk // 32)), dtype=torch.int32, device=block_idx.device)
+    rc = lib().msa_block_mask(ctypes.byref(d), _ptr(block_idx), _ptr(mask), _stream(block_idx.device))
+    _check(rc, "msa_block_mask")
+    return mask
+
+
+def msa_mask_blocks(mask, *, seqlen_k, topk=16, block_size=128, block_idx=None):
+    """Traversal of block masks [B, H_kv, S_q, n_words]: the set blocks in
+    ascending order, at most topk per row, -1 padded -> [B, H_kv, S_q, topk]."""
+    import torch
+    B, Hkv, Sq, nw = mask.shape
+    d = _selection_dims(B, Hkv, Sq, seqlen_k, topk, block_size)
+    if nw != -(-d.n_blk // 32):
+        raise ValueError("mask last dim must be ceil(ceil(seqlen_k / block_size) / 32)")
+    if block_idx is None:
+        block_idx = torch.empty((B, Hkv, Sq, topk), dtype=torch.int32, device=mask.device)
+    rc = lib().msa_mask_blocks(ctypes.byref(d), _ptr(mask), _ptr(block_idx), _stream(mask.device))
+    _check(rc, "msa_mask_blocks")
     return block_idx
 
 

@@ -24,6 +24,12 @@ hipError_t launch_index_select(const uint16_t* q_idx, const uint16_t* k_idx, int
 hipError_t launch_block_topk(const float* bm, int32_t* idx, int batch, int S_q, int S_k,
                              int H_kv, int n_blk, int topk, hipStream_t stream);
 
+// Block-mask form of selections (see block_mask.hip).
+hipError_t launch_block_mask(const int32_t* sel, uint32_t* mask, long n_rows, int topk, int n_blk,
+                             hipStream_t stream);
+hipError_t launch_mask_blocks(const uint32_t* mask, int32_t* sel, long n_rows, int n_blk, int cap,
+                              hipStream_t stream);
+
 // Sparse attention (see sparse_attn.hip).
 struct AttnShape {
   int batch, S_q, S_k, H_q, H_kv, n_blk, topk;

@@ -145,6 +145,28 @@ msa_status msa_block_topk(const msa_dims* d, const float* block_scores, int32_t*
                                          d->topk, static_cast<hipStream_t>(stream)));
 }
 
+msa_status msa_block_mask(const msa_dims* d, const int32_t* block_idx, uint32_t* mask,
+                          void* stream) {
+  msa_status st = check_dims(d, false, false);
+  if (st != MSA_OK || is_empty(*d)) return st;
+  if (!block_idx || !mask) return MSA_ERR_NULL_PTR;
+  if (!aligned16(block_idx) || !aligned16(mask)) return MSA_ERR_MISALIGNED;
+  const long rows = long(d->batch) * d->num_heads_kv * d->seqlen_q;
+  return from_hip(msa::launch_block_mask(block_idx, mask, rows, d->topk, int(n_blocks(*d)),
+                                         static_cast<hipStream_t>(stream)));
+}
+
+msa_status msa_mask_blocks(const msa_dims* d, const uint32_t* mask, int32_t* block_idx,
+                           void* stream) {
+  msa_status st = check_dims(d, false, false);
+  if (st != MSA_OK || is_empty(*d)) return st;
+  if (!block_idx || !mask) return MSA_ERR_NULL_PTR;
+  if (!aligned16(block_idx) || !aligned16(mask)) return MSA_ERR_MISALIGNED;
+  const long rows = long(d->batch) * d->num_heads_kv * d->seqlen_q;
+  return from_hip(msa::launch_mask_blocks(mask, block_idx, rows, int(n_blocks(*d)), d->topk,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 msa_status msa_sparse_attn_fwd(const msa_dims* d, const void* q, const void* k, const void* v,
                                const int32_t* block_idx, void* out, float* lse, void* ws,
                                size_t ws_bytes, void* stream) {

@@ -168,6 +168,33 @@ msa_status msa_forward(const msa_dims* dims, const void* q, const void* k,
                        void* out, float* lse, int32_t* block_idx_out, void* ws,
                        size_t ws_bytes, void* stream);
 
+/*
+ * Block-mask form of a selection (Sparse Attention Part II, section 4.3: the
+ * blocks a query visits kept as one flag per block, 32 flags to an unsigned
+ * word, block j at bit j mod 32 of word floor(j / 32)):
+ *
+ *   mask[b][g][i][w], w < ceil(n_blk / 32), n_blk = ceil(seqlen_k / block_size):
+ *   bit j mod 32 of word floor(j / 32) is 1 iff j appears in block_idx[b][g][i][0 .. topk-1].
+ *
+ * Entries equal to -1, or outside 0 .. n_blk-1, set nothing; bits past the
+ * last block are 0.  Storage: 4 * ceil(n_blk / 32) bytes per row.  Uses the
+ * dims' batch, seqlen_q, seqlen_k, num_heads_kv, block_size (128) and topk.
+ * Pointers are device pointers, 16-byte aligned; the call allocates nothing.
+ */
+msa_status msa_block_mask(const msa_dims* dims, const int32_t* block_idx,
+                          uint32_t* mask, void* stream);
+
+/*
+ * The traversal of the same section: for each row, walk the words in order;
+ * a word's popcount is its number of active blocks and the position of its
+ * rank-th set bit gives block 32 w + bit.  block_idx[b][g][i][0 .. topk-1]
+ * receives the blocks in ascending order, at most topk of them (the lowest
+ * ones when a row has more), then -1.  Bits past the last block are ignored.
+ * Same layouts and dims as msa_block_mask.
+ */
+msa_status msa_mask_blocks(const msa_dims* dims, const uint32_t* mask,
+                           int32_t* block_idx, void* stream);
+
 /* Internal stages of msa_forward, in launch order (for msa_forward_profiled). */
 typedef enum msa_stage {
   MSA_STAGE_INDEX_SCORES = 0,  /* index scores fused with the block max-pool */

@@ -55,6 +55,14 @@ def topk(d, bm=A, idx=A):
     return msa.lib().msa_block_topk(ctypes.byref(d), bm, idx, None)
 
 
+def bmask(d, idx=A, mask=A):
+    return msa.lib().msa_block_mask(None if d is None else ctypes.byref(d), idx, mask, None)
+
+
+def mblocks(d, mask=A, idx=A):
+    return msa.lib().msa_mask_blocks(None if d is None else ctypes.byref(d), mask, idx, None)
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=-1), 2), (dict(seqlen_q=600), 2), (dict(num_heads_q=7), 2), (dict(topk=0), 2),
     (dict(block_size=0), 2), (dict(num_heads_kv=0), 2), (dict(head_dim=0), 2),
@@ -89,6 +97,10 @@ def test_null_and_misaligned_pointers():
     assert scores(d, qi=MIS) == 4
     assert topk(d, idx=NULL) == 1
     assert topk(d, bm=MIS) == 4
+    assert bmask(None) == 1 and mblocks(None) == 1
+    assert bmask(d, idx=NULL) == 1 and bmask(d, mask=NULL) == 1
+    assert mblocks(d, mask=NULL) == 1 and mblocks(d, idx=NULL) == 1
+    assert bmask(d, idx=MIS) == 4 and mblocks(d, mask=MIS) == 4
 
 
 def _al(x):
@@ -131,7 +143,14 @@ def test_empty_problems_are_ok_without_pointers():
         assert attn(d, q=NULL, k=NULL, v=NULL, idx=NULL, out=NULL, ws=NULL, nbytes=0) == 0
         assert scores(d, qi=NULL, ki=NULL, bm=NULL) == 0
         assert topk(d, bm=NULL, idx=NULL) == 0
+        assert bmask(d, idx=NULL, mask=NULL) == 0 and mblocks(d, mask=NULL, idx=NULL) == 0
         assert msa.msa_workspace_bytes(d, msa.ENTRY_FORWARD) == 0
+
+
+def test_mask_entries_check_dims():
+    assert bmask(dims(topk=0)) == 2 and mblocks(dims(topk=0)) == 2
+    assert bmask(dims(block_size=64)) == 3 and mblocks(dims(causal=0)) == 3
+    assert bmask(dims(topk=65)) == 3 and mblocks(dims(seqlen_q=600)) == 2
 
 
 def test_size_limits():
