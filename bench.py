@@ -123,6 +123,34 @@ def fused_selection(w):
     return w.seqlen_q * w.heads_kv > 32 and w.topk <= 16
 
 
+def selection_mask_rates(w, t, steps):
+    """The block-mask form of the workload's selection (Sparse Attention Part
+    II, section 4.3): time msa_block_mask and msa_mask_blocks on the forward's
+    selection; bytes = what each call reads and writes."""
+    import torch
+
+    import block_sparse_gqa_scores_amd as msa
+
+    stream = torch.cuda.current_stream()
+    _, idx = msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk, return_idx=True)
+    mask = msa.msa_block_mask(idx, seqlen_k=w.seqlen_k)
+    back = torch.empty_like(idx)
+    torch.cuda.synchronize()
+    rows = w.batch * w.heads_kv * w.seqlen_q
+    idx_bytes, mask_bytes = rows * w.topk * 4, rows * (-(-w.n_blk // 32)) * 4
+    res = {"workload": f"{w.name} selection ({rows} rows of {w.topk} blocks, {w.n_blk} blocks per row)"}
+    for name, fn in (("block_mask", lambda: msa.msa_block_mask(idx, seqlen_k=w.seqlen_k, mask=mask)),
+                     ("mask_blocks", lambda: msa.msa_mask_blocks(mask, seqlen_k=w.seqlen_k, topk=w.topk,
+                                                                 block_idx=back))):
+        fn()
+        ms = time_loop(fn, steps, stream)
+        res[name] = {"ms": ms, "bytes": idx_bytes + mask_bytes,
+                     "GB/s": (idx_bytes + mask_bytes) / (ms * 1e-3) / 1e9}
+    torch.cuda.synchronize()
+    res["round_trip_exact"] = bool(torch.equal(back, idx))
+    return res
+
+
 def stage_work(w, chunks):
     """Algorithmic work of each stage per launch: (bound, amount, unit).  With
     the fused selection the Top-k runs inside the index stage and its own
@@ -288,6 +316,7 @@ def main():
         "algorithmic_flops": {"index": fi, "attention": fa},
         "stages": stages, "attn_chunks": chunks, "roofline": roof, "wall_s_timed": wall,
     }
+    res["selection_mask"] = selection_mask_rates(w, t, args.steps)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)

@@ -3,6 +3,8 @@
 // word, block j at bit j mod 32 of word floor(j / 32), bits past the last
 // block left zero; a traversal recovers the blocks from each word's popcount
 // and the position of its rank-th set bit.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -31,31 +33,36 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(const int32_t* __r
   mask[x] = word;
 }
 
-// One wave per row.  Lane l takes words l, l + 64, ...; a wave-wide prefix
-// sum of the words' popcounts gives each word's first output position, and
-// the lane then emits its word's set bits in rank order (the lowest set bit,
-// then clear it: the rank-th pass finds the rank-th set bit).  Positions past
-// `cap` are dropped; the rest of the row is padded with -1.  Bits past the
-// last block are ignored.
+// A wave takes 64 / SEG rows of at most SEG words each (SEG a power of two
+// <= 64; rows wider than 64 words loop over 64-word chunks with SEG = 64).
+// Inside a row's segment, lane l takes word l (then l + SEG, ...); a prefix
+// sum of the words' popcounts across the segment gives each word's first
+// output position, and the lane then emits its word's set bits in rank order
+// (the lowest set bit, then clear it: the rank-th pass finds the rank-th set
+// bit).  Positions past `cap` are dropped; the rest of the row is padded with
+// -1.  Bits past the last block are ignored.
+template <int SEG>
 __global__ __launch_bounds__(kThreads) void mask_blocks_kernel(const uint32_t* __restrict__ mask,
                                                                int32_t* __restrict__ sel,
                                                                long n_rows, int n_blk, int n_words, int cap) {
+  constexpr int RPW = 64 / SEG;  // rows per wave
   const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (row >= n_rows) return;  // wave-uniform
-  const uint32_t* m = mask + row * n_words;
-  int32_t* out = sel + row * cap;
-  int base = 0;  // set bits in the words already handled
-  for (int w0 = 0; w0 < n_words && base < cap; w0 += 64) {
-    const int w = w0 + lane;
-    uint32_t word = w < n_words ? m[w] : 0u;
+  const int sl = lane % SEG;     // lane within the row's segment
+  const long row = ((long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * RPW + lane / SEG;
+  const bool live = row < n_rows;
+  const uint32_t* m = mask + (live ? row : 0) * n_words;
+  int32_t* out = sel + (live ? row : 0) * cap;
+  int base = 0;  // set bits in the words already handled (the same in the whole segment)
+  for (int w0 = 0; w0 < n_words; w0 += SEG) {
+    const int w = w0 + sl;
+    uint32_t word = (live && w < n_words) ? m[w] : 0u;
     if (w == n_words - 1 && (n_blk & 31)) word &= (1u << (n_blk & 31)) - 1u;  // bits past the last block
     const int cnt = __popc(word);
-    int incl = cnt;  // inclusive prefix sum over the lanes
+    int incl = cnt;  // inclusive prefix sum over the segment
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
+    for (int o = 1; o < SEG; o <<= 1) {
+      const int t = __shfl_up(incl, o, SEG);
+      if (sl >= o) incl += t;
     }
     int pos = base + incl - cnt;
     while (word != 0u && pos < cap) {
@@ -63,9 +70,10 @@ __global__ __launch_bounds__(kThreads) void mask_blocks_kernel(const uint32_t* _
       out[pos++] = 32 * w + bit;
       word &= word - 1u;
     }
-    base += __shfl(incl, 63, 64);
+    base += __shfl(incl, SEG - 1, SEG);
   }
-  for (int e = min(base, cap) + lane; e < cap; e += 64) out[e] = -1;
+  if (live)
+    for (int e = min(base, cap) + sl; e < cap; e += SEG) out[e] = -1;
 }
 
 }  // namespace
@@ -82,9 +90,17 @@ hipError_t launch_block_mask(const int32_t* sel, uint32_t* mask, long n_rows, in
 hipError_t launch_mask_blocks(const uint32_t* mask, int32_t* sel, long n_rows, int n_blk, int cap,
                               hipStream_t stream) {
   const int n_words = (n_blk + 31) / 32;
-  const long grid = (n_rows + kThreads / 64 - 1) / (kThreads / 64);
-  hipLaunchKernelGGL(mask_blocks_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, mask, sel, n_rows,
-                     n_blk, n_words, cap);
+  auto go = [&](auto seg) {
+    constexpr int SEG = decltype(seg)::value;
+    const long rows_per_wg = (kThreads / 64) * (64 / SEG);
+    hipLaunchKernelGGL(mask_blocks_kernel<SEG>, dim3((unsigned)((n_rows + rows_per_wg - 1) / rows_per_wg)),
+                       dim3(kThreads), 0, stream, mask, sel, n_rows, n_blk, n_words, cap);
+  };
+  if (n_words <= 4) go(std::integral_constant<int, 4>{});
+  else if (n_words <= 8) go(std::integral_constant<int, 8>{});
+  else if (n_words <= 16) go(std::integral_constant<int, 16>{});
+  else if (n_words <= 32) go(std::integral_constant<int, 32>{});
+  else go(std::integral_constant<int, 64>{});
   return hipGetLastError();
 }
 
