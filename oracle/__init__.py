@@ -40,8 +40,9 @@ def _load():
         lib.oracle_select.argtypes = [P, P, ctypes.c_int64, P, P]
         lib.oracle_attention.argtypes = [P, P, P, P, P, ctypes.c_int64, P, P, P, ctypes.c_int]
         lib.oracle_forward.argtypes = [P, P, P, P, P, P, P, ctypes.c_int64, P, P, P, P, ctypes.c_int]
+        lib.oracle_kl_rows.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, P, ctypes.c_int]
         for f in (lib.oracle_block_scores, lib.oracle_select, lib.oracle_attention,
-                  lib.oracle_forward, lib.oracle_default_threads):
+                  lib.oracle_forward, lib.oracle_kl_rows, lib.oracle_default_threads):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -170,6 +171,27 @@ def forward(p: Problem, q, k, v, q_idx, k_idx, rows=None, threads=0):
     if rc:
         raise ValueError("oracle_forward rejected its arguments")
     return {"bm": bm, "sel": sel, "out": out, "lse": lse, "rows": rows}
+
+
+def kl_rows(p: Problem, q, k, q_idx, k_idx, sel, rows=None, threads=0):
+    """KL-alignment loss term of each listed row (Sparse Attention Part II,
+    section 3.2): KL(teacher || student) over the row's selected visible
+    tokens, teacher = the group's mean per-head attention probabilities,
+    student = softmax of the raw index scores.  The loss is the mean over
+    all N * H_kv rows."""
+    rows = _rows(p, rows)
+    qq = _u16(q, (p.batch, p.seqlen_q, p.heads_q, p.head_dim))
+    kk = _u16(k, (p.batch, p.seqlen_k, p.heads_kv, p.head_dim))
+    qi = _u16(q_idx, (p.batch, p.seqlen_q, p.heads_kv, p.index_dim))
+    ki = _u16(k_idx, (p.batch, p.seqlen_k, p.index_dim))
+    sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(len(rows), p.topk)
+    kl = np.empty(len(rows), dtype=np.float64)
+    d = p._c()
+    rc = _load().oracle_kl_rows(ctypes.byref(d), _ptr(qq), _ptr(kk), _ptr(qi), _ptr(ki), _ptr(rows),
+                                len(rows), _ptr(sel), _ptr(kl), threads or default_threads())
+    if rc:
+        raise ValueError("oracle_kl_rows rejected its arguments")
+    return kl
 
 
 # ------------------------------------------------- block-mask selection format

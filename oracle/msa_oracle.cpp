@@ -19,6 +19,11 @@
 //     (here: higher score first, then lower block index).
 //   MiniMax Sparse Attention (api.staik.se blog): the Top-k selects on raw
 //     scores (exp-free), per GQA group.
+//   Sparse Attention Part II, section 3.2, alignment loss: on the tokens of a
+//     row's selected blocks, KL(teacher || student) with the teacher the mean
+//     of the group's per-head attention probabilities (each head normalised
+//     over those tokens) and the student the softmax of the index token
+//     scores there; the loss averages the term over N * H_kv rows.
 //
 // Readings where the pages are silent (each also listed in the design notes):
 //   - index score = raw dot product (no scale, no activation);
@@ -167,6 +172,64 @@ void attention_row(const Dims& d, const uint16_t* q, const uint16_t* k,
   }
 }
 
+// Auxiliary loss of the index branch, forward value, for one (query, group)
+// row (Sparse Attention Part II, section 3.2): on the row's token set T (the
+// visible tokens of its selected blocks), the teacher P averages the group's
+// per-head attention probabilities, each head normalised over T; the student
+// P_idx is the softmax over T of the index token scores; the row's term is
+// KL(P || P_idx) = sum over T of P ln(P / P_idx).  Index scores enter the
+// softmax as raw dot products (the pages give them no scale; a reading).
+double kl_row(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* q_idx,
+              const uint16_t* k_idx, int64_t b, int64_t i, int64_t g, const int32_t* sel) {
+  const int64_t G = d.heads_q / d.heads_kv;
+  const int64_t D = d.head_dim;
+  const int64_t t = position(d, i);
+  const double scale =
+      d.softmax_scale != 0.0 ? d.softmax_scale : 1.0 / std::sqrt((double)D);
+  std::vector<int64_t> tokens;
+  for (int64_t e = 0; e < d.topk; ++e) {
+    if (sel[e] < 0) continue;
+    for (int64_t s = (int64_t)sel[e] * d.block_size;
+         s < ((int64_t)sel[e] + 1) * d.block_size && s <= t; ++s)
+      tokens.push_back(s);
+  }
+  const size_t n = tokens.size();
+  // Teacher: mean over the group's heads of each head's softmax over T.
+  std::vector<double> teacher(n, 0.0), a(n);
+  for (int64_t hh = 0; hh < G; ++hh) {
+    const uint16_t* qrow = q + ((b * d.seqlen_q + i) * d.heads_q + g * G + hh) * D;
+    double m = -std::numeric_limits<double>::infinity();
+    for (size_t x = 0; x < n; ++x) {
+      const uint16_t* krow = k + ((b * d.seqlen_k + tokens[x]) * d.heads_kv + g) * D;
+      double dot = 0.0;
+      for (int64_t c = 0; c < D; ++c) dot += widen_bf16(qrow[c]) * widen_bf16(krow[c]);
+      a[x] = dot * scale;
+      m = std::max(m, a[x]);
+    }
+    double sum = 0.0;
+    for (size_t x = 0; x < n; ++x) sum += std::exp(a[x] - m);
+    for (size_t x = 0; x < n; ++x) teacher[x] += std::exp(a[x] - m) / sum / (double)G;
+  }
+  // Student: softmax over T of the raw index scores.
+  std::vector<double> z(n);
+  const uint16_t* qi = q_idx + ((b * d.seqlen_q + i) * d.heads_kv + g) * d.index_dim;
+  double zm = -std::numeric_limits<double>::infinity();
+  for (size_t x = 0; x < n; ++x) {
+    const uint16_t* krow = k_idx + (b * d.seqlen_k + tokens[x]) * d.index_dim;
+    double dot = 0.0;
+    for (int64_t c = 0; c < d.index_dim; ++c) dot += widen_bf16(qi[c]) * widen_bf16(krow[c]);
+    z[x] = dot;
+    zm = std::max(zm, dot);
+  }
+  double zs = 0.0;
+  for (size_t x = 0; x < n; ++x) zs += std::exp(z[x] - zm);
+  const double log_zs = zm + std::log(zs);
+  double kl = 0.0;
+  for (size_t x = 0; x < n; ++x)
+    if (teacher[x] > 0.0) kl += teacher[x] * (std::log(teacher[x]) - (z[x] - log_zs));
+  return kl;
+}
+
 }  // namespace
 
 extern "C" {
@@ -255,6 +318,33 @@ int oracle_forward(const oracle_dims* od, const uint16_t* q, const uint16_t* k,
   rc = oracle_select(od, rows, n_rows, bm, sel);
   if (rc) return rc;
   return oracle_attention(od, q, k, v, rows, n_rows, sel, out, lse, threads);
+}
+
+// KL-alignment loss terms of the listed rows over their selections (section
+// 3.2); kl: n_rows doubles.  The loss is their mean over all N * H_kv rows.
+int oracle_kl_rows(const oracle_dims* od, const uint16_t* q, const uint16_t* k,
+                   const uint16_t* q_idx, const uint16_t* k_idx, const int64_t* rows,
+                   int64_t n_rows, const int32_t* sel, double* kl, int threads) {
+  const Dims* d = reinterpret_cast<const Dims*>(od);
+  if (!dims_ok(d) || !q || !k || !q_idx || !k_idx || !rows || !sel || !kl || n_rows < 0)
+    return -1;
+  const int64_t nb = n_blocks(*d);
+  for (int64_t r = 0; r < n_rows; ++r) {
+    if (!row_ok(*d, rows + 3 * r)) return -1;
+    const int64_t local = position(*d, rows[3 * r + 1]) / d->block_size;
+    bool has_local = false;
+    for (int64_t e = 0; e < d->topk; ++e) {
+      const int32_t j = sel[r * d->topk + e];
+      if (j < -1 || j >= nb || j > local) return -1;
+      has_local |= (j == local);
+    }
+    if (!has_local) return -1;
+  }
+  for_rows(n_rows, threads, [&](int64_t r) {
+    const int64_t* rw = rows + 3 * r;
+    kl[r] = kl_row(*d, q, k, q_idx, k_idx, rw[0], rw[1], rw[2], sel + r * d->topk);
+  });
+  return 0;
 }
 
 // Threads the oracle uses when asked for "all cores".
