@@ -49,4 +49,14 @@ hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint1
                               void* ws, size_t ws_bytes, hipStream_t stream,
                               const StageEvents* events = nullptr);
 
+// Writes n zero floats (a kernel, so the call can sit inside a graph capture).
+hipError_t launch_fill_zero(float* dst, long n, hipStream_t stream);
+
+// Alignment loss of the index branch, forward value (see sparse_attn.hip).
+size_t kl_loss_workspace(const AttnShape& s);
+hipError_t launch_kl_loss(const AttnShape& s, int D_idx, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* q_idx, const uint16_t* k_idx, const int32_t* idx,
+                          const float* lse, float* kl_rows, float* loss, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
 }  // namespace msa

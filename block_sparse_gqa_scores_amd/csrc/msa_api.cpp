@@ -117,6 +117,9 @@ size_t msa_workspace_bytes(const msa_dims* d, int entry) {
       if (is_empty(*d)) return 0;
       return forward_bm_bytes(*d) + align256(idx_bytes(*d)) +
              msa::sparse_attn_workspace(attn_shape(*d));
+    case MSA_ENTRY_KL_LOSS_FWD:
+      if (check_dims(d, true, true) != MSA_OK) return bad;
+      return is_empty(*d) ? 0 : msa::kl_loss_workspace(attn_shape(*d));
     default:
       return bad;
   }
@@ -184,6 +187,32 @@ msa_status msa_sparse_attn_fwd(const msa_dims* d, const void* q, const void* k, 
       s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), block_idx, static_cast<uint16_t*>(out), lse, ws, ws_bytes,
       static_cast<hipStream_t>(stream)));
+}
+
+msa_status msa_kl_loss_fwd(const msa_dims* d, const void* q, const void* k, const void* q_idx,
+                           const void* k_idx, const int32_t* block_idx, const float* lse,
+                           float* kl_rows, float* loss, void* ws, size_t ws_bytes, void* stream) {
+  msa_status st = check_dims(d, true, true);
+  if (st != MSA_OK) return st;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  if (is_empty(*d)) {
+    if (!loss) return MSA_OK;
+    if (!aligned16(loss)) return MSA_ERR_MISALIGNED;
+    return from_hip(msa::launch_fill_zero(loss, 1, strm));
+  }
+  if (!q || !k || !q_idx || !k_idx || !block_idx || !lse) return MSA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_idx) || !aligned16(k_idx) ||
+      !aligned16(block_idx) || !aligned16(lse) || (kl_rows && !aligned16(kl_rows)) ||
+      (loss && !aligned16(loss)))
+    return MSA_ERR_MISALIGNED;
+  const msa::AttnShape s = attn_shape(*d);
+  const size_t need = msa::kl_loss_workspace(s);
+  if (!ws || ws_bytes < need) return ws ? MSA_ERR_WORKSPACE_TOO_SMALL : MSA_ERR_NULL_PTR;
+  if (!aligned16(ws)) return MSA_ERR_MISALIGNED;
+  return from_hip(msa::launch_kl_loss(
+      s, d->index_dim, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx), block_idx, lse,
+      kl_rows, loss, ws, ws_bytes, strm));
 }
 
 namespace {

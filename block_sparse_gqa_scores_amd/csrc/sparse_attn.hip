@@ -70,6 +70,15 @@ struct Params {
   float* part_lse;       // [slot][G]: log2-sum-exp of the block's visible logits
   float* part_sc;        // [slot][G]: max |O_e| of the row
   uint16_t* part_o;      // [slot][G * D] fp16: O_e / max |O_e|, in record order (below)
+  // Alignment loss (kl_* kernels below).
+  const uint16_t* q_idx;
+  const uint16_t* k_idx;
+  const float* lse_in;   // [B][H_q][S_q] natural-log LSE of the main branch
+  float4* kl_rec;        // [slot]: (sum P, sum P ln P, sum P (z - m), m)
+  float* kl_l;           // [slot]: sum exp(z - m)
+  float* kl_rows;        // [B][H_kv][S_q] or null
+  float* kl_wsum;        // per merge workgroup: sum of its rows' terms
+  float* loss;           // or null
 };
 
 // Record order of one slot's G x D partial outputs.  The MFMA output puts
@@ -577,23 +586,309 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse,
   }
 }
 
+// ------------------------------------------------------------------------
+// Alignment loss of the index branch, forward value (Sparse Attention Part
+// II, section 3.2): for row (b, i, g) with token set T (the visible tokens of
+// its selected blocks),
+//   KL_row = sum_{x in T} P(x) ln(P(x) / Pidx(x)),
+//   P(x) = (1/G) sum_h exp(scale q_h . k_x - lse_h)   (each head normalised on T),
+//   Pidx = softmax over T of z(x) = q_idx . k_idx_x   (raw index scores),
+// and the loss is the mean of KL_row over the B * S_q * H_kv rows.  With
+// S = sum P, A = sum P ln P and, for any shift m, C = sum P (z - m) and
+// L = sum exp(z - m), the row term is A - C + S (m + ln L - ... ) rearranged
+// per block below; neither distribution is ever written out (the expansion
+// of the KL term the MSA kernel notes describe).
+//
+// The same edge buckets as the attention: a work item loads K_j and the index
+// keys of block j into LDS once and runs all its edges against them.  For an
+// edge (query i, block j) it leaves the record (S_j, A_j, C_j, m_j) and L_j
+// with m_j = max z over the block's visible tokens; a merge per row combines
+//   M = max m_j, L = sum_j L_j e^(m_j - M), LSE = M + ln L,
+//   KL_row = sum_j (A_j - C_j + S_j (LSE - m_j)).
+//
+// Scores are formed as S = Q K^T (query heads on MFMA rows, keys on lanes),
+// so the G heads of a query sit in registers of one lane (and of its partner
+// in the other half of the wave for G >= 8): the group mean of the teacher is
+// an in-lane sum.  The index scores use the same layout: the A operand holds
+// the query's index row once per head (G copies), which makes z(query, key)
+// land in the lanes that hold the teacher for (query, key).
+template <int G, int DIDX>
+__global__ __launch_bounds__(kThreads, 2) void kl_partial_kernel(Params p) {
+  constexpr int QW = 32 / G;                 // queries per wave sub-tile
+  constexpr int QT = kSubTiles * 4 * QW;     // edges per work item
+  constexpr int ICH = DIDX / 8;              // 16-byte chunks per index key
+  constexpr int RPS = G >= 8 ? G / 2 : G;    // registers per (query, key) in a lane
+  constexpr int NL = 16 / RPS;               // queries per lane
+  __shared__ u32x4 ktile[kBlock * 16];       // [key][16 chunks], swizzled
+  __shared__ u32x4 itile[kBlock * ICH];      // [key][ICH chunks], swizzled
+  __shared__ __align__(16) float s_lse[QT * G];  // log2(e) * lse of (edge, head)
+  __shared__ int32_t s_slot[QT];
+  __shared__ int32_t s_i[QT];
+
+  const int w = blockIdx.x;
+  if (w >= p.tile_off[p.NB]) return;  // uniform: past the last work item
+  const int2 item = p.work[w];
+  const int bucket = item.x;
+  const int start = item.y;
+  const int n_here = min(p.QT, p.counts[bucket] - start);
+  const int ebase = p.offsets[bucket] + start;
+  const int bgw = bucket / p.n_blk;
+  const int j = bucket - bgw * p.n_blk;
+  const int bg = bgw / p.n_win;
+  const int b = bg / p.H_kv;
+  const int g = bg - b * p.H_kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  // Edges past n_here repeat the last one (same inputs, same record).
+  for (int x = tid; x < QT; x += kThreads) {
+    const int sl = p.edges[ebase + min(x, n_here - 1)];
+    s_slot[x] = sl;
+    s_i[x] = p.q0 + (int)((sl / p.topk) % p.Qc);
+  }
+  for (int x = tid; x < QT * G; x += kThreads) {
+    const int e = x / G, hh = x - (x / G) * G;
+    const int sl = p.edges[ebase + min(e, n_here - 1)];
+    const int i = p.q0 + (int)((sl / p.topk) % p.Qc);
+    s_lse[x] = p.lse_in[((size_t)b * p.H_q + g * G + hh) * p.S_q + i] * kLog2e;
+  }
+  {
+    const size_t row_stride = (size_t)p.H_kv * kD;
+    const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int qd = it * kThreads + tid;
+      const int row = qd >> 4, c = qd & 15;
+      // Keys past S_k are masked for every query; a clamped row is read.
+      const int s = min(j * kBlock + row, p.S_k - 1);
+      ktile[row * 16 + (c ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * c);
+    }
+    const uint16_t* ib = p.k_idx + (size_t)b * p.S_k * DIDX;
+#pragma unroll
+    for (int it = 0; it < kBlock * ICH / kThreads; ++it) {
+      const int qd = it * kThreads + tid;
+      const int row = qd / ICH, c = qd % ICH;
+      const int s = min(j * kBlock + row, p.S_k - 1);
+      itile[row * ICH + (c ^ (row & (ICH - 1)))] = *reinterpret_cast<const u32x4*>(ib + (size_t)s * DIDX + 8 * c);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int off = p.S_k - p.S_q;
+  const int n = lane & 31;                       // key column of this lane / A row
+  const int qm = n / G, hm = n - (n / G) * G;    // A row: query qm of the sub-tile, head hm
+  const float c = p.scale_log2;
+  const float invG = 1.f / G;
+
+  // Query (within the sub-tile) of query slot l of this lane: the D rows
+  // 8 (r / 4) + 4 h + r % 4 for r = l RPS .. l RPS + RPS - 1.
+  auto q_of = [&](int l) {
+    const int r0 = l * RPS;
+    return (8 * (r0 >> 2) + 4 * h + (r0 & 3)) / G;
+  };
+  auto load_q = [&](u32x4* dq, int i) {
+    const uint16_t* qrow = p.q + (((size_t)b * p.S_q + i) * p.H_q + g * G + hm) * kD + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) dq[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
+  };
+  auto load_qi = [&](u32x4* di, int i) {
+    const uint16_t* irow = p.q_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < DIDX / 16; ++ks) di[ks] = *reinterpret_cast<const u32x4*>(irow + 16 * ks);
+  };
+
+  u32x4 qb[8], ib[DIDX / 16];
+  load_q(qb, s_i[wave * QW + qm]);
+  load_qi(ib, s_i[wave * QW + qm]);
+  for (int sub = 0; sub < n_here; sub += 4 * QW) {
+    const int e0 = sub + wave * QW;  // first edge of this wave's sub-tile
+    if (e0 >= n_here) break;         // wave-uniform
+    const int i_next = s_i[min(e0 + 4 * QW, QT - QW) + qm];
+
+    float lse2[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 v = *reinterpret_cast<const float4*>(&s_lse[e0 * G + 8 * r4 + 4 * h]);
+      lse2[4 * r4 + 0] = v.x; lse2[4 * r4 + 1] = v.y; lse2[4 * r4 + 2] = v.z; lse2[4 * r4 + 3] = v.w;
+    }
+    int tq[NL];
+#pragma unroll
+    for (int l = 0; l < NL; ++l) tq[l] = s_i[e0 + q_of(l)] + off;
+    // Any key of the block past any query of the sub-tile: mask needed.
+    const bool masked = __builtin_amdgcn_ballot_w64(j * kBlock + kBlock - 1 > s_i[e0 + qm] + off) != 0;
+
+    // Index scores first; the index rows of the next sub-tile load meanwhile.
+    float pt[4][NL], zv[4][NL];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int krow = nt * 32 + n;
+      f32x16 za = zero16();
+#pragma unroll
+      for (int ks = 0; ks < DIDX / 16; ++ks)
+        za = mfma32x32x16(ib[ks], itile[krow * ICH + ((2 * ks + h) ^ (krow & (ICH - 1)))], za);
+#pragma unroll
+      for (int l = 0; l < NL; ++l) zv[nt][l] = za[l * RPS];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    load_qi(ib, i_next);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int krow = nt * 32 + n;
+      f32x16 sa = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        sa = mfma32x32x16(qb[ks], ktile[krow * 16 + ((2 * ks + h) ^ (krow & 15))], sa);
+      const int key = j * kBlock + krow;
+#pragma unroll
+      for (int l = 0; l < NL; ++l) {
+        float acc = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < RPS; ++rr) {
+          const int r = l * RPS + rr;
+          float x = sa[r];
+          if (masked && key > tq[l]) x = neg_inf();
+          acc += __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -lse2[r]));
+        }
+        pt[nt][l] = acc;
+      }
+      // One key tile at a time: keeps the live accumulators to two.
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (G >= 8) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int l = 0; l < NL; ++l) pt[nt][l] += swap_halves(pt[nt][l]);
+    }
+    load_q(qb, i_next);  // lands while the statistics below are reduced
+
+    // Per query: max of z over the visible keys, then the four sums.  For
+    // G >= 8 both halves hold the same (query, key) values: half h takes the
+    // key tiles 2h and 2h + 1 and the sums run over all 64 lanes.
+    constexpr int NT = G >= 8 ? 2 : 4;
+    constexpr int WIDTH = G >= 8 ? 64 : 32;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      float P[NT], Z[NT];
+      bool vis[NT];
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        const int nt = G >= 8 ? 2 * h + u : u;
+        if constexpr (G >= 8) {
+          P[u] = (h ? pt[2 + u][l] : pt[u][l]) * invG;
+          Z[u] = h ? zv[2 + u][l] : zv[u][l];
+        } else {
+          P[u] = pt[u][l] * invG;
+          Z[u] = zv[u][l];
+        }
+        vis[u] = j * kBlock + nt * 32 + n <= tq[l];
+      }
+      float mz = neg_inf();
+#pragma unroll
+      for (int u = 0; u < NT; ++u) if (vis[u]) mz = __builtin_fmaxf(mz, Z[u]);
+#pragma unroll
+      for (int o = 1; o < WIDTH; o <<= 1) mz = __builtin_fmaxf(mz, __shfl_xor(mz, o, 64));
+      float sS = 0.f, sA = 0.f, sC = 0.f, sL = 0.f;
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        const float d = Z[u] - mz;
+        sS += P[u];
+        sA += P[u] > 1e-30f ? P[u] * __builtin_amdgcn_logf(P[u]) : 0.f;
+        sC += P[u] > 0.f ? P[u] * d : 0.f;
+        sL += vis[u] ? __builtin_amdgcn_exp2f(d * kLog2e) : 0.f;
+      }
+#pragma unroll
+      for (int o = 1; o < WIDTH; o <<= 1) {
+        sS += __shfl_xor(sS, o, 64);
+        sA += __shfl_xor(sA, o, 64);
+        sC += __shfl_xor(sC, o, 64);
+        sL += __shfl_xor(sL, o, 64);
+      }
+      if (n == 0 && (G < 8 || h == 0)) {
+        const int sl = s_slot[e0 + q_of(l)];
+        p.kl_rec[sl] = make_float4(sS, sA * 0.69314718055994530942f, sC, mz);
+        p.kl_l[sl] = sL;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Row terms and the loss.  One thread per row (b, g, i); the records of its
+// selected blocks are combined online:
+//   M running max of m_j, L = sum L_j e^(m_j - M), U = sum S_j (m_j - M),
+//   KL_row = sum (A_j - C_j) - U + (sum S_j) ln L.
+// Each workgroup leaves the sum of its rows' terms; kl_total_kernel adds those
+// in a fixed order, so the loss is identical from run to run.
+__global__ __launch_bounds__(256) void kl_merge_kernel(Params p) {
+  __shared__ float red[256];
+  const long r = (long)blockIdx.x * 256 + threadIdx.x;
+  const long rows = (long)p.B * p.H_kv * p.S_q;
+  float kl = 0.f;
+  if (r < rows) {
+    const int i = (int)(r % p.S_q);
+    const int local = (i + p.S_k - p.S_q) / kBlock;
+    const int32_t* sel = p.idx + r * p.topk;
+    float M = neg_inf(), L = 0.f, U = 0.f, S = 0.f, AC = 0.f;
+    constexpr float kLog2e = 1.4426950408889634f;
+    for (int e = 0; e < p.topk; ++e) {
+      const int jj = sel[e];
+      if (jj < 0 || jj > local) continue;
+      const float4 rec = p.kl_rec[r * p.topk + e];
+      const float lj = p.kl_l[r * p.topk + e];
+      if (rec.w > M) {  // rescale what was summed against the old maximum
+        if (M != neg_inf()) {
+          L *= __builtin_amdgcn_exp2f((M - rec.w) * kLog2e);
+          U += S * (M - rec.w);
+        }
+        M = rec.w;
+      }
+      const float dm = rec.w - M;
+      L += lj * __builtin_amdgcn_exp2f(dm * kLog2e);
+      U += rec.x * dm;
+      S += rec.x;
+      AC += rec.y - rec.z;
+    }
+    kl = AC - U + S * (__builtin_amdgcn_logf(L) * 0.69314718055994530942f);
+    if (p.kl_rows) p.kl_rows[r] = kl;
+  }
+  red[threadIdx.x] = kl;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) p.kl_wsum[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void kl_total_kernel(Params p, int n_wg, float inv_rows) {
+  __shared__ float red[256];
+  float s = 0.f;
+  for (int x = threadIdx.x; x < n_wg; x += 256) s += p.kl_wsum[x];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *p.loss = red[0] * inv_rows;
+}
+
 struct Layout {
   int Qc, QT, n_scan_wg;
   long NB, E, T;
   int W, n_win;
   size_t counts, cursor, offsets, tile_off, blk_sums, edges, work, part_lse, part_sc, part_o, total;
+  size_t kl_rec, kl_l, kl_wsum;  // alignment-loss layout only
+  int n_kl_wg;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-Layout make_layout(const AttnShape& s) {
-  Layout L{};
-  const int G = s.H_q / s.H_kv;
-  L.QT = kSubTiles * 4 * (32 / G);
-  const size_t per_query = (size_t)s.batch * s.H_kv * s.topk * ((size_t)G * (kD * 2 + 8) + 8 + 4);
-  long qc = (long)(kPartBudget / per_query);
-  if (qc >= 128) qc -= qc % 128;
-  L.Qc = (int)std::max(1L, std::min<long>(qc, s.S_q));
+// Bucket geometry and the build arrays for a chunk of Qc queries; returns the
+// offset past them.
+size_t layout_build(Layout& L, const AttnShape& s) {
   // Window: about QT edges per (window, block) bucket at the chunk's mean
   // number of visible blocks, at least kMinWindow queries; the whole chunk
   // when that exceeds it.
@@ -614,6 +909,18 @@ Layout make_layout(const AttnShape& s) {
   L.blk_sums = o; o = align256(o + (size_t)L.n_scan_wg * 8);
   L.edges = o;    o = align256(o + L.E * 4);
   L.work = o;     o = align256(o + L.T * 8);
+  return o;
+}
+
+Layout make_layout(const AttnShape& s) {
+  Layout L{};
+  const int G = s.H_q / s.H_kv;
+  L.QT = kSubTiles * 4 * (32 / G);
+  const size_t per_query = (size_t)s.batch * s.H_kv * s.topk * ((size_t)G * (kD * 2 + 8) + 8 + 4);
+  long qc = (long)(kPartBudget / per_query);
+  if (qc >= 128) qc -= qc % 128;
+  L.Qc = (int)std::max(1L, std::min<long>(qc, s.S_q));
+  size_t o = layout_build(L, s);
   L.part_lse = o; o = align256(o + (size_t)L.E * G * 4);
   L.part_sc = o;  o = align256(o + (size_t)L.E * G * 4);
   L.part_o = o;   o = align256(o + (size_t)L.E * G * kD * 2);
@@ -621,9 +928,62 @@ Layout make_layout(const AttnShape& s) {
   return L;
 }
 
+// The alignment loss keeps 20 bytes per edge, so one chunk covers all queries.
+Layout make_kl_layout(const AttnShape& s) {
+  Layout L{};
+  const int G = s.H_q / s.H_kv;
+  L.QT = kSubTiles * 4 * (32 / G);
+  L.Qc = s.S_q;
+  size_t o = layout_build(L, s);
+  const long rows = (long)s.batch * s.H_kv * s.S_q;
+  L.n_kl_wg = (int)((rows + 255) / 256);
+  L.kl_rec = o;  o = align256(o + (size_t)L.E * 16);
+  L.kl_l = o;    o = align256(o + (size_t)L.E * 4);
+  L.kl_wsum = o; o = align256(o + (size_t)L.n_kl_wg * 4);
+  L.total = o;
+  return L;
+}
+
 int grid_cap(long n, int per) {
   long g = (n + per - 1) / per;
   return (int)std::max(1L, std::min(g, 65536L));
+}
+
+// Edge buckets of the chunk starting at p.q0: counts, scans, scatter.
+void launch_build(const AttnShape& s, const Layout& L, const Params& p, hipStream_t st) {
+  const long slots = (long)s.batch * s.H_kv * L.Qc * s.topk;
+  hipLaunchKernelGGL(zero_kernel, dim3(grid_cap(L.NB, 256)), dim3(256), 0, st, p.counts, L.NB);
+  hipLaunchKernelGGL(zero_kernel, dim3(grid_cap(L.NB, 256)), dim3(256), 0, st, p.cursor, L.NB);
+  const bool lds_hist = s.n_blk <= kHistBins;
+  const long build_grid = (long)s.batch * s.H_kv * ((L.Qc + kBuildQueries - 1) / kBuildQueries);
+  if (lds_hist)
+    hipLaunchKernelGGL(bucket_count_kernel, dim3((unsigned)build_grid), dim3(256), s.n_blk * 4, st, p);
+  else
+    hipLaunchKernelGGL(count_kernel, dim3(grid_cap(slots, 256)), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(scan_local_kernel, dim3(L.n_scan_wg), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(scan_blocks_kernel, dim3(1), dim3(256), 0, st, p, L.n_scan_wg);
+  hipLaunchKernelGGL(scan_add_kernel, dim3(L.n_scan_wg), dim3(256), 0, st, p);
+  if (lds_hist)
+    hipLaunchKernelGGL(bucket_fill_kernel, dim3((unsigned)build_grid), dim3(256), s.n_blk * 8, st, p);
+  else
+    hipLaunchKernelGGL(fill_kernel, dim3(grid_cap(slots, 256)), dim3(256), 0, st, p);
+}
+
+Params base_params(const AttnShape& s, const Layout& L, char* base, const int32_t* idx) {
+  Params p{};
+  p.idx = idx;
+  p.B = s.batch; p.S_q = s.S_q; p.S_k = s.S_k; p.H_q = s.H_q; p.H_kv = s.H_kv;
+  p.G = s.H_q / s.H_kv; p.n_blk = s.n_blk; p.topk = s.topk;
+  p.Qc = L.Qc; p.NB = (int)L.NB; p.QT = L.QT; p.scale_log2 = s.scale_log2;
+  p.W = L.W; p.n_win = L.n_win;
+  p.counts = reinterpret_cast<int32_t*>(base + L.counts);
+  p.cursor = reinterpret_cast<int32_t*>(base + L.cursor);
+  p.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  p.tile_off = reinterpret_cast<int32_t*>(base + L.tile_off);
+  p.blk_sums = reinterpret_cast<int32_t*>(base + L.blk_sums);
+  p.edges = reinterpret_cast<int32_t*>(base + L.edges);
+  p.work = reinterpret_cast<int2*>(base + L.work);
+  return p;
 }
 
 }  // namespace
@@ -646,22 +1006,7 @@ static hipError_t launch_g(const AttnShape& s, const Layout& L, Params p, bool w
     p.q0 = q0;
     const bool first = q0 == 0, last = q0 + L.Qc >= s.S_q;
     mark(2, false, first, last);
-    const long slots = (long)s.batch * s.H_kv * L.Qc * s.topk;
-    hipLaunchKernelGGL(zero_kernel, dim3(grid_cap(L.NB, 256)), dim3(256), 0, st, p.counts, L.NB);
-    hipLaunchKernelGGL(zero_kernel, dim3(grid_cap(L.NB, 256)), dim3(256), 0, st, p.cursor, L.NB);
-    const bool lds_hist = s.n_blk <= kHistBins;
-    const long build_grid = (long)s.batch * s.H_kv * ((L.Qc + kBuildQueries - 1) / kBuildQueries);
-    if (lds_hist)
-      hipLaunchKernelGGL(bucket_count_kernel, dim3((unsigned)build_grid), dim3(256), s.n_blk * 4, st, p);
-    else
-      hipLaunchKernelGGL(count_kernel, dim3(grid_cap(slots, 256)), dim3(256), 0, st, p);
-    hipLaunchKernelGGL(scan_local_kernel, dim3(L.n_scan_wg), dim3(256), 0, st, p);
-    hipLaunchKernelGGL(scan_blocks_kernel, dim3(1), dim3(256), 0, st, p, L.n_scan_wg);
-    hipLaunchKernelGGL(scan_add_kernel, dim3(L.n_scan_wg), dim3(256), 0, st, p);
-    if (lds_hist)
-      hipLaunchKernelGGL(bucket_fill_kernel, dim3((unsigned)build_grid), dim3(256), s.n_blk * 8, st, p);
-    else
-      hipLaunchKernelGGL(fill_kernel, dim3(grid_cap(slots, 256)), dim3(256), 0, st, p);
+    launch_build(s, L, p, st);
     mark(2, true, first, last);
     mark(3, false, first, last);
     hipLaunchKernelGGL(attn_partial_kernel<G>, dim3((unsigned)L.T), dim3(kThreads), 0, st, p);
@@ -685,19 +1030,8 @@ hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint1
   const Layout L = make_layout(s);
   if (ws_bytes < L.total) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
-  Params p{};
-  p.q = q; p.k = k; p.v = v; p.idx = idx; p.out = out; p.lse = lse;
-  p.B = s.batch; p.S_q = s.S_q; p.S_k = s.S_k; p.H_q = s.H_q; p.H_kv = s.H_kv;
-  p.G = s.H_q / s.H_kv; p.n_blk = s.n_blk; p.topk = s.topk;
-  p.Qc = L.Qc; p.NB = (int)L.NB; p.QT = L.QT; p.scale_log2 = s.scale_log2;
-  p.W = L.W; p.n_win = L.n_win;
-  p.counts = reinterpret_cast<int32_t*>(base + L.counts);
-  p.cursor = reinterpret_cast<int32_t*>(base + L.cursor);
-  p.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
-  p.tile_off = reinterpret_cast<int32_t*>(base + L.tile_off);
-  p.blk_sums = reinterpret_cast<int32_t*>(base + L.blk_sums);
-  p.edges = reinterpret_cast<int32_t*>(base + L.edges);
-  p.work = reinterpret_cast<int2*>(base + L.work);
+  Params p = base_params(s, L, base, idx);
+  p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
   p.part_lse = reinterpret_cast<float*>(base + L.part_lse);
   p.part_sc = reinterpret_cast<float*>(base + L.part_sc);
   p.part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
@@ -709,6 +1043,72 @@ hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint1
     case 8: return launch_g<8>(s, L, p, with_lse, stream, events);
     case 16: return launch_g<16>(s, L, p, with_lse, stream, events);
     case 32: return launch_g<32>(s, L, p, with_lse, stream, events);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace msa
+
+namespace msa {
+
+namespace {
+__global__ void fill_zero_kernel(float* a, long n) {
+  for (long x = (long)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (long)gridDim.x * blockDim.x)
+    a[x] = 0.f;
+}
+}  // namespace
+
+hipError_t launch_fill_zero(float* dst, long n, hipStream_t stream) {
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_cap(n, 256)), dim3(256), 0, stream, dst, n);
+  return hipGetLastError();
+}
+
+size_t kl_loss_workspace(const AttnShape& s) { return make_kl_layout(s).total; }
+
+namespace {
+template <int G, int DIDX>
+hipError_t launch_kl_g(const AttnShape& s, const Layout& L, const Params& p, hipStream_t st) {
+  launch_build(s, L, p, st);
+  hipLaunchKernelGGL((kl_partial_kernel<G, DIDX>), dim3((unsigned)L.T), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(kl_merge_kernel, dim3((unsigned)L.n_kl_wg), dim3(256), 0, st, p);
+  if (p.loss) {
+    const double rows = (double)s.batch * s.H_kv * s.S_q;
+    hipLaunchKernelGGL(kl_total_kernel, dim3(1), dim3(256), 0, st, p, L.n_kl_wg, (float)(1.0 / rows));
+  }
+  return hipGetLastError();
+}
+
+template <int DIDX>
+hipError_t launch_kl_d(const AttnShape& s, const Layout& L, const Params& p, hipStream_t st) {
+  switch (p.G) {
+    case 1: return launch_kl_g<1, DIDX>(s, L, p, st);
+    case 2: return launch_kl_g<2, DIDX>(s, L, p, st);
+    case 4: return launch_kl_g<4, DIDX>(s, L, p, st);
+    case 8: return launch_kl_g<8, DIDX>(s, L, p, st);
+    case 16: return launch_kl_g<16, DIDX>(s, L, p, st);
+    case 32: return launch_kl_g<32, DIDX>(s, L, p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace
+
+hipError_t launch_kl_loss(const AttnShape& s, int D_idx, const uint16_t* q, const uint16_t* k,
+                          const uint16_t* q_idx, const uint16_t* k_idx, const int32_t* idx,
+                          const float* lse, float* kl_rows, float* loss, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  const Layout L = make_kl_layout(s);
+  if (ws_bytes < L.total) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(ws);
+  Params p = base_params(s, L, base, idx);
+  p.q = q; p.k = k; p.q_idx = q_idx; p.k_idx = k_idx; p.lse_in = lse;
+  p.kl_rec = reinterpret_cast<float4*>(base + L.kl_rec);
+  p.kl_l = reinterpret_cast<float*>(base + L.kl_l);
+  p.kl_wsum = reinterpret_cast<float*>(base + L.kl_wsum);
+  p.kl_rows = kl_rows;
+  p.loss = loss;
+  switch (D_idx) {
+    case 64: return launch_kl_d<64>(s, L, p, stream);
+    case 128: return launch_kl_d<128>(s, L, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -36,7 +36,8 @@
  *     MSA_ERR_HIP.  Faults inside kernels surface at the caller's next
  *     synchronisation, as for any asynchronous HIP work.
  *   - Results are bit-identical from run to run.
- *   - batch == 0 or seqlen_q == 0 is an empty problem: MSA_OK, no launch.
+ *   - batch == 0 or seqlen_q == 0 is an empty problem: MSA_OK, no launch
+ *     (except msa_kl_loss_fwd, which writes its loss of 0).
  *
  * Supported on this device path: causal = 1, head_dim = 128,
  * index_dim in {64, 128}, block_size = 128, 1 <= topk <= 64,
@@ -83,7 +84,8 @@ typedef enum msa_entry {
   MSA_ENTRY_INDEX_SCORES = 0,
   MSA_ENTRY_BLOCK_TOPK = 1,
   MSA_ENTRY_SPARSE_ATTN_FWD = 2,
-  MSA_ENTRY_FORWARD = 3
+  MSA_ENTRY_FORWARD = 3,
+  MSA_ENTRY_KL_LOSS_FWD = 4
 } msa_entry;
 
 /*
@@ -194,6 +196,37 @@ msa_status msa_block_mask(const msa_dims* dims, const int32_t* block_idx,
  */
 msa_status msa_mask_blocks(const msa_dims* dims, const uint32_t* mask,
                            int32_t* block_idx, void* stream);
+
+/*
+ * Alignment loss of the index branch, forward value (Sparse Attention Part
+ * II, section 3.2: after the dense warm-up, the index projections are trained
+ * by a KL term over the tokens of the selected blocks; the target is the
+ * group's mean main-branch distribution and is not differentiated).  For row
+ * (b, g, i) with T_i as in msa_sparse_attn_fwd:
+ *
+ *   P(s)    = (1/G) sum_{h in group g} exp(scale * q[b][i][h] . k[b][s][g] - lse[b][h][i])
+ *   Pidx(s) = softmax over s in T_i of z(s) = q_idx[b][i][g] . k_idx[b][s]
+ *   kl_rows[b][g][i] = sum_{s in T_i} P(s) ln(P(s) / Pidx(s))
+ *   *loss = (1 / (B * S_q * H_kv)) * sum of kl_rows
+ *
+ * G = H_q / H_kv.  The index score z is the raw dot product (no scale), the
+ * same token score that msa_index_scores max-pools.  `lse` is the main
+ * branch's log-sum-exp over the same selection, exactly as msa_forward or
+ * msa_sparse_attn_fwd return it ([B][H_q][S_q], natural log); it normalises
+ * each head's probabilities on T_i, so neither distribution is formed in
+ * memory.  block_idx follows the rules of msa_sparse_attn_fwd.  kl_rows
+ * ([B][H_kv][S_q] fp32) and loss (one fp32) are each optional (NULL skips
+ * it); the loss is summed in a fixed order, so it is identical from run to
+ * run.  `ws` holds msa_workspace_bytes(dims, MSA_ENTRY_KL_LOSS_FWD) bytes
+ * (edge lists and 20 bytes per selected block per row); contents on entry do
+ * not matter.  An empty problem writes *loss = 0 when loss is not NULL.
+ * Uses every field of dims (both branches).
+ */
+msa_status msa_kl_loss_fwd(const msa_dims* dims, const void* q, const void* k,
+                           const void* q_idx, const void* k_idx,
+                           const int32_t* block_idx, const float* lse,
+                           float* kl_rows, float* loss, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /* Internal stages of msa_forward, in launch order (for msa_forward_profiled). */
 typedef enum msa_stage {

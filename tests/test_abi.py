@@ -63,6 +63,11 @@ def mblocks(d, mask=A, idx=A):
     return msa.lib().msa_mask_blocks(None if d is None else ctypes.byref(d), mask, idx, None)
 
 
+def kl(d, q=A, k=A, qi=A, ki=A, idx=A, lse=A, rows=A, loss=A, ws=A, nbytes=1 << 40):
+    return msa.lib().msa_kl_loss_fwd(None if d is None else ctypes.byref(d), q, k, qi, ki, idx, lse,
+                                     rows, loss, ws, nbytes, None)
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=-1), 2), (dict(seqlen_q=600), 2), (dict(num_heads_q=7), 2), (dict(topk=0), 2),
     (dict(block_size=0), 2), (dict(num_heads_kv=0), 2), (dict(head_dim=0), 2),
@@ -101,6 +106,26 @@ def test_null_and_misaligned_pointers():
     assert bmask(d, idx=NULL) == 1 and bmask(d, mask=NULL) == 1
     assert mblocks(d, mask=NULL) == 1 and mblocks(d, idx=NULL) == 1
     assert bmask(d, idx=MIS) == 4 and mblocks(d, mask=MIS) == 4
+    assert kl(None) == 1
+    for kw in ("q", "k", "qi", "ki", "idx", "lse"):
+        assert kl(d, **{kw: NULL}) == 1, kw
+        assert kl(d, **{kw: MIS}) == 4, kw
+    assert kl(d, rows=MIS) == 4 and kl(d, loss=MIS) == 4 and kl(d, ws=MIS) == 4
+    assert kl(d, ws=NULL, nbytes=0) == 1
+
+
+def test_kl_entry_checks_both_branches():
+    for kw, status in ((dict(index_dim=96), 3), (dict(head_dim=64), 3), (dict(num_heads_q=6), 3),
+                       (dict(softmax_scale=-1.0), 2), (dict(causal=0), 3), (dict(topk=0), 2)):
+        assert kl(dims(**kw)) == status, kw
+    d = dims()
+    need = msa.msa_workspace_bytes(d, msa.ENTRY_KL_LOSS_FWD)
+    rows = d.batch * d.num_heads_kv * d.seqlen_q
+    # 20 bytes of records per selected block of every row, besides the edge lists
+    assert need >= rows * d.topk * (16 + 4 + 4)
+    assert kl(d, nbytes=need - 1) == 5
+    with pytest.raises(msa.MsaError):
+        msa.msa_workspace_bytes(dims(index_dim=96), msa.ENTRY_KL_LOSS_FWD)
 
 
 def _al(x):
@@ -144,6 +169,9 @@ def test_empty_problems_are_ok_without_pointers():
         assert scores(d, qi=NULL, ki=NULL, bm=NULL) == 0
         assert topk(d, bm=NULL, idx=NULL) == 0
         assert bmask(d, idx=NULL, mask=NULL) == 0 and mblocks(d, mask=NULL, idx=NULL) == 0
+        assert kl(d, q=NULL, k=NULL, qi=NULL, ki=NULL, idx=NULL, lse=NULL, rows=NULL, loss=NULL,
+                  ws=NULL, nbytes=0) == 0
+        assert msa.msa_workspace_bytes(d, msa.ENTRY_KL_LOSS_FWD) == 0
         assert msa.msa_workspace_bytes(d, msa.ENTRY_FORWARD) == 0
 
 
