@@ -99,6 +99,113 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Cross-lane exchanges without LDS traffic.
+//
+// swap32(a, b): lanes 32..63 of a trade places with lanes 0..31 of b
+// (v_permlane32_swap): afterwards a = (a[0..31], b[0..31]) and
+// b = (a[32..63], b[32..63]).  So a + b holds the two halves' sum of the old a
+// in lanes 0..31 and of the old b in lanes 32..63.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// swap16(a, b): the odd 16-lane rows of a trade places with the even rows of
+// b (v_permlane16_swap): afterwards a = (a.r0, b.r0, a.r2, b.r2) and
+// b = (a.r1, b.r1, a.r3, b.r3).
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// Value of x in the lane that the DPP control `ctl` selects (within a row).
+template <int ctl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctl, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7 - i within each 8
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15 - i within each row
+
+// Sum / max over the 16 lanes of each row, in every lane of the row.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  return v + dpp<kDppMirror>(v);
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = __builtin_fmaxf(v, dpp<kDppXor1>(v));
+  v = __builtin_fmaxf(v, dpp<kDppXor2>(v));
+  v = __builtin_fmaxf(v, dpp<kDppHalfMirror>(v));
+  return __builtin_fmaxf(v, dpp<kDppMirror>(v));
+}
+
+// Reductions of several values at once over 32 or 64 lanes, built from the
+// swaps above.  scatter32<N>: element i < N/2 becomes the two halves' total
+// (sum, or max when MAX) of element i in lanes 0..31 and of element i + N/2
+// in lanes 32..63.  scatter16<N>: the same across each pair of rows (rows 0, 1
+// and rows 2, 3): element i + (N/2) * (row & 1) in the result.  gather32 and
+// gather16 undo the split of an already reduced vector, so every lane holds
+// all N elements.  allred32 / allred16 combine one value across the halves /
+// row pairs.
+template <bool MAX>
+__device__ __forceinline__ float combine(float a, float b) { return MAX ? __builtin_fmaxf(a, b) : a + b; }
+
+template <int N, bool MAX>
+__device__ __forceinline__ void scatter32(float* v) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    float a = v[i], b = v[i + N / 2];
+    swap32(a, b);
+    v[i] = combine<MAX>(a, b);
+  }
+}
+template <int N, bool MAX>
+__device__ __forceinline__ void scatter16(float* v) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    float a = v[i], b = v[i + N / 2];
+    swap16(a, b);
+    v[i] = combine<MAX>(a, b);
+  }
+}
+template <int N>
+__device__ __forceinline__ void gather32(float* v) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    float a = v[i], b = v[i];
+    swap32(a, b);
+    v[i] = a;
+    v[i + N / 2] = b;
+  }
+}
+template <int N>
+__device__ __forceinline__ void gather16(float* v) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    float a = v[i], b = v[i];
+    swap16(a, b);
+    v[i] = a;
+    v[i + N / 2] = b;
+  }
+}
+template <bool MAX>
+__device__ __forceinline__ float allred32(float x) {
+  float a = x, b = x;
+  swap32(a, b);
+  return combine<MAX>(a, b);
+}
+template <bool MAX>
+__device__ __forceinline__ float allred16(float x) {
+  float a = x, b = x;
+  swap16(a, b);
+  return combine<MAX>(a, b);
+}
+
 // Order-preserving unsigned key of a float: a < b (non-NaN) iff key(a) < key(b).
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);

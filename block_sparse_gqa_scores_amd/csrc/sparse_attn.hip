@@ -74,8 +74,7 @@ struct Params {
   const uint16_t* q_idx;
   const uint16_t* k_idx;
   const float* lse_in;   // [B][H_q][S_q] natural-log LSE of the main branch
-  float4* kl_rec;        // [slot]: (sum P, sum P ln P, sum P (z - m), m)
-  float* kl_l;           // [slot]: sum exp(z - m)
+  float* kl_rec;         // [slot][8]: sum P, sum P ln P, sum P (z - m), sum e^(z - m), m
   float* kl_rows;        // [B][H_kv][S_q] or null
   float* kl_wsum;        // per merge workgroup: sum of its rows' terms
   float* loss;           // or null
@@ -715,8 +714,6 @@ __global__ __launch_bounds__(kThreads, 2) void kl_partial_kernel(Params p) {
     int tq[NL];
 #pragma unroll
     for (int l = 0; l < NL; ++l) tq[l] = s_i[e0 + q_of(l)] + off;
-    // Any key of the block past any query of the sub-tile: mask needed.
-    const bool masked = __builtin_amdgcn_ballot_w64(j * kBlock + kBlock - 1 > s_i[e0 + qm] + off) != 0;
 
     // Index scores first; the index rows of the next sub-tile load meanwhile.
     float pt[4][NL], zv[4][NL];
@@ -739,76 +736,126 @@ __global__ __launch_bounds__(kThreads, 2) void kl_partial_kernel(Params p) {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
         sa = mfma32x32x16(qb[ks], ktile[krow * 16 + ((2 * ks + h) ^ (krow & 15))], sa);
-      const int key = j * kBlock + krow;
+      // Keys past a query are dropped after the head sum (the same keys for
+      // every head of the query), where vis is applied.
 #pragma unroll
       for (int l = 0; l < NL; ++l) {
         float acc = 0.f;
 #pragma unroll
         for (int rr = 0; rr < RPS; ++rr) {
           const int r = l * RPS + rr;
-          float x = sa[r];
-          if (masked && key > tq[l]) x = neg_inf();
-          acc += __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -lse2[r]));
+          acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -lse2[r]));
         }
         pt[nt][l] = acc;
       }
       // One key tile at a time: keeps the live accumulators to two.
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (G >= 8) {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int l = 0; l < NL; ++l) pt[nt][l] += swap_halves(pt[nt][l]);
-    }
-    load_q(qb, i_next);  // lands while the statistics below are reduced
-
-    // Per query: max of z over the visible keys, then the four sums.  For
-    // G >= 8 both halves hold the same (query, key) values: half h takes the
-    // key tiles 2h and 2h + 1 and the sums run over all 64 lanes.
+    // Teacher and index score of each (query slot l, key tile u) of this
+    // lane.  For G >= 8 the halves hold head partial sums of the same queries:
+    // one swap32 per pair of key tiles completes the head sums and leaves
+    // tiles 0, 1 in half 0 and tiles 2, 3 in half 1 (sums then run over all 64
+    // lanes); for G <= 4 each half has its own queries and all four tiles.
     constexpr int NT = G >= 8 ? 2 : 4;
-    constexpr int WIDTH = G >= 8 ? 64 : 32;
+    float P[NL][NT], Z[NL][NT];
+    bool vis[NL][NT];
 #pragma unroll
-    for (int l = 0; l < NL; ++l) {
-      float P[NT], Z[NT];
-      bool vis[NT];
+    for (int l = 0; l < NL; ++l)
 #pragma unroll
       for (int u = 0; u < NT; ++u) {
-        const int nt = G >= 8 ? 2 * h + u : u;
+        float pv;
         if constexpr (G >= 8) {
-          P[u] = (h ? pt[2 + u][l] : pt[u][l]) * invG;
-          Z[u] = h ? zv[2 + u][l] : zv[u][l];
+          float a = pt[u][l], bq = pt[2 + u][l];
+          swap32(a, bq);
+          pv = (a + bq) * invG;
+          float za = zv[u][l], zb = zv[2 + u][l];
+          swap32(za, zb);
+          Z[l][u] = za;
         } else {
-          P[u] = pt[u][l] * invG;
-          Z[u] = zv[u][l];
+          pv = pt[u][l] * invG;
+          Z[l][u] = zv[u][l];
         }
-        vis[u] = j * kBlock + nt * 32 + n <= tq[l];
+        const int nt = G >= 8 ? 2 * h + u : u;
+        vis[l][u] = j * kBlock + nt * 32 + n <= tq[l];
+        P[l][u] = vis[l][u] ? pv : 0.f;
       }
-      float mz = neg_inf();
+    load_q(qb, i_next);  // lands while the statistics below are reduced
+
+    // m_l = max of z over the visible keys of query slot l, in every lane;
+    // mown = the maximum of the slot whose sums this lane's row writes below.
+    float mz[NL], mown;
 #pragma unroll
-      for (int u = 0; u < NT; ++u) if (vis[u]) mz = __builtin_fmaxf(mz, Z[u]);
+    for (int l = 0; l < NL; ++l) {
+      float m = neg_inf();
 #pragma unroll
-      for (int o = 1; o < WIDTH; o <<= 1) mz = __builtin_fmaxf(mz, __shfl_xor(mz, o, 64));
+      for (int u = 0; u < NT; ++u) m = vis[l][u] ? __builtin_fmaxf(m, Z[l][u]) : m;
+      mz[l] = m;
+    }
+    float mw[NL > 1 ? NL / 2 : 1];  // row-held maxima of the G <= 4 split
+    if constexpr (G >= 8) {
+      if constexpr (NL == 4) {
+        scatter32<4, true>(mz);
+        scatter16<2, true>(mz);
+        mz[0] = row_max16(mz[0]);
+        mown = mz[0];
+        gather16<2>(mz);
+        gather32<4>(mz);
+      } else if constexpr (NL == 2) {
+        scatter32<2, true>(mz);
+        mz[0] = row_max16(allred16<true>(mz[0]));
+        mown = mz[0];
+        gather32<2>(mz);
+      } else {
+        mz[0] = row_max16(allred16<true>(allred32<true>(mz[0])));
+        mown = mz[0];
+      }
+    } else {
+      scatter16<NL, true>(mz);
+#pragma unroll
+      for (int x = 0; x < NL / 2; ++x) mw[x] = mz[x] = row_max16(mz[x]);
+      gather16<NL>(mz);
+      mown = 0.f;
+    }
+
+    // Sums per slot: S = sum P, A = sum P ln P, C = sum P (z - m), L = sum e^(z - m).
+    constexpr int V0 = 4 * NL;
+    float sums[V0];
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
       float sS = 0.f, sA = 0.f, sC = 0.f, sL = 0.f;
 #pragma unroll
       for (int u = 0; u < NT; ++u) {
-        const float d = Z[u] - mz;
-        sS += P[u];
-        sA += P[u] > 1e-30f ? P[u] * __builtin_amdgcn_logf(P[u]) : 0.f;
-        sC += P[u] > 0.f ? P[u] * d : 0.f;
-        sL += vis[u] ? __builtin_amdgcn_exp2f(d * kLog2e) : 0.f;
+        const float pv = P[l][u];
+        const float d = Z[l][u] - mz[l];
+        sS += pv;
+        sA += pv > 1e-30f ? pv * __builtin_amdgcn_logf(pv) : 0.f;
+        sC += pv > 0.f ? pv * d : 0.f;
+        sL += vis[l][u] ? __builtin_amdgcn_exp2f(d * kLog2e) : 0.f;
       }
+      sums[4 * l + 0] = sS;
+      sums[4 * l + 1] = sA * 0.69314718055994530942f;
+      sums[4 * l + 2] = sC;
+      sums[4 * l + 3] = sL;
+    }
+    // Reduce-scatter: lanes of row rho (of half h) end with VR totals.
+    constexpr int VR = G >= 8 ? V0 / 4 : V0 / 2;
+    if constexpr (G >= 8) {
+      scatter32<V0, false>(sums);
+      scatter16<V0 / 2, false>(sums);
+    } else {
+      scatter16<V0, false>(sums);
+    }
 #pragma unroll
-      for (int o = 1; o < WIDTH; o <<= 1) {
-        sS += __shfl_xor(sS, o, 64);
-        sA += __shfl_xor(sA, o, 64);
-        sC += __shfl_xor(sC, o, 64);
-        sL += __shfl_xor(sL, o, 64);
-      }
-      if (n == 0 && (G < 8 || h == 0)) {
+    for (int x = 0; x < VR; ++x) sums[x] = row_sum16(sums[x]);
+    if ((lane & 15) == 0) {
+      const int rho = (lane >> 4) & 1;
+#pragma unroll
+      for (int x = 0; x < VR; ++x) {
+        const int orig = G >= 8 ? x + VR * rho + 2 * VR * h : x + VR * rho;
+        const int l = orig >> 2, qq = orig & 3;
         const int sl = s_slot[e0 + q_of(l)];
-        p.kl_rec[sl] = make_float4(sS, sA * 0.69314718055994530942f, sC, mz);
-        p.kl_l[sl] = sL;
+        p.kl_rec[(size_t)sl * 8 + qq] = sums[x];
+        if (qq == 0) p.kl_rec[(size_t)sl * 8 + 4] = G >= 8 ? mown : mw[x >> 2];
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -835,17 +882,17 @@ __global__ __launch_bounds__(256) void kl_merge_kernel(Params p) {
     for (int e = 0; e < p.topk; ++e) {
       const int jj = sel[e];
       if (jj < 0 || jj > local) continue;
-      const float4 rec = p.kl_rec[r * p.topk + e];
-      const float lj = p.kl_l[r * p.topk + e];
-      if (rec.w > M) {  // rescale what was summed against the old maximum
+      const float4 rec = *reinterpret_cast<const float4*>(p.kl_rec + (r * p.topk + e) * 8);
+      const float mj = p.kl_rec[(r * p.topk + e) * 8 + 4];
+      if (mj > M) {  // rescale what was summed against the old maximum
         if (M != neg_inf()) {
-          L *= __builtin_amdgcn_exp2f((M - rec.w) * kLog2e);
-          U += S * (M - rec.w);
+          L *= __builtin_amdgcn_exp2f((M - mj) * kLog2e);
+          U += S * (M - mj);
         }
-        M = rec.w;
+        M = mj;
       }
-      const float dm = rec.w - M;
-      L += lj * __builtin_amdgcn_exp2f(dm * kLog2e);
+      const float dm = mj - M;
+      L += rec.w * __builtin_amdgcn_exp2f(dm * kLog2e);
       U += rec.x * dm;
       S += rec.x;
       AC += rec.y - rec.z;
@@ -880,7 +927,7 @@ struct Layout {
   long NB, E, T;
   int W, n_win;
   size_t counts, cursor, offsets, tile_off, blk_sums, edges, work, part_lse, part_sc, part_o, total;
-  size_t kl_rec, kl_l, kl_wsum;  // alignment-loss layout only
+  size_t kl_rec, kl_wsum;  // alignment-loss layout only
   int n_kl_wg;
 };
 
@@ -928,7 +975,7 @@ Layout make_layout(const AttnShape& s) {
   return L;
 }
 
-// The alignment loss keeps 20 bytes per edge, so one chunk covers all queries.
+// The alignment loss keeps 32 bytes per edge, so one chunk covers all queries.
 Layout make_kl_layout(const AttnShape& s) {
   Layout L{};
   const int G = s.H_q / s.H_kv;
@@ -937,8 +984,7 @@ Layout make_kl_layout(const AttnShape& s) {
   size_t o = layout_build(L, s);
   const long rows = (long)s.batch * s.H_kv * s.S_q;
   L.n_kl_wg = (int)((rows + 255) / 256);
-  L.kl_rec = o;  o = align256(o + (size_t)L.E * 16);
-  L.kl_l = o;    o = align256(o + (size_t)L.E * 4);
+  L.kl_rec = o;  o = align256(o + (size_t)L.E * 32);
   L.kl_wsum = o; o = align256(o + (size_t)L.n_kl_wg * 4);
   L.total = o;
   return L;
@@ -1101,8 +1147,7 @@ hipError_t launch_kl_loss(const AttnShape& s, int D_idx, const uint16_t* q, cons
   char* base = static_cast<char*>(ws);
   Params p = base_params(s, L, base, idx);
   p.q = q; p.k = k; p.q_idx = q_idx; p.k_idx = k_idx; p.lse_in = lse;
-  p.kl_rec = reinterpret_cast<float4*>(base + L.kl_rec);
-  p.kl_l = reinterpret_cast<float*>(base + L.kl_l);
+  p.kl_rec = reinterpret_cast<float*>(base + L.kl_rec);
   p.kl_wsum = reinterpret_cast<float*>(base + L.kl_wsum);
   p.kl_rows = kl_rows;
   p.loss = loss;
