@@ -9,8 +9,9 @@ Prints ONE JSON line.  ``value`` is tokens/s (queries of the batch per second)
 on the 32K prefill workload (B=1, S=32768, 64/8 heads, head dim 128, index dim
 128, block 128, k=16).  Alongside: algorithmic TFLOP/s and the fraction of the
 bf16 MFMA peak, per-entry-point times, the roofline of the dominant step, the
-CPU oracle timed on a bounded row sample, and the decode workload (64
-sequences against a 256K-token cache) as HBM GB/s and fraction of peak.
+CPU oracle timed on a bounded row sample, the decode workload (64 sequences
+against a 256K-token cache) as HBM GB/s and fraction of peak, and the forward
+value of the index branch's alignment loss on the same selection.
 """
 from __future__ import annotations
 
@@ -151,6 +152,40 @@ def selection_mask_rates(w, t, steps):
     return res
 
 
+def kl_loss_flops(w):
+    """Algorithmic FLOPs of the alignment loss: the main-branch logits of every
+    head and the index scores, over each row's selected visible tokens."""
+    tok = w.batch * float(visible_tokens(w).sum())
+    return 2.0 * w.head_dim * w.heads_q * tok + 2.0 * w.index_dim * w.heads_kv * tok
+
+
+def alignment_loss_rate(w, t, steps):
+    """Forward value of the index branch's alignment loss (Sparse Attention
+    Part II, section 3.2) on the forward's selection and LSE: time of
+    msa_kl_loss_fwd, algorithmic TFLOP/s and the fraction of the MFMA peak."""
+    import torch
+
+    import block_sparse_gqa_scores_amd as msa
+
+    stream = torch.cuda.current_stream()
+    _, lse, idx = msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk,
+                                  return_lse=True, return_idx=True)
+    d = msa.dims_of(t["q"], t["k"], t["q_idx"], t["k_idx"], topk=w.topk)
+    ws = torch.empty(msa.msa_workspace_bytes(d, msa.ENTRY_KL_LOSS_FWD), dtype=torch.uint8, device=lse.device)
+
+    def fn():
+        return msa.msa_kl_loss_fwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, workspace=ws)
+
+    loss = fn()
+    ms = time_loop(fn, steps, stream)
+    fl = kl_loss_flops(w)
+    tf = fl / (ms * 1e-3) / 1e12
+    res = {"workload": w.name, "ms": ms, "algorithmic_flops": fl, "TFLOP/s": tf,
+           "mfma_frac": tf / PEAK_BF16_TFLOPS, "loss": float(loss.item())}
+    del ws
+    return res
+
+
 def stage_work(w, chunks):
     """Algorithmic work of each stage per launch: (bound, amount, unit).  With
     the fused selection the Top-k runs inside the index stage and its own
@@ -273,6 +308,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-kl", action="store_true", help="skip the alignment-loss measurement")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run one plain device copy of this many bytes first (counter calibration)")
     ap.add_argument("--no-copy-rate", action="store_true",
@@ -317,6 +353,9 @@ def main():
         "stages": stages, "attn_chunks": chunks, "roofline": roof, "wall_s_timed": wall,
     }
     res["selection_mask"] = selection_mask_rates(w, t, args.steps)
+    if not args.no_kl:
+        print("[bench] alignment loss ...", file=sys.stderr, flush=True)
+        res["alignment_loss"] = alignment_loss_rate(w, t, args.steps)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
