@@ -41,8 +41,16 @@ def _load():
         lib.oracle_attention.argtypes = [P, P, P, P, P, ctypes.c_int64, P, P, P, ctypes.c_int]
         lib.oracle_forward.argtypes = [P, P, P, P, P, P, P, ctypes.c_int64, P, P, P, P, ctypes.c_int]
         lib.oracle_kl_rows.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, P, ctypes.c_int]
+        lib.oracle_kl_rows_f64.argtypes = lib.oracle_kl_rows.argtypes
+        lib.oracle_attention_f64.argtypes = lib.oracle_attention.argtypes
+        lib.oracle_attention_bwd.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, P, P, P, ctypes.c_int]
+        lib.oracle_attention_bwd_f64.argtypes = lib.oracle_attention_bwd.argtypes
+        lib.oracle_kl_bwd.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, P, P, P, ctypes.c_int]
+        lib.oracle_kl_bwd_f64.argtypes = lib.oracle_kl_bwd.argtypes
         for f in (lib.oracle_block_scores, lib.oracle_select, lib.oracle_attention,
-                  lib.oracle_forward, lib.oracle_kl_rows, lib.oracle_default_threads):
+                  lib.oracle_forward, lib.oracle_kl_rows, lib.oracle_default_threads,
+                  lib.oracle_kl_rows_f64, lib.oracle_attention_f64, lib.oracle_attention_bwd,
+                  lib.oracle_attention_bwd_f64, lib.oracle_kl_bwd, lib.oracle_kl_bwd_f64):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -107,6 +115,22 @@ def _u16(a, shape):
     return a
 
 
+def _inputs(arrays_shapes):
+    """bf16 bit patterns (uint16) or fp64 values, all of one kind; returns
+    (contiguous arrays, True when fp64)."""
+    f64 = all(np.asarray(a).dtype == np.float64 for a, _ in arrays_shapes)
+    out = []
+    for a, shape in arrays_shapes:
+        if f64:
+            a = np.ascontiguousarray(a, dtype=np.float64)
+            if tuple(a.shape) != tuple(shape):
+                raise ValueError(f"shape {a.shape} != {shape}")
+            out.append(a)
+        else:
+            out.append(_u16(a, shape))
+    return out, f64
+
+
 def _rows(p, rows):
     rows = p.all_rows() if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     return rows.reshape(-1, 3)
@@ -138,15 +162,16 @@ def select(p: Problem, bm, rows=None):
 
 def attention(p: Problem, q, k, v, sel, rows=None, threads=0):
     rows = _rows(p, rows)
-    qq = _u16(q, (p.batch, p.seqlen_q, p.heads_q, p.head_dim))
-    kk = _u16(k, (p.batch, p.seqlen_k, p.heads_kv, p.head_dim))
-    vv = _u16(v, (p.batch, p.seqlen_k, p.heads_kv, p.head_dim))
+    (qq, kk, vv), f64 = _inputs([(q, (p.batch, p.seqlen_q, p.heads_q, p.head_dim)),
+                                 (k, (p.batch, p.seqlen_k, p.heads_kv, p.head_dim)),
+                                 (v, (p.batch, p.seqlen_k, p.heads_kv, p.head_dim))])
     sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(len(rows), p.topk)
     out = np.empty((len(rows), p.group, p.head_dim), dtype=np.float64)
     lse = np.empty((len(rows), p.group), dtype=np.float64)
     d = p._c()
-    rc = _load().oracle_attention(ctypes.byref(d), _ptr(qq), _ptr(kk), _ptr(vv), _ptr(rows),
-                                  len(rows), _ptr(sel), _ptr(out), _ptr(lse), threads or default_threads())
+    fn = _load().oracle_attention_f64 if f64 else _load().oracle_attention
+    rc = fn(ctypes.byref(d), _ptr(qq), _ptr(kk), _ptr(vv), _ptr(rows),
+            len(rows), _ptr(sel), _ptr(out), _ptr(lse), threads or default_threads())
     if rc:
         raise ValueError("oracle_attention rejected its arguments")
     return out, lse
@@ -180,18 +205,69 @@ def kl_rows(p: Problem, q, k, q_idx, k_idx, sel, rows=None, threads=0):
     student = softmax of the raw index scores.  The loss is the mean over
     all N * H_kv rows."""
     rows = _rows(p, rows)
-    qq = _u16(q, (p.batch, p.seqlen_q, p.heads_q, p.head_dim))
-    kk = _u16(k, (p.batch, p.seqlen_k, p.heads_kv, p.head_dim))
-    qi = _u16(q_idx, (p.batch, p.seqlen_q, p.heads_kv, p.index_dim))
-    ki = _u16(k_idx, (p.batch, p.seqlen_k, p.index_dim))
+    (qq, kk, qi, ki), f64 = _inputs(_kl_shapes(p, q, k, q_idx, k_idx))
     sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(len(rows), p.topk)
     kl = np.empty(len(rows), dtype=np.float64)
     d = p._c()
-    rc = _load().oracle_kl_rows(ctypes.byref(d), _ptr(qq), _ptr(kk), _ptr(qi), _ptr(ki), _ptr(rows),
-                                len(rows), _ptr(sel), _ptr(kl), threads or default_threads())
+    fn = _load().oracle_kl_rows_f64 if f64 else _load().oracle_kl_rows
+    rc = fn(ctypes.byref(d), _ptr(qq), _ptr(kk), _ptr(qi), _ptr(ki), _ptr(rows),
+            len(rows), _ptr(sel), _ptr(kl), threads or default_threads())
     if rc:
         raise ValueError("oracle_kl_rows rejected its arguments")
     return kl
+
+
+def _kl_shapes(p, q, k, q_idx, k_idx):
+    return [(q, (p.batch, p.seqlen_q, p.heads_q, p.head_dim)),
+            (k, (p.batch, p.seqlen_k, p.heads_kv, p.head_dim)),
+            (q_idx, (p.batch, p.seqlen_q, p.heads_kv, p.index_dim)),
+            (k_idx, (p.batch, p.seqlen_k, p.index_dim))]
+
+
+def attention_bwd(p: Problem, q, k, v, dout, sel, rows=None, threads=0, want_dkv=True):
+    """Gradient of the main branch given dO (same layout as q): dq of each
+    listed row [n_rows, G, D], and dk, dv [B, S_k, H_kv, D] summed over the
+    listed rows (None when want_dkv is False).  The selection carries no
+    gradient; inside it the attention is a softmax attention over the
+    selected visible tokens."""
+    rows = _rows(p, rows)
+    (qq, kk, vv, do), f64 = _inputs([(q, (p.batch, p.seqlen_q, p.heads_q, p.head_dim)),
+                                     (k, (p.batch, p.seqlen_k, p.heads_kv, p.head_dim)),
+                                     (v, (p.batch, p.seqlen_k, p.heads_kv, p.head_dim)),
+                                     (dout, (p.batch, p.seqlen_q, p.heads_q, p.head_dim))])
+    sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(len(rows), p.topk)
+    dq = np.empty((len(rows), p.group, p.head_dim), dtype=np.float64)
+    dk = np.empty((p.batch, p.seqlen_k, p.heads_kv, p.head_dim), dtype=np.float64) if want_dkv else None
+    dv = np.empty_like(dk) if want_dkv else None
+    d = p._c()
+    fn = _load().oracle_attention_bwd_f64 if f64 else _load().oracle_attention_bwd
+    rc = fn(ctypes.byref(d), _ptr(qq), _ptr(kk), _ptr(vv), _ptr(do), _ptr(rows), len(rows), _ptr(sel),
+            _ptr(dq), None if dk is None else _ptr(dk), None if dv is None else _ptr(dv),
+            threads or default_threads())
+    if rc:
+        raise ValueError("oracle_attention_bwd rejected its arguments")
+    return dq, dk, dv
+
+
+def kl_bwd(p: Problem, q, k, q_idx, k_idx, sel, rows=None, threads=0, want_dk=True):
+    """Gradient of the listed rows' KL terms with respect to the index
+    inputs, the teacher held fixed (section 3.2 detaches it): dq_idx of each
+    row [n_rows, D_idx], dk_idx [B, S_k, D_idx] summed over the rows, and each
+    row's log-sum-exp of the index scores over its tokens.  Unscaled: the
+    loss's 1 / (N H_kv) is the caller's."""
+    rows = _rows(p, rows)
+    (qq, kk, qi, ki), f64 = _inputs(_kl_shapes(p, q, k, q_idx, k_idx))
+    sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(len(rows), p.topk)
+    dqi = np.empty((len(rows), p.index_dim), dtype=np.float64)
+    dki = np.empty((p.batch, p.seqlen_k, p.index_dim), dtype=np.float64) if want_dk else None
+    lse_z = np.empty(len(rows), dtype=np.float64)
+    d = p._c()
+    fn = _load().oracle_kl_bwd_f64 if f64 else _load().oracle_kl_bwd
+    rc = fn(ctypes.byref(d), _ptr(qq), _ptr(kk), _ptr(qi), _ptr(ki), _ptr(rows), len(rows), _ptr(sel),
+            _ptr(dqi), None if dki is None else _ptr(dki), _ptr(lse_z), threads or default_threads())
+    if rc:
+        raise ValueError("oracle_kl_bwd rejected its arguments")
+    return dqi, dki, lse_z
 
 
 # ------------------------------------------------- block-mask selection format
