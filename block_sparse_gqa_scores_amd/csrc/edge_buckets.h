@@ -1,0 +1,94 @@
+// Edge buckets: the work lists shared by the kernels that run KV-stationary
+// over a selection (attention forward, alignment loss).
+//
+// An edge is (query i, group g, selected block j) of a query chunk; its slot
+// is ((b * H_kv + g) * Qc + il) * topk + e for entry e of row (b, g, i).
+// Buckets group edges by (b, g, query window w, block j), bucket index
+// ((b * H_kv + g) * n_win + w) * n_blk + j; work items are (bucket, first
+// edge) with at most QT edges each.  The build (sparse_attn.hip) counts edges
+// per bucket, scans the counts and scatters the slots.
+#pragma once
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace msa {
+namespace edges {
+
+constexpr int kThreads = 256;  // threads per workgroup of the edge kernels
+constexpr int kD = 128;         // head dim
+constexpr int kBlock = 128;     // keys per block
+constexpr int kSubTiles = 16;   // 4-wave sub-tiles per work item
+constexpr int kScanPerWg = 1024;
+constexpr size_t kPartBudget = size_t(16) << 30;  // bytes of partials per chunk
+constexpr int kBuildQueries = 256;   // queries per bucket-build workgroup
+constexpr int kHistBins = 8192;      // widest row whose histogram lives in LDS
+constexpr int kMinWindow = 2048;     // smallest query window (a multiple of kBuildQueries)
+
+struct Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* idx;
+  uint16_t* out;
+  float* lse;
+  int B, S_q, S_k, H_q, H_kv, G, n_blk, topk;
+  int q0, Qc;            // this chunk's queries: [q0, q0 + Qc) clipped to S_q
+  int NB;                // buckets = B * H_kv * n_win * n_blk
+  int W, n_win;          // queries per window (a multiple of kBuildQueries unless
+                         // it is the whole chunk), windows per chunk
+  int QT;                // edges per work item
+  float scale_log2;
+  int32_t* counts;
+  int32_t* cursor;
+  int32_t* offsets;      // NB + 1
+  int32_t* tile_off;     // NB + 1
+  int32_t* blk_sums;     // 2 * n_scan_wg
+  int32_t* edges;        // slot ids grouped by bucket
+  int2* work;            // (bucket, first edge in bucket)
+  float* part_lse;       // [slot][G]: log2-sum-exp of the block's visible logits
+  float* part_sc;        // [slot][G]: max |O_e| of the row
+  uint16_t* part_o;      // [slot][G * D] fp16: O_e / max |O_e|, in record order (below)
+  // Alignment loss (kl_* kernels below).
+  const uint16_t* q_idx;
+  const uint16_t* k_idx;
+  const float* lse_in;   // [B][H_q][S_q] natural-log LSE of the main branch
+  float* kl_rec;         // [slot][8]: sum P, sum P ln P, sum P (z - m), sum e^(z - m), m
+  float* kl_rows;        // [B][H_kv][S_q] or null
+  float* kl_wsum;        // per merge workgroup: sum of its rows' terms
+  float* loss;           // or null
+};
+
+// Slot of edge (b, g, il, e) inside the chunk.
+__device__ __forceinline__ long slot_of(const Params& p, int bg, int il, int e) {
+  return ((long)bg * p.Qc + il) * p.topk + e;
+}
+
+struct Layout {
+  int Qc, QT, n_scan_wg;
+  long NB, E, T;
+  int W, n_win;
+  size_t counts, cursor, offsets, tile_off, blk_sums, edges, work, part_lse, part_sc, part_o, total;
+  size_t kl_rec, kl_wsum;  // alignment-loss layout only
+  int n_kl_wg;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline int grid_cap(long n, int per) {
+  long g = (n + per - 1) / per;
+  return (int)std::max(1L, std::min(g, 65536L));
+}
+
+// Bucket geometry and the build arrays for a chunk of L.Qc queries (L.QT set
+// by the caller); returns the offset past them.
+size_t layout_build(Layout& L, const AttnShape& s);
+// Edge buckets of the chunk starting at p.q0: counts, scans, scatter.
+void launch_build(const AttnShape& s, const Layout& L, const Params& p, hipStream_t st);
+// Params with the shape, the layout and the build arrays of `base` filled in.
+Params base_params(const AttnShape& s, const Layout& L, char* base, const int32_t* idx);
+
+}  // namespace edges
+}  // namespace msa
