@@ -19,9 +19,10 @@ MSA_OK = 0
 STATUS_NAMES = {0: "MSA_OK", 1: "MSA_ERR_NULL_PTR", 2: "MSA_ERR_INVALID_DIMS", 3: "MSA_ERR_UNSUPPORTED",
                 4: "MSA_ERR_MISALIGNED", 5: "MSA_ERR_WORKSPACE_TOO_SMALL", 6: "MSA_ERR_HIP"}
 ENTRY_INDEX_SCORES, ENTRY_BLOCK_TOPK, ENTRY_SPARSE_ATTN_FWD, ENTRY_FORWARD, ENTRY_KL_LOSS_FWD = 0, 1, 2, 3, 4
+ENTRY_SPARSE_ATTN_BWD = 5
 EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
             "msa_forward_profiled", "msa_attn_chunks", "msa_workspace_bytes", "msa_status_str",
-            "msa_block_mask", "msa_mask_blocks", "msa_kl_loss_fwd")
+            "msa_block_mask", "msa_mask_blocks", "msa_kl_loss_fwd", "msa_sparse_attn_bwd")
 STAGES = ("index_scores", "block_topk", "attn_build", "attn_partial", "attn_merge")
 
 
@@ -70,8 +71,10 @@ def lib():
         L.msa_block_mask.argtypes = [D, P, P, P]
         L.msa_mask_blocks.argtypes = [D, P, P, P]
         L.msa_kl_loss_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_sparse_attn_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for f in (L.msa_index_scores, L.msa_block_topk, L.msa_sparse_attn_fwd, L.msa_forward,
-                  L.msa_forward_profiled, L.msa_block_mask, L.msa_mask_blocks, L.msa_kl_loss_fwd):
+                  L.msa_forward_profiled, L.msa_block_mask, L.msa_mask_blocks, L.msa_kl_loss_fwd,
+                  L.msa_sparse_attn_bwd):
             f.restype = ctypes.c_int
         L.msa_attn_chunks.argtypes = [D]
         L.msa_attn_chunks.restype = ctypes.c_int
@@ -286,3 +289,24 @@ def msa_kl_loss_fwd(q, k, q_idx, k_idx, block_idx, lse, *, block_size=128, softm
                                _stream(q.device))
     _check(rc, "msa_kl_loss_fwd")
     return (loss, rows) if return_rows else loss
+
+
+def msa_sparse_attn_bwd(q, k, v, block_idx, out, lse, dout, *, block_size=128, softmax_scale=0.0,
+                        workspace=None):
+    """Main-branch backward over the selection: returns (dq, dk, dv), bf16,
+    from the upstream gradient dout and the forward's out and lse."""
+    import torch
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _bf16_cuda(n, t, 4)
+    d = dims_of(q, k, topk=block_idx.shape[-1], block_size=block_size, softmax_scale=softmax_scale)
+    d.index_dim = 128
+    for n, t, dt in (("block_idx", block_idx, torch.int32), ("lse", lse, torch.float32)):
+        if not (t.is_cuda and t.dtype == dt and t.is_contiguous()):
+            raise ValueError(f"{n} must be a contiguous {dt} CUDA tensor")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws, nbytes = _workspace(d, ENTRY_SPARSE_ATTN_BWD, workspace, q.device)
+    rc = lib().msa_sparse_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out),
+                                   _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nbytes,
+                                   _stream(q.device))
+    _check(rc, "msa_sparse_attn_bwd")
+    return dq, dk, dv

@@ -1,0 +1,478 @@
+// Main branch, backward: dQ, dK, dV of the block-sparse causal GQA attention
+// from the upstream gradient dO.  The selection is a discrete choice and
+// carries no gradient; inside it the attention is a softmax attention over
+// the visible tokens of the selected blocks (Sparse Attention Part II,
+// section 2), differentiated the usual way.  With P the probabilities of a
+// head over its tokens and Delta = sum_d dO O (= sum_s P_s dP_s):
+//   dP_s = dO . v_s,  dS_s = P_s (dP_s - Delta),
+//   dV_s += P_s dO,  dK_s += scale dS_s q,  dq = scale sum_s dS_s k_s.
+//
+// Schedule (the re-parameterisation of block-sparse attention as a
+// variable-length attention over key blocks that the MSA notes credit to
+// MoBA): the forward's edge buckets, walked KV-stationary.  One workgroup owns
+// one (batch, group, block): it loads K_j, V_j and K_j^T into LDS once and
+// runs every edge of the block (all query windows of the chunk), so dK_j and
+// dV_j accumulate in registers and are written once, with no atomics.  Its
+// four waves split the block's 128 keys; the edges go through in sub-tiles of
+// 32 MFMA rows (32 / G queries x G heads) staged in LDS, in a fixed order
+// (windows ascending, slots sorted inside each bucket), so the sums and the
+// results are identical from run to run.  dq of an edge needs all 128 keys:
+// dS goes through LDS and each wave then forms a quarter of the head dims,
+// written as a per-edge fp16 record; a merge adds a query's records.
+#include "edge_buckets.h"
+
+namespace msa {
+using namespace edges;
+namespace {
+
+constexpr int kTStride = kBlock + 8;  // bf16 per row of K^T [d][key]
+constexpr int kQStride = 32 + 8;      // bf16 per row of Q^T / dO^T [d][row]
+constexpr int kSStride = kBlock + 8;  // bf16 per row of dS [row][key]
+constexpr int kSortSmall = 1024;      // buckets up to this size sort in a small workgroup
+
+struct BwdParams {
+  Params e;              // edge buckets, q, k, v, idx and shapes of the chunk
+  const uint16_t* dout;  // [B][S_q][H_q][D] bf16
+  const uint16_t* out;   // forward output, same layout
+  const float* lse;      // forward LSE [B][H_q][S_q] (natural log)
+  float* delta;          // [B][H_q][S_q]: sum_d dO O
+  uint16_t* dq_rec;      // [slot][G][D] fp16: the edge's dq / its quarter's scale
+  float* dq_sc;          // [slot][G][4]: max |dq| over each quarter of the head dims
+  uint16_t* dq;          // [B][S_q][H_q][D] bf16
+  uint16_t* dk;          // [B][S_k][H_kv][D] bf16
+  uint16_t* dv;
+  float* dk_acc;         // fp32 sums of earlier chunks (several chunks only)
+  float* dv_acc;
+  float scale;           // softmax scale
+  int first, last;       // this chunk is the first / the last
+};
+
+// Delta = sum_d dO O per (b, h, i): 16 lanes per row, one 16-byte chunk each.
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams bp) {
+  const Params& p = bp.e;
+  const long row = ((long)blockIdx.x * 256 + threadIdx.x) >> 4;  // (b, i, h), h fastest
+  const int c = threadIdx.x & 15;
+  const long rows = (long)p.B * p.S_q * p.H_q;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(bp.dout + row * kD + 8 * c);
+    const u32x4 o = *reinterpret_cast<const u32x4*>(bp.out + row * kD + 8 * c);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) acc += bf16_lo(a[x]) * bf16_lo(o[x]) + bf16_hi(a[x]) * bf16_hi(o[x]);
+  }
+  acc = row_sum16(acc);
+  if (row < rows && c == 0) {
+    const int h = (int)(row % p.H_q);
+    const long bi = row / p.H_q;
+    const int i = (int)(bi % p.S_q);
+    const int b = (int)(bi / p.S_q);
+    bp.delta[((long)b * p.H_q + h) * p.S_q + i] = acc;
+  }
+}
+
+// Sorts each bucket's edge slots ascending (the fill scatters them in an
+// order that depends on scheduling).  Bitonic network in LDS over the next
+// power of two of the bucket's size; SIZE bounds the buckets this instance
+// takes (the other instance skips them).
+template <int SIZE, bool LARGE>
+__global__ __launch_bounds__(256) void bucket_sort_kernel(Params p) {
+  __shared__ int32_t v[SIZE];
+  const long bucket = blockIdx.x;
+  const int n = p.counts[bucket];
+  if (n <= 1 || (LARGE ? n <= kSortSmall : n > kSortSmall)) return;  // uniform
+  if (n > SIZE) return;  // more edges than queries in a window: repeated blocks in a row
+  int P = 2;
+  while (P < n) P <<= 1;
+  int32_t* e = p.edges + p.offsets[bucket];
+  for (int x = threadIdx.x; x < P; x += 256) v[x] = x < n ? e[x] : 0x7FFFFFFF;
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1)
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int x = threadIdx.x; x < P; x += 256) {
+        const int y = x ^ jj;
+        if (y > x) {
+          const int32_t a = v[x], c = v[y];
+          const bool up = (x & k) == 0;
+          if ((a > c) == up) {
+            v[x] = c;
+            v[y] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int x = threadIdx.x; x < n; x += 256) e[x] = v[x];
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
+  constexpr int QW = 32 / G;                // queries per sub-tile
+  const Params& p = bp.e;
+  __shared__ u32x4 ktile[kBlock * 16];      // K_j [key][16 chunks], swizzled
+  __shared__ u32x4 vtile[kBlock * 16];      // V_j, same
+  __shared__ __align__(16) uint32_t kt[kD * kTStride / 2];    // K_j^T [d][key]
+  __shared__ u32x4 sq[32 * 16];             // Q rows of the sub-tile [row][chunk], swizzled
+  __shared__ u32x4 sdo[32 * 16];            // dO rows, same
+  __shared__ __align__(16) uint32_t sqt[kD * kQStride / 2];   // Q^T [d][row]
+  __shared__ __align__(16) uint32_t sdot[kD * kQStride / 2];  // dO^T [d][row]
+  __shared__ __align__(16) uint16_t sds[32 * kSStride];  // dS [row][key] bf16
+  __shared__ __align__(16) float s_lse[32];
+  __shared__ __align__(16) float s_delta[32];
+  __shared__ int s_t[QW];                   // position of each query (-1: no edge)
+  __shared__ int s_slot[QW];
+
+  const int BG = p.B * p.H_kv;
+  const int j = blockIdx.x / BG;            // early (busier) blocks first
+  const int bg = blockIdx.x - j * BG;
+  const int b = bg / p.H_kv;
+  const int g = bg - b * p.H_kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int n = lane & 31;
+  const int off = p.S_k - p.S_q;
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float c = p.scale_log2;
+
+  {  // K_j, V_j row-major and K_j^T into LDS (rows past S_k clamped: masked for every query)
+    const size_t row_stride = (size_t)p.H_kv * kD;
+    const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+    const uint16_t* vb = p.v + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int qd = it * kThreads + tid;
+      const int row = qd >> 4, cc = qd & 15;
+      const int s = min(j * kBlock + row, p.S_k - 1);
+      ktile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * cc);
+      vtile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(vb + (size_t)s * row_stride + 8 * cc);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int u = it * kThreads + tid;
+      const int kp = (u & 15) + 16 * ((u >> 6) & 3);
+      const int d0 = ((u >> 4) & 3) + 4 * ((u >> 8) & 3);
+      const int s0 = min(j * kBlock + 2 * kp, p.S_k - 1);
+      const int s1 = min(j * kBlock + 2 * kp + 1, p.S_k - 1);
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(kb + (size_t)s0 * row_stride + 8 * d0);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(kb + (size_t)s1 * row_stride + 8 * d0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t a = (e & 1) ? (lo[e >> 1] >> 16) : (lo[e >> 1] & 0xFFFFu);
+        const uint32_t c2 = (e & 1) ? (hi[e >> 1] & 0xFFFF0000u) : (hi[e >> 1] << 16);
+        kt[((8 * d0 + e) * kTStride + 2 * kp) >> 1] = a | c2;
+      }
+    }
+  }
+
+  f32x16 dk_acc[4], dv_acc[4];  // [key row][d tile]: this wave's 32 keys x 128 dims
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) dk_acc[dt] = dv_acc[dt] = zero16();
+
+  const int key0 = 32 * wave;          // this wave's keys within the block
+  const int key_abs = j * kBlock + key0 + n;
+  for (int w = 0; w < p.n_win; ++w) {
+    const long bucket = ((long)bg * p.n_win + w) * p.n_blk + j;
+    const int cnt = p.counts[bucket];
+    const int32_t* ed = p.edges + p.offsets[bucket];
+    for (int base = 0; base < cnt; base += QW) {  // uniform across the workgroup
+      __syncthreads();  // the previous sub-tile's LDS reads are done
+      // Stage the sub-tile: rows r = q * G + hh (query q, head hh).  Rows of
+      // queries past the bucket's end repeat the last edge with dO = 0 and
+      // LSE = +inf, so they add nothing.
+      {
+        const int pr = tid >> 4, cc = tid & 15;  // row pair (2 pr, 2 pr + 1), chunk cc
+        u32x4 qa[2], da[2];
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          const int r = 2 * pr + y, q = r / G, hh = r - (r / G) * G;
+          const bool valid = base + q < cnt;
+          const int sl = ed[min(base + q, cnt - 1)];
+          const int i = p.q0 + (int)((sl / p.topk) % p.Qc);
+          const size_t rowoff = (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + 8 * cc;
+          qa[y] = *reinterpret_cast<const u32x4*>(p.q + rowoff);
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          da[y] = valid ? *reinterpret_cast<const u32x4*>(bp.dout + rowoff) : z;
+          sq[r * 16 + (cc ^ (r & 15))] = qa[y];
+          sdo[r * 16 + (cc ^ (r & 15))] = da[y];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 8 * cc + e;
+          const uint32_t q0 = (e & 1) ? (qa[0][e >> 1] >> 16) : (qa[0][e >> 1] & 0xFFFFu);
+          const uint32_t q1 = (e & 1) ? (qa[1][e >> 1] & 0xFFFF0000u) : (qa[1][e >> 1] << 16);
+          const uint32_t o0 = (e & 1) ? (da[0][e >> 1] >> 16) : (da[0][e >> 1] & 0xFFFFu);
+          const uint32_t o1 = (e & 1) ? (da[1][e >> 1] & 0xFFFF0000u) : (da[1][e >> 1] << 16);
+          sqt[(d * kQStride + 2 * pr) >> 1] = q0 | q1;
+          sdot[(d * kQStride + 2 * pr) >> 1] = o0 | o1;
+        }
+        if (tid < 32) {
+          const int r = tid, q = r / G, hh = r - (r / G) * G;
+          const bool valid = base + q < cnt;
+          const int sl = ed[min(base + q, cnt - 1)];
+          const int i = p.q0 + (int)((sl / p.topk) % p.Qc);
+          const size_t li = ((size_t)b * p.H_q + g * G + hh) * p.S_q + i;
+          s_lse[r] = valid ? bp.lse[li] * kLog2e : __builtin_inff();
+          s_delta[r] = valid ? bp.delta[li] : 0.f;
+          if (hh == 0) {
+            s_t[q] = valid ? i + off : -1;
+            s_slot[q] = valid ? sl : -1;
+          }
+        }
+      }
+      __syncthreads();
+
+      // S = Q K^T and dP = dO V^T for this wave's 32 keys: rows on registers,
+      // keys on lanes (D[row][key]).
+      f32x16 sacc = zero16(), pacc = zero16();
+      const int krow = key0 + n;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int ch = 2 * ks + h;
+        sacc = mfma32x32x16(sq[n * 16 + (ch ^ (n & 15))], ktile[krow * 16 + (ch ^ (krow & 15))], sacc);
+        pacc = mfma32x32x16(sdo[n * 16 + (ch ^ (n & 15))], vtile[krow * 16 + (ch ^ (krow & 15))], pacc);
+      }
+      // P and dS; rows r -> 8 (r / 4) + 4 h + r % 4.
+      float lse4[16], del4[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 a = *reinterpret_cast<const float4*>(&s_lse[8 * r4 + 4 * h]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&s_delta[8 * r4 + 4 * h]);
+        lse4[4 * r4] = a.x; lse4[4 * r4 + 1] = a.y; lse4[4 * r4 + 2] = a.z; lse4[4 * r4 + 3] = a.w;
+        del4[4 * r4] = d4.x; del4[4 * r4 + 1] = d4.y; del4[4 * r4 + 2] = d4.z; del4[4 * r4 + 3] = d4.w;
+      }
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = mfma32_row(r, lane);
+        const bool vis = key_abs <= s_t[row / G];
+        const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse4[r]));
+        pv[r] = vis ? e2 : 0.f;
+        dsv[r] = pv[r] * (pacc[r] - del4[r]);
+      }
+      // dV += P^T dO and dK += dS^T Q: A = this lane's P / dS (row = key,
+      // k = the 8 rows of registers 8 kk .. 8 kk + 7), B = dO^T / Q^T rows of
+      // the same 8 rows: 8 (e / 4) + 4 h + e % 4 + 16 kk.
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 pa, sa;
+        pa[0] = pack_bf16x2(pv[8 * kk + 0], pv[8 * kk + 1]);
+        pa[1] = pack_bf16x2(pv[8 * kk + 2], pv[8 * kk + 3]);
+        pa[2] = pack_bf16x2(pv[8 * kk + 4], pv[8 * kk + 5]);
+        pa[3] = pack_bf16x2(pv[8 * kk + 6], pv[8 * kk + 7]);
+        sa[0] = pack_bf16x2(dsv[8 * kk + 0], dsv[8 * kk + 1]);
+        sa[1] = pack_bf16x2(dsv[8 * kk + 2], dsv[8 * kk + 3]);
+        sa[2] = pack_bf16x2(dsv[8 * kk + 4], dsv[8 * kk + 5]);
+        sa[3] = pack_bf16x2(dsv[8 * kk + 6], dsv[8 * kk + 7]);
+        const int r0 = 16 * kk + 4 * h;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int d = 32 * dt + n;
+          const uint2 o0 = *reinterpret_cast<const uint2*>(&sdot[(d * kQStride + r0) >> 1]);
+          const uint2 o1 = *reinterpret_cast<const uint2*>(&sdot[(d * kQStride + r0 + 8) >> 1]);
+          const uint2 q0 = *reinterpret_cast<const uint2*>(&sqt[(d * kQStride + r0) >> 1]);
+          const uint2 q1 = *reinterpret_cast<const uint2*>(&sqt[(d * kQStride + r0 + 8) >> 1]);
+          const u32x4 ob = {o0.x, o0.y, o1.x, o1.y};
+          const u32x4 qb = {q0.x, q0.y, q1.x, q1.y};
+          dv_acc[dt] = mfma32x32x16(pa, ob, dv_acc[dt]);
+          dk_acc[dt] = mfma32x32x16(sa, qb, dk_acc[dt]);
+        }
+      }
+      // dS to LDS as [row][key] for dq.
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t w2 = pack_bf16x2(dsv[r], 0.f);
+        sds[mfma32_row(r, lane) * kSStride + key0 + n] = (uint16_t)(w2 & 0xFFFFu);
+      }
+      __syncthreads();
+
+      // dq for head dims 32 wave .. 32 wave + 31 over all 128 keys:
+      // D[row][d] = sum_key dS[row][key] K[key][d].
+      f32x16 qacc = zero16();
+      const int dcol = 32 * wave + n;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&sds[n * kSStride + 16 * ks + 8 * h]);
+        const u32x4 kb = *reinterpret_cast<const u32x4*>(&kt[(dcol * kTStride + 16 * ks + 8 * h) >> 1]);
+        qacc = mfma32x32x16(a, kb, qacc);
+      }
+      // Per (row, quarter): scale = max |dq| over the quarter's 32 dims (the
+      // 32 lanes of this half), stored with the fp16 values divided by it.
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = qacc[r] * bp.scale;
+        const float m = row_max16(allred16<true>(__builtin_fabsf(x)));
+        const int row = mfma32_row(r, lane);
+        const int q = row / G, hh = row - (row / G) * G;
+        const int sl = s_slot[q];
+        if (sl >= 0) {
+          const float inv = m > 0.f ? 1.f / m : 0.f;
+          const uint32_t hv = pack_f16x2(x * inv, 0.f);
+          bp.dq_rec[((size_t)sl * G + hh) * kD + dcol] = (uint16_t)(hv & 0xFFFFu);
+          if (n == 0) bp.dq_sc[((size_t)sl * G + hh) * 4 + wave] = m;
+        }
+      }
+    }
+  }
+
+  // dK (times the softmax scale) and dV of this wave's keys.
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int d = 32 * dt + n;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = j * kBlock + key0 + mfma32_row(r, lane);
+      if (key >= p.S_k) continue;
+      const size_t o = (((size_t)b * p.S_k + key) * p.H_kv + g) * kD + d;
+      float kv = dk_acc[dt][r] * bp.scale, vv = dv_acc[dt][r];
+      if (!bp.first) {
+        kv += bp.dk_acc[o];
+        vv += bp.dv_acc[o];
+      }
+      if (bp.last) {
+        bp.dk[o] = (uint16_t)(pack_bf16x2(kv, 0.f) & 0xFFFFu);
+        bp.dv[o] = (uint16_t)(pack_bf16x2(vv, 0.f) & 0xFFFFu);
+      } else {
+        bp.dk_acc[o] = kv;
+        bp.dv_acc[o] = vv;
+      }
+    }
+  }
+}
+
+// dq of each (query, group): the sum of its edges' records.  One wave per
+// row; lane l takes 16-byte pieces l, l + 64, ... of the row's G x D values.
+template <int G>
+__global__ __launch_bounds__(256) void dq_merge_kernel(BwdParams bp) {
+  constexpr int NF = G * kD / 8;          // 16-byte pieces per row
+  constexpr int F = (NF + 63) / 64;
+  const Params& p = bp.e;
+  const int lane = threadIdx.x & 63;
+  const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= (long)p.B * p.H_kv * p.Qc) return;
+  const int il = (int)(r % p.Qc);
+  const int bg = (int)(r / p.Qc);
+  const int i = p.q0 + il;
+  if (i >= p.S_q) return;
+  const int b = bg / p.H_kv, g = bg - (bg / p.H_kv) * p.H_kv;
+  const int32_t* sel = p.idx + ((long)bg * p.S_q + i) * p.topk;
+  const int local = (i + p.S_k - p.S_q) / kBlock;
+  const long slot0 = ((long)bg * p.Qc + il) * p.topk;
+  float acc[F][8];
+#pragma unroll
+  for (int u = 0; u < F; ++u)
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc[u][x] = 0.f;
+  for (int e = 0; e < p.topk; ++e) {
+    const int jj = sel[e];
+    if (jj < 0 || jj > local) continue;  // uniform
+    const long slot = slot0 + e;
+#pragma unroll
+    for (int u = 0; u < F; ++u) {
+      const int f = lane + 64 * u;
+      if (f >= NF) continue;
+      const int hh = f / 16, dq0 = (f % 16) * 8;
+      const float sc = bp.dq_sc[(slot * G + hh) * 4 + dq0 / 32];
+      const u32x4 x = *reinterpret_cast<const u32x4*>(bp.dq_rec + (slot * G + hh) * kD + dq0);
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        acc[u][2 * y] += sc * f16_lo(x[y]);
+        acc[u][2 * y + 1] += sc * f16_hi(x[y]);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < F; ++u) {
+    const int f = lane + 64 * u;
+    if (f >= NF) continue;
+    const int hh = f / 16, dq0 = (f % 16) * 8;
+    uint4 o;
+    o.x = pack_bf16x2(acc[u][0], acc[u][1]);
+    o.y = pack_bf16x2(acc[u][2], acc[u][3]);
+    o.z = pack_bf16x2(acc[u][4], acc[u][5]);
+    o.w = pack_bf16x2(acc[u][6], acc[u][7]);
+    *reinterpret_cast<uint4*>(bp.dq + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + dq0) = o;
+  }
+}
+
+struct BwdLayout {
+  Layout L;
+  size_t delta, dq_rec, dq_sc, dk_acc, dv_acc, total;
+  int chunks;
+};
+
+BwdLayout make_bwd_layout(const AttnShape& s) {
+  BwdLayout B{};
+  Layout& L = B.L;
+  const int G = s.H_q / s.H_kv;
+  L.QT = kSubTiles * 4 * (32 / G);
+  const size_t per_query = (size_t)s.batch * s.H_kv * s.topk * ((size_t)G * (kD * 2 + 16) + 4);
+  long qc = (long)(kPartBudget / per_query);
+  if (qc >= 128) qc -= qc % 128;
+  L.Qc = (int)std::max(1L, std::min<long>(qc, s.S_q));
+  size_t o = layout_build(L, s);
+  B.chunks = (s.S_q + L.Qc - 1) / L.Qc;
+  B.delta = o;  o = align256(o + (size_t)s.batch * s.H_q * s.S_q * 4);
+  B.dq_rec = o; o = align256(o + (size_t)L.E * G * kD * 2);
+  B.dq_sc = o;  o = align256(o + (size_t)L.E * G * 16);
+  const size_t kv = (size_t)s.batch * s.S_k * s.H_kv * kD * 4;
+  B.dk_acc = o; o = align256(o + (B.chunks > 1 ? kv : 0));
+  B.dv_acc = o; o = align256(o + (B.chunks > 1 ? kv : 0));
+  B.total = o;
+  L.total = o;
+  return B;
+}
+
+template <int G>
+hipError_t launch_bwd_g(const AttnShape& s, const BwdLayout& BL, BwdParams bp, hipStream_t st) {
+  const Layout& L = BL.L;
+  const long rows = (long)s.batch * s.S_q * s.H_q;
+  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, st, bp);
+  for (int q0 = 0, ci = 0; q0 < s.S_q; q0 += L.Qc, ++ci) {
+    bp.e.q0 = q0;
+    bp.first = ci == 0;
+    bp.last = q0 + L.Qc >= s.S_q;
+    launch_build(s, L, bp.e, st);
+    hipLaunchKernelGGL((bucket_sort_kernel<kSortSmall, false>), dim3((unsigned)L.NB), dim3(256), 0, st, bp.e);
+    hipLaunchKernelGGL((bucket_sort_kernel<kMaxWindow, true>), dim3((unsigned)L.NB), dim3(256), 0, st, bp.e);
+    hipLaunchKernelGGL(attn_bwd_kernel<G>, dim3((unsigned)(s.batch * s.H_kv * s.n_blk)), dim3(kThreads), 0, st, bp);
+    const long mrows = (long)s.batch * s.H_kv * L.Qc;
+    hipLaunchKernelGGL(dq_merge_kernel<G>, dim3((unsigned)((mrows + 3) / 4)), dim3(256), 0, st, bp);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t sparse_attn_bwd_workspace(const AttnShape& s) { return make_bwd_layout(s).total; }
+
+hipError_t launch_sparse_attn_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k,
+                                  const uint16_t* v, const int32_t* idx, const uint16_t* out,
+                                  const float* lse, const uint16_t* dout, uint16_t* dq,
+                                  uint16_t* dk, uint16_t* dv, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  const BwdLayout BL = make_bwd_layout(s);
+  if (ws_bytes < BL.total) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(ws);
+  BwdParams bp{};
+  bp.e = base_params(s, BL.L, base, idx);
+  bp.e.q = q; bp.e.k = k; bp.e.v = v;
+  bp.dout = dout; bp.out = out; bp.lse = lse;
+  bp.delta = reinterpret_cast<float*>(base + BL.delta);
+  bp.dq_rec = reinterpret_cast<uint16_t*>(base + BL.dq_rec);
+  bp.dq_sc = reinterpret_cast<float*>(base + BL.dq_sc);
+  bp.dk_acc = reinterpret_cast<float*>(base + BL.dk_acc);
+  bp.dv_acc = reinterpret_cast<float*>(base + BL.dv_acc);
+  bp.dq = dq; bp.dk = dk; bp.dv = dv;
+  bp.scale = s.scale;
+  switch (bp.e.G) {
+    case 1: return launch_bwd_g<1>(s, BL, bp, stream);
+    case 2: return launch_bwd_g<2>(s, BL, bp, stream);
+    case 4: return launch_bwd_g<4>(s, BL, bp, stream);
+    case 8: return launch_bwd_g<8>(s, BL, bp, stream);
+    case 16: return launch_bwd_g<16>(s, BL, bp, stream);
+    case 32: return launch_bwd_g<32>(s, BL, bp, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace msa

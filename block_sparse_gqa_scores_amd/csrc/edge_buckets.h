@@ -26,6 +26,7 @@ constexpr size_t kPartBudget = size_t(16) << 30;  // bytes of partials per chunk
 constexpr int kBuildQueries = 256;   // queries per bucket-build workgroup
 constexpr int kHistBins = 8192;      // widest row whose histogram lives in LDS
 constexpr int kMinWindow = 2048;     // smallest query window (a multiple of kBuildQueries)
+constexpr int kMaxWindow = 16384;    // largest query window (bounds a bucket's edge count)
 
 struct Params {
   const uint16_t* q;

@@ -49,6 +49,14 @@ hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint1
                               void* ws, size_t ws_bytes, hipStream_t stream,
                               const StageEvents* events = nullptr);
 
+// Main branch, backward (see attn_bwd.hip).
+size_t sparse_attn_bwd_workspace(const AttnShape& s);
+hipError_t launch_sparse_attn_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k,
+                                  const uint16_t* v, const int32_t* idx, const uint16_t* out,
+                                  const float* lse, const uint16_t* dout, uint16_t* dq,
+                                  uint16_t* dk, uint16_t* dv, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
 // Writes n zero floats (a kernel, so the call can sit inside a graph capture).
 hipError_t launch_fill_zero(float* dst, long n, hipStream_t stream);
 

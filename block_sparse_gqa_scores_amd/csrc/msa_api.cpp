@@ -120,6 +120,9 @@ size_t msa_workspace_bytes(const msa_dims* d, int entry) {
     case MSA_ENTRY_KL_LOSS_FWD:
       if (check_dims(d, true, true) != MSA_OK) return bad;
       return is_empty(*d) ? 0 : msa::kl_loss_workspace(attn_shape(*d));
+    case MSA_ENTRY_SPARSE_ATTN_BWD:
+      if (check_dims(d, false, true) != MSA_OK) return bad;
+      return is_empty(*d) ? 0 : msa::sparse_attn_bwd_workspace(attn_shape(*d));
     default:
       return bad;
   }
@@ -187,6 +190,29 @@ msa_status msa_sparse_attn_fwd(const msa_dims* d, const void* q, const void* k, 
       s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), block_idx, static_cast<uint16_t*>(out), lse, ws, ws_bytes,
       static_cast<hipStream_t>(stream)));
+}
+
+msa_status msa_sparse_attn_bwd(const msa_dims* d, const void* q, const void* k, const void* v,
+                               const int32_t* block_idx, const void* out, const float* lse,
+                               const void* dout, void* dq, void* dk, void* dv, void* ws,
+                               size_t ws_bytes, void* stream) {
+  msa_status st = check_dims(d, false, true);
+  if (st != MSA_OK || is_empty(*d)) return st;
+  if (!q || !k || !v || !block_idx || !out || !lse || !dout || !dq || !dk || !dv)
+    return MSA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) ||
+      !aligned16(out) || !aligned16(lse) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return MSA_ERR_MISALIGNED;
+  const msa::AttnShape s = attn_shape(*d);
+  const size_t need = msa::sparse_attn_bwd_workspace(s);
+  if (!ws || ws_bytes < need) return ws ? MSA_ERR_WORKSPACE_TOO_SMALL : MSA_ERR_NULL_PTR;
+  if (!aligned16(ws)) return MSA_ERR_MISALIGNED;
+  return from_hip(msa::launch_sparse_attn_bwd(
+      s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), block_idx, static_cast<const uint16_t*>(out), lse,
+      static_cast<const uint16_t*>(dout), static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk),
+      static_cast<uint16_t*>(dv), ws, ws_bytes, static_cast<hipStream_t>(stream)));
 }
 
 msa_status msa_kl_loss_fwd(const msa_dims* d, const void* q, const void* k, const void* q_idx,

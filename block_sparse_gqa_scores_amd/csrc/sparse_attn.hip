@@ -559,11 +559,11 @@ namespace edges {
 // offset past them.
 size_t layout_build(Layout& L, const AttnShape& s) {
   // Window: about QT edges per (window, block) bucket at the chunk's mean
-  // number of visible blocks, at least kMinWindow queries; the whole chunk
-  // when that exceeds it.
+  // number of visible blocks, between kMinWindow and kMaxWindow queries; the
+  // whole chunk when that exceeds it.
   const long vis = std::max(1L, ((long)s.S_k - s.S_q + s.S_q / 2) / kBlock);
   long w = ((long)L.QT * vis / std::max(1, s.topk) + kBuildQueries - 1) / kBuildQueries * kBuildQueries;
-  w = std::max<long>(w, kMinWindow);
+  w = std::min<long>(std::max<long>(w, kMinWindow), kMaxWindow);
   L.W = w < L.Qc ? (int)w : L.Qc;
   L.n_win = (L.Qc + L.W - 1) / L.W;
   L.NB = (long)s.batch * s.H_kv * L.n_win * s.n_blk;

@@ -85,7 +85,8 @@ typedef enum msa_entry {
   MSA_ENTRY_BLOCK_TOPK = 1,
   MSA_ENTRY_SPARSE_ATTN_FWD = 2,
   MSA_ENTRY_FORWARD = 3,
-  MSA_ENTRY_KL_LOSS_FWD = 4
+  MSA_ENTRY_KL_LOSS_FWD = 4,
+  MSA_ENTRY_SPARSE_ATTN_BWD = 5
 } msa_entry;
 
 /*
@@ -227,6 +228,36 @@ msa_status msa_kl_loss_fwd(const msa_dims* dims, const void* q, const void* k,
                            const int32_t* block_idx, const float* lse,
                            float* kl_rows, float* loss, void* ws,
                            size_t ws_bytes, void* stream);
+
+/*
+ * Main branch, backward (the backward pass that the MSA kernel notes fuse
+ * over the selected blocks, The Architecture of Infinity, baystreetwire.com;
+ * Sparse Attention Part II, section 2: inside the selection the attention is
+ * an ordinary softmax attention over the selected tokens).  The selection is
+ * a discrete choice and carries no gradient.  For each head h of group g,
+ * with P_s = exp(scale * q[b][i][h] . k[b][s][g] - lse[b][h][i]) on T_i and
+ * Delta = sum_d dout[b][i][h][d] * out[b][i][h][d]:
+ *
+ *   dS_s = P_s (dout[b][i][h] . v[b][s][g] - Delta)
+ *   dq[b][i][h] = scale * sum_{s in T_i} dS_s k[b][s][g]
+ *   dk[b][s][g] = scale * sum over (i, h in g) with s in T_i of dS_s q[b][i][h]
+ *   dv[b][s][g] = sum over (i, h in g) with s in T_i of P_s dout[b][i][h]
+ *
+ * Inputs: q, k, v, block_idx (as msa_sparse_attn_fwd), out and lse exactly as
+ * the forward returned them for this selection, dout [B][S_q][H_q][D] bf16.
+ * Outputs (written in full, bf16): dq like q; dk, dv like k and v (zero for
+ * keys no query selects).  Sums run in a fixed order: results are identical
+ * from run to run.  `ws` holds msa_workspace_bytes(dims,
+ * MSA_ENTRY_SPARSE_ATTN_BWD) bytes (edge lists, per-edge dq records of
+ * G * (2 D + 16) bytes, and fp32 dk / dv sums when the queries run in several
+ * chunks); contents on entry do not matter.  Uses the main-branch fields of
+ * dims (index_dim is ignored).
+ */
+msa_status msa_sparse_attn_bwd(const msa_dims* dims, const void* q, const void* k,
+                               const void* v, const int32_t* block_idx,
+                               const void* out, const float* lse, const void* dout,
+                               void* dq, void* dk, void* dv, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /* Internal stages of msa_forward, in launch order (for msa_forward_profiled). */
 typedef enum msa_stage {

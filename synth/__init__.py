@@ -22,7 +22,8 @@ Generator definition
   (tensor id 6): a normal element becomes g_j * z before rounding; an integer
   element becomes rint_half_even(g_j * n), still an exact bf16 integer.
 
-Tensor ids: Q 1, K 2, V 3, Q_idx 4, K_idx 5, gain 6.
+Tensor ids: Q 1, K 2, V 3, Q_idx 4, K_idx 5, gain 6, dO 7 (the upstream gradient
+of the output, for the backward).
 """
 from __future__ import annotations
 
@@ -32,7 +33,7 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "q_idx": 4, "k_idx": 5, "gain": 6}
+TENSOR_IDS = {"q": 1, "k": 2, "v": 3, "q_idx": 4, "k_idx": 5, "gain": 6, "dout": 7}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa_synth.so")
 
@@ -80,6 +81,7 @@ class Workload:
             "v": (B, Sk, self.heads_kv, self.head_dim),
             "q_idx": (B, Sq, self.heads_kv, self.index_dim),
             "k_idx": (B, Sk, self.index_dim),
+            "dout": (B, Sq, self.heads_q, self.head_dim),
         }
 
     def kind(self, name: str) -> str:

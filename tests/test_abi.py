@@ -114,6 +114,33 @@ def test_null_and_misaligned_pointers():
     assert kl(d, ws=NULL, nbytes=0) == 1
 
 
+def bwd(d, q=A, k=A, v=A, idx=A, out=A, lse=A, do=A, dq=A, dk=A, dv=A, ws=A, nbytes=1 << 40):
+    return msa.lib().msa_sparse_attn_bwd(None if d is None else ctypes.byref(d), q, k, v, idx, out, lse,
+                                         do, dq, dk, dv, ws, nbytes, None)
+
+
+def test_bwd_entry_checks():
+    d = dims()
+    assert bwd(None) == 1
+    for kw in ("q", "k", "v", "idx", "out", "lse", "do", "dq", "dk", "dv"):
+        assert bwd(d, **{kw: NULL}) == 1, kw
+        assert bwd(d, **{kw: MIS}) == 4, kw
+    assert bwd(d, ws=NULL, nbytes=0) == 1 and bwd(d, ws=MIS) == 4
+    need = msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_BWD)
+    rows = d.batch * d.num_heads_kv * d.seqlen_q
+    G = d.num_heads_q // d.num_heads_kv
+    assert need >= rows * d.topk * G * (2 * 128 + 16)
+    assert bwd(d, nbytes=need - 1) == 5
+    # the main branch only: index_dim does not matter (the workspace check is reached)
+    assert bwd(dims(index_dim=96), nbytes=need - 1) == 5
+    for kw, status in ((dict(head_dim=64), 3), (dict(num_heads_q=6), 3), (dict(causal=0), 3),
+                       (dict(softmax_scale=-1.0), 2), (dict(topk=65), 3)):
+        assert bwd(dims(**kw)) == status, kw
+    e = dims(batch=0)
+    assert bwd(e, q=NULL, k=NULL, v=NULL, idx=NULL, out=NULL, lse=NULL, do=NULL, dq=NULL, dk=NULL,
+               dv=NULL, ws=NULL, nbytes=0) == 0
+
+
 def test_kl_entry_checks_both_branches():
     for kw, status in ((dict(index_dim=96), 3), (dict(head_dim=64), 3), (dict(num_heads_q=6), 3),
                        (dict(softmax_scale=-1.0), 2), (dict(causal=0), 3), (dict(topk=0), 2)):
