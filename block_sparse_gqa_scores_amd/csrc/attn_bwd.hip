@@ -26,9 +26,22 @@ using namespace edges;
 namespace {
 
 constexpr int kTStride = kBlock + 8;  // bf16 per row of K^T [d][key]
-constexpr int kQStride = 32 + 8;      // bf16 per row of Q^T / dO^T [d][row]
+constexpr int kQStride = 32 + 4;      // bf16 per row of Q^T / dO^T [d][row] (conflict-free)
 constexpr int kSStride = kBlock + 8;  // bf16 per row of dS [row][key]
 constexpr int kSortSmall = 1024;      // buckets up to this size sort in a small workgroup
+
+// Chunk swizzle of the staged rows: distinct chunks both for 16 consecutive
+// rows (the MFMA operand reads) and for 16 rows of one parity (the staging
+// writes), so neither conflicts on LDS banks.
+__device__ __forceinline__ int rsw(int r) { return ((r >> 1) ^ ((r & 1) << 3)) & 15; }
+
+// dq records: per slot, 4 quarters of the head dims x G heads x 32 values in
+// the order the dq tile holds them, position p = 16 h + r for MFMA register r
+// of lane half h, which is dim 32 quarter + 8 (r / 4) + 4 h + r % 4.
+__device__ __forceinline__ int rec_dim(int quarter, int pos) {
+  const int h = pos >> 4, r = pos & 15;
+  return 32 * quarter + 8 * (r >> 2) + 4 * h + (r & 3);
+}
 
 struct BwdParams {
   Params e;              // edge buckets, q, k, v, idx and shapes of the chunk
@@ -36,8 +49,8 @@ struct BwdParams {
   const uint16_t* out;   // forward output, same layout
   const float* lse;      // forward LSE [B][H_q][S_q] (natural log)
   float* delta;          // [B][H_q][S_q]: sum_d dO O
-  uint16_t* dq_rec;      // [slot][G][D] fp16: the edge's dq / its quarter's scale
-  float* dq_sc;          // [slot][G][4]: max |dq| over each quarter of the head dims
+  uint16_t* dq_rec;      // [slot][4][G][32] fp16: the edge's dq / its quarter's scale (rec_dim order)
+  float* dq_sc;          // [slot][4][G]: max |dq| over each quarter of the head dims
   uint16_t* dq;          // [B][S_q][H_q][D] bf16
   uint16_t* dk;          // [B][S_k][H_kv][D] bf16
   uint16_t* dv;
@@ -168,56 +181,90 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
 
   const int key0 = 32 * wave;          // this wave's keys within the block
   const int key_abs = j * kBlock + key0 + n;
-  for (int w = 0; w < p.n_win; ++w) {
-    const long bucket = ((long)bg * p.n_win + w) * p.n_blk + j;
-    const int cnt = p.counts[bucket];
-    const int32_t* ed = p.edges + p.offsets[bucket];
-    for (int base = 0; base < cnt; base += QW) {  // uniform across the workgroup
-      __syncthreads();  // the previous sub-tile's LDS reads are done
-      // Stage the sub-tile: rows r = q * G + hh (query q, head hh).  Rows of
-      // queries past the bucket's end repeat the last edge with dO = 0 and
-      // LSE = +inf, so they add nothing.
-      {
-        const int pr = tid >> 4, cc = tid & 15;  // row pair (2 pr, 2 pr + 1), chunk cc
-        u32x4 qa[2], da[2];
+  // Sub-tiles in a fixed order: windows ascending, QW edges at a time.  The
+  // rows of the next sub-tile are fetched into registers while the current
+  // one computes; rows of queries past a bucket's end repeat its last edge
+  // with dO = 0 and LSE = +inf, so they add nothing.
+  struct Cursor {
+    int w, base, cnt;
+    const int32_t* ed;
+  };
+  auto next = [&](Cursor& cu) {  // uniform; false past the last sub-tile
+    cu.base += QW;
+    while (cu.base >= cu.cnt) {
+      if (++cu.w >= p.n_win) return false;
+      const long bucket = ((long)bg * p.n_win + cu.w) * p.n_blk + j;
+      cu.cnt = p.counts[bucket];
+      cu.ed = p.edges + p.offsets[bucket];
+      cu.base = 0;
+    }
+    return true;
+  };
+  const int pr = tid & 15, cc = tid >> 4;  // staging role: rows (2 pr, 2 pr + 1), chunk cc
+  u32x4 qa[2], da[2];
+  float f_lse = 0.f, f_delta = 0.f;
+  int f_t = -1, f_slot = -1;
+  auto fetch = [&](const Cursor& cu) {
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          const int r = 2 * pr + y, q = r / G, hh = r - (r / G) * G;
-          const bool valid = base + q < cnt;
-          const int sl = ed[min(base + q, cnt - 1)];
-          const int i = p.q0 + (int)((sl / p.topk) % p.Qc);
-          const size_t rowoff = (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + 8 * cc;
-          qa[y] = *reinterpret_cast<const u32x4*>(p.q + rowoff);
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          da[y] = valid ? *reinterpret_cast<const u32x4*>(bp.dout + rowoff) : z;
-          sq[r * 16 + (cc ^ (r & 15))] = qa[y];
-          sdo[r * 16 + (cc ^ (r & 15))] = da[y];
-        }
+    for (int y = 0; y < 2; ++y) {
+      const int r = 2 * pr + y, q = r / G, hh = r - (r / G) * G;
+      const bool valid = cu.base + q < cu.cnt;
+      const int sl = cu.ed[min(cu.base + q, cu.cnt - 1)];
+      const int i = p.q0 + (int)((sl / p.topk) % p.Qc);
+      const size_t rowoff = (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + 8 * cc;
+      qa[y] = *reinterpret_cast<const u32x4*>(p.q + rowoff);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      da[y] = valid ? *reinterpret_cast<const u32x4*>(bp.dout + rowoff) : z;
+    }
+    if (tid < 32) {
+      const int r = tid, q = r / G, hh = r - (r / G) * G;
+      const bool valid = cu.base + q < cu.cnt;
+      const int sl = cu.ed[min(cu.base + q, cu.cnt - 1)];
+      const int i = p.q0 + (int)((sl / p.topk) % p.Qc);
+      const size_t li = ((size_t)b * p.H_q + g * G + hh) * p.S_q + i;
+      f_lse = valid ? bp.lse[li] * kLog2e : __builtin_inff();
+      f_delta = valid ? bp.delta[li] : 0.f;
+      f_t = valid ? i + off : -1;
+      f_slot = valid ? sl : -1;
+    }
+  };
+  Cursor cur{-1, 0, 0, nullptr};
+  cur.base = -QW;
+  bool have = next(cur);
+  if (have) fetch(cur);
+  while (have) {
+    __syncthreads();  // the previous sub-tile's LDS reads are done
+    {  // stage the fetched rows: row-major and transposed
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 8 * cc + e;
-          const uint32_t q0 = (e & 1) ? (qa[0][e >> 1] >> 16) : (qa[0][e >> 1] & 0xFFFFu);
-          const uint32_t q1 = (e & 1) ? (qa[1][e >> 1] & 0xFFFF0000u) : (qa[1][e >> 1] << 16);
-          const uint32_t o0 = (e & 1) ? (da[0][e >> 1] >> 16) : (da[0][e >> 1] & 0xFFFFu);
-          const uint32_t o1 = (e & 1) ? (da[1][e >> 1] & 0xFFFF0000u) : (da[1][e >> 1] << 16);
-          sqt[(d * kQStride + 2 * pr) >> 1] = q0 | q1;
-          sdot[(d * kQStride + 2 * pr) >> 1] = o0 | o1;
-        }
-        if (tid < 32) {
-          const int r = tid, q = r / G, hh = r - (r / G) * G;
-          const bool valid = base + q < cnt;
-          const int sl = ed[min(base + q, cnt - 1)];
-          const int i = p.q0 + (int)((sl / p.topk) % p.Qc);
-          const size_t li = ((size_t)b * p.H_q + g * G + hh) * p.S_q + i;
-          s_lse[r] = valid ? bp.lse[li] * kLog2e : __builtin_inff();
-          s_delta[r] = valid ? bp.delta[li] : 0.f;
-          if (hh == 0) {
-            s_t[q] = valid ? i + off : -1;
-            s_slot[q] = valid ? sl : -1;
-          }
+      for (int y = 0; y < 2; ++y) {
+        const int r = 2 * pr + y;
+        sq[r * 16 + (cc ^ rsw(r))] = qa[y];
+        sdo[r * 16 + (cc ^ rsw(r))] = da[y];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 8 * cc + e;
+        const uint32_t q0 = (e & 1) ? (qa[0][e >> 1] >> 16) : (qa[0][e >> 1] & 0xFFFFu);
+        const uint32_t q1 = (e & 1) ? (qa[1][e >> 1] & 0xFFFF0000u) : (qa[1][e >> 1] << 16);
+        const uint32_t o0 = (e & 1) ? (da[0][e >> 1] >> 16) : (da[0][e >> 1] & 0xFFFFu);
+        const uint32_t o1 = (e & 1) ? (da[1][e >> 1] & 0xFFFF0000u) : (da[1][e >> 1] << 16);
+        sqt[(d * kQStride + 2 * pr) >> 1] = q0 | q1;
+        sdot[(d * kQStride + 2 * pr) >> 1] = o0 | o1;
+      }
+      if (tid < 32) {
+        s_lse[tid] = f_lse;
+        s_delta[tid] = f_delta;
+        if (tid % G == 0) {
+          s_t[tid / G] = f_t;
+          s_slot[tid / G] = f_slot;
         }
       }
-      __syncthreads();
+    }
+    __syncthreads();
+    Cursor nx = cur;
+    const bool have_next = next(nx);
+    if (have_next) fetch(nx);  // in flight during this sub-tile's work
+    asm volatile("" ::: "memory");
 
       // S = Q K^T and dP = dO V^T for this wave's 32 keys: rows on registers,
       // keys on lanes (D[row][key]).
@@ -226,8 +273,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const int ch = 2 * ks + h;
-        sacc = mfma32x32x16(sq[n * 16 + (ch ^ (n & 15))], ktile[krow * 16 + (ch ^ (krow & 15))], sacc);
-        pacc = mfma32x32x16(sdo[n * 16 + (ch ^ (n & 15))], vtile[krow * 16 + (ch ^ (krow & 15))], pacc);
+        sacc = mfma32x32x16(sq[n * 16 + (ch ^ rsw(n))], ktile[krow * 16 + (ch ^ (krow & 15))], sacc);
+        pacc = mfma32x32x16(sdo[n * 16 + (ch ^ rsw(n))], vtile[krow * 16 + (ch ^ (krow & 15))], pacc);
       }
       // P and dS; rows r -> 8 (r / 4) + 4 h + r % 4.
       float lse4[16], del4[16];
@@ -283,33 +330,42 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
       }
       __syncthreads();
 
-      // dq for head dims 32 wave .. 32 wave + 31 over all 128 keys:
-      // D[row][d] = sum_key dS[row][key] K[key][d].
+      // dq for head dims 32 wave .. 32 wave + 31 over all 128 keys, as
+      // dq^T[d][row] = sum_key K^T[d][key] dS[row][key]: rows on lanes, each
+      // lane holding 16 dims of its row (4 runs of 4 consecutive dims).
       f32x16 qacc = zero16();
-      const int dcol = 32 * wave + n;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&sds[n * kSStride + 16 * ks + 8 * h]);
-        const u32x4 kb = *reinterpret_cast<const u32x4*>(&kt[(dcol * kTStride + 16 * ks + 8 * h) >> 1]);
-        qacc = mfma32x32x16(a, kb, qacc);
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(&kt[((32 * wave + n) * kTStride + 16 * ks + 8 * h) >> 1]);
+        const u32x4 sb = *reinterpret_cast<const u32x4*>(&sds[n * kSStride + 16 * ks + 8 * h]);
+        qacc = mfma32x32x16(ka, sb, qacc);
       }
-      // Per (row, quarter): scale = max |dq| over the quarter's 32 dims (the
-      // 32 lanes of this half), stored with the fp16 values divided by it.
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = qacc[r] * bp.scale;
-        const float m = row_max16(allred16<true>(__builtin_fabsf(x)));
-        const int row = mfma32_row(r, lane);
-        const int q = row / G, hh = row - (row / G) * G;
+      // Record of (row n, quarter `wave`): the 32 dims over this lane and its
+      // partner in the other half; scale = their max |dq|, values / scale in fp16.
+      {
+        const int q = n / G, hh = n - (n / G) * G;
         const int sl = s_slot[q];
+        float m = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = max3abs(qacc[r], qacc[r], m);
+        m = __builtin_fmaxf(m, swap_halves(m)) * bp.scale;
         if (sl >= 0) {
-          const float inv = m > 0.f ? 1.f / m : 0.f;
-          const uint32_t hv = pack_f16x2(x * inv, 0.f);
-          bp.dq_rec[((size_t)sl * G + hh) * kD + dcol] = (uint16_t)(hv & 0xFFFFu);
-          if (n == 0) bp.dq_sc[((size_t)sl * G + hh) * 4 + wave] = m;
+          const float inv = m > 0.f ? bp.scale * __builtin_amdgcn_rcpf(m) : 0.f;
+          // 32 contiguous bytes per lane; the slot's quarter is 512 contiguous bytes.
+          u32x4* rec = reinterpret_cast<u32x4*>(bp.dq_rec + (((size_t)sl * 4 + wave) * G + hh) * 32 + 16 * h);
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            u32x4 v4;
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+              v4[x] = pack_f16x2(qacc[8 * half + 2 * x] * inv, qacc[8 * half + 2 * x + 1] * inv);
+            rec[half] = v4;
+          }
+          if (h == 0) bp.dq_sc[((size_t)sl * 4 + wave) * G + hh] = m;
         }
       }
-    }
+    cur = nx;
+    have = have_next;
   }
 
   // dK (times the softmax scale) and dV of this wave's keys.
@@ -338,10 +394,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
 }
 
 // dq of each (query, group): the sum of its edges' records.  One wave per
-// row; lane l takes 16-byte pieces l, l + 64, ... of the row's G x D values.
+// row; lane l takes 16-byte pieces l, l + 64, ... of the row's records: piece
+// f is quarter f / (4 G), head (f / 4) % G, positions 8 (f % 4) .. + 7, i.e.
+// two runs of 4 consecutive dims (rec_dim).
 template <int G>
 __global__ __launch_bounds__(256) void dq_merge_kernel(BwdParams bp) {
-  constexpr int NF = G * kD / 8;          // 16-byte pieces per row
+  constexpr int NF = G * kD / 8;          // 16-byte pieces per record
   constexpr int F = (NF + 63) / 64;
   const Params& p = bp.e;
   const int lane = threadIdx.x & 63;
@@ -368,9 +426,8 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdParams bp) {
     for (int u = 0; u < F; ++u) {
       const int f = lane + 64 * u;
       if (f >= NF) continue;
-      const int hh = f / 16, dq0 = (f % 16) * 8;
-      const float sc = bp.dq_sc[(slot * G + hh) * 4 + dq0 / 32];
-      const u32x4 x = *reinterpret_cast<const u32x4*>(bp.dq_rec + (slot * G + hh) * kD + dq0);
+      const float sc = bp.dq_sc[slot * 4 * G + f / 4];  // (quarter, head) = f / 4
+      const u32x4 x = *reinterpret_cast<const u32x4*>(bp.dq_rec + slot * (4 * G * 32) + 8 * f);
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
         acc[u][2 * y] += sc * f16_lo(x[y]);
@@ -382,13 +439,16 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdParams bp) {
   for (int u = 0; u < F; ++u) {
     const int f = lane + 64 * u;
     if (f >= NF) continue;
-    const int hh = f / 16, dq0 = (f % 16) * 8;
-    uint4 o;
-    o.x = pack_bf16x2(acc[u][0], acc[u][1]);
-    o.y = pack_bf16x2(acc[u][2], acc[u][3]);
-    o.z = pack_bf16x2(acc[u][4], acc[u][5]);
-    o.w = pack_bf16x2(acc[u][6], acc[u][7]);
-    *reinterpret_cast<uint4*>(bp.dq + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + dq0) = o;
+    const int quarter = f / (4 * G), hh = (f / 4) % G, pos = 8 * (f % 4);
+    uint16_t* o = bp.dq + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD;
+    // positions pos .. pos + 3 and pos + 4 .. pos + 7 are two runs of 4 dims
+    uint2 lo, hi;
+    lo.x = pack_bf16x2(acc[u][0], acc[u][1]);
+    lo.y = pack_bf16x2(acc[u][2], acc[u][3]);
+    hi.x = pack_bf16x2(acc[u][4], acc[u][5]);
+    hi.y = pack_bf16x2(acc[u][6], acc[u][7]);
+    *reinterpret_cast<uint2*>(o + rec_dim(quarter, pos)) = lo;
+    *reinterpret_cast<uint2*>(o + rec_dim(quarter, pos + 4)) = hi;
   }
 }
 
