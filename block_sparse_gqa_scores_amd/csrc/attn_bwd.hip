@@ -25,8 +25,6 @@ namespace msa {
 using namespace edges;
 namespace {
 
-constexpr int kTStride = kBlock + 8;  // bf16 per row of K^T [d][key]
-constexpr int kQStride = 32 + 4;      // bf16 per row of Q^T / dO^T [d][row] (conflict-free)
 constexpr int kSStride = kBlock + 8;  // bf16 per row of dS [row][key]
 constexpr int kSortSmall = 1024;      // buckets up to this size sort in a small workgroup
 
@@ -41,6 +39,25 @@ __device__ __forceinline__ int rsw(int r) { return ((r >> 1) ^ ((r & 1) << 3)) &
 __device__ __forceinline__ int rec_dim(int quarter, int pos) {
   const int h = pos >> 4, r = pos & 15;
   return 32 * quarter + 8 * (r >> 2) + 4 * h + (r & 3);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): each lane names 4 consecutive
+// bf16 values; within each group of 16 lanes, lane i receives, as element e,
+// value i % 4 of those named by lane 4 e + i / 4.  So when lane i of a group
+// names row r0 + i / 4, columns c0 + 4 (i % 4) .. + 3 of a row-major tile,
+// lane i receives rows r0 .. r0 + 3 of column c0 + i: a 4 x 16 block read
+// transposed (checked on the device: lane i gets elements i, i + 16, i + 32,
+// i + 48 of a 64-element run).
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const void* lds_addr) {
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)lds_addr);
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Byte offset of element (row, col) in a row-major [row][128] bf16 tile of
+// 16-byte chunks stored at chunk (col / 8) ^ sw.
+__device__ __forceinline__ int tile_off(int row, int col, int sw) {
+  return row * 256 + 16 * ((col >> 3) ^ sw) + 2 * (col & 7);
 }
 
 struct BwdParams {
@@ -123,11 +140,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
   const Params& p = bp.e;
   __shared__ u32x4 ktile[kBlock * 16];      // K_j [key][16 chunks], swizzled
   __shared__ u32x4 vtile[kBlock * 16];      // V_j, same
-  __shared__ __align__(16) uint32_t kt[kD * kTStride / 2];    // K_j^T [d][key]
   __shared__ u32x4 sq[32 * 16];             // Q rows of the sub-tile [row][chunk], swizzled
   __shared__ u32x4 sdo[32 * 16];            // dO rows, same
-  __shared__ __align__(16) uint32_t sqt[kD * kQStride / 2];   // Q^T [d][row]
-  __shared__ __align__(16) uint32_t sdot[kD * kQStride / 2];  // dO^T [d][row]
   __shared__ __align__(16) uint16_t sds[32 * kSStride];  // dS [row][key] bf16
   __shared__ __align__(16) float s_lse[32];
   __shared__ __align__(16) float s_delta[32];
@@ -145,7 +159,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
   constexpr float kLog2e = 1.4426950408889634f;
   const float c = p.scale_log2;
 
-  {  // K_j, V_j row-major and K_j^T into LDS (rows past S_k clamped: masked for every query)
+  {  // K_j, V_j row-major into LDS (rows past S_k clamped: masked for every query)
     const size_t row_stride = (size_t)p.H_kv * kD;
     const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
     const uint16_t* vb = p.v + ((size_t)b * p.S_k * p.H_kv + g) * kD;
@@ -156,22 +170,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
       const int s = min(j * kBlock + row, p.S_k - 1);
       ktile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * cc);
       vtile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(vb + (size_t)s * row_stride + 8 * cc);
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int u = it * kThreads + tid;
-      const int kp = (u & 15) + 16 * ((u >> 6) & 3);
-      const int d0 = ((u >> 4) & 3) + 4 * ((u >> 8) & 3);
-      const int s0 = min(j * kBlock + 2 * kp, p.S_k - 1);
-      const int s1 = min(j * kBlock + 2 * kp + 1, p.S_k - 1);
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(kb + (size_t)s0 * row_stride + 8 * d0);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(kb + (size_t)s1 * row_stride + 8 * d0);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t a = (e & 1) ? (lo[e >> 1] >> 16) : (lo[e >> 1] & 0xFFFFu);
-        const uint32_t c2 = (e & 1) ? (hi[e >> 1] & 0xFFFF0000u) : (hi[e >> 1] << 16);
-        kt[((8 * d0 + e) * kTStride + 2 * kp) >> 1] = a | c2;
-      }
     }
   }
 
@@ -234,22 +232,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
   if (have) fetch(cur);
   while (have) {
     __syncthreads();  // the previous sub-tile's LDS reads are done
-    {  // stage the fetched rows: row-major and transposed
+    {  // stage the fetched rows (row-major, chunks swizzled by rsw)
 #pragma unroll
       for (int y = 0; y < 2; ++y) {
         const int r = 2 * pr + y;
         sq[r * 16 + (cc ^ rsw(r))] = qa[y];
         sdo[r * 16 + (cc ^ rsw(r))] = da[y];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * cc + e;
-        const uint32_t q0 = (e & 1) ? (qa[0][e >> 1] >> 16) : (qa[0][e >> 1] & 0xFFFFu);
-        const uint32_t q1 = (e & 1) ? (qa[1][e >> 1] & 0xFFFF0000u) : (qa[1][e >> 1] << 16);
-        const uint32_t o0 = (e & 1) ? (da[0][e >> 1] >> 16) : (da[0][e >> 1] & 0xFFFFu);
-        const uint32_t o1 = (e & 1) ? (da[1][e >> 1] & 0xFFFF0000u) : (da[1][e >> 1] << 16);
-        sqt[(d * kQStride + 2 * pr) >> 1] = q0 | q1;
-        sdot[(d * kQStride + 2 * pr) >> 1] = o0 | o1;
       }
       if (tid < 32) {
         s_lse[tid] = f_lse;
@@ -308,14 +296,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
         sa[1] = pack_bf16x2(dsv[8 * kk + 2], dsv[8 * kk + 3]);
         sa[2] = pack_bf16x2(dsv[8 * kk + 4], dsv[8 * kk + 5]);
         sa[3] = pack_bf16x2(dsv[8 * kk + 6], dsv[8 * kk + 7]);
+        // Lane (d = 32 dt + n, h) needs rows r0 .. r0 + 3 and r0 + 8 .. r0 + 11
+        // of column d: two transposing reads of the row-major staged tiles.
         const int r0 = 16 * kk + 4 * h;
+        const int lr = lane & 15;
+        const int ra = r0 + (lr >> 2), rb = r0 + 8 + (lr >> 2);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const int d = 32 * dt + n;
-          const uint2 o0 = *reinterpret_cast<const uint2*>(&sdot[(d * kQStride + r0) >> 1]);
-          const uint2 o1 = *reinterpret_cast<const uint2*>(&sdot[(d * kQStride + r0 + 8) >> 1]);
-          const uint2 q0 = *reinterpret_cast<const uint2*>(&sqt[(d * kQStride + r0) >> 1]);
-          const uint2 q1 = *reinterpret_cast<const uint2*>(&sqt[(d * kQStride + r0 + 8) >> 1]);
+          const int c0 = 32 * dt + 16 * (n >> 4) + 4 * (lr & 3);
+          const uint2 o0 = lds_read_tr16(reinterpret_cast<const char*>(sdo) + tile_off(ra, c0, rsw(ra)));
+          const uint2 o1 = lds_read_tr16(reinterpret_cast<const char*>(sdo) + tile_off(rb, c0, rsw(rb)));
+          const uint2 q0 = lds_read_tr16(reinterpret_cast<const char*>(sq) + tile_off(ra, c0, rsw(ra)));
+          const uint2 q1 = lds_read_tr16(reinterpret_cast<const char*>(sq) + tile_off(rb, c0, rsw(rb)));
           const u32x4 ob = {o0.x, o0.y, o1.x, o1.y};
           const u32x4 qb = {q0.x, q0.y, q1.x, q1.y};
           dv_acc[dt] = mfma32x32x16(pa, ob, dv_acc[dt]);
@@ -336,7 +328,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
       f32x16 qacc = zero16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(&kt[((32 * wave + n) * kTStride + 16 * ks + 8 * h) >> 1]);
+        // K^T operand: keys 16 ks + 8 h .. + 7 of column 32 wave + n, as two
+        // transposing reads of the row-major K tile.
+        const int lr = lane & 15;
+        const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
+        const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
+        const uint2 ka0 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + tile_off(k0, c0, k0 & 15));
+        const uint2 ka1 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + tile_off(k1, c0, k1 & 15));
+        const u32x4 ka = {ka0.x, ka0.y, ka1.x, ka1.y};
         const u32x4 sb = *reinterpret_cast<const u32x4*>(&sds[n * kSStride + 16 * ks + 8 * h]);
         qacc = mfma32x32x16(ka, sb, qacc);
       }
