@@ -19,10 +19,11 @@ MSA_OK = 0
 STATUS_NAMES = {0: "MSA_OK", 1: "MSA_ERR_NULL_PTR", 2: "MSA_ERR_INVALID_DIMS", 3: "MSA_ERR_UNSUPPORTED",
                 4: "MSA_ERR_MISALIGNED", 5: "MSA_ERR_WORKSPACE_TOO_SMALL", 6: "MSA_ERR_HIP"}
 ENTRY_INDEX_SCORES, ENTRY_BLOCK_TOPK, ENTRY_SPARSE_ATTN_FWD, ENTRY_FORWARD, ENTRY_KL_LOSS_FWD = 0, 1, 2, 3, 4
-ENTRY_SPARSE_ATTN_BWD = 5
+ENTRY_SPARSE_ATTN_BWD, ENTRY_KL_LOSS_BWD = 5, 6
 EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
             "msa_forward_profiled", "msa_attn_chunks", "msa_workspace_bytes", "msa_status_str",
-            "msa_block_mask", "msa_mask_blocks", "msa_kl_loss_fwd", "msa_sparse_attn_bwd")
+            "msa_block_mask", "msa_mask_blocks", "msa_kl_loss_fwd", "msa_sparse_attn_bwd",
+            "msa_kl_loss_bwd")
 STAGES = ("index_scores", "block_topk", "attn_build", "attn_partial", "attn_merge")
 
 
@@ -70,11 +71,12 @@ def lib():
                                            ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
         L.msa_block_mask.argtypes = [D, P, P, P]
         L.msa_mask_blocks.argtypes = [D, P, P, P]
-        L.msa_kl_loss_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_kl_loss_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_kl_loss_bwd.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
         L.msa_sparse_attn_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for f in (L.msa_index_scores, L.msa_block_topk, L.msa_sparse_attn_fwd, L.msa_forward,
                   L.msa_forward_profiled, L.msa_block_mask, L.msa_mask_blocks, L.msa_kl_loss_fwd,
-                  L.msa_sparse_attn_bwd):
+                  L.msa_sparse_attn_bwd, L.msa_kl_loss_bwd):
             f.restype = ctypes.c_int
         L.msa_attn_chunks.argtypes = [D]
         L.msa_attn_chunks.restype = ctypes.c_int
@@ -261,13 +263,14 @@ def default_softmax_scale(head_dim: int = 128) -> float:
 
 
 def msa_kl_loss_fwd(q, k, q_idx, k_idx, block_idx, lse, *, block_size=128, softmax_scale=0.0,
-                    return_rows=False, workspace=None):
+                    return_rows=False, return_lse_idx=False, workspace=None):
     """Alignment loss of the index branch (forward value): the mean over
     (batch, query, group) rows of KL(group-mean main-branch probabilities ||
     softmax of the index scores) on each row's selected tokens.  ``lse`` is
     the main branch's log-sum-exp over the same selection ([B, H_q, S_q], as
-    msa_forward returns it).  Returns the loss as a 0-d fp32 tensor, and the
-    per-row terms [B, H_kv, S_q] when return_rows is set."""
+    msa_forward returns it).  Returns the loss as a 0-d fp32 tensor, then the
+    per-row terms [B, H_kv, S_q] when return_rows is set and the rows'
+    log-sum-exps of the index scores [B, H_kv, S_q] when return_lse_idx is."""
     import torch
     for n, t, nd in (("q", q, 4), ("k", k, 4), ("q_idx", q_idx, 4), ("k_idx", k_idx, 3)):
         _bf16_cuda(n, t, nd)
@@ -281,14 +284,16 @@ def msa_kl_loss_fwd(q, k, q_idx, k_idx, block_idx, lse, *, block_size=128, softm
     if tuple(block_idx.shape[:3]) != (d.batch, d.num_heads_kv, d.seqlen_q):
         raise ValueError("block_idx must be [B, H_kv, S_q, topk]")
     loss = torch.empty((), dtype=torch.float32, device=q.device)
-    rows = torch.empty((d.batch, d.num_heads_kv, d.seqlen_q), dtype=torch.float32, device=q.device) \
-        if return_rows else None
+    shape = (d.batch, d.num_heads_kv, d.seqlen_q)
+    rows = torch.empty(shape, dtype=torch.float32, device=q.device) if return_rows else None
+    lse_idx = torch.empty(shape, dtype=torch.float32, device=q.device) if return_lse_idx else None
     ws, nbytes = _workspace(d, ENTRY_KL_LOSS_FWD, workspace, q.device)
     rc = lib().msa_kl_loss_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx),
-                               _ptr(block_idx), _ptr(lse), _ptr(rows), _ptr(loss), _ptr(ws), nbytes,
-                               _stream(q.device))
+                               _ptr(block_idx), _ptr(lse), _ptr(rows), _ptr(loss), _ptr(lse_idx), _ptr(ws),
+                               nbytes, _stream(q.device))
     _check(rc, "msa_kl_loss_fwd")
-    return (loss, rows) if return_rows else loss
+    res = [loss] + ([rows] if return_rows else []) + ([lse_idx] if return_lse_idx else [])
+    return res[0] if len(res) == 1 else tuple(res)
 
 
 def msa_sparse_attn_bwd(q, k, v, block_idx, out, lse, dout, *, block_size=128, softmax_scale=0.0,
@@ -310,3 +315,26 @@ def msa_sparse_attn_bwd(q, k, v, block_idx, out, lse, dout, *, block_size=128, s
                                    _stream(q.device))
     _check(rc, "msa_sparse_attn_bwd")
     return dq, dk, dv
+
+
+def msa_kl_loss_bwd(q, k, q_idx, k_idx, block_idx, lse, lse_idx, grad_loss=1.0, *, block_size=128,
+                    softmax_scale=0.0, workspace=None):
+    """Gradient of grad_loss * (the alignment loss) with respect to q_idx and
+    k_idx, the teacher detached: returns (dq_idx, dk_idx), bf16.  lse is the
+    main branch's LSE and lse_idx the index scores' LSE of msa_kl_loss_fwd."""
+    import torch
+    for n, t, nd in (("q", q, 4), ("k", k, 4), ("q_idx", q_idx, 4), ("k_idx", k_idx, 3)):
+        _bf16_cuda(n, t, nd)
+    d = dims_of(q, k, q_idx, k_idx, topk=block_idx.shape[-1], block_size=block_size,
+                softmax_scale=softmax_scale)
+    for n, t, dt in (("block_idx", block_idx, torch.int32), ("lse", lse, torch.float32),
+                     ("lse_idx", lse_idx, torch.float32)):
+        if not (t.is_cuda and t.dtype == dt and t.is_contiguous()):
+            raise ValueError(f"{n} must be a contiguous {dt} CUDA tensor")
+    dq_idx, dk_idx = torch.empty_like(q_idx), torch.empty_like(k_idx)
+    ws, nbytes = _workspace(d, ENTRY_KL_LOSS_BWD, workspace, q.device)
+    rc = lib().msa_kl_loss_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx),
+                               _ptr(lse), _ptr(lse_idx), float(grad_loss), _ptr(dq_idx), _ptr(dk_idx), _ptr(ws),
+                               nbytes, _stream(q.device))
+    _check(rc, "msa_kl_loss_bwd")
+    return dq_idx, dk_idx

@@ -28,38 +28,6 @@ namespace {
 constexpr int kSStride = kBlock + 8;  // bf16 per row of dS [row][key]
 constexpr int kSortSmall = 1024;      // buckets up to this size sort in a small workgroup
 
-// Chunk swizzle of the staged rows: distinct chunks both for 16 consecutive
-// rows (the MFMA operand reads) and for 16 rows of one parity (the staging
-// writes), so neither conflicts on LDS banks.
-__device__ __forceinline__ int rsw(int r) { return ((r >> 1) ^ ((r & 1) << 3)) & 15; }
-
-// dq records: per slot, 4 quarters of the head dims x G heads x 32 values in
-// the order the dq tile holds them, position p = 16 h + r for MFMA register r
-// of lane half h, which is dim 32 quarter + 8 (r / 4) + 4 h + r % 4.
-__device__ __forceinline__ int rec_dim(int quarter, int pos) {
-  const int h = pos >> 4, r = pos & 15;
-  return 32 * quarter + 8 * (r >> 2) + 4 * h + (r & 3);
-}
-
-// Transposing LDS read (ds_read_b64_tr_b16): each lane names 4 consecutive
-// bf16 values; within each group of 16 lanes, lane i receives, as element e,
-// value i % 4 of those named by lane 4 e + i / 4.  So when lane i of a group
-// names row r0 + i / 4, columns c0 + 4 (i % 4) .. + 3 of a row-major tile,
-// lane i receives rows r0 .. r0 + 3 of column c0 + i: a 4 x 16 block read
-// transposed (checked on the device: lane i gets elements i, i + 16, i + 32,
-// i + 48 of a 64-element run).
-typedef short v4s __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint2 lds_read_tr16(const void* lds_addr) {
-  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)lds_addr);
-  return __builtin_bit_cast(uint2, r);
-}
-
-// Byte offset of element (row, col) in a row-major [row][128] bf16 tile of
-// 16-byte chunks stored at chunk (col / 8) ^ sw.
-__device__ __forceinline__ int tile_off(int row, int col, int sw) {
-  return row * 256 + 16 * ((col >> 3) ^ sw) + 2 * (col & 7);
-}
-
 struct BwdParams {
   Params e;              // edge buckets, q, k, v, idx and shapes of the chunk
   const uint16_t* dout;  // [B][S_q][H_q][D] bf16
@@ -304,10 +272,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const int c0 = 32 * dt + 16 * (n >> 4) + 4 * (lr & 3);
-          const uint2 o0 = lds_read_tr16(reinterpret_cast<const char*>(sdo) + tile_off(ra, c0, rsw(ra)));
-          const uint2 o1 = lds_read_tr16(reinterpret_cast<const char*>(sdo) + tile_off(rb, c0, rsw(rb)));
-          const uint2 q0 = lds_read_tr16(reinterpret_cast<const char*>(sq) + tile_off(ra, c0, rsw(ra)));
-          const uint2 q1 = lds_read_tr16(reinterpret_cast<const char*>(sq) + tile_off(rb, c0, rsw(rb)));
+          const uint2 o0 = lds_read_tr16(reinterpret_cast<const char*>(sdo) + lds_tile_off(ra, c0, rsw(ra)));
+          const uint2 o1 = lds_read_tr16(reinterpret_cast<const char*>(sdo) + lds_tile_off(rb, c0, rsw(rb)));
+          const uint2 q0 = lds_read_tr16(reinterpret_cast<const char*>(sq) + lds_tile_off(ra, c0, rsw(ra)));
+          const uint2 q1 = lds_read_tr16(reinterpret_cast<const char*>(sq) + lds_tile_off(rb, c0, rsw(rb)));
           const u32x4 ob = {o0.x, o0.y, o1.x, o1.y};
           const u32x4 qb = {q0.x, q0.y, q1.x, q1.y};
           dv_acc[dt] = mfma32x32x16(pa, ob, dv_acc[dt]);
@@ -333,8 +301,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
         const int lr = lane & 15;
         const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
         const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
-        const uint2 ka0 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + tile_off(k0, c0, k0 & 15));
-        const uint2 ka1 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + tile_off(k1, c0, k1 & 15));
+        const uint2 ka0 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + lds_tile_off(k0, c0, k0 & 15));
+        const uint2 ka1 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + lds_tile_off(k1, c0, k1 & 15));
         const u32x4 ka = {ka0.x, ka0.y, ka1.x, ka1.y};
         const u32x4 sb = *reinterpret_cast<const u32x4*>(&sds[n * kSStride + 16 * ks + 8 * h]);
         qacc = mfma32x32x16(ka, sb, qacc);
@@ -479,6 +447,17 @@ BwdLayout make_bwd_layout(const AttnShape& s) {
   return B;
 }
 
+}  // namespace
+
+namespace edges {
+void launch_bucket_sort(const Layout& L, const Params& p, hipStream_t st) {
+  hipLaunchKernelGGL((bucket_sort_kernel<kSortSmall, false>), dim3((unsigned)L.NB), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((bucket_sort_kernel<kMaxWindow, true>), dim3((unsigned)L.NB), dim3(256), 0, st, p);
+}
+}  // namespace edges
+
+namespace {
+
 template <int G>
 hipError_t launch_bwd_g(const AttnShape& s, const BwdLayout& BL, BwdParams bp, hipStream_t st) {
   const Layout& L = BL.L;
@@ -489,8 +468,7 @@ hipError_t launch_bwd_g(const AttnShape& s, const BwdLayout& BL, BwdParams bp, h
     bp.first = ci == 0;
     bp.last = q0 + L.Qc >= s.S_q;
     launch_build(s, L, bp.e, st);
-    hipLaunchKernelGGL((bucket_sort_kernel<kSortSmall, false>), dim3((unsigned)L.NB), dim3(256), 0, st, bp.e);
-    hipLaunchKernelGGL((bucket_sort_kernel<kMaxWindow, true>), dim3((unsigned)L.NB), dim3(256), 0, st, bp.e);
+    launch_bucket_sort(L, bp.e, st);
     hipLaunchKernelGGL(attn_bwd_kernel<G>, dim3((unsigned)(s.batch * s.H_kv * s.n_blk)), dim3(kThreads), 0, st, bp);
     const long mrows = (long)s.batch * s.H_kv * L.Qc;
     hipLaunchKernelGGL(dq_merge_kernel<G>, dim3((unsigned)((mrows + 3) / 4)), dim3(256), 0, st, bp);

@@ -206,6 +206,31 @@ __device__ __forceinline__ float allred16(float x) {
   return combine<MAX>(a, b);
 }
 
+// Chunk swizzle of the staged rows: distinct chunks both for 16 consecutive
+// rows (the MFMA operand reads) and for 16 rows of one parity (the staging
+// writes), so neither conflicts on LDS banks.
+__device__ __forceinline__ int rsw(int r) { return ((r >> 1) ^ ((r & 1) << 3)) & 15; }
+
+// Transposing LDS read (ds_read_b64_tr_b16): each lane names 4 consecutive
+// bf16 values; within each group of 16 lanes, lane i receives, as element e,
+// value i % 4 of those named by lane 4 e + i / 4.  So when lane i of a group
+// names row r0 + i / 4, columns c0 + 4 (i % 4) .. + 3 of a row-major tile,
+// lane i receives rows r0 .. r0 + 3 of column c0 + i: a 4 x 16 block read
+// transposed (checked on the device: lane i gets elements i, i + 16, i + 32,
+// i + 48 of a 64-element run).
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const void* lds_addr) {
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)lds_addr);
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Byte offset of element (row, col) in a row-major bf16 tile of CH 16-byte
+// chunks per row (CH * 8 columns), chunk c of a row stored at c ^ sw.
+template <int CH = 16>
+__device__ __forceinline__ int lds_tile_off(int row, int col, int sw) {
+  return row * (16 * CH) + 16 * ((col >> 3) ^ sw) + 2 * (col & 7);
+}
+
 // Order-preserving unsigned key of a float: a < b (non-NaN) iff key(a) < key(b).
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);

@@ -58,6 +58,7 @@ struct Params {
   const float* lse_in;   // [B][H_q][S_q] natural-log LSE of the main branch
   float* kl_rec;         // [slot][8]: sum P, sum P ln P, sum P (z - m), sum e^(z - m), m
   float* kl_rows;        // [B][H_kv][S_q] or null
+  float* kl_lse;         // [B][H_kv][S_q]: log-sum-exp of the index scores over T, or null
   float* kl_wsum;        // per merge workgroup: sum of its rows' terms
   float* loss;           // or null
 };
@@ -76,6 +77,15 @@ struct Layout {
   int n_kl_wg;
 };
 
+// Gradient records of the backward kernels: per slot, quarters of 32 dims
+// (x heads) of 32 values each, in the order a transposed MFMA tile holds
+// them: position p = 16 h + r for MFMA register r of lane half h, which is
+// dim 32 quarter + 8 (r / 4) + 4 h + r % 4.
+__device__ __forceinline__ int rec_dim(int quarter, int pos) {
+  const int h = pos >> 4, r = pos & 15;
+  return 32 * quarter + 8 * (r >> 2) + 4 * h + (r & 3);
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline int grid_cap(long n, int per) {
@@ -88,6 +98,9 @@ inline int grid_cap(long n, int per) {
 size_t layout_build(Layout& L, const AttnShape& s);
 // Edge buckets of the chunk starting at p.q0: counts, scans, scatter.
 void launch_build(const AttnShape& s, const Layout& L, const Params& p, hipStream_t st);
+// Sorts each bucket's edge slots ascending, so that work that sums over a
+// bucket's edges does so in a fixed order (attn_bwd.hip).
+void launch_bucket_sort(const Layout& L, const Params& p, hipStream_t st);
 // Params with the shape, the layout and the build arrays of `base` filled in.
 Params base_params(const AttnShape& s, const Layout& L, char* base, const int32_t* idx);
 

@@ -57,6 +57,13 @@ hipError_t launch_sparse_attn_bwd(const AttnShape& s, const uint16_t* q, const u
                                   uint16_t* dk, uint16_t* dv, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
 
+// Alignment loss, backward (see kl_bwd.hip).
+size_t kl_loss_bwd_workspace(const AttnShape& s, int D_idx);
+hipError_t launch_kl_loss_bwd(const AttnShape& s, int D_idx, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* q_idx, const uint16_t* k_idx, const int32_t* idx,
+                              const float* lse, const float* lse_idx, float coef, uint16_t* dq_idx,
+                              uint16_t* dk_idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
 // Writes n zero floats (a kernel, so the call can sit inside a graph capture).
 hipError_t launch_fill_zero(float* dst, long n, hipStream_t stream);
 
@@ -64,7 +71,7 @@ hipError_t launch_fill_zero(float* dst, long n, hipStream_t stream);
 size_t kl_loss_workspace(const AttnShape& s);
 hipError_t launch_kl_loss(const AttnShape& s, int D_idx, const uint16_t* q, const uint16_t* k,
                           const uint16_t* q_idx, const uint16_t* k_idx, const int32_t* idx,
-                          const float* lse, float* kl_rows, float* loss, void* ws, size_t ws_bytes,
-                          hipStream_t stream);
+                          const float* lse, float* kl_rows, float* loss, float* lse_idx, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
 
 }  // namespace msa

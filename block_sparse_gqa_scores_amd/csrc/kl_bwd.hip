@@ -1,0 +1,408 @@
+// Alignment loss, backward: gradients of c * sum_rows KL_row with respect to
+// the index inputs q_idx and k_idx (Sparse Attention Part II, section 3.2:
+// the teacher is detached, so nothing flows into the main branch; the
+// indexer's input is detached too, so these are the gradients the index
+// projections receive).  For row (b, g, i) over its tokens T,
+//   d KL_row / d z_s = Pidx_s - P_s,   Pidx_s = exp(z_s - LSE_z),
+//   P_s = (1/G) sum_h exp(scale q_h . k_s - lse_h)   (the teacher),
+// so with g_s = c (Pidx_s - P_s):
+//   dq_idx[b][i][g] = sum_s g_s k_idx[b][s],
+//   dk_idx[b][s] = sum over rows (b, g, i) with s in T of g_s q_idx[b][i][g].
+// c is the caller's gradient of the loss divided by B * S_q * H_kv (the loss
+// is the mean of the row terms).
+//
+// Schedule: as the main-branch backward (attn_bwd.hip).  One workgroup per
+// (batch, group, block) runs every edge of the block in sorted order; its four
+// waves split the block's keys.  Per 32-row sub-tile (32 / G queries x G
+// heads) it recomputes the teacher from S = Q K^T and the forward's LSE (the
+// head mean is an in-lane sum plus one half-wave exchange), the index scores
+// z with the query's index row repeated on its heads' rows, then g.  The
+// block's dk_idx accumulates in registers (per group; the groups are added in
+// a fixed order at the end, since all groups share one index key head);
+// dq_idx of each edge goes through LDS and a per-edge fp16 record, added per
+// row by a merge.
+#include "edge_buckets.h"
+
+namespace msa {
+using namespace edges;
+namespace {
+
+constexpr int kGStride = kBlock + 8;  // bf16 per row of the g tile [row][key]
+
+struct KlBwdParams {
+  Params e;
+  const float* lse;      // main-branch LSE [B][H_q][S_q] (natural log)
+  const float* lse_idx;  // [B][H_kv][S_q]: log-sum-exp of z over T (natural log)
+  float coef;            // gradient of the loss / (B * S_q * H_kv)
+  uint16_t* rec;         // [slot][D_idx / 32][32] fp16 (rec_dim order) / scale
+  float* rec_sc;         // [slot][D_idx / 32]
+  float* dk_part;        // [B][H_kv][S_k][D_idx] fp32, per group
+  uint16_t* dq_idx;      // [B][S_q][H_kv][D_idx] bf16
+  uint16_t* dk_idx;      // [B][S_k][D_idx] bf16
+  int D_idx;
+  int first;             // this chunk is the first (dk_part is stored, not added)
+};
+
+template <int G, int DIDX>
+__global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
+  constexpr int QW = 32 / G;
+  constexpr int ICH = DIDX / 8;             // 16-byte chunks per index row
+  constexpr int NDT = DIDX / 32;            // 32-dim tiles of the index dims
+  constexpr int RPS = G >= 8 ? G / 2 : G;   // registers of one query in a lane
+  constexpr int NL = 16 / RPS;              // queries per lane
+  const Params& p = kp.e;
+  __shared__ u32x4 ktile[kBlock * 16];      // K_j rows, chunk c at c ^ (key & 15)
+  __shared__ u32x4 itile[kBlock * ICH];     // k_idx rows, chunk c at c ^ (key & (ICH - 1))
+  __shared__ u32x4 sq[32 * 16];             // Q rows of the sub-tile, chunk c at c ^ rsw(row)
+  __shared__ u32x4 sqi[32 * ICH];           // q_idx row of each row's query, chunk c at c ^ (rsw(row) & (ICH - 1))
+  __shared__ __align__(16) uint16_t sg[32 * kGStride];  // g [row][key] bf16
+  __shared__ __align__(16) float s_lse[32];
+  __shared__ float s_lsez[QW];
+  __shared__ int s_t[QW];
+  __shared__ int s_slot[QW];
+
+  const int BG = p.B * p.H_kv;
+  const int j = blockIdx.x / BG;
+  const int bg = blockIdx.x - j * BG;
+  const int b = bg / p.H_kv;
+  const int g = bg - b * p.H_kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int n = lane & 31;
+  const int off = p.S_k - p.S_q;
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float c = p.scale_log2;
+  const float invG = 1.f / G;
+
+  {  // K_j and k_idx of block j (rows past S_k clamped: never visible)
+    const size_t row_stride = (size_t)p.H_kv * kD;
+    const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int qd = it * kThreads + tid;
+      const int row = qd >> 4, cc = qd & 15;
+      const int s = min(j * kBlock + row, p.S_k - 1);
+      ktile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * cc);
+    }
+    const uint16_t* ib = p.k_idx + (size_t)b * p.S_k * DIDX;
+#pragma unroll
+    for (int it = 0; it < kBlock * ICH / kThreads; ++it) {
+      const int qd = it * kThreads + tid;
+      const int row = qd / ICH, cc = qd % ICH;
+      const int s = min(j * kBlock + row, p.S_k - 1);
+      itile[row * ICH + (cc ^ (row & (ICH - 1)))] = *reinterpret_cast<const u32x4*>(ib + (size_t)s * DIDX + 8 * cc);
+    }
+  }
+
+  f32x16 dk_acc[NDT];  // [key row][index-dim tile]: this wave's 32 keys
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) dk_acc[dt] = zero16();
+  const int key0 = 32 * wave;
+  const int key_abs = j * kBlock + key0 + n;
+
+  struct Cursor {
+    int w, base, cnt;
+    const int32_t* ed;
+  };
+  auto next = [&](Cursor& cu) {  // uniform; false past the last sub-tile
+    cu.base += QW;
+    while (cu.base >= cu.cnt) {
+      if (++cu.w >= p.n_win) return false;
+      const long bucket = ((long)bg * p.n_win + cu.w) * p.n_blk + j;
+      cu.cnt = p.counts[bucket];
+      cu.ed = p.edges + p.offsets[bucket];
+      cu.base = 0;
+    }
+    return true;
+  };
+  Cursor cur{-1, -QW, 0, nullptr};
+  bool have = next(cur);
+  while (have) {
+    __syncthreads();  // the previous sub-tile's LDS reads are done
+    {  // stage rows r = q * G + hh: Q rows, the query's index row, statistics
+      const int pr = tid & 15, cc = tid >> 4;  // rows (2 pr, 2 pr + 1), chunk cc
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        const int r = 2 * pr + y, q = r / G, hh = r - (r / G) * G;
+        const int sl = cur.ed[min(cur.base + q, cur.cnt - 1)];
+        const int i = p.q0 + (int)((sl / p.topk) % p.Qc);
+        sq[r * 16 + (cc ^ rsw(r))] =
+            *reinterpret_cast<const u32x4*>(p.q + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + 8 * cc);
+        if (cc < ICH)
+          sqi[r * ICH + (cc ^ (rsw(r) & (ICH - 1)))] =
+              *reinterpret_cast<const u32x4*>(p.q_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX + 8 * cc);
+      }
+      if (tid < 32) {
+        const int r = tid, q = r / G, hh = r - (r / G) * G;
+        const bool valid = cur.base + q < cur.cnt;
+        const int sl = cur.ed[min(cur.base + q, cur.cnt - 1)];
+        const int i = p.q0 + (int)((sl / p.topk) % p.Qc);
+        s_lse[r] = valid ? kp.lse[((size_t)b * p.H_q + g * G + hh) * p.S_q + i] * kLog2e : __builtin_inff();
+        if (hh == 0) {
+          s_lsez[q] = valid ? kp.lse_idx[((size_t)b * p.H_kv + g) * p.S_q + i] * kLog2e : __builtin_inff();
+          s_t[q] = valid ? i + off : -1;
+          s_slot[q] = valid ? sl : -1;
+        }
+      }
+    }
+    __syncthreads();
+    Cursor nx = cur;
+    const bool have_next = next(nx);
+
+    // S and z for this wave's 32 keys: rows on registers, keys on lanes.
+    f32x16 sacc = zero16(), zacc = zero16();
+    const int krow = key0 + n;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int ch = 2 * ks + h;
+      sacc = mfma32x32x16(sq[n * 16 + (ch ^ rsw(n))], ktile[krow * 16 + (ch ^ (krow & 15))], sacc);
+    }
+#pragma unroll
+    for (int ks = 0; ks < DIDX / 16; ++ks) {
+      const int ch = 2 * ks + h;
+      zacc = mfma32x32x16(sqi[n * ICH + (ch ^ (rsw(n) & (ICH - 1)))], itile[krow * ICH + (ch ^ (krow & (ICH - 1)))], zacc);
+    }
+    // Teacher per (query slot l, key): the mean over the query's heads.
+    float lse4[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 a = *reinterpret_cast<const float4*>(&s_lse[8 * r4 + 4 * h]);
+      lse4[4 * r4] = a.x; lse4[4 * r4 + 1] = a.y; lse4[4 * r4 + 2] = a.z; lse4[4 * r4 + 3] = a.w;
+    }
+    float gq[NL];
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      float acc = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < RPS; ++rr) {
+        const int r = l * RPS + rr;
+        acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse4[r]));
+      }
+      if constexpr (G >= 8) acc += swap_halves(acc);
+      const int q = mfma32_row(l * RPS, lane) / G;
+      const bool vis = key_abs <= s_t[q];
+      const float pidx = __builtin_amdgcn_exp2f(__builtin_fmaf(zacc[l * RPS], kLog2e, -s_lsez[q]));
+      gq[l] = vis ? kp.coef * (pidx - acc * invG) : 0.f;
+    }
+    // dk_idx += g^T q_idx: A = g of each register's row (a query's value on
+    // each of its G rows, times 1/G), B = the rows' index rows, transposed.
+    {
+      const int lr = lane & 15;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 ga;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r0 = 8 * kk + 2 * x;
+          ga[x] = pack_bf16x2(gq[r0 / RPS] * invG, gq[(r0 + 1) / RPS] * invG);
+        }
+        const int rbase = 16 * kk + 4 * h;
+        const int ra = rbase + (lr >> 2), rb = rbase + 8 + (lr >> 2);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int c0 = 32 * dt + 16 * (n >> 4) + 4 * (lr & 3);
+          const uint2 b0 = lds_read_tr16(reinterpret_cast<const char*>(sqi) + lds_tile_off<ICH>(ra, c0, rsw(ra) & (ICH - 1)));
+          const uint2 b1 = lds_read_tr16(reinterpret_cast<const char*>(sqi) + lds_tile_off<ICH>(rb, c0, rsw(rb) & (ICH - 1)));
+          const u32x4 bb = {b0.x, b0.y, b1.x, b1.y};
+          dk_acc[dt] = mfma32x32x16(ga, bb, dk_acc[dt]);
+        }
+      }
+    }
+    // g to LDS as [row][key] for dq_idx (each row carries its query's g).
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      sg[mfma32_row(r, lane) * kGStride + key0 + n] = (uint16_t)(pack_bf16x2(gq[r / RPS], 0.f) & 0xFFFFu);
+    __syncthreads();
+
+    // dq_idx^T[c'][row] = sum_key k_idx^T[c'][key] g[row][key] for index dims
+    // 32 wave .. 32 wave + 31 (waves past D_idx / 32 idle); one record per query.
+    if (wave < NDT) {
+      f32x16 qacc = zero16();
+      const int lr = lane & 15;
+      const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
+        const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k0, c0, k0 & (ICH - 1)));
+        const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k1, c0, k1 & (ICH - 1)));
+        const u32x4 ka = {a0.x, a0.y, a1.x, a1.y};
+        const u32x4 gb = *reinterpret_cast<const u32x4*>(&sg[n * kGStride + 16 * ks + 8 * h]);
+        qacc = mfma32x32x16(ka, gb, qacc);
+      }
+      const int q = n / G, hh = n - (n / G) * G;
+      const int sl = s_slot[q];
+      float m = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = max3abs(qacc[r], qacc[r], m);
+      m = __builtin_fmaxf(m, swap_halves(m));
+      if (hh == 0 && sl >= 0) {
+        const float inv = m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
+        u32x4* rec = reinterpret_cast<u32x4*>(kp.rec + ((size_t)sl * NDT + wave) * 32 + 16 * h);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          u32x4 v4;
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            v4[x] = pack_f16x2(qacc[8 * half + 2 * x] * inv, qacc[8 * half + 2 * x + 1] * inv);
+          rec[half] = v4;
+        }
+        if (h == 0) kp.rec_sc[(size_t)sl * NDT + wave] = m;
+      }
+    }
+    cur = nx;
+    have = have_next;
+  }
+
+  // This group's dk_idx for the wave's keys (fp32, summed over chunks).
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int dcol = 32 * dt + n;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = j * kBlock + key0 + mfma32_row(r, lane);
+      if (key >= p.S_k) continue;
+      float* o = kp.dk_part + (((size_t)b * p.H_kv + g) * p.S_k + key) * DIDX + dcol;
+      *o = kp.first ? dk_acc[dt][r] : *o + dk_acc[dt][r];
+    }
+  }
+}
+
+// dq_idx of each row: the sum of its edges' records; 16 lanes per row, 8
+// index dims each.
+template <int DIDX>
+__global__ __launch_bounds__(256) void kl_dq_merge_kernel(KlBwdParams kp) {
+  constexpr int NDT = DIDX / 32;
+  constexpr int NP = DIDX / 8;  // 16-byte pieces per record
+  const Params& p = kp.e;
+  const long r = ((long)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int f = threadIdx.x & 15;
+  if (r >= (long)p.B * p.H_kv * p.Qc || f >= NP) return;
+  const int il = (int)(r % p.Qc);
+  const int bg = (int)(r / p.Qc);
+  const int i = p.q0 + il;
+  if (i >= p.S_q) return;
+  const int b = bg / p.H_kv, g = bg - (bg / p.H_kv) * p.H_kv;
+  const int32_t* sel = p.idx + ((long)bg * p.S_q + i) * p.topk;
+  const int local = (i + p.S_k - p.S_q) / kBlock;
+  const long slot0 = ((long)bg * p.Qc + il) * p.topk;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < p.topk; ++e) {
+    const int jj = sel[e];
+    if (jj < 0 || jj > local) continue;
+    const long slot = slot0 + e;
+    const float sc = kp.rec_sc[slot * NDT + f / 4];
+    const u32x4 x = *reinterpret_cast<const u32x4*>(kp.rec + slot * DIDX + 8 * f);
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      acc[2 * y] += sc * f16_lo(x[y]);
+      acc[2 * y + 1] += sc * f16_hi(x[y]);
+    }
+  }
+  uint16_t* o = kp.dq_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX;
+  const int quarter = f / 4, pos = 8 * (f % 4);
+  uint2 lo, hi;
+  lo.x = pack_bf16x2(acc[0], acc[1]);
+  lo.y = pack_bf16x2(acc[2], acc[3]);
+  hi.x = pack_bf16x2(acc[4], acc[5]);
+  hi.y = pack_bf16x2(acc[6], acc[7]);
+  *reinterpret_cast<uint2*>(o + rec_dim(quarter, pos)) = lo;
+  *reinterpret_cast<uint2*>(o + rec_dim(quarter, pos + 4)) = hi;
+}
+
+// dk_idx = the sum of the groups' parts, in group order.
+template <int DIDX>
+__global__ __launch_bounds__(256) void kl_dk_reduce_kernel(KlBwdParams kp) {
+  const Params& p = kp.e;
+  const long n = (long)p.B * p.S_k * DIDX;
+  for (long x = (long)blockIdx.x * 256 + threadIdx.x; x < n; x += (long)gridDim.x * 256) {
+    const int c2 = (int)(x % DIDX);
+    const long bs = x / DIDX;
+    const int s = (int)(bs % p.S_k);
+    const int b = (int)(bs / p.S_k);
+    float acc = 0.f;
+    for (int g = 0; g < p.H_kv; ++g) acc += kp.dk_part[(((size_t)b * p.H_kv + g) * p.S_k + s) * DIDX + c2];
+    kp.dk_idx[x] = (uint16_t)(pack_bf16x2(acc, 0.f) & 0xFFFFu);
+  }
+}
+
+struct KlBwdLayout {
+  Layout L;
+  size_t rec, rec_sc, dk_part, total;
+};
+
+KlBwdLayout make_kl_bwd_layout(const AttnShape& s, int D_idx) {
+  KlBwdLayout K{};
+  Layout& L = K.L;
+  const int G = s.H_q / s.H_kv;
+  L.QT = kSubTiles * 4 * (32 / G);
+  const size_t per_query = (size_t)s.batch * s.H_kv * s.topk * ((size_t)D_idx * 2 + 16 + 4);
+  long qc = (long)(kPartBudget / per_query);
+  if (qc >= 128) qc -= qc % 128;
+  L.Qc = (int)std::max(1L, std::min<long>(qc, s.S_q));
+  size_t o = layout_build(L, s);
+  K.rec = o;     o = align256(o + (size_t)L.E * D_idx * 2);
+  K.rec_sc = o;  o = align256(o + (size_t)L.E * (D_idx / 32) * 4);
+  K.dk_part = o; o = align256(o + (size_t)s.batch * s.H_kv * s.S_k * D_idx * 4);
+  K.total = o;
+  L.total = o;
+  return K;
+}
+
+template <int G, int DIDX>
+hipError_t launch_kl_bwd_g(const AttnShape& s, const KlBwdLayout& K, KlBwdParams kp, hipStream_t st) {
+  const Layout& L = K.L;
+  for (int q0 = 0, ci = 0; q0 < s.S_q; q0 += L.Qc, ++ci) {
+    kp.e.q0 = q0;
+    kp.first = ci == 0;
+    launch_build(s, L, kp.e, st);
+    launch_bucket_sort(L, kp.e, st);
+    hipLaunchKernelGGL((kl_bwd_kernel<G, DIDX>), dim3((unsigned)(s.batch * s.H_kv * s.n_blk)), dim3(kThreads), 0, st, kp);
+    const long rows = (long)s.batch * s.H_kv * L.Qc;
+    hipLaunchKernelGGL(kl_dq_merge_kernel<DIDX>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, st, kp);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const long n = (long)s.batch * s.S_k * DIDX;
+  hipLaunchKernelGGL(kl_dk_reduce_kernel<DIDX>, dim3(grid_cap(n, 256)), dim3(256), 0, st, kp);
+  return hipGetLastError();
+}
+
+template <int DIDX>
+hipError_t launch_kl_bwd_d(const AttnShape& s, const KlBwdLayout& K, const KlBwdParams& kp, hipStream_t st) {
+  switch (kp.e.G) {
+    case 1: return launch_kl_bwd_g<1, DIDX>(s, K, kp, st);
+    case 2: return launch_kl_bwd_g<2, DIDX>(s, K, kp, st);
+    case 4: return launch_kl_bwd_g<4, DIDX>(s, K, kp, st);
+    case 8: return launch_kl_bwd_g<8, DIDX>(s, K, kp, st);
+    case 16: return launch_kl_bwd_g<16, DIDX>(s, K, kp, st);
+    case 32: return launch_kl_bwd_g<32, DIDX>(s, K, kp, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+size_t kl_loss_bwd_workspace(const AttnShape& s, int D_idx) { return make_kl_bwd_layout(s, D_idx).total; }
+
+hipError_t launch_kl_loss_bwd(const AttnShape& s, int D_idx, const uint16_t* q, const uint16_t* k,
+                              const uint16_t* q_idx, const uint16_t* k_idx, const int32_t* idx,
+                              const float* lse, const float* lse_idx, float coef, uint16_t* dq_idx,
+                              uint16_t* dk_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const KlBwdLayout K = make_kl_bwd_layout(s, D_idx);
+  if (ws_bytes < K.total) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(ws);
+  KlBwdParams kp{};
+  kp.e = base_params(s, K.L, base, idx);
+  kp.e.q = q; kp.e.k = k; kp.e.q_idx = q_idx; kp.e.k_idx = k_idx;
+  kp.lse = lse; kp.lse_idx = lse_idx; kp.coef = coef;
+  kp.rec = reinterpret_cast<uint16_t*>(base + K.rec);
+  kp.rec_sc = reinterpret_cast<float*>(base + K.rec_sc);
+  kp.dk_part = reinterpret_cast<float*>(base + K.dk_part);
+  kp.dq_idx = dq_idx; kp.dk_idx = dk_idx; kp.D_idx = D_idx;
+  switch (D_idx) {
+    case 64: return launch_kl_bwd_d<64>(s, K, kp, stream);
+    case 128: return launch_kl_bwd_d<128>(s, K, kp, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace msa

@@ -318,8 +318,10 @@ __global__ __launch_bounds__(256) void kl_merge_kernel(Params p) {
       S += rec.x;
       AC += rec.y - rec.z;
     }
-    kl = AC - U + S * (__builtin_amdgcn_logf(L) * 0.69314718055994530942f);
+    const float lnL = __builtin_amdgcn_logf(L) * 0.69314718055994530942f;
+    kl = AC - U + S * lnL;
     if (p.kl_rows) p.kl_rows[r] = kl;
+    if (p.kl_lse) p.kl_lse[r] = M + lnL;
   }
   red[threadIdx.x] = kl;
   __syncthreads();
@@ -400,8 +402,8 @@ hipError_t launch_kl_d(const AttnShape& s, const Layout& L, const Params& p, hip
 
 hipError_t launch_kl_loss(const AttnShape& s, int D_idx, const uint16_t* q, const uint16_t* k,
                           const uint16_t* q_idx, const uint16_t* k_idx, const int32_t* idx,
-                          const float* lse, float* kl_rows, float* loss, void* ws, size_t ws_bytes,
-                          hipStream_t stream) {
+                          const float* lse, float* kl_rows, float* loss, float* lse_idx, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
   const Layout L = make_kl_layout(s);
   if (ws_bytes < L.total) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
@@ -410,6 +412,7 @@ hipError_t launch_kl_loss(const AttnShape& s, int D_idx, const uint16_t* q, cons
   p.kl_rec = reinterpret_cast<float*>(base + L.kl_rec);
   p.kl_wsum = reinterpret_cast<float*>(base + L.kl_wsum);
   p.kl_rows = kl_rows;
+  p.kl_lse = lse_idx;
   p.loss = loss;
   switch (D_idx) {
     case 64: return launch_kl_d<64>(s, L, p, stream);

@@ -123,6 +123,9 @@ size_t msa_workspace_bytes(const msa_dims* d, int entry) {
     case MSA_ENTRY_SPARSE_ATTN_BWD:
       if (check_dims(d, false, true) != MSA_OK) return bad;
       return is_empty(*d) ? 0 : msa::sparse_attn_bwd_workspace(attn_shape(*d));
+    case MSA_ENTRY_KL_LOSS_BWD:
+      if (check_dims(d, true, true) != MSA_OK) return bad;
+      return is_empty(*d) ? 0 : msa::kl_loss_bwd_workspace(attn_shape(*d), d->index_dim);
     default:
       return bad;
   }
@@ -197,7 +200,16 @@ msa_status msa_sparse_attn_bwd(const msa_dims* d, const void* q, const void* k, 
                                const void* dout, void* dq, void* dk, void* dv, void* ws,
                                size_t ws_bytes, void* stream) {
   msa_status st = check_dims(d, false, true);
-  if (st != MSA_OK || is_empty(*d)) return st;
+  if (st != MSA_OK) return st;
+  if (is_empty(*d)) {  // no query: zero key gradients
+    if (d->batch == 0 || d->seqlen_k == 0) return MSA_OK;
+    if (!dk || !dv) return MSA_ERR_NULL_PTR;
+    if (!aligned16(dk) || !aligned16(dv)) return MSA_ERR_MISALIGNED;
+    const long n = long(d->batch) * d->seqlen_k * d->num_heads_kv * d->head_dim / 2;
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+    if (msa::launch_fill_zero(static_cast<float*>(dk), n, strm) != hipSuccess) return MSA_ERR_HIP;
+    return from_hip(msa::launch_fill_zero(static_cast<float*>(dv), n, strm));
+  }
   if (!q || !k || !v || !block_idx || !out || !lse || !dout || !dq || !dk || !dv)
     return MSA_ERR_NULL_PTR;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) ||
@@ -215,9 +227,43 @@ msa_status msa_sparse_attn_bwd(const msa_dims* d, const void* q, const void* k, 
       static_cast<uint16_t*>(dv), ws, ws_bytes, static_cast<hipStream_t>(stream)));
 }
 
+msa_status msa_kl_loss_bwd(const msa_dims* d, const void* q, const void* k, const void* q_idx,
+                           const void* k_idx, const int32_t* block_idx, const float* lse,
+                           const float* lse_idx, float grad_loss, void* dq_idx, void* dk_idx,
+                           void* ws, size_t ws_bytes, void* stream) {
+  msa_status st = check_dims(d, true, true);
+  if (st != MSA_OK) return st;
+  if (!std::isfinite(grad_loss)) return MSA_ERR_INVALID_DIMS;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  if (is_empty(*d)) {  // no row: zero index-key gradient
+    if (d->batch == 0 || d->seqlen_k == 0) return MSA_OK;
+    if (!dk_idx) return MSA_ERR_NULL_PTR;
+    if (!aligned16(dk_idx)) return MSA_ERR_MISALIGNED;
+    const long n = long(d->batch) * d->seqlen_k * d->index_dim / 2;
+    return from_hip(msa::launch_fill_zero(static_cast<float*>(dk_idx), n, strm));
+  }
+  if (!q || !k || !q_idx || !k_idx || !block_idx || !lse || !lse_idx || !dq_idx || !dk_idx)
+    return MSA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_idx) || !aligned16(k_idx) ||
+      !aligned16(block_idx) || !aligned16(lse) || !aligned16(lse_idx) || !aligned16(dq_idx) ||
+      !aligned16(dk_idx))
+    return MSA_ERR_MISALIGNED;
+  const msa::AttnShape s = attn_shape(*d);
+  const size_t need = msa::kl_loss_bwd_workspace(s, d->index_dim);
+  if (!ws || ws_bytes < need) return ws ? MSA_ERR_WORKSPACE_TOO_SMALL : MSA_ERR_NULL_PTR;
+  if (!aligned16(ws)) return MSA_ERR_MISALIGNED;
+  const float coef = float(double(grad_loss) / (double(d->batch) * d->seqlen_q * d->num_heads_kv));
+  return from_hip(msa::launch_kl_loss_bwd(
+      s, d->index_dim, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx), block_idx, lse,
+      lse_idx, coef, static_cast<uint16_t*>(dq_idx), static_cast<uint16_t*>(dk_idx), ws, ws_bytes,
+      strm));
+}
+
 msa_status msa_kl_loss_fwd(const msa_dims* d, const void* q, const void* k, const void* q_idx,
                            const void* k_idx, const int32_t* block_idx, const float* lse,
-                           float* kl_rows, float* loss, void* ws, size_t ws_bytes, void* stream) {
+                           float* kl_rows, float* loss, float* lse_idx, void* ws, size_t ws_bytes,
+                           void* stream) {
   msa_status st = check_dims(d, true, true);
   if (st != MSA_OK) return st;
   hipStream_t strm = static_cast<hipStream_t>(stream);
@@ -229,7 +275,7 @@ msa_status msa_kl_loss_fwd(const msa_dims* d, const void* q, const void* k, cons
   if (!q || !k || !q_idx || !k_idx || !block_idx || !lse) return MSA_ERR_NULL_PTR;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_idx) || !aligned16(k_idx) ||
       !aligned16(block_idx) || !aligned16(lse) || (kl_rows && !aligned16(kl_rows)) ||
-      (loss && !aligned16(loss)))
+      (loss && !aligned16(loss)) || (lse_idx && !aligned16(lse_idx)))
     return MSA_ERR_MISALIGNED;
   const msa::AttnShape s = attn_shape(*d);
   const size_t need = msa::kl_loss_workspace(s);
@@ -238,7 +284,7 @@ msa_status msa_kl_loss_fwd(const msa_dims* d, const void* q, const void* k, cons
   return from_hip(msa::launch_kl_loss(
       s, d->index_dim, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx), block_idx, lse,
-      kl_rows, loss, ws, ws_bytes, strm));
+      kl_rows, loss, lse_idx, ws, ws_bytes, strm));
 }
 
 namespace {

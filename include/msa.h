@@ -86,7 +86,8 @@ typedef enum msa_entry {
   MSA_ENTRY_SPARSE_ATTN_FWD = 2,
   MSA_ENTRY_FORWARD = 3,
   MSA_ENTRY_KL_LOSS_FWD = 4,
-  MSA_ENTRY_SPARSE_ATTN_BWD = 5
+  MSA_ENTRY_SPARSE_ATTN_BWD = 5,
+  MSA_ENTRY_KL_LOSS_BWD = 6
 } msa_entry;
 
 /*
@@ -218,16 +219,18 @@ msa_status msa_mask_blocks(const msa_dims* dims, const uint32_t* mask,
  * memory.  block_idx follows the rules of msa_sparse_attn_fwd.  kl_rows
  * ([B][H_kv][S_q] fp32) and loss (one fp32) are each optional (NULL skips
  * it); the loss is summed in a fixed order, so it is identical from run to
- * run.  `ws` holds msa_workspace_bytes(dims, MSA_ENTRY_KL_LOSS_FWD) bytes
- * (edge lists and 20 bytes per selected block per row); contents on entry do
+ * run.  lse_idx ([B][H_kv][S_q] fp32, optional) receives each row's
+ * log-sum-exp of z over T_i, which msa_kl_loss_bwd takes.  `ws` holds
+ * msa_workspace_bytes(dims, MSA_ENTRY_KL_LOSS_FWD) bytes
+ * (edge lists and 32 bytes per selected block per row); contents on entry do
  * not matter.  An empty problem writes *loss = 0 when loss is not NULL.
  * Uses every field of dims (both branches).
  */
 msa_status msa_kl_loss_fwd(const msa_dims* dims, const void* q, const void* k,
                            const void* q_idx, const void* k_idx,
                            const int32_t* block_idx, const float* lse,
-                           float* kl_rows, float* loss, void* ws,
-                           size_t ws_bytes, void* stream);
+                           float* kl_rows, float* loss, float* lse_idx,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Main branch, backward (the backward pass that the MSA kernel notes fuse
@@ -246,7 +249,8 @@ msa_status msa_kl_loss_fwd(const msa_dims* dims, const void* q, const void* k,
  * Inputs: q, k, v, block_idx (as msa_sparse_attn_fwd), out and lse exactly as
  * the forward returned them for this selection, dout [B][S_q][H_q][D] bf16.
  * Outputs (written in full, bf16): dq like q; dk, dv like k and v (zero for
- * keys no query selects).  Sums run in a fixed order: results are identical
+ * keys no query selects; an empty problem with batch > 0 writes dk = dv = 0).
+ * Sums run in a fixed order: results are identical
  * from run to run.  `ws` holds msa_workspace_bytes(dims,
  * MSA_ENTRY_SPARSE_ATTN_BWD) bytes (edge lists, per-edge dq records of
  * G * (2 D + 16) bytes, and fp32 dk / dv sums when the queries run in several
@@ -258,6 +262,31 @@ msa_status msa_sparse_attn_bwd(const msa_dims* dims, const void* q, const void* 
                                const void* out, const float* lse, const void* dout,
                                void* dq, void* dk, void* dv, void* ws,
                                size_t ws_bytes, void* stream);
+
+/*
+ * Alignment loss, backward: the gradient of grad_loss * loss (loss as
+ * msa_kl_loss_fwd defines it) with respect to the index inputs.  The teacher
+ * is detached (Sparse Attention Part II, section 3.2), so q, k get nothing
+ * from this loss; the KL expansion (The Architecture of Infinity) makes the
+ * gradient of each index score z(s) of row (b, g, i), for s in T_i,
+ *
+ *   g(s) = grad_loss / (B * S_q * H_kv) * (exp(z(s) - lse_idx[b][g][i]) - P(s))
+ *   dq_idx[b][i][g] = sum_{s in T_i} g(s) k_idx[b][s]
+ *   dk_idx[b][s]    = sum over rows (b, g, i) with s in T_i of g(s) q_idx[b][i][g]
+ *
+ * with P the teacher of msa_kl_loss_fwd.  Inputs as msa_kl_loss_fwd, plus
+ * lse_idx as that call wrote it for the same selection.  Outputs bf16, written
+ * in full: dq_idx like q_idx, dk_idx like k_idx (zero for keys no row
+ * selects; an empty problem with batch > 0 writes dk_idx = 0).  Fixed
+ * summation order: identical from run to run.  `ws` holds
+ * msa_workspace_bytes(dims, MSA_ENTRY_KL_LOSS_BWD) bytes (edge lists,
+ * 2 D_idx + 16 bytes per selected block per row, and fp32 dk_idx per group).
+ */
+msa_status msa_kl_loss_bwd(const msa_dims* dims, const void* q, const void* k,
+                           const void* q_idx, const void* k_idx,
+                           const int32_t* block_idx, const float* lse,
+                           const float* lse_idx, float grad_loss, void* dq_idx,
+                           void* dk_idx, void* ws, size_t ws_bytes, void* stream);
 
 /* Internal stages of msa_forward, in launch order (for msa_forward_profiled). */
 typedef enum msa_stage {

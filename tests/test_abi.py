@@ -63,9 +63,14 @@ def mblocks(d, mask=A, idx=A):
     return msa.lib().msa_mask_blocks(None if d is None else ctypes.byref(d), mask, idx, None)
 
 
-def kl(d, q=A, k=A, qi=A, ki=A, idx=A, lse=A, rows=A, loss=A, ws=A, nbytes=1 << 40):
+def kl(d, q=A, k=A, qi=A, ki=A, idx=A, lse=A, rows=A, loss=A, lsei=A, ws=A, nbytes=1 << 40):
     return msa.lib().msa_kl_loss_fwd(None if d is None else ctypes.byref(d), q, k, qi, ki, idx, lse,
-                                     rows, loss, ws, nbytes, None)
+                                     rows, loss, lsei, ws, nbytes, None)
+
+
+def klb(d, q=A, k=A, qi=A, ki=A, idx=A, lse=A, lsei=A, grad=1.0, dqi=A, dki=A, ws=A, nbytes=1 << 40):
+    return msa.lib().msa_kl_loss_bwd(None if d is None else ctypes.byref(d), q, k, qi, ki, idx, lse,
+                                     lsei, grad, dqi, dki, ws, nbytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -111,6 +116,13 @@ def test_null_and_misaligned_pointers():
         assert kl(d, **{kw: NULL}) == 1, kw
         assert kl(d, **{kw: MIS}) == 4, kw
     assert kl(d, rows=MIS) == 4 and kl(d, loss=MIS) == 4 and kl(d, ws=MIS) == 4
+    assert kl(d, lsei=MIS) == 4
+    assert klb(None) == 1
+    for kw in ("q", "k", "qi", "ki", "idx", "lse", "lsei", "dqi", "dki"):
+        assert klb(d, **{kw: NULL}) == 1, kw
+        assert klb(d, **{kw: MIS}) == 4, kw
+    assert klb(d, ws=NULL, nbytes=0) == 1 and klb(d, ws=MIS) == 4
+    assert klb(d, grad=float("nan")) == 2 and klb(d, grad=float("inf")) == 2
     assert kl(d, ws=NULL, nbytes=0) == 1
 
 
@@ -139,6 +151,18 @@ def test_bwd_entry_checks():
     e = dims(batch=0)
     assert bwd(e, q=NULL, k=NULL, v=NULL, idx=NULL, out=NULL, lse=NULL, do=NULL, dq=NULL, dk=NULL,
                dv=NULL, ws=NULL, nbytes=0) == 0
+
+
+def test_kl_bwd_entry_checks():
+    d = dims()
+    need = msa.msa_workspace_bytes(d, msa.ENTRY_KL_LOSS_BWD)
+    rows = d.batch * d.num_heads_kv * d.seqlen_q
+    assert need >= rows * d.topk * (2 * d.index_dim + 16)
+    assert klb(d, nbytes=need - 1) == 5
+    for kw, status in ((dict(index_dim=96), 3), (dict(head_dim=64), 3), (dict(causal=0), 3)):
+        assert klb(dims(**kw)) == status, kw
+    assert klb(dims(batch=0), q=NULL, k=NULL, qi=NULL, ki=NULL, idx=NULL, lse=NULL, lsei=NULL, dqi=NULL,
+               dki=NULL, ws=NULL, nbytes=0) == 0
 
 
 def test_kl_entry_checks_both_branches():

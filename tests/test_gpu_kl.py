@@ -167,7 +167,7 @@ def test_kl_empty_problem_writes_zero_loss():
     loss = torch.full((4,), 7.0, device="cuda")
     d = msa.Dims.make(0, 0, 0, 8, 2)
     rc = msa.lib().msa_kl_loss_fwd(d, None, None, None, None, None, None, None,
-                                   loss.data_ptr(), None, 0, None)
+                                   loss.data_ptr(), None, None, 0, None)
     torch.cuda.synchronize()
     assert rc == 0 and loss[0].item() == 0.0 and loss[1].item() == 7.0
 

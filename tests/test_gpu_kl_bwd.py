@@ -1,0 +1,143 @@
+"""GPU parity of the alignment loss's backward (msa_kl_loss_bwd through the C
+ABI) against the oracle's gradients with respect to the index inputs (teacher
+detached, Sparse Attention Part II, section 3.2).
+
+The device side runs its own forward (selection and LSE), the loss forward
+(which also returns each row's log-sum-exp of the index scores), then the
+backward with grad_loss = 1; the oracle computes its own selection and, in
+fp64, the unscaled gradients, scaled here by 1 / (B S_q H_kv).
+
+Tolerance (bf16 gradients against fp64): per tensor, the error beyond the
+output's own bf16 rounding is at most 1e-2 * max |ref|, and the mean of that
+excess at most 1e-3 * max |ref|.  The device rounds g to bf16 before the matrix products
+(relative 2^-9 per term), accumulates in fp32 and keeps each edge's dq_idx as
+fp16 scaled by its 32-dim quarter's maximum (2^-12).  The rows' index-score
+log-sum-exps must agree to 1e-6 relative (fp32 against fp64).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_gqa_scores_amd as msa
+import oracle
+import synth
+from gpu_util import bf16_half_ulp, inputs_for, to_u16
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL = 1e-2
+MEAN_REL = 1e-3
+
+
+def W(name, B, Sq, Sk, Hq, Hkv, Didx=128, topk=16, **kw):
+    return synth.Workload(name, B, Sq, Sk, Hq, Hkv, index_dim=Didx, topk=topk, **kw)
+
+
+def device_kl_bwd(w, t, grad=1.0):
+    out, lse, idx = msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk,
+                                    return_lse=True, return_idx=True)
+    loss, lse_idx = msa.msa_kl_loss_fwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, return_lse_idx=True)
+    dqi, dki = msa.msa_kl_loss_bwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, lse_idx, grad)
+    torch.cuda.synchronize()
+    return idx, lse_idx, dqi, dki
+
+
+def check(name, got, ref):
+    got = got.astype(np.float64)
+    err = np.abs(got - ref)
+    excess = np.maximum(err - bf16_half_ulp(ref), 0.0)
+    big = float(np.abs(ref).max())
+    print(f"{name}: max|ref| {big:.4g}, max err {err.max():.3e} (beyond rounding {excess.max():.3e}), "
+          f"mean err {err.mean():.3e} (beyond rounding {excess.mean():.3e})", flush=True)
+    assert excess.max() <= MAX_REL * big, f"{name}: max error {excess.max():.3e} > {MAX_REL * big:.3e}"
+    assert excess.mean() <= MEAN_REL * big, f"{name}: mean error {excess.mean():.3e} > {MEAN_REL * big:.3e}"
+
+
+def oracle_side(w, h, rows, want_dk=True, threads=0):
+    p = oracle.Problem.of(w)
+    ref = oracle.forward(p, h["q"], h["k"], h["v"], h["q_idx"], h["k_idx"], rows=rows, threads=threads)
+    dqi, dki, lse_z = oracle.kl_bwd(p, h["q"], h["k"], h["q_idx"], h["k_idx"], ref["sel"], rows,
+                                    want_dk=want_dk, threads=threads)
+    c = 1.0 / (w.batch * w.seqlen_q * w.heads_kv)
+    return ref["sel"], dqi * c, (dki * c if dki is not None else None), lse_z
+
+
+CASES = [
+    W("klb_4k", 1, 4096, 4096, 8, 2, Didx=64),                 # two query windows, D_idx 64
+    W("klb_ragged", 2, 700, 1000, 8, 2, topk=5),               # S_k % 128 != 0, S_q < S_k
+    W("klb_gqa8", 1, 2600, 2600, 64, 8),                       # G = 8
+    W("klb_mha", 1, 600, 777, 4, 4, Didx=64, topk=3),          # G = 1
+    W("klb_g2", 1, 500, 1300, 8, 4, topk=6),                   # G = 2
+    W("klb_g16", 1, 500, 640, 32, 2, topk=2),                  # G = 16
+    W("klb_g32", 2, 300, 300, 32, 1, Didx=64, topk=4),         # G = 32
+    W("klb_topk1", 1, 400, 900, 8, 2, topk=1),                 # local block only
+    W("klb_decode", 3, 1, 5000, 16, 2, Didx=64),               # S_q = 1
+    W("klb_k64", 1, 130, 9000, 4, 1, topk=64),                 # the largest topk
+    W("klb_gain", 1, 1500, 3000, 16, 2, gain=True, topk=6),    # uneven blocks
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_kl_bwd_parity(w):
+    t = inputs_for(w)
+    idx, lse_idx, dqi, dki = device_kl_bwd(w, t)
+    h = {n: to_u16(x) for n, x in t.items()}
+    rows = oracle.Problem.of(w).all_rows()
+    sel, rdqi, rdki, lse_z = oracle_side(w, h, rows)
+    got_sel = idx.cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]]
+    assert (got_sel == sel).all(), "selection differs"
+    li = lse_idx.cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]].astype(np.float64)
+    assert np.abs(li - lse_z).max() <= 1e-6 * max(1.0, np.abs(lse_z).max()), np.abs(li - lse_z).max()
+    dqin = dqi.float().cpu().numpy()
+    check(f"{w.name} dq_idx", dqin[rows[:, 0], rows[:, 1], rows[:, 2]], rdqi)
+    check(f"{w.name} dk_idx", dki.float().cpu().numpy(), rdki)
+
+
+def test_kl_bwd_grad_scale_and_determinism():
+    """grad_loss scales the gradients linearly (2^k exactly); repeated calls
+    are bit-identical."""
+    w = W("klb_det", 1, 1500, 4000, 16, 2, topk=8)
+    t = inputs_for(w)
+    a = device_kl_bwd(w, t, 1.0)
+    b = device_kl_bwd(w, t, 1.0)
+    c = device_kl_bwd(w, t, 4.0)
+    assert torch.equal(a[2], b[2]) and torch.equal(a[3], b[3])
+    assert torch.equal(c[2].float(), 4 * a[2].float()) and torch.equal(c[3].float(), 4 * a[3].float())
+
+
+def test_kl_bwd_without_queries_writes_zero_key_gradient():
+    dki = torch.full((2, 300, 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    d = msa.Dims.make(2, 0, 300, 8, 2, index_dim=64)
+    rc = msa.lib().msa_kl_loss_bwd(d, None, None, None, None, None, None, None, 1.0, None,
+                                   dki.data_ptr(), None, 0, None)
+    torch.cuda.synchronize()
+    assert rc == 0 and not dki.float().any()
+
+
+def test_kl_bwd_prefill_32k():
+    """Full size: dq_idx on sampled rows; dk_idx of the last two key blocks,
+    whose rows (all groups) are all among the last 256 queries; and, over all
+    keys, sum_s dk_idx[s] = 0 (student and teacher both sum to one on every
+    row)."""
+    w = synth.WORKLOADS["prefill_32k"]
+    print("[prefill_32k] inputs, forward, loss, backward", flush=True)
+    t = inputs_for(w)
+    idx, lse_idx, dqi, dki = device_kl_bwd(w, t)
+    tot = dki.float()[0].sum(0)
+    scale = dki.float()[0].abs().sum(0)
+    print(f"[prefill_32k] |sum dk_idx| max {tot.abs().max().item():.3e} (sum |dk_idx| {scale.max().item():.3e})",
+          flush=True)
+    assert (tot.abs() <= 4e-3 * scale + 1e-12).all()
+    rng = np.random.default_rng(4)
+    qs = np.unique(np.concatenate([rng.integers(0, w.seqlen_q, 24), [0, 127, 2047, 2048],
+                                   np.arange(w.seqlen_q - 256, w.seqlen_q)]))
+    rows = np.array([(0, q, g) for q in qs for g in range(w.heads_kv)], dtype=np.int64)
+    h = {n: to_u16(x) for n, x in t.items()}
+    dqin, dkin, sel_dev = dqi.float().cpu().numpy(), dki.float().cpu().numpy(), idx.cpu().numpy()
+    del t
+    print(f"[prefill_32k] oracle on {len(rows)} rows", flush=True)
+    sel, rdqi, rdki, _ = oracle_side(w, h, rows, threads=8)
+    assert (sel_dev[rows[:, 0], rows[:, 2], rows[:, 1]] == sel).all()
+    check("prefill_32k dq_idx", dqin[rows[:, 0], rows[:, 1], rows[:, 2]], rdqi)
+    lo = (w.n_blk - 2) * 128
+    check("prefill_32k dk_idx (last 2 blocks)", dkin[0, lo:], rdki[0, lo:])
