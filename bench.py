@@ -10,8 +10,9 @@ on the 32K prefill workload (B=1, S=32768, 64/8 heads, head dim 128, index dim
 128, block 128, k=16).  Alongside: algorithmic TFLOP/s and the fraction of the
 bf16 MFMA peak, per-entry-point times, the roofline of the dominant step, the
 CPU oracle timed on a bounded row sample, the decode workload (64 sequences
-against a 256K-token cache) as HBM GB/s and fraction of peak, and the forward
-value of the index branch's alignment loss on the same selection.
+against a 256K-token cache) as HBM GB/s and fraction of peak, the forward
+value of the index branch's alignment loss on the same selection, and the
+backward (main branch and alignment loss) beside it.
 """
 from __future__ import annotations
 
@@ -186,6 +187,47 @@ def alignment_loss_rate(w, t, steps):
     return res
 
 
+def backward_rates(w, t, steps):
+    """The backward on the forward's selection (next to the forward, not part
+    of its step): msa_sparse_attn_bwd (dq, dk, dv from a seeded dO) and
+    msa_kl_loss_bwd (gradients of the alignment loss into q_idx, k_idx).
+    Algorithmic FLOPs per call: the main branch recomputes S and forms dP,
+    dV, dK and dq, five products of 2 D H_q sum|T_i| each; the loss backward
+    recomputes the main logits (2 D H_q sum|T_i|) and forms z, dk_idx and
+    dq_idx (2 D_idx H_kv sum|T_i| each)."""
+    import torch
+
+    import block_sparse_gqa_scores_amd as msa
+    import synth
+
+    stream = torch.cuda.current_stream()
+    dout = torch.empty_like(t["q"])
+    synth.fill_device(w, "dout", dout)
+    out, lse, idx = msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk,
+                                    return_lse=True, return_idx=True)
+    _, lse_idx = msa.msa_kl_loss_fwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, return_lse_idx=True)
+    d = msa.dims_of(t["q"], t["k"], t["q_idx"], t["k_idx"], topk=w.topk)
+    ws = torch.empty(max(msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_BWD),
+                         msa.msa_workspace_bytes(d, msa.ENTRY_KL_LOSS_BWD)), dtype=torch.uint8, device=lse.device)
+    tok = w.batch * float(visible_tokens(w).sum())
+    legs = {
+        "sparse_attn_bwd": (lambda: msa.msa_sparse_attn_bwd(t["q"], t["k"], t["v"], idx, out, lse, dout,
+                                                             workspace=ws),
+                            5 * 2.0 * w.head_dim * w.heads_q * tok),
+        "kl_loss_bwd": (lambda: msa.msa_kl_loss_bwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, lse_idx,
+                                                     1.0, workspace=ws),
+                        2.0 * w.head_dim * w.heads_q * tok + 3 * 2.0 * w.index_dim * w.heads_kv * tok),
+    }
+    res = {"workload": w.name}
+    for name, (fn, fl) in legs.items():
+        fn()
+        ms = time_loop(fn, steps, stream)
+        tf = fl / (ms * 1e-3) / 1e12
+        res[name] = {"ms": ms, "algorithmic_flops": fl, "TFLOP/s": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}
+    del ws, dout
+    return res
+
+
 def stage_work(w, chunks):
     """Algorithmic work of each stage per launch: (bound, amount, unit).  With
     the fused selection the Top-k runs inside the index stage and its own
@@ -309,6 +351,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-kl", action="store_true", help="skip the alignment-loss measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run one plain device copy of this many bytes first (counter calibration)")
     ap.add_argument("--no-copy-rate", action="store_true",
@@ -356,6 +399,9 @@ def main():
     if not args.no_kl:
         print("[bench] alignment loss ...", file=sys.stderr, flush=True)
         res["alignment_loss"] = alignment_loss_rate(w, t, args.steps)
+    if not args.no_backward:
+        print("[bench] backward ...", file=sys.stderr, flush=True)
+        res["backward"] = backward_rates(w, t, max(2, args.steps // 2))
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
