@@ -33,9 +33,10 @@ struct BwdParams {
   const uint16_t* dout;  // [B][S_q][H_q][D] bf16
   const uint16_t* out;   // forward output, same layout
   const float* lse;      // forward LSE [B][H_q][S_q] (natural log)
-  float* delta;          // [B][H_q][S_q]: sum_d dO O
+  float2* stat;          // [B][H_q][S_q]: (LSE in log2 units, sum_d dO O)
   uint16_t* dq_rec;      // [slot][4][G][32] fp16: the edge's dq / its quarter's scale (rec_dim order)
   float* dq_sc;          // [slot][4][G]: max |dq| over each quarter of the head dims
+  long sink;             // record slot written by padding rows (never read)
   uint16_t* dq;          // [B][S_q][H_q][D] bf16
   uint16_t* dk;          // [B][S_k][H_kv][D] bf16
   uint16_t* dv;
@@ -64,7 +65,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams bp) {
     const long bi = row / p.H_q;
     const int i = (int)(bi % p.S_q);
     const int b = (int)(bi / p.S_q);
-    bp.delta[((long)b * p.H_q + h) * p.S_q + i] = acc;
+    const long li = ((long)b * p.H_q + h) * p.S_q + i;
+    bp.stat[li] = make_float2(bp.lse[li] * 1.4426950408889634f, acc);
   }
 }
 
@@ -111,8 +113,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
   __shared__ u32x4 sq[32 * 16];             // Q rows of the sub-tile [row][chunk], swizzled
   __shared__ u32x4 sdo[32 * 16];            // dO rows, same
   __shared__ __align__(16) uint16_t sds[32 * kSStride];  // dS [row][key] bf16
-  __shared__ __align__(16) float s_lse[32];
-  __shared__ __align__(16) float s_delta[32];
+  __shared__ __align__(16) float2 s_stat[32];  // (LSE log2, delta) of each row
   __shared__ int s_t[QW];                   // position of each query (-1: no edge)
   __shared__ int s_slot[QW];
 
@@ -155,71 +156,143 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
     int w, base, cnt;
     const int32_t* ed;
   };
-  auto next = [&](Cursor& cu) {  // uniform; false past the last sub-tile
-    cu.base += QW;
-    while (cu.base >= cu.cnt) {
-      if (++cu.w >= p.n_win) return false;
-      const long bucket = ((long)bg * p.n_win + cu.w) * p.n_blk + j;
-      cu.cnt = p.counts[bucket];
-      cu.ed = p.edges + p.offsets[bucket];
-      cu.base = 0;
+  // Advances to the next sub-tile; past the last one it returns false and
+  // leaves the cursor on the last sub-tile, so its addresses stay valid.
+  auto next = [&](Cursor& cu) {  // uniform
+    Cursor t = cu;
+    t.base += QW;
+    while (t.base >= t.cnt) {
+      if (++t.w >= p.n_win) return false;
+      const long bucket = ((long)bg * p.n_win + t.w) * p.n_blk + j;
+      t.cnt = __builtin_amdgcn_readfirstlane(p.counts[bucket]);
+      t.ed = p.edges + __builtin_amdgcn_readfirstlane(p.offsets[bucket]);
+      t.base = 0;
     }
+    cu = t;
     return true;
   };
   const int pr = tid & 15, cc = tid >> 4;  // staging role: rows (2 pr, 2 pr + 1), chunk cc
-  u32x4 qa[2], da[2];
-  float f_lse = 0.f, f_delta = 0.f;
-  int f_t = -1, f_slot = -1;
-  auto fetch = [&](const Cursor& cu) {
+  // Edge ids one sub-tile ahead of the rows: e for this thread's staging
+  // rows (one query unless G = 1), e2 for the statistics of row tid % 32.  A
+  // row past a bucket's end repeats the bucket's last edge and is flagged
+  // invalid; the flags come from the cursor alone, so nothing waits for the
+  // ids before they are used.
+  constexpr int NI = G >= 2 ? 1 : 2;
+  struct Ids {
+    int e[NI];
+    int e2;
+    int valid;  // bit y: e[y]; bit 2: e2
+  };
+  auto load_ids = [&](const Cursor& cu, Ids& d) {
+    int v = 0;
+#pragma unroll
+    for (int y = 0; y < NI; ++y) {
+      const int q = (2 * pr + y) / G;
+      d.e[y] = cu.ed[min(cu.base + q, cu.cnt - 1)];
+      v |= (cu.base + q < cu.cnt) << y;
+    }
+    const int q2 = (tid & 31) / G;
+    d.e2 = cu.ed[min(cu.base + q2, cu.cnt - 1)];
+    d.valid = v | (cu.base + q2 < cu.cnt) << 2;
+  };
+  // The rows of one sub-tile as fetched by this thread (two sets alternate).
+  struct Fetched {
+    u32x4 qa[2], da[2];
+    float2 st;
+    Ids id;
+  };
+  auto fetch = [&](const Ids& d, Fetched& f) {
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
-      const int r = 2 * pr + y, q = r / G, hh = r - (r / G) * G;
-      const bool valid = cu.base + q < cu.cnt;
-      const int sl = cu.ed[min(cu.base + q, cu.cnt - 1)];
-      const int i = p.q0 + (int)((sl / p.topk) % p.Qc);
+      const int r = 2 * pr + y, hh = r % G;
+      const int i = p.q0 + (int)((d.e[y % NI] / p.topk) % p.Qc);
       const size_t rowoff = (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + 8 * cc;
-      qa[y] = *reinterpret_cast<const u32x4*>(p.q + rowoff);
+      f.qa[y] = *reinterpret_cast<const u32x4*>(p.q + rowoff);
+      f.da[y] = *reinterpret_cast<const u32x4*>(bp.dout + rowoff);
+    }
+    if (tid < 32) {  // (loading it in every thread costs registers)
+      const int hh = tid % G;
+      const int i = p.q0 + (int)((d.e2 / p.topk) % p.Qc);
+      f.st = bp.stat[((size_t)b * p.H_q + g * G + hh) * p.S_q + i];
+    }
+    f.id = d;
+  };
+  // The dq records of one sub-tile (rows without an edge, and the dummy
+  // stores of the prologue, write the sink).
+  auto store_records = [&](const f32x16& qacc, bool dummy) {
+    const int q = n / G, hh = n - (n / G) * G;
+    const int sl = dummy ? -1 : s_slot[q];
+    const long slot = sl >= 0 ? sl : bp.sink;
+    float m = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m = max3abs(qacc[r], qacc[r], m);
+    m = __builtin_fmaxf(m, swap_halves(m)) * bp.scale;
+    const float inv = m > 0.f ? bp.scale * __builtin_amdgcn_rcpf(m) : 0.f;
+    // 32 contiguous bytes per lane; the slot's quarter is 512 contiguous bytes.
+    u32x4* rec = reinterpret_cast<u32x4*>(bp.dq_rec + ((slot * 4 + wave) * G + hh) * 32 + 16 * h);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x4 v4;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        v4[x] = pack_f16x2(qacc[8 * half + 2 * x] * inv, qacc[8 * half + 2 * x + 1] * inv);
+      rec[half] = v4;
+    }
+    bp.dq_sc[(slot * 4 + wave) * G + hh] = m;  // both halves store the same m
+  };
+  // Pipeline, in issue order: sub-tile n stages rows fetched during n - 2,
+  // requests the ids of n + 3 and then the rows of n + 2, computes, and
+  // stores its dq records.  Every request is unconditional (past the end
+  // the cursor repeats the last sub-tile), so the memory counter's order is
+  // the same on every iteration and the waits stay exact: the rows of n + 1
+  // and the records of n - 1 stay in flight while n stages.  The prologue
+  // issues the same sequence, with two dummy record stores.
+  Cursor cur{-1, -QW, 0, nullptr};
+  bool h0 = next(cur), h1 = false, h2 = false;
+  Fetched fx, fy;
+  Ids ids;
+  if (h0) {
+    Ids i0;
+    load_ids(cur, i0);
+    h1 = next(cur);
+    load_ids(cur, ids);
+    fetch(i0, fx);
+    store_records(zero16(), true);
+    h2 = h1 && next(cur);
+    Ids i2;
+    load_ids(cur, i2);
+    fetch(ids, fy);
+    ids = i2;
+    store_records(zero16(), true);
+  }
+
+  auto step = [&](Fetched& f) {
+    __syncthreads();  // the previous sub-tile's LDS reads are done
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int r = 2 * pr + y;
       const u32x4 z = {0u, 0u, 0u, 0u};
-      da[y] = valid ? *reinterpret_cast<const u32x4*>(bp.dout + rowoff) : z;
+      sq[r * 16 + (cc ^ rsw(r))] = f.qa[y];
+      sdo[r * 16 + (cc ^ rsw(r))] = (f.id.valid >> (y % NI)) & 1 ? f.da[y] : z;
     }
     if (tid < 32) {
-      const int r = tid, q = r / G, hh = r - (r / G) * G;
-      const bool valid = cu.base + q < cu.cnt;
-      const int sl = cu.ed[min(cu.base + q, cu.cnt - 1)];
-      const int i = p.q0 + (int)((sl / p.topk) % p.Qc);
-      const size_t li = ((size_t)b * p.H_q + g * G + hh) * p.S_q + i;
-      f_lse = valid ? bp.lse[li] * kLog2e : __builtin_inff();
-      f_delta = valid ? bp.delta[li] : 0.f;
-      f_t = valid ? i + off : -1;
-      f_slot = valid ? sl : -1;
-    }
-  };
-  Cursor cur{-1, 0, 0, nullptr};
-  cur.base = -QW;
-  bool have = next(cur);
-  if (have) fetch(cur);
-  while (have) {
-    __syncthreads();  // the previous sub-tile's LDS reads are done
-    {  // stage the fetched rows (row-major, chunks swizzled by rsw)
-#pragma unroll
-      for (int y = 0; y < 2; ++y) {
-        const int r = 2 * pr + y;
-        sq[r * 16 + (cc ^ rsw(r))] = qa[y];
-        sdo[r * 16 + (cc ^ rsw(r))] = da[y];
-      }
-      if (tid < 32) {
-        s_lse[tid] = f_lse;
-        s_delta[tid] = f_delta;
-        if (tid % G == 0) {
-          s_t[tid / G] = f_t;
-          s_slot[tid / G] = f_slot;
-        }
+      const int x = f.id.e2;
+      const bool valid = (f.id.valid >> 2) & 1;
+      s_stat[tid] = valid ? f.st : make_float2(__builtin_inff(), 0.f);
+      if (tid % G == 0) {
+        s_t[tid / G] = valid ? p.q0 + (int)((x / p.topk) % p.Qc) + off : -1;
+        s_slot[tid / G] = valid ? x : -1;
       }
     }
     __syncthreads();
-    Cursor nx = cur;
-    const bool have_next = next(nx);
-    if (have_next) fetch(nx);  // in flight during this sub-tile's work
+    {
+      const bool h3 = h2 && next(cur);
+      Ids nid;
+      load_ids(cur, nid);
+      fetch(ids, f);
+      ids = nid;
+      h2 = h3;
+    }
     asm volatile("" ::: "memory");
 
       // S = Q K^T and dP = dO V^T for this wave's 32 keys: rows on registers,
@@ -236,10 +309,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
       float lse4[16], del4[16];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const float4 a = *reinterpret_cast<const float4*>(&s_lse[8 * r4 + 4 * h]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&s_delta[8 * r4 + 4 * h]);
-        lse4[4 * r4] = a.x; lse4[4 * r4 + 1] = a.y; lse4[4 * r4 + 2] = a.z; lse4[4 * r4 + 3] = a.w;
-        del4[4 * r4] = d4.x; del4[4 * r4 + 1] = d4.y; del4[4 * r4 + 2] = d4.z; del4[4 * r4 + 3] = d4.w;
+        const float4 a = *reinterpret_cast<const float4*>(&s_stat[8 * r4 + 4 * h]);
+        const float4 d = *reinterpret_cast<const float4*>(&s_stat[8 * r4 + 4 * h + 2]);
+        lse4[4 * r4] = a.x; lse4[4 * r4 + 1] = a.z; lse4[4 * r4 + 2] = d.x; lse4[4 * r4 + 3] = d.z;
+        del4[4 * r4] = a.y; del4[4 * r4 + 1] = a.w; del4[4 * r4 + 2] = d.y; del4[4 * r4 + 3] = d.w;
       }
       float pv[16], dsv[16];
 #pragma unroll
@@ -307,32 +380,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
         const u32x4 sb = *reinterpret_cast<const u32x4*>(&sds[n * kSStride + 16 * ks + 8 * h]);
         qacc = mfma32x32x16(ka, sb, qacc);
       }
-      // Record of (row n, quarter `wave`): the 32 dims over this lane and its
-      // partner in the other half; scale = their max |dq|, values / scale in fp16.
-      {
-        const int q = n / G, hh = n - (n / G) * G;
-        const int sl = s_slot[q];
-        float m = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) m = max3abs(qacc[r], qacc[r], m);
-        m = __builtin_fmaxf(m, swap_halves(m)) * bp.scale;
-        if (sl >= 0) {
-          const float inv = m > 0.f ? bp.scale * __builtin_amdgcn_rcpf(m) : 0.f;
-          // 32 contiguous bytes per lane; the slot's quarter is 512 contiguous bytes.
-          u32x4* rec = reinterpret_cast<u32x4*>(bp.dq_rec + (((size_t)sl * 4 + wave) * G + hh) * 32 + 16 * h);
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            u32x4 v4;
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-              v4[x] = pack_f16x2(qacc[8 * half + 2 * x] * inv, qacc[8 * half + 2 * x + 1] * inv);
-            rec[half] = v4;
-          }
-          if (h == 0) bp.dq_sc[((size_t)sl * 4 + wave) * G + hh] = m;
-        }
-      }
-    cur = nx;
-    have = have_next;
+      store_records(qacc, false);
+  };
+  while (h0) {  // uniform
+    bool hb = h2;
+    step(fx);
+    h0 = h1;
+    h1 = hb;
+    if (!h0) break;
+    hb = h2;
+    step(fy);
+    h0 = h1;
+    h1 = hb;
   }
 
   // dK (times the softmax scale) and dV of this wave's keys.
@@ -421,7 +480,7 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdParams bp) {
 
 struct BwdLayout {
   Layout L;
-  size_t delta, dq_rec, dq_sc, dk_acc, dv_acc, total;
+  size_t stat, dq_rec, dq_sc, dk_acc, dv_acc, total;
   int chunks;
 };
 
@@ -436,9 +495,10 @@ BwdLayout make_bwd_layout(const AttnShape& s) {
   L.Qc = (int)std::max(1L, std::min<long>(qc, s.S_q));
   size_t o = layout_build(L, s);
   B.chunks = (s.S_q + L.Qc - 1) / L.Qc;
-  B.delta = o;  o = align256(o + (size_t)s.batch * s.H_q * s.S_q * 4);
-  B.dq_rec = o; o = align256(o + (size_t)L.E * G * kD * 2);
-  B.dq_sc = o;  o = align256(o + (size_t)L.E * G * 16);
+  B.stat = o;   o = align256(o + (size_t)s.batch * s.H_q * s.S_q * 8);
+  // One record past the chunk's edges takes the stores of padding rows.
+  B.dq_rec = o; o = align256(o + (size_t)(L.E + 1) * G * kD * 2);
+  B.dq_sc = o;  o = align256(o + (size_t)(L.E + 1) * G * 16);
   const size_t kv = (size_t)s.batch * s.S_k * s.H_kv * kD * 4;
   B.dk_acc = o; o = align256(o + (B.chunks > 1 ? kv : 0));
   B.dv_acc = o; o = align256(o + (B.chunks > 1 ? kv : 0));
@@ -494,7 +554,8 @@ hipError_t launch_sparse_attn_bwd(const AttnShape& s, const uint16_t* q, const u
   bp.e = base_params(s, BL.L, base, idx);
   bp.e.q = q; bp.e.k = k; bp.e.v = v;
   bp.dout = dout; bp.out = out; bp.lse = lse;
-  bp.delta = reinterpret_cast<float*>(base + BL.delta);
+  bp.stat = reinterpret_cast<float2*>(base + BL.stat);
+  bp.sink = BL.L.E;
   bp.dq_rec = reinterpret_cast<uint16_t*>(base + BL.dq_rec);
   bp.dq_sc = reinterpret_cast<float*>(base + BL.dq_sc);
   bp.dk_acc = reinterpret_cast<float*>(base + BL.dk_acc);
