@@ -36,6 +36,7 @@ struct KlBwdParams {
   float coef;            // gradient of the loss / (B * S_q * H_kv)
   uint16_t* rec;         // [slot][D_idx / 32][32] fp16 (rec_dim order) / scale
   float* rec_sc;         // [slot][D_idx / 32]
+  long sink;             // record slot written by padding rows (never read)
   float* dk_part;        // [B][H_kv][S_k][D_idx] fp32, per group
   uint16_t* dq_idx;      // [B][S_q][H_kv][D_idx] bf16
   uint16_t* dk_idx;      // [B][S_k][D_idx] bf16
@@ -103,50 +104,133 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
     int w, base, cnt;
     const int32_t* ed;
   };
-  auto next = [&](Cursor& cu) {  // uniform; false past the last sub-tile
-    cu.base += QW;
-    while (cu.base >= cu.cnt) {
-      if (++cu.w >= p.n_win) return false;
-      const long bucket = ((long)bg * p.n_win + cu.w) * p.n_blk + j;
-      cu.cnt = p.counts[bucket];
-      cu.ed = p.edges + p.offsets[bucket];
-      cu.base = 0;
+  // Advances to the next sub-tile; past the last one it returns false and
+  // leaves the cursor on the last sub-tile, so its addresses stay valid.
+  auto next = [&](Cursor& cu) {  // uniform
+    Cursor t = cu;
+    t.base += QW;
+    while (t.base >= t.cnt) {
+      if (++t.w >= p.n_win) return false;
+      const long bucket = ((long)bg * p.n_win + t.w) * p.n_blk + j;
+      t.cnt = __builtin_amdgcn_readfirstlane(p.counts[bucket]);
+      t.ed = p.edges + __builtin_amdgcn_readfirstlane(p.offsets[bucket]);
+      t.base = 0;
     }
+    cu = t;
     return true;
   };
-  Cursor cur{-1, -QW, 0, nullptr};
-  bool have = next(cur);
-  while (have) {
-    __syncthreads();  // the previous sub-tile's LDS reads are done
-    {  // stage rows r = q * G + hh: Q rows, the query's index row, statistics
-      const int pr = tid & 15, cc = tid >> 4;  // rows (2 pr, 2 pr + 1), chunk cc
+  const int pr = tid & 15, cc = tid >> 4;  // staging role: rows (2 pr, 2 pr + 1), chunk cc
+  // Edge ids one sub-tile ahead of the rows: e for this thread's staging
+  // rows (one query unless G = 1), e2 for the statistics of row tid % 32;
+  // validity flags come from the cursor alone.
+  constexpr int NI = G >= 2 ? 1 : 2;
+  struct Ids {
+    int e[NI];
+    int e2;
+    int valid;  // bit y: e[y]; bit 2: e2
+  };
+  auto load_ids = [&](const Cursor& cu, Ids& d) {
+    int v = 0;
 #pragma unroll
-      for (int y = 0; y < 2; ++y) {
-        const int r = 2 * pr + y, q = r / G, hh = r - (r / G) * G;
-        const int sl = cur.ed[min(cur.base + q, cur.cnt - 1)];
-        const int i = p.q0 + (int)((sl / p.topk) % p.Qc);
-        sq[r * 16 + (cc ^ rsw(r))] =
-            *reinterpret_cast<const u32x4*>(p.q + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + 8 * cc);
-        if (cc < ICH)
-          sqi[r * ICH + (cc ^ (rsw(r) & (ICH - 1)))] =
-              *reinterpret_cast<const u32x4*>(p.q_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX + 8 * cc);
-      }
-      if (tid < 32) {
-        const int r = tid, q = r / G, hh = r - (r / G) * G;
-        const bool valid = cur.base + q < cur.cnt;
-        const int sl = cur.ed[min(cur.base + q, cur.cnt - 1)];
-        const int i = p.q0 + (int)((sl / p.topk) % p.Qc);
-        s_lse[r] = valid ? kp.lse[((size_t)b * p.H_q + g * G + hh) * p.S_q + i] * kLog2e : __builtin_inff();
-        if (hh == 0) {
-          s_lsez[q] = valid ? kp.lse_idx[((size_t)b * p.H_kv + g) * p.S_q + i] * kLog2e : __builtin_inff();
-          s_t[q] = valid ? i + off : -1;
-          s_slot[q] = valid ? sl : -1;
-        }
+    for (int y = 0; y < NI; ++y) {
+      const int q = (2 * pr + y) / G;
+      d.e[y] = cu.ed[min(cu.base + q, cu.cnt - 1)];
+      v |= (cu.base + q < cu.cnt) << y;
+    }
+    const int q2 = (tid & 31) / G;
+    d.e2 = cu.ed[min(cu.base + q2, cu.cnt - 1)];
+    d.valid = v | (cu.base + q2 < cu.cnt) << 2;
+  };
+  // The rows of one sub-tile as fetched by this thread (two sets alternate):
+  // Q rows, the query's index row (chunk cc % ICH; threads past ICH repeat
+  // a chunk and do not stage it), and for the first 32 threads the row's
+  // main-branch LSE and its query's index-score LSE.
+  struct Fetched {
+    u32x4 qa[2], qi[2];
+    float lse, lsez;
+    Ids id;
+  };
+  auto fetch = [&](const Ids& d, Fetched& f) {
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int r = 2 * pr + y, hh = r % G;
+      const int i = p.q0 + (int)((d.e[y % NI] / p.topk) % p.Qc);
+      f.qa[y] = *reinterpret_cast<const u32x4*>(p.q + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + 8 * cc);
+      f.qi[y] = *reinterpret_cast<const u32x4*>(p.q_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX +
+                                                8 * (cc % ICH));
+    }
+    if (tid < 32) {
+      const int hh = tid % G;
+      const int i = p.q0 + (int)((d.e2 / p.topk) % p.Qc);
+      f.lse = kp.lse[((size_t)b * p.H_q + g * G + hh) * p.S_q + i];
+      f.lsez = kp.lse_idx[((size_t)b * p.H_kv + g) * p.S_q + i];
+    }
+    f.id = d;
+  };
+  // Pipeline, in issue order: sub-tile n stages rows fetched during n - 2,
+  // requests the ids of n + 3 and then the rows of n + 2, computes, and
+  // stores its dq_idx records.  Every request but the statistics is
+  // unconditional (past the end the cursor repeats the last sub-tile, and
+  // rows that store no record write the sink), so the memory counter's
+  // order is the same on every iteration and its waits stay tight.
+  Cursor cur{-1, -QW, 0, nullptr};
+  bool h0 = next(cur), h1 = false, h2 = false;
+  Fetched fx, fy;
+  Ids ids;
+
+  // The dq_idx record of each query of a sub-tile, written by the lanes of
+  // its first row (the other rows hold the same values); every other lane,
+  // and the dummy stores of the prologue, write the sink.
+  auto store_records = [&](const f32x16& qacc, bool dummy) {
+    const int q = n / G, hh = n - (n / G) * G;
+    const int sl = dummy ? -1 : s_slot[q];
+    const long slot = hh == 0 && sl >= 0 ? sl : kp.sink;
+    float m = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m = max3abs(qacc[r], qacc[r], m);
+    m = __builtin_fmaxf(m, swap_halves(m));
+    const float inv = m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
+    u32x4* rec = reinterpret_cast<u32x4*>(kp.rec + (slot * NDT + wave) * 32 + 16 * h);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x4 v4;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        v4[x] = pack_f16x2(qacc[8 * half + 2 * x] * inv, qacc[8 * half + 2 * x + 1] * inv);
+      rec[half] = v4;
+    }
+    kp.rec_sc[slot * NDT + wave] = m;  // both halves store the same m
+  };
+
+  auto step = [&](Fetched& f) {
+    __syncthreads();  // the previous sub-tile's LDS reads are done
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int r = 2 * pr + y;
+      sq[r * 16 + (cc ^ rsw(r))] = f.qa[y];
+      if (cc < ICH) sqi[r * ICH + (cc ^ (rsw(r) & (ICH - 1)))] = f.qi[y];
+    }
+    if (tid < 32) {
+      const int x = f.id.e2;
+      const bool valid = (f.id.valid >> 2) & 1;
+      s_lse[tid] = valid ? f.lse * kLog2e : __builtin_inff();
+      if (tid % G == 0) {
+        const int i = p.q0 + (int)((x / p.topk) % p.Qc);
+        s_lsez[tid / G] = valid ? f.lsez * kLog2e : __builtin_inff();
+        s_t[tid / G] = valid ? i + off : -1;
+        s_slot[tid / G] = valid ? x : -1;
       }
     }
     __syncthreads();
-    Cursor nx = cur;
-    const bool have_next = next(nx);
+    {
+      const bool h3 = h2 && next(cur);
+      Ids nid;
+      load_ids(cur, nid);
+      fetch(ids, f);
+      ids = nid;
+      h2 = h3;
+    }
+    asm volatile("" ::: "memory");
 
     // S and z for this wave's 32 keys: rows on registers, keys on lanes.
     f32x16 sacc = zero16(), zacc = zero16();
@@ -228,28 +312,33 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
         const u32x4 gb = *reinterpret_cast<const u32x4*>(&sg[n * kGStride + 16 * ks + 8 * h]);
         qacc = mfma32x32x16(ka, gb, qacc);
       }
-      const int q = n / G, hh = n - (n / G) * G;
-      const int sl = s_slot[q];
-      float m = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) m = max3abs(qacc[r], qacc[r], m);
-      m = __builtin_fmaxf(m, swap_halves(m));
-      if (hh == 0 && sl >= 0) {
-        const float inv = m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
-        u32x4* rec = reinterpret_cast<u32x4*>(kp.rec + ((size_t)sl * NDT + wave) * 32 + 16 * h);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          u32x4 v4;
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            v4[x] = pack_f16x2(qacc[8 * half + 2 * x] * inv, qacc[8 * half + 2 * x + 1] * inv);
-          rec[half] = v4;
-        }
-        if (h == 0) kp.rec_sc[(size_t)sl * NDT + wave] = m;
-      }
+      store_records(qacc, false);
     }
-    cur = nx;
-    have = have_next;
+  };
+  if (h0) {  // uniform
+    Ids i0;
+    load_ids(cur, i0);
+    h1 = next(cur);
+    load_ids(cur, ids);
+    fetch(i0, fx);
+    if (wave < NDT) store_records(zero16(), true);
+    h2 = h1 && next(cur);
+    Ids i2;
+    load_ids(cur, i2);
+    fetch(ids, fy);
+    ids = i2;
+    if (wave < NDT) store_records(zero16(), true);
+  }
+  while (h0) {  // uniform
+    bool hb = h2;
+    step(fx);
+    h0 = h1;
+    h1 = hb;
+    if (!h0) break;
+    hb = h2;
+    step(fy);
+    h0 = h1;
+    h1 = hb;
   }
 
   // This group's dk_idx for the wave's keys (fp32, summed over chunks).
@@ -339,8 +428,9 @@ KlBwdLayout make_kl_bwd_layout(const AttnShape& s, int D_idx) {
   if (qc >= 128) qc -= qc % 128;
   L.Qc = (int)std::max(1L, std::min<long>(qc, s.S_q));
   size_t o = layout_build(L, s);
-  K.rec = o;     o = align256(o + (size_t)L.E * D_idx * 2);
-  K.rec_sc = o;  o = align256(o + (size_t)L.E * (D_idx / 32) * 4);
+  // One record past the chunk's edges takes the stores of padding rows.
+  K.rec = o;     o = align256(o + (size_t)(L.E + 1) * D_idx * 2);
+  K.rec_sc = o;  o = align256(o + (size_t)(L.E + 1) * (D_idx / 32) * 4);
   K.dk_part = o; o = align256(o + (size_t)s.batch * s.H_kv * s.S_k * D_idx * 4);
   K.total = o;
   L.total = o;
@@ -396,6 +486,7 @@ hipError_t launch_kl_loss_bwd(const AttnShape& s, int D_idx, const uint16_t* q, 
   kp.lse = lse; kp.lse_idx = lse_idx; kp.coef = coef;
   kp.rec = reinterpret_cast<uint16_t*>(base + K.rec);
   kp.rec_sc = reinterpret_cast<float*>(base + K.rec_sc);
+  kp.sink = K.L.E;
   kp.dk_part = reinterpret_cast<float*>(base + K.dk_part);
   kp.dq_idx = dq_idx; kp.dk_idx = dk_idx; kp.D_idx = D_idx;
   switch (D_idx) {
