@@ -33,7 +33,7 @@ struct BwdParams {
   const uint16_t* dout;  // [B][S_q][H_q][D] bf16
   const uint16_t* out;   // forward output, same layout
   const float* lse;      // forward LSE [B][H_q][S_q] (natural log)
-  float2* stat;          // [B][H_q][S_q]: (LSE in log2 units, sum_d dO O)
+  float2* stat;          // [B][H_kv][S_q][G]: (LSE in log2 units, sum_d dO O), a query's heads together
   uint16_t* dq_rec;      // [slot][4][G][32] fp16: the edge's dq / its quarter's scale (rec_dim order)
   float* dq_sc;          // [slot][4][G]: max |dq| over each quarter of the head dims
   long sink;             // record slot written by padding rows (never read)
@@ -66,7 +66,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams bp) {
     const int i = (int)(bi % p.S_q);
     const int b = (int)(bi / p.S_q);
     const long li = ((long)b * p.H_q + h) * p.S_q + i;
-    bp.stat[li] = make_float2(bp.lse[li] * 1.4426950408889634f, acc);
+    const int G = p.H_q / p.H_kv;
+    bp.stat[(((long)b * p.H_kv + h / G) * p.S_q + i) * G + h % G] = make_float2(bp.lse[li] * 1.4426950408889634f, acc);
   }
 }
 
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
     if (tid < 32) {  // (loading it in every thread costs registers)
       const int hh = tid % G;
       const int i = p.q0 + (int)((d.e2 / p.topk) % p.Qc);
-      f.st = bp.stat[((size_t)b * p.H_q + g * G + hh) * p.S_q + i];
+      f.st = bp.stat[((size_t)bg * p.S_q + i) * G + hh];
     }
     f.id = d;
   };

@@ -56,6 +56,7 @@ struct Params {
   const uint16_t* q_idx;
   const uint16_t* k_idx;
   const float* lse_in;   // [B][H_q][S_q] natural-log LSE of the main branch
+  const float* lse_t;    // [B][H_kv][S_q][G]: the same in log2 units, grouped per query
   float* kl_rec;         // [slot][8]: sum P, sum P ln P, sum P (z - m), sum e^(z - m), m
   float* kl_rows;        // [B][H_kv][S_q] or null
   float* kl_lse;         // [B][H_kv][S_q]: log-sum-exp of the index scores over T, or null
@@ -73,7 +74,7 @@ struct Layout {
   long NB, E, T;
   int W, n_win;
   size_t counts, cursor, offsets, tile_off, blk_sums, edges, work, part_lse, part_sc, part_o, total;
-  size_t kl_rec, kl_wsum;  // alignment-loss layout only
+  size_t kl_rec, kl_wsum, lse_t;  // alignment-loss layout only
   int n_kl_wg;
 };
 
@@ -101,6 +102,9 @@ void launch_build(const AttnShape& s, const Layout& L, const Params& p, hipStrea
 // Sorts each bucket's edge slots ascending, so that work that sums over a
 // bucket's edges does so in a fixed order (attn_bwd.hip).
 void launch_bucket_sort(const Layout& L, const Params& p, hipStream_t st);
+// lse_t[b][g][i][hh] = log2(e) * lse[b][g G + hh][i]: the main branch's LSE of
+// a query's G heads in 4 G contiguous bytes (kl_loss.hip).
+void launch_lse_group(const AttnShape& s, const float* lse, float* lse_t, hipStream_t st);
 // Params with the shape, the layout and the build arrays of `base` filled in.
 Params base_params(const AttnShape& s, const Layout& L, char* base, const int32_t* idx);
 

@@ -31,7 +31,6 @@ constexpr int kGStride = kBlock + 8;  // bf16 per row of the g tile [row][key]
 
 struct KlBwdParams {
   Params e;
-  const float* lse;      // main-branch LSE [B][H_q][S_q] (natural log)
   const float* lse_idx;  // [B][H_kv][S_q]: log-sum-exp of z over T (natural log)
   float coef;            // gradient of the loss / (B * S_q * H_kv)
   uint16_t* rec;         // [slot][D_idx / 32][32] fp16 (rec_dim order) / scale
@@ -162,7 +161,7 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
     if (tid < 32) {
       const int hh = tid % G;
       const int i = p.q0 + (int)((d.e2 / p.topk) % p.Qc);
-      f.lse = kp.lse[((size_t)b * p.H_q + g * G + hh) * p.S_q + i];
+      f.lse = p.lse_t[((size_t)bg * p.S_q + i) * G + hh];
       f.lsez = kp.lse_idx[((size_t)b * p.H_kv + g) * p.S_q + i];
     }
     f.id = d;
@@ -213,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
     if (tid < 32) {
       const int x = f.id.e2;
       const bool valid = (f.id.valid >> 2) & 1;
-      s_lse[tid] = valid ? f.lse * kLog2e : __builtin_inff();
+      s_lse[tid] = valid ? f.lse : __builtin_inff();
       if (tid % G == 0) {
         const int i = p.q0 + (int)((x / p.topk) % p.Qc);
         s_lsez[tid / G] = valid ? f.lsez * kLog2e : __builtin_inff();
@@ -415,7 +414,7 @@ __global__ __launch_bounds__(256) void kl_dk_reduce_kernel(KlBwdParams kp) {
 
 struct KlBwdLayout {
   Layout L;
-  size_t rec, rec_sc, dk_part, total;
+  size_t rec, rec_sc, dk_part, lse_t, total;
 };
 
 KlBwdLayout make_kl_bwd_layout(const AttnShape& s, int D_idx) {
@@ -432,6 +431,7 @@ KlBwdLayout make_kl_bwd_layout(const AttnShape& s, int D_idx) {
   K.rec = o;     o = align256(o + (size_t)(L.E + 1) * D_idx * 2);
   K.rec_sc = o;  o = align256(o + (size_t)(L.E + 1) * (D_idx / 32) * 4);
   K.dk_part = o; o = align256(o + (size_t)s.batch * s.H_kv * s.S_k * D_idx * 4);
+  K.lse_t = o;   o = align256(o + (size_t)s.batch * s.H_q * s.S_q * 4);
   K.total = o;
   L.total = o;
   return K;
@@ -483,7 +483,10 @@ hipError_t launch_kl_loss_bwd(const AttnShape& s, int D_idx, const uint16_t* q, 
   KlBwdParams kp{};
   kp.e = base_params(s, K.L, base, idx);
   kp.e.q = q; kp.e.k = k; kp.e.q_idx = q_idx; kp.e.k_idx = k_idx;
-  kp.lse = lse; kp.lse_idx = lse_idx; kp.coef = coef;
+  kp.lse_idx = lse_idx; kp.coef = coef;
+  float* lse_t = reinterpret_cast<float*>(base + K.lse_t);
+  kp.e.lse_t = lse_t;
+  launch_lse_group(s, lse, lse_t, stream);
   kp.rec = reinterpret_cast<uint16_t*>(base + K.rec);
   kp.rec_sc = reinterpret_cast<float*>(base + K.rec_sc);
   kp.sink = K.L.E;

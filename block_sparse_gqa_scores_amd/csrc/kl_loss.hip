@@ -66,11 +66,10 @@ __global__ __launch_bounds__(kThreads, 2) void kl_partial_kernel(Params p) {
     s_slot[x] = sl;
     s_i[x] = p.q0 + (int)((sl / p.topk) % p.Qc);
   }
-  for (int x = tid; x < QT * G; x += kThreads) {
-    const int e = x / G, hh = x - (x / G) * G;
-    const int sl = p.edges[ebase + min(e, n_here - 1)];
-    const int i = p.q0 + (int)((sl / p.topk) % p.Qc);
-    s_lse[x] = p.lse_in[((size_t)b * p.H_q + g * G + hh) * p.S_q + i] * kLog2e;
+  __syncthreads();
+  {  // each edge's G head LSEs are one contiguous run of lse_t
+    const float* lq = p.lse_t + (size_t)bg * p.S_q * G;
+    for (int x = tid; x < QT * G; x += kThreads) s_lse[x] = lq[(size_t)s_i[x / G] * G + x % G];
   }
   {
     const size_t row_stride = (size_t)p.H_kv * kD;
@@ -356,8 +355,20 @@ Layout make_kl_layout(const AttnShape& s) {
   L.n_kl_wg = (int)((rows + 255) / 256);
   L.kl_rec = o;  o = align256(o + (size_t)L.E * 32);
   L.kl_wsum = o; o = align256(o + (size_t)L.n_kl_wg * 4);
+  L.lse_t = o;   o = align256(o + (size_t)s.batch * s.H_q * s.S_q * 4);
   L.total = o;
   return L;
+}
+
+__global__ void lse_group_kernel(const float* lse, float* lse_t, int H_q, int G, int S_q, long n) {
+  for (long x = (long)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (long)gridDim.x * blockDim.x) {
+    // x = ((b H_q + h) S_q + i): reads in order, writes to (b, h / G, i, h % G).
+    const int i = (int)(x % S_q);
+    const long bh = x / S_q;
+    const int h = (int)(bh % H_q);
+    const long b = bh / H_q;
+    lse_t[((b * (H_q / G) + h / G) * S_q + i) * G + h % G] = lse[x] * 1.4426950408889634f;
+  }
 }
 
 __global__ void fill_zero_kernel(float* a, long n) {
@@ -365,6 +376,14 @@ __global__ void fill_zero_kernel(float* a, long n) {
     a[x] = 0.f;
 }
 }  // namespace
+
+namespace edges {
+void launch_lse_group(const AttnShape& s, const float* lse, float* lse_t, hipStream_t st) {
+  const long n = (long)s.batch * s.H_q * s.S_q;
+  hipLaunchKernelGGL(lse_group_kernel, dim3(grid_cap(n, 256)), dim3(256), 0, st, lse, lse_t, s.H_q,
+                     s.H_q / s.H_kv, s.S_q, n);
+}
+}  // namespace edges
 
 hipError_t launch_fill_zero(float* dst, long n, hipStream_t stream) {
   hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_cap(n, 256)), dim3(256), 0, stream, dst, n);
@@ -411,6 +430,9 @@ hipError_t launch_kl_loss(const AttnShape& s, int D_idx, const uint16_t* q, cons
   p.q = q; p.k = k; p.q_idx = q_idx; p.k_idx = k_idx; p.lse_in = lse;
   p.kl_rec = reinterpret_cast<float*>(base + L.kl_rec);
   p.kl_wsum = reinterpret_cast<float*>(base + L.kl_wsum);
+  float* lse_t = reinterpret_cast<float*>(base + L.lse_t);
+  p.lse_t = lse_t;
+  launch_lse_group(s, lse, lse_t, stream);
   p.kl_rows = kl_rows;
   p.kl_lse = lse_idx;
   p.loss = loss;
