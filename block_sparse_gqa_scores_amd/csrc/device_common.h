@@ -31,6 +31,16 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                  0, 0, 0);
 }
 
+// D = A * B + C on a 16x16 tile with K = 32 (v_mfma_f32_16x16x32_bf16).
+// Lane l supplies A[m = l % 16][k = 8 * (l / 16) + e] and
+// B[k = 8 * (l / 16) + e][n = l % 16] for e = 0..7; it receives
+// D[m = 4 * (l / 16) + r][n = l % 16] in register r (checked on the device).
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 // Row index (within a 32x32 MFMA output tile) held by register r of lane l.

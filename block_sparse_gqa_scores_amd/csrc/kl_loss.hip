@@ -117,13 +117,28 @@ __global__ __launch_bounds__(kThreads, 2) void kl_partial_kernel(Params p) {
     for (int ks = 0; ks < DIDX / 16; ++ks) di[ks] = *reinterpret_cast<const u32x4*>(irow + 16 * ks);
   };
 
-  u32x4 qb[8], ib[DIDX / 16];
+  // With G >= 8 a sub-tile has at most 4 queries, and z (one value per query
+  // and key) takes 16x16x32 instructions whose A row m carries query m % 4
+  // (the last query repeated past QW): every 16-lane group of the result then
+  // holds all the queries, in register order, for its 16 keys.
+  constexpr bool kZ16 = G >= 8;
+  constexpr int ZKS = DIDX / 32;
+  const int qz = min(lane & 3, QW - 1);
+  auto load_qz = [&](u32x4* dz, int i) {
+    const uint16_t* irow = p.q_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < ZKS; ++ks) dz[ks] = *reinterpret_cast<const u32x4*>(irow + 32 * ks);
+  };
+
+  u32x4 qb[8], ib[kZ16 ? 1 : DIDX / 16], iz[kZ16 ? ZKS : 1];
   load_q(qb, s_i[wave * QW + qm]);
-  load_qi(ib, s_i[wave * QW + qm]);
+  if constexpr (kZ16) load_qz(iz, s_i[wave * QW + qz]);
+  else load_qi(ib, s_i[wave * QW + qm]);
   for (int sub = 0; sub < n_here; sub += 4 * QW) {
     const int e0 = sub + wave * QW;  // first edge of this wave's sub-tile
     if (e0 >= n_here) break;         // wave-uniform
     const int i_next = s_i[min(e0 + 4 * QW, QT - QW) + qm];
+    const int iz_next = s_i[min(e0 + 4 * QW, QT - QW) + qz];
 
     float lse2[16];
 #pragma unroll
@@ -137,18 +152,39 @@ __global__ __launch_bounds__(kThreads, 2) void kl_partial_kernel(Params p) {
 
     // Index scores first; the index rows of the next sub-tile load meanwhile.
     float pt[4][NL], zv[4][NL];
+    if constexpr (kZ16) {
+      // Key tiles 2 nt and 2 nt + 1 (16 keys each); lane n (= lane % 32)
+      // takes key 32 nt + n from the first for n < 16, else from the second,
+      // and register l is query l (= q_of(l) for G >= 8).
+      const bool upper = (lane >> 4) & 1;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int krow = nt * 32 + n;
-      f32x16 za = zero16();
+      for (int nt = 0; nt < 4; ++nt) {
+        const int k0 = nt * 32 + (lane & 15), k1 = k0 + 16;
+        f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < DIDX / 16; ++ks)
-        za = mfma32x32x16(ib[ks], itile[krow * ICH + ((2 * ks + h) ^ (krow & (ICH - 1)))], za);
+        for (int ks = 0; ks < ZKS; ++ks) {
+          const int ch = 4 * ks + (lane >> 4);
+          z0 = mfma16x16x32(iz[ks], itile[k0 * ICH + (ch ^ (k0 & (ICH - 1)))], z0);
+          z1 = mfma16x16x32(iz[ks], itile[k1 * ICH + (ch ^ (k1 & (ICH - 1)))], z1);
+        }
 #pragma unroll
-      for (int l = 0; l < NL; ++l) zv[nt][l] = za[l * RPS];
-      __builtin_amdgcn_sched_barrier(0);
+        for (int l = 0; l < NL; ++l) zv[nt][l] = upper ? z1[l] : z0[l];
+      }
+      load_qz(iz, iz_next);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int krow = nt * 32 + n;
+        f32x16 za = zero16();
+#pragma unroll
+        for (int ks = 0; ks < DIDX / 16; ++ks)
+          za = mfma32x32x16(ib[ks], itile[krow * ICH + ((2 * ks + h) ^ (krow & (ICH - 1)))], za);
+#pragma unroll
+        for (int l = 0; l < NL; ++l) zv[nt][l] = za[l * RPS];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      load_qi(ib, i_next);
     }
-    load_qi(ib, i_next);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int krow = nt * 32 + n;
