@@ -232,17 +232,42 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
     asm volatile("" ::: "memory");
 
     // S and z for this wave's 32 keys: rows on registers, keys on lanes.
-    f32x16 sacc = zero16(), zacc = zero16();
+    f32x16 sacc = zero16();
     const int krow = key0 + n;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const int ch = 2 * ks + h;
       sacc = mfma32x32x16(sq[n * 16 + (ch ^ rsw(n))], ktile[krow * 16 + (ch ^ (krow & 15))], sacc);
     }
+    // z of query slot l at key key0 + n.  With G >= 8 a sub-tile has at most
+    // 4 queries: 16x16x32 tiles whose A row m is query m % 4 (the last one
+    // repeated past QW), keys key0 .. + 15 and key0 + 16 .. + 31; lane n takes
+    // the tile holding its key, and register l is query l (= the query of
+    // slot l).  Otherwise z repeats each query's index row on its heads' rows.
+    float zv[NL];
+    if constexpr (G >= 8) {
+      const int qr = min(lane & 3, QW - 1) * G;  // a row of query qr / G in sqi
+      const int k0 = key0 + (lane & 15), k1 = k0 + 16;
+      f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < DIDX / 16; ++ks) {
-      const int ch = 2 * ks + h;
-      zacc = mfma32x32x16(sqi[n * ICH + (ch ^ (rsw(n) & (ICH - 1)))], itile[krow * ICH + (ch ^ (krow & (ICH - 1)))], zacc);
+      for (int ks = 0; ks < DIDX / 32; ++ks) {
+        const int ch = 4 * ks + (lane >> 4);
+        const u32x4 a = sqi[qr * ICH + (ch ^ (rsw(qr) & (ICH - 1)))];
+        z0 = mfma16x16x32(a, itile[k0 * ICH + (ch ^ (k0 & (ICH - 1)))], z0);
+        z1 = mfma16x16x32(a, itile[k1 * ICH + (ch ^ (k1 & (ICH - 1)))], z1);
+      }
+      const bool upper = (lane >> 4) & 1;
+#pragma unroll
+      for (int l = 0; l < NL; ++l) zv[l] = upper ? z1[l] : z0[l];
+    } else {
+      f32x16 zacc = zero16();
+#pragma unroll
+      for (int ks = 0; ks < DIDX / 16; ++ks) {
+        const int ch = 2 * ks + h;
+        zacc = mfma32x32x16(sqi[n * ICH + (ch ^ (rsw(n) & (ICH - 1)))], itile[krow * ICH + (ch ^ (krow & (ICH - 1)))], zacc);
+      }
+#pragma unroll
+      for (int l = 0; l < NL; ++l) zv[l] = zacc[l * RPS];
     }
     // Teacher per (query slot l, key): the mean over the query's heads.
     float lse4[16];
@@ -263,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
       if constexpr (G >= 8) acc += swap_halves(acc);
       const int q = mfma32_row(l * RPS, lane) / G;
       const bool vis = key_abs <= s_t[q];
-      const float pidx = __builtin_amdgcn_exp2f(__builtin_fmaf(zacc[l * RPS], kLog2e, -s_lsez[q]));
+      const float pidx = __builtin_amdgcn_exp2f(__builtin_fmaf(zv[l], kLog2e, -s_lsez[q]));
       gq[l] = vis ? kp.coef * (pidx - acc * invG) : 0.f;
     }
     // dk_idx += g^T q_idx: A = g of each register's row (a query's value on
