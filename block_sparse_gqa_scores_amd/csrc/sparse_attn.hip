@@ -430,6 +430,133 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
   }
 }
 
+// Decode form of the partial (one query per (b, g) row, S_q = 1): every
+// selected block is its own work item, so no bucket build is needed; one
+// workgroup per (b, g, entry e) writes the record of slot (b H_kv + g) k + e,
+// in the layout of attn_partial_kernel's records.  K rows go from memory
+// straight into the MFMA A operand; V goes through LDS row-major and comes
+// back transposed (ds_read_b64_tr_b16).  S^T = K q^T puts this wave's 32 keys
+// on registers and the heads on lanes; the block's per-head max and sum are
+// exchanged across the four waves in LDS; P goes to LDS as [head][key]; wave w
+// then forms O^T for head dims 32 w .. 32 w + 31 over all 128 keys.
+constexpr int kPStride = kBlock + 8;  // bf16 per head row of P
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void attn_decode_kernel(Params p) {
+  __shared__ u32x4 vtile[kBlock * 16];                  // V_j [key][chunk ^ rsw(key)]
+  __shared__ __align__(16) uint16_t sp[G * kPStride];   // P [head][key] bf16
+  __shared__ float s_m[4][32], s_l[4][32], s_a[4][32];  // per-wave max, sum, max |O|
+
+  const int e = blockIdx.x % p.topk;
+  const int bg = blockIdx.x / p.topk;
+  const int b = bg / p.H_kv, g = bg - b * p.H_kv;
+  const int t = p.S_k - 1;                              // the query's position
+  const int jj = p.idx[(long)bg * p.topk + e];
+  if (jj < 0 || jj > t / kBlock) return;  // uniform; the merge skips this entry too
+  const long slot = (long)bg * p.topk + e;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, n = lane & 31;
+  const float c = p.scale_log2;
+
+  // Every load first: V tile pieces, this lane's K row (key 32 w + n), q of
+  // head n (the last head repeated past G).
+  const size_t row_stride = (size_t)p.H_kv * kD;
+  const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+  const uint16_t* vb = p.v + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+  u32x4 vr[8], kr[8], qr[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int qd = it * kThreads + tid;
+    const int s = min(jj * kBlock + (qd >> 4), p.S_k - 1);  // rows past S_k: masked below
+    vr[it] = *reinterpret_cast<const u32x4*>(vb + (size_t)s * row_stride + 8 * (qd & 15));
+  }
+  {
+    const int s = min(jj * kBlock + 32 * wave + n, p.S_k - 1);
+    const uint16_t* qrow = p.q + ((size_t)b * p.H_q + g * G + min(n, G - 1)) * kD + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      kr[ks] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 16 * ks + 8 * h);
+      qr[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int qd = it * kThreads + tid;
+    const int row = qd >> 4;
+    vtile[row * 16 + ((qd & 15) ^ rsw(row))] = vr[it];
+  }
+
+  // S^T[key 32 w + 8 (r / 4) + 4 h + r % 4][head n].
+  f32x16 sacc = zero16();
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) sacc = mfma32x32x16(kr[ks], qr[ks], sacc);
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (jj * kBlock + 32 * wave + mfma32_row(r, lane) > t) sacc[r] = neg_inf();
+  float mx = max16(neg_inf(), sacc);
+  mx = __builtin_fmaxf(mx, swap_halves(mx));
+  if (h == 0) s_m[wave][n] = mx;
+  __syncthreads();  // also the V tile
+  mx = __builtin_fmaxf(__builtin_fmaxf(s_m[0][n], s_m[1][n]), __builtin_fmaxf(s_m[2][n], s_m[3][n]));
+  const float bias = -mx * c;
+  float l = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    sacc[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, bias));
+    l += sacc[r];
+  }
+  l += swap_halves(l);
+  if (h == 0) s_l[wave][n] = l;
+  if (n < G) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      uint2 v2;
+      v2.x = pack_bf16x2(sacc[4 * r4], sacc[4 * r4 + 1]);
+      v2.y = pack_bf16x2(sacc[4 * r4 + 2], sacc[4 * r4 + 3]);
+      *reinterpret_cast<uint2*>(&sp[n * kPStride + 32 * wave + 8 * r4 + 4 * h]) = v2;
+    }
+  }
+  __syncthreads();
+  l = (s_l[0][n] + s_l[1][n]) + (s_l[2][n] + s_l[3][n]);
+
+  // O^T[dim 32 w + 8 (r / 4) + 4 h + r % 4][head n] over keys 16 kk + 8 h + 0..7.
+  f32x16 oacc = zero16();
+  {
+    const int lr = lane & 15;
+    const int hn = min(n, G - 1);
+    const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int r0 = 16 * kk + 8 * h + (lr >> 2), r1 = r0 + 4;
+      const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(vtile) + lds_tile_off(r0, c0, rsw(r0)));
+      const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(vtile) + lds_tile_off(r1, c0, rsw(r1)));
+      const u32x4 pb = *reinterpret_cast<const u32x4*>(&sp[hn * kPStride + 16 * kk + 8 * h]);
+      oacc = mfma32x32x16(u32x4{a0.x, a0.y, a1.x, a1.y}, pb, oacc);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) amax = max3abs(oacc[r], oacc[r + 1], amax);
+  amax = __builtin_fmaxf(amax, swap_halves(amax));
+  if (h == 0) s_a[wave][n] = amax;
+  __syncthreads();
+  amax = __builtin_fmaxf(__builtin_fmaxf(s_a[0][n], s_a[1][n]), __builtin_fmaxf(s_a[2][n], s_a[3][n]));
+  if (n < G) {
+    const float inv = amax > 0.f ? 1.f / amax : 0.f;
+    uint2* po = reinterpret_cast<uint2*>(p.part_o + (size_t)slot * G * kD);
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      uint2 v2;
+      v2.x = pack_f16x2(oacc[4 * rq + 0] * inv, oacc[4 * rq + 1] * inv);
+      v2.y = pack_f16x2(oacc[4 * rq + 2] * inv, oacc[4 * rq + 3] * inv);
+      po[record_unit<G>(wave, rq, n, h)] = v2;
+    }
+    if (wave == 0 && h == 0) {
+      p.part_lse[(size_t)slot * G + n] = mx * c + __builtin_amdgcn_logf(l);
+      p.part_sc[(size_t)slot * G + n] = amax / l;
+    }
+  }
+}
+
 // Combines the partials of each (query, group): one wave per row.
 // O = sum_e 2^(lse_e - M) sc_e x_e / sum_e 2^(lse_e - M), LSE = M + log2(sum).
 // Every record shares one element order, so the sums run in record order and
@@ -638,10 +765,13 @@ static hipError_t launch_g(const AttnShape& s, const Layout& L, Params p, bool w
     p.q0 = q0;
     const bool first = q0 == 0, last = q0 + L.Qc >= s.S_q;
     mark(2, false, first, last);
-    launch_build(s, L, p, st);
+    if (s.S_q > 1) launch_build(s, L, p, st);
     mark(2, true, first, last);
     mark(3, false, first, last);
-    hipLaunchKernelGGL(attn_partial_kernel<G>, dim3((unsigned)L.T), dim3(kThreads), 0, st, p);
+    if (s.S_q > 1)
+      hipLaunchKernelGGL(attn_partial_kernel<G>, dim3((unsigned)L.T), dim3(kThreads), 0, st, p);
+    else  // one query per row: every selected block is its own work item
+      hipLaunchKernelGGL(attn_decode_kernel<G>, dim3((unsigned)(s.batch * s.H_kv * s.topk)), dim3(kThreads), 0, st, p);
     mark(3, true, first, last);
     const long rows = (long)s.batch * s.H_kv * L.Qc;
     mark(4, false, first, last);
