@@ -10,15 +10,17 @@
 // Schedule (the re-parameterisation of block-sparse attention as a
 // variable-length attention over key blocks that the MSA notes credit to
 // MoBA): the forward's edge buckets, walked KV-stationary.  One workgroup owns
-// one (batch, group, block): it loads K_j, V_j and K_j^T into LDS once and
+// one (batch, group, block): it loads K_j and V_j into LDS once and
 // runs every edge of the block (all query windows of the chunk), so dK_j and
 // dV_j accumulate in registers and are written once, with no atomics.  Its
 // four waves split the block's 128 keys; the edges go through in sub-tiles of
 // 32 MFMA rows (32 / G queries x G heads) staged in LDS, in a fixed order
 // (windows ascending, slots sorted inside each bucket), so the sums and the
-// results are identical from run to run.  dq of an edge needs all 128 keys:
-// dS goes through LDS and each wave then forms a quarter of the head dims,
-// written as a per-edge fp16 record; a merge adds a query's records.
+// results are identical from run to run.  Transposed operands (K^T, dO^T,
+// Q^T) come from the row-major tiles through transposing LDS reads.  dq of an
+// edge needs all 128 keys: dS goes through LDS and each wave then forms a
+// quarter of the head dims, written as a per-edge fp16 record; a merge adds a
+// query's records.
 #include "edge_buckets.h"
 
 namespace msa {
@@ -149,10 +151,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
 
   const int key0 = 32 * wave;          // this wave's keys within the block
   const int key_abs = j * kBlock + key0 + n;
-  // Sub-tiles in a fixed order: windows ascending, QW edges at a time.  The
-  // rows of the next sub-tile are fetched into registers while the current
-  // one computes; rows of queries past a bucket's end repeat its last edge
-  // with dO = 0 and LSE = +inf, so they add nothing.
+  // Sub-tiles in a fixed order: windows ascending, QW edges at a time (the
+  // fetch pipeline below keeps two sub-tiles of rows in flight); rows of
+  // queries past a bucket's end repeat its last edge with dO = 0 and
+  // LSE = +inf, so they add nothing.
   struct Cursor {
     int w, base, cnt;
     const int32_t* ed;

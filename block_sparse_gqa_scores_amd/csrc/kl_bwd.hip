@@ -16,7 +16,8 @@
 // waves split the block's keys.  Per 32-row sub-tile (32 / G queries x G
 // heads) it recomputes the teacher from S = Q K^T and the forward's LSE (the
 // head mean is an in-lane sum plus one half-wave exchange), the index scores
-// z with the query's index row repeated on its heads' rows, then g.  The
+// z (16x16x32 tiles with the sub-tile's queries on every 16-lane group for
+// G >= 8, else the query's index row repeated on its heads' rows), then g.  The
 // block's dk_idx accumulates in registers (per group; the groups are added in
 // a fixed order at the end, since all groups share one index key head);
 // dq_idx of each edge goes through LDS and a per-edge fp16 record, added per

@@ -29,9 +29,11 @@ namespace {
 // Scores are formed as S = Q K^T (query heads on MFMA rows, keys on lanes),
 // so the G heads of a query sit in registers of one lane (and of its partner
 // in the other half of the wave for G >= 8): the group mean of the teacher is
-// an in-lane sum.  The index scores use the same layout: the A operand holds
-// the query's index row once per head (G copies), which makes z(query, key)
-// land in the lanes that hold the teacher for (query, key).
+// an in-lane sum.  The index scores must land in the lanes that hold the
+// teacher for (query, key): for G >= 8 (at most 4 queries per sub-tile) they
+// come from 16x16x32 tiles whose A row m carries query m % 4 (see the kernel);
+// for G < 8 the A operand holds the query's index row once per head (G
+// copies), in the teacher's own layout.
 template <int G, int DIDX>
 __global__ __launch_bounds__(kThreads, 2) void kl_partial_kernel(Params p) {
   constexpr int QW = 32 / G;                 // queries per wave sub-tile
