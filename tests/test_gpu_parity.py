@@ -44,6 +44,12 @@ SMALL = [
     W("g32", 2, 300, 300, 32, 1, Didx=64, topk=4),                      # G = 32, one group
     W("topk1", 1, 400, 900, 8, 2, topk=1),                              # local block only
     W("decode_small", 3, 1, 5000, 16, 2, Didx=64),                      # S_q = 1: decode kernels
+    W("decode_mha", 2, 1, 3000, 4, 4, topk=8),                          # decode, G = 1
+    W("decode_g2", 2, 1, 2500, 8, 4, Didx=64, topk=5),                  # decode, G = 2
+    W("decode_g4", 3, 1, 4100, 8, 2),                                   # decode, G = 4
+    W("decode_g16", 2, 1, 3300, 32, 2, topk=6),                         # decode, G = 16
+    W("decode_g32", 2, 1, 2049, 32, 1, Didx=64),                        # decode, G = 32
+    W("decode_short", 4, 1, 300, 16, 2),                                # 3 blocks < k: unused entries
     W("decode_r32", 2, 4, 3001, 64, 8),                                 # 32 rows per sequence
     W("scale", 1, 300, 1400, 8, 4, topk=4),
     W("gain", 1, 1500, 3000, 16, 2, gain=True, topk=6),                 # uneven block scores
