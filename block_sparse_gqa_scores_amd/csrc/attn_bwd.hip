@@ -131,19 +131,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
   constexpr float kLog2e = 1.4426950408889634f;
   const float c = p.scale_log2;
 
-  {  // K_j, V_j row-major into LDS (rows past S_k clamped: masked for every query)
-    const size_t row_stride = (size_t)p.H_kv * kD;
-    const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
-    const uint16_t* vb = p.v + ((size_t)b * p.S_k * p.H_kv + g) * kD;
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int qd = it * kThreads + tid;
-      const int row = qd >> 4, cc = qd & 15;
-      const int s = min(j * kBlock + row, p.S_k - 1);
-      ktile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * cc);
-      vtile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(vb + (size_t)s * row_stride + 8 * cc);
-    }
-  }
 
   f32x16 dk_acc[4], dv_acc[4];  // [key row][d tile]: this wave's 32 keys x 128 dims
 #pragma unroll
@@ -251,7 +238,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
   // and the records of n - 1 stay in flight while n stages.  The prologue
   // issues the same sequence, with two dummy record stores.
   Cursor cur{-1, -QW, 0, nullptr};
+  // The block's tiles, loaded only when some edge selects the block (a
+  // workgroup without edges just writes zero gradients).
+  auto load_tiles = [&]() {  // K_j, V_j row-major into LDS (rows past S_k clamped: masked for every query)
+    const size_t row_stride = (size_t)p.H_kv * kD;
+    const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+    const uint16_t* vb = p.v + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int qd = it * kThreads + tid;
+      const int row = qd >> 4, cc = qd & 15;
+      const int s = min(j * kBlock + row, p.S_k - 1);
+      ktile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * cc);
+      vtile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(vb + (size_t)s * row_stride + 8 * cc);
+    }
+  };
   bool h0 = next(cur), h1 = false, h2 = false;
+  if (h0) load_tiles();  // uniform
   Fetched fx, fy;
   Ids ids;
   if (h0) {

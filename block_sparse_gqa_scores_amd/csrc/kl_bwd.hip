@@ -74,25 +74,6 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
   const float c = p.scale_log2;
   const float invG = 1.f / G;
 
-  {  // K_j and k_idx of block j (rows past S_k clamped: never visible)
-    const size_t row_stride = (size_t)p.H_kv * kD;
-    const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int qd = it * kThreads + tid;
-      const int row = qd >> 4, cc = qd & 15;
-      const int s = min(j * kBlock + row, p.S_k - 1);
-      ktile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * cc);
-    }
-    const uint16_t* ib = p.k_idx + (size_t)b * p.S_k * DIDX;
-#pragma unroll
-    for (int it = 0; it < kBlock * ICH / kThreads; ++it) {
-      const int qd = it * kThreads + tid;
-      const int row = qd / ICH, cc = qd % ICH;
-      const int s = min(j * kBlock + row, p.S_k - 1);
-      itile[row * ICH + (cc ^ (row & (ICH - 1)))] = *reinterpret_cast<const u32x4*>(ib + (size_t)s * DIDX + 8 * cc);
-    }
-  }
 
   f32x16 dk_acc[NDT];  // [key row][index-dim tile]: this wave's 32 keys
 #pragma unroll
@@ -174,7 +155,29 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
   // rows that store no record write the sink), so the memory counter's
   // order is the same on every iteration and its waits stay tight.
   Cursor cur{-1, -QW, 0, nullptr};
+  // The block's tiles, loaded only when some edge selects the block (a
+  // workgroup without edges just writes zero gradients).
+  auto load_tiles = [&]() {  // K_j and k_idx of block j (rows past S_k clamped: never visible)
+    const size_t row_stride = (size_t)p.H_kv * kD;
+    const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int qd = it * kThreads + tid;
+      const int row = qd >> 4, cc = qd & 15;
+      const int s = min(j * kBlock + row, p.S_k - 1);
+      ktile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * cc);
+    }
+    const uint16_t* ib = p.k_idx + (size_t)b * p.S_k * DIDX;
+#pragma unroll
+    for (int it = 0; it < kBlock * ICH / kThreads; ++it) {
+      const int qd = it * kThreads + tid;
+      const int row = qd / ICH, cc = qd % ICH;
+      const int s = min(j * kBlock + row, p.S_k - 1);
+      itile[row * ICH + (cc ^ (row & (ICH - 1)))] = *reinterpret_cast<const u32x4*>(ib + (size_t)s * DIDX + 8 * cc);
+    }
+  };
   bool h0 = next(cur), h1 = false, h2 = false;
+  if (h0) load_tiles();  // uniform
   Fetched fx, fy;
   Ids ids;
 
