@@ -162,22 +162,24 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
   __syncthreads();
 
   // Selection mode: this lane's row, its local block, and its kept blocks as
-  // 64-bit keys (order-preserving score << 32 | ~index: larger is better).
-  // Unused slots hold 0 (worse than any block); slots past k-1 hold ~0 (never
-  // the worst, never replaced).
+  // 64-bit keys (order-preserving score << 32 | ~index: larger is better),
+  // in ascending order, so keep[0] is the worst.  Unused slots hold 0 (worse
+  // than any block); slots past k-1 hold ~0 (never the worst, never moved).
   const int my_r = w_r0 + lane;
   const int my_l = my_r < R ? (my_r / a.H_kv + off) / kBlock : -1;
   uint64_t keep[kKeep];
 #pragma unroll
   for (int t = 0; t < kKeep; ++t) keep[t] = t < a.topk - 1 ? 0ull : ~0ull;
-  uint64_t worst = a.topk - 1 > 0 ? 0ull : ~0ull;
-  int wi = 0;
 
   const bool lo = lane < 32;
-  // Block max of block j for this lane's rows (tile kt in LDS).
-  auto block_max = [&](int j, const u32x4* kt, float (&best)[NT / 2]) {
+  // Block max of block j for this lane's rows (tile kt in LDS).  mid() runs
+  // right after the first tile row's matrix instructions are issued, so its
+  // vector work executes while they do (selection mode puts the previous
+  // block's Top-k offer there).
+  auto block_max = [&](int j, const u32x4* kt, float (&best)[NT / 2], auto&& mid) {
     // Selection mode skips blocks at or past every local block of the wave.
     if (SELECT ? j >= w_t_max / kBlock : j * kBlock > w_t_max) {
+      mid();
 #pragma unroll
       for (int p2 = 0; p2 < NT / 2; ++p2) best[p2] = neg_inf();  // nothing visible to this wave
     } else {
@@ -214,6 +216,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
 #pragma unroll
           for (int n = 0; n < NT; ++n) acc[n] = mfma32x32x16(ka[ks], qb[n][ks], acc[n]);
         }
+        if (mt == 0) mid();
         if (need_mask) {
 #pragma unroll
           for (int n = 0; n < NT; ++n)
@@ -241,24 +244,24 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
       }
     }
   };
-  // Selection mode: offer block j's max to this lane's row.
+  // Selection mode: offer block j's max to this lane's row.  A block enters
+  // when it beats the worst kept one (keep[0]), which drops out: the kept
+  // blocks below the new key move down one slot, and the key takes the slot
+  // above them.  Every slot is one pair of selects on compares that do not
+  // depend on each other, with no branch, so the offer can sit among the
+  // next block's matrix instructions.  Keys are distinct (they carry the block
+  // index), so the kept set after the last offer does not depend on the order
+  // of the offers.  Blocks at or past the local block (and j = INT_MAX) offer
+  // the key 0, which enters nowhere.
   auto offer = [&](int j, float bmax) {
-    const uint64_t x = ((uint64_t)order_key(bmax) << 32) | (uint32_t)~(uint32_t)j;
-    const bool take = j < my_l && x > worst;
-    if (__builtin_amdgcn_ballot_w64(take) != 0) {
-      if (take) {
+    const uint64_t x = j < my_l ? ((uint64_t)order_key(bmax) << 32) | (uint32_t)~(uint32_t)j : 0ull;
+    bool above[kKeep];  // x beats keep[t]
 #pragma unroll
-        for (int t = 0; t < kKeep; ++t)
-          if (t == wi) keep[t] = x;
-        worst = keep[0];
-        wi = 0;
+    for (int t = 0; t < kKeep; ++t) above[t] = x > keep[t];
 #pragma unroll
-        for (int t = 1; t < kKeep; ++t)
-          if (keep[t] < worst) {
-            worst = keep[t];
-            wi = t;
-          }
-      }
+    for (int t = 0; t < kKeep; ++t) {
+      const bool up = t + 1 < kKeep && above[t + 1];
+      keep[t] = up ? keep[t + 1] : (above[t] ? x : keep[t]);
     }
   };
 
@@ -266,6 +269,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
     // Two blocks per barrier: blocks jj, jj + 1 in buffers 2 h, 2 h + 1 (h =
     // pair parity); the next pair's tiles are loaded meanwhile and stored into
     // the other half.
+    // Each block's offer runs during the next block's matrix instructions;
+    // the last one after the loop.
+    int pend_j = INT_MAX;
+    float pend_b = 0.f;
     for (int jj = 0; jj < nj_live; jj += 2) {
       const int h = (jj >> 1) & 1;
       const bool more = jj + 2 < nj_live;
@@ -275,11 +282,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
       }
       asm volatile("" ::: "memory");
       float best[NT / 2];
-      block_max(j0 + jj, ktile[2 * h], best);
-      offer(j0 + jj, best[0]);
+      block_max(j0 + jj, ktile[2 * h], best, [&] { offer(pend_j, pend_b); });
+      pend_j = j0 + jj;
+      pend_b = best[0];
       if (jj + 1 < nj_live) {
-        block_max(j0 + jj + 1, ktile[2 * h + 1], best);
-        offer(j0 + jj + 1, best[0]);
+        block_max(j0 + jj + 1, ktile[2 * h + 1], best, [&] { offer(pend_j, pend_b); });
+        pend_j = j0 + jj + 1;
+        pend_b = best[0];
       }
       asm volatile("" ::: "memory");
       if (more) {
@@ -288,6 +297,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
       }
       __syncthreads();
     }
+    offer(pend_j, pend_b);
   } else {
     for (int jj = 0; jj < nj_live; ++jj) {
       const int j = j0 + jj;
@@ -296,7 +306,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
       // compute and its LDS stores after it, so the loads fly during the MFMAs.
       asm volatile("" ::: "memory");
       float best[NT / 2];
-      block_max(j, ktile[jj & 1], best);
+      block_max(j, ktile[jj & 1], best, [] {});
 #pragma unroll
       for (int p2 = 0; p2 < NT / 2; ++p2)
         stage[(wave * ROWS_W + 64 * p2 + lane) * kStageStride + jj] = best[p2];
