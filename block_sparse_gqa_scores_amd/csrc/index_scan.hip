@@ -55,6 +55,13 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   else return chunk ^ ((row >> 1) & 7);
 }
 
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4):
+// lane l of the wave writes them at wave_base + l.  wave_base is the same in
+// every lane.  A device function, so the host pass never sees the builtin.
+__device__ __forceinline__ void load_lds16(const uint16_t* src, u32x4* wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)wave_base, 16, 0, 0);
+}
+
 // NT 32-row MFMA N tiles per wave: every 16-byte key fragment read from LDS
 // feeds NT matrix instructions.  SELECT: selection mode (above).
 template <int DIDX, int NT, int WAVES, bool SELECT>
@@ -123,38 +130,32 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
   }
 
   const uint16_t* kbase = a.k_idx + (size_t)b * a.S_k * DIDX;
-  // Tile geometry of this thread's LOADS 16-byte pieces: piece q = it *
-  // kThreads + tid is key row q / CPR, chunk q % CPR (the same chunk for every
-  // piece, as kThreads % CPR == 0).  The indices are recomputed from an opaque
-  // copy of tid at each use instead of being held across the loop.
-  u32x4 pre[LOADS], pre2[LOADS];  // native vectors: stay in registers
+  // Key tiles go from memory straight into LDS (global_load_lds_dwordx4: lane
+  // l of a wave writes the 16 bytes at the wave's LDS base + 16 l), so no
+  // registers stage them.  LDS piece q = it * kThreads + tid is key row
+  // q / CPR, stored chunk q % CPR, which holds the row's chunk
+  // swz(row, q % CPR) (the swizzle is its own inverse).  The indices are
+  // recomputed from an opaque copy of tid at each use instead of being held
+  // across the loop.  Rows past S_k are causally masked for every query;
+  // reading a clamped row instead keeps the loads unconditional.
 #define MSA_TILE_TID                                                                       \
   int t_ = tid;                                                                            \
   asm volatile("" : "+v"(t_));
-  // Rows past S_k are causally masked for every query; reading a clamped row
-  // instead keeps the loads unconditional (a fixed count in flight).
-#define MSA_LOAD_TILE(J, PRE)                                                              \
+#define MSA_LOAD_TILE(J, BUF)                                                              \
   {                                                                                        \
     MSA_TILE_TID                                                                           \
     _Pragma("unroll") for (int it = 0; it < LOADS; ++it) {                                 \
-      const int s_ = min((J) * kBlock + (it * kThreads + t_) / CPR, a.S_k - 1);            \
-      PRE[it] = *reinterpret_cast<const u32x4*>(kbase + (size_t)s_ * DIDX + 8 * (t_ % CPR)); \
-    }                                                                                      \
-  }
-#define MSA_STORE_TILE(BUF, PRE)                                                           \
-  {                                                                                        \
-    MSA_TILE_TID                                                                           \
-    _Pragma("unroll") for (int it = 0; it < LOADS; ++it) {                                 \
-      const int row_ = (it * kThreads + t_) / CPR;                                         \
-      ktile[BUF][row_ * CPR + swz<DIDX>(row_, t_ % CPR)] = PRE[it];                        \
+      const int q_ = it * kThreads + t_;                                                   \
+      const int row_ = q_ / CPR;                                                           \
+      const int s_ = min((J) * kBlock + row_, a.S_k - 1);                                  \
+      load_lds16(kbase + (size_t)s_ * DIDX + 8 * swz<DIDX>(row_, q_ % CPR),                 \
+                 &ktile[BUF][it * kThreads + wave * 64]);                                  \
     }                                                                                      \
   }
 
   if (nj_live > 0) {
-    MSA_LOAD_TILE(j0, pre)
-    if constexpr (SELECT) { MSA_LOAD_TILE(j0 + min(1, nj_live - 1), pre2) }
-    MSA_STORE_TILE(0, pre)
-    if constexpr (SELECT) { MSA_STORE_TILE(1, pre2) }
+    MSA_LOAD_TILE(j0, 0)
+    if constexpr (SELECT) { MSA_LOAD_TILE(j0 + min(1, nj_live - 1), 1) }
   }
   // Everything loaded so far (index queries, first tile) has landed; saying so
   // explicitly keeps the loop's MFMAs from waiting on the next tile's loads.
@@ -276,9 +277,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
     for (int jj = 0; jj < nj_live; jj += 2) {
       const int h = (jj >> 1) & 1;
       const bool more = jj + 2 < nj_live;
+      // The other half was last read before the previous barrier.
       if (more) {
-        MSA_LOAD_TILE(j0 + jj + 2, pre)
-        MSA_LOAD_TILE(j0 + min(jj + 3, nj_live - 1), pre2)
+        MSA_LOAD_TILE(j0 + jj + 2, 2 * (h ^ 1))
+        MSA_LOAD_TILE(j0 + min(jj + 3, nj_live - 1), 2 * (h ^ 1) + 1)
       }
       asm volatile("" ::: "memory");
       float best[NT / 2];
@@ -290,35 +292,31 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
         pend_j = j0 + jj + 1;
         pend_b = best[0];
       }
-      asm volatile("" ::: "memory");
-      if (more) {
-        MSA_STORE_TILE(2 * (h ^ 1), pre)
-        MSA_STORE_TILE(2 * (h ^ 1) + 1, pre2)
-      }
+      // This wave's tile loads have landed before anyone reads them.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
     offer(pend_j, pend_b);
   } else {
     for (int jj = 0; jj < nj_live; ++jj) {
       const int j = j0 + jj;
-      if (jj + 1 < nj_live) { MSA_LOAD_TILE(j + 1, pre) }
-      // Compiler-only fences: keep the next tile's global loads before the
-      // compute and its LDS stores after it, so the loads fly during the MFMAs.
+      // The other buffer was last read before the previous barrier.
+      if (jj + 1 < nj_live) { MSA_LOAD_TILE(j + 1, (jj & 1) ^ 1) }
+      // Compiler-only fence: keep the next tile's loads before the compute,
+      // so they fly during the MFMAs.
       asm volatile("" ::: "memory");
       float best[NT / 2];
       block_max(j, ktile[jj & 1], best, [] {});
 #pragma unroll
       for (int p2 = 0; p2 < NT / 2; ++p2)
         stage[(wave * ROWS_W + 64 * p2 + lane) * kStageStride + jj] = best[p2];
-      asm volatile("" ::: "memory");
-      if (jj + 1 < nj_live) { MSA_STORE_TILE((jj & 1) ^ 1, pre) }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
   }
 
 #undef MSA_TILE_TID
 #undef MSA_LOAD_TILE
-#undef MSA_STORE_TILE
 
   if constexpr (SELECT) {
     // Kept blocks in ascending order, then the local block, then -1 padding.
