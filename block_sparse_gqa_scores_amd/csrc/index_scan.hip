@@ -134,22 +134,32 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
   // l of a wave writes the 16 bytes at the wave's LDS base + 16 l), so no
   // registers stage them.  LDS piece q = it * kThreads + tid is key row
   // q / CPR, stored chunk q % CPR, which holds the row's chunk
-  // swz(row, q % CPR) (the swizzle is its own inverse).  The indices are
-  // recomputed from an opaque copy of tid at each use instead of being held
-  // across the loop.  Rows past S_k are causally masked for every query;
-  // reading a clamped row instead keeps the loads unconditional.
-#define MSA_TILE_TID                                                                       \
-  int t_ = tid;                                                                            \
-  asm volatile("" : "+v"(t_));
+  // swz(row, q % CPR) (the swizzle is its own inverse): its element offset
+  // inside a key block is kofs[it].  A block that lies inside S_k is then a
+  // uniform base plus kofs; for the last, partial block the rows past S_k
+  // (causally masked for every query) read the last key row instead, which
+  // keeps the loads unconditional.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  int kofs[LOADS];
+#pragma unroll
+  for (int it = 0; it < LOADS; ++it) {
+    const int q = it * kThreads + tid;
+    kofs[it] = (q / CPR) * DIDX + 8 * swz<DIDX>(q / CPR, q % CPR);
+  }
 #define MSA_LOAD_TILE(J, BUF)                                                              \
   {                                                                                        \
-    MSA_TILE_TID                                                                           \
-    _Pragma("unroll") for (int it = 0; it < LOADS; ++it) {                                 \
-      const int q_ = it * kThreads + t_;                                                   \
-      const int row_ = q_ / CPR;                                                           \
-      const int s_ = min((J) * kBlock + row_, a.S_k - 1);                                  \
-      load_lds16(kbase + (size_t)s_ * DIDX + 8 * swz<DIDX>(row_, q_ % CPR),                 \
-                 &ktile[BUF][it * kThreads + wave * 64]);                                  \
+    const int j_ = (J);                                                                    \
+    const uint16_t* kb_ = kbase + (size_t)j_ * kBlock * DIDX;                              \
+    if (j_ * kBlock + kBlock <= a.S_k) {                                                   \
+      _Pragma("unroll") for (int it = 0; it < LOADS; ++it)                                 \
+        load_lds16(kb_ + kofs[it], &ktile[BUF][it * kThreads + wave_s * 64]);              \
+    } else {                                                                               \
+      _Pragma("unroll") for (int it = 0; it < LOADS; ++it) {                               \
+        const int row_ = kofs[it] / DIDX;                                                  \
+        const int s_ = min(j_ * kBlock + row_, a.S_k - 1);                                 \
+        load_lds16(kbase + (size_t)s_ * DIDX + (kofs[it] - row_ * DIDX),                   \
+                   &ktile[BUF][it * kThreads + wave_s * 64]);                              \
+      }                                                                                    \
     }                                                                                      \
   }
 
@@ -315,7 +325,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
     }
   }
 
-#undef MSA_TILE_TID
 #undef MSA_LOAD_TILE
 
   if constexpr (SELECT) {
