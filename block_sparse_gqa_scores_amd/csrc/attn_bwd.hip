@@ -195,14 +195,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
       const int r = 2 * pr + y, hh = r % G;
-      const int i = p.q0 + (int)((d.e[y % NI] / p.topk) % p.Qc);
+      const int i = slot_query(p, bg, d.e[y % NI]);
       const size_t rowoff = (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + 8 * cc;
       f.qa[y] = *reinterpret_cast<const u32x4*>(p.q + rowoff);
       f.da[y] = *reinterpret_cast<const u32x4*>(bp.dout + rowoff);
     }
     if (tid < 32) {  // (loading it in every thread costs registers)
       const int hh = tid % G;
-      const int i = p.q0 + (int)((d.e2 / p.topk) % p.Qc);
+      const int i = slot_query(p, bg, d.e2);
       f.st = bp.stat[((size_t)bg * p.S_q + i) * G + hh];
     }
     f.id = d;
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
       const bool valid = (f.id.valid >> 2) & 1;
       s_stat[tid] = valid ? f.st : make_float2(__builtin_inff(), 0.f);
       if (tid % G == 0) {
-        s_t[tid / G] = valid ? p.q0 + (int)((x / p.topk) % p.Qc) + off : -1;
+        s_t[tid / G] = valid ? slot_query(p, bg, x) + off : -1;
         s_slot[tid / G] = valid ? x : -1;
       }
     }

@@ -41,6 +41,8 @@ struct Params {
   int W, n_win;          // queries per window (a multiple of kBuildQueries unless
                          // it is the whole chunk), windows per chunk
   int QT;                // edges per work item
+  uint32_t topk_m;       // slot / topk == (slot * topk_m) >> topk_s (set_topk_divisor)
+  int topk_s;
   float scale_log2;
   int32_t* counts;
   int32_t* cursor;
@@ -67,6 +69,25 @@ struct Params {
 // Slot of edge (b, g, il, e) inside the chunk.
 __device__ __forceinline__ long slot_of(const Params& p, int bg, int il, int e) {
   return ((long)bg * p.Qc + il) * p.topk + e;
+}
+
+// Division of a slot by topk as a multiply and a shift (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994):
+// with l = ceil(log2 topk) and m = ceil(2^(31 + l) / topk) < 2^32,
+// n / topk == (n * m) >> (31 + l) for every 0 <= n < 2^31.  Slots are int32.
+inline void set_topk_divisor(Params& p) {
+  int l = 0;
+  while ((1 << l) < p.topk) ++l;
+  const uint64_t num = uint64_t(1) << (31 + l);
+  p.topk_m = (uint32_t)((num + (uint64_t)p.topk - 1) / (uint64_t)p.topk);
+  p.topk_s = 31 + l;
+}
+__device__ __forceinline__ int slot_row(const Params& p, int slot) {
+  return (int)(((uint64_t)(uint32_t)slot * p.topk_m) >> p.topk_s);
+}
+// Query of a slot of group row bg: slot / topk = bg * Qc + (query - q0).
+__device__ __forceinline__ int slot_query(const Params& p, int bg, int slot) {
+  return p.q0 + slot_row(p, slot) - bg * p.Qc;
 }
 
 struct Layout {

@@ -135,14 +135,14 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
       const int r = 2 * pr + y, hh = r % G;
-      const int i = p.q0 + (int)((d.e[y % NI] / p.topk) % p.Qc);
+      const int i = slot_query(p, bg, d.e[y % NI]);
       f.qa[y] = *reinterpret_cast<const u32x4*>(p.q + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + 8 * cc);
       f.qi[y] = *reinterpret_cast<const u32x4*>(p.q_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX +
                                                 8 * (cc % ICH));
     }
     if (tid < 32) {
       const int hh = tid % G;
-      const int i = p.q0 + (int)((d.e2 / p.topk) % p.Qc);
+      const int i = slot_query(p, bg, d.e2);
       f.lse = p.lse_t[((size_t)bg * p.S_q + i) * G + hh];
       f.lsez = kp.lse_idx[((size_t)b * p.H_kv + g) * p.S_q + i];
     }
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
       const bool valid = (f.id.valid >> 2) & 1;
       s_lse[tid] = valid ? f.lse : __builtin_inff();
       if (tid % G == 0) {
-        const int i = p.q0 + (int)((x / p.topk) % p.Qc);
+        const int i = slot_query(p, bg, x);
         s_lsez[tid / G] = valid ? f.lsez * kLog2e : __builtin_inff();
         s_t[tid / G] = valid ? i + off : -1;
         s_slot[tid / G] = valid ? x : -1;

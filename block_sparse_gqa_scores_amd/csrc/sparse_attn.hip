@@ -739,6 +739,7 @@ Params base_params(const AttnShape& s, const Layout& L, char* base, const int32_
   p.G = s.H_q / s.H_kv; p.n_blk = s.n_blk; p.topk = s.topk;
   p.Qc = L.Qc; p.NB = (int)L.NB; p.QT = L.QT; p.scale_log2 = s.scale_log2;
   p.W = L.W; p.n_win = L.n_win;
+  set_topk_divisor(p);
   p.counts = reinterpret_cast<int32_t*>(base + L.counts);
   p.cursor = reinterpret_cast<int32_t*>(base + L.cursor);
   p.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
