@@ -332,6 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
       // dV += P^T dO and dK += dS^T Q: A = this lane's P / dS (row = key,
       // k = the 8 rows of registers 8 kk .. 8 kk + 7), B = dO^T / Q^T rows of
       // the same 8 rows: 8 (e / 4) + 4 h + e % 4 + 16 kk.
+      u32x4 ds_bf[2];  // the bf16 dS of this lane's rows, also staged for dq below
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         u32x4 pa, sa;
@@ -343,6 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
         sa[1] = pack_bf16x2(dsv[8 * kk + 2], dsv[8 * kk + 3]);
         sa[2] = pack_bf16x2(dsv[8 * kk + 4], dsv[8 * kk + 5]);
         sa[3] = pack_bf16x2(dsv[8 * kk + 6], dsv[8 * kk + 7]);
+        ds_bf[kk] = sa;
         // Lane (d = 32 dt + n, h) needs rows r0 .. r0 + 3 and r0 + 8 .. r0 + 11
         // of column d: two transposing reads of the row-major staged tiles.
         const int r0 = 16 * kk + 4 * h;
@@ -361,11 +363,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
           dk_acc[dt] = mfma32x32x16(sa, qb, dk_acc[dt]);
         }
       }
-      // dS to LDS as [row][key] for dq.
+      // dS to LDS as [row][key] for dq: the halves of the dK operand above.
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const uint32_t w2 = pack_bf16x2(dsv[r], 0.f);
-        sds[mfma32_row(r, lane) * kSStride + key0 + n] = (uint16_t)(w2 & 0xFFFFu);
+        const uint32_t w2 = ds_bf[r >> 3][(r & 7) >> 1];
+        sds[mfma32_row(r, lane) * kSStride + key0 + n] = (uint16_t)((r & 1) ? (w2 >> 16) : (w2 & 0xFFFFu));
       }
       __syncthreads();
 
