@@ -38,6 +38,7 @@ struct KlBwdParams {
   float* rec_sc;         // [slot][D_idx / 32]
   long sink;             // record slot written by padding rows (never read)
   float* dk_part;        // [B][H_kv][S_k][D_idx] fp32, per group
+  int32_t* dk_flag;      // [B][H_kv][n_blk]: 1 if the group's dk_part rows of the block hold data
   uint16_t* dq_idx;      // [B][S_q][H_kv][D_idx] bf16
   uint16_t* dk_idx;      // [B][S_k][D_idx] bf16
   int D_idx;
@@ -178,6 +179,11 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
   };
   bool h0 = next(cur), h1 = false, h2 = false;
   if (h0) load_tiles();  // uniform
+  // Whether this group's dk_part rows of the block already hold an earlier
+  // chunk's sums; read before the loop's barriers, written after them.
+  const bool any = h0;
+  const long flag_at = (long)bg * p.n_blk + j;
+  const bool had = !kp.first && kp.dk_flag[flag_at] != 0;
   Fetched fx, fy;
   Ids ids;
 
@@ -369,18 +375,24 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
     h1 = hb;
   }
 
-  // This group's dk_idx for the wave's keys (fp32, summed over chunks).
+  // This group's dk_idx for the wave's keys (fp32, summed over chunks).  A
+  // block that no edge of the chunk selects stores nothing: its flag tells
+  // the reduce whether the rows hold anything (on a decode-shaped problem
+  // nearly every block is such a block).
+  if (any) {  // uniform
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    const int dcol = 32 * dt + n;
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int dcol = 32 * dt + n;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = j * kBlock + key0 + mfma32_row(r, lane);
-      if (key >= p.S_k) continue;
-      float* o = kp.dk_part + (((size_t)b * p.H_kv + g) * p.S_k + key) * DIDX + dcol;
-      *o = kp.first ? dk_acc[dt][r] : *o + dk_acc[dt][r];
+      for (int r = 0; r < 16; ++r) {
+        const int key = j * kBlock + key0 + mfma32_row(r, lane);
+        if (key >= p.S_k) continue;
+        float* o = kp.dk_part + (((size_t)b * p.H_kv + g) * p.S_k + key) * DIDX + dcol;
+        *o = had ? *o + dk_acc[dt][r] : dk_acc[dt][r];
+      }
     }
   }
+  if (tid == 0 && (kp.first || any)) kp.dk_flag[flag_at] = had || any;
 }
 
 // dq_idx of each row: the sum of its edges' records; 16 lanes per row, 8
@@ -425,7 +437,8 @@ __global__ __launch_bounds__(256) void kl_dq_merge_kernel(KlBwdParams kp) {
   *reinterpret_cast<uint2*>(o + rec_dim(quarter, pos + 4)) = hi;
 }
 
-// dk_idx = the sum of the groups' parts, in group order.
+// dk_idx = the sum of the groups' parts, in group order, over the groups
+// whose part of the key's block holds data (the others are zero).
 template <int DIDX>
 __global__ __launch_bounds__(256) void kl_dk_reduce_kernel(KlBwdParams kp) {
   const Params& p = kp.e;
@@ -436,14 +449,16 @@ __global__ __launch_bounds__(256) void kl_dk_reduce_kernel(KlBwdParams kp) {
     const int s = (int)(bs % p.S_k);
     const int b = (int)(bs / p.S_k);
     float acc = 0.f;
-    for (int g = 0; g < p.H_kv; ++g) acc += kp.dk_part[(((size_t)b * p.H_kv + g) * p.S_k + s) * DIDX + c2];
+    for (int g = 0; g < p.H_kv; ++g)
+      if (kp.dk_flag[((long)b * p.H_kv + g) * p.n_blk + s / kBlock] != 0)
+        acc += kp.dk_part[(((size_t)b * p.H_kv + g) * p.S_k + s) * DIDX + c2];
     kp.dk_idx[x] = (uint16_t)(pack_bf16x2(acc, 0.f) & 0xFFFFu);
   }
 }
 
 struct KlBwdLayout {
   Layout L;
-  size_t rec, rec_sc, dk_part, lse_t, total;
+  size_t rec, rec_sc, dk_part, dk_flag, lse_t, total;
 };
 
 KlBwdLayout make_kl_bwd_layout(const AttnShape& s, int D_idx) {
@@ -460,6 +475,7 @@ KlBwdLayout make_kl_bwd_layout(const AttnShape& s, int D_idx) {
   K.rec = o;     o = align256(o + (size_t)(L.E + 1) * D_idx * 2);
   K.rec_sc = o;  o = align256(o + (size_t)(L.E + 1) * (D_idx / 32) * 4);
   K.dk_part = o; o = align256(o + (size_t)s.batch * s.H_kv * s.S_k * D_idx * 4);
+  K.dk_flag = o; o = align256(o + (size_t)s.batch * s.H_kv * s.n_blk * 4);
   K.lse_t = o;   o = align256(o + (size_t)s.batch * s.H_q * s.S_q * 4);
   K.total = o;
   L.total = o;
@@ -520,6 +536,7 @@ hipError_t launch_kl_loss_bwd(const AttnShape& s, int D_idx, const uint16_t* q, 
   kp.rec_sc = reinterpret_cast<float*>(base + K.rec_sc);
   kp.sink = K.L.E;
   kp.dk_part = reinterpret_cast<float*>(base + K.dk_part);
+  kp.dk_flag = reinterpret_cast<int32_t*>(base + K.dk_flag);
   kp.dq_idx = dq_idx; kp.dk_idx = dk_idx; kp.D_idx = D_idx;
   switch (D_idx) {
     case 64: return launch_kl_bwd_d<64>(s, K, kp, stream);
