@@ -438,21 +438,28 @@ __global__ __launch_bounds__(256) void kl_dq_merge_kernel(KlBwdParams kp) {
 }
 
 // dk_idx = the sum of the groups' parts, in group order, over the groups
-// whose part of the key's block holds data (the others are zero).
+// whose part of the key's block holds data (the others are zero).  One
+// workgroup per (batch, key block); four index dims per thread and step.
 template <int DIDX>
 __global__ __launch_bounds__(256) void kl_dk_reduce_kernel(KlBwdParams kp) {
   const Params& p = kp.e;
-  const long n = (long)p.B * p.S_k * DIDX;
-  for (long x = (long)blockIdx.x * 256 + threadIdx.x; x < n; x += (long)gridDim.x * 256) {
-    const int c2 = (int)(x % DIDX);
-    const long bs = x / DIDX;
-    const int s = (int)(bs % p.S_k);
-    const int b = (int)(bs / p.S_k);
-    float acc = 0.f;
-    for (int g = 0; g < p.H_kv; ++g)
-      if (kp.dk_flag[((long)b * p.H_kv + g) * p.n_blk + s / kBlock] != 0)
-        acc += kp.dk_part[(((size_t)b * p.H_kv + g) * p.S_k + s) * DIDX + c2];
-    kp.dk_idx[x] = (uint16_t)(pack_bf16x2(acc, 0.f) & 0xFFFFu);
+  const int b = blockIdx.x / p.n_blk;
+  const int j = blockIdx.x - b * p.n_blk;
+  const int keys = min(kBlock, p.S_k - j * kBlock);
+  const int n4 = keys * DIDX / 4;
+  const size_t row0 = (size_t)j * kBlock * DIDX;  // the block's first element in a [S_k][D_idx] plane
+  for (int x = threadIdx.x; x < n4; x += 256) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int g = 0; g < p.H_kv; ++g) {
+      const long bg = (long)b * p.H_kv + g;
+      if (kp.dk_flag[bg * p.n_blk + j] == 0) continue;  // uniform
+      const float4 v = *reinterpret_cast<const float4*>(kp.dk_part + bg * p.S_k * DIDX + row0 + 4 * x);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    uint2 o;
+    o.x = pack_bf16x2(acc.x, acc.y);
+    o.y = pack_bf16x2(acc.z, acc.w);
+    *reinterpret_cast<uint2*>(kp.dk_idx + (size_t)b * p.S_k * DIDX + row0 + 4 * x) = o;
   }
 }
 
@@ -496,8 +503,7 @@ hipError_t launch_kl_bwd_g(const AttnShape& s, const KlBwdLayout& K, KlBwdParams
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  const long n = (long)s.batch * s.S_k * DIDX;
-  hipLaunchKernelGGL(kl_dk_reduce_kernel<DIDX>, dim3(grid_cap(n, 256)), dim3(256), 0, st, kp);
+  hipLaunchKernelGGL(kl_dk_reduce_kernel<DIDX>, dim3((unsigned)((long)s.batch * s.n_blk)), dim3(256), 0, st, kp);
   return hipGetLastError();
 }
 
