@@ -254,6 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
     }
   };
   bool h0 = next(cur), h1 = false, h2 = false;
+  const bool any = h0;   // some edge of this chunk selects the block
   if (h0) load_tiles();  // uniform
   Fetched fx, fy;
   Ids ids;
@@ -400,6 +401,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
     step(fy);
     h0 = h1;
     h1 = hb;
+  }
+
+  // A block that no edge of the chunk selects adds nothing: in a middle chunk
+  // the running sums stay as they are, and a one-chunk problem writes zero
+  // rows 16 bytes at a time (on a decode-shaped problem nearly every block is
+  // such a block).  First and last chunks of several take the path below.
+  if (!any) {  // uniform
+    if (!bp.first && !bp.last) return;
+    if (bp.first && bp.last) {
+      const int keys = min(kBlock, p.S_k - j * kBlock);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (int x = tid; x < keys * 16; x += kThreads) {  // 16 pieces of 16 bytes per row
+        const size_t o = (((size_t)b * p.S_k + j * kBlock + (x >> 4)) * p.H_kv + g) * kD + 8 * (x & 15);
+        *reinterpret_cast<u32x4*>(bp.dk + o) = z;
+        *reinterpret_cast<u32x4*>(bp.dv + o) = z;
+      }
+      return;
+    }
   }
 
   // dK (times the softmax scale) and dV of this wave's keys.
