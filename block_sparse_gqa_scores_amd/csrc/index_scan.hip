@@ -258,8 +258,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
   // Selection mode: offer block j's max to this lane's row.  A block enters
   // when it beats the worst kept one (keep[0]), which drops out: the kept
   // blocks below the new key move down one slot, and the key takes the slot
-  // above them.  Every slot is one pair of selects on compares that do not
-  // depend on each other, with no branch, so the offer can sit among the
+  // above them.  Every slot is a 64-bit compare and a nested select, and no
+  // slot depends on another; with no branch, the offer can sit among the
   // next block's matrix instructions.  Keys are distinct (they carry the block
   // index), so the kept set after the last offer does not depend on the order
   // of the offers.  Blocks at or past the local block (and j = INT_MAX) offer
@@ -278,10 +278,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
 
   if constexpr (SELECT) {
     // Two blocks per barrier: blocks jj, jj + 1 in buffers 2 h, 2 h + 1 (h =
-    // pair parity); the next pair's tiles are loaded meanwhile and stored into
-    // the other half.
-    // Each block's offer runs during the next block's matrix instructions;
-    // the last one after the loop.
+    // pair parity); the next pair's tiles load meanwhile straight into the
+    // other half.  Each block's offer runs during the next block's matrix
+    // instructions; the last one after the loop.
     int pend_j = INT_MAX;
     float pend_b = 0.f;
     for (int jj = 0; jj < nj_live; jj += 2) {
