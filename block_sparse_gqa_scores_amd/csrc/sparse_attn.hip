@@ -461,7 +461,10 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(Params p) {
   const float c = p.scale_log2;
 
   // Every load first: V tile pieces, this lane's K row (key 32 w + n), q of
-  // head n (the last head repeated past G).
+  // head n (the last head repeated past G).  The V pieces are read once and
+  // only staged through LDS, so they are loaded non-temporally (0.12 ->
+  // 0.11 ms on 64 x 256K); the same hint on the K rows, which feed the
+  // matrix operands directly, measured slower.
   const size_t row_stride = (size_t)p.H_kv * kD;
   const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
   const uint16_t* vb = p.v + ((size_t)b * p.S_k * p.H_kv + g) * kD;
@@ -470,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(Params p) {
   for (int it = 0; it < 8; ++it) {
     const int qd = it * kThreads + tid;
     const int s = min(jj * kBlock + (qd >> 4), p.S_k - 1);  // rows past S_k: masked below
-    vr[it] = *reinterpret_cast<const u32x4*>(vb + (size_t)s * row_stride + 8 * (qd & 15));
+    vr[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (size_t)s * row_stride + 8 * (qd & 15)));
   }
   {
     const int s = min(jj * kBlock + 32 * wave + n, p.S_k - 1);
