@@ -480,7 +480,8 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdParams bp) {
       const int f = lane + 64 * u;
       if (f >= NF) continue;
       const float sc = bp.dq_sc[slot * 4 * G + f / 4];  // (quarter, head) = f / 4
-      const u32x4 x = *reinterpret_cast<const u32x4*>(bp.dq_rec + slot * (4 * G * 32) + 8 * f);
+      // Each record is read once: a non-temporal load (1 % faster on 32K).
+      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp.dq_rec + slot * (4 * G * 32) + 8 * f));
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
         acc[u][2 * y] += sc * f16_lo(x[y]);
