@@ -33,6 +33,10 @@ using namespace edges;
 namespace {
 
 constexpr int kVStride = kBlock + 4;  // bf16 per row of the transposed V tile
+// 4-wave sub-tiles per forward work item: twice the backward's (kSubTiles),
+// so a bucket's K/V tiles are loaded for up to 512 edges (G = 8); measured
+// 1.7 % faster for the partial kernel on 32K than 256, 128 was 3 % slower.
+constexpr int kSubTilesFwd = 2 * kSubTiles;
 constexpr long kMergePairRows = 1 << 16;  // from this many rows on, two merge rows per wave
 
 // Record order of one slot's G x D partial outputs.  The MFMA output puts
@@ -255,7 +259,7 @@ __global__ void fill_kernel(Params p) {
 template <int G>
 __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
   constexpr int QW = 32 / G;  // queries per wave (32 MFMA rows = QW queries x G heads)
-  constexpr int QT = kSubTiles * 4 * QW;               // edges per work item
+  constexpr int QT = kSubTilesFwd * 4 * QW;            // edges per work item
   __shared__ u32x4 ktile[kBlock * 16];                 // [key][16 chunks], swizzled
   __shared__ uint32_t vt[kD * kVStride / 2];           // [d][key] bf16, padded rows
   __shared__ int32_t s_slot[QT];                       // this item's edge slots
@@ -672,7 +676,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse,
 Layout make_layout(const AttnShape& s) {
   Layout L{};
   const int G = s.H_q / s.H_kv;
-  L.QT = kSubTiles * 4 * (32 / G);
+  L.QT = kSubTilesFwd * 4 * (32 / G);
   const size_t per_query = (size_t)s.batch * s.H_kv * s.topk * ((size_t)G * (kD * 2 + 8) + 8 + 4);
   long qc = (long)(kPartBudget / per_query);
   if (qc >= 128) qc -= qc % 128;
