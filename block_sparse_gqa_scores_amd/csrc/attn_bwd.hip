@@ -506,35 +506,6 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdParams bp) {
   }
 }
 
-struct BwdLayout {
-  Layout L;
-  size_t stat, dq_rec, dq_sc, dk_acc, dv_acc, total;
-  int chunks;
-};
-
-BwdLayout make_bwd_layout(const AttnShape& s) {
-  BwdLayout B{};
-  Layout& L = B.L;
-  const int G = s.H_q / s.H_kv;
-  L.QT = kSubTiles * 4 * (32 / G);
-  const size_t per_query = (size_t)s.batch * s.H_kv * s.topk * ((size_t)G * (kD * 2 + 16) + 4);
-  long qc = (long)(kPartBudget / per_query);
-  if (qc >= 128) qc -= qc % 128;
-  L.Qc = (int)std::max(1L, std::min<long>(qc, s.S_q));
-  size_t o = layout_build(L, s);
-  B.chunks = (s.S_q + L.Qc - 1) / L.Qc;
-  B.stat = o;   o = align256(o + (size_t)s.batch * s.H_q * s.S_q * 8);
-  // One record past the chunk's edges takes the stores of padding rows.
-  B.dq_rec = o; o = align256(o + (size_t)(L.E + 1) * G * kD * 2);
-  B.dq_sc = o;  o = align256(o + (size_t)(L.E + 1) * G * 16);
-  const size_t kv = (size_t)s.batch * s.S_k * s.H_kv * kD * 4;
-  B.dk_acc = o; o = align256(o + (B.chunks > 1 ? kv : 0));
-  B.dv_acc = o; o = align256(o + (B.chunks > 1 ? kv : 0));
-  B.total = o;
-  L.total = o;
-  return B;
-}
-
 }  // namespace
 
 namespace edges {
@@ -568,15 +539,14 @@ hipError_t launch_bwd_g(const AttnShape& s, const BwdLayout& BL, BwdParams bp, h
 
 }  // namespace
 
-size_t sparse_attn_bwd_workspace(const AttnShape& s) { return make_bwd_layout(s).total; }
-
 hipError_t launch_sparse_attn_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const int32_t* idx, const uint16_t* out,
                                   const float* lse, const uint16_t* dout, uint16_t* dq,
                                   uint16_t* dk, uint16_t* dv, void* ws, size_t ws_bytes,
                                   hipStream_t stream) {
-  const BwdLayout BL = make_bwd_layout(s);
-  if (ws_bytes < BL.total) return hipErrorInvalidValue;
+  const int qc = bwd_chunk(s, ws_bytes);
+  if (qc <= 0) return hipErrorInvalidValue;
+  const BwdLayout BL = make_bwd_layout(s, qc);
   char* base = static_cast<char*>(ws);
   BwdParams bp{};
   bp.e = base_params(s, BL.L, base, idx);

@@ -13,20 +13,10 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace msa {
 namespace edges {
-
-constexpr int kThreads = 256;  // threads per workgroup of the edge kernels
-constexpr int kD = 128;         // head dim
-constexpr int kBlock = 128;     // keys per block
-constexpr int kSubTiles = 16;   // 4-wave sub-tiles per work item
-constexpr int kScanPerWg = 1024;
-constexpr size_t kPartBudget = size_t(16) << 30;  // bytes of partials per chunk
-constexpr int kBuildQueries = 256;   // queries per bucket-build workgroup
-constexpr int kHistBins = 8192;      // widest row whose histogram lives in LDS
-constexpr int kMinWindow = 2048;     // smallest query window (a multiple of kBuildQueries)
-constexpr int kMaxWindow = 16384;    // largest query window (bounds a bucket's edge count)
 
 struct Params {
   const uint16_t* q;
@@ -90,15 +80,6 @@ __device__ __forceinline__ int slot_query(const Params& p, int bg, int slot) {
   return p.q0 + slot_row(p, slot) - bg * p.Qc;
 }
 
-struct Layout {
-  int Qc, QT, n_scan_wg;
-  long NB, E, T;
-  int W, n_win;
-  size_t counts, cursor, offsets, tile_off, blk_sums, edges, work, part_lse, part_sc, part_o, total;
-  size_t kl_rec, kl_wsum, lse_t;  // alignment-loss layout only
-  int n_kl_wg;
-};
-
 // Gradient records of the backward kernels: per slot, quarters of 32 dims
 // (x heads) of 32 values each, in the order a transposed MFMA tile holds
 // them: position p = 16 h + r for MFMA register r of lane half h, which is
@@ -108,16 +89,6 @@ __device__ __forceinline__ int rec_dim(int quarter, int pos) {
   return 32 * quarter + 8 * (r >> 2) + 4 * h + (r & 3);
 }
 
-inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-inline int grid_cap(long n, int per) {
-  long g = (n + per - 1) / per;
-  return (int)std::max(1L, std::min(g, 65536L));
-}
-
-// Bucket geometry and the build arrays for a chunk of L.Qc queries (L.QT set
-// by the caller); returns the offset past them.
-size_t layout_build(Layout& L, const AttnShape& s);
 // Edge buckets of the chunk starting at p.q0: counts, scans, scatter.
 void launch_build(const AttnShape& s, const Layout& L, const Params& p, hipStream_t st);
 // Sorts each bucket's edge slots ascending, so that work that sums over a

@@ -24,6 +24,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace msa {
 namespace {
@@ -44,7 +45,7 @@ struct ScanArgs {
   int topk;
 };
 
-constexpr int kKeep = 15;  // selection mode: earlier blocks kept per row (k <= 16)
+constexpr int kKeep = kSelectKeep;  // selection mode: earlier blocks kept per row (k <= 16)
 
 // 16-byte chunk position inside an LDS row of the key tile, XOR-swizzled so
 // that the 16 lanes reading one chunk column of 16 consecutive rows hit 16
@@ -519,10 +520,6 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, flo
   else
     hipLaunchKernelGGL((index_scan_prefill<64, kNT, kWaves, false>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
-}
-
-bool index_select_fused(int S_q, int H_kv, int topk) {
-  return S_q * H_kv > 32 && topk <= kKeep + 1;
 }
 
 hipError_t launch_index_select(const uint16_t* q_idx, const uint16_t* k_idx, int32_t* sel,

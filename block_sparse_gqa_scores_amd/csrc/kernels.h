@@ -36,13 +36,22 @@ struct AttnShape {
   float scale_log2;  // softmax scale * log2(e)
   float scale;       // softmax scale
 };
+// Workspace of the attention forward: the default size (query chunks whose
+// per-edge records fit 16 GiB) and the smallest it accepts (one query per
+// chunk).  A launch runs in the largest query chunks that fit its ws_bytes
+// (never larger than the default ones); sparse_attn_chunks counts them, 0
+// when ws_bytes is below the minimum.
 size_t sparse_attn_workspace(const AttnShape& s);
-int sparse_attn_chunks(const AttnShape& s);
+size_t sparse_attn_workspace_min(const AttnShape& s);
+int sparse_attn_chunks(const AttnShape& s, size_t ws_bytes);
 
-// Optional stage events: ev[2 s] before the first launch of stage s,
-// ev[2 s + 1] after its last launch (stages 2, 3, 4 of msa_stage here).
+// Optional stage events of msa_forward_profiled: ev[0..1] bracket the index
+// scores, ev[2..3] the Top-k, and chunk c's attention stages take
+// ev[4 + 6 c + 2 m] (before) and ev[4 + 6 c + 2 m + 1] (after) for m = 0
+// (bucket build), 1 (partial), 2 (merge).  n >= 4 + 6 * chunks.
 struct StageEvents {
-  hipEvent_t ev[10];
+  const hipEvent_t* ev;
+  int n;
 };
 hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint16_t* k,
                               const uint16_t* v, const int32_t* idx, uint16_t* out, float* lse,
@@ -51,6 +60,8 @@ hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint1
 
 // Main branch, backward (see attn_bwd.hip).
 size_t sparse_attn_bwd_workspace(const AttnShape& s);
+size_t sparse_attn_bwd_workspace_min(const AttnShape& s);
+int sparse_attn_bwd_chunks(const AttnShape& s, size_t ws_bytes);
 hipError_t launch_sparse_attn_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const int32_t* idx, const uint16_t* out,
                                   const float* lse, const uint16_t* dout, uint16_t* dq,
@@ -59,6 +70,8 @@ hipError_t launch_sparse_attn_bwd(const AttnShape& s, const uint16_t* q, const u
 
 // Alignment loss, backward (see kl_bwd.hip).
 size_t kl_loss_bwd_workspace(const AttnShape& s, int D_idx);
+size_t kl_loss_bwd_workspace_min(const AttnShape& s, int D_idx);
+int kl_loss_bwd_chunks(const AttnShape& s, int D_idx, size_t ws_bytes);
 hipError_t launch_kl_loss_bwd(const AttnShape& s, int D_idx, const uint16_t* q, const uint16_t* k,
                               const uint16_t* q_idx, const uint16_t* k_idx, const int32_t* idx,
                               const float* lse, const float* lse_idx, float coef, uint16_t* dq_idx,

@@ -463,32 +463,6 @@ __global__ __launch_bounds__(256) void kl_dk_reduce_kernel(KlBwdParams kp) {
   }
 }
 
-struct KlBwdLayout {
-  Layout L;
-  size_t rec, rec_sc, dk_part, dk_flag, lse_t, total;
-};
-
-KlBwdLayout make_kl_bwd_layout(const AttnShape& s, int D_idx) {
-  KlBwdLayout K{};
-  Layout& L = K.L;
-  const int G = s.H_q / s.H_kv;
-  L.QT = kSubTiles * 4 * (32 / G);
-  const size_t per_query = (size_t)s.batch * s.H_kv * s.topk * ((size_t)D_idx * 2 + 16 + 4);
-  long qc = (long)(kPartBudget / per_query);
-  if (qc >= 128) qc -= qc % 128;
-  L.Qc = (int)std::max(1L, std::min<long>(qc, s.S_q));
-  size_t o = layout_build(L, s);
-  // One record past the chunk's edges takes the stores of padding rows.
-  K.rec = o;     o = align256(o + (size_t)(L.E + 1) * D_idx * 2);
-  K.rec_sc = o;  o = align256(o + (size_t)(L.E + 1) * (D_idx / 32) * 4);
-  K.dk_part = o; o = align256(o + (size_t)s.batch * s.H_kv * s.S_k * D_idx * 4);
-  K.dk_flag = o; o = align256(o + (size_t)s.batch * s.H_kv * s.n_blk * 4);
-  K.lse_t = o;   o = align256(o + (size_t)s.batch * s.H_q * s.S_q * 4);
-  K.total = o;
-  L.total = o;
-  return K;
-}
-
 template <int G, int DIDX>
 hipError_t launch_kl_bwd_g(const AttnShape& s, const KlBwdLayout& K, KlBwdParams kp, hipStream_t st) {
   const Layout& L = K.L;
@@ -522,14 +496,13 @@ hipError_t launch_kl_bwd_d(const AttnShape& s, const KlBwdLayout& K, const KlBwd
 
 }  // namespace
 
-size_t kl_loss_bwd_workspace(const AttnShape& s, int D_idx) { return make_kl_bwd_layout(s, D_idx).total; }
-
 hipError_t launch_kl_loss_bwd(const AttnShape& s, int D_idx, const uint16_t* q, const uint16_t* k,
                               const uint16_t* q_idx, const uint16_t* k_idx, const int32_t* idx,
                               const float* lse, const float* lse_idx, float coef, uint16_t* dq_idx,
                               uint16_t* dk_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
-  const KlBwdLayout K = make_kl_bwd_layout(s, D_idx);
-  if (ws_bytes < K.total) return hipErrorInvalidValue;
+  const int qc = kl_bwd_chunk(s, D_idx, ws_bytes);
+  if (qc <= 0) return hipErrorInvalidValue;
+  const KlBwdLayout K = make_kl_bwd_layout(s, D_idx, qc);
   char* base = static_cast<char*>(ws);
   KlBwdParams kp{};
   kp.e = base_params(s, K.L, base, idx);

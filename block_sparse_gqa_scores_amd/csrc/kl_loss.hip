@@ -382,22 +382,6 @@ __global__ __launch_bounds__(256) void kl_total_kernel(Params p, int n_wg, float
   if (threadIdx.x == 0) *p.loss = red[0] * inv_rows;
 }
 
-// The alignment loss keeps 32 bytes per edge, so one chunk covers all queries.
-Layout make_kl_layout(const AttnShape& s) {
-  Layout L{};
-  const int G = s.H_q / s.H_kv;
-  L.QT = kSubTiles * 4 * (32 / G);
-  L.Qc = s.S_q;
-  size_t o = layout_build(L, s);
-  const long rows = (long)s.batch * s.H_kv * s.S_q;
-  L.n_kl_wg = (int)((rows + 255) / 256);
-  L.kl_rec = o;  o = align256(o + (size_t)L.E * 32);
-  L.kl_wsum = o; o = align256(o + (size_t)L.n_kl_wg * 4);
-  L.lse_t = o;   o = align256(o + (size_t)s.batch * s.H_q * s.S_q * 4);
-  L.total = o;
-  return L;
-}
-
 __global__ void lse_group_kernel(const float* lse, float* lse_t, int H_q, int G, int S_q, long n) {
   for (long x = (long)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (long)gridDim.x * blockDim.x) {
     // x = ((b H_q + h) S_q + i): reads in order, writes to (b, h / G, i, h % G).
@@ -427,8 +411,6 @@ hipError_t launch_fill_zero(float* dst, long n, hipStream_t stream) {
   hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_cap(n, 256)), dim3(256), 0, stream, dst, n);
   return hipGetLastError();
 }
-
-size_t kl_loss_workspace(const AttnShape& s) { return make_kl_layout(s).total; }
 
 namespace {
 template <int G, int DIDX>

@@ -85,6 +85,42 @@ size_t forward_bm_bytes(const msa_dims& d) { return fused_select(d) ? 0 : align2
 
 msa_status from_hip(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
+// Default (`min` false) or smallest (`min` true) workspace of an entry point;
+// (size_t)-1 when the dims are not valid for it.
+size_t workspace_of(const msa_dims* d, int entry, bool min) {
+  const size_t bad = ~size_t(0);
+  switch (entry) {
+    case MSA_ENTRY_INDEX_SCORES:
+      return check_dims(d, true, false) == MSA_OK ? 0 : bad;
+    case MSA_ENTRY_BLOCK_TOPK:
+      return check_dims(d, false, false) == MSA_OK ? 0 : bad;
+    case MSA_ENTRY_SPARSE_ATTN_FWD:
+      if (check_dims(d, false, true) != MSA_OK) return bad;
+      if (is_empty(*d)) return 0;
+      return min ? msa::sparse_attn_workspace_min(attn_shape(*d)) : msa::sparse_attn_workspace(attn_shape(*d));
+    case MSA_ENTRY_FORWARD:
+      if (check_dims(d, true, true) != MSA_OK) return bad;
+      if (is_empty(*d)) return 0;
+      return forward_bm_bytes(*d) + align256(idx_bytes(*d)) +
+             (min ? msa::sparse_attn_workspace_min(attn_shape(*d)) : msa::sparse_attn_workspace(attn_shape(*d)));
+    case MSA_ENTRY_KL_LOSS_FWD:
+      if (check_dims(d, true, true) != MSA_OK) return bad;
+      return is_empty(*d) ? 0 : msa::kl_loss_workspace(attn_shape(*d));
+    case MSA_ENTRY_SPARSE_ATTN_BWD:
+      if (check_dims(d, false, true) != MSA_OK) return bad;
+      if (is_empty(*d)) return 0;
+      return min ? msa::sparse_attn_bwd_workspace_min(attn_shape(*d))
+                 : msa::sparse_attn_bwd_workspace(attn_shape(*d));
+    case MSA_ENTRY_KL_LOSS_BWD:
+      if (check_dims(d, true, true) != MSA_OK) return bad;
+      if (is_empty(*d)) return 0;
+      return min ? msa::kl_loss_bwd_workspace_min(attn_shape(*d), d->index_dim)
+                 : msa::kl_loss_bwd_workspace(attn_shape(*d), d->index_dim);
+    default:
+      return bad;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -102,32 +138,27 @@ const char* msa_status_str(msa_status s) {
   return "MSA_ERR_UNKNOWN";
 }
 
-size_t msa_workspace_bytes(const msa_dims* d, int entry) {
-  const size_t bad = ~size_t(0);
+size_t msa_workspace_bytes(const msa_dims* d, int entry) { return workspace_of(d, entry, false); }
+
+size_t msa_workspace_min_bytes(const msa_dims* d, int entry) { return workspace_of(d, entry, true); }
+
+int msa_attn_chunks(const msa_dims* d, int entry, size_t ws_bytes) {
+  const size_t need = workspace_of(d, entry, true);
+  if (need == ~size_t(0) || ws_bytes < need || is_empty(*d)) return 0;
+  const msa::AttnShape s = attn_shape(*d);
   switch (entry) {
-    case MSA_ENTRY_INDEX_SCORES:
-      return check_dims(d, true, false) == MSA_OK ? 0 : bad;
-    case MSA_ENTRY_BLOCK_TOPK:
-      return check_dims(d, false, false) == MSA_OK ? 0 : bad;
     case MSA_ENTRY_SPARSE_ATTN_FWD:
-      if (check_dims(d, false, true) != MSA_OK) return bad;
-      return is_empty(*d) ? 0 : msa::sparse_attn_workspace(attn_shape(*d));
+      return msa::sparse_attn_chunks(s, ws_bytes);
     case MSA_ENTRY_FORWARD:
-      if (check_dims(d, true, true) != MSA_OK) return bad;
-      if (is_empty(*d)) return 0;
-      return forward_bm_bytes(*d) + align256(idx_bytes(*d)) +
-             msa::sparse_attn_workspace(attn_shape(*d));
+      return msa::sparse_attn_chunks(s, ws_bytes - forward_bm_bytes(*d) - align256(idx_bytes(*d)));
     case MSA_ENTRY_KL_LOSS_FWD:
-      if (check_dims(d, true, true) != MSA_OK) return bad;
-      return is_empty(*d) ? 0 : msa::kl_loss_workspace(attn_shape(*d));
+      return 1;
     case MSA_ENTRY_SPARSE_ATTN_BWD:
-      if (check_dims(d, false, true) != MSA_OK) return bad;
-      return is_empty(*d) ? 0 : msa::sparse_attn_bwd_workspace(attn_shape(*d));
+      return msa::sparse_attn_bwd_chunks(s, ws_bytes);
     case MSA_ENTRY_KL_LOSS_BWD:
-      if (check_dims(d, true, true) != MSA_OK) return bad;
-      return is_empty(*d) ? 0 : msa::kl_loss_bwd_workspace(attn_shape(*d), d->index_dim);
+      return msa::kl_loss_bwd_chunks(s, d->index_dim, ws_bytes);
     default:
-      return bad;
+      return 0;
   }
 }
 
@@ -186,7 +217,7 @@ msa_status msa_sparse_attn_fwd(const msa_dims* d, const void* q, const void* k, 
       !aligned16(out) || (lse && !aligned16(lse)))
     return MSA_ERR_MISALIGNED;
   const msa::AttnShape s = attn_shape(*d);
-  const size_t need = msa::sparse_attn_workspace(s);
+  const size_t need = msa::sparse_attn_workspace_min(s);
   if (!ws || ws_bytes < need) return ws ? MSA_ERR_WORKSPACE_TOO_SMALL : MSA_ERR_NULL_PTR;
   if (!aligned16(ws)) return MSA_ERR_MISALIGNED;
   return from_hip(msa::launch_sparse_attn(
@@ -217,7 +248,7 @@ msa_status msa_sparse_attn_bwd(const msa_dims* d, const void* q, const void* k, 
       !aligned16(dk) || !aligned16(dv))
     return MSA_ERR_MISALIGNED;
   const msa::AttnShape s = attn_shape(*d);
-  const size_t need = msa::sparse_attn_bwd_workspace(s);
+  const size_t need = msa::sparse_attn_bwd_workspace_min(s);
   if (!ws || ws_bytes < need) return ws ? MSA_ERR_WORKSPACE_TOO_SMALL : MSA_ERR_NULL_PTR;
   if (!aligned16(ws)) return MSA_ERR_MISALIGNED;
   return from_hip(msa::launch_sparse_attn_bwd(
@@ -249,7 +280,7 @@ msa_status msa_kl_loss_bwd(const msa_dims* d, const void* q, const void* k, cons
       !aligned16(dk_idx))
     return MSA_ERR_MISALIGNED;
   const msa::AttnShape s = attn_shape(*d);
-  const size_t need = msa::kl_loss_bwd_workspace(s, d->index_dim);
+  const size_t need = msa::kl_loss_bwd_workspace_min(s, d->index_dim);
   if (!ws || ws_bytes < need) return ws ? MSA_ERR_WORKSPACE_TOO_SMALL : MSA_ERR_NULL_PTR;
   if (!aligned16(ws)) return MSA_ERR_MISALIGNED;
   const float coef = float(double(grad_loss) / (double(d->batch) * d->seqlen_q * d->num_heads_kv));
@@ -302,9 +333,10 @@ msa_status forward_impl(const msa_dims* d, const void* q, const void* k, const v
   const msa::AttnShape s = attn_shape(*d);
   const size_t bm_sz = forward_bm_bytes(*d);
   const size_t idx_sz = align256(idx_bytes(*d));
-  const size_t attn_sz = msa::sparse_attn_workspace(s);
-  const size_t need = bm_sz + idx_sz + attn_sz;
+  const size_t need = bm_sz + idx_sz + msa::sparse_attn_workspace_min(s);
   if (!ws || ws_bytes < need) return ws ? MSA_ERR_WORKSPACE_TOO_SMALL : MSA_ERR_NULL_PTR;
+  if (ev && ev->n < 4 + 6 * msa::sparse_attn_chunks(s, ws_bytes - bm_sz - idx_sz)) return MSA_ERR_INVALID_DIMS;
+  const size_t attn_sz = ws_bytes - bm_sz - idx_sz;
   if (!aligned16(ws)) return MSA_ERR_MISALIGNED;
   char* base = static_cast<char*>(ws);
   float* bm = reinterpret_cast<float*>(base);
@@ -312,7 +344,7 @@ msa_status forward_impl(const msa_dims* d, const void* q, const void* k, const v
   void* attn_ws = base + bm_sz + idx_sz;
   hipStream_t strm = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_INDEX_SCORES], strm);
+  if (ev) (void)hipEventRecord(ev->ev[0], strm);
   if (fused_select(*d)) {
     // One kernel scores and selects; the Top-k stage is empty.
     e = msa::launch_index_select(static_cast<const uint16_t*>(q_idx),
@@ -320,20 +352,20 @@ msa_status forward_impl(const msa_dims* d, const void* q, const void* k, const v
                                  d->seqlen_k, d->num_heads_kv, d->index_dim, s.n_blk, d->topk,
                                  strm);
     if (e != hipSuccess) return MSA_ERR_HIP;
-    if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_INDEX_SCORES + 1], strm);
-    if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_BLOCK_TOPK], strm);
+    if (ev) (void)hipEventRecord(ev->ev[1], strm);
+    if (ev) (void)hipEventRecord(ev->ev[2], strm);
   } else {
     e = msa::launch_index_scores(static_cast<const uint16_t*>(q_idx),
                                  static_cast<const uint16_t*>(k_idx), bm, d->batch, d->seqlen_q,
                                  d->seqlen_k, d->num_heads_kv, d->index_dim, s.n_blk, strm);
     if (e != hipSuccess) return MSA_ERR_HIP;
-    if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_INDEX_SCORES + 1], strm);
-    if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_BLOCK_TOPK], strm);
+    if (ev) (void)hipEventRecord(ev->ev[1], strm);
+    if (ev) (void)hipEventRecord(ev->ev[2], strm);
     e = msa::launch_block_topk(bm, idx, d->batch, d->seqlen_q, d->seqlen_k, d->num_heads_kv,
                                s.n_blk, d->topk, strm);
     if (e != hipSuccess) return MSA_ERR_HIP;
   }
-  if (ev) (void)hipEventRecord(ev->ev[2 * MSA_STAGE_BLOCK_TOPK + 1], strm);
+  if (ev) (void)hipEventRecord(ev->ev[3], strm);
   e = msa::launch_sparse_attn(s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                               static_cast<const uint16_t*>(v), idx, static_cast<uint16_t*>(out),
                               lse, attn_ws, attn_sz, strm, ev);
@@ -354,19 +386,11 @@ msa_status msa_forward_profiled(const msa_dims* d, const void* q, const void* k,
                                 int32_t* block_idx_out, void* ws, size_t ws_bytes, void* stream,
                                 void* const* events, int n_events) {
   if (!events) return MSA_ERR_NULL_PTR;
-  if (n_events < 2 * MSA_N_STAGES) return MSA_ERR_INVALID_DIMS;
-  msa::StageEvents ev;
-  for (int x = 0; x < 2 * MSA_N_STAGES; ++x) {
+  if (n_events < 4) return MSA_ERR_INVALID_DIMS;
+  for (int x = 0; x < n_events; ++x)
     if (!events[x]) return MSA_ERR_NULL_PTR;
-    ev.ev[x] = static_cast<hipEvent_t>(events[x]);
-  }
+  msa::StageEvents ev{reinterpret_cast<const hipEvent_t*>(events), n_events};
   return forward_impl(d, q, k, v, q_idx, k_idx, out, lse, block_idx_out, ws, ws_bytes, stream, &ev);
-}
-
-int msa_attn_chunks(const msa_dims* d) {
-  if (check_dims(d, false, true) != MSA_OK) return 0;
-  if (is_empty(*d)) return 0;
-  return msa::sparse_attn_chunks(attn_shape(*d));
 }
 
 }  // extern "C"

@@ -33,10 +33,6 @@ using namespace edges;
 namespace {
 
 constexpr int kVStride = kBlock + 4;  // bf16 per row of the transposed V tile
-// 4-wave sub-tiles per forward work item: twice the backward's (kSubTiles),
-// so a bucket's K/V tiles are loaded for up to 512 edges (G = 8); measured
-// 1.7 % faster for the partial kernel on 32K than 256, 128 was 3 % slower.
-constexpr int kSubTilesFwd = 2 * kSubTiles;
 constexpr long kMergePairRows = 1 << 16;  // from this many rows on, two merge rows per wave
 
 // Record order of one slot's G x D partial outputs.  The MFMA output puts
@@ -673,51 +669,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse,
   }
 }
 
-Layout make_layout(const AttnShape& s) {
-  Layout L{};
-  const int G = s.H_q / s.H_kv;
-  L.QT = kSubTilesFwd * 4 * (32 / G);
-  const size_t per_query = (size_t)s.batch * s.H_kv * s.topk * ((size_t)G * (kD * 2 + 8) + 8 + 4);
-  long qc = (long)(kPartBudget / per_query);
-  if (qc >= 128) qc -= qc % 128;
-  L.Qc = (int)std::max(1L, std::min<long>(qc, s.S_q));
-  size_t o = layout_build(L, s);
-  L.part_lse = o; o = align256(o + (size_t)L.E * G * 4);
-  L.part_sc = o;  o = align256(o + (size_t)L.E * G * 4);
-  L.part_o = o;   o = align256(o + (size_t)L.E * G * kD * 2);
-  L.total = o;
-  return L;
-}
-
 }  // namespace
 
 namespace edges {
-
-// Bucket geometry and the build arrays for a chunk of Qc queries; returns the
-// offset past them.
-size_t layout_build(Layout& L, const AttnShape& s) {
-  // Window: about QT edges per (window, block) bucket at the chunk's mean
-  // number of visible blocks, between kMinWindow and kMaxWindow queries; the
-  // whole chunk when that exceeds it.
-  const long vis = std::max(1L, ((long)s.S_k - s.S_q + s.S_q / 2) / kBlock);
-  long w = ((long)L.QT * vis / std::max(1, s.topk) + kBuildQueries - 1) / kBuildQueries * kBuildQueries;
-  w = std::min<long>(std::max<long>(w, kMinWindow), kMaxWindow);
-  L.W = w < L.Qc ? (int)w : L.Qc;
-  L.n_win = (L.Qc + L.W - 1) / L.W;
-  L.NB = (long)s.batch * s.H_kv * L.n_win * s.n_blk;
-  L.E = (long)s.batch * s.H_kv * L.Qc * s.topk;
-  L.T = (L.E + L.QT - 1) / L.QT + std::min(L.NB, L.E);
-  L.n_scan_wg = (int)((L.NB + kScanPerWg - 1) / kScanPerWg);
-  size_t o = 0;
-  L.counts = o;   o = align256(o + L.NB * 4);
-  L.cursor = o;   o = align256(o + L.NB * 4);
-  L.offsets = o;  o = align256(o + (L.NB + 1) * 4);
-  L.tile_off = o; o = align256(o + (L.NB + 1) * 4);
-  L.blk_sums = o; o = align256(o + (size_t)L.n_scan_wg * 8);
-  L.edges = o;    o = align256(o + L.E * 4);
-  L.work = o;     o = align256(o + L.T * 8);
-  return o;
-}
 
 // Edge buckets of the chunk starting at p.q0: counts, scans, scatter.
 void launch_build(const AttnShape& s, const Layout& L, const Params& p, hipStream_t st) {
@@ -759,38 +713,32 @@ Params base_params(const AttnShape& s, const Layout& L, char* base, const int32_
 
 }  // namespace edges
 
-size_t sparse_attn_workspace(const AttnShape& s) { return make_layout(s).total; }
-
-int sparse_attn_chunks(const AttnShape& s) {
-  const Layout L = make_layout(s);
-  return (s.S_q + L.Qc - 1) / L.Qc;
-}
-
 template <int G>
 static hipError_t launch_g(const AttnShape& s, const Layout& L, Params p, bool with_lse, hipStream_t st,
                            const StageEvents* ev) {
-  // Stage s of msa_stage: 2 = build, 3 = partial, 4 = merge.
-  auto mark = [&](int stage, bool after, bool first, bool last) {
-    if (ev && ((!after && first) || (after && last))) (void)hipEventRecord(ev->ev[2 * stage + (after ? 1 : 0)], st);
+  // Chunk c's stage m (0 = build, 1 = partial, 2 = merge) is bracketed by
+  // events 4 + 6 c + 2 m and 4 + 6 c + 2 m + 1 (see StageEvents).
+  auto mark = [&](int c, int m, int after) {
+    const int x = 4 + 6 * c + 2 * m + after;
+    if (ev && x < ev->n) (void)hipEventRecord(ev->ev[x], st);
   };
-  for (int q0 = 0; q0 < s.S_q; q0 += L.Qc) {
+  for (int q0 = 0, c = 0; q0 < s.S_q; q0 += L.Qc, ++c) {
     p.q0 = q0;
-    const bool first = q0 == 0, last = q0 + L.Qc >= s.S_q;
-    mark(2, false, first, last);
+    mark(c, 0, 0);
     if (s.S_q > 1) launch_build(s, L, p, st);
-    mark(2, true, first, last);
-    mark(3, false, first, last);
+    mark(c, 0, 1);
+    mark(c, 1, 0);
     if (s.S_q > 1)
       hipLaunchKernelGGL(attn_partial_kernel<G>, dim3((unsigned)L.T), dim3(kThreads), 0, st, p);
     else  // one query per row: every selected block is its own work item
       hipLaunchKernelGGL(attn_decode_kernel<G>, dim3((unsigned)(s.batch * s.H_kv * s.topk)), dim3(kThreads), 0, st, p);
-    mark(3, true, first, last);
+    mark(c, 1, 1);
     const long rows = (long)s.batch * s.H_kv * L.Qc;
-    mark(4, false, first, last);
+    mark(c, 2, 0);
     const int rpw = rows >= kMergePairRows ? 2 : 1;
     hipLaunchKernelGGL(merge_kernel<G>, dim3((unsigned)((rows + 4 * rpw - 1) / (4 * rpw))), dim3(kThreads), 0,
                        st, p, with_lse ? 1 : 0, rpw);
-    mark(4, true, first, last);
+    mark(c, 2, 1);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -801,8 +749,9 @@ hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint1
                               const uint16_t* v, const int32_t* idx, uint16_t* out, float* lse,
                               void* ws, size_t ws_bytes, hipStream_t stream,
                               const StageEvents* events) {
-  const Layout L = make_layout(s);
-  if (ws_bytes < L.total) return hipErrorInvalidValue;
+  const int qc = fwd_chunk(s, ws_bytes);
+  if (qc <= 0) return hipErrorInvalidValue;
+  const Layout L = make_fwd_layout(s, qc);
   char* base = static_cast<char*>(ws);
   Params p = base_params(s, L, base, idx);
   p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;

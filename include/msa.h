@@ -35,7 +35,16 @@
  *     returns its status and launches nothing.  A HIP launch error returns
  *     MSA_ERR_HIP.  Faults inside kernels surface at the caller's next
  *     synchronisation, as for any asynchronous HIP work.
- *   - Results are bit-identical from run to run.
+ *   - Results are bit-identical from run to run (for the same ws_bytes).
+ *   - Workspace: an entry point that takes `ws` accepts any ws_bytes from
+ *     msa_workspace_min_bytes(dims, entry) up; msa_workspace_bytes(dims,
+ *     entry) is the size it is designed for.  The entries that keep per-edge
+ *     records (the attention forward, msa_forward, both backward entries) run
+ *     the queries in the largest chunks whose workspace fits ws_bytes, never
+ *     larger than with msa_workspace_bytes (whole 128-query blocks from 128
+ *     queries on; msa_attn_chunks counts them).  Smaller workspaces give the
+ *     same forward results; the backward's key gradients are then summed
+ *     across chunks in fp32, so their last bits may depend on ws_bytes.
  *   - batch == 0 or seqlen_q == 0 is an empty problem: MSA_OK, no launch
  *     (except msa_kl_loss_fwd, which writes its loss of 0).
  *
@@ -61,7 +70,7 @@ typedef enum msa_status {
   MSA_ERR_INVALID_DIMS = 2,       /* negative sizes or scale, S_k < S_q, H_q % H_kv != 0, ... */
   MSA_ERR_UNSUPPORTED = 3,        /* meaningful, but outside the device path's set */
   MSA_ERR_MISALIGNED = 4,         /* a pointer is not 16-byte aligned */
-  MSA_ERR_WORKSPACE_TOO_SMALL = 5,/* ws_bytes < msa_workspace_bytes(...) */
+  MSA_ERR_WORKSPACE_TOO_SMALL = 5,/* ws_bytes < msa_workspace_min_bytes(...) */
   MSA_ERR_HIP = 6                 /* a HIP runtime call or launch failed */
 } msa_status;
 
@@ -147,8 +156,9 @@ msa_status msa_block_topk(const msa_dims* dims, const float* block_scores,
  * Entries of block_idx equal to -1 are ignored; the others must be distinct,
  * lie in 0 .. l_i, and include l_i (as msa_block_topk writes them).  Inputs
  * q, k, v, block_idx are read only.  `lse` may be NULL.  `ws` is scratch of at
- * least msa_workspace_bytes(dims, MSA_ENTRY_SPARSE_ATTN_FWD) bytes, owned by
- * the caller; its contents on entry do not matter and are clobbered.
+ * least msa_workspace_min_bytes(dims, MSA_ENTRY_SPARSE_ATTN_FWD) bytes (see
+ * the workspace convention above), owned by the caller; its contents on entry
+ * do not matter and are clobbered.
  */
 msa_status msa_sparse_attn_fwd(const msa_dims* dims, const void* q,
                                const void* k, const void* v,
@@ -165,7 +175,9 @@ msa_status msa_sparse_attn_fwd(const msa_dims* dims, const void* q,
  * first two run as one kernel that keeps each row's running Top-k in
  * registers and never writes the block scores (same selection, bit for bit).
  * `block_idx_out` (may be NULL) receives the selection; `lse` may be NULL.
- * `ws` must hold msa_workspace_bytes(dims, MSA_ENTRY_FORWARD) bytes.
+ * `ws` must hold at least msa_workspace_min_bytes(dims, MSA_ENTRY_FORWARD)
+ * bytes: the block scores (when they are written), the selection, then the
+ * attention's workspace in the rest.
  */
 msa_status msa_forward(const msa_dims* dims, const void* q, const void* k,
                        const void* v, const void* q_idx, const void* k_idx,
@@ -251,10 +263,11 @@ msa_status msa_kl_loss_fwd(const msa_dims* dims, const void* q, const void* k,
  * Outputs (written in full, bf16): dq like q; dk, dv like k and v (zero for
  * keys no query selects; an empty problem with batch > 0 writes dk = dv = 0).
  * Sums run in a fixed order: results are identical
- * from run to run.  `ws` holds msa_workspace_bytes(dims,
- * MSA_ENTRY_SPARSE_ATTN_BWD) bytes (edge lists, per-edge dq records of
- * G * (2 D + 16) bytes, and fp32 dk / dv sums when the queries run in several
- * chunks); contents on entry do not matter.  Uses the main-branch fields of
+ * from run to run for the same ws_bytes.  `ws` holds at least
+ * msa_workspace_min_bytes(dims, MSA_ENTRY_SPARSE_ATTN_BWD) bytes (edge lists,
+ * per-edge dq records of G * (2 D + 16) bytes per chunk, and fp32 dk / dv
+ * sums when the queries run in several chunks); contents on entry do not
+ * matter.  Uses the main-branch fields of
  * dims (index_dim is ignored).
  */
 msa_status msa_sparse_attn_bwd(const msa_dims* dims, const void* q, const void* k,
@@ -278,9 +291,10 @@ msa_status msa_sparse_attn_bwd(const msa_dims* dims, const void* q, const void* 
  * lse_idx as that call wrote it for the same selection.  Outputs bf16, written
  * in full: dq_idx like q_idx, dk_idx like k_idx (zero for keys no row
  * selects; an empty problem with batch > 0 writes dk_idx = 0).  Fixed
- * summation order: identical from run to run.  `ws` holds
- * msa_workspace_bytes(dims, MSA_ENTRY_KL_LOSS_BWD) bytes (edge lists,
- * 2 D_idx + 16 bytes per selected block per row, and fp32 dk_idx per group).
+ * summation order: identical from run to run.  `ws` holds at least
+ * msa_workspace_min_bytes(dims, MSA_ENTRY_KL_LOSS_BWD) bytes (edge lists,
+ * 2 D_idx + 16 bytes per selected block per row of a query chunk, and fp32
+ * dk_idx per group).
  */
 msa_status msa_kl_loss_bwd(const msa_dims* dims, const void* q, const void* k,
                            const void* q_idx, const void* k_idx,
@@ -301,12 +315,18 @@ typedef enum msa_stage {
 /*
  * msa_forward with timing instrumentation, for profilers and benchmarks (the
  * tracing hooks of the forward path; same arguments, same results).  `events`
- * holds 2 * MSA_N_STAGES caller-created hipEvent_t handles: events[2 s] is
- * recorded on `stream` before the first launch of stage s and events[2 s + 1]
- * after its last launch.  When the attention runs in several query chunks
- * (see msa_attn_chunks), each stage is launched once per chunk and the pair
- * spans all of them.  Returns MSA_ERR_NULL_PTR if events is NULL or holds a
- * NULL handle, MSA_ERR_INVALID_DIMS if n_events < 2 * MSA_N_STAGES.
+ * holds n_events caller-created hipEvent_t handles, all recorded on `stream`:
+ *   events[0], events[1]   before and after the index scores
+ *                          (MSA_STAGE_INDEX_SCORES; with the fused selection
+ *                          this pair covers the Top-k too)
+ *   events[2], events[3]   before and after the Top-k (MSA_STAGE_BLOCK_TOPK;
+ *                          an empty pair with the fused selection)
+ *   events[4 + 6 c + 2 m], events[4 + 6 c + 2 m + 1]
+ *                          before and after stage MSA_STAGE_ATTN_BUILD + m
+ *                          (m = 0, 1, 2) of query chunk c, c = 0 .. chunks-1
+ * where chunks = msa_attn_chunks(dims, MSA_ENTRY_FORWARD, ws_bytes).  Returns
+ * MSA_ERR_NULL_PTR if events is NULL or holds a NULL handle, and
+ * MSA_ERR_INVALID_DIMS if n_events < 4 + 6 * chunks.
  */
 msa_status msa_forward_profiled(const msa_dims* dims, const void* q, const void* k,
                                 const void* v, const void* q_idx, const void* k_idx,
@@ -315,18 +335,28 @@ msa_status msa_forward_profiled(const msa_dims* dims, const void* q, const void*
                                 void* const* events, int n_events);
 
 /*
- * Number of query chunks the attention stages run in for these dims (the
- * per-edge partial results of one chunk must fit the workspace budget of at
- * most 16 GiB); 0 for invalid dims.
+ * Number of query chunks the entry point runs in with a workspace of ws_bytes
+ * (see the workspace convention above): 1 or more for the entries that take a
+ * workspace (always 1 for MSA_ENTRY_KL_LOSS_FWD); 0 for invalid dims, an
+ * empty problem, ws_bytes below msa_workspace_min_bytes, or an entry without
+ * a workspace.
  */
-int msa_attn_chunks(const msa_dims* dims);
+int msa_attn_chunks(const msa_dims* dims, int entry, size_t ws_bytes);
 
 /*
- * Bytes of caller-provided workspace the given entry point needs for these
- * dims (0 for entries that need none).  Returns (size_t)-1 when the dims are
- * not valid for that entry point.
+ * Bytes of caller-provided workspace the given entry point is designed for
+ * with these dims (0 for entries that need none): its query chunks keep at
+ * most 16 GiB of per-edge records.  Returns (size_t)-1 when the dims are not
+ * valid for that entry point.
  */
 size_t msa_workspace_bytes(const msa_dims* dims, int entry);
+
+/*
+ * The smallest workspace the entry point accepts for these dims (one query
+ * per chunk); below it the call returns MSA_ERR_WORKSPACE_TOO_SMALL.
+ * (size_t)-1 when the dims are not valid for that entry point.
+ */
+size_t msa_workspace_min_bytes(const msa_dims* dims, int entry);
 
 /* Static, human-readable name of a status code. */
 const char* msa_status_str(msa_status status);

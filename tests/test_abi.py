@@ -138,10 +138,12 @@ def test_bwd_entry_checks():
         assert bwd(d, **{kw: NULL}) == 1, kw
         assert bwd(d, **{kw: MIS}) == 4, kw
     assert bwd(d, ws=NULL, nbytes=0) == 1 and bwd(d, ws=MIS) == 4
-    need = msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_BWD)
+    full = msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_BWD)
+    need = msa.msa_workspace_min_bytes(d, msa.ENTRY_SPARSE_ATTN_BWD)
     rows = d.batch * d.num_heads_kv * d.seqlen_q
     G = d.num_heads_q // d.num_heads_kv
-    assert need >= rows * d.topk * G * (2 * 128 + 16)
+    assert full >= rows * d.topk * G * (2 * 128 + 16)
+    assert 0 < need <= full
     assert bwd(d, nbytes=need - 1) == 5
     # the main branch only: index_dim does not matter (the workspace check is reached)
     assert bwd(dims(index_dim=96), nbytes=need - 1) == 5
@@ -155,9 +157,11 @@ def test_bwd_entry_checks():
 
 def test_kl_bwd_entry_checks():
     d = dims()
-    need = msa.msa_workspace_bytes(d, msa.ENTRY_KL_LOSS_BWD)
+    full = msa.msa_workspace_bytes(d, msa.ENTRY_KL_LOSS_BWD)
+    need = msa.msa_workspace_min_bytes(d, msa.ENTRY_KL_LOSS_BWD)
     rows = d.batch * d.num_heads_kv * d.seqlen_q
-    assert need >= rows * d.topk * (2 * d.index_dim + 16)
+    assert full >= rows * d.topk * (2 * d.index_dim + 16)
+    assert 0 < need < full
     assert klb(d, nbytes=need - 1) == 5
     for kw, status in ((dict(index_dim=96), 3), (dict(head_dim=64), 3), (dict(causal=0), 3)):
         assert klb(dims(**kw)) == status, kw
@@ -201,9 +205,12 @@ def test_workspace_checks():
     attn3 = msa.msa_workspace_bytes(d3, msa.ENTRY_SPARSE_ATTN_FWD)
     assert msa.msa_workspace_bytes(d3, msa.ENTRY_FORWARD) == (
         _al(2 * d3.n_blk * 4) + _al(2 * 16 * 4) + attn3)
-    assert fwd(d, nbytes=need - 1) == 5
-    need_a = msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_FWD)
-    assert need_a > 0 and attn(d, nbytes=need_a - 1) == 5
+    min_f = msa.msa_workspace_min_bytes(d, msa.ENTRY_FORWARD)
+    min_a = msa.msa_workspace_min_bytes(d, msa.ENTRY_SPARSE_ATTN_FWD)
+    # The minimum differs from the designed size only in the attention part.
+    assert 0 < min_a < attn_ws and min_f == need - attn_ws + min_a
+    assert fwd(d, nbytes=min_f - 1) == 5
+    assert attn(d, nbytes=min_a - 1) == 5
     assert msa.msa_workspace_bytes(d, msa.ENTRY_INDEX_SCORES) == 0
     assert msa.msa_workspace_bytes(d, msa.ENTRY_BLOCK_TOPK) == 0
     with pytest.raises(msa.MsaError):
@@ -249,7 +256,9 @@ def test_profiled_entry_rejects_bad_events():
     ev = (ctypes.c_void_p * 10)(*([0x20000] * 10))
     args = (ctypes.byref(d), A, A, A, A, A, A, NULL, NULL, A, 1 << 40, None)
     assert L.msa_forward_profiled(*args, None, 10) == 1
-    assert L.msa_forward_profiled(*args, ev, 9) == 2
+    assert L.msa_forward_profiled(*args, ev, 3) == 2
+    assert msa.n_stage_events(1) == 10
+    assert L.msa_forward_profiled(*args, ev, 9) == 2      # one chunk records 10 events
     holes = (ctypes.c_void_p * 10)(*([0x20000] * 9 + [0]))
     assert L.msa_forward_profiled(*args, holes, 10) == 1
     bad = dims(causal=0)
@@ -263,3 +272,29 @@ def test_attn_chunks():
     # partials of 131072 queries x 8 groups x 16 blocks exceed one chunk's budget
     big = dims(seqlen_q=131072, seqlen_k=131072, num_heads_q=64, num_heads_kv=8)
     assert msa.msa_attn_chunks(big) >= 2
+    assert msa.msa_attn_chunks(dims(), msa.ENTRY_INDEX_SCORES, 1 << 30) == 0
+    assert msa.msa_attn_chunks(dims(), msa.ENTRY_KL_LOSS_FWD) == 1
+
+
+@pytest.mark.parametrize("entry", [msa.ENTRY_SPARSE_ATTN_FWD, msa.ENTRY_FORWARD, msa.ENTRY_SPARSE_ATTN_BWD,
+                                   msa.ENTRY_KL_LOSS_BWD])
+def test_chunks_follow_the_workspace(entry):
+    """The query chunk is the largest that fits ws_bytes: the designed size
+    runs one chunk here, the minimum one query per chunk, and sizes between
+    give whole 128-query blocks, more chunks for less memory."""
+    d = dims(seqlen_q=1000, seqlen_k=1300, topk=6)
+    full = msa.msa_workspace_bytes(d, entry)
+    low = msa.msa_workspace_min_bytes(d, entry)
+    assert msa.msa_attn_chunks(d, entry, full) == 1
+    assert msa.msa_attn_chunks(d, entry, low) == 1000
+    assert msa.msa_attn_chunks(d, entry, low - 1) == 0
+    assert msa.msa_attn_chunks(d, entry, full * 4) == 1   # never larger than the designed chunks
+    seen = []
+    for frac in (0.9, 0.7, 0.5, 0.35, 0.2):
+        n = msa.msa_attn_chunks(d, entry, int(low + frac * (full - low)))
+        assert 1 <= n <= 1000
+        # chunks of 128 m queries (m = 1 .. 7) give 8, 4, 3, 2 or 2 chunks;
+        # more than 8 means chunks below one 128-query block
+        assert n in (1, 2, 3, 4, 8) or n > 8, n
+        seen.append(n)
+    assert seen == sorted(seen) and seen[-1] >= 2
