@@ -5,13 +5,13 @@ The device side runs its own forward (selection, output, LSE) and then the
 backward on a seeded upstream gradient dO; the oracle computes its own
 selection and, in fp64, dq of each row and dk, dv summed over the rows.
 
-Tolerance (bf16 gradients against fp64): per tensor, the error beyond the
-output's own bf16 rounding is at most 1e-2 * max(1, max |ref|), and the mean
-of that excess at most 1e-3 * max(1, max |ref|).  The device feeds P and dS
-to the matrix cores in bf16 (relative error 2^-9 per element, averaging out
-over the 128 keys of a block and the rows that meet at a key), accumulates in
-fp32, and keeps each edge's dq as fp16 scaled by the maximum of its 32-dim
-quarter (2^-12 of that maximum).
+Tolerance: the one rule of gpu_util.check_close with s = max |ref| of the
+tensor (the error beyond the output's own bf16 rounding at most 1e-2 s, the
+mean error at most 1e-3 s).  The device feeds P and dS to the matrix cores in
+bf16 (relative error 2^-9 per element, averaging out over the 128 keys of a
+block and the rows that meet at a key), accumulates in fp32, and keeps each
+edge's dq as fp16 scaled by the maximum of its 32-dim quarter (2^-12 of that
+maximum).  Outputs and workspaces are poisoned before every call.
 
 Full-size workloads are checked on rows the oracle computes one by one (dq),
 on the last key blocks (whose rows are all among the last queries, so their
@@ -28,35 +28,32 @@ import torch
 import block_sparse_gqa_scores_amd as msa
 import oracle
 import synth
-from gpu_util import bf16_half_ulp, inputs_for, to_u16
+from gpu_util import check_close, forward_outputs, inputs_for, poisoned, poisoned_workspace, to_u16
 
 pytestmark = pytest.mark.gpu
-
-MAX_REL = 1e-2
-MEAN_REL = 1e-3
 
 
 def W(name, B, Sq, Sk, Hq, Hkv, Didx=128, topk=16, **kw):
     return synth.Workload(name, B, Sq, Sk, Hq, Hkv, index_dim=Didx, topk=topk, **kw)
 
 
-def device_bwd(w, t):
+def device_bwd(w, t, ws_bytes=None):
+    """Forward, then the backward on poisoned outputs and workspace; ws_bytes
+    sizes the backward's workspace (None: the designed size)."""
     out, lse, idx = msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk,
-                                    return_lse=True, return_idx=True)
-    dq, dk, dv = msa.msa_sparse_attn_bwd(t["q"], t["k"], t["v"], idx, out, lse, t["dout"])
+                                    **forward_outputs(w))
+    d = msa.dims_of(t["q"], t["k"], topk=w.topk)
+    nbytes = msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_BWD) if ws_bytes is None else ws_bytes
+    dq, dk, dv = msa.msa_sparse_attn_bwd(
+        t["q"], t["k"], t["v"], idx, out, lse, t["dout"], workspace=poisoned_workspace(nbytes),
+        dq=poisoned(t["q"].shape, torch.bfloat16), dk=poisoned(t["k"].shape, torch.bfloat16),
+        dv=poisoned(t["v"].shape, torch.bfloat16))
     torch.cuda.synchronize()
     return idx, dq, dk, dv
 
 
 def check(name, got, ref):
-    got = got.astype(np.float64)
-    err = np.abs(got - ref)
-    excess = np.maximum(err - bf16_half_ulp(ref), 0.0)
-    big = max(1.0, float(np.abs(ref).max()))
-    print(f"{name}: max|ref| {np.abs(ref).max():.4g}, max err {err.max():.3e} (beyond rounding "
-          f"{excess.max():.3e}), mean err {err.mean():.3e}", flush=True)
-    assert excess.max() <= MAX_REL * big, f"{name}: max error {excess.max():.3e} > {MAX_REL * big:.3e}"
-    assert excess.mean() <= MEAN_REL * big, f"{name}: mean error {excess.mean():.3e} > {MEAN_REL * big:.3e}"
+    return check_close(name, got, ref, float(np.abs(ref).max()))
 
 
 def compare_all(w, t, idx, dq, dk, dv, rows=None):

@@ -21,7 +21,8 @@ import torch
 import block_sparse_gqa_scores_amd as msa
 import oracle
 import synth
-from gpu_util import host_inputs, inputs_for, to_u16
+from gpu_util import (forward_outputs, host_inputs, inputs_for, poisoned, poisoned_workspace, spread_index_queries,
+                      student_max_weight, to_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,9 +35,14 @@ def W(name, B, Sq, Sk, Hq, Hkv, Didx=128, topk=16, **kw):
 
 
 def device_kl(w, t):
+    """Forward, then the loss forward on poisoned outputs and workspace."""
     out, lse, idx = msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk,
-                                    return_lse=True, return_idx=True)
-    loss, rows = msa.msa_kl_loss_fwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, return_rows=True)
+                                    **forward_outputs(w))
+    d = msa.dims_of(t["q"], t["k"], t["q_idx"], t["k_idx"], topk=w.topk)
+    loss, rows = msa.msa_kl_loss_fwd(
+        t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, loss=poisoned((), torch.float32),
+        rows=poisoned((w.batch, w.heads_kv, w.seqlen_q), torch.float32),
+        workspace=poisoned_workspace(msa.msa_workspace_bytes(d, msa.ENTRY_KL_LOSS_FWD)))
     torch.cuda.synchronize()
     return idx, lse, loss, rows
 
@@ -100,6 +106,34 @@ def test_kl_parity(w):
         exp_loss = oracle.kl_rows(oracle.Problem.of(w), h["q"], h["k"], h["q_idx"], h["k_idx"],
                                   idx.cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]], rows).mean()
         assert abs(loss.item() - exp_loss) <= KL_ABS + KL_REL * abs(exp_loss)
+
+
+SPREAD = [
+    W("kl_spread_g2", 1, 900, 2600, 8, 4, topk=8),            # G = 2
+    W("kl_spread_g8", 1, 700, 3000, 64, 8, topk=12),          # G = 8 (16x16x32 index tiles)
+    W("kl_spread_g8_d64", 2, 300, 2200, 16, 2, Didx=64),      # G = 8, D_idx 64, whole prefix selected
+]
+
+
+@pytest.mark.parametrize("w", SPREAD, ids=lambda w: w.name)
+def test_kl_parity_spread_student(w):
+    """A student that is not nearly one-hot (index rows with two +-1 channels,
+    spread_index_queries): the non-dominant mass of the index softmax (the
+    L, S and C sums of every block, not only the top token) now carries the
+    row terms, and every row is compared with the oracle."""
+    t = spread_index_queries(w, inputs_for(w))
+    idx, lse, loss, kl_dev = device_kl(w, t)
+    h = host_inputs(t)
+    rows = oracle.Problem.of(w).all_rows()
+    sel = idx.cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]]
+    pick = rows[:: max(1, len(rows) // 200)]
+    mw = student_max_weight(w, h, idx.cpu().numpy()[pick[:, 0], pick[:, 2], pick[:, 1]], pick)
+    late = pick[:, 1] + w.seqlen_k - w.seqlen_q >= 1024   # rows that see at least 1024 tokens
+    print(f"{w.name}: student max weight median {np.median(mw[late]):.4f}, max {mw[late].max():.4f}", flush=True)
+    assert np.median(mw[late]) < 0.05
+    exp = check_rows(w, h, idx.cpu().numpy(), kl_dev.cpu().numpy(), rows, w.name)
+    assert abs(loss.item() - exp.mean()) <= KL_ABS + KL_REL * abs(exp.mean())
+    del sel
 
 
 def test_kl_caller_selection_unsorted_with_holes():

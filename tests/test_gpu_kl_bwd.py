@@ -7,12 +7,13 @@ The device side runs its own forward (selection and LSE), the loss forward
 backward with grad_loss = 1; the oracle computes its own selection and, in
 fp64, the unscaled gradients, scaled here by 1 / (B S_q H_kv).
 
-Tolerance (bf16 gradients against fp64): per tensor, the error beyond the
-output's own bf16 rounding is at most 1e-2 * max |ref|, and the mean of that
-excess at most 1e-3 * max |ref|.  The device rounds g to bf16 before the matrix products
-(relative 2^-9 per term), accumulates in fp32 and keeps each edge's dq_idx as
-fp16 scaled by its 32-dim quarter's maximum (2^-12).  The rows' index-score
-log-sum-exps must agree to 1e-6 relative (fp32 against fp64).
+Tolerance: the one rule of gpu_util.check_close with s = max |ref| of the
+tensor (the error beyond the output's own bf16 rounding at most 1e-2 s, the
+mean error at most 1e-3 s).  The device rounds g to bf16 before the matrix
+products (relative 2^-9 per term), accumulates in fp32 and keeps each edge's
+dq_idx as fp16 scaled by its 32-dim quarter's maximum (2^-12).  The rows'
+index-score log-sum-exps must agree to 1e-6 relative (fp32 against fp64).
+Outputs and workspaces are poisoned before every call.
 """
 import numpy as np
 import pytest
@@ -21,36 +22,37 @@ import torch
 import block_sparse_gqa_scores_amd as msa
 import oracle
 import synth
-from gpu_util import bf16_half_ulp, inputs_for, to_u16
+from gpu_util import (check_close, forward_outputs, host_inputs, inputs_for, poisoned, poisoned_workspace,
+                      spread_index_queries, student_max_weight, to_u16)
 
 pytestmark = pytest.mark.gpu
-
-MAX_REL = 1e-2
-MEAN_REL = 1e-3
 
 
 def W(name, B, Sq, Sk, Hq, Hkv, Didx=128, topk=16, **kw):
     return synth.Workload(name, B, Sq, Sk, Hq, Hkv, index_dim=Didx, topk=topk, **kw)
 
 
-def device_kl_bwd(w, t, grad=1.0):
+def device_kl_bwd(w, t, grad=1.0, ws_bytes=None):
+    """Forward, loss forward and loss backward on poisoned outputs and
+    workspaces; ws_bytes sizes the backward's workspace (None: designed)."""
     out, lse, idx = msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk,
-                                    return_lse=True, return_idx=True)
-    loss, lse_idx = msa.msa_kl_loss_fwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, return_lse_idx=True)
-    dqi, dki = msa.msa_kl_loss_bwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, lse_idx, grad)
+                                    **forward_outputs(w))
+    d = msa.dims_of(t["q"], t["k"], t["q_idx"], t["k_idx"], topk=w.topk)
+    loss, lse_idx = msa.msa_kl_loss_fwd(
+        t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse,
+        lse_idx=poisoned((w.batch, w.heads_kv, w.seqlen_q), torch.float32),
+        workspace=poisoned_workspace(msa.msa_workspace_bytes(d, msa.ENTRY_KL_LOSS_FWD)))
+    nbytes = msa.msa_workspace_bytes(d, msa.ENTRY_KL_LOSS_BWD) if ws_bytes is None else ws_bytes
+    dqi, dki = msa.msa_kl_loss_bwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, lse_idx, grad,
+                                   dq_idx=poisoned(t["q_idx"].shape, torch.bfloat16),
+                                   dk_idx=poisoned(t["k_idx"].shape, torch.bfloat16),
+                                   workspace=poisoned_workspace(nbytes))
     torch.cuda.synchronize()
     return idx, lse_idx, dqi, dki
 
 
 def check(name, got, ref):
-    got = got.astype(np.float64)
-    err = np.abs(got - ref)
-    excess = np.maximum(err - bf16_half_ulp(ref), 0.0)
-    big = float(np.abs(ref).max())
-    print(f"{name}: max|ref| {big:.4g}, max err {err.max():.3e} (beyond rounding {excess.max():.3e}), "
-          f"mean err {err.mean():.3e} (beyond rounding {excess.mean():.3e})", flush=True)
-    assert excess.max() <= MAX_REL * big, f"{name}: max error {excess.max():.3e} > {MAX_REL * big:.3e}"
-    assert excess.mean() <= MEAN_REL * big, f"{name}: mean error {excess.mean():.3e} > {MEAN_REL * big:.3e}"
+    return check_close(name, got, ref, float(np.abs(ref).max()))
 
 
 def oracle_side(w, h, rows, want_dk=True, threads=0):
@@ -86,6 +88,36 @@ def test_kl_bwd_parity(w):
     sel, rdqi, rdki, lse_z = oracle_side(w, h, rows)
     got_sel = idx.cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]]
     assert (got_sel == sel).all(), "selection differs"
+    li = lse_idx.cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]].astype(np.float64)
+    assert np.abs(li - lse_z).max() <= 1e-6 * max(1.0, np.abs(lse_z).max()), np.abs(li - lse_z).max()
+    dqin = dqi.float().cpu().numpy()
+    check(f"{w.name} dq_idx", dqin[rows[:, 0], rows[:, 1], rows[:, 2]], rdqi)
+    check(f"{w.name} dk_idx", dki.float().cpu().numpy(), rdki)
+
+
+SPREAD = [
+    W("klb_spread_g2", 1, 900, 2600, 8, 4, topk=8),           # G = 2
+    W("klb_spread_g8", 1, 700, 3000, 64, 8, topk=12),         # G = 8
+    W("klb_spread_g8_d64", 2, 300, 2200, 16, 2, Didx=64),     # G = 8, D_idx 64
+]
+
+
+@pytest.mark.parametrize("w", SPREAD, ids=lambda w: w.name)
+def test_kl_bwd_parity_spread_student(w):
+    """The gradient g = c (P_idx - P) with a spread student (two +-1 channels
+    per index row): P_idx of every token, not only the top one, enters dq_idx
+    and dk_idx; compared with the oracle on every row and key."""
+    t = spread_index_queries(w, inputs_for(w))
+    idx, lse_idx, dqi, dki = device_kl_bwd(w, t)
+    h = host_inputs(t)
+    rows = oracle.Problem.of(w).all_rows()
+    sel, rdqi, rdki, lse_z = oracle_side(w, h, rows)
+    assert (idx.cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]] == sel).all(), "selection differs"
+    pick = rows[:: max(1, len(rows) // 200)]
+    mw = student_max_weight(w, h, idx.cpu().numpy()[pick[:, 0], pick[:, 2], pick[:, 1]], pick)
+    late = pick[:, 1] + w.seqlen_k - w.seqlen_q >= 1024
+    print(f"{w.name}: student max weight median {np.median(mw[late]):.4f}", flush=True)
+    assert np.median(mw[late]) < 0.05
     li = lse_idx.cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]].astype(np.float64)
     assert np.abs(li - lse_z).max() <= 1e-6 * max(1.0, np.abs(lse_z).max()), np.abs(li - lse_z).max()
     dqin = dqi.float().cpu().numpy()
