@@ -6,13 +6,17 @@ are seeded synthetic tensors drawn on the device and resident in HBM before
 the timed region starts.
 
 Prints ONE JSON line.  ``value`` is tokens/s (queries of the batch per second)
-on the 32K prefill workload (B=1, S=32768, 64/8 heads, head dim 128, index dim
-128, block 128, k=16).  Alongside: algorithmic TFLOP/s and the fraction of the
-bf16 MFMA peak, per-entry-point times, the roofline of the dominant step, the
-CPU oracle timed on a bounded row sample, the decode workload (64 sequences
-against a 256K-token cache) as HBM GB/s and fraction of peak, the forward
-value of the index branch's alignment loss on the same selection, and the
-backward (main branch and alignment loss) beside it.
+on the largest single-GPU prefill workload: 16384 new queries at positions
+1032192 .. 1048575 of a 1,048,576-token causal prefix (B=1, 64/8 heads, head
+dim 128, index dim 128, block 128, k=16).  Alongside: mean, median and
+minimum step times, algorithmic TFLOP/s and the fraction of the bf16 MFMA
+peak, every stage's time and rate (per-chunk launches summed), the attention
+as one step, the roofline of the dominant kernel, the CPU oracle timed on a
+bounded row sample of the same workload, the 32K and 128K (per-block gain)
+prefill workloads, the decode workload (64 sequences against a 256K-token
+cache) as HBM GB/s and fraction of peak, and on the 32K workload the forward
+value of the index branch's alignment loss, the backward (main branch and
+alignment loss) and the block-mask form of the selection.
 """
 from __future__ import annotations
 
@@ -79,8 +83,11 @@ def time_loop(fn, steps, stream):
 
 
 def run_workload(w, steps, warmup):
-    """Warm up, time `steps` forward steps, then time each internal stage over
-    another `steps` steps with events recorded on the launch stream."""
+    """Warm up, time `steps` forward steps (an event at every step boundary,
+    so the mean, median and minimum come from one timed run), then time each
+    internal stage over another `steps` steps through msa_forward_profiled:
+    the index scores and the Top-k once per step, the three attention stages
+    once per query chunk."""
     import torch
 
     import block_sparse_gqa_scores_amd as msa
@@ -89,7 +96,9 @@ def run_workload(w, steps, warmup):
     dev = torch.device("cuda", 0)
     t = synth.device_tensors(w, dev)
     d = msa.dims_of(t["q"], t["k"], t["q_idx"], t["k_idx"], topk=w.topk)
-    ws = torch.empty(msa.msa_workspace_bytes(d, msa.ENTRY_FORWARD), dtype=torch.uint8, device=dev)
+    ws_bytes = msa.msa_workspace_bytes(d, msa.ENTRY_FORWARD)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    chunks = msa.msa_attn_chunks(d, msa.ENTRY_FORWARD, ws_bytes)
     out = torch.empty_like(t["q"])
     stream = torch.cuda.current_stream(dev)
 
@@ -99,15 +108,23 @@ def run_workload(w, steps, warmup):
 
     for _ in range(warmup):
         step()
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = time_loop(step, steps, stream)
+    bounds[0].record(stream)
+    for k in range(steps):
+        step()
+        bounds[k + 1].record(stream)
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    per_step = [bounds[k].elapsed_time(bounds[k + 1]) for k in range(steps)]
+    timing = {"mean": bounds[0].elapsed_time(bounds[-1]) / steps, "median": float(np.median(per_step)),
+              "min": float(min(per_step)), "wall_s": wall}
 
-    n_st = len(msa.STAGES)
+    n_ev = msa.n_stage_events(chunks)
     evs = []
     for _ in range(steps):
-        pair = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_st)]
+        pair = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
         for e in pair:
             e.record(stream)  # creates the underlying event
         evs.append(pair)
@@ -115,9 +132,16 @@ def run_workload(w, steps, warmup):
     for pair in evs:
         step([e.cuda_event for e in pair])
     torch.cuda.synchronize()
-    stage_ms = {name: sum(p[2 * s].elapsed_time(p[2 * s + 1]) for p in evs) / steps
-                for s, name in enumerate(msa.STAGES)}
-    return t, ms, wall, stage_ms, msa.msa_attn_chunks(d)
+
+    def span(p, x):
+        return p[x].elapsed_time(p[x + 1])
+
+    stage_ms = {"index_scores": sum(span(p, 0) for p in evs) / steps,
+                "block_topk": sum(span(p, 2) for p in evs) / steps}
+    for m, name in enumerate(msa.ATTN_STAGES):
+        # per step: the sum over the chunks' launches of this stage
+        stage_ms[name] = sum(span(p, 4 + 6 * c + 2 * m) for p in evs for c in range(chunks)) / steps
+    return t, timing, stage_ms, chunks
 
 
 def fused_selection(w):
@@ -228,51 +252,100 @@ def backward_rates(w, t, steps):
     return res
 
 
-def stage_work(w, chunks):
-    """Algorithmic work of each stage per launch: (bound, amount, unit).  With
-    the fused selection the Top-k runs inside the index stage and its own
-    stage is empty (bound "fused")."""
+def stage_work(w):
+    """Algorithmic work of each forward stage per step: (bound, amount, unit).
+    With the fused selection the Top-k runs inside the index stage and its own
+    stage is empty (bound "fused").  The attention stages' work is the whole
+    step's, summed over the query chunks they run in."""
     rows = w.batch * w.heads_kv * w.seqlen_q
     edges = w.batch * w.heads_kv * float(np.minimum(positions(w) // w.block_size + 1, w.topk).sum())
     G = w.group
     index = ("mfma", index_flops(w), "FLOP")
     if w.seqlen_q * w.heads_kv <= 32:  # decode: the index-key cache stream bounds the scan
         index = ("hbm", w.batch * (w.seqlen_k * w.index_dim * 2.0 + rows / w.batch * (w.index_dim * 2.0 + w.n_blk * 4.0)), "B")
+    partial = ("mfma", attn_flops(w), "FLOP")
+    if w.seqlen_q == 1:  # decode: one query per block, the selected K/V bytes bound it
+        partial = ("hbm", w.batch * w.heads_kv * float(visible_tokens(w).sum()) * w.head_dim * 4.0
+                   + w.batch * w.heads_q * w.head_dim * 2.0, "B")
     return {
         "index_scores": index,
         "block_topk": ("fused", 0.0, "B") if fused_selection(w) else ("hbm", rows * (w.n_blk + w.topk) * 4.0, "B"),
-        "attn_build": ("hbm", (rows * w.topk * 4.0 * 2 + edges * 4.0) / chunks, "B"),
-        "attn_partial": ("mfma", attn_flops(w) / chunks, "FLOP"),
-        "attn_merge": ("hbm", (edges * G * (2 * w.head_dim + 8) + rows * G * w.head_dim * 2.0) / chunks, "B"),
+        "attn_build": ("hbm", rows * w.topk * 4.0 * 2 + edges * 4.0, "B"),
+        "attn_partial": partial,
+        "attn_merge": ("hbm", edges * G * (2 * w.head_dim + 8) + rows * G * w.head_dim * 2.0, "B"),
     }
 
 
+LAUNCHES = {"index_scores": lambda chunks: 1, "block_topk": lambda chunks: 1,
+            "attn_build": lambda chunks: chunks, "attn_partial": lambda chunks: chunks,
+            "attn_merge": lambda chunks: chunks}
+
+
+def rate(bound, amount, ms):
+    """Achieved rate of `amount` of work in `ms`: (value, unit, peak)."""
+    if bound == "mfma":
+        return amount / (ms * 1e-3) / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS
+    return amount / (ms * 1e-3) / 1e9, "GB/s", PEAK_HBM_GBS
+
+
+def stage_rates(w, stage_ms, chunks):
+    """Per stage: ms per step, launches per step, and the achieved rate of its
+    work over its own time (a one-launch stage over that launch, a per-chunk
+    stage over the sum of its chunks' launches)."""
+    out = {}
+    for name, (bound, amount, _) in stage_work(w).items():
+        st = {"ms_per_step": stage_ms[name], "launches_per_step": LAUNCHES[name](chunks), "bound": bound}
+        if bound != "fused" and stage_ms[name] > 0:
+            r, unit, peak = rate(bound, amount, stage_ms[name])
+            st[unit] = r
+            st["frac"] = r / peak
+        out[name] = st
+    return out
+
+
+def attention_step(w, stage_ms, chunks):
+    """The block-sparse attention as one step (bucket build + partial +
+    merge, all chunks): algorithmic FLOPs over its whole time."""
+    ms = stage_ms["attn_build"] + stage_ms["attn_partial"] + stage_ms["attn_merge"]
+    tf = attn_flops(w) / (ms * 1e-3) / 1e12
+    return {"ms_per_step": ms, "chunks": chunks, "algorithmic_flops": attn_flops(w), "TFLOP/s": tf,
+            "mfma_frac": tf / PEAK_BF16_TFLOPS,
+            "what": "bucket build + attention partials + merge, summed over the query chunks"}
+
+
 def roofline(w, stage_ms, chunks):
-    work = stage_work(w, chunks)
+    """The dominant kernel's algorithmic work per launch over its average
+    launch time (HIP events on the launch stream)."""
+    work = stage_work(w)
     dom = max(stage_ms, key=stage_ms.get)
     bound, amount, _ = work[dom]
-    per_launch_ms = stage_ms[dom] / chunks
-    if bound == "mfma":
-        ach = amount / (per_launch_ms * 1e-3) / 1e12
-        r = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        ach = amount / (per_launch_ms * 1e-3) / 1e9
-        r = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    r.update(frac=r["achieved"] / r["peak"], traffic=measured_traffic(w, dom),
-             kernel=KERNEL_OF_STAGE[dom], launches_per_step=chunks, avg_launch_ms=per_launch_ms)
-    return r
+    n = LAUNCHES[dom](chunks)
+    per_launch_ms = stage_ms[dom] / n
+    ach, unit, peak = rate(bound, amount / n, per_launch_ms)
+    return {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
+            "traffic": measured_traffic(w, dom), "kernel": kernel_of_stage(w, dom), "launches_per_step": n,
+            "avg_launch_ms": per_launch_ms, "work_per_launch": amount / n}
 
 
-TRAFFIC_FILES = {("prefill_32k", "attn_partial"): ("attn_partial_prefill_32k_traffic.txt",
-                                                   ("sparse_attn.hip", "device_common.h"))}
+# Committed counter summaries: HBM bytes per launch of a kernel on a workload,
+# valid while the sha256 of the listed sources matches the measured code.
+TRAFFIC_FILES = {
+    ("prefill_32k", "attn_partial"): ("attn_partial_prefill_32k_traffic.txt", ("sparse_attn.hip", "device_common.h")),
+    ("chunk_16k_of_1m", "index_scores"): ("index_scan_chunk_16k_of_1m_traffic.txt", ("index_scan.hip", "device_common.h")),
+    ("decode_64x256k", "index_scores"): ("index_scan_decode_64x256k_traffic.txt", ("index_scan.hip", "device_common.h")),
+}
+
+
+def source_digest(files):
+    import hashlib
+    csrc = os.path.join(ROOT, "block_sparse_gqa_scores_amd", "csrc")
+    return hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in files)).hexdigest()
 
 
 def measured_traffic(w, stage):
     """HBM bytes per launch from the committed counter summary of this kernel
     (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel calibration), or
     None when there is none or the kernel's source changed since."""
-    import hashlib
-
     key = TRAFFIC_FILES.get((w.name, stage))
     if key is None:
         return None
@@ -284,20 +357,32 @@ def measured_traffic(w, stage):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    csrc = os.path.join(ROOT, "block_sparse_gqa_scores_amd", "csrc")
-    digest = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in key[1])).hexdigest()
-    if digest != fields.get("source_sha256"):
+    if source_digest(key[1]) != fields.get("source_sha256"):
         return None
     return float(fields["hbm_bytes_per_launch"])
 
 
-KERNEL_OF_STAGE = {
-    "index_scores": "index_scan_prefill (selection mode with k <= 16; index_scan_decode when S_q * H_kv <= 32)",
-    "block_topk": "block_topk_kernel",
-    "attn_build": "zero/bucket_count/scan/bucket_fill kernels",
-    "attn_partial": "attn_partial_kernel<G>",
-    "attn_merge": "merge_kernel<G>",
-}
+def kernel_of_stage(w, stage):
+    if stage == "index_scores":
+        if w.seqlen_q * w.heads_kv <= 32:
+            return f"index_scan_decode<{w.index_dim}>"
+        return f"index_scan_prefill<{w.index_dim}, 2, 8, {'true' if fused_selection(w) else 'false'}>"
+    return {"block_topk": "block_topk_kernel", "attn_build": "zero/bucket_count/scan/bucket_fill kernels",
+            "attn_partial": f"attn_decode_kernel<{w.group}>" if w.seqlen_q == 1 else f"attn_partial_kernel<{w.group}>",
+            "attn_merge": f"merge_kernel<{w.group}>"}[stage]
+
+
+def forward_summary(w, timing, stage_ms, chunks):
+    """ms per step (mean, median, min), tokens/s, algorithmic TFLOP/s of the
+    whole forward, the stages and the attention step of one workload."""
+    fi, fa = index_flops(w), attn_flops(w)
+    ms = timing["mean"]
+    return {"workload": w.name, "ms_per_step": ms, "ms_per_step_median": timing["median"],
+            "ms_per_step_min": timing["min"], "tokens/s": w.batch * w.seqlen_q / (ms * 1e-3),
+            "TFLOP/s": (fi + fa) / (ms * 1e-3) / 1e12, "mfma_frac": (fi + fa) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "algorithmic_flops": {"index": fi, "attention": fa}, "attn_chunks": chunks,
+            "stages": stage_rates(w, stage_ms, chunks), "attention": attention_step(w, stage_ms, chunks),
+            "roofline": roofline(w, stage_ms, chunks)}
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -315,6 +400,17 @@ def sample_rows(w, n_random, seed=1):
     qs.update(int(x) for x in rng.integers(0, w.seqlen_q, size=n_random))
     rows = [(int(rng.integers(0, w.batch)), q, g) for q in sorted(qs) for g in range(w.heads_kv)]
     return np.array(rows, dtype=np.int64)
+
+
+def cpu_model():
+    """The host CPU's model name (the "model name" line of /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(w, t, budget_s):
@@ -336,22 +432,38 @@ def cpu_baseline(w, t, budget_s):
     dt = time.perf_counter() - t0
     rows_per_s = len(rows) / dt
     return {"value": rows_per_s / w.heads_kv, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{len(rows)} (query, group) rows of {w.name} (stratified, seed 1) in {dt:.1f} s; "
                       f"{rows_per_s:.1f} rows/s; a token is one query with all {w.heads_kv} groups"}
+
+
+def release():
+    import gc
+
+    import torch
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 # ------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill_32k")
+    ap.add_argument("--workload", default="chunk_16k_of_1m",
+                    help="headline workload (default: the largest single-GPU prefill, 16K queries on a 1M prefix)")
+    ap.add_argument("--secondary", default="prefill_32k,prefill_128k_gain",
+                    help="comma-separated forward workloads reported beside the headline ('' for none)")
+    ap.add_argument("--legs-workload", default="prefill_32k",
+                    help="workload of the alignment-loss, backward and selection-mask legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-kl", action="store_true", help="skip the alignment-loss measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-mask", action="store_true", help="skip the selection-mask measurement")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run one plain device copy of this many bytes first (counter calibration)")
     ap.add_argument("--no-copy-rate", action="store_true",
@@ -370,56 +482,66 @@ def main():
     if args.copy_probe:
         synth.copy_probe(args.copy_probe)
     print(f"[bench] workload {w.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
-    t, ms, wall, stage_ms, chunks = run_workload(w, args.steps, args.warmup)
-    fi, fa = index_flops(w), attn_flops(w)
-    tokens = w.batch * w.seqlen_q
-    tflops = (fi + fa) / (ms * 1e-3) / 1e12
-    roof = roofline(w, stage_ms, chunks)
-    stages = {}
-    for name, (bound, amount, unit) in stage_work(w, chunks).items():
-        stages[name] = {"ms_per_step": stage_ms[name], "bound": bound}
-        if bound != "fused":
-            rate = amount / (stage_ms[name] / chunks * 1e-3)
-            stages[name]["TFLOP/s" if unit == "FLOP" else "GB/s"] = rate / (1e12 if unit == "FLOP" else 1e9)
-    print(f"[bench] {ms:.3f} ms/step; stages {json.dumps(stage_ms)}", file=sys.stderr, flush=True)
+    t, timing, stage_ms, chunks = run_workload(w, args.steps, args.warmup)
+    head = forward_summary(w, timing, stage_ms, chunks)
+    ms = timing["mean"]
+    print(f"[bench] {ms:.3f} ms/step (median {timing['median']:.3f}, min {timing['min']:.3f}); "
+          f"stages {json.dumps(stage_ms)}", file=sys.stderr, flush=True)
 
     res = {
-        "metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "metric": METRIC, "value": head["tokens/s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "ms_per_step_median": timing["median"], "ms_per_step_min": timing["min"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen_q": w.seqlen_q, "seqlen_k": w.seqlen_k,
                    "heads_q": w.heads_q, "heads_kv": w.heads_kv, "head_dim": w.head_dim,
                    "index_dim": w.index_dim, "block_size": w.block_size, "topk": w.topk,
                    "parallelism": "single GPU"},
-        "tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
-        "algorithmic_flops": {"index": fi, "attention": fa},
-        "stages": stages, "attn_chunks": chunks, "roofline": roof, "wall_s_timed": wall,
+        "tflops": head["TFLOP/s"], "mfma_frac": head["mfma_frac"],
+        "algorithmic_flops": head["algorithmic_flops"], "stages": head["stages"], "attn_chunks": chunks,
+        "attention": head["attention"], "roofline": head["roofline"], "wall_s_timed": timing["wall_s"],
     }
-    res["selection_mask"] = selection_mask_rates(w, t, args.steps)
-    if not args.no_kl:
-        print("[bench] alignment loss ...", file=sys.stderr, flush=True)
-        res["alignment_loss"] = alignment_loss_rate(w, t, args.steps)
-    if not args.no_backward:
-        print("[bench] backward ...", file=sys.stderr, flush=True)
-        res["backward"] = backward_rates(w, t, max(2, args.steps // 2))
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
     del t
-    torch.cuda.empty_cache()
+    release()
+    res["workloads"] = {}
+    for name in [x for x in args.secondary.split(",") if x and x != w.name]:
+        ws_ = synth.WORKLOADS[name]
+        print(f"[bench] secondary workload {name}", file=sys.stderr, flush=True)
+        ts, tim_s, st_s, ch_s = run_workload(ws_, args.steps, args.warmup)
+        res["workloads"][name] = forward_summary(ws_, tim_s, st_s, ch_s)
+        del ts
+        release()
+    legs = synth.WORKLOADS[args.legs_workload]
+    if not (args.no_mask and args.no_kl and args.no_backward):
+        tl = synth.device_tensors(legs, torch.device("cuda", 0))
+        if not args.no_mask:
+            res["selection_mask"] = selection_mask_rates(legs, tl, args.steps)
+        if not args.no_kl:
+            print("[bench] alignment loss ...", file=sys.stderr, flush=True)
+            res["alignment_loss"] = alignment_loss_rate(legs, tl, args.steps)
+        if not args.no_backward:
+            print("[bench] backward ...", file=sys.stderr, flush=True)
+            res["backward"] = backward_rates(legs, tl, max(2, args.steps // 2))
+        del tl
+        release()
     if not args.no_decode:
         wd = synth.WORKLOADS["decode_64x256k"]
         print(f"[bench] decode workload {wd.name}", file=sys.stderr, flush=True)
-        td, msd, _, stage_d, chunks_d = run_workload(wd, args.steps, args.warmup)
+        td, tim_d, stage_d, chunks_d = run_workload(wd, args.steps, args.warmup)
         nbytes = decode_bytes(wd)
+        msd = tim_d["mean"]
         gbs = nbytes / (msd * 1e-3) / 1e9
-        res["decode"] = {"workload": wd.name, "ms_per_step": msd, "algorithmic_bytes": nbytes,
+        res["decode"] = {"workload": wd.name, "ms_per_step": msd, "ms_per_step_median": tim_d["median"],
+                         "ms_per_step_min": tim_d["min"], "algorithmic_bytes": nbytes,
                          "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
                          "tokens/s": wd.batch * wd.seqlen_q / (msd * 1e-3),
-                         "stages_ms": stage_d, "roofline": roofline(wd, stage_d, chunks_d)}
+                         "stages": stage_rates(wd, stage_d, chunks_d), "roofline": roofline(wd, stage_d, chunks_d)}
         del td
+        release()
     if not args.no_copy_rate:
-        torch.cuda.empty_cache()
         # Reference rate of the same HBM: a plain streaming copy (reads and
         # writes 1 GiB each), for reading the GB/s figures above.
         res["copy_rate"] = {"GB/s": synth.copy_probe(1 << 30, reps=11), "bytes": 1 << 30,

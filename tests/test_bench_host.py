@@ -69,3 +69,39 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_multi_chunk_stage_accounting():
+    """With the attention in 3 query chunks, each stage is rated over its own
+    time: the one-launch index scan over that launch, the per-chunk stages
+    over the sum of their launches; no rate exceeds its peak for plausible
+    times, and the roofline's per-launch work times launches is the step's."""
+    w = synth.WORKLOADS["prefill_128k_gain"]
+    stage_ms = {"index_scores": 11.8, "block_topk": 0.004, "attn_build": 0.3, "attn_partial": 12.0,
+                "attn_merge": 6.5}
+    chunks = 3
+    st = bench.stage_rates(w, stage_ms, chunks)
+    assert st["index_scores"]["launches_per_step"] == 1 and st["attn_partial"]["launches_per_step"] == 3
+    assert st["index_scores"]["TFLOP/s"] == pytest.approx(bench.index_flops(w) / 11.8e-3 / 1e12)
+    assert st["attn_partial"]["TFLOP/s"] == pytest.approx(bench.attn_flops(w) / 12.0e-3 / 1e12)
+    for name, x in st.items():
+        if "frac" in x:
+            assert 0 < x["frac"] < 1, name
+    att = bench.attention_step(w, stage_ms, chunks)
+    assert att["ms_per_step"] == pytest.approx(0.3 + 12.0 + 6.5)
+    assert att["TFLOP/s"] == pytest.approx(bench.attn_flops(w) / 18.8e-3 / 1e12)
+    r = bench.roofline(w, stage_ms, chunks)
+    assert r["kernel"].startswith("attn_partial_kernel") and r["launches_per_step"] == 3
+    assert r["avg_launch_ms"] == pytest.approx(4.0)
+    assert r["work_per_launch"] * 3 == pytest.approx(bench.attn_flops(w))
+    assert r["frac"] < 1
+    # the fused selection has no Top-k stage of its own
+    assert st["block_topk"]["bound"] == "fused" and "frac" not in st["block_topk"]
+
+
+def test_decode_stages_are_rated_in_bytes():
+    w = synth.WORKLOADS["decode_64x256k"]
+    st = bench.stage_rates(w, {"index_scores": 0.64, "block_topk": 0.005, "attn_build": 0.0,
+                               "attn_partial": 0.11, "attn_merge": 0.01}, 1)
+    assert st["index_scores"]["bound"] == "hbm" and st["attn_partial"]["bound"] == "hbm"
+    assert 0 < st["index_scores"]["frac"] < 1 and 0 < st["attn_partial"]["frac"] < 1
