@@ -329,12 +329,10 @@ def mask_blocks(mask, cap: int):
     return out.reshape(mask.shape[:-1] + (cap,))
 
 
-def mask_blocks_by_traversal(mask_row, cap: int):
-    """One row, written as the section's loop: for each word, popcount, then
-    nth_set_bit for every rank.  Pure Python, for small cases."""
-    out = []
-    for w, word in enumerate(np.asarray(mask_row, dtype=np.uint32).tolist()):
-        for rank in range(popcount(word)):
-            out.append(32 * w + nth_set_bit(word, rank))
-    out = out[:cap]
+def mask_blocks_by_scan(mask_row, n_blk: int, cap: int):
+    """One row from the bit-set definition alone: block j is in the row when
+    bit j mod 32 of word floor(j / 32) is set; scanning j = 0 .. n_blk-1 in
+    order keeps the first cap of them.  Pure Python, for small cases."""
+    words = [int(x) for x in np.asarray(mask_row, dtype=np.uint32).tolist()]
+    out = [j for j in range(n_blk) if (words[j // 32] >> (j % 32)) & 1][:cap]
     return out + [-1] * (cap - len(out))

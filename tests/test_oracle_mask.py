@@ -14,7 +14,7 @@ def test_worked_example_word_is_73():
     assert m.shape == (1, 1) and int(m[0, 0]) == 0b01001001 == 73
     assert oracle.popcount(73) == 3
     assert [oracle.nth_set_bit(73, r) for r in range(3)] == [0, 3, 6]
-    assert oracle.mask_blocks_by_traversal(m[0], 4) == [0, 3, 6, -1]
+    assert oracle.mask_blocks_by_scan(m[0], 8, 4) == [0, 3, 6, -1]
     assert oracle.mask_blocks(m, 4).tolist() == [[0, 3, 6, -1]]
 
 
@@ -41,8 +41,8 @@ def test_unused_bits_stay_zero_and_out_of_range_entries_are_ignored():
 
 
 def test_traversal_equals_definition_on_random_masks():
-    """The vectorised traversal equals the section's popcount / nth-set-bit
-    loop, and both equal the sorted list of set positions."""
+    """The vectorised traversal equals a scan of every block position against
+    its word and bit, and both equal the sorted list of set positions."""
     rng = np.random.default_rng(3)
     for n_blk in (1, 31, 32, 33, 95, 256):
         nw = oracle.mask_words(n_blk)
@@ -59,7 +59,7 @@ def test_traversal_equals_definition_on_random_masks():
                     pos = np.nonzero(bitsv[r])[0][:cap].tolist()
                     want = pos + [-1] * (cap - len(pos))
                     assert got[r].tolist() == want
-                    assert oracle.mask_blocks_by_traversal(words[r], cap) == want
+                    assert oracle.mask_blocks_by_scan(words[r], n_blk, cap) == want
 
 
 def test_round_trip_of_selections():
