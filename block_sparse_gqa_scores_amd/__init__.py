@@ -23,7 +23,8 @@ ENTRY_SPARSE_ATTN_BWD, ENTRY_KL_LOSS_BWD = 5, 6
 EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
             "msa_forward_profiled", "msa_attn_chunks", "msa_workspace_bytes", "msa_workspace_min_bytes",
             "msa_status_str", "msa_block_mask", "msa_mask_blocks", "msa_kl_loss_fwd", "msa_sparse_attn_bwd",
-            "msa_kl_loss_bwd")
+            "msa_kl_loss_bwd", "msa_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 256 << 20  # MSA_NOALLOC_SCRATCH_BYTES of msa.h
 # Stages of msa_forward_profiled: the index scores and the Top-k once, then the
 # three attention stages once per query chunk.
 STAGES = ("index_scores", "block_topk", "attn_build", "attn_partial", "attn_merge")
@@ -77,6 +78,7 @@ def lib():
         L.msa_forward.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_forward_profiled.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P,
                                            ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+        L.msa_forward_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P]
         L.msa_block_mask.argtypes = [D, P, P, P]
         L.msa_mask_blocks.argtypes = [D, P, P, P]
         L.msa_kl_loss_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -84,7 +86,7 @@ def lib():
         L.msa_sparse_attn_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for f in (L.msa_index_scores, L.msa_block_topk, L.msa_sparse_attn_fwd, L.msa_forward,
                   L.msa_forward_profiled, L.msa_block_mask, L.msa_mask_blocks, L.msa_kl_loss_fwd,
-                  L.msa_sparse_attn_bwd, L.msa_kl_loss_bwd):
+                  L.msa_sparse_attn_bwd, L.msa_kl_loss_bwd, L.msa_forward_noalloc):
             f.restype = ctypes.c_int
         L.msa_attn_chunks.argtypes = [D, ctypes.c_int, ctypes.c_size_t]
         L.msa_attn_chunks.restype = ctypes.c_int
@@ -346,6 +348,29 @@ def msa_forward(q, k, v, q_idx, k_idx, *, topk=16, block_size=128, softmax_scale
         res.append(lse)
     if want_idx:
         res.append(block_idx)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def msa_forward_noalloc(q, k, v, q_idx, k_idx, *, topk=16, block_size=128, softmax_scale=0.0, out=None,
+                        lse=None, block_idx=None, return_lse=False, return_idx=False):
+    """msa_forward on the library's static scratch instead of a caller
+    workspace (the C entry point allocates nothing; outputs not passed in are
+    allocated here, before the call).  Returns as msa_forward."""
+    import torch
+    d = dims_of(q, k, q_idx, k_idx, topk=topk, block_size=block_size, softmax_scale=softmax_scale)
+    dev = q.device
+    _main_inputs(d, dev, q=q, k=k, v=v, q_idx=q_idx, k_idx=k_idx)
+    out = _out("out", out, torch.bfloat16, tuple(q.shape), dev)
+    want_lse, want_idx = return_lse or lse is not None, return_idx or block_idx is not None
+    if want_lse:
+        lse = _out("lse", lse, torch.float32, (d.batch, d.num_heads_q, d.seqlen_q), dev)
+    if want_idx:
+        block_idx = _out("block_idx", block_idx, torch.int32, (d.batch, d.num_heads_kv, d.seqlen_q, topk), dev)
+    rc = lib().msa_forward_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx), _ptr(out),
+                                   _ptr(lse if want_lse else None), _ptr(block_idx if want_idx else None),
+                                   _stream(dev))
+    _check(rc, "msa_forward_noalloc")
+    res = [out] + ([lse] if want_lse else []) + ([block_idx] if want_idx else [])
     return res[0] if len(res) == 1 else tuple(res)
 
 

@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libmsa.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "msa")
 
 SOURCES = ["index_scan.hip", "block_topk.hip", "sparse_attn.hip", "kl_loss.hip", "attn_bwd.hip", "kl_bwd.hip",
-           "block_mask.hip", "plan.cpp", "msa_api.cpp"]
+           "block_mask.hip", "noalloc.hip", "plan.cpp", "msa_api.cpp"]
 ARCH = "gfx950"
 # Packed fp32 vector ops are kept out of the generated code on purpose.
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "msa.h"
+
 namespace msa {
 
 // Block scores (see index_scan.hip).
@@ -76,6 +78,12 @@ hipError_t launch_kl_loss_bwd(const AttnShape& s, int D_idx, const uint16_t* q, 
                               const uint16_t* q_idx, const uint16_t* k_idx, const int32_t* idx,
                               const float* lse, const float* lse_idx, float coef, uint16_t* dq_idx,
                               uint16_t* dk_idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+// The host checks msa_forward makes before anything else (dims, then the
+// pointers' presence and alignment); MSA_OK for an empty problem as well.
+msa_status forward_checks(const msa_dims* d, const void* q, const void* k, const void* v,
+                          const void* q_idx, const void* k_idx, const void* out, const float* lse,
+                          const int32_t* block_idx_out);
 
 // Writes n zero floats (a kernel, so the call can sit inside a graph capture).
 hipError_t launch_fill_zero(float* dst, long n, hipStream_t stream);

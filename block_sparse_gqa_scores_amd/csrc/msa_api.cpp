@@ -123,6 +123,22 @@ size_t workspace_of(const msa_dims* d, int entry, bool min) {
 
 }  // namespace
 
+namespace msa {
+
+msa_status forward_checks(const msa_dims* d, const void* q, const void* k, const void* v,
+                          const void* q_idx, const void* k_idx, const void* out, const float* lse,
+                          const int32_t* block_idx_out) {
+  msa_status st = check_dims(d, true, true);
+  if (st != MSA_OK || is_empty(*d)) return st;
+  if (!q || !k || !v || !q_idx || !k_idx || !out) return MSA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_idx) || !aligned16(k_idx) ||
+      !aligned16(out) || (lse && !aligned16(lse)) || (block_idx_out && !aligned16(block_idx_out)))
+    return MSA_ERR_MISALIGNED;
+  return MSA_OK;
+}
+
+}  // namespace msa
+
 extern "C" {
 
 const char* msa_status_str(msa_status s) {
@@ -324,12 +340,8 @@ msa_status forward_impl(const msa_dims* d, const void* q, const void* k, const v
                         const void* q_idx, const void* k_idx, void* out, float* lse,
                         int32_t* block_idx_out, void* ws, size_t ws_bytes, void* stream,
                         const msa::StageEvents* ev) {
-  msa_status st = check_dims(d, true, true);
+  msa_status st = msa::forward_checks(d, q, k, v, q_idx, k_idx, out, lse, block_idx_out);
   if (st != MSA_OK || is_empty(*d)) return st;
-  if (!q || !k || !v || !q_idx || !k_idx || !out) return MSA_ERR_NULL_PTR;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_idx) || !aligned16(k_idx) ||
-      !aligned16(out) || (lse && !aligned16(lse)) || (block_idx_out && !aligned16(block_idx_out)))
-    return MSA_ERR_MISALIGNED;
   const msa::AttnShape s = attn_shape(*d);
   const size_t bm_sz = forward_bm_bytes(*d);
   const size_t idx_sz = align256(idx_bytes(*d));

@@ -185,6 +185,28 @@ msa_status msa_forward(const msa_dims* dims, const void* q, const void* k,
                        size_t ws_bytes, void* stream);
 
 /*
+ * msa_forward for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same
+ * computation and results as msa_forward, with the workspace taken from a
+ * static device array inside the library instead of the caller.  The array
+ * holds MSA_NOALLOC_SCRATCH_BYTES bytes on each GPU the call runs on (the
+ * current device; `stream` must belong to it), from the first call there
+ * until the process ends; the attention runs in as many query chunks as that
+ * size requires.  The call allocates and frees nothing.  A problem whose
+ * smallest workspace (msa_workspace_min_bytes(dims, MSA_ENTRY_FORWARD)) is
+ * larger returns MSA_ERR_WORKSPACE_TOO_SMALL and launches nothing.  All
+ * calls on one GPU share the array: calls that overlap on one GPU (several
+ * streams or host threads) race and must be serialised by the caller.
+ * Arguments, checks and errors otherwise as msa_forward; MSA_ERR_HIP also if
+ * the array's address cannot be obtained.
+ */
+#define MSA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+msa_status msa_forward_noalloc(const msa_dims* dims, const void* q, const void* k,
+                               const void* v, const void* q_idx, const void* k_idx,
+                               void* out, float* lse, int32_t* block_idx_out,
+                               void* stream);
+
+/*
  * Block-mask form of a selection (Sparse Attention Part II, section 4.3: the
  * blocks a query visits kept as one flag per block, 32 flags to an unsigned
  * word, block j at bit j mod 32 of word floor(j / 32)):

@@ -244,6 +244,25 @@ def test_size_limits():
     assert fwd(dims(batch=1 << 10, seqlen_q=1 << 17, seqlen_k=1 << 17, topk=16)) == 3
 
 
+def test_noalloc_host_checks():
+    """msa_forward_noalloc makes msa_forward's host checks before any HIP call,
+    and rejects a problem whose smallest workspace exceeds its static scratch
+    (only failure paths here: nothing may be launched)."""
+    L = msa.lib()
+
+    def call(d, q=A, k=A, v=A, qi=A, ki=A, out=A, lse=NULL, idx=NULL):
+        return L.msa_forward_noalloc(None if d is None else ctypes.byref(d), q, k, v, qi, ki, out, lse, idx, None)
+
+    assert call(None) == 1
+    assert call(dims(causal=0)) == 3 and call(dims(topk=0)) == 2
+    assert call(dims(), q=NULL) == 1 and call(dims(), out=MIS) == 4 and call(dims(), lse=MIS) == 4
+    assert call(dims(batch=0), q=NULL, k=NULL, v=NULL, qi=NULL, ki=NULL, out=NULL) == 0
+    # topk 32 stages block scores: 8 x 32768 rows x 256 blocks x 4 bytes = 256 MiB alone
+    big = dims(seqlen_q=32768, seqlen_k=32768, num_heads_q=64, num_heads_kv=8, topk=32)
+    assert msa.msa_workspace_min_bytes(big, msa.ENTRY_FORWARD) > msa.NOALLOC_SCRATCH_BYTES
+    assert call(big) == 5
+
+
 def test_status_strings():
     for code, name in msa.STATUS_NAMES.items():
         assert msa.msa_status_str(code) == name
