@@ -21,6 +21,7 @@
 // score is strictly higher: equal scores keep the lower index, as the
 // selection rule requires.
 #include <climits>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -382,6 +383,342 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
   }
 }
 
+// Selection mode (scores + Top-k in one pass, k <= 16): one workgroup of
+// eight waves per 512-row tile sweeps the key blocks 0 .. (its largest local
+// block - 1), two blocks per barrier, the next two blocks' tiles loading
+// straight into the other half of the LDS meanwhile.  Each wave owns 64 rows
+// (two 32-row MFMA N tiles) and keeps their index queries in registers.
+//
+// The instruction stream of a block is one software pipeline, so the matrix
+// pipe does not drain between 32-key tile rows:
+//   - tile rows alternate between two accumulator sets: the maxima of row mt
+//     are taken while the MFMAs of row mt + 1 run (the last row's during the
+//     next block's first row);
+//   - the operand fragments are read from LDS three MFMA pairs ahead;
+//   - the previous block's maximum is finished (one lane-half swap) during
+//     the next block's first row and its Top-k offer during the rows after;
+//   - nothing in a block branches, and the MFMAs, LDS reads and vector
+//     instructions are interleaved explicitly (sched_group_barrier).
+// A row's kept blocks are 64-bit keys (order-preserving score << 32 |
+// ~index: larger is better), ascending, keep[0] the worst; a key that beats
+// keep[0] enters and keep[0] drops out.  Blocks arrive in ascending order,
+// keys are distinct, so the kept set after the last offer is the exact
+// top-(k-1) with ties to the lower index, whatever the offers' order.
+// Calls f(std::integral_constant<int, i>) for i = B .. E - 1 in order: a
+// loop whose every index is a compile-time constant.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Anchors in the instruction stream (empty statements, no instruction is
+// emitted; statements with side effects keep their order): pin(v) makes v be
+// computed before this point, launder(v) makes whatever uses v after it wait
+// for this point.  Together they hold a computation between two points.
+__device__ __forceinline__ void pin(float v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void pin(uint64_t v) {
+  asm volatile("" ::"v"((uint32_t)v), "v"((uint32_t)(v >> 32)));
+}
+__device__ __forceinline__ void launder(float& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void launder(uint64_t& v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  v = ((uint64_t)hi << 32) | lo;
+}
+
+// Key of block j for this lane's row from the block's maxima m[0], m[1] of
+// the wave's two N tiles: lanes < 32 own a row of tile 0 and lanes >= 32 a row
+// of tile 1, and each 32-key group of the block sits in the two lane halves,
+// so one swap of halves gives every lane its row's maximum over 128 keys.
+// Blocks at or past the row's local block (and j = INT_MAX) give 0, which
+// enters nowhere.  No branch: the compiler would otherwise split the block's
+// instruction stream at a divergent one.
+__device__ __forceinline__ uint64_t offer_key(const float (&m)[2], int j, int my_l) {
+  float lo_half = m[0], hi_half = m[1];
+  swap32(lo_half, hi_half);
+  const uint32_t u = __float_as_uint(__builtin_fmaxf(lo_half, hi_half));
+  const uint32_t score = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);  // order_key(max)
+  const uint32_t ok = 0u - (uint32_t)(j < my_l);
+  return ((uint64_t)(score & ok) << 32) | (uint32_t)(~(uint32_t)j & ok);
+}
+
+template <int DIDX>
+__global__ __launch_bounds__(512, 1) void index_select_kernel(ScanArgs a) {
+  constexpr int WAVES = 8;
+  constexpr int kThr = 64 * WAVES;
+  constexpr int KS = DIDX / 16;                  // MFMA k-steps per tile row
+  constexpr int CPR = DIDX / 8;                  // 16-byte chunks per key row
+  constexpr int TILE_CHUNKS = kBlock * CPR;
+  constexpr int TILE_BYTES = TILE_CHUNKS * 16;
+  constexpr int ROW_BYTES = 32 * CPR * 16;       // one 32-key tile row
+  constexpr int LOADS = TILE_CHUNKS / kThr;      // 16-byte loads per thread per tile
+  constexpr int STEPS = 4 * KS;                  // MFMA pairs per block
+  constexpr int PF = 3;                          // fragment prefetch distance (pairs)
+  constexpr int ROWS_WG = WAVES * 64;
+  __shared__ u32x4 ktile[4 * TILE_CHUNKS];       // two pairs of key tiles
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int b = blockIdx.x / a.n_qtiles;
+  const int qt = a.n_qtiles - 1 - (blockIdx.x - b * a.n_qtiles);  // longest rows first
+
+  const int R = a.S_q * a.H_kv;
+  const int off = a.S_k - a.S_q;                 // position of query i is i + off
+  const int wg_r0 = qt * ROWS_WG;
+  const int wg_r1 = min(wg_r0 + ROWS_WG, R) - 1;
+  const int nj = max(0, (wg_r1 / a.H_kv + off) / kBlock);  // blocks before the largest local block
+  const int w_r0 = wg_r0 + wave * 64;
+
+  // Stationary B operand: this wave's 64 index-query rows (rows past R read
+  // the last row; they are never stored).
+  u32x4 qb[2][KS];
+  {
+    const uint16_t* qbase = a.q_idx + (size_t)b * R * DIDX;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int r = min(w_r0 + 32 * n + (lane & 31), R - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qb[n][ks] = *reinterpret_cast<const u32x4*>(qbase + (size_t)r * DIDX + 16 * ks + 8 * (lane >> 5));
+    }
+  }
+
+  // Key tiles go from memory straight into LDS (global_load_lds_dwordx4:
+  // lane l of a wave writes the 16 bytes at the wave's LDS base + 16 l); LDS
+  // piece q = it * kThr + tid is key row q / CPR, stored chunk q % CPR, which
+  // holds the row's chunk swz(row, q % CPR) (the swizzle is its own inverse).
+  // Rows past S_k (only in the last block; masked for every row, since only
+  // blocks before a row's local block are ranked) read the last key row.
+  const uint16_t* kbase = a.k_idx + (size_t)b * a.S_k * DIDX;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  int kofs[LOADS];
+#pragma unroll
+  for (int it = 0; it < LOADS; ++it) {
+    const int q = it * kThr + tid;
+    kofs[it] = (q / CPR) * DIDX + 8 * swz<DIDX>(q / CPR, q % CPR);
+  }
+  auto load_tile = [&](int j, int buf) {
+    const uint16_t* kb = kbase + (size_t)j * kBlock * DIDX;
+    if (j * kBlock + kBlock <= a.S_k) {
+#pragma unroll
+      for (int it = 0; it < LOADS; ++it)
+        load_lds16(kb + kofs[it], &ktile[buf * TILE_CHUNKS + it * kThr + wave_s * 64]);
+    } else {
+#pragma unroll
+      for (int it = 0; it < LOADS; ++it) {
+        const int row = kofs[it] / DIDX;
+        const int s = min(j * kBlock + row, a.S_k - 1);
+        load_lds16(kbase + (size_t)s * DIDX + (kofs[it] - row * DIDX),
+                   &ktile[buf * TILE_CHUNKS + it * kThr + wave_s * 64]);
+      }
+    }
+  };
+
+  // Byte offset of this lane's operand fragment for k-step ks inside a tile
+  // row (key row lane % 32, chunk 2 ks + lane / 32, swizzled); a row mt of
+  // block slot s of pair half h adds h * 2 TILE_BYTES + s * TILE_BYTES +
+  // mt * ROW_BYTES, which fits the instruction's immediate offset but for h.
+  int fb[KS];  // of pair half 0; moved to the other half and back pair by pair
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    fb[ks] = ((lane & 31) * CPR + swz<DIDX>(lane & 31, 2 * ks + (lane >> 5))) * 16;
+  const char* lds = reinterpret_cast<const char*>(ktile);
+
+  if (nj > 0) {
+    load_tile(0, 0);
+    load_tile(min(1, nj - 1), 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int my_r = w_r0 + lane;
+  const int my_l = my_r < R ? (my_r / a.H_kv + off) / kBlock : -1;
+  uint64_t keep[kKeep];
+#pragma unroll
+  for (int t = 0; t < kKeep; ++t) keep[t] = t < a.topk - 1 ? 0ull : ~0ull;
+
+  f32x16 acc[2][2];  // [set][n tile]; set 1 starts as -inf: no block before the first
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[1][n][r] = neg_inf();
+  }
+  float mlast[2] = {neg_inf(), neg_inf()};  // previous block's maxima (rows 0..2 taken)
+  int jlast = INT_MAX;                       // previous block (INT_MAX: none, offers nothing)
+
+  // Row maxima as micro-ops, so that each MFMA step carries a fixed share:
+  // op k of max16 for one N tile (k = 0..7): five maxima of three
+  // accumulators, two of those, then the running maximum.  Each result is
+  // pinned to its step (an empty asm statement that takes it as an input):
+  // otherwise the optimizer sinks the maxima of the later rows to their first
+  // use, at the block's end, where they would run without any MFMA beside them.
+  struct RowMax {
+    float t[5], u[2];
+  };
+  auto max_op = [](RowMax& rm, const f32x16& x, float& m, auto K) {
+    constexpr int k = decltype(K)::value;
+    if constexpr (k < 5) {
+      float a = x[3 * k], b = x[3 * k + 1], c = x[3 * k + 2];
+      launder(a);
+      launder(b);
+      launder(c);
+      rm.t[k] = max3f(a, b, c);
+      pin(rm.t[k]);
+    } else if constexpr (k == 5) {
+      rm.u[0] = max3f(rm.t[0], rm.t[1], rm.t[2]);
+      pin(rm.u[0]);
+    } else if constexpr (k == 6) {
+      float c = x[15];
+      launder(c);
+      rm.u[1] = max3f(rm.t[3], rm.t[4], c);
+      pin(rm.u[1]);
+    } else {
+      m = max3f(rm.u[0], rm.u[1], m);
+      pin(m);
+    }
+  };
+
+  // One block: the MFMAs of its 4 tile rows (row mt into accumulator set
+  // mt & 1), each step (one MFMA pair) with a fixed share of vector work on
+  // earlier rows:
+  //   row 0: the previous block's last row maxima (set 1), then its key x;
+  //   rows 1..3: the maxima of rows 0..2, and the kept keys offered x one
+  //   slot at a time (the ones below x move down one slot, x takes the slot
+  //   above them).
+  // Each step is its own scheduling region (sched_barrier), so the LDS read
+  // for three steps ahead stays where it is written and the vector work stays
+  // between this step's MFMAs.  Steps are a compile-time loop, so every index
+  // into the register arrays is a constant.  `fb` holds the per-k-step
+  // fragment addresses of the pair half, `slot` the block's place in the
+  // pair, `jo` the block index its offer will carry (INT_MAX for a repeated
+  // last block).
+  constexpr int OPS = 16 / KS;  // max16 micro-ops per N tile per step (2 at D_idx 128)
+  auto block = [&](const int (&fb)[KS], const int slot, const int jo) {
+    u32x4 ring[4];
+    static_for<0, PF>([&](auto S) {
+      constexpr int sp = decltype(S)::value;
+      ring[sp] = *reinterpret_cast<const u32x4*>(lds + fb[sp % KS] + slot * TILE_BYTES + (sp / KS) * ROW_BYTES);
+    });
+    float mrow[2] = {neg_inf(), neg_inf()};
+    RowMax rm[2];
+    uint64_t x = 0;
+    bool above0 = false;  // x beats keep[t] for the next slot t to update
+    static_for<0, STEPS>([&](auto S) {
+      constexpr int s = decltype(S)::value;
+      constexpr int mt = s / KS, ks = s % KS, set = mt & 1;
+      if constexpr (s + PF < STEPS) {
+        constexpr int sp = s + PF;
+        ring[sp % 4] = *reinterpret_cast<const u32x4*>(lds + fb[sp % KS] + slot * TILE_BYTES + (sp / KS) * ROW_BYTES);
+      }
+      const u32x4 fa = ring[s % 4];
+      // Maxima of the previous row (of the previous block's last row in row 0).
+      auto row_ops = [&](int n) {
+        static_for<0, OPS>([&](auto O) {
+          constexpr int k = ks * OPS + decltype(O)::value;
+          if constexpr (k < 8) {
+            if constexpr (mt == 0) max_op(rm[n], acc[1][n], mlast[n], std::integral_constant<int, k>{});
+            else max_op(rm[n], acc[set ^ 1][n], mrow[n], std::integral_constant<int, k>{});
+          }
+        });
+      };
+      acc[set][0] = mfma32x32x16(fa, qb[0][ks], ks == 0 ? zero16() : acc[set][0]);
+      row_ops(0);
+      acc[set][1] = mfma32x32x16(fa, qb[1][ks], ks == 0 ? zero16() : acc[set][1]);
+      row_ops(1);
+      if constexpr (mt == 0 && ks == KS - 1) {
+        x = offer_key(mlast, jlast, my_l);
+        above0 = x > keep[0];
+        pin(x);
+      }
+      if constexpr (mt >= 1) {
+        // Slots in ascending order over rows 1..3: slot t compares x with
+        // keep[t + 1] before that one moves, so two flags are live at a time.
+        static_for<0, kKeep>([&](auto T) {
+          constexpr int t = decltype(T)::value;
+          if constexpr (t * 3 * KS / kKeep == (mt - 1) * KS + ks) {
+            launder(x);
+            const bool above1 = t + 1 < kKeep && x > keep[t + 1 < kKeep ? t + 1 : t];
+            keep[t] = above1 ? keep[t + 1 < kKeep ? t + 1 : t] : (above0 ? x : keep[t]);
+            pin(keep[t]);
+            above0 = above1;
+          }
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    mlast[0] = mrow[0];
+    mlast[1] = mrow[1];
+    jlast = jo;
+  };
+
+  for (int jj = 0; jj < nj; jj += 2) {
+    const int h = (jj >> 1) & 1;  // pair half of blocks jj, jj + 1
+    // The other half was last read before the previous barrier.
+    if (jj + 2 < nj) {
+      load_tile(jj + 2, 2 * (h ^ 1));
+      load_tile(min(jj + 3, nj - 1), 2 * (h ^ 1) + 1);
+    }
+    // A pair past the last block repeats it (its tile was loaded clamped)
+    // and offers nothing for the repeat.
+    block(fb, 0, jj);
+    block(fb, 1, jj + 1 < nj ? jj + 1 : INT_MAX);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) fb[ks] += h ? -2 * TILE_BYTES : 2 * TILE_BYTES;
+    // This wave's tile loads have landed before anyone reads them.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  // The last block's last row and its offer.
+  {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) mlast[n] = max16(mlast[n], acc[1][n]);
+    const uint64_t x = offer_key(mlast, jlast, my_l);
+    bool above[kKeep];
+#pragma unroll
+    for (int t = 0; t < kKeep; ++t) above[t] = x > keep[t];
+#pragma unroll
+    for (int t = 0; t < kKeep; ++t) {
+      const bool up = t + 1 < kKeep && above[t + 1];
+      keep[t] = up ? keep[t + 1] : (above[t] ? x : keep[t]);
+    }
+  }
+
+  // Kept blocks in ascending order, then the local block, then -1 padding.
+  if (my_r < R) {
+    int js[16];
+#pragma unroll
+    for (int t = 0; t < kKeep; ++t)
+      js[t] = (keep[t] != 0ull && keep[t] != ~0ull) ? (int)~(uint32_t)keep[t] : INT_MAX;
+    js[15] = INT_MAX;
+#pragma unroll
+    for (int k2 = 2; k2 <= 16; k2 <<= 1)
+#pragma unroll
+      for (int h2 = k2 >> 1; h2 > 0; h2 >>= 1)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int u = t ^ h2;
+          if (u > t) {
+            const int mn = min(js[t], js[u]), mx = max(js[t], js[u]);
+            const bool up = (t & k2) == 0;
+            js[t] = up ? mn : mx;
+            js[u] = up ? mx : mn;
+          }
+        }
+    int n = 0;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) n += js[t] != INT_MAX;
+    const int i = my_r / a.H_kv, g = my_r - (my_r / a.H_kv) * a.H_kv;
+    int32_t* out = a.sel + (((size_t)b * a.H_kv + g) * a.S_q + i) * a.topk;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (e < a.topk) out[e] = e < n ? js[e] : (e == n ? my_l : -1);
+  }
+}
+
 // Few rows per sequence (decode): one wave covers every row of a sequence
 // (at most 32), so the waves of a workgroup split the key blocks between them
 // and need no barrier.  A wave reads its key block with fully coalesced loads
@@ -531,9 +868,9 @@ hipError_t launch_index_select(const uint16_t* q_idx, const uint16_t* k_idx, int
   a.n_qtiles = (R + kRowsPerWg - 1) / kRowsPerWg;
   const long grid = (long)batch * a.n_qtiles;
   if (D_idx == 128)
-    hipLaunchKernelGGL((index_scan_prefill<128, kNT, kWaves, true>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL(index_select_kernel<128>, dim3((unsigned)grid), dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL((index_scan_prefill<64, kNT, kWaves, true>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL(index_select_kernel<64>, dim3((unsigned)grid), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
