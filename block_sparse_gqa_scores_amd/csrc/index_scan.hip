@@ -607,7 +607,12 @@ __global__ __launch_bounds__(512, 1) void index_select_kernel(ScanArgs a) {
     RowMax rm[2];
     uint64_t x = 0;
     bool above0 = false;  // x beats keep[t] for the next slot t to update
-    static_for<0, STEPS>([&](auto S) {
+    // Whether some lane's key beats its worst kept key: when none does (the
+    // common case once many blocks have been seen), nothing can enter and
+    // rows 1..3 skip the offer slots (a wave-uniform branch per slot).
+    bool any = false;
+    // Step s of the block; rows 1..3 carry the offer slots.
+    auto step = [&](auto S) {
       constexpr int s = decltype(S)::value;
       constexpr int mt = s / KS, ks = s % KS, set = mt & 1;
       if constexpr (s + PF < STEPS) {
@@ -632,6 +637,7 @@ __global__ __launch_bounds__(512, 1) void index_select_kernel(ScanArgs a) {
       if constexpr (mt == 0 && ks == KS - 1) {
         x = offer_key(mlast, jlast, my_l);
         above0 = x > keep[0];
+        any = __builtin_amdgcn_ballot_w64(above0) != 0;
         pin(x);
       }
       if constexpr (mt >= 1) {
@@ -639,17 +645,19 @@ __global__ __launch_bounds__(512, 1) void index_select_kernel(ScanArgs a) {
         // keep[t + 1] before that one moves, so two flags are live at a time.
         static_for<0, kKeep>([&](auto T) {
           constexpr int t = decltype(T)::value;
-          if constexpr (t * 3 * KS / kKeep == (mt - 1) * KS + ks) {
-            launder(x);
+          if constexpr (t * 3 * KS / kKeep == (mt - 1) * KS + ks) if (any) {
+            // The kept keys ascend, so above1 implies above0.
             const bool above1 = t + 1 < kKeep && x > keep[t + 1 < kKeep ? t + 1 : t];
-            keep[t] = above1 ? keep[t + 1 < kKeep ? t + 1 : t] : (above0 ? x : keep[t]);
+            const uint64_t up = above1 ? keep[t + 1 < kKeep ? t + 1 : t] : x;
+            keep[t] = above0 ? up : keep[t];
             pin(keep[t]);
             above0 = above1;
           }
         });
       }
       __builtin_amdgcn_sched_barrier(0);
-    });
+    };
+    static_for<0, STEPS>(step);
     mlast[0] = mrow[0];
     mlast[1] = mrow[1];
     jlast = jo;
