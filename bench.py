@@ -366,7 +366,9 @@ def kernel_of_stage(w, stage):
     if stage == "index_scores":
         if w.seqlen_q * w.heads_kv <= 32:
             return f"index_scan_decode<{w.index_dim}>"
-        return f"index_scan_prefill<{w.index_dim}, 2, 8, {'true' if fused_selection(w) else 'false'}>"
+        if fused_selection(w):
+            return f"index_select_kernel<{w.index_dim}>"
+        return f"index_scan_prefill<{w.index_dim}, 2, 8>"
     return {"block_topk": "block_topk_kernel", "attn_build": "zero/bucket_count/scan/bucket_fill kernels",
             "attn_partial": f"attn_decode_kernel<{w.group}>" if w.seqlen_q == 1 else f"attn_partial_kernel<{w.group}>",
             "attn_merge": f"merge_kernel<{w.group}>"}[stage]

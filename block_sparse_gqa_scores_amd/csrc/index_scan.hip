@@ -12,10 +12,10 @@
 // matrix, and 256 consecutive rows (32 queries when H_kv = 8) share one
 // 128-block window of causal positions.
 //
-// Selection mode (the forward path with k <= 16): one workgroup sweeps every
-// key block before its rows' local blocks and keeps, per row, the running best
-// k-1 blocks in registers, so neither the block scores nor a separate Top-k
-// pass touch memory (the streaming form of the exact top-k of Sparse
+// Selection (index_select_kernel, the forward path with k <= 16): one
+// workgroup sweeps every key block before its rows' local blocks and keeps,
+// per row, the running best k-1 blocks in registers, so neither the block
+// scores nor a separate Top-k pass touch memory (the streaming form of the exact top-k of Sparse
 // Attention Part II, sections 4.2 and 4.4).  Blocks arrive in ascending index
 // order, so a new block displaces the current worst kept block only when its
 // score is strictly higher: equal scores keep the lower index, as the
@@ -42,11 +42,11 @@ struct ScanArgs {
   int S_q, S_k, H_kv, n_blk;
   int n_qtiles;   // ceil(S_q * H_kv / rows per workgroup)
   int batch;
-  int32_t* sel;   // selection mode: [B][H_kv][S_q][topk] output
+  int32_t* sel;   // selection: [B][H_kv][S_q][topk] output
   int topk;
 };
 
-constexpr int kKeep = kSelectKeep;  // selection mode: earlier blocks kept per row (k <= 16)
+constexpr int kKeep = kSelectKeep;  // selection: earlier blocks kept per row (k <= 16)
 
 // 16-byte chunk position inside an LDS row of the key tile, XOR-swizzled so
 // that the 16 lanes reading one chunk column of 16 consecutive rows hit 16
@@ -64,11 +64,12 @@ __device__ __forceinline__ void load_lds16(const uint16_t* src, u32x4* wave_base
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)wave_base, 16, 0, 0);
 }
 
-// NT 32-row MFMA N tiles per wave: every 16-byte key fragment read from LDS
-// feeds NT matrix instructions.  SELECT: selection mode (above).
-template <int DIDX, int NT, int WAVES, bool SELECT>
+// Block scores of many rows (prefill): a workgroup of WAVES waves covers
+// WAVES * 32 * NT rows and kChunk key blocks.  NT 32-row MFMA N tiles per
+// wave: every 16-byte key fragment read from LDS feeds NT matrix
+// instructions.
+template <int DIDX, int NT, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) {
-  static_assert(!SELECT || NT == 2, "selection mode keeps one row per lane");
   constexpr int kThreads = 64 * WAVES;
   constexpr int KS = DIDX / 16;           // MFMA k-steps
   constexpr int CPR = DIDX / 8;           // 16-byte chunks per key row
@@ -76,36 +77,26 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
   constexpr int LOADS = TILE_CHUNKS / kThreads;  // 16-byte loads per thread
   constexpr int ROWS_W = 32 * NT;
   constexpr int ROWS_WG = WAVES * ROWS_W;
-  // Selection mode works on two key blocks per barrier: four tile buffers.
-  constexpr int NBUF = SELECT ? 4 : 2;
-  __shared__ u32x4 ktile[NBUF][TILE_CHUNKS];
-  __shared__ float stage[SELECT ? 1 : ROWS_WG * kStageStride];
+  __shared__ u32x4 ktile[2][TILE_CHUNKS];
+  __shared__ float stage[ROWS_WG * kStageStride];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  int chunk, b, qt;
-  if constexpr (SELECT) {  // one workgroup per row tile, longest rows first
-    chunk = 0;
-    b = blockIdx.x / a.n_qtiles;
-    qt = a.n_qtiles - 1 - (blockIdx.x - b * a.n_qtiles);
-  } else {
-    const int per_chunk = a.batch * a.n_qtiles;
-    chunk = blockIdx.x / per_chunk;
-    const int rem = blockIdx.x - chunk * per_chunk;
-    b = rem / a.n_qtiles;
-    qt = rem - b * a.n_qtiles;
-  }
+  const int per_chunk = a.batch * a.n_qtiles;
+  const int chunk = blockIdx.x / per_chunk;
+  const int rem = blockIdx.x - chunk * per_chunk;
+  const int b = rem / a.n_qtiles;
+  const int qt = rem - b * a.n_qtiles;
 
   const int R = a.S_q * a.H_kv;
   const int off = a.S_k - a.S_q;        // position of query i is i + off
   const int wg_r0 = qt * ROWS_WG;
   const int wg_r1 = min(wg_r0 + ROWS_WG, R) - 1;  // last valid row
   const int j0 = chunk * kChunk;
-  const int nj = SELECT ? a.n_blk : min(kChunk, a.n_blk - j0);
+  const int nj = min(kChunk, a.n_blk - j0);
   const int wg_lmax = (wg_r1 / a.H_kv + off) / kBlock;  // largest local block
-  // Selection ranks only blocks before a row's local block.
-  const int nj_live = max(0, min(nj, wg_lmax - j0 + (SELECT ? 0 : 1)));
+  const int nj_live = max(0, min(nj, wg_lmax - j0 + 1));
 
   // The wave's rows and their causal positions.
   const int w_r0 = wg_r0 + wave * ROWS_W;
@@ -165,39 +156,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
     }                                                                                      \
   }
 
-  if (nj_live > 0) {
-    MSA_LOAD_TILE(j0, 0)
-    if constexpr (SELECT) { MSA_LOAD_TILE(j0 + min(1, nj_live - 1), 1) }
-  }
+  if (nj_live > 0) { MSA_LOAD_TILE(j0, 0) }
   // Everything loaded so far (index queries, first tile) has landed; saying so
   // explicitly keeps the loop's MFMAs from waiting on the next tile's loads.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // Selection mode: this lane's row, its local block, and its kept blocks as
-  // 64-bit keys (order-preserving score << 32 | ~index: larger is better),
-  // in ascending order, so keep[0] is the worst.  Unused slots hold 0 (worse
-  // than any block); slots past k-1 hold ~0 (never the worst, never moved).
-  const int my_r = w_r0 + lane;
-  const int my_l = my_r < R ? (my_r / a.H_kv + off) / kBlock : -1;
-  uint64_t keep[kKeep];
-#pragma unroll
-  for (int t = 0; t < kKeep; ++t) keep[t] = t < a.topk - 1 ? 0ull : ~0ull;
-
   const bool lo = lane < 32;
-  // Block max of block j for this lane's rows (tile kt in LDS).  mid() runs
-  // right after the first tile row's matrix instructions are issued, so its
-  // vector work executes while they do (selection mode puts the previous
-  // block's Top-k offer there).
-  auto block_max = [&](int j, const u32x4* kt, float (&best)[NT / 2], auto&& mid) {
-    // Selection mode skips blocks at or past every local block of the wave.
-    if (SELECT ? j >= w_t_max / kBlock : j * kBlock > w_t_max) {
-      mid();
+  // Block max of block j for this lane's rows (tile kt in LDS).
+  auto block_max = [&](int j, const u32x4* kt, float (&best)[NT / 2]) {
+    if (j * kBlock > w_t_max) {
 #pragma unroll
       for (int p2 = 0; p2 < NT / 2; ++p2) best[p2] = neg_inf();  // nothing visible to this wave
     } else {
-      // Selection mode ranks a block only for rows that see all of it.
-      const bool need_mask = !SELECT && j * kBlock + kBlock - 1 > w_t_min;
+      const bool need_mask = j * kBlock + kBlock - 1 > w_t_min;
       float m[NT];
 #pragma unroll
       for (int n = 0; n < NT; ++n) m[n] = neg_inf();
@@ -229,7 +201,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
 #pragma unroll
           for (int n = 0; n < NT; ++n) acc[n] = mfma32x32x16(ka[ks], qb[n][ks], acc[n]);
         }
-        if (mt == 0) mid();
         if (need_mask) {
 #pragma unroll
           for (int n = 0; n < NT; ++n)
@@ -257,110 +228,24 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
       }
     }
   };
-  // Selection mode: offer block j's max to this lane's row.  A block enters
-  // when it beats the worst kept one (keep[0]), which drops out: the kept
-  // blocks below the new key move down one slot, and the key takes the slot
-  // above them.  Every slot is a 64-bit compare and a nested select, and no
-  // slot depends on another; with no branch, the offer can sit among the
-  // next block's matrix instructions.  Keys are distinct (they carry the block
-  // index), so the kept set after the last offer does not depend on the order
-  // of the offers.  Blocks at or past the local block (and j = INT_MAX) offer
-  // the key 0, which enters nowhere.
-  auto offer = [&](int j, float bmax) {
-    const uint64_t x = j < my_l ? ((uint64_t)order_key(bmax) << 32) | (uint32_t)~(uint32_t)j : 0ull;
-    bool above[kKeep];  // x beats keep[t]
+  for (int jj = 0; jj < nj_live; ++jj) {
+    const int j = j0 + jj;
+    // The other buffer was last read before the previous barrier.
+    if (jj + 1 < nj_live) { MSA_LOAD_TILE(j + 1, (jj & 1) ^ 1) }
+    // Compiler-only fence: keep the next tile's loads before the compute,
+    // so they fly during the MFMAs.
+    asm volatile("" ::: "memory");
+    float best[NT / 2];
+    block_max(j, ktile[jj & 1], best);
 #pragma unroll
-    for (int t = 0; t < kKeep; ++t) above[t] = x > keep[t];
-#pragma unroll
-    for (int t = 0; t < kKeep; ++t) {
-      const bool up = t + 1 < kKeep && above[t + 1];
-      keep[t] = up ? keep[t + 1] : (above[t] ? x : keep[t]);
-    }
-  };
-
-  if constexpr (SELECT) {
-    // Two blocks per barrier: blocks jj, jj + 1 in buffers 2 h, 2 h + 1 (h =
-    // pair parity); the next pair's tiles load meanwhile straight into the
-    // other half.  Each block's offer runs during the next block's matrix
-    // instructions; the last one after the loop.
-    int pend_j = INT_MAX;
-    float pend_b = 0.f;
-    for (int jj = 0; jj < nj_live; jj += 2) {
-      const int h = (jj >> 1) & 1;
-      const bool more = jj + 2 < nj_live;
-      // The other half was last read before the previous barrier.
-      if (more) {
-        MSA_LOAD_TILE(j0 + jj + 2, 2 * (h ^ 1))
-        MSA_LOAD_TILE(j0 + min(jj + 3, nj_live - 1), 2 * (h ^ 1) + 1)
-      }
-      asm volatile("" ::: "memory");
-      float best[NT / 2];
-      block_max(j0 + jj, ktile[2 * h], best, [&] { offer(pend_j, pend_b); });
-      pend_j = j0 + jj;
-      pend_b = best[0];
-      if (jj + 1 < nj_live) {
-        block_max(j0 + jj + 1, ktile[2 * h + 1], best, [&] { offer(pend_j, pend_b); });
-        pend_j = j0 + jj + 1;
-        pend_b = best[0];
-      }
-      // This wave's tile loads have landed before anyone reads them.
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-    }
-    offer(pend_j, pend_b);
-  } else {
-    for (int jj = 0; jj < nj_live; ++jj) {
-      const int j = j0 + jj;
-      // The other buffer was last read before the previous barrier.
-      if (jj + 1 < nj_live) { MSA_LOAD_TILE(j + 1, (jj & 1) ^ 1) }
-      // Compiler-only fence: keep the next tile's loads before the compute,
-      // so they fly during the MFMAs.
-      asm volatile("" ::: "memory");
-      float best[NT / 2];
-      block_max(j, ktile[jj & 1], best, [] {});
-#pragma unroll
-      for (int p2 = 0; p2 < NT / 2; ++p2)
-        stage[(wave * ROWS_W + 64 * p2 + lane) * kStageStride + jj] = best[p2];
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-    }
+    for (int p2 = 0; p2 < NT / 2; ++p2)
+      stage[(wave * ROWS_W + 64 * p2 + lane) * kStageStride + jj] = best[p2];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 
 #undef MSA_LOAD_TILE
 
-  if constexpr (SELECT) {
-    // Kept blocks in ascending order, then the local block, then -1 padding.
-    if (my_r < R) {
-      int js[16];
-#pragma unroll
-      for (int t = 0; t < kKeep; ++t)
-        js[t] = (keep[t] != 0ull && keep[t] != ~0ull) ? (int)~(uint32_t)keep[t] : INT_MAX;
-      js[15] = INT_MAX;
-#pragma unroll
-      for (int k2 = 2; k2 <= 16; k2 <<= 1)
-#pragma unroll
-        for (int h2 = k2 >> 1; h2 > 0; h2 >>= 1)
-#pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const int u = t ^ h2;
-            if (u > t) {
-              const int mn = min(js[t], js[u]), mx = max(js[t], js[u]);
-              const bool up = (t & k2) == 0;
-              js[t] = up ? mn : mx;
-              js[u] = up ? mx : mn;
-            }
-          }
-      int n = 0;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) n += js[t] != INT_MAX;
-      const int i = my_r / a.H_kv, g = my_r - (my_r / a.H_kv) * a.H_kv;
-      int32_t* out = a.sel + (((size_t)b * a.H_kv + g) * a.S_q + i) * a.topk;
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (e < a.topk) out[e] = e < n ? js[e] : (e == n ? my_l : -1);
-    }
-    return;
-  }
   // Each row's nj block scores are contiguous in memory.
   for (int rr = tid; rr < ROWS_WG; rr += kThreads) {
     const int r = wg_r0 + rr;
@@ -383,7 +268,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
   }
 }
 
-// Selection mode (scores + Top-k in one pass, k <= 16): one workgroup of
+// Selection (scores + Top-k in one pass, k <= 16): one workgroup of
 // eight waves per 512-row tile sweeps the key blocks 0 .. (its largest local
 // block - 1), two blocks per barrier, the next two blocks' tiles loading
 // straight into the other half of the LDS meanwhile.  Each wave owns 64 rows
@@ -397,8 +282,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
 //   - the operand fragments are read from LDS three MFMA pairs ahead;
 //   - the previous block's maximum is finished (one lane-half swap) during
 //     the next block's first row and its Top-k offer during the rows after;
-//   - nothing in a block branches, and the MFMAs, LDS reads and vector
-//     instructions are interleaved explicitly (sched_group_barrier).
+//   - the MFMAs, LDS reads and vector instructions are placed step by step
+//     (one MFMA pair per step, a scheduling barrier between steps), and the
+//     only branches in a block are wave-uniform: a block whose key no lane
+//     would keep skips the offer slots.
 // A row's kept blocks are 64-bit keys (order-preserving score << 32 |
 // ~index: larger is better), ascending, keep[0] the worst; a key that beats
 // keep[0] enters and keep[0] drops out.  Blocks arrive in ascending order,
@@ -832,15 +719,10 @@ __global__ __launch_bounds__(kThreads, 1) void index_scan_decode(ScanArgs a) {
 
 }  // namespace
 
-// N tiles per wave and waves per workgroup of the prefill kernel.
-#ifndef MSA_SCAN_NT
-#define MSA_SCAN_NT 2
-#endif
-#ifndef MSA_SCAN_WAVES
-#define MSA_SCAN_WAVES 8
-#endif
-constexpr int kNT = MSA_SCAN_NT;
-constexpr int kWaves = MSA_SCAN_WAVES;
+// N tiles per wave and waves per workgroup of the prefill scores kernel; the
+// selection kernel uses the same row tile (8 waves of 64 rows).
+constexpr int kNT = 2;
+constexpr int kWaves = 8;
 constexpr int kRowsPerWg = kWaves * 32 * kNT;
 
 hipError_t launch_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, float* bm,
@@ -861,9 +743,9 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const uint16_t* k_idx, flo
   const long n_chunks = (n_blk + kChunk - 1) / kChunk;
   const long grid = n_chunks * batch * a.n_qtiles;
   if (D_idx == 128)
-    hipLaunchKernelGGL((index_scan_prefill<128, kNT, kWaves, false>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((index_scan_prefill<128, kNT, kWaves>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
   else
-    hipLaunchKernelGGL((index_scan_prefill<64, kNT, kWaves, false>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((index_scan_prefill<64, kNT, kWaves>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -80,7 +80,7 @@ size_t layout_build(Layout& L, const AttnShape& s);
 }  // namespace edges
 
 // The fused index scan keeps this many earlier blocks per row in registers
-// (selection mode, index_scan.hip), so it covers topk <= kSelectKeep + 1.
+// (the selection kernel of the index scan), so it covers topk <= kSelectKeep + 1.
 constexpr int kSelectKeep = 15;
 
 // Attention forward: bucket arrays, then per-edge partial records.
