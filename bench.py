@@ -272,7 +272,8 @@ def stage_work(w):
         "block_topk": ("fused", 0.0, "B") if fused_selection(w) else ("hbm", rows * (w.n_blk + w.topk) * 4.0, "B"),
         "attn_build": ("hbm", rows * w.topk * 4.0 * 2 + edges * 4.0, "B"),
         "attn_partial": partial,
-        "attn_merge": ("hbm", edges * G * (2 * w.head_dim + 8) + rows * G * w.head_dim * 2.0, "B"),
+        # records of 12-bit codes (1.5 bytes a value) plus 8 bytes of statistics per head
+        "attn_merge": ("hbm", edges * G * (1.5 * w.head_dim + 8) + rows * G * w.head_dim * 2.0, "B"),
     }
 
 

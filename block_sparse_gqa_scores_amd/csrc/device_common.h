@@ -106,6 +106,38 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
+// 12-bit codes.  A value x of a row whose largest magnitude is amax is stored
+// as round(x * s) + 2048 with s = 2047 / amax, an integer in 1 .. 4095; it
+// reads back as (code - 2048) / s, within amax / 4094 of x.
+//
+// q12_code: fma(x, s, 2^23 + 2048) rounds x * s + 2048 to the nearest integer
+// (from 2^23 to 2^24 floats are spaced by 1) and leaves it in the low 12 bits
+// of the result; the bits above are the exponent field of 2^23, 0x4B000000,
+// which any left shift by 8 or more moves out of the word.
+__device__ __forceinline__ uint32_t q12_code(float x, float s) {
+  return __float_as_uint(__builtin_fmaf(x, s, 8390656.0f));
+}
+// Eight codes (from q12_code) into three dwords, code v at bits 12 v .. 12 v + 11
+// of the 96-bit word d0 | d1 << 32 | d2 << 64.
+__device__ __forceinline__ void q12_pack8(const uint32_t (&c)[8], uint32_t& d0, uint32_t& d1, uint32_t& d2) {
+  d0 = (c[0] & 0xFFFu) | (c[1] << 12) | (c[2] << 24);
+  d1 = ((c[2] >> 8) & 0xFu) | ((c[3] & 0xFFFu) << 4) | (c[4] << 16) | (c[5] << 28);
+  d2 = ((c[5] >> 4) & 0xFFu) | (c[6] << 8) | (c[7] << 20);
+}
+// The eight codes of d0, d1, d2 (q12_pack8) as floats.
+__device__ __forceinline__ void q12_unpack8(uint32_t d0, uint32_t d1, uint32_t d2, float (&y)[8]) {
+  const uint32_t c2 = (uint32_t)((((uint64_t)d1 << 32) | d0) >> 24);
+  const uint32_t c5 = (uint32_t)((((uint64_t)d2 << 32) | d1) >> 28);
+  y[0] = (float)(d0 & 0xFFFu);
+  y[1] = (float)((d0 >> 12) & 0xFFFu);
+  y[2] = (float)(c2 & 0xFFFu);
+  y[3] = (float)((d1 >> 4) & 0xFFFu);
+  y[4] = (float)((d1 >> 16) & 0xFFFu);
+  y[5] = (float)(c5 & 0xFFFu);
+  y[6] = (float)((d2 >> 8) & 0xFFFu);
+  y[7] = (float)(d2 >> 20);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -119,6 +151,19 @@ __device__ __forceinline__ void swap32(float& a, float& b) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
   a = __uint_as_float(r[0]);
   b = __uint_as_float(r[1]);
+}
+
+// max and sum of x over lanes l and l ^ 32, in every lane (one
+// v_permlane32_swap instead of a ds_bpermute round trip).
+__device__ __forceinline__ float halves_max(float x) {
+  float a = x, b = x;
+  swap32(a, b);
+  return __builtin_fmaxf(a, b);
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  float a = x, b = x;
+  swap32(a, b);
+  return a + b;
 }
 
 // swap16(a, b): the odd 16-lane rows of a trade places with the even rows of

@@ -41,9 +41,9 @@ struct Params {
   int32_t* blk_sums;     // 2 * n_scan_wg
   int32_t* edges;        // slot ids grouped by bucket
   int2* work;            // (bucket, first edge in bucket)
-  float* part_lse;       // [slot][G]: log2-sum-exp of the block's visible logits
-  float* part_sc;        // [slot][G]: max |O_e| of the row
-  uint16_t* part_o;      // [slot][G * D] fp16: O_e / max |O_e|, in record order (below)
+  f32x2* part_stat;      // [slot][G]: log2-sum-exp of the block's visible logits, and
+                         // the scale of the row's codes (value = (code - 2048) scale)
+  u32x4* part_o;         // [slot][kRecBytes(G)]: O_e / l_e as 12-bit codes (sparse_attn.hip)
   // Alignment loss (kl_* kernels below).
   const uint16_t* q_idx;
   const uint16_t* k_idx;

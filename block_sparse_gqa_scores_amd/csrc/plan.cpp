@@ -44,11 +44,11 @@ bool index_select_fused(int S_q, int H_kv, int topk) {
 }
 
 // ---------------------------------------------------------------- forward
-// Bytes of per-edge records per query: G partial rows (fp16 output, log2-sum-exp,
+// Bytes of per-edge records per query: G partial rows (12-bit output codes, log2-sum-exp,
 // scale) and the edge slot, for each (b, g) row's topk entries.
 static size_t fwd_per_query(const AttnShape& s) {
   const int G = s.H_q / s.H_kv;
-  return (size_t)s.batch * s.H_kv * s.topk * ((size_t)G * (kD * 2 + 8) + 8 + 4);
+  return (size_t)s.batch * s.H_kv * s.topk * ((size_t)G * (kD * 3 / 2 + 8) + 8 + 4);
 }
 
 // Workspace layout for query chunks of Qc queries.
@@ -58,9 +58,8 @@ Layout make_fwd_layout(const AttnShape& s, int Qc) {
   L.QT = kSubTilesFwd * 4 * (32 / G);
   L.Qc = Qc;
   size_t o = layout_build(L, s);
-  L.part_lse = o; o = align256(o + (size_t)L.E * G * 4);
-  L.part_sc = o;  o = align256(o + (size_t)L.E * G * 4);
-  L.part_o = o;   o = align256(o + (size_t)L.E * G * kD * 2);
+  L.part_stat = o; o = align256(o + (size_t)L.E * G * 8);
+  L.part_o = o;   o = align256(o + (size_t)L.E * G * kD * 3 / 2);  // 12-bit codes
   L.total = o;
   return L;
 }

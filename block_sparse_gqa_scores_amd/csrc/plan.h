@@ -34,7 +34,7 @@ struct Layout {
   int Qc, QT, n_scan_wg;
   long NB, E, T;
   int W, n_win;
-  size_t counts, cursor, offsets, tile_off, blk_sums, edges, work, part_lse, part_sc, part_o, total;
+  size_t counts, cursor, offsets, tile_off, blk_sums, edges, work, part_stat, part_o, total;
   size_t kl_rec, kl_wsum, lse_t;  // alignment-loss layout only
   int n_kl_wg;
 };

@@ -35,16 +35,42 @@ namespace {
 constexpr int kVStride = kBlock + 4;  // bf16 per row of the transposed V tile
 constexpr long kMergePairRows = 1 << 16;  // from this many rows on, two merge rows per wave
 
-// Record order of one slot's G x D partial outputs.  The MFMA output puts
-// O[hh][d] of a query in lane (row hh, half h) at register 4 * rq + c of tile
-// dt, with d = 32 dt + 8 rq + 4 h + c.  Unit u (4 fp16, 8 bytes) holds
-// c = 0..3 of (dt, rq, hh, h) at u = ((dt * 4 + rq) * G + hh) * 2 + h, so the
-// 2 G lanes of one query write 16 G contiguous bytes per store instruction
-// (a full 128-byte line at G = 8).  Two consecutive units are the 8
-// consecutive d = 32 dt + 8 rq + 0..7 of head hh.
+// Record of one slot: its query's G x D partial outputs O_e / l_e as 12-bit
+// codes (q12_code: each head's row scaled by its own largest magnitude), 1.5
+// bytes a value, plus the row's LSE and scale in part_stat.
+//
+// The MFMA output puts O[hh][d] of a query in lane (row hh, half h) at
+// register v = 4 rq + c of tile dt, with d = 32 dt + 8 rq + 4 h + c.  Piece
+// f = (dt G + hh) 2 + h is the 16 values of one lane's tile, 24 bytes: codes
+// 0..7 and 8..15 packed by q12_pack8 into dwords d0 d1 d2 and d3 d4 d5;
+// d0..d3 go to area A of the record (16 bytes per piece) and d4 d5 to area B
+// (8 bytes per piece).  The 2 G lanes of one query write 32 G contiguous
+// bytes of A and 16 G of B per store instruction.
+template <int G> constexpr int kRecBytes = 8 * G * 24;  // 8 G pieces
+template <int G> constexpr int kRecA = 8 * G * 16;      // area B starts here
+
+__device__ __forceinline__ int piece_of(int G, int dt, int hh, int h) { return (dt * G + hh) * 2 + h; }
+
+// Stores the 16 values x (one lane's tile, row scaled by s) as piece f of the
+// record at rec.
 template <int G>
-__device__ __forceinline__ int record_unit(int dt, int rq, int hh, int h) {
-  return ((dt * 4 + rq) * G + hh) * 2 + h;
+__device__ __forceinline__ void store_piece(u32x4* rec, int f, const f32x16& x, float s) {
+  uint32_t c0[8], c1[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    c0[v] = q12_code(x[v], s);
+    c1[v] = q12_code(x[8 + v], s);
+  }
+  uint32_t a0, a1, a2, a3, b0, b1;
+  q12_pack8(c0, a0, a1, a2);
+  q12_pack8(c1, a3, b0, b1);
+  const u32x4 a = {a0, a1, a2, a3};
+  // The merge reads a record back only after gigabytes of other records, so
+  // caching it would only evict Q rows and K/V tiles that other work still
+  // reads: the stores are non-temporal.
+  __builtin_nontemporal_store(a, rec + f);
+  __builtin_nontemporal_store((uint64_t)b0 | ((uint64_t)b1 << 32),
+                              reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(rec) + kRecA<G>) + f);
 }
 
 __global__ void zero_kernel(int32_t* a, long n) {
@@ -325,14 +351,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
 
   int slot = row_slot(0);
   int i = q_of_slot(slot);
-  u32x4 qb[8];
-  load_q(qb, i);
-  for (int sub = 0; sub < n_here; sub += 4 * QW) {
-    if (sub + wave * QW >= n_here) break;  // wave-uniform
-    // Next sub-tile's Q rows fly while this one computes.
+  // One sub-tile on the Q rows in qb while the next sub-tile's Q rows load
+  // into qn; false when this wave has no rows left (wave-uniform).  The loop
+  // below alternates the two register sets instead of copying qn to qb.
+  auto sub_tile = [&](int sub, const u32x4 (&qb)[8], u32x4 (&qn)[8]) -> bool {
+    if (sub + wave * QW >= n_here) return false;
     const int slot_n = row_slot(sub + 4 * QW);
     const int i_n = q_of_slot(slot_n);
-    u32x4 qn[8];
     load_q(qn, i_n);
     asm volatile("" ::: "memory");
 
@@ -361,9 +386,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
     float mx = neg_inf();
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) mx = max16(mx, sacc[mt]);
-    mx = __builtin_fmaxf(mx, swap_halves(mx));
+    mx = halves_max(mx);
     const float c = p.scale_log2;
     const float bias = -mx * c;
+    // l sums the fp32 weights: the LSE it gives feeds the alignment loss,
+    // whose teacher probabilities need it to a few 1e-6.
     float l = 0.f;
     u32x4 pb[4][2];  // P in bf16, packed as the B operand of O^T = V^T P^T
 #pragma unroll
@@ -375,14 +402,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
         l += e2;
       }
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        pb[mt][qq][0] = pack_bf16x2(sacc[mt][8 * qq + 0], sacc[mt][8 * qq + 1]);
-        pb[mt][qq][1] = pack_bf16x2(sacc[mt][8 * qq + 2], sacc[mt][8 * qq + 3]);
-        pb[mt][qq][2] = pack_bf16x2(sacc[mt][8 * qq + 4], sacc[mt][8 * qq + 5]);
-        pb[mt][qq][3] = pack_bf16x2(sacc[mt][8 * qq + 6], sacc[mt][8 * qq + 7]);
-      }
+      for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2)
+          pb[mt][qq][w2] = pack_bf16x2(sacc[mt][8 * qq + 2 * w2], sacc[mt][8 * qq + 2 * w2 + 1]);
     }
-    l += swap_halves(l);
+    l = halves_sum(l);
 
     f32x16 oacc[4];
 #pragma unroll
@@ -405,31 +430,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) amax = max3abs(oacc[dt][r], oacc[dt][r + 1], amax);
-    amax = __builtin_fmaxf(amax, swap_halves(amax));
+    amax = halves_max(amax);
     {
-      // Non-temporal stores: the merge reads a record back only after
-      // gigabytes of other records (8.6 GB per launch on the 32K workload),
-      // so caching it would only evict Q rows and K/V tiles that other work
-      // items still read (measured: 3.36 -> 3.18 ms on the 32K workload).
-      const float inv = amax > 0.f ? 1.f / amax : 0.f;
-      uint64_t* po = reinterpret_cast<uint64_t*>(p.part_o + (size_t)slot * G * kD);
+      const float s = amax > 0.f ? 2047.f * __builtin_amdgcn_rcpf(amax) : 0.f;
+      u32x4* rec = p.part_o + (size_t)slot * (kRecBytes<G> / 16);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const uint64_t lo = pack_f16x2(oacc[dt][4 * rq + 0] * inv, oacc[dt][4 * rq + 1] * inv);
-          const uint64_t hi = pack_f16x2(oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
-          __builtin_nontemporal_store(lo | (hi << 32), po + record_unit<G>(dt, rq, hh, h));
-        }
+      for (int dt = 0; dt < 4; ++dt) store_piece<G>(rec, piece_of(G, dt, hh, h), oacc[dt], s);
       // Both wave halves hold the same row statistics; both store them.
-      p.part_lse[(size_t)slot * G + hh] = mx * c + __builtin_amdgcn_logf(l);
-      p.part_sc[(size_t)slot * G + hh] = amax / l;
+      p.part_stat[(size_t)slot * G + hh] = f32x2{mx * c + __builtin_amdgcn_logf(l), amax * __builtin_amdgcn_rcpf(2047.f * l)};
     }
     asm volatile("" ::: "memory");
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qb[ks] = qn[ks];
     slot = slot_n;
     i = i_n;
+    return true;
+  };
+  u32x4 q0[8], q1[8];
+  load_q(q0, i);
+  for (int sub = 0;; sub += 8 * QW) {
+    if (!sub_tile(sub, q0, q1)) break;
+    if (!sub_tile(sub + 4 * QW, q1, q0)) break;
   }
 }
 
@@ -547,41 +566,35 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(Params p) {
   __syncthreads();
   amax = __builtin_fmaxf(__builtin_fmaxf(s_a[0][n], s_a[1][n]), __builtin_fmaxf(s_a[2][n], s_a[3][n]));
   if (n < G) {
-    const float inv = amax > 0.f ? 1.f / amax : 0.f;
-    uint2* po = reinterpret_cast<uint2*>(p.part_o + (size_t)slot * G * kD);
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      uint2 v2;
-      v2.x = pack_f16x2(oacc[4 * rq + 0] * inv, oacc[4 * rq + 1] * inv);
-      v2.y = pack_f16x2(oacc[4 * rq + 2] * inv, oacc[4 * rq + 3] * inv);
-      po[record_unit<G>(wave, rq, n, h)] = v2;
-    }
+    const float s = amax > 0.f ? 2047.f * __builtin_amdgcn_rcpf(amax) : 0.f;
+    store_piece<G>(p.part_o + (size_t)slot * (kRecBytes<G> / 16), piece_of(G, wave, n, h), oacc, s);
     if (wave == 0 && h == 0) {
-      p.part_lse[(size_t)slot * G + n] = mx * c + __builtin_amdgcn_logf(l);
-      p.part_sc[(size_t)slot * G + n] = amax / l;
+      p.part_stat[(size_t)slot * G + n] = f32x2{mx * c + __builtin_amdgcn_logf(l), amax * __builtin_amdgcn_rcpf(2047.f * l)};
     }
   }
 }
 
 // Combines the partials of each (query, group): one wave per row.
-// O = sum_e 2^(lse_e - M) sc_e x_e / sum_e 2^(lse_e - M), LSE = M + log2(sum).
-// Every record shares one element order, so the sums run in record order and
-// the order is undone once, when O is written.
+// O = sum_e 2^(lse_e - M) sc_e (y_e - 2048) / sum_e 2^(lse_e - M) over the
+// records' 12-bit codes y_e, LSE = M + log2(sum).  Every record shares one
+// element order, so the sums run in record order and the order is undone
+// once, when O is written.  Lane l reads piece l (+ 64 u) of every record,
+// all of one head, (l / 2) mod G; the offset 2048 is taken off once, as
+// 2048 sum_e 2^(lse_e - M) sc_e.
 //
 // The entries that count form a wave-uniform bit mask (one ballot).  Records
 // are read kBatch at a time with unconditional loads (an entry that does not
 // count reads its own slot, which lies inside the workspace, and is skipped
-// after the load), so a lane keeps kBatch x F 16-byte loads (16 at G <= 8) in
-// flight.
+// after the load), so a lane keeps kBatch x F x 2 loads in flight.
 //
 // Records are read once and the output is written once, both non-temporal,
 // so neither stream displaces what is still to be read (32K workload:
 // 1.85 -> 1.66 ms).
 template <int G>
 __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse, int rows_per_wave) {
-  constexpr int NF = G * kD / 8;            // 16-byte pieces (8 halves) per record
-  constexpr int F = (NF + 63) / 64;         // pieces per lane
-  constexpr int kBatch = F >= 8 ? 2 : (F >= 4 ? 4 : 8);  // records per batch of loads
+  constexpr int NP = 8 * G;                  // pieces per record
+  constexpr int F = (NP + 63) / 64;          // pieces per lane
+  constexpr int kBatch = F >= 4 ? 4 : (F >= 2 ? 8 : 16);  // records per batch of loads
   const int lane = threadIdx.x & 63;
   // rows_per_wave consecutive rows per wave: the next row's loads start while
   // the previous row's output stores drain.
@@ -601,24 +614,31 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse,
     // before any of them is used; the softmax max is kept online, one rescale
     // per batch, so no pass over the statistics precedes the records.
     const int je = lane < p.topk ? sel[lane] : -1;
-    const int hh = lane % G;
-    float M = neg_inf(), L = 0.f, acc[F][8];
+    const int hh = (lane >> 1) % G;
+    float M = neg_inf(), L = 0.f, W = 0.f, acc[F][16];
 #pragma unroll
     for (int u = 0; u < F; ++u)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[u][c] = 0.f;
+      for (int c = 0; c < 16; ++c) acc[u][c] = 0.f;
     unsigned long long valid = 0;
     for (int e0 = 0; e0 < p.topk; e0 += kBatch) {
-      u32x4 x[kBatch][F];
+      u32x4 xa[kBatch][F];
+      uint64_t xb[kBatch][F];
       float lse[kBatch], sc[kBatch];
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
         const long slot = slot0 + min(e0 + k, p.topk - 1);
-        lse[k] = p.part_lse[slot * G + hh];
-        sc[k] = p.part_sc[slot * G + hh];
-        const u32x4* rec = reinterpret_cast<const u32x4*>(p.part_o + (size_t)slot * G * kD);
+        const f32x2 st = p.part_stat[slot * G + hh];
+        lse[k] = st[0];
+        sc[k] = st[1];
+        const u32x4* rec = p.part_o + (size_t)slot * (kRecBytes<G> / 16);
+        const uint64_t* rb = reinterpret_cast<const uint64_t*>(reinterpret_cast<const char*>(rec) + kRecA<G>);
 #pragma unroll
-        for (int u = 0; u < F; ++u) x[k][u] = __builtin_nontemporal_load(rec + min(lane + 64 * u, NF - 1));
+        for (int u = 0; u < F; ++u) {
+          const int f = min(lane + 64 * u, NP - 1);
+          xa[k][u] = __builtin_nontemporal_load(rec + f);
+          xb[k][u] = __builtin_nontemporal_load(rb + f);
+        }
       }
       asm volatile("" ::: "memory");  // keep the loads above together
       if (e0 == 0) valid = __builtin_amdgcn_ballot_w64(je >= 0 && je <= local);
@@ -633,36 +653,47 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse,
       const float alpha = __builtin_amdgcn_exp2f(M - m_new);  // 0 while M = -inf
       M = m_new;
       L *= alpha;
+      W *= alpha;
 #pragma unroll
       for (int u = 0; u < F; ++u)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[u][c] *= alpha;
+        for (int c = 0; c < 16; ++c) acc[u][c] *= alpha;
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
         if (!((bits >> k) & 1u)) continue;  // wave-uniform
         const float wl = __builtin_amdgcn_exp2f(lse[k] - M);
         const float wx = wl * sc[k];
         L += wl;
+        W += wx;
 #pragma unroll
-        for (int u = 0; u < F; ++u)
+        for (int u = 0; u < F; ++u) {
+          float y[8];
+          q12_unpack8(xa[k][u][0], xa[k][u][1], xa[k][u][2], y);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            acc[u][2 * c] += wx * f16_lo(x[k][u][c]);
-            acc[u][2 * c + 1] += wx * f16_hi(x[k][u][c]);
-          }
+          for (int c = 0; c < 8; ++c) acc[u][c] = __builtin_fmaf(wx, y[c], acc[u][c]);
+          q12_unpack8(xa[k][u][3], (uint32_t)xb[k][u], (uint32_t)(xb[k][u] >> 32), y);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[u][8 + c] = __builtin_fmaf(wx, y[c], acc[u][8 + c]);
+        }
       }
     }
     const float inv = 1.f / L;
+    const float off = 2048.f * W;
+    uint16_t* orow = p.out + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD;
 #pragma unroll
     for (int u = 0; u < F; ++u) {
       const int f = lane + 64 * u;
-      if (f >= NF) continue;
-      // 16-byte piece f holds d = 32 dt + 8 rq + 0..7 of head hh, f = (dt * 4 + rq) * G + hh.
-      const int d = (f / G) * 8;
-      const u32x4 o = {pack_bf16x2(acc[u][0] * inv, acc[u][1] * inv), pack_bf16x2(acc[u][2] * inv, acc[u][3] * inv),
-                       pack_bf16x2(acc[u][4] * inv, acc[u][5] * inv), pack_bf16x2(acc[u][6] * inv, acc[u][7] * inv)};
-      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(p.out + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + d));
-      if (with_lse && d == 0)
+      if (f >= NP) continue;
+      // Piece f = (dt G + hh) 2 + h holds d = 32 dt + 8 rq + 4 h + 0..3 at values 4 rq + 0..3.
+      const int dt = (f >> 1) / G, h = f & 1;
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const float* a = &acc[u][4 * rq];
+        const uint64_t o = (uint64_t)pack_bf16x2((a[0] - off) * inv, (a[1] - off) * inv) |
+                           ((uint64_t)pack_bf16x2((a[2] - off) * inv, (a[3] - off) * inv) << 32);
+        __builtin_nontemporal_store(o, reinterpret_cast<uint64_t*>(orow + 32 * dt + 8 * rq + 4 * h));
+      }
+      if (with_lse && dt == 0 && h == 0)
         p.lse[((size_t)b * p.H_q + g * G + hh) * p.S_q + i] =
             (M + __builtin_amdgcn_logf(L)) * 0.69314718055994530942f;
     }
@@ -755,9 +786,8 @@ hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint1
   char* base = static_cast<char*>(ws);
   Params p = base_params(s, L, base, idx);
   p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
-  p.part_lse = reinterpret_cast<float*>(base + L.part_lse);
-  p.part_sc = reinterpret_cast<float*>(base + L.part_sc);
-  p.part_o = reinterpret_cast<uint16_t*>(base + L.part_o);
+  p.part_stat = reinterpret_cast<f32x2*>(base + L.part_stat);
+  p.part_o = reinterpret_cast<u32x4*>(base + L.part_o);
   const bool with_lse = lse != nullptr;
   switch (p.G) {
     case 1: return launch_g<1>(s, L, p, with_lse, stream, events);
