@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace msa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -55,6 +57,16 @@ __device__ __forceinline__ int mfma32_row(int r, int lane) {
 // operand, and a read too early returns the register's previous contents).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+}
+
+// Calls f(std::integral_constant<int, i>) for i = B .. E - 1 in order: a
+// loop whose every index is a compile-time constant.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // Max of the 16 values of an MFMA 32x32 output register block and `m`.

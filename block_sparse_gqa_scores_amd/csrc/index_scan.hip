@@ -291,16 +291,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scan_prefill(ScanArgs a) 
 // keep[0] enters and keep[0] drops out.  Blocks arrive in ascending order,
 // keys are distinct, so the kept set after the last offer is the exact
 // top-(k-1) with ties to the lower index, whatever the offers' order.
-// Calls f(std::integral_constant<int, i>) for i = B .. E - 1 in order: a
-// loop whose every index is a compile-time constant.
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
 // Anchors in the instruction stream (empty statements, no instruction is
 // emitted; statements with side effects keep their order): pin(v) makes v be
 // computed before this point, launder(v) makes whatever uses v after it wait

@@ -361,31 +361,51 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
     load_q(qn, i_n);
     asm volatile("" ::: "memory");
 
+    // The two matrix phases are software pipelines, one MFMA per step with a
+    // scheduling barrier between steps: every operand fragment is read from
+    // LDS three steps ahead into a ring of four, and the vector work of one
+    // 32-key chunk runs two values a step during the next chunk's MFMAs.
     const int t = i + off;
-    f32x16 sacc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int krow = mt * 32 + n;
-      u32x4 ka[8];
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) ka[ks] = ktile[krow * 16 + ((2 * ks + h) ^ (krow & 15))];
-      sacc[mt] = mfma32x32x16(ka[0], qb[0], zero16());
-#pragma unroll
-      for (int ks = 1; ks < 8; ++ks) sacc[mt] = mfma32x32x16(ka[ks], qb[ks], sacc[mt]);
-    }
     // Causal mask only where the block reaches past some row's position (the
     // query's own block); raw scores are ranked, the scale is applied inside
     // the exponent: p = 2^(s * c - m * c) with c = scale * log2(e).
-    if (__builtin_amdgcn_ballot_w64(j * kBlock + kBlock - 1 > t) != 0) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+    // A finished 32-key chunk is masked (one wave-uniform branch) before its
+    // values enter the row max.
+    const bool need_mask = __builtin_amdgcn_ballot_w64(j * kBlock + kBlock - 1 > t) != 0;
+    // Register r of this lane holds key 32 mt + 8 (r / 4) + 4 h + r % 4 of the
+    // block; keys past t - 128 j are masked for this lane's row.
+    const int lim = t - j * kBlock - 4 * h;
+    f32x16 sacc[4];
+    auto mask_chunk = [&](auto MT) {
+      constexpr int mt = decltype(MT)::value;
+      if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (j * kBlock + mt * 32 + mfma32_row(r, lane) > t) sacc[mt][r] = neg_inf();
-    }
+          if (mt * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[mt][r] = neg_inf();
+      }
+    };
     float mx = neg_inf();
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) mx = max16(mx, sacc[mt]);
+    // Values r, r + 1 of chunk mt into the row max.
+    auto max2 = [&](auto MT, auto R) {
+      constexpr int mt = decltype(MT)::value, r = decltype(R)::value;
+      mx = max3f(sacc[mt][r], sacc[mt][r + 1], mx);
+    };
+    // S^T = K Q^T, step st = 8 mt + ks: K rows 32 mt + n, k-step ks.  Row
+    // 32 mt + n keeps its 16-byte chunks swizzled by n & 15.
+    const u32x4* klane = ktile + n * 16;
+    auto kfrag = [&](int st) { return klane[(st >> 3) * 512 + ((2 * (st & 7) + h) ^ (n & 15))]; };
+    u32x4 ring[4];
+    static_for<0, 3>([&](auto P) { ring[P] = kfrag(P); });
+    static_for<0, 32>([&](auto S) {
+      constexpr int st = decltype(S)::value, mt = st / 8, ks = st % 8;
+      if constexpr (st + 3 < 32) ring[(st + 3) % 4] = kfrag(st + 3);
+      sacc[mt] = mfma32x32x16(ring[st % 4], qb[ks], ks == 0 ? zero16() : sacc[mt]);
+      if constexpr (mt >= 1 && ks == 0) mask_chunk(std::integral_constant<int, mt - 1>{});
+      if constexpr (mt >= 1) max2(std::integral_constant<int, mt - 1>{}, std::integral_constant<int, 2 * ks>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    mask_chunk(std::integral_constant<int, 3>{});
+    static_for<0, 8>([&](auto K) { max2(std::integral_constant<int, 3>{}, std::integral_constant<int, 2 * K>{}); });
     mx = halves_max(mx);
     const float c = p.scale_log2;
     const float bias = -mx * c;
@@ -393,38 +413,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
     // whose teacher probabilities need it to a few 1e-6.
     float l = 0.f;
     u32x4 pb[4][2];  // P in bf16, packed as the B operand of O^T = V^T P^T
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][r], c, bias));
-        sacc[mt][r] = e2;
-        l += e2;
-      }
-#pragma unroll
-      for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2)
-          pb[mt][qq][w2] = pack_bf16x2(sacc[mt][8 * qq + 2 * w2], sacc[mt][8 * qq + 2 * w2 + 1]);
-    }
-    l = halves_sum(l);
+    // Weights of values r, r + 1 of chunk mt, packed into pb.
+    auto exp2v = [&](auto MT, auto R) {
+      constexpr int mt = decltype(MT)::value, r = decltype(R)::value;
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][r], c, bias));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][r + 1], c, bias));
+      l += e0;
+      l += e1;
+      pb[mt][r / 8][(r % 8) / 2] = pack_bf16x2(e0, e1);
+    };
+    static_for<0, 8>([&](auto K) { exp2v(std::integral_constant<int, 0>{}, std::integral_constant<int, 2 * K>{}); });
 
+    // O^T = V^T P^T, step st = 8 mt + 4 qq + dt: V^T[d][key] with
+    // d = 32 dt + n, keys 32 mt + 16 qq + 4 h + 0..3 and + 8..11, from one
+    // lane base plus compile-time offsets (in dwords).
     f32x16 oacc[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        const int key0 = mt * 32 + 16 * qq + 4 * h;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int d = dt * 32 + n;
-          const uint2 a0 = *reinterpret_cast<const uint2*>(&vt[(d * kVStride + key0) >> 1]);
-          const uint2 a1 = *reinterpret_cast<const uint2*>(&vt[(d * kVStride + key0 + 8) >> 1]);
-          const u32x4 av = {a0.x, a0.y, a1.x, a1.y};
-          oacc[dt] = (mt == 0 && qq == 0) ? mfma32x32x16(av, pb[mt][qq], zero16())
-                                          : mfma32x32x16(av, pb[mt][qq], oacc[dt]);
-        }
-      }
+    const uint32_t* vlane = vt + n * (kVStride / 2) + 2 * h;
+    auto vfrag = [&](int st) {
+      const uint32_t* va = vlane + (st & 3) * 16 * kVStride + (st >> 3) * 16 + 8 * ((st >> 2) & 1);
+      const uint2 a0 = *reinterpret_cast<const uint2*>(va);
+      const uint2 a1 = *reinterpret_cast<const uint2*>(va + 4);
+      return u32x4{a0.x, a0.y, a1.x, a1.y};
+    };
+    static_for<0, 3>([&](auto P) { ring[P] = vfrag(P); });
+    static_for<0, 32>([&](auto S) {
+      constexpr int st = decltype(S)::value, mt = st / 8, qq = (st / 4) % 2, dt = st % 4;
+      if constexpr (st + 3 < 32) ring[(st + 3) % 4] = vfrag(st + 3);
+      oacc[dt] = mfma32x32x16(ring[st % 4], pb[mt][qq], mt == 0 && qq == 0 ? zero16() : oacc[dt]);
+      if constexpr (mt < 3) exp2v(std::integral_constant<int, mt + 1>{}, std::integral_constant<int, 2 * (st % 8)>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    l = halves_sum(l);
     float amax = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
