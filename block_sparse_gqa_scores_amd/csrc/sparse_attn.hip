@@ -593,6 +593,11 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(Params p) {
   }
 }
 
+// Value of x held by lane l ^ 1 (DPP quad_perm [1, 0, 3, 2]).
+__device__ __forceinline__ float swap_adjacent(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
 // Combines the partials of each (query, group): one wave per row.
 // O = sum_e 2^(lse_e - M) sc_e (y_e - 2048) / sum_e 2^(lse_e - M) over the
 // records' 12-bit codes y_e, LSE = M + log2(sum).  Every record shares one
@@ -702,15 +707,31 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse,
 #pragma unroll
     for (int u = 0; u < F; ++u) {
       const int f = lane + 64 * u;
-      if (f >= NP) continue;
-      // Piece f = (dt G + hh) 2 + h holds d = 32 dt + 8 rq + 4 h + 0..3 at values 4 rq + 0..3.
+      if (f >= NP) continue;  // NP is even: lanes f and f ^ 1 skip together
+      // Piece f = (dt G + hh) 2 + h holds d = 32 dt + 8 rq + 4 h + 0..3 at
+      // values 4 rq + 0..3.  Lanes f and f ^ 1 (h = 0, 1) trade halves so
+      // that lane h writes the 16 consecutive d = 32 dt + 16 h + 0..15 (two
+      // 16-byte stores; whole 64-byte segments per lane pair): h = 0 sends
+      // its rq = 2, 3 values and h = 1 its rq = 0, 1.
       const int dt = (f >> 1) / G, h = f & 1;
+      float v[16], x[8];
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const float* a = &acc[u][4 * rq];
-        const uint64_t o = (uint64_t)pack_bf16x2((a[0] - off) * inv, (a[1] - off) * inv) |
-                           ((uint64_t)pack_bf16x2((a[2] - off) * inv, (a[3] - off) * inv) << 32);
-        __builtin_nontemporal_store(o, reinterpret_cast<uint64_t*>(orow + 32 * dt + 8 * rq + 4 * h));
+      for (int c = 0; c < 16; ++c) v[c] = (acc[u][c] - off) * inv;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = swap_adjacent(h ? v[k] : v[8 + k]);
+      float o[16];  // d = 32 dt + 16 h + 0..15
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        o[k] = h ? x[k] : v[k];
+        o[4 + k] = h ? v[8 + k] : x[k];
+        o[8 + k] = h ? x[4 + k] : v[4 + k];
+        o[12 + k] = h ? v[12 + k] : x[4 + k];
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const u32x4 w4 = {pack_bf16x2(o[8 * q], o[8 * q + 1]), pack_bf16x2(o[8 * q + 2], o[8 * q + 3]),
+                          pack_bf16x2(o[8 * q + 4], o[8 * q + 5]), pack_bf16x2(o[8 * q + 6], o[8 * q + 7])};
+        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(orow + 32 * dt + 16 * h + 8 * q));
       }
       if (with_lse && dt == 0 && h == 0)
         p.lse[((size_t)b * p.H_q + g * G + hh) * p.S_q + i] =
