@@ -334,6 +334,8 @@ TRAFFIC_FILES = {
     ("prefill_32k", "attn_partial"): ("attn_partial_prefill_32k_traffic.txt", ("sparse_attn.hip", "device_common.h")),
     ("chunk_16k_of_1m", "index_scores"): ("index_scan_chunk_16k_of_1m_traffic.txt", ("index_scan.hip", "device_common.h")),
     ("decode_64x256k", "index_scores"): ("index_scan_decode_64x256k_traffic.txt", ("index_scan.hip", "device_common.h")),
+    ("prefill_128k_gain", "attn_partial"): ("attn_partial_prefill_128k_gain_traffic.txt",
+                                            ("sparse_attn.hip", "device_common.h")),
 }
 
 
@@ -386,6 +388,41 @@ def forward_summary(w, timing, stage_ms, chunks):
             "algorithmic_flops": {"index": fi, "attention": fa}, "attn_chunks": chunks,
             "stages": stage_rates(w, stage_ms, chunks), "attention": attention_step(w, stage_ms, chunks),
             "roofline": roofline(w, stage_ms, chunks)}
+
+
+def selection_stats(w, t, tiles=(8, 32, 128)):
+    """Block-level against token-level sparsity of one forward's selection:
+    for query tiles of T consecutive queries of one (b, g), the distinct
+    blocks the tile selects (its union) against its (query, block) edges.
+    eff = edges / (union x T) is the fraction of a query-tile kernel's rows
+    (every query of the tile against every block of the union) that would
+    carry an edge; the edge-bucketed kernels here do work per edge only.
+    Also the mean visible tokens per (query, group) row."""
+    import torch
+
+    import block_sparse_gqa_scores_amd as msa
+
+    _, idx = msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk, return_idx=True)
+    B, H, S, K = idx.shape
+    valid = idx >= 0
+    out = {"edges": int(valid.sum().item()), "rows": B * H * S,
+           "visible_tokens_per_row": float(visible_tokens(w).mean())}
+    for T in tiles:
+        if S % T:
+            continue
+        x = idx.reshape(B * H, S // T, T * K).long()
+        v = x >= 0
+        bm = torch.zeros(B * H, S // T, w.n_blk + 1, dtype=torch.bool, device=x.device)
+        bm.scatter_(2, torch.where(v, x, w.n_blk), True)
+        u = bm[..., :w.n_blk].sum(-1)
+        total_u = float(u.sum().item())
+        out[f"tile{T}"] = {"union_mean": total_u / u.numel(), "union_median": float(u.float().median().item()),
+                           "edges_per_tile": float(v.sum().item()) / u.numel(),
+                           "eff": float(v.sum().item()) / (total_u * T)}
+        del bm, u, x, v
+    del idx
+    torch.cuda.empty_cache()
+    return out
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -457,7 +494,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="chunk_16k_of_1m",
                     help="headline workload (default: the largest single-GPU prefill, 16K queries on a 1M prefix)")
-    ap.add_argument("--secondary", default="prefill_32k,prefill_128k_gain",
+    ap.add_argument("--secondary", default="prefill_32k,prefill_128k_gain,prefill_4k",
                     help="comma-separated forward workloads reported beside the headline ('' for none)")
     ap.add_argument("--legs-workload", default="prefill_32k",
                     help="workload of the alignment-loss, backward and selection-mask legs")
@@ -504,6 +541,7 @@ def main():
         "algorithmic_flops": head["algorithmic_flops"], "stages": head["stages"], "attn_chunks": chunks,
         "attention": head["attention"], "roofline": head["roofline"], "wall_s_timed": timing["wall_s"],
     }
+    res["selection"] = selection_stats(w, t)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
@@ -515,6 +553,7 @@ def main():
         print(f"[bench] secondary workload {name}", file=sys.stderr, flush=True)
         ts, tim_s, st_s, ch_s = run_workload(ws_, args.steps, args.warmup)
         res["workloads"][name] = forward_summary(ws_, tim_s, st_s, ch_s)
+        res["workloads"][name]["selection"] = selection_stats(ws_, ts)
         del ts
         release()
     legs = synth.WORKLOADS[args.legs_workload]
@@ -541,7 +580,8 @@ def main():
                          "ms_per_step_min": tim_d["min"], "algorithmic_bytes": nbytes,
                          "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
                          "tokens/s": wd.batch * wd.seqlen_q / (msd * 1e-3),
-                         "stages": stage_rates(wd, stage_d, chunks_d), "roofline": roofline(wd, stage_d, chunks_d)}
+                         "stages": stage_rates(wd, stage_d, chunks_d), "roofline": roofline(wd, stage_d, chunks_d),
+                         "selection": selection_stats(wd, td, tiles=())}
         del td
         release()
     if not args.no_copy_rate:
