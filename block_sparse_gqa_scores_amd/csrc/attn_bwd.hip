@@ -36,8 +36,8 @@ struct BwdParams {
   const uint16_t* out;   // forward output, same layout
   const float* lse;      // forward LSE [B][H_q][S_q] (natural log)
   float2* stat;          // [B][H_kv][S_q][G]: (LSE in log2 units, sum_d dO O), a query's heads together
-  uint16_t* dq_rec;      // [slot][4][G][32] fp16: the edge's dq / its quarter's scale (rec_dim order)
-  float* dq_sc;          // [slot][4][G]: max |dq| over each quarter of the head dims
+  u32x4* dq_rec;         // [slot][kRecBytes(G)]: the edge's dq as 12-bit codes, piece (quarter G + head) 2 + half
+  float* dq_sc;          // [slot][4][G]: scale of each quarter's codes (dq = (code - 2048) scale)
   long sink;             // record slot written by padding rows (never read)
   uint16_t* dq;          // [B][S_q][H_q][D] bf16
   uint16_t* dk;          // [B][S_k][H_kv][D] bf16
@@ -208,27 +208,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
     f.id = d;
   };
   // The dq records of one sub-tile (rows without an edge, and the dummy
-  // stores of the prologue, write the sink).
+  // stores of the prologue, write the sink): this wave's quarter of the head
+  // dims, a piece per lane, as 12-bit codes scaled by the quarter's largest
+  // magnitude.  Cached stores: non-temporal ones measured 5 % slower here.
   auto store_records = [&](const f32x16& qacc, bool dummy) {
     const int q = n / G, hh = n - (n / G) * G;
     const int sl = dummy ? -1 : s_slot[q];
     const long slot = sl >= 0 ? sl : bp.sink;
     float m = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) m = max3abs(qacc[r], qacc[r], m);
-    m = __builtin_fmaxf(m, swap_halves(m)) * bp.scale;
-    const float inv = m > 0.f ? bp.scale * __builtin_amdgcn_rcpf(m) : 0.f;
-    // 32 contiguous bytes per lane; the slot's quarter is 512 contiguous bytes.
-    u32x4* rec = reinterpret_cast<u32x4*>(bp.dq_rec + ((slot * 4 + wave) * G + hh) * 32 + 16 * h);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x4 v4;
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-        v4[x] = pack_f16x2(qacc[8 * half + 2 * x] * inv, qacc[8 * half + 2 * x + 1] * inv);
-      rec[half] = v4;
-    }
-    bp.dq_sc[(slot * 4 + wave) * G + hh] = m;  // both halves store the same m
+    for (int r = 0; r < 16; r += 2) m = max3abs(qacc[r], qacc[r + 1], m);
+    m = halves_max(m);
+    const float s = m > 0.f ? 2047.f * __builtin_amdgcn_rcpf(m) : 0.f;
+    store_piece<G, false>(bp.dq_rec + slot * (kRecBytes<G> / 16), (wave * G + hh) * 2 + h, qacc, s);
+    bp.dq_sc[(slot * 4 + wave) * G + hh] = m * bp.scale * (1.f / 2047.f);  // both halves store the same value
   };
   // Pipeline, in issue order: sub-tile n stages rows fetched during n - 2,
   // requests the ids of n + 3 and then the rows of n + 2, computes, and
@@ -447,13 +440,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
 }
 
 // dq of each (query, group): the sum of its edges' records.  One wave per
-// row; lane l takes 16-byte pieces l, l + 64, ... of the row's records: piece
-// f is quarter f / (4 G), head (f / 4) % G, positions 8 (f % 4) .. + 7, i.e.
-// two runs of 4 consecutive dims (rec_dim).
+// row; lane l takes piece l (+ 64 u) of every record, i.e. (quarter, head,
+// half) = ((f / 2) / G, (f / 2) % G, f % 2), and adds sc (code - 2048) of its
+// 16 values, the offset taken off once.  All entries of the row are
+// requested together with unconditional loads (an entry that does not count
+// reads its own slot, inside the workspace, and is skipped), 16 at a time.
 template <int G>
 __global__ __launch_bounds__(256) void dq_merge_kernel(BwdParams bp) {
-  constexpr int NF = G * kD / 8;          // 16-byte pieces per record
-  constexpr int F = (NF + 63) / 64;
+  constexpr int NP = 8 * G;          // pieces per record
+  constexpr int F = (NP + 63) / 64;  // pieces per lane
+  constexpr int kBatch = F >= 4 ? 4 : (F >= 2 ? 8 : 16);
   const Params& p = bp.e;
   const int lane = threadIdx.x & 63;
   const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -466,43 +462,50 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdParams bp) {
   const int32_t* sel = p.idx + ((long)bg * p.S_q + i) * p.topk;
   const int local = (i + p.S_k - p.S_q) / kBlock;
   const long slot0 = ((long)bg * p.Qc + il) * p.topk;
-  float acc[F][8];
+  const int je = lane < p.topk ? sel[lane] : -1;
+  const unsigned long long valid = __builtin_amdgcn_ballot_w64(je >= 0 && je <= local);
+  float acc[F][16], W[F];
 #pragma unroll
-  for (int u = 0; u < F; ++u)
+  for (int u = 0; u < F; ++u) {
+    W[u] = 0.f;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) acc[u][x] = 0.f;
-  for (int e = 0; e < p.topk; ++e) {
-    const int jj = sel[e];
-    if (jj < 0 || jj > local) continue;  // uniform
-    const long slot = slot0 + e;
+    for (int c = 0; c < 16; ++c) acc[u][c] = 0.f;
+  }
+  for (int e0 = 0; e0 < p.topk; e0 += kBatch) {
+    u32x4 xa[kBatch][F];
+    uint64_t xb[kBatch][F];
+    float sc[kBatch][F];
 #pragma unroll
-    for (int u = 0; u < F; ++u) {
-      const int f = lane + 64 * u;
-      if (f >= NF) continue;
-      const float sc = bp.dq_sc[slot * 4 * G + f / 4];  // (quarter, head) = f / 4
-      // Each record is read once: a non-temporal load (1 % faster on 32K).
-      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bp.dq_rec + slot * (4 * G * 32) + 8 * f));
+    for (int k = 0; k < kBatch; ++k) {
+      const long slot = slot0 + min(e0 + k, p.topk - 1);
+      const u32x4* rec = bp.dq_rec + slot * (kRecBytes<G> / 16);
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        acc[u][2 * y] += sc * f16_lo(x[y]);
-        acc[u][2 * y + 1] += sc * f16_hi(x[y]);
+      for (int u = 0; u < F; ++u) {
+        const int f = min(lane + 64 * u, NP - 1);
+        load_piece<G>(rec, f, xa[k][u], xb[k][u]);
+        sc[k][u] = bp.dq_sc[slot * 4 * G + (f >> 1)];  // (quarter, head) = f / 2
+      }
+    }
+    const unsigned bits = (unsigned)(valid >> e0) & ((1u << kBatch) - 1u);  // e0 < topk <= 64
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (!((bits >> k) & 1u)) continue;  // wave-uniform
+#pragma unroll
+      for (int u = 0; u < F; ++u) {
+        add_piece(xa[k][u], xb[k][u], sc[k][u], acc[u]);
+        W[u] += sc[k][u];
       }
     }
   }
 #pragma unroll
   for (int u = 0; u < F; ++u) {
     const int f = lane + 64 * u;
-    if (f >= NF) continue;
-    const int quarter = f / (4 * G), hh = (f / 4) % G, pos = 8 * (f % 4);
-    uint16_t* o = bp.dq + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD;
-    // positions pos .. pos + 3 and pos + 4 .. pos + 7 are two runs of 4 dims
-    uint2 lo, hi;
-    lo.x = pack_bf16x2(acc[u][0], acc[u][1]);
-    lo.y = pack_bf16x2(acc[u][2], acc[u][3]);
-    hi.x = pack_bf16x2(acc[u][4], acc[u][5]);
-    hi.y = pack_bf16x2(acc[u][6], acc[u][7]);
-    *reinterpret_cast<uint2*>(o + rec_dim(quarter, pos)) = lo;
-    *reinterpret_cast<uint2*>(o + rec_dim(quarter, pos + 4)) = hi;
+    if (f >= NP) continue;  // NP is even: lanes f and f ^ 1 skip together
+    const int quarter = (f >> 1) / G, hh = (f >> 1) % G, h = f & 1;
+    float v[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) v[c] = acc[u][c] - 2048.f * W[u];
+    store_run32<false>(bp.dq + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + 32 * quarter, h, v);
   }
 }
 
@@ -554,7 +557,7 @@ hipError_t launch_sparse_attn_bwd(const AttnShape& s, const uint16_t* q, const u
   bp.dout = dout; bp.out = out; bp.lse = lse;
   bp.stat = reinterpret_cast<float2*>(base + BL.stat);
   bp.sink = BL.L.E;
-  bp.dq_rec = reinterpret_cast<uint16_t*>(base + BL.dq_rec);
+  bp.dq_rec = reinterpret_cast<u32x4*>(base + BL.dq_rec);
   bp.dq_sc = reinterpret_cast<float*>(base + BL.dq_sc);
   bp.dk_acc = reinterpret_cast<float*>(base + BL.dk_acc);
   bp.dv_acc = reinterpret_cast<float*>(base + BL.dv_acc);

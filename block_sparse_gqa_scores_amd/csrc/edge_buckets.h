@@ -80,6 +80,91 @@ __device__ __forceinline__ int slot_query(const Params& p, int bg, int slot) {
   return p.q0 + slot_row(p, slot) - bg * p.Qc;
 }
 
+// Records of 12-bit codes (q12_code in device_common.h).  A piece is the 16
+// values one lane holds of a 32 x 32 MFMA output tile, its register r at
+// position 8 (r / 4) + 4 h + r % 4 of the tile's 32-row run (h = lane / 32);
+// it takes 24 bytes: codes 0..7 and 8..15 packed by q12_pack8 into dwords
+// d0 d1 d2 and d3 d4 d5, with d0..d3 in area A of the record (16 bytes per
+// piece) and d4 d5 in area B (8 bytes per piece).  A record holds 8 G pieces.
+template <int G> constexpr int kRecBytes = 8 * G * 24;
+template <int G> constexpr int kRecA = 8 * G * 16;  // area B starts here
+
+// Stores the 16 values x, scaled by s, as piece f of the record at rec
+// (non-temporally when NT).
+template <int G, bool NT>
+__device__ __forceinline__ void store_piece(u32x4* rec, int f, const f32x16& x, float s) {
+  uint32_t c0[8], c1[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    c0[v] = q12_code(x[v], s);
+    c1[v] = q12_code(x[8 + v], s);
+  }
+  uint32_t a0, a1, a2, a3, b0, b1;
+  q12_pack8(c0, a0, a1, a2);
+  q12_pack8(c1, a3, b0, b1);
+  const u32x4 a = {a0, a1, a2, a3};
+  const uint64_t bb = (uint64_t)b0 | ((uint64_t)b1 << 32);
+  uint64_t* rb = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(rec) + kRecA<G>) + f;
+  if constexpr (NT) {
+    __builtin_nontemporal_store(a, rec + f);
+    __builtin_nontemporal_store(bb, rb);
+  } else {
+    rec[f] = a;
+    *rb = bb;
+  }
+}
+
+// Piece f of the record at rec (non-temporal loads: a record is read once).
+template <int G>
+__device__ __forceinline__ void load_piece(const u32x4* rec, int f, u32x4& a, uint64_t& b) {
+  a = __builtin_nontemporal_load(rec + f);
+  b = __builtin_nontemporal_load(reinterpret_cast<const uint64_t*>(reinterpret_cast<const char*>(rec) + kRecA<G>) + f);
+}
+
+// acc[v] += w * code v of a loaded piece (the offset 2048 is left in).
+__device__ __forceinline__ void add_piece(const u32x4& a, uint64_t b, float w, float (&acc)[16]) {
+  float y[8];
+  q12_unpack8(a[0], a[1], a[2], y);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = __builtin_fmaf(w, y[c], acc[c]);
+  q12_unpack8(a[3], (uint32_t)b, (uint32_t)(b >> 32), y);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[8 + c] = __builtin_fmaf(w, y[c], acc[8 + c]);
+}
+
+// Value of x held by lane l ^ 1 (DPP quad_perm [1, 0, 3, 2]).
+__device__ __forceinline__ float swap_adjacent(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
+// Writes a piece's 16 values, as bf16, into the 32-value run `row` (the values
+// at positions 8 (c / 4) + 4 h + c % 4).  Lanes l and l ^ 1, holding h = 0 and
+// h = 1 of the same run, trade halves so that lane h writes positions
+// 16 h .. 16 h + 15 as two 16-byte stores: whole 64-byte segments per lane
+// pair.  Both lanes of a pair must be active.
+template <bool NT>
+__device__ __forceinline__ void store_run32(uint16_t* row, int h, const float (&v)[16]) {
+  float x[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] = swap_adjacent(h ? v[k] : v[8 + k]);
+  float o[16];  // positions 16 h + 0..15
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[k] = h ? x[k] : v[k];
+    o[4 + k] = h ? v[8 + k] : x[k];
+    o[8 + k] = h ? x[4 + k] : v[4 + k];
+    o[12 + k] = h ? v[12 + k] : x[4 + k];
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const u32x4 w4 = {pack_bf16x2(o[8 * q], o[8 * q + 1]), pack_bf16x2(o[8 * q + 2], o[8 * q + 3]),
+                      pack_bf16x2(o[8 * q + 4], o[8 * q + 5]), pack_bf16x2(o[8 * q + 6], o[8 * q + 7])};
+    u32x4* dst = reinterpret_cast<u32x4*>(row + 16 * h + 8 * q);
+    if constexpr (NT) __builtin_nontemporal_store(w4, dst);
+    else *dst = w4;
+  }
+}
+
 // Gradient records of the backward kernels: per slot, quarters of 32 dims
 // (x heads) of 32 values each, in the order a transposed MFMA tile holds
 // them: position p = 16 h + r for MFMA register r of lane half h, which is

@@ -85,7 +85,7 @@ int sparse_attn_chunks(const AttnShape& s, size_t ws_bytes) {
 // (G x D fp16 values and 4 scales per head) and edge slots.
 static size_t bwd_per_query(const AttnShape& s) {
   const int G = s.H_q / s.H_kv;
-  return (size_t)s.batch * s.H_kv * s.topk * ((size_t)G * (kD * 2 + 16) + 4);
+  return (size_t)s.batch * s.H_kv * s.topk * ((size_t)G * (kD * 3 / 2 + 16) + 4);
 }
 
 // Workspace layout for query chunks of Qc queries; with more than one chunk
@@ -100,7 +100,7 @@ BwdLayout make_bwd_layout(const AttnShape& s, int Qc) {
   B.chunks = (s.S_q + L.Qc - 1) / L.Qc;
   B.stat = o;   o = align256(o + (size_t)s.batch * s.H_q * s.S_q * 8);
   // One record past the chunk's edges takes the stores of padding rows.
-  B.dq_rec = o; o = align256(o + (size_t)(L.E + 1) * G * kD * 2);
+  B.dq_rec = o; o = align256(o + (size_t)(L.E + 1) * G * kD * 3 / 2);  // 12-bit codes
   B.dq_sc = o;  o = align256(o + (size_t)(L.E + 1) * G * 16);
   const size_t kv = (size_t)s.batch * s.S_k * s.H_kv * kD * 4;
   B.dk_acc = o; o = align256(o + (B.chunks > 1 ? kv : 0));

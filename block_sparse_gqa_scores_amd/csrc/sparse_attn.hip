@@ -46,32 +46,7 @@ constexpr long kMergePairRows = 1 << 16;  // from this many rows on, two merge r
 // d0..d3 go to area A of the record (16 bytes per piece) and d4 d5 to area B
 // (8 bytes per piece).  The 2 G lanes of one query write 32 G contiguous
 // bytes of A and 16 G of B per store instruction.
-template <int G> constexpr int kRecBytes = 8 * G * 24;  // 8 G pieces
-template <int G> constexpr int kRecA = 8 * G * 16;      // area B starts here
-
 __device__ __forceinline__ int piece_of(int G, int dt, int hh, int h) { return (dt * G + hh) * 2 + h; }
-
-// Stores the 16 values x (one lane's tile, row scaled by s) as piece f of the
-// record at rec.
-template <int G>
-__device__ __forceinline__ void store_piece(u32x4* rec, int f, const f32x16& x, float s) {
-  uint32_t c0[8], c1[8];
-#pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    c0[v] = q12_code(x[v], s);
-    c1[v] = q12_code(x[8 + v], s);
-  }
-  uint32_t a0, a1, a2, a3, b0, b1;
-  q12_pack8(c0, a0, a1, a2);
-  q12_pack8(c1, a3, b0, b1);
-  const u32x4 a = {a0, a1, a2, a3};
-  // The merge reads a record back only after gigabytes of other records, so
-  // caching it would only evict Q rows and K/V tiles that other work still
-  // reads: the stores are non-temporal.
-  __builtin_nontemporal_store(a, rec + f);
-  __builtin_nontemporal_store((uint64_t)b0 | ((uint64_t)b1 << 32),
-                              reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(rec) + kRecA<G>) + f);
-}
 
 __global__ void zero_kernel(int32_t* a, long n) {
   for (long x = (long)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (long)gridDim.x * blockDim.x)
@@ -454,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
       const float s = amax > 0.f ? 2047.f * __builtin_amdgcn_rcpf(amax) : 0.f;
       u32x4* rec = p.part_o + (size_t)slot * (kRecBytes<G> / 16);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) store_piece<G>(rec, piece_of(G, dt, hh, h), oacc[dt], s);
+      for (int dt = 0; dt < 4; ++dt) store_piece<G, true>(rec, piece_of(G, dt, hh, h), oacc[dt], s);
       // Both wave halves hold the same row statistics; both store them.
       p.part_stat[(size_t)slot * G + hh] = f32x2{mx * c + __builtin_amdgcn_logf(l), amax * __builtin_amdgcn_rcpf(2047.f * l)};
     }
@@ -586,16 +561,11 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(Params p) {
   amax = __builtin_fmaxf(__builtin_fmaxf(s_a[0][n], s_a[1][n]), __builtin_fmaxf(s_a[2][n], s_a[3][n]));
   if (n < G) {
     const float s = amax > 0.f ? 2047.f * __builtin_amdgcn_rcpf(amax) : 0.f;
-    store_piece<G>(p.part_o + (size_t)slot * (kRecBytes<G> / 16), piece_of(G, wave, n, h), oacc, s);
+    store_piece<G, true>(p.part_o + (size_t)slot * (kRecBytes<G> / 16), piece_of(G, wave, n, h), oacc, s);
     if (wave == 0 && h == 0) {
       p.part_stat[(size_t)slot * G + n] = f32x2{mx * c + __builtin_amdgcn_logf(l), amax * __builtin_amdgcn_rcpf(2047.f * l)};
     }
   }
-}
-
-// Value of x held by lane l ^ 1 (DPP quad_perm [1, 0, 3, 2]).
-__device__ __forceinline__ float swap_adjacent(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
 }
 
 // Combines the partials of each (query, group): one wave per row.
@@ -656,13 +626,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse,
         lse[k] = st[0];
         sc[k] = st[1];
         const u32x4* rec = p.part_o + (size_t)slot * (kRecBytes<G> / 16);
-        const uint64_t* rb = reinterpret_cast<const uint64_t*>(reinterpret_cast<const char*>(rec) + kRecA<G>);
 #pragma unroll
-        for (int u = 0; u < F; ++u) {
-          const int f = min(lane + 64 * u, NP - 1);
-          xa[k][u] = __builtin_nontemporal_load(rec + f);
-          xb[k][u] = __builtin_nontemporal_load(rb + f);
-        }
+        for (int u = 0; u < F; ++u) load_piece<G>(rec, min(lane + 64 * u, NP - 1), xa[k][u], xb[k][u]);
       }
       asm volatile("" ::: "memory");  // keep the loads above together
       if (e0 == 0) valid = __builtin_amdgcn_ballot_w64(je >= 0 && je <= local);
@@ -690,15 +655,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse,
         L += wl;
         W += wx;
 #pragma unroll
-        for (int u = 0; u < F; ++u) {
-          float y[8];
-          q12_unpack8(xa[k][u][0], xa[k][u][1], xa[k][u][2], y);
-#pragma unroll
-          for (int c = 0; c < 8; ++c) acc[u][c] = __builtin_fmaf(wx, y[c], acc[u][c]);
-          q12_unpack8(xa[k][u][3], (uint32_t)xb[k][u], (uint32_t)(xb[k][u] >> 32), y);
-#pragma unroll
-          for (int c = 0; c < 8; ++c) acc[u][8 + c] = __builtin_fmaf(wx, y[c], acc[u][8 + c]);
-        }
+        for (int u = 0; u < F; ++u) add_piece(xa[k][u], xb[k][u], wx, acc[u]);
       }
     }
     const float inv = 1.f / L;
@@ -714,25 +671,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse,
       // 16-byte stores; whole 64-byte segments per lane pair): h = 0 sends
       // its rq = 2, 3 values and h = 1 its rq = 0, 1.
       const int dt = (f >> 1) / G, h = f & 1;
-      float v[16], x[8];
+      float v[16];
 #pragma unroll
       for (int c = 0; c < 16; ++c) v[c] = (acc[u][c] - off) * inv;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) x[k] = swap_adjacent(h ? v[k] : v[8 + k]);
-      float o[16];  // d = 32 dt + 16 h + 0..15
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        o[k] = h ? x[k] : v[k];
-        o[4 + k] = h ? v[8 + k] : x[k];
-        o[8 + k] = h ? x[4 + k] : v[4 + k];
-        o[12 + k] = h ? v[12 + k] : x[4 + k];
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const u32x4 w4 = {pack_bf16x2(o[8 * q], o[8 * q + 1]), pack_bf16x2(o[8 * q + 2], o[8 * q + 3]),
-                          pack_bf16x2(o[8 * q + 4], o[8 * q + 5]), pack_bf16x2(o[8 * q + 6], o[8 * q + 7])};
-        __builtin_nontemporal_store(w4, reinterpret_cast<u32x4*>(orow + 32 * dt + 16 * h + 8 * q));
-      }
+      store_run32<true>(orow + 32 * dt, h, v);
       if (with_lse && dt == 0 && h == 0)
         p.lse[((size_t)b * p.H_q + g * G + hh) * p.S_q + i] =
             (M + __builtin_amdgcn_logf(L)) * 0.69314718055994530942f;

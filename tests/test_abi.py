@@ -142,7 +142,7 @@ def test_bwd_entry_checks():
     need = msa.msa_workspace_min_bytes(d, msa.ENTRY_SPARSE_ATTN_BWD)
     rows = d.batch * d.num_heads_kv * d.seqlen_q
     G = d.num_heads_q // d.num_heads_kv
-    assert full >= rows * d.topk * G * (2 * 128 + 16)
+    assert full >= rows * d.topk * G * (128 * 3 // 2 + 16)  # 12-bit dq record + scales per edge and head
     assert 0 < need <= full
     assert bwd(d, nbytes=need - 1) == 5
     # the main branch only: index_dim does not matter (the workspace check is reached)
