@@ -213,12 +213,13 @@ def alignment_loss_rate(w, t, steps):
 
 def backward_rates(w, t, steps):
     """The backward on the forward's selection (next to the forward, not part
-    of its step): msa_sparse_attn_bwd (dq, dk, dv from a seeded dO) and
-    msa_kl_loss_bwd (gradients of the alignment loss into q_idx, k_idx).
-    Algorithmic FLOPs per call: the main branch recomputes S and forms dP,
-    dV, dK and dq, five products of 2 D H_q sum|T_i| each; the loss backward
-    recomputes the main logits (2 D H_q sum|T_i|) and forms z, dk_idx and
-    dq_idx (2 D_idx H_kv sum|T_i| each)."""
+    of its step): msa_sparse_attn_bwd (dq, dk, dv from a seeded dO),
+    msa_kl_loss_bwd (gradients of the alignment loss into q_idx, k_idx) and
+    msa_backward (both in one pass).  Algorithmic FLOPs per call: the main
+    branch recomputes S and forms dP, dV, dK and dq, five products of
+    2 D H_q sum|T_i| each; the loss backward recomputes the main logits
+    (2 D H_q sum|T_i|) and forms z, dk_idx and dq_idx (2 D_idx H_kv sum|T_i|
+    each); the fused pass forms S once for both."""
     import torch
 
     import block_sparse_gqa_scores_amd as msa
@@ -232,15 +233,21 @@ def backward_rates(w, t, steps):
     _, lse_idx = msa.msa_kl_loss_fwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, return_lse_idx=True)
     d = msa.dims_of(t["q"], t["k"], t["q_idx"], t["k_idx"], topk=w.topk)
     ws = torch.empty(max(msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_BWD),
-                         msa.msa_workspace_bytes(d, msa.ENTRY_KL_LOSS_BWD)), dtype=torch.uint8, device=lse.device)
+                         msa.msa_workspace_bytes(d, msa.ENTRY_KL_LOSS_BWD),
+                         msa.msa_workspace_bytes(d, msa.ENTRY_BACKWARD)), dtype=torch.uint8, device=lse.device)
     tok = w.batch * float(visible_tokens(w).sum())
+    main_fl = 5 * 2.0 * w.head_dim * w.heads_q * tok
+    loss_fl = 2.0 * w.head_dim * w.heads_q * tok + 3 * 2.0 * w.index_dim * w.heads_kv * tok
     legs = {
         "sparse_attn_bwd": (lambda: msa.msa_sparse_attn_bwd(t["q"], t["k"], t["v"], idx, out, lse, dout,
                                                              workspace=ws),
-                            5 * 2.0 * w.head_dim * w.heads_q * tok),
+                            main_fl),
         "kl_loss_bwd": (lambda: msa.msa_kl_loss_bwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, lse_idx,
                                                      1.0, workspace=ws),
-                        2.0 * w.head_dim * w.heads_q * tok + 3 * 2.0 * w.index_dim * w.heads_kv * tok),
+                        loss_fl),
+        "fused": (lambda: msa.msa_backward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], idx, out, lse, lse_idx,
+                                           dout, 1.0, workspace=ws),
+                  main_fl + loss_fl - 2.0 * w.head_dim * w.heads_q * tok),
     }
     res = {"workload": w.name}
     for name, (fn, fl) in legs.items():

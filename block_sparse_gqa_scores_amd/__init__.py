@@ -19,11 +19,11 @@ MSA_OK = 0
 STATUS_NAMES = {0: "MSA_OK", 1: "MSA_ERR_NULL_PTR", 2: "MSA_ERR_INVALID_DIMS", 3: "MSA_ERR_UNSUPPORTED",
                 4: "MSA_ERR_MISALIGNED", 5: "MSA_ERR_WORKSPACE_TOO_SMALL", 6: "MSA_ERR_HIP"}
 ENTRY_INDEX_SCORES, ENTRY_BLOCK_TOPK, ENTRY_SPARSE_ATTN_FWD, ENTRY_FORWARD, ENTRY_KL_LOSS_FWD = 0, 1, 2, 3, 4
-ENTRY_SPARSE_ATTN_BWD, ENTRY_KL_LOSS_BWD = 5, 6
+ENTRY_SPARSE_ATTN_BWD, ENTRY_KL_LOSS_BWD, ENTRY_BACKWARD = 5, 6, 7
 EXPORTED = ("msa_index_scores", "msa_block_topk", "msa_sparse_attn_fwd", "msa_forward",
             "msa_forward_profiled", "msa_attn_chunks", "msa_workspace_bytes", "msa_workspace_min_bytes",
             "msa_status_str", "msa_block_mask", "msa_mask_blocks", "msa_kl_loss_fwd", "msa_sparse_attn_bwd",
-            "msa_kl_loss_bwd", "msa_forward_noalloc")
+            "msa_kl_loss_bwd", "msa_forward_noalloc", "msa_backward")
 NOALLOC_SCRATCH_BYTES = 256 << 20  # MSA_NOALLOC_SCRATCH_BYTES of msa.h
 # Stages of msa_forward_profiled: the index scores and the Top-k once, then the
 # three attention stages once per query chunk.
@@ -84,9 +84,11 @@ def lib():
         L.msa_kl_loss_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_kl_loss_bwd.argtypes = [D, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
         L.msa_sparse_attn_bwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P,
+                                   ctypes.c_size_t, P]
         for f in (L.msa_index_scores, L.msa_block_topk, L.msa_sparse_attn_fwd, L.msa_forward,
                   L.msa_forward_profiled, L.msa_block_mask, L.msa_mask_blocks, L.msa_kl_loss_fwd,
-                  L.msa_sparse_attn_bwd, L.msa_kl_loss_bwd, L.msa_forward_noalloc):
+                  L.msa_sparse_attn_bwd, L.msa_kl_loss_bwd, L.msa_forward_noalloc, L.msa_backward):
             f.restype = ctypes.c_int
         L.msa_attn_chunks.argtypes = [D, ctypes.c_int, ctypes.c_size_t]
         L.msa_attn_chunks.restype = ctypes.c_int
@@ -431,6 +433,33 @@ def msa_sparse_attn_bwd(q, k, v, block_idx, out, lse, dout, *, block_size=128, s
                                    _stream(dev))
     _check(rc, "msa_sparse_attn_bwd")
     return dq, dk, dv
+
+
+def msa_backward(q, k, v, q_idx, k_idx, block_idx, out, lse, lse_idx, dout, grad_loss=1.0, *, block_size=128,
+                 softmax_scale=0.0, dq=None, dk=None, dv=None, dq_idx=None, dk_idx=None, workspace=None):
+    """Both backward passes in one (the fused backward): returns (dq, dk, dv,
+    dq_idx, dk_idx), bf16, equal to msa_sparse_attn_bwd's and
+    msa_kl_loss_bwd's outputs."""
+    import torch
+    _rank("block_idx", block_idx, 4)
+    d = dims_of(q, k, q_idx, k_idx, topk=block_idx.shape[-1], block_size=block_size,
+                softmax_scale=softmax_scale)
+    dev = q.device
+    _main_inputs(d, dev, q=q, k=k, v=v, q_idx=q_idx, k_idx=k_idx, out=out, dout=dout)
+    _selection(d, dev, block_idx)
+    _lse(d, dev, "lse", lse)
+    _expect("lse_idx", lse_idx, torch.float32, (d.batch, d.num_heads_kv, d.seqlen_q), dev)
+    dq = _out("dq", dq, torch.bfloat16, tuple(q.shape), dev)
+    dk = _out("dk", dk, torch.bfloat16, tuple(k.shape), dev)
+    dv = _out("dv", dv, torch.bfloat16, tuple(v.shape), dev)
+    dq_idx = _out("dq_idx", dq_idx, torch.bfloat16, tuple(q_idx.shape), dev)
+    dk_idx = _out("dk_idx", dk_idx, torch.bfloat16, tuple(k_idx.shape), dev)
+    ws, nbytes = _workspace(d, ENTRY_BACKWARD, workspace, dev)
+    rc = lib().msa_backward(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx),
+                            _ptr(out), _ptr(lse), _ptr(lse_idx), _ptr(dout), float(grad_loss), _ptr(dq), _ptr(dk),
+                            _ptr(dv), _ptr(dq_idx), _ptr(dk_idx), _ptr(ws), nbytes, _stream(dev))
+    _check(rc, "msa_backward")
+    return dq, dk, dv, dq_idx, dk_idx
 
 
 def msa_kl_loss_bwd(q, k, q_idx, k_idx, block_idx, lse, lse_idx, grad_loss=1.0, *, block_size=128,

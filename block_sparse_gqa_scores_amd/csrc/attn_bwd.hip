@@ -21,7 +21,7 @@
 // edge needs all 128 keys: dS goes through LDS and each wave then forms a
 // quarter of the head dims, written as a per-edge fp16 record; a merge adds a
 // query's records.
-#include "edge_buckets.h"
+#include "bwd_common.h"
 
 namespace msa {
 using namespace edges;
@@ -30,23 +30,6 @@ namespace {
 constexpr int kSStride = kBlock + 8;  // bf16 per row of dS [row][key]
 constexpr int kSortSmall = 1024;      // buckets up to this size sort in a small workgroup
 
-struct BwdParams {
-  Params e;              // edge buckets, q, k, v, idx and shapes of the chunk
-  const uint16_t* dout;  // [B][S_q][H_q][D] bf16
-  const uint16_t* out;   // forward output, same layout
-  const float* lse;      // forward LSE [B][H_q][S_q] (natural log)
-  float2* stat;          // [B][H_kv][S_q][G]: (LSE in log2 units, sum_d dO O), a query's heads together
-  u32x4* dq_rec;         // [slot][kRecBytes(G)]: the edge's dq as 12-bit codes, piece (quarter G + head) 2 + half
-  float* dq_sc;          // [slot][4][G]: scale of each quarter's codes (dq = (code - 2048) scale)
-  long sink;             // record slot written by padding rows (never read)
-  uint16_t* dq;          // [B][S_q][H_q][D] bf16
-  uint16_t* dk;          // [B][S_k][H_kv][D] bf16
-  uint16_t* dv;
-  float* dk_acc;         // fp32 sums of earlier chunks (several chunks only)
-  float* dv_acc;
-  float scale;           // softmax scale
-  int first, last;       // this chunk is the first / the last
-};
 
 // Delta = sum_d dO O per (b, h, i): 16 lanes per row, one 16-byte chunk each.
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams bp) {
@@ -107,9 +90,21 @@ __global__ __launch_bounds__(256) void bucket_sort_kernel(Params p) {
   for (int x = threadIdx.x; x < n; x += 256) e[x] = v[x];
 }
 
-template <int G>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
+// DIDX = 0: the main branch alone.  DIDX = D_idx: the fused pass, which also
+// forms the alignment loss's gradients (kl_bwd.hip states them) from the same
+// S, P, staged Q rows and edge walk: the teacher is the head mean of P, z and
+// g = coef (P_idx - teacher) are formed per sub-tile, dk_idx accumulates per
+// group in registers and dq_idx leaves per-edge records, in the loss
+// backward's formats and orders (so both gradients equal the separate
+// passes' bit for bit).
+template <int G, int DIDX>
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlBwdParams kp) {
   constexpr int QW = 32 / G;                // queries per sub-tile
+  constexpr bool KL = DIDX > 0;
+  constexpr int ICH = KL ? DIDX / 8 : 1;    // 16-byte chunks per index row
+  constexpr int NDT = KL ? DIDX / 32 : 1;   // 32-dim tiles of the index dims
+  constexpr int RPS = G >= 8 ? G / 2 : G;   // registers of one query in a lane
+  constexpr int NL = 16 / RPS;              // queries per lane
   const Params& p = bp.e;
   __shared__ u32x4 ktile[kBlock * 16];      // K_j [key][16 chunks], swizzled
   __shared__ u32x4 vtile[kBlock * 16];      // V_j, same
@@ -119,6 +114,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
   __shared__ __align__(16) float2 s_stat[32];  // (LSE log2, delta) of each row
   __shared__ int s_t[QW];                   // position of each query (-1: no edge)
   __shared__ int s_slot[QW];
+  // Fused pass only: k_idx of the block, the rows' index queries, g, and each
+  // query's index-score LSE.
+  __shared__ u32x4 itile[KL ? kBlock * ICH : 1];  // chunk c at c ^ (key & (ICH - 1))
+  __shared__ u32x4 sqi[KL ? 32 * ICH : 1];        // chunk c at c ^ (rsw(row) & (ICH - 1))
+  __shared__ __align__(16) uint16_t sg[KL ? 32 * kGStride : 8];  // g [row][key] bf16
+  __shared__ float s_lsez[KL ? QW : 1];
 
   const int BG = p.B * p.H_kv;
   const int j = blockIdx.x / BG;            // early (busier) blocks first
@@ -135,6 +136,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
   f32x16 dk_acc[4], dv_acc[4];  // [key row][d tile]: this wave's 32 keys x 128 dims
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) dk_acc[dt] = dv_acc[dt] = zero16();
+  f32x16 ki_acc[NDT];  // fused pass: dk_idx of this wave's keys [key row][index-dim tile]
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) ki_acc[dt] = zero16();
+  const float invG = 1.f / G;
 
   const int key0 = 32 * wave;          // this wave's keys within the block
   const int key_abs = j * kBlock + key0 + n;
@@ -190,6 +195,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
     u32x4 qa[2], da[2];
     float2 st;
     Ids id;
+    u32x4 qi[2];  // fused pass: the rows' index-query chunks (cc % ICH)
+    float lsez;   // fused pass: the row's query's index-score LSE
   };
   auto fetch = [&](const Ids& d, Fetched& f) {
 #pragma unroll
@@ -199,11 +206,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
       const size_t rowoff = (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + 8 * cc;
       f.qa[y] = *reinterpret_cast<const u32x4*>(p.q + rowoff);
       f.da[y] = *reinterpret_cast<const u32x4*>(bp.dout + rowoff);
+      if constexpr (KL)
+        f.qi[y] = *reinterpret_cast<const u32x4*>(p.q_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX +
+                                                  8 * (cc % ICH));
     }
     if (tid < 32) {  // (loading it in every thread costs registers)
       const int hh = tid % G;
       const int i = slot_query(p, bg, d.e2);
       f.st = bp.stat[((size_t)bg * p.S_q + i) * G + hh];
+      if constexpr (KL) f.lsez = kp.lse_idx[((size_t)b * p.H_kv + g) * p.S_q + i];
     }
     f.id = d;
   };
@@ -222,6 +233,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
     const float s = m > 0.f ? 2047.f * __builtin_amdgcn_rcpf(m) : 0.f;
     store_piece<G, false>(bp.dq_rec + slot * (kRecBytes<G> / 16), (wave * G + hh) * 2 + h, qacc, s);
     bp.dq_sc[(slot * 4 + wave) * G + hh] = m * bp.scale * (1.f / 2047.f);  // both halves store the same value
+  };
+  // Fused pass: the dq_idx record of each query of a sub-tile, as the loss
+  // backward writes it, by the lanes of the query's first row (the other
+  // rows hold the same values); every other lane writes the sink.
+  auto store_kl_records = [&](const f32x16& qacc, bool dummy) {
+    const int q = n / G, hh = n - (n / G) * G;
+    const int sl = dummy ? -1 : s_slot[q];
+    const long slot = hh == 0 && sl >= 0 ? sl : kp.sink;
+    float m = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m = max3abs(qacc[r], qacc[r], m);
+    m = __builtin_fmaxf(m, swap_halves(m));
+    const float inv = m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
+    u32x4* rec = reinterpret_cast<u32x4*>(kp.rec + (slot * NDT + wave) * 32 + 16 * h);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x4 v4;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        v4[x] = pack_f16x2(qacc[8 * half + 2 * x] * inv, qacc[8 * half + 2 * x + 1] * inv);
+      rec[half] = v4;
+    }
+    kp.rec_sc[slot * NDT + wave] = m;  // both halves store the same m
   };
   // Pipeline, in issue order: sub-tile n stages rows fetched during n - 2,
   // requests the ids of n + 3 and then the rows of n + 2, computes, and
@@ -245,10 +279,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
       ktile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * cc);
       vtile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(vb + (size_t)s * row_stride + 8 * cc);
     }
+    if constexpr (KL) {
+      const uint16_t* ib = p.k_idx + (size_t)b * p.S_k * DIDX;
+#pragma unroll
+      for (int it = 0; it < kBlock * ICH / kThreads; ++it) {
+        const int qd = it * kThreads + tid;
+        const int row = qd / ICH, cc = qd % ICH;
+        const int s = min(j * kBlock + row, p.S_k - 1);
+        itile[row * ICH + (cc ^ (row & (ICH - 1)))] = *reinterpret_cast<const u32x4*>(ib + (size_t)s * DIDX + 8 * cc);
+      }
+    }
   };
   bool h0 = next(cur), h1 = false, h2 = false;
   const bool any = h0;   // some edge of this chunk selects the block
   if (h0) load_tiles();  // uniform
+  // Fused pass: whether this group's dk_idx part of the block already holds
+  // an earlier chunk's sums; read before the loop's barriers, written after.
+  const long flag_at = (long)bg * p.n_blk + j;
+  bool had = false;
+  if constexpr (KL) had = !kp.first && kp.dk_flag[flag_at] != 0;
   Fetched fx, fy;
   Ids ids;
   if (h0) {
@@ -258,15 +307,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
     load_ids(cur, ids);
     fetch(i0, fx);
     store_records(zero16(), true);
+    if constexpr (KL) if (wave < NDT) store_kl_records(zero16(), true);
     h2 = h1 && next(cur);
     Ids i2;
     load_ids(cur, i2);
     fetch(ids, fy);
     ids = i2;
     store_records(zero16(), true);
+    if constexpr (KL) if (wave < NDT) store_kl_records(zero16(), true);
   }
 
-  auto step = [&](Fetched& f) {
+  auto step = [&](Fetched& f_) {
+    Fetched& f = f_;
+    // The fused pass holds three sets of accumulators: there the lane
+    // coordinates are re-derived from an opaque copy each sub-tile, so the
+    // compiler recomputes the LDS addresses built from them instead of
+    // keeping them all live across the loop.
+    int tid_l = tid;
+    if constexpr (KL) asm volatile("" : "+v"(tid_l));
+    const int lane = tid_l & 63, h = lane >> 5, n = lane & 31;
+    const int key_abs = j * kBlock + key0 + n;
     __syncthreads();  // the previous sub-tile's LDS reads are done
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
@@ -274,6 +334,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
       const u32x4 z = {0u, 0u, 0u, 0u};
       sq[r * 16 + (cc ^ rsw(r))] = f.qa[y];
       sdo[r * 16 + (cc ^ rsw(r))] = (f.id.valid >> (y % NI)) & 1 ? f.da[y] : z;
+      if constexpr (KL)
+        if (cc < ICH) sqi[r * ICH + (cc ^ (rsw(r) & (ICH - 1)))] = f.qi[y];
     }
     if (tid < 32) {
       const int x = f.id.e2;
@@ -282,6 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
       if (tid % G == 0) {
         s_t[tid / G] = valid ? slot_query(p, bg, x) + off : -1;
         s_slot[tid / G] = valid ? x : -1;
+        if constexpr (KL) s_lsez[tid / G] = valid ? f.lsez * kLog2e : __builtin_inff();
       }
     }
     __syncthreads();
@@ -322,6 +385,82 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
         const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse4[r]));
         pv[r] = vis ? e2 : 0.f;
         dsv[r] = pv[r] * (pacc[r] - del4[r]);
+      }
+      if constexpr (KL) {
+        // z of query slot l at key key0 + n.  With G >= 8 a sub-tile has at
+        // most 4 queries: 16x16x32 tiles whose A row m is query m % 4 (the
+        // last one repeated past QW), keys key0 .. + 15 and key0 + 16 .. + 31;
+        // lane n takes the tile holding its key, and register l is query l.
+        // Otherwise z repeats each query's index row on its heads' rows.
+        float zv[NL];
+        if constexpr (G >= 8) {
+          const int qr = min(lane & 3, QW - 1) * G;  // a row of query qr / G in sqi
+          const int k0 = key0 + (lane & 15), k1 = k0 + 16;
+          f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < DIDX / 32; ++ks) {
+            const int ch = 4 * ks + (lane >> 4);
+            const u32x4 a = sqi[qr * ICH + (ch ^ (rsw(qr) & (ICH - 1)))];
+            z0 = mfma16x16x32(a, itile[k0 * ICH + (ch ^ (k0 & (ICH - 1)))], z0);
+            z1 = mfma16x16x32(a, itile[k1 * ICH + (ch ^ (k1 & (ICH - 1)))], z1);
+          }
+          const bool upper = (lane >> 4) & 1;
+#pragma unroll
+          for (int l = 0; l < NL; ++l) zv[l] = upper ? z1[l] : z0[l];
+        } else {
+          f32x16 zacc = zero16();
+#pragma unroll
+          for (int ks = 0; ks < DIDX / 16; ++ks) {
+            const int ch = 2 * ks + h;
+            zacc = mfma32x32x16(sqi[n * ICH + (ch ^ (rsw(n) & (ICH - 1)))],
+                                itile[krow * ICH + (ch ^ (krow & (ICH - 1)))], zacc);
+          }
+#pragma unroll
+          for (int l = 0; l < NL; ++l) zv[l] = zacc[l * RPS];
+        }
+        // g per (query slot l, key): the teacher is the mean of P over the
+        // query's heads (an in-lane sum, and the other half's heads for G >= 8).
+        float gq[NL];
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+          float acc = 0.f;
+#pragma unroll
+          for (int rr = 0; rr < RPS; ++rr) acc += pv[l * RPS + rr];
+          if constexpr (G >= 8) acc += swap_halves(acc);
+          const int q = mfma32_row(l * RPS, lane) / G;
+          const bool vis = key_abs <= s_t[q];
+          const float pidx = __builtin_amdgcn_exp2f(__builtin_fmaf(zv[l], kLog2e, -s_lsez[q]));
+          gq[l] = vis ? kp.coef * (pidx - acc * invG) : 0.f;
+        }
+        // dk_idx += g^T q_idx: A = g of each register's row (its query's
+        // value on each of its G rows, times 1/G), B = the rows' index rows,
+        // transposed.
+        {
+          const int lr = lane & 15;
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            u32x4 ga;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              const int r0 = 8 * kk + 2 * x;
+              ga[x] = pack_bf16x2(gq[r0 / RPS] * invG, gq[(r0 + 1) / RPS] * invG);
+            }
+            const int rbase = 16 * kk + 4 * h;
+            const int ra = rbase + (lr >> 2), rb = rbase + 8 + (lr >> 2);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+              const int c0 = 32 * dt + 16 * (n >> 4) + 4 * (lr & 3);
+              const uint2 b0 = lds_read_tr16(reinterpret_cast<const char*>(sqi) + lds_tile_off<ICH>(ra, c0, rsw(ra) & (ICH - 1)));
+              const uint2 b1 = lds_read_tr16(reinterpret_cast<const char*>(sqi) + lds_tile_off<ICH>(rb, c0, rsw(rb) & (ICH - 1)));
+              const u32x4 bb = {b0.x, b0.y, b1.x, b1.y};
+              ki_acc[dt] = mfma32x32x16(ga, bb, ki_acc[dt]);
+            }
+          }
+        }
+        // g to LDS as [row][key] for dq_idx (each row carries its query's g).
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sg[mfma32_row(r, lane) * kGStride + key0 + n] = (uint16_t)(pack_bf16x2(gq[r / RPS], 0.f) & 0xFFFFu);
       }
       // dV += P^T dO and dK += dS^T Q: A = this lane's P / dS (row = key,
       // k = the 8 rows of registers 8 kk .. 8 kk + 7), B = dO^T / Q^T rows of
@@ -383,6 +522,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
         qacc = mfma32x32x16(ka, sb, qacc);
       }
       store_records(qacc, false);
+      // Fused pass: dq_idx^T[c'][row] = sum_key k_idx^T[c'][key] g[row][key]
+      // for index dims 32 wave .. 32 wave + 31 (waves past D_idx / 32 idle).
+      if constexpr (KL) {
+        if (wave < NDT) {
+          f32x16 iacc = zero16();
+          const int lr = lane & 15;
+          const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
+            const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k0, c0, k0 & (ICH - 1)));
+            const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k1, c0, k1 & (ICH - 1)));
+            const u32x4 ka = {a0.x, a0.y, a1.x, a1.y};
+            const u32x4 gb = *reinterpret_cast<const u32x4*>(&sg[n * kGStride + 16 * ks + 8 * h]);
+            iacc = mfma32x32x16(ka, gb, iacc);
+          }
+          store_kl_records(iacc, false);
+        }
+      }
   };
   while (h0) {  // uniform
     bool hb = h2;
@@ -394,6 +552,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
     step(fy);
     h0 = h1;
     h1 = hb;
+  }
+
+  // Fused pass: this group's dk_idx for the wave's keys (fp32, summed over
+  // chunks), as the loss backward stores it, and the block's flag.
+  if constexpr (KL) {
+    if (any) {  // uniform
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int dcol = 32 * dt + n;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j * kBlock + key0 + mfma32_row(r, lane);
+          if (key >= p.S_k) continue;
+          float* o = kp.dk_part + (((size_t)b * p.H_kv + g) * p.S_k + key) * DIDX + dcol;
+          *o = had ? *o + ki_acc[dt][r] : ki_acc[dt][r];
+        }
+      }
+    }
+    if (tid == 0 && (kp.first || any)) kp.dk_flag[flag_at] = had || any;
   }
 
   // A block that no edge of the chunk selects adds nothing: in a middle chunk
@@ -531,7 +708,8 @@ hipError_t launch_bwd_g(const AttnShape& s, const BwdLayout& BL, BwdParams bp, h
     bp.last = q0 + L.Qc >= s.S_q;
     launch_build(s, L, bp.e, st);
     launch_bucket_sort(L, bp.e, st);
-    hipLaunchKernelGGL(attn_bwd_kernel<G>, dim3((unsigned)(s.batch * s.H_kv * s.n_blk)), dim3(kThreads), 0, st, bp);
+    hipLaunchKernelGGL((attn_bwd_kernel<G, 0>), dim3((unsigned)(s.batch * s.H_kv * s.n_blk)), dim3(kThreads), 0, st, bp,
+                       KlBwdParams{});
     const long mrows = (long)s.batch * s.H_kv * L.Qc;
     hipLaunchKernelGGL(dq_merge_kernel<G>, dim3((unsigned)((mrows + 3) / 4)), dim3(256), 0, st, bp);
     const hipError_t err = hipGetLastError();
@@ -540,7 +718,84 @@ hipError_t launch_bwd_g(const AttnShape& s, const BwdLayout& BL, BwdParams bp, h
   return hipSuccess;
 }
 
+template <int G, int DIDX>
+hipError_t launch_fused_g(const AttnShape& s, const FusedBwdLayout& FL, BwdParams bp, KlBwdParams kp,
+                          hipStream_t st) {
+  const Layout& L = FL.B.L;
+  const long rows = (long)s.batch * s.S_q * s.H_q;
+  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, st, bp);
+  for (int q0 = 0, ci = 0; q0 < s.S_q; q0 += L.Qc, ++ci) {
+    bp.e.q0 = q0;
+    bp.first = ci == 0;
+    bp.last = q0 + L.Qc >= s.S_q;
+    kp.first = ci == 0;
+    launch_build(s, L, bp.e, st);
+    launch_bucket_sort(L, bp.e, st);
+    kp.e = bp.e;
+    hipLaunchKernelGGL((attn_bwd_kernel<G, DIDX>), dim3((unsigned)(s.batch * s.H_kv * s.n_blk)), dim3(kThreads), 0,
+                       st, bp, kp);
+    const long mrows = (long)s.batch * s.H_kv * L.Qc;
+    hipLaunchKernelGGL(dq_merge_kernel<G>, dim3((unsigned)((mrows + 3) / 4)), dim3(256), 0, st, bp);
+    const hipError_t err = launch_kl_dq_merge(kp, DIDX, mrows, st);
+    if (err != hipSuccess) return err;
+  }
+  return launch_kl_dk_reduce(kp, DIDX, (long)s.batch * s.n_blk, st);
+}
+
+template <int DIDX>
+hipError_t launch_fused_d(const AttnShape& s, const FusedBwdLayout& FL, const BwdParams& bp,
+                          const KlBwdParams& kp, hipStream_t st) {
+  switch (bp.e.G) {
+    case 1: return launch_fused_g<1, DIDX>(s, FL, bp, kp, st);
+    case 2: return launch_fused_g<2, DIDX>(s, FL, bp, kp, st);
+    case 4: return launch_fused_g<4, DIDX>(s, FL, bp, kp, st);
+    case 8: return launch_fused_g<8, DIDX>(s, FL, bp, kp, st);
+    case 16: return launch_fused_g<16, DIDX>(s, FL, bp, kp, st);
+    case 32: return launch_fused_g<32, DIDX>(s, FL, bp, kp, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_backward(const AttnShape& s, int D_idx, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const uint16_t* q_idx, const uint16_t* k_idx,
+                           const int32_t* idx, const uint16_t* out, const float* lse,
+                           const float* lse_idx, const uint16_t* dout, float coef, uint16_t* dq,
+                           uint16_t* dk, uint16_t* dv, uint16_t* dq_idx, uint16_t* dk_idx, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  const int qc = fused_bwd_chunk(s, D_idx, ws_bytes);
+  if (qc <= 0) return hipErrorInvalidValue;
+  const FusedBwdLayout FL = make_fused_bwd_layout(s, D_idx, qc);
+  const BwdLayout& BL = FL.B;
+  char* base = static_cast<char*>(ws);
+  BwdParams bp{};
+  bp.e = base_params(s, BL.L, base, idx);
+  bp.e.q = q; bp.e.k = k; bp.e.v = v; bp.e.q_idx = q_idx; bp.e.k_idx = k_idx;
+  bp.dout = dout; bp.out = out; bp.lse = lse;
+  bp.stat = reinterpret_cast<float2*>(base + BL.stat);
+  bp.sink = BL.L.E;
+  bp.dq_rec = reinterpret_cast<u32x4*>(base + BL.dq_rec);
+  bp.dq_sc = reinterpret_cast<float*>(base + BL.dq_sc);
+  bp.dk_acc = reinterpret_cast<float*>(base + BL.dk_acc);
+  bp.dv_acc = reinterpret_cast<float*>(base + BL.dv_acc);
+  bp.dq = dq; bp.dk = dk; bp.dv = dv;
+  bp.scale = s.scale;
+  KlBwdParams kp{};
+  kp.e = bp.e;
+  kp.lse_idx = lse_idx; kp.coef = coef;
+  kp.rec = reinterpret_cast<uint16_t*>(base + FL.rec);
+  kp.rec_sc = reinterpret_cast<float*>(base + FL.rec_sc);
+  kp.sink = BL.L.E;
+  kp.dk_part = reinterpret_cast<float*>(base + FL.dk_part);
+  kp.dk_flag = reinterpret_cast<int32_t*>(base + FL.dk_flag);
+  kp.dq_idx = dq_idx; kp.dk_idx = dk_idx; kp.D_idx = D_idx;
+  switch (D_idx) {
+    case 64: return launch_fused_d<64>(s, FL, bp, kp, stream);
+    case 128: return launch_fused_d<128>(s, FL, bp, kp, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_sparse_attn_bwd(const AttnShape& s, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const int32_t* idx, const uint16_t* out,

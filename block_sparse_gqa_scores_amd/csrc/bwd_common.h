@@ -1,0 +1,52 @@
+// Parameters shared by the backward kernels: the main branch's
+// (attn_bwd.hip), the alignment loss's (kl_bwd.hip), and the fused pass that
+// computes both gradients over one walk of the edges (attn_bwd.hip).
+#pragma once
+
+#include "edge_buckets.h"
+
+namespace msa {
+namespace edges {
+
+constexpr int kGStride = kBlock + 8;  // bf16 per row of the loss backward's g tile [row][key]
+
+struct BwdParams {
+  Params e;              // edge buckets, q, k, v, idx and shapes of the chunk
+  const uint16_t* dout;  // [B][S_q][H_q][D] bf16
+  const uint16_t* out;   // forward output, same layout
+  const float* lse;      // forward LSE [B][H_q][S_q] (natural log)
+  float2* stat;          // [B][H_kv][S_q][G]: (LSE in log2 units, sum_d dO O), a query's heads together
+  u32x4* dq_rec;         // [slot][kRecBytes(G)]: the edge's dq as 12-bit codes, piece (quarter G + head) 2 + half
+  float* dq_sc;          // [slot][4][G]: scale of each quarter's codes (dq = (code - 2048) scale)
+  long sink;             // record slot written by padding rows (never read)
+  uint16_t* dq;          // [B][S_q][H_q][D] bf16
+  uint16_t* dk;          // [B][S_k][H_kv][D] bf16
+  uint16_t* dv;
+  float* dk_acc;         // fp32 sums of earlier chunks (several chunks only)
+  float* dv_acc;
+  float scale;           // softmax scale
+  int first, last;       // this chunk is the first / the last
+};
+
+struct KlBwdParams {
+  Params e;
+  const float* lse_idx;  // [B][H_kv][S_q]: log-sum-exp of z over T (natural log)
+  float coef;            // gradient of the loss / (B * S_q * H_kv)
+  uint16_t* rec;         // [slot][D_idx / 32][32] fp16 (rec_dim order) / scale
+  float* rec_sc;         // [slot][D_idx / 32]
+  long sink;             // record slot written by padding rows (never read)
+  float* dk_part;        // [B][H_kv][S_k][D_idx] fp32, per group
+  int32_t* dk_flag;      // [B][H_kv][n_blk]: 1 if the group's dk_part rows of the block hold data
+  uint16_t* dq_idx;      // [B][S_q][H_kv][D_idx] bf16
+  uint16_t* dk_idx;      // [B][S_k][D_idx] bf16
+  int D_idx;
+  int first;             // this chunk is the first (dk_part is stored, not added)
+};
+
+// The loss backward's per-row dq_idx merge (rows of the chunk at p.q0) and
+// its per-group dk_idx reduce, for D_idx = 64 or 128 (kl_bwd.hip).
+hipError_t launch_kl_dq_merge(const KlBwdParams& kp, int D_idx, long rows, hipStream_t st);
+hipError_t launch_kl_dk_reduce(const KlBwdParams& kp, int D_idx, long blocks, hipStream_t st);
+
+}  // namespace edges
+}  // namespace msa

@@ -79,6 +79,17 @@ hipError_t launch_kl_loss_bwd(const AttnShape& s, int D_idx, const uint16_t* q, 
                               const float* lse, const float* lse_idx, float coef, uint16_t* dq_idx,
                               uint16_t* dk_idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
+// Both backward passes over one walk of the edges (the fused backward).
+size_t backward_workspace(const AttnShape& s, int D_idx);
+size_t backward_workspace_min(const AttnShape& s, int D_idx);
+int backward_chunks(const AttnShape& s, int D_idx, size_t ws_bytes);
+hipError_t launch_backward(const AttnShape& s, int D_idx, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const uint16_t* q_idx, const uint16_t* k_idx,
+                           const int32_t* idx, const uint16_t* out, const float* lse,
+                           const float* lse_idx, const uint16_t* dout, float coef, uint16_t* dq,
+                           uint16_t* dk, uint16_t* dv, uint16_t* dq_idx, uint16_t* dk_idx, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
 // The host checks msa_forward makes before anything else (dims, then the
 // pointers' presence and alignment); MSA_OK for an empty problem as well.
 msa_status forward_checks(const msa_dims* d, const void* q, const void* k, const void* v,

@@ -22,28 +22,13 @@
 // a fixed order at the end, since all groups share one index key head);
 // dq_idx of each edge goes through LDS and a per-edge fp16 record, added per
 // row by a merge.
-#include "edge_buckets.h"
+#include "bwd_common.h"
 
 namespace msa {
 using namespace edges;
 namespace {
 
-constexpr int kGStride = kBlock + 8;  // bf16 per row of the g tile [row][key]
 
-struct KlBwdParams {
-  Params e;
-  const float* lse_idx;  // [B][H_kv][S_q]: log-sum-exp of z over T (natural log)
-  float coef;            // gradient of the loss / (B * S_q * H_kv)
-  uint16_t* rec;         // [slot][D_idx / 32][32] fp16 (rec_dim order) / scale
-  float* rec_sc;         // [slot][D_idx / 32]
-  long sink;             // record slot written by padding rows (never read)
-  float* dk_part;        // [B][H_kv][S_k][D_idx] fp32, per group
-  int32_t* dk_flag;      // [B][H_kv][n_blk]: 1 if the group's dk_part rows of the block hold data
-  uint16_t* dq_idx;      // [B][S_q][H_kv][D_idx] bf16
-  uint16_t* dk_idx;      // [B][S_k][D_idx] bf16
-  int D_idx;
-  int first;             // this chunk is the first (dk_part is stored, not added)
-};
 
 template <int G, int DIDX>
 __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
@@ -462,6 +447,25 @@ __global__ __launch_bounds__(256) void kl_dk_reduce_kernel(KlBwdParams kp) {
     *reinterpret_cast<uint2*>(kp.dk_idx + (size_t)b * p.S_k * DIDX + row0 + 4 * x) = o;
   }
 }
+
+}  // namespace
+
+namespace edges {
+hipError_t launch_kl_dq_merge(const KlBwdParams& kp, int D_idx, long rows, hipStream_t st) {
+  const dim3 grid((unsigned)((rows * 16 + 255) / 256));
+  if (D_idx == 64) hipLaunchKernelGGL(kl_dq_merge_kernel<64>, grid, dim3(256), 0, st, kp);
+  else hipLaunchKernelGGL(kl_dq_merge_kernel<128>, grid, dim3(256), 0, st, kp);
+  return hipGetLastError();
+}
+
+hipError_t launch_kl_dk_reduce(const KlBwdParams& kp, int D_idx, long blocks, hipStream_t st) {
+  if (D_idx == 64) hipLaunchKernelGGL(kl_dk_reduce_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, kp);
+  else hipLaunchKernelGGL(kl_dk_reduce_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, st, kp);
+  return hipGetLastError();
+}
+}  // namespace edges
+
+namespace {
 
 template <int G, int DIDX>
 hipError_t launch_kl_bwd_g(const AttnShape& s, const KlBwdLayout& K, KlBwdParams kp, hipStream_t st) {

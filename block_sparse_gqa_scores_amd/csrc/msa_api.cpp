@@ -116,6 +116,11 @@ size_t workspace_of(const msa_dims* d, int entry, bool min) {
       if (is_empty(*d)) return 0;
       return min ? msa::kl_loss_bwd_workspace_min(attn_shape(*d), d->index_dim)
                  : msa::kl_loss_bwd_workspace(attn_shape(*d), d->index_dim);
+    case MSA_ENTRY_BACKWARD:
+      if (check_dims(d, true, true) != MSA_OK) return bad;
+      if (is_empty(*d)) return 0;
+      return min ? msa::backward_workspace_min(attn_shape(*d), d->index_dim)
+                 : msa::backward_workspace(attn_shape(*d), d->index_dim);
     default:
       return bad;
   }
@@ -173,6 +178,8 @@ int msa_attn_chunks(const msa_dims* d, int entry, size_t ws_bytes) {
       return msa::sparse_attn_bwd_chunks(s, ws_bytes);
     case MSA_ENTRY_KL_LOSS_BWD:
       return msa::kl_loss_bwd_chunks(s, d->index_dim, ws_bytes);
+    case MSA_ENTRY_BACKWARD:
+      return msa::backward_chunks(s, d->index_dim, ws_bytes);
     default:
       return 0;
   }
@@ -305,6 +312,47 @@ msa_status msa_kl_loss_bwd(const msa_dims* d, const void* q, const void* k, cons
       static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx), block_idx, lse,
       lse_idx, coef, static_cast<uint16_t*>(dq_idx), static_cast<uint16_t*>(dk_idx), ws, ws_bytes,
       strm));
+}
+
+msa_status msa_backward(const msa_dims* d, const void* q, const void* k, const void* v,
+                        const void* q_idx, const void* k_idx, const int32_t* block_idx,
+                        const void* out, const float* lse, const float* lse_idx,
+                        const void* dout, float grad_loss, void* dq, void* dk, void* dv,
+                        void* dq_idx, void* dk_idx, void* ws, size_t ws_bytes, void* stream) {
+  msa_status st = check_dims(d, true, true);
+  if (st != MSA_OK) return st;
+  if (!std::isfinite(grad_loss)) return MSA_ERR_INVALID_DIMS;
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  if (is_empty(*d)) {  // no query: zero key gradients
+    if (d->batch == 0 || d->seqlen_k == 0) return MSA_OK;
+    if (!dk || !dv || !dk_idx) return MSA_ERR_NULL_PTR;
+    if (!aligned16(dk) || !aligned16(dv) || !aligned16(dk_idx)) return MSA_ERR_MISALIGNED;
+    const long n = long(d->batch) * d->seqlen_k * d->num_heads_kv * d->head_dim / 2;
+    if (msa::launch_fill_zero(static_cast<float*>(dk), n, strm) != hipSuccess) return MSA_ERR_HIP;
+    if (msa::launch_fill_zero(static_cast<float*>(dv), n, strm) != hipSuccess) return MSA_ERR_HIP;
+    const long ni = long(d->batch) * d->seqlen_k * d->index_dim / 2;
+    return from_hip(msa::launch_fill_zero(static_cast<float*>(dk_idx), ni, strm));
+  }
+  if (!q || !k || !v || !q_idx || !k_idx || !block_idx || !out || !lse || !lse_idx || !dout || !dq ||
+      !dk || !dv || !dq_idx || !dk_idx)
+    return MSA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_idx) || !aligned16(k_idx) ||
+      !aligned16(block_idx) || !aligned16(out) || !aligned16(lse) || !aligned16(lse_idx) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dq_idx) ||
+      !aligned16(dk_idx))
+    return MSA_ERR_MISALIGNED;
+  const msa::AttnShape s = attn_shape(*d);
+  const size_t need = msa::backward_workspace_min(s, d->index_dim);
+  if (!ws || ws_bytes < need) return ws ? MSA_ERR_WORKSPACE_TOO_SMALL : MSA_ERR_NULL_PTR;
+  if (!aligned16(ws)) return MSA_ERR_MISALIGNED;
+  const float coef = float(double(grad_loss) / (double(d->batch) * d->seqlen_q * d->num_heads_kv));
+  return from_hip(msa::launch_backward(
+      s, d->index_dim, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(q_idx),
+      static_cast<const uint16_t*>(k_idx), block_idx, static_cast<const uint16_t*>(out), lse, lse_idx,
+      static_cast<const uint16_t*>(dout), coef, static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk),
+      static_cast<uint16_t*>(dv), static_cast<uint16_t*>(dq_idx), static_cast<uint16_t*>(dk_idx), ws,
+      ws_bytes, strm));
 }
 
 msa_status msa_kl_loss_fwd(const msa_dims* d, const void* q, const void* k, const void* q_idx,

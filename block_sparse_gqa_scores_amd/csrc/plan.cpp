@@ -131,6 +131,48 @@ int sparse_attn_bwd_chunks(const AttnShape& s, size_t ws_bytes) {
   return qc > 0 ? (s.S_q + qc - 1) / qc : 0;
 }
 
+// ---------------------------------------------------------------- fused backward
+static size_t kl_bwd_per_query(const AttnShape& s, int D_idx);
+
+// Bytes of per-edge records per query: the main backward's and the loss
+// backward's (the edge slot once).
+static size_t fused_bwd_per_query(const AttnShape& s, int D_idx) {
+  return bwd_per_query(s) + kl_bwd_per_query(s, D_idx) - (size_t)s.batch * s.H_kv * s.topk * 4;
+}
+
+FusedBwdLayout make_fused_bwd_layout(const AttnShape& s, int D_idx, int Qc) {
+  FusedBwdLayout F{};
+  F.B = make_bwd_layout(s, Qc);
+  const edges::Layout& L = F.B.L;
+  size_t o = F.B.total;
+  // One record past the chunk's edges takes the stores of padding rows.
+  F.rec = o;     o = align256(o + (size_t)(L.E + 1) * D_idx * 2);
+  F.rec_sc = o;  o = align256(o + (size_t)(L.E + 1) * (D_idx / 32) * 4);
+  F.dk_part = o; o = align256(o + (size_t)s.batch * s.H_kv * s.S_k * D_idx * 4);
+  F.dk_flag = o; o = align256(o + (size_t)s.batch * s.H_kv * s.n_blk * 4);
+  F.total = o;
+  return F;
+}
+
+int fused_bwd_chunk(const AttnShape& s, int D_idx, size_t ws_bytes) {
+  return fit_chunk(default_chunk(s.S_q, fused_bwd_per_query(s, D_idx)), ws_bytes,
+                   [&](int qc) { return make_fused_bwd_layout(s, D_idx, qc).total; });
+}
+
+size_t backward_workspace(const AttnShape& s, int D_idx) {
+  return make_fused_bwd_layout(s, D_idx, default_chunk(s.S_q, fused_bwd_per_query(s, D_idx))).total;
+}
+
+size_t backward_workspace_min(const AttnShape& s, int D_idx) {
+  return std::min(make_fused_bwd_layout(s, D_idx, 1).total,
+                  make_fused_bwd_layout(s, D_idx, default_chunk(s.S_q, fused_bwd_per_query(s, D_idx))).total);
+}
+
+int backward_chunks(const AttnShape& s, int D_idx, size_t ws_bytes) {
+  const int qc = fused_bwd_chunk(s, D_idx, ws_bytes);
+  return qc > 0 ? (s.S_q + qc - 1) / qc : 0;
+}
+
 // ---------------------------------------------------------------- alignment loss
 // The alignment loss keeps 32 bytes per edge, so one chunk covers all queries.
 Layout make_kl_layout(const AttnShape& s) {

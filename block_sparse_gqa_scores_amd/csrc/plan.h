@@ -106,6 +106,16 @@ struct KlBwdLayout {
 KlBwdLayout make_kl_bwd_layout(const AttnShape& s, int D_idx, int Qc);
 int kl_bwd_chunk(const AttnShape& s, int D_idx, size_t ws_bytes);
 
+// Fused backward (both gradients over one walk of the edges): the main
+// backward's layout, then the loss backward's dq_idx records, per-group fp32
+// dk_idx parts and their flags.
+struct FusedBwdLayout {
+  BwdLayout B;
+  size_t rec, rec_sc, dk_part, dk_flag, total;
+};
+FusedBwdLayout make_fused_bwd_layout(const AttnShape& s, int D_idx, int Qc);
+int fused_bwd_chunk(const AttnShape& s, int D_idx, size_t ws_bytes);
+
 // Alignment-loss forward: one chunk (32 bytes of records per edge).
 edges::Layout make_kl_layout(const AttnShape& s);
 

@@ -96,7 +96,8 @@ typedef enum msa_entry {
   MSA_ENTRY_FORWARD = 3,
   MSA_ENTRY_KL_LOSS_FWD = 4,
   MSA_ENTRY_SPARSE_ATTN_BWD = 5,
-  MSA_ENTRY_KL_LOSS_BWD = 6
+  MSA_ENTRY_KL_LOSS_BWD = 6,
+  MSA_ENTRY_BACKWARD = 7
 } msa_entry;
 
 /*
@@ -323,6 +324,30 @@ msa_status msa_kl_loss_bwd(const msa_dims* dims, const void* q, const void* k,
                            const int32_t* block_idx, const float* lse,
                            const float* lse_idx, float grad_loss, void* dq_idx,
                            void* dk_idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The fused backward: msa_sparse_attn_bwd and msa_kl_loss_bwd in one pass
+ * over the selected blocks (the MSA kernel notes fuse the proxy backward with
+ * the main backward because the proxy's signal needs both probability sets
+ * at once, The Architecture of Infinity, baystreetwire.com; Sparse Attention
+ * Part II, section 3.2 for the loss).  One walk of the edges forms S = Q K^T
+ * and P once for both: dq, dk, dv as msa_sparse_attn_bwd defines them, and
+ * dq_idx, dk_idx (the gradient of grad_loss * loss) as msa_kl_loss_bwd does.
+ * Inputs: q, k, v, q_idx, k_idx, block_idx as msa_forward; out and lse as the
+ * forward returned them; lse_idx as msa_kl_loss_fwd wrote it for the same
+ * selection; dout [B][S_q][H_q][D] bf16.  Outputs bf16, written in full:
+ * dq like q, dk and dv like k and v, dq_idx like q_idx, dk_idx like k_idx;
+ * each equals the separate entry point's output bit for bit at the same
+ * ws_bytes (same arithmetic, same summation orders).  `ws` holds at least
+ * msa_workspace_min_bytes(dims, MSA_ENTRY_BACKWARD) bytes (both passes'
+ * per-edge records); contents on entry do not matter.  Errors as the two
+ * separate calls.
+ */
+msa_status msa_backward(const msa_dims* dims, const void* q, const void* k, const void* v,
+                        const void* q_idx, const void* k_idx, const int32_t* block_idx,
+                        const void* out, const float* lse, const float* lse_idx,
+                        const void* dout, float grad_loss, void* dq, void* dk, void* dv,
+                        void* dq_idx, void* dk_idx, void* ws, size_t ws_bytes, void* stream);
 
 /* Internal stages of msa_forward, in launch order (for msa_forward_profiled). */
 typedef enum msa_stage {

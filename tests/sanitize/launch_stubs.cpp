@@ -40,6 +40,10 @@ hipError_t launch_sparse_attn_bwd(const AttnShape&, const uint16_t*, const uint1
 hipError_t launch_kl_loss_bwd(const AttnShape&, int, const uint16_t*, const uint16_t*, const uint16_t*,
                               const uint16_t*, const int32_t*, const float*, const float*, float, uint16_t*,
                               uint16_t*, void*, size_t, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
+hipError_t launch_backward(const AttnShape&, int, const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,
+                           const uint16_t*, const int32_t*, const uint16_t*, const float*, const float*,
+                           const uint16_t*, float, uint16_t*, uint16_t*, uint16_t*, uint16_t*, uint16_t*, void*,
+                           size_t, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 hipError_t launch_fill_zero(float*, long, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 hipError_t launch_kl_loss(const AttnShape&, int, const uint16_t*, const uint16_t*, const uint16_t*,
                           const uint16_t*, const int32_t*, const float*, float*, float*, float*, void*, size_t,

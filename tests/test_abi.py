@@ -169,6 +169,37 @@ def test_kl_bwd_entry_checks():
                dki=NULL, ws=NULL, nbytes=0) == 0
 
 
+def fb(d, q=A, k=A, v=A, qi=A, ki=A, idx=A, out=A, lse=A, lsei=A, do=A, grad=1.0, dq=A, dk=A, dv=A, dqi=A, dki=A,
+       ws=A, nbytes=1 << 40):
+    return msa.lib().msa_backward(None if d is None else ctypes.byref(d), q, k, v, qi, ki, idx, out, lse, lsei, do,
+                                  grad, dq, dk, dv, dqi, dki, ws, nbytes, None)
+
+
+def test_fused_bwd_entry_checks():
+    d = dims()
+    assert fb(None) == 1
+    for kw in ("q", "k", "v", "qi", "ki", "idx", "out", "lse", "lsei", "do", "dq", "dk", "dv", "dqi", "dki"):
+        assert fb(d, **{kw: NULL}) == 1, kw
+        assert fb(d, **{kw: MIS}) == 4, kw
+    assert fb(d, ws=NULL, nbytes=0) == 1 and fb(d, ws=MIS) == 4
+    assert fb(d, grad=float("inf")) == 2
+    full = msa.msa_workspace_bytes(d, msa.ENTRY_BACKWARD)
+    need = msa.msa_workspace_min_bytes(d, msa.ENTRY_BACKWARD)
+    # both passes' records: at least the two separate entry points' smallest workspaces' records
+    assert full >= msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_BWD)
+    assert full >= msa.msa_workspace_bytes(d, msa.ENTRY_KL_LOSS_BWD)
+    assert 0 < need <= full
+    assert fb(d, nbytes=need - 1) == 5
+    assert msa.msa_attn_chunks(d, msa.ENTRY_BACKWARD, full) == 1
+    assert msa.msa_attn_chunks(d, msa.ENTRY_BACKWARD, need) >= 1
+    assert msa.msa_attn_chunks(d, msa.ENTRY_BACKWARD, need - 1) == 0
+    for kw, status in ((dict(index_dim=96), 3), (dict(head_dim=64), 3), (dict(causal=0), 3),
+                       (dict(softmax_scale=-1.0), 2), (dict(topk=65), 3)):
+        assert fb(dims(**kw)) == status, kw
+    assert fb(dims(batch=0), **{k: NULL for k in ("q", "k", "v", "qi", "ki", "idx", "out", "lse", "lsei", "do",
+                                                    "dq", "dk", "dv", "dqi", "dki", "ws")}, nbytes=0) == 0
+
+
 def test_kl_entry_checks_both_branches():
     for kw, status in ((dict(index_dim=96), 3), (dict(head_dim=64), 3), (dict(num_heads_q=6), 3),
                        (dict(softmax_scale=-1.0), 2), (dict(causal=0), 3), (dict(topk=0), 2)):

@@ -1,0 +1,148 @@
+"""GPU parity of the fused backward (msa_backward through the C ABI): both
+gradients from one walk of the edges.
+
+The fused pass forms dq, dk, dv with the main backward's arithmetic and
+dq_idx, dk_idx with the loss backward's, in the same summation orders, so at
+one query chunk each output must equal the separate entry point's bit for
+bit (msa_sparse_attn_bwd, msa_kl_loss_bwd), on every shape those tests
+cover.  With several query chunks (forced through a small workspace) the
+outputs are compared with the oracle's gradients on every row and key, by
+the one tolerance rule of gpu_util.check_close.  Outputs and workspaces are
+poisoned before every call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_gqa_scores_amd as msa
+import oracle
+import synth
+from gpu_util import (check_close, forward_outputs, inputs_for, poisoned, poisoned_workspace,
+                      spread_index_queries, to_u16)
+
+pytestmark = pytest.mark.gpu
+
+
+def W(name, B, Sq, Sk, Hq, Hkv, Didx=128, topk=16, **kw):
+    return synth.Workload(name, B, Sq, Sk, Hq, Hkv, index_dim=Didx, topk=topk, **kw)
+
+
+def prepare(w, t):
+    """Forward, loss forward and a seeded upstream gradient."""
+    t["dout"] = torch.empty_like(t["q"])
+    synth.fill_device(w, "dout", t["dout"])
+    out, lse, idx = msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk,
+                                    **forward_outputs(w))
+    _, lse_idx = msa.msa_kl_loss_fwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, return_lse_idx=True)
+    return out, lse, idx, lse_idx
+
+
+def fused(w, t, out, lse, idx, lse_idx, grad=1.0, ws_bytes=None):
+    d = msa.dims_of(t["q"], t["k"], t["q_idx"], t["k_idx"], topk=w.topk)
+    nbytes = msa.msa_workspace_bytes(d, msa.ENTRY_BACKWARD) if ws_bytes is None else ws_bytes
+    res = msa.msa_backward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], idx, out, lse, lse_idx, t["dout"],
+                           grad, workspace=poisoned_workspace(nbytes),
+                           dq=poisoned(t["q"].shape, torch.bfloat16), dk=poisoned(t["k"].shape, torch.bfloat16),
+                           dv=poisoned(t["v"].shape, torch.bfloat16),
+                           dq_idx=poisoned(t["q_idx"].shape, torch.bfloat16),
+                           dk_idx=poisoned(t["k_idx"].shape, torch.bfloat16))
+    torch.cuda.synchronize()
+    return res
+
+
+def separate(w, t, out, lse, idx, lse_idx, grad=1.0):
+    d = msa.dims_of(t["q"], t["k"], t["q_idx"], t["k_idx"], topk=w.topk)
+    dq, dk, dv = msa.msa_sparse_attn_bwd(
+        t["q"], t["k"], t["v"], idx, out, lse, t["dout"],
+        workspace=poisoned_workspace(msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_BWD)))
+    dqi, dki = msa.msa_kl_loss_bwd(
+        t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, lse_idx, grad,
+        workspace=poisoned_workspace(msa.msa_workspace_bytes(d, msa.ENTRY_KL_LOSS_BWD)))
+    torch.cuda.synchronize()
+    return dq, dk, dv, dqi, dki
+
+
+NAMES = ("dq", "dk", "dv", "dq_idx", "dk_idx")
+
+CASES = [
+    W("fb_4k", 1, 4096, 4096, 8, 2, Didx=64),                  # two query windows, D_idx 64
+    W("fb_ragged", 2, 700, 1000, 8, 2, topk=5),                # S_k % 128 != 0, S_q < S_k
+    W("fb_gqa8", 1, 2600, 2600, 64, 8),                        # G = 8
+    W("fb_mha", 1, 600, 777, 4, 4, Didx=64, topk=3),           # G = 1
+    W("fb_g2", 1, 500, 1300, 8, 4, topk=6),                    # G = 2
+    W("fb_g16", 1, 500, 640, 32, 2, topk=2),                   # G = 16
+    W("fb_g32", 2, 300, 300, 32, 1, Didx=64, topk=4),          # G = 32
+    W("fb_decode", 3, 1, 5000, 16, 2, Didx=64),                # S_q = 1
+    W("fb_gain", 1, 1500, 3000, 16, 2, gain=True, topk=6),     # uneven blocks
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_fused_equals_separate(w):
+    t = inputs_for(w)
+    out, lse, idx, lse_idx = prepare(w, t)
+    d = msa.dims_of(t["q"], t["k"], t["q_idx"], t["k_idx"], topk=w.topk)
+    nbytes = msa.msa_workspace_bytes(d, msa.ENTRY_BACKWARD)
+    assert msa.msa_attn_chunks(d, msa.ENTRY_BACKWARD, nbytes) == 1
+    got = fused(w, t, out, lse, idx, lse_idx, grad=0.75)
+    ref = separate(w, t, out, lse, idx, lse_idx, grad=0.75)
+    for name, a, b in zip(NAMES, got, ref):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{w.name} {name} differs"
+
+
+def test_fused_spread_student_equals_separate():
+    """With a spread student (two +-1 channels per index row) every token's
+    P_idx enters g; the fused pass still equals the separate ones."""
+    w = W("fb_spread_g8", 1, 700, 3000, 64, 8, topk=12)
+    t = spread_index_queries(w, inputs_for(w))
+    out, lse, idx, lse_idx = prepare(w, t)
+    got = fused(w, t, out, lse, idx, lse_idx)
+    ref = separate(w, t, out, lse, idx, lse_idx)
+    for name, a, b in zip(NAMES, got, ref):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{w.name} {name} differs"
+
+
+@pytest.mark.parametrize("chunks", [2, 3])
+def test_fused_chunked_against_oracle(chunks):
+    """A workspace that fits only part of the queries runs the fused pass in
+    several chunks (dk, dv and dk_idx carry fp32 sums across them); every
+    row's dq, dq_idx and every key's dk, dv, dk_idx against the oracle."""
+    w = W("fb_chunks", 1, 1024, 1536, 16, 2, Didx=64, topk=6)
+    t = inputs_for(w)
+    out, lse, idx, lse_idx = prepare(w, t)
+    d = msa.dims_of(t["q"], t["k"], t["q_idx"], t["k_idx"], topk=w.topk)
+    lo, hi = msa.msa_workspace_min_bytes(d, msa.ENTRY_BACKWARD), msa.msa_workspace_bytes(d, msa.ENTRY_BACKWARD)
+    nbytes = next(b for b in range(lo, hi + 1, max(1, (hi - lo) // 4096))
+                  if msa.msa_attn_chunks(d, msa.ENTRY_BACKWARD, b) <= chunks)
+    assert msa.msa_attn_chunks(d, msa.ENTRY_BACKWARD, nbytes) == chunks
+    dq, dk, dv, dqi, dki = fused(w, t, out, lse, idx, lse_idx, ws_bytes=nbytes)
+    p = oracle.Problem.of(w)
+    rows = p.all_rows()
+    h = {n: to_u16(x) for n, x in t.items()}
+    ref = oracle.forward(p, h["q"], h["k"], h["v"], h["q_idx"], h["k_idx"], rows=rows)
+    assert (idx.cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]] == ref["sel"]).all(), "selection differs"
+    rdq, rdk, rdv = oracle.attention_bwd(p, h["q"], h["k"], h["v"], h["dout"], ref["sel"], rows)
+    rdqi, rdki, _ = oracle.kl_bwd(p, h["q"], h["k"], h["q_idx"], h["k_idx"], ref["sel"], rows)
+    c = 1.0 / (w.batch * w.seqlen_q * w.heads_kv)
+    G = w.group
+    dqn = dq.float().cpu().numpy()
+    gdq = np.stack([dqn[bb, ii, gg * G:(gg + 1) * G] for bb, ii, gg in rows])
+    for name, got, r in (("dq", gdq, rdq), ("dk", dk.float().cpu().numpy(), rdk),
+                         ("dv", dv.float().cpu().numpy(), rdv)):
+        check_close(f"{chunks} chunks {name}", got, r, max(1.0, float(np.abs(r).max())))
+    dqin = dqi.float().cpu().numpy()
+    check_close(f"{chunks} chunks dq_idx", dqin[rows[:, 0], rows[:, 1], rows[:, 2]], rdqi * c,
+                float(np.abs(rdqi * c).max()))
+    check_close(f"{chunks} chunks dk_idx", dki.float().cpu().numpy(), rdki * c, float(np.abs(rdki * c).max()))
+
+
+def test_fused_without_queries_writes_zero_key_gradients():
+    """seqlen_q = 0 with keys present: dk = dv = dk_idx = 0."""
+    dk = torch.full((2, 300, 2, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    dv = torch.full_like(dk, 5.0)
+    dki = torch.full((2, 300, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    d = msa.Dims.make(2, 0, 300, 8, 2, index_dim=64)
+    rc = msa.lib().msa_backward(d, None, None, None, None, None, None, None, None, None, None, 1.0, None,
+                                dk.data_ptr(), dv.data_ptr(), None, dki.data_ptr(), None, 0, None)
+    torch.cuda.synchronize()
+    assert rc == 0 and not dk.float().any() and not dv.float().any() and not dki.float().any()
