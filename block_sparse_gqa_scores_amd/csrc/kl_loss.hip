@@ -187,27 +187,58 @@ __global__ __launch_bounds__(kThreads, 2) void kl_partial_kernel(Params p) {
       }
       load_qi(ib, i_next);
     }
+    // S = Q K^T as a software pipeline, one MFMA per step (step st = 8 nt +
+    // ks, key tile nt) with a scheduling barrier between steps: each K
+    // fragment is read three steps ahead into a ring of four, and the
+    // teacher sums of tile nt - 1 run two values a step during tile nt's
+    // MFMAs (in the same order as one pass would add them).  Keys past a
+    // query are dropped after the head sum (the same keys for every head of
+    // the query), where vis is applied.  G = 1 keeps 64 teacher values per
+    // lane and has no registers for the ring: one tile at a time there.
+    if constexpr (G == 1) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int krow = nt * 32 + n;
-      f32x16 sa = zero16();
+      for (int nt = 0; nt < 4; ++nt) {
+        const int krow = nt * 32 + n;
+        f32x16 sa = zero16();
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        sa = mfma32x32x16(qb[ks], ktile[krow * 16 + ((2 * ks + h) ^ (krow & 15))], sa);
-      // Keys past a query are dropped after the head sum (the same keys for
-      // every head of the query), where vis is applied.
+        for (int ks = 0; ks < 8; ++ks)
+          sa = mfma32x32x16(qb[ks], ktile[krow * 16 + ((2 * ks + h) ^ (krow & 15))], sa);
 #pragma unroll
-      for (int l = 0; l < NL; ++l) {
-        float acc = 0.f;
+        for (int l = 0; l < NL; ++l) {
+          float acc = 0.f;
 #pragma unroll
-        for (int rr = 0; rr < RPS; ++rr) {
-          const int r = l * RPS + rr;
-          acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -lse2[r]));
+          for (int rr = 0; rr < RPS; ++rr) {
+            const int r = l * RPS + rr;
+            acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -lse2[r]));
+          }
+          pt[nt][l] = acc;
         }
-        pt[nt][l] = acc;
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // One key tile at a time: keeps the live accumulators to two.
-      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      const u32x4* klane = ktile + n * 16;  // row 32 nt + n keeps its chunks swizzled by n & 15
+      auto kfrag = [&](int st) { return klane[(st >> 3) * 512 + ((2 * (st & 7) + h) ^ (n & 15))]; };
+      f32x16 sa[2];
+      // Values r, r + 1 of tile NT (accumulator sa[NT & 1]) into pt[NT].
+      auto teach2 = [&](auto NT, auto R) {
+        constexpr int nt = decltype(NT)::value, r = decltype(R)::value;
+#pragma unroll
+        for (int x = r; x < r + 2; ++x) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[nt & 1][x], c, -lse2[x]));
+          if (x % RPS == 0) pt[nt][x / RPS] = 0.f;
+          pt[nt][x / RPS] += e;
+        }
+      };
+      u32x4 ring[4];
+      static_for<0, 3>([&](auto P) { ring[P] = kfrag(P); });
+      static_for<0, 32>([&](auto S) {
+        constexpr int st = decltype(S)::value, nt = st / 8, ks = st % 8;
+        if constexpr (st + 3 < 32) ring[(st + 3) % 4] = kfrag(st + 3);
+        sa[nt & 1] = mfma32x32x16(qb[ks], ring[st % 4], ks == 0 ? zero16() : sa[nt & 1]);
+        if constexpr (nt >= 1) teach2(std::integral_constant<int, nt - 1>{}, std::integral_constant<int, 2 * ks>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      static_for<0, 8>([&](auto K) { teach2(std::integral_constant<int, 3>{}, std::integral_constant<int, 2 * K>{}); });
     }
     // Teacher and index score of each (query slot l, key tile u) of this
     // lane.  For G >= 8 the halves hold head partial sums of the same queries:
