@@ -299,25 +299,82 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
   bool had = false;
   if constexpr (KL) had = !kp.first && kp.dk_flag[flag_at] != 0;
   Fetched fx, fy;
-  Ids ids;
+  Ids ide, ido;  // ids of the even and of the odd sub-tiles
   if (h0) {
     Ids i0;
     load_ids(cur, i0);
     h1 = next(cur);
-    load_ids(cur, ids);
+    load_ids(cur, ido);
     fetch(i0, fx);
     store_records(zero16(), true);
     if constexpr (KL) if (wave < NDT) store_kl_records(zero16(), true);
     h2 = h1 && next(cur);
-    Ids i2;
-    load_ids(cur, i2);
-    fetch(ids, fy);
-    ids = i2;
+    load_ids(cur, ide);
+    fetch(ido, fy);
     store_records(zero16(), true);
     if constexpr (KL) if (wave < NDT) store_kl_records(zero16(), true);
   }
 
-  auto step = [&](Fetched& f_) {
+  // Operands that are the same for every sub-tile can stay in registers
+  // once loaded instead of being read from LDS each sub-tile: the K_j and V_j
+  // rows of the wave's keys (S, dP), K^T of the wave's head dims (dq), and in
+  // the fused pass the k_idx rows (z) and k_idx^T (dq_idx).  Which ones do
+  // is bounded by the register file (one wave per SIMD: 512 registers).
+  constexpr bool FKV = !(KL && G == 1), FKT = !KL, FZ = false, FQ = false;
+  constexpr int NZ = !KL ? 1 : G >= 8 ? 2 * (DIDX / 32) : DIDX / 16;
+  u32x4 kf[FKV ? 8 : 1], vf[FKV ? 8 : 1], ktf[FKT ? 8 : 1], zf[FZ ? NZ : 1], qf[FQ ? 8 : 1];
+  auto load_frags = [&]() {
+    const int krow = key0 + n;
+    if constexpr (FKV) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        kf[ks] = ktile[krow * 16 + ((2 * ks + h) ^ (krow & 15))];
+        vf[ks] = vtile[krow * 16 + ((2 * ks + h) ^ (krow & 15))];
+      }
+    }
+    const int lr = lane & 15;
+    if constexpr (FKT) {
+      const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
+        const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + lds_tile_off(k0, c0, k0 & 15));
+        const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + lds_tile_off(k1, c0, k1 & 15));
+        ktf[ks] = u32x4{a0.x, a0.y, a1.x, a1.y};
+      }
+    }
+    if constexpr (FZ) {
+      if constexpr (G >= 8) {
+        const int k0 = key0 + (lane & 15), k1 = k0 + 16;
+#pragma unroll
+        for (int ks = 0; ks < DIDX / 32; ++ks) {
+          const int ch = 4 * ks + (lane >> 4);
+          zf[2 * ks] = itile[k0 * ICH + (ch ^ (k0 & (ICH - 1)))];
+          zf[2 * ks + 1] = itile[k1 * ICH + (ch ^ (k1 & (ICH - 1)))];
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < DIDX / 16; ++ks) {
+          const int ch = 2 * ks + h;
+          zf[ks] = itile[krow * ICH + (ch ^ (krow & (ICH - 1)))];
+        }
+      }
+    }
+    if constexpr (FQ) {
+      if (wave < NDT) {
+        const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
+          const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k0, c0, k0 & (ICH - 1)));
+          const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k1, c0, k1 & (ICH - 1)));
+          qf[ks] = u32x4{a0.x, a0.y, a1.x, a1.y};
+        }
+      }
+    }
+  };
+
+  auto step = [&](Fetched& f_, const Ids& use, Ids& load) {
     Fetched& f = f_;
     // The fused pass holds three sets of accumulators: there the lane
     // coordinates are re-derived from an opaque copy each sub-tile, so the
@@ -350,10 +407,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
     __syncthreads();
     {
       const bool h3 = h2 && next(cur);
-      Ids nid;
-      load_ids(cur, nid);
-      fetch(ids, f);
-      ids = nid;
+      load_ids(cur, load);
+      fetch(use, f);
       h2 = h3;
     }
     asm volatile("" ::: "memory");
@@ -365,8 +420,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const int ch = 2 * ks + h;
-        sacc = mfma32x32x16(sq[n * 16 + (ch ^ rsw(n))], ktile[krow * 16 + (ch ^ (krow & 15))], sacc);
-        pacc = mfma32x32x16(sdo[n * 16 + (ch ^ rsw(n))], vtile[krow * 16 + (ch ^ (krow & 15))], pacc);
+        const u32x4 kb = FKV ? kf[FKV ? ks : 0] : ktile[krow * 16 + (ch ^ (krow & 15))];
+        const u32x4 vb = FKV ? vf[FKV ? ks : 0] : vtile[krow * 16 + (ch ^ (krow & 15))];
+        sacc = mfma32x32x16(sq[n * 16 + (ch ^ rsw(n))], kb, sacc);
+        pacc = mfma32x32x16(sdo[n * 16 + (ch ^ rsw(n))], vb, pacc);
       }
       // P and dS; rows r -> 8 (r / 4) + 4 h + r % 4.
       float lse4[16], del4[16];
@@ -401,8 +458,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
           for (int ks = 0; ks < DIDX / 32; ++ks) {
             const int ch = 4 * ks + (lane >> 4);
             const u32x4 a = sqi[qr * ICH + (ch ^ (rsw(qr) & (ICH - 1)))];
-            z0 = mfma16x16x32(a, itile[k0 * ICH + (ch ^ (k0 & (ICH - 1)))], z0);
-            z1 = mfma16x16x32(a, itile[k1 * ICH + (ch ^ (k1 & (ICH - 1)))], z1);
+            z0 = mfma16x16x32(a, FZ ? zf[FZ ? 2 * ks : 0] : itile[k0 * ICH + (ch ^ (k0 & (ICH - 1)))], z0);
+            z1 = mfma16x16x32(a, FZ ? zf[FZ ? 2 * ks + 1 : 0] : itile[k1 * ICH + (ch ^ (k1 & (ICH - 1)))], z1);
           }
           const bool upper = (lane >> 4) & 1;
 #pragma unroll
@@ -413,7 +470,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
           for (int ks = 0; ks < DIDX / 16; ++ks) {
             const int ch = 2 * ks + h;
             zacc = mfma32x32x16(sqi[n * ICH + (ch ^ (rsw(n) & (ICH - 1)))],
-                                itile[krow * ICH + (ch ^ (krow & (ICH - 1)))], zacc);
+                                FZ ? zf[FZ ? ks : 0] : itile[krow * ICH + (ch ^ (krow & (ICH - 1)))], zacc);
           }
 #pragma unroll
           for (int l = 0; l < NL; ++l) zv[l] = zacc[l * RPS];
@@ -515,9 +572,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
         const int lr = lane & 15;
         const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
         const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
-        const uint2 ka0 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + lds_tile_off(k0, c0, k0 & 15));
-        const uint2 ka1 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + lds_tile_off(k1, c0, k1 & 15));
-        const u32x4 ka = {ka0.x, ka0.y, ka1.x, ka1.y};
+        u32x4 ka;
+        if constexpr (FKT) {
+          ka = ktf[ks];
+        } else {
+          const uint2 ka0 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + lds_tile_off(k0, c0, k0 & 15));
+          const uint2 ka1 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + lds_tile_off(k1, c0, k1 & 15));
+          ka = u32x4{ka0.x, ka0.y, ka1.x, ka1.y};
+        }
         const u32x4 sb = *reinterpret_cast<const u32x4*>(&sds[n * kSStride + 16 * ks + 8 * h]);
         qacc = mfma32x32x16(ka, sb, qacc);
       }
@@ -532,9 +594,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
 #pragma unroll
           for (int ks = 0; ks < 8; ++ks) {
             const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
-            const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k0, c0, k0 & (ICH - 1)));
-            const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k1, c0, k1 & (ICH - 1)));
-            const u32x4 ka = {a0.x, a0.y, a1.x, a1.y};
+            u32x4 ka;
+            if constexpr (FQ) {
+              ka = qf[ks];
+            } else {
+              const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k0, c0, k0 & (ICH - 1)));
+              const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k1, c0, k1 & (ICH - 1)));
+              ka = u32x4{a0.x, a0.y, a1.x, a1.y};
+            }
             const u32x4 gb = *reinterpret_cast<const u32x4*>(&sg[n * kGStride + 16 * ks + 8 * h]);
             iacc = mfma32x32x16(ka, gb, iacc);
           }
@@ -542,14 +609,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
         }
       }
   };
+  if (h0) {  // uniform
+    __syncthreads();  // the tiles are in LDS
+    load_frags();
+  }
   while (h0) {  // uniform
     bool hb = h2;
-    step(fx);
+    step(fx, ide, ido);
     h0 = h1;
     h1 = hb;
     if (!h0) break;
     hb = h2;
-    step(fy);
+    step(fy, ido, ide);
     h0 = h1;
     h1 = hb;
   }

@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
   const long flag_at = (long)bg * p.n_blk + j;
   const bool had = !kp.first && kp.dk_flag[flag_at] != 0;
   Fetched fx, fy;
-  Ids ids;
+  Ids ide, ido;  // ids of the even and of the odd sub-tiles
 
   // The dq_idx record of each query of a sub-tile, written by the lanes of
   // its first row (the other rows hold the same values); every other lane,
@@ -196,7 +196,45 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
     kp.rec_sc[slot * NDT + wave] = m;  // both halves store the same m
   };
 
-  auto step = [&](Fetched& f) {
+  // The block's operands that are the same for every sub-tile stay in
+  // registers once loaded (K_j rows of the wave's keys for S, their k_idx
+  // rows for z, k_idx^T of the wave's index dims for dq_idx), which takes
+  // three quarters of the LDS reads of a sub-tile off the LDS.
+  constexpr int NZ = G >= 8 ? 2 * (DIDX / 32) : DIDX / 16;
+  u32x4 kf[8], zf[NZ], qf[8];
+  auto load_frags = [&]() {
+    const int krow = key0 + n;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kf[ks] = ktile[krow * 16 + ((2 * ks + h) ^ (krow & 15))];
+    if constexpr (G >= 8) {
+      const int k0 = key0 + (lane & 15), k1 = k0 + 16;
+#pragma unroll
+      for (int ks = 0; ks < DIDX / 32; ++ks) {
+        const int ch = 4 * ks + (lane >> 4);
+        zf[2 * ks] = itile[k0 * ICH + (ch ^ (k0 & (ICH - 1)))];
+        zf[2 * ks + 1] = itile[k1 * ICH + (ch ^ (k1 & (ICH - 1)))];
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < DIDX / 16; ++ks) {
+        const int ch = 2 * ks + h;
+        zf[ks] = itile[krow * ICH + (ch ^ (krow & (ICH - 1)))];
+      }
+    }
+    if (wave < NDT) {
+      const int lr = lane & 15;
+      const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
+        const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k0, c0, k0 & (ICH - 1)));
+        const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k1, c0, k1 & (ICH - 1)));
+        qf[ks] = u32x4{a0.x, a0.y, a1.x, a1.y};
+      }
+    }
+  };
+
+  auto step = [&](Fetched& f, const Ids& use, Ids& load) {
     __syncthreads();  // the previous sub-tile's LDS reads are done
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
@@ -218,10 +256,8 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
     __syncthreads();
     {
       const bool h3 = h2 && next(cur);
-      Ids nid;
-      load_ids(cur, nid);
-      fetch(ids, f);
-      ids = nid;
+      load_ids(cur, load);
+      fetch(use, f);
       h2 = h3;
     }
     asm volatile("" ::: "memory");
@@ -232,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const int ch = 2 * ks + h;
-      sacc = mfma32x32x16(sq[n * 16 + (ch ^ rsw(n))], ktile[krow * 16 + (ch ^ (krow & 15))], sacc);
+      sacc = mfma32x32x16(sq[n * 16 + (ch ^ rsw(n))], kf[ks], sacc);
     }
     // z of query slot l at key key0 + n.  With G >= 8 a sub-tile has at most
     // 4 queries: 16x16x32 tiles whose A row m is query m % 4 (the last one
@@ -248,8 +284,8 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
       for (int ks = 0; ks < DIDX / 32; ++ks) {
         const int ch = 4 * ks + (lane >> 4);
         const u32x4 a = sqi[qr * ICH + (ch ^ (rsw(qr) & (ICH - 1)))];
-        z0 = mfma16x16x32(a, itile[k0 * ICH + (ch ^ (k0 & (ICH - 1)))], z0);
-        z1 = mfma16x16x32(a, itile[k1 * ICH + (ch ^ (k1 & (ICH - 1)))], z1);
+        z0 = mfma16x16x32(a, zf[2 * ks], z0);
+        z1 = mfma16x16x32(a, zf[2 * ks + 1], z1);
       }
       const bool upper = (lane >> 4) & 1;
 #pragma unroll
@@ -259,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
 #pragma unroll
       for (int ks = 0; ks < DIDX / 16; ++ks) {
         const int ch = 2 * ks + h;
-        zacc = mfma32x32x16(sqi[n * ICH + (ch ^ (rsw(n) & (ICH - 1)))], itile[krow * ICH + (ch ^ (krow & (ICH - 1)))], zacc);
+        zacc = mfma32x32x16(sqi[n * ICH + (ch ^ (rsw(n) & (ICH - 1)))], zf[ks], zacc);
       }
 #pragma unroll
       for (int l = 0; l < NL; ++l) zv[l] = zacc[l * RPS];
@@ -320,16 +356,10 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
     // 32 wave .. 32 wave + 31 (waves past D_idx / 32 idle); one record per query.
     if (wave < NDT) {
       f32x16 qacc = zero16();
-      const int lr = lane & 15;
-      const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
-        const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k0, c0, k0 & (ICH - 1)));
-        const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k1, c0, k1 & (ICH - 1)));
-        const u32x4 ka = {a0.x, a0.y, a1.x, a1.y};
         const u32x4 gb = *reinterpret_cast<const u32x4*>(&sg[n * kGStride + 16 * ks + 8 * h]);
-        qacc = mfma32x32x16(ka, gb, qacc);
+        qacc = mfma32x32x16(qf[ks], gb, qacc);
       }
       store_records(qacc, false);
     }
@@ -338,24 +368,26 @@ __global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
     Ids i0;
     load_ids(cur, i0);
     h1 = next(cur);
-    load_ids(cur, ids);
+    load_ids(cur, ido);
     fetch(i0, fx);
     if (wave < NDT) store_records(zero16(), true);
     h2 = h1 && next(cur);
-    Ids i2;
-    load_ids(cur, i2);
-    fetch(ids, fy);
-    ids = i2;
+    load_ids(cur, ide);
+    fetch(ido, fy);
     if (wave < NDT) store_records(zero16(), true);
+  }
+  if (h0) {  // uniform
+    __syncthreads();  // the tiles are in LDS
+    load_frags();
   }
   while (h0) {  // uniform
     bool hb = h2;
-    step(fx);
+    step(fx, ide, ido);
     h0 = h1;
     h1 = hb;
     if (!h0) break;
     hb = h2;
-    step(fy);
+    step(fy, ido, ide);
     h0 = h1;
     h1 = hb;
   }
