@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
   // rows of the wave's keys (S, dP), K^T of the wave's head dims (dq), and in
   // the fused pass the k_idx rows (z) and k_idx^T (dq_idx).  Which ones do
   // is bounded by the register file (one wave per SIMD: 512 registers).
-  constexpr bool FKV = !(KL && G == 1), FKT = !KL, FZ = false, FQ = false;
+  constexpr bool FKV = !(KL && G == 1), FKT = !KL, FZ = false, FQ = KL && (DIDX == 64 || G >= 8);
   constexpr int NZ = !KL ? 1 : G >= 8 ? 2 * (DIDX / 32) : DIDX / 16;
   u32x4 kf[FKV ? 8 : 1], vf[FKV ? 8 : 1], ktf[FKT ? 8 : 1], zf[FZ ? NZ : 1], qf[FQ ? 8 : 1];
   auto load_frags = [&]() {
