@@ -31,6 +31,7 @@ struct Params {
   int W, n_win;          // queries per window (a multiple of kBuildQueries unless
                          // it is the whole chunk), windows per chunk
   int QT;                // edges per work item
+  int dense_q;           // forward only: queries below this take no edges (dense tiles); else 0
   uint32_t topk_m;       // slot / topk == (slot * topk_m) >> topk_s (set_topk_divisor)
   int topk_s;
   float scale_log2;

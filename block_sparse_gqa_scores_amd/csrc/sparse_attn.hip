@@ -57,8 +57,9 @@ __global__ void zero_kernel(int32_t* a, long n) {
 // kBuildQueries queries of one (b, g), counts their edges per block in LDS and
 // touches global memory once per distinct block.  Used when the histogram of
 // n_blk bins fits in LDS; count_kernel / fill_kernel below cover wider rows.
+// Rows below p.dense_q are attended by the dense tiles (dense_tile) and get no edges.
 __device__ __forceinline__ bool edge_ok(const Params& p, int i, int j) {
-  return j >= 0 && j <= (i + p.S_k - p.S_q) / kBlock;
+  return i >= p.dense_q && j >= 0 && j <= (i + p.S_k - p.S_q) / kBlock;
 }
 
 __global__ __launch_bounds__(256) void bucket_count_kernel(Params p) {
@@ -124,7 +125,7 @@ __global__ void count_kernel(Params p) {
     const int i = p.q0 + il;
     if (i >= p.S_q) continue;
     const int j = p.idx[((long)bg * p.S_q + i) * p.topk + e];
-    if (j >= 0 && j <= (i + p.S_k - p.S_q) / kBlock)
+    if (edge_ok(p, i, j))
       atomicAdd(&p.counts[((long)bg * p.n_win + il / p.W) * p.n_blk + j], 1);
   }
 }
@@ -238,12 +239,192 @@ __global__ void fill_kernel(Params p) {
     const int i = p.q0 + il;
     if (i >= p.S_q) continue;
     const int j = p.idx[((long)bg * p.S_q + i) * p.topk + e];
-    if (j >= 0 && j <= (i + p.S_k - p.S_q) / kBlock) {
+    if (edge_ok(p, i, j)) {
       const long bucket = ((long)bg * p.n_win + il / p.W) * p.n_blk + j;
       const int pos = p.offsets[bucket] + atomicAdd(&p.cursor[bucket], 1);
       p.edges[pos] = (int32_t)s;
     }
   }
+}
+
+// Rows whose local block is below topk (t < 128 topk): under the selection
+// rule such a row takes every block of its causal prefix, so neighbouring
+// queries share one union of at most topk blocks.  Their attention runs
+// query-stationary, in the flash form of Sparse Attention Part II section
+// 4.1: a workgroup takes 4 QW consecutive queries of one (b, g), each wave
+// 32 MFMA rows (QW queries x G heads) with its Q rows in registers, and walks
+// the blocks 0 .. (local block of the tile's last query) in order.  Each
+// block's K and V pass through LDS once for the four waves (the group's heads
+// share the load), and every row keeps its running max, sum and output in
+// registers (online softmax), so O and the LSE are written directly, with no
+// per-edge record and no merge.  A row takes only the blocks its own
+// selection names (a caller's selection may be any subset holding the local
+// block) and the causal mask on its own block; a wave skips a block none of
+// its rows takes.  Rows past the dense range repeat the last one and store
+// nothing.  The matrix phases are the partial kernel's pipelines.
+template <int G>
+__device__ __forceinline__ void dense_tile(const Params& p, int n_dense, int with_lse, int wg, u32x4* ktile,
+                                           uint32_t* vt) {
+  constexpr int QW = 32 / G;   // queries per wave
+  constexpr int QWG = 4 * QW;  // queries per workgroup
+
+  const int tiles = (n_dense + QWG - 1) / QWG;
+  const int bg = wg / tiles;
+  const int il0 = (wg - bg * tiles) * QWG;  // first query of the tile, in the chunk
+  const int b = bg / p.H_kv;
+  const int g = bg - b * p.H_kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int n = lane & 31;  // MFMA row of this lane
+  const int qi = n / G, hh = n - (n / G) * G;
+  const int off = p.S_k - p.S_q;
+  const int il = il0 + wave * QW + qi;
+  const bool row_ok = il < n_dense;
+  const int i = p.q0 + min(il, n_dense - 1);
+  const int t = i + off;
+  const int lrow = t / kBlock;
+  uint64_t selm = 0;  // blocks this row's selection names (all below topk <= 64)
+  {
+    const int32_t* sel = p.idx + ((long)bg * p.S_q + i) * p.topk;
+    for (int e = 0; e < p.topk; ++e) {
+      const int j = sel[e];
+      if (j >= 0 && j <= lrow) selm |= 1ull << j;
+    }
+  }
+  const int jmax = (p.q0 + min(il0 + QWG, n_dense) - 1 + off) / kBlock;  // uniform
+  u32x4 qb[8];
+  {
+    const uint16_t* qrow = p.q + ((size_t)b * p.S_q + i) * p.H_q * kD + (size_t)(g * G + hh) * kD + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qb[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
+  }
+  const float c = p.scale_log2;
+  float m = neg_inf(), l = 0.f;  // running raw-score max and (per half) weight sum
+  f32x16 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = zero16();
+
+  for (int j = 0; j <= jmax; ++j) {
+    __syncthreads();  // the previous block's LDS reads are done
+    {
+      const size_t row_stride = (size_t)p.H_kv * kD;
+      const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+      const uint16_t* vb = p.v + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int qd = it * kThreads + tid;
+        const int row = qd >> 4, cc = qd & 15;
+        const int s2 = min(j * kBlock + row, p.S_k - 1);  // rows past S_k: masked for every row
+        ktile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s2 * row_stride + 8 * cc);
+      }
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int u = it * kThreads + tid;
+        const int kp = (u & 15) + 16 * ((u >> 6) & 3);
+        const int d0 = ((u >> 4) & 3) + 4 * ((u >> 8) & 3);
+        const int s0 = min(j * kBlock + 2 * kp, p.S_k - 1);
+        const int s1 = min(j * kBlock + 2 * kp + 1, p.S_k - 1);
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(vb + (size_t)s0 * row_stride + 8 * d0);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(vb + (size_t)s1 * row_stride + 8 * d0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t a = (e & 1) ? (lo[e >> 1] >> 16) : (lo[e >> 1] & 0xFFFFu);
+          const uint32_t c2 = (e & 1) ? (hi[e >> 1] & 0xFFFF0000u) : (hi[e >> 1] << 16);
+          vt[((8 * d0 + e) * kVStride + 2 * kp) >> 1] = a | c2;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const bool mine = (selm >> j) & 1;
+    if (__builtin_amdgcn_ballot_w64(mine) == 0) continue;  // uniform: no row of this wave takes j
+
+    // S^T = K Q^T as in the partial kernel; a row that does not take j has
+    // every key masked, its own block the keys past t.
+    const bool need_mask = __builtin_amdgcn_ballot_w64(!mine || j * kBlock + kBlock - 1 > t) != 0;
+    const int lim = mine ? t - j * kBlock - 4 * h : -1;
+    f32x16 sacc[4];
+    auto mask_chunk = [&](auto MT) {
+      constexpr int mt = decltype(MT)::value;
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (mt * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[mt][r] = neg_inf();
+      }
+    };
+    float mx = neg_inf();
+    auto max2 = [&](auto MT, auto R) {
+      constexpr int mt = decltype(MT)::value, r = decltype(R)::value;
+      mx = max3f(sacc[mt][r], sacc[mt][r + 1], mx);
+    };
+    const u32x4* klane = ktile + n * 16;
+    auto kfrag = [&](int st) { return klane[(st >> 3) * 512 + ((2 * (st & 7) + h) ^ (n & 15))]; };
+    u32x4 ring[4];
+    static_for<0, 3>([&](auto P) { ring[P] = kfrag(P); });
+    static_for<0, 32>([&](auto S) {
+      constexpr int st = decltype(S)::value, mt = st / 8, ks = st % 8;
+      if constexpr (st + 3 < 32) ring[(st + 3) % 4] = kfrag(st + 3);
+      sacc[mt] = mfma32x32x16(ring[st % 4], qb[ks], ks == 0 ? zero16() : sacc[mt]);
+      if constexpr (mt >= 1 && ks == 0) mask_chunk(std::integral_constant<int, mt - 1>{});
+      if constexpr (mt >= 1) max2(std::integral_constant<int, mt - 1>{}, std::integral_constant<int, 2 * ks>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    mask_chunk(std::integral_constant<int, 3>{});
+    static_for<0, 8>([&](auto K) { max2(std::integral_constant<int, 3>{}, std::integral_constant<int, 2 * K>{}); });
+    mx = halves_max(mx);
+    // Online softmax: rescale what the earlier blocks left by 2^((m - m') c).
+    const float m_new = __builtin_fmaxf(m, mx);
+    const bool none = m_new == neg_inf();  // nothing visible yet for this row
+    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f((m - m_new) * c);
+    const float bias = none ? 0.f : -m_new * c;
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    u32x4 pb[4][2];
+    auto exp2v = [&](auto MT, auto R) {
+      constexpr int mt = decltype(MT)::value, r = decltype(R)::value;
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][r], c, bias));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][r + 1], c, bias));
+      l += e0;
+      l += e1;
+      pb[mt][r / 8][(r % 8) / 2] = pack_bf16x2(e0, e1);
+    };
+    static_for<0, 8>([&](auto K) { exp2v(std::integral_constant<int, 0>{}, std::integral_constant<int, 2 * K>{}); });
+    const uint32_t* vlane = vt + n * (kVStride / 2) + 2 * h;
+    auto vfrag = [&](int st) {
+      const uint32_t* va = vlane + (st & 3) * 16 * kVStride + (st >> 3) * 16 + 8 * ((st >> 2) & 1);
+      const uint2 a0 = *reinterpret_cast<const uint2*>(va);
+      const uint2 a1 = *reinterpret_cast<const uint2*>(va + 4);
+      return u32x4{a0.x, a0.y, a1.x, a1.y};
+    };
+    static_for<0, 3>([&](auto P) { ring[P] = vfrag(P); });
+    static_for<0, 32>([&](auto S) {
+      constexpr int st = decltype(S)::value, mt = st / 8, qq = (st / 4) % 2, dt = st % 4;
+      if constexpr (st + 3 < 32) ring[(st + 3) % 4] = vfrag(st + 3);
+      oacc[dt] = mfma32x32x16(ring[st % 4], pb[mt][qq], oacc[dt]);
+      if constexpr (mt < 3) exp2v(std::integral_constant<int, mt + 1>{}, std::integral_constant<int, 2 * (st % 8)>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+  l = halves_sum(l);
+  if (!row_ok) return;
+  // Register r of tile dt holds d = 32 dt + 8 (r / 4) + 4 h + r % 4 of the row.
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t* orow = p.out + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + 4 * h;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      uint2 w;
+      w.x = pack_bf16x2(oacc[dt][4 * r4] * inv, oacc[dt][4 * r4 + 1] * inv);
+      w.y = pack_bf16x2(oacc[dt][4 * r4 + 2] * inv, oacc[dt][4 * r4 + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * r4) = w;
+    }
+  if (with_lse && h == 0)
+    p.lse[((size_t)b * p.H_q + g * G + hh) * p.S_q + i] =
+        (m * c + __builtin_amdgcn_logf(l)) * 0.69314718055994530942f;
 }
 
 // One work item: (bucket (b, g, j), up to QT of its edges).
@@ -253,15 +434,24 @@ __global__ void fill_kernel(Params p) {
 // exactly the same values, which keeps every load and store unconditional (a
 // fixed number of memory operations in flight, no exec-skip branches).  The Q
 // rows of the next sub-tile are loaded while the current one computes.
+//
+// The first n_dense_wg workgroups of the launch are instead the dense tiles
+// (dense_tile above): they are the longest, so they start first and the
+// work items fill in around them.
 template <int G>
-__global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p, int n_dense, int n_dense_wg,
+                                                                   int with_lse) {
   constexpr int QW = 32 / G;  // queries per wave (32 MFMA rows = QW queries x G heads)
   constexpr int QT = kSubTilesFwd * 4 * QW;            // edges per work item
   __shared__ u32x4 ktile[kBlock * 16];                 // [key][16 chunks], swizzled
   __shared__ uint32_t vt[kD * kVStride / 2];           // [d][key] bf16, padded rows
   __shared__ int32_t s_slot[QT];                       // this item's edge slots
 
-  const int w = blockIdx.x;
+  if ((int)blockIdx.x < n_dense_wg) {  // uniform
+    dense_tile<G>(p, n_dense, with_lse, blockIdx.x, ktile, vt);
+    return;
+  }
+  const int w = blockIdx.x - n_dense_wg;
   if (w >= p.tile_off[p.NB]) return;  // uniform: past the last work item
   const int2 item = p.work[w];
   const int bucket = item.x;
@@ -599,6 +789,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Params p, int with_lse,
     const int bg = (int)(r / p.Qc);
     const int i = p.q0 + il;
     if (i >= p.S_q) continue;  // past the end of this (b, g); the next row may be valid
+    if (i < p.dense_q) continue;  // written by its dense tile
     const int b = bg / p.H_kv, g = bg - (bg / p.H_kv) * p.H_kv;
     const int32_t* sel = p.idx + ((long)bg * p.S_q + i) * p.topk;
     const int local = (i + p.S_k - p.S_q) / kBlock;  // entries past it are ignored
@@ -741,8 +932,12 @@ static hipError_t launch_g(const AttnShape& s, const Layout& L, Params p, bool w
     if (s.S_q > 1) launch_build(s, L, p, st);
     mark(c, 0, 1);
     mark(c, 1, 0);
+    const int n_dense = std::min(std::min(L.Qc, s.S_q - q0), std::max(0, p.dense_q - q0));
+    constexpr int QWG = 4 * (32 / G);  // queries per dense tile
+    const int n_dense_wg = n_dense > 0 ? s.batch * s.H_kv * ((n_dense + QWG - 1) / QWG) : 0;
     if (s.S_q > 1)
-      hipLaunchKernelGGL(attn_partial_kernel<G>, dim3((unsigned)L.T), dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL(attn_partial_kernel<G>, dim3((unsigned)(L.T + n_dense_wg)), dim3(kThreads), 0, st, p,
+                         n_dense, n_dense_wg, with_lse ? 1 : 0);
     else  // one query per row: every selected block is its own work item
       hipLaunchKernelGGL(attn_decode_kernel<G>, dim3((unsigned)(s.batch * s.H_kv * s.topk)), dim3(kThreads), 0, st, p);
     mark(c, 1, 1);
@@ -768,6 +963,9 @@ hipError_t launch_sparse_attn(const AttnShape& s, const uint16_t* q, const uint1
   char* base = static_cast<char*>(ws);
   Params p = base_params(s, L, base, idx);
   p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
+  // Rows whose local block is below topk take their whole causal prefix
+  // (query-stationary kernel); decode keeps its own kernel for every row.
+  p.dense_q = s.S_q > 1 ? std::min(s.S_q, std::max(0, s.topk * kBlock - (s.S_k - s.S_q))) : 0;
   p.part_stat = reinterpret_cast<f32x2*>(base + L.part_stat);
   p.part_o = reinterpret_cast<u32x4*>(base + L.part_o);
   const bool with_lse = lse != nullptr;

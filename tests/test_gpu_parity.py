@@ -154,6 +154,46 @@ def test_sparse_attn_fwd_with_caller_selection():
     assert np.abs(got_l - ref_lse).max() < 1e-3
 
 
+@pytest.mark.parametrize("shape", [("dense_sel_g8", 1, 1100, 1300, 16, 2, 12),  # offset 200: tiles straddle blocks
+                                   ("dense_sel_g1", 2, 700, 700, 4, 4, 8)],
+                         ids=lambda s: s[0])
+def test_dense_rows_take_only_their_selection(shape):
+    """Rows whose local block is below topk go through the query-stationary
+    dense tiles.  On a caller's selection each row takes only the blocks it
+    names: here random subsets of its prefix (any size, unsorted, -1 entries),
+    some rows their local block alone."""
+    name, B, Sq, Sk, Hq, Hkv, k = shape
+    w = W(name, B, Sq, Sk, Hq, Hkv, topk=k)
+    assert (Sq - 1 + Sk - Sq) // 128 < k  # every row is a dense row
+    t = inputs_for(w)
+    rng = np.random.default_rng(5)
+    sel = np.full((B, Hkv, Sq, k), -1, dtype=np.int32)
+    for b in range(B):
+        for g in range(Hkv):
+            for i in range(Sq):
+                local = (i + Sk - Sq) // 128
+                n_other = 0 if i % 7 == 0 else int(rng.integers(0, local + 1))
+                others = rng.choice(local, size=min(local, n_other), replace=False)
+                row = np.concatenate([others, [local]])
+                slots = rng.choice(k, size=len(row), replace=False)
+                sel[b, g, i, slots] = row
+    idx = torch.from_numpy(sel).cuda()
+    out, lse = msa.msa_sparse_attn_fwd(t["q"], t["k"], t["v"], idx, return_lse=True)
+    torch.cuda.synchronize()
+    p = oracle.Problem.of(w)
+    h = host_inputs(t)
+    rows = p.all_rows()
+    sel_rows = sel[rows[:, 0], rows[:, 2], rows[:, 1]]
+    ref_out, ref_lse = oracle.attention(p, h["q"], h["k"], h["v"], sel_rows, rows)
+    o = out.float().cpu().numpy()
+    G = w.group
+    got = np.stack([o[b, i, g * G:(g + 1) * G] for b, i, g in rows]).astype(np.float64)
+    check_close(f"{name} out", got, ref_out)
+    l = lse.cpu().numpy()
+    got_l = np.stack([l[b, g * G:(g + 1) * G, i] for b, i, g in rows])
+    assert np.abs(got_l - ref_lse).max() < 1e-3
+
+
 def test_deterministic():
     w = W("determinism", 1, 1500, 4000, 16, 2, topk=8)
     t = inputs_for(w)
