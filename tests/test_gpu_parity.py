@@ -55,6 +55,9 @@ SMALL = [
     W("scale", 1, 300, 1400, 8, 4, topk=4),
     W("gain", 1, 1500, 3000, 16, 2, gain=True, topk=6),                 # uneven block scores
     W("k64", 1, 130, 9000, 4, 1, topk=64),                              # the largest topk
+    W("dense_k1", 2, 300, 300, 8, 2, topk=1),                           # dense rows: block 0 only
+    W("dense_k64", 1, 900, 900, 4, 1, Didx=64, topk=64),                # every row dense, k = 64
+    W("dense_g32", 1, 260, 390, 32, 1, topk=3),                         # dense tiles of one query (G = 32)
 ]
 
 
