@@ -247,6 +247,119 @@ __global__ void fill_kernel(Params p) {
   }
 }
 
+// K_j and V_j of (b, g) into LDS: K row-major [key][16 chunks], chunk c of
+// key r at c ^ (r & 15); V transposed to [d][key] with padded rows (both the
+// transposing writes and the operand reads are free of bank conflicts).  Keys
+// past S_k are masked for every query (their weight is exactly 0), so a
+// clamped row is read instead of branching.
+__device__ __forceinline__ void load_kv_tile(const Params& p, int b, int g, int j, u32x4* ktile, uint32_t* vt,
+                                             int tid) {
+  const size_t row_stride = (size_t)p.H_kv * kD;
+  const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+  const uint16_t* vb = p.v + ((size_t)b * p.S_k * p.H_kv + g) * kD;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int qd = it * kThreads + tid;
+    const int row = qd >> 4, c = qd & 15;
+    const int s = min(j * kBlock + row, p.S_k - 1);
+    ktile[row * 16 + (c ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * c);
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int u = it * kThreads + tid;
+    const int kp = (u & 15) + 16 * ((u >> 6) & 3);
+    const int d0 = ((u >> 4) & 3) + 4 * ((u >> 8) & 3);
+    const int s0 = min(j * kBlock + 2 * kp, p.S_k - 1);
+    const int s1 = min(j * kBlock + 2 * kp + 1, p.S_k - 1);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(vb + (size_t)s0 * row_stride + 8 * d0);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(vb + (size_t)s1 * row_stride + 8 * d0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t a = (e & 1) ? (lo[e >> 1] >> 16) : (lo[e >> 1] & 0xFFFFu);
+      const uint32_t c2 = (e & 1) ? (hi[e >> 1] & 0xFFFF0000u) : (hi[e >> 1] << 16);
+      vt[((8 * d0 + e) * kVStride + 2 * kp) >> 1] = a | c2;
+    }
+  }
+}
+
+// S^T = K Q^T of one 32-row sub-tile (Q rows in qb, this lane's row n, half
+// h) against the block in ktile, as a software pipeline: one MFMA per step
+// (step st = 8 mt + ks: K rows 32 mt + n, k-step ks) with a scheduling
+// barrier between steps, each K fragment read three steps ahead into a ring
+// of four, and the row maximum of a finished 32-key chunk taken during the
+// next chunk's MFMAs.  Register r of chunk mt holds key 32 mt + 8 (r / 4) +
+// 4 h + r % 4; when need_mask (wave-uniform), keys above lim are set to
+// -inf (one branch per finished chunk).  Returns the row's maximum.
+__device__ __forceinline__ float s_block(const u32x4* ktile, const u32x4 (&qb)[8], int n, int h, bool need_mask,
+                                         int lim, f32x16 (&sacc)[4]) {
+  auto mask_chunk = [&](auto MT) {
+    constexpr int mt = decltype(MT)::value;
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (mt * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[mt][r] = neg_inf();
+    }
+  };
+  float mx = neg_inf();
+  auto max2 = [&](auto MT, auto R) {
+    constexpr int mt = decltype(MT)::value, r = decltype(R)::value;
+    mx = max3f(sacc[mt][r], sacc[mt][r + 1], mx);
+  };
+  // Row 32 mt + n keeps its 16-byte chunks swizzled by n & 15.
+  const u32x4* klane = ktile + n * 16;
+  auto kfrag = [&](int st) { return klane[(st >> 3) * 512 + ((2 * (st & 7) + h) ^ (n & 15))]; };
+  u32x4 ring[4];
+  static_for<0, 3>([&](auto P) { ring[P] = kfrag(P); });
+  static_for<0, 32>([&](auto S) {
+    constexpr int st = decltype(S)::value, mt = st / 8, ks = st % 8;
+    if constexpr (st + 3 < 32) ring[(st + 3) % 4] = kfrag(st + 3);
+    sacc[mt] = mfma32x32x16(ring[st % 4], qb[ks], ks == 0 ? zero16() : sacc[mt]);
+    if constexpr (mt >= 1 && ks == 0) mask_chunk(std::integral_constant<int, mt - 1>{});
+    if constexpr (mt >= 1) max2(std::integral_constant<int, mt - 1>{}, std::integral_constant<int, 2 * ks>{});
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  mask_chunk(std::integral_constant<int, 3>{});
+  static_for<0, 8>([&](auto K) { max2(std::integral_constant<int, 3>{}, std::integral_constant<int, 2 * K>{}); });
+  return halves_max(mx);
+}
+
+// P = 2^(S c + bias) in bf16 as the B operand of O^T = V^T P^T, and O^T added
+// into oacc (from zero when ZERO): a software pipeline like s_block's, step
+// st = 8 mt + 4 qq + dt over V^T[d][key] with d = 32 dt + n, keys 32 mt + 16 qq
+// + 4 h + 0..3 and + 8..11 (one lane base plus compile-time offsets), the
+// exponentials of chunk mt + 1 issued two values a step during chunk mt's
+// MFMAs.  l gains this lane half's fp32 weights.
+template <bool ZERO>
+__device__ __forceinline__ void pv_block(const uint32_t* vt, const f32x16 (&sacc)[4], float c, float bias, int n,
+                                         int h, float& l, f32x16 (&oacc)[4]) {
+  u32x4 pb[4][2];
+  auto exp2v = [&](auto MT, auto R) {
+    constexpr int mt = decltype(MT)::value, r = decltype(R)::value;
+    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][r], c, bias));
+    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][r + 1], c, bias));
+    l += e0;
+    l += e1;
+    pb[mt][r / 8][(r % 8) / 2] = pack_bf16x2(e0, e1);
+  };
+  static_for<0, 8>([&](auto K) { exp2v(std::integral_constant<int, 0>{}, std::integral_constant<int, 2 * K>{}); });
+  const uint32_t* vlane = vt + n * (kVStride / 2) + 2 * h;
+  auto vfrag = [&](int st) {
+    const uint32_t* va = vlane + (st & 3) * 16 * kVStride + (st >> 3) * 16 + 8 * ((st >> 2) & 1);
+    const uint2 a0 = *reinterpret_cast<const uint2*>(va);
+    const uint2 a1 = *reinterpret_cast<const uint2*>(va + 4);
+    return u32x4{a0.x, a0.y, a1.x, a1.y};
+  };
+  u32x4 ring[4];
+  static_for<0, 3>([&](auto P) { ring[P] = vfrag(P); });
+  static_for<0, 32>([&](auto S) {
+    constexpr int st = decltype(S)::value, mt = st / 8, qq = (st / 4) % 2, dt = st % 4;
+    if constexpr (st + 3 < 32) ring[(st + 3) % 4] = vfrag(st + 3);
+    oacc[dt] = mfma32x32x16(ring[st % 4], pb[mt][qq], ZERO && mt == 0 && qq == 0 ? zero16() : oacc[dt]);
+    if constexpr (mt < 3) exp2v(std::integral_constant<int, mt + 1>{}, std::integral_constant<int, 2 * (st % 8)>{});
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
 // Rows whose local block is below topk (t < 128 topk): under the selection
 // rule such a row takes every block of its causal prefix, so neighbouring
 // queries share one union of at most topk blocks.  Their attention runs
@@ -305,108 +418,27 @@ __device__ __forceinline__ void dense_tile(const Params& p, int n_dense, int wit
 
   for (int j = 0; j <= jmax; ++j) {
     __syncthreads();  // the previous block's LDS reads are done
-    {
-      const size_t row_stride = (size_t)p.H_kv * kD;
-      const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
-      const uint16_t* vb = p.v + ((size_t)b * p.S_k * p.H_kv + g) * kD;
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int qd = it * kThreads + tid;
-        const int row = qd >> 4, cc = qd & 15;
-        const int s2 = min(j * kBlock + row, p.S_k - 1);  // rows past S_k: masked for every row
-        ktile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s2 * row_stride + 8 * cc);
-      }
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int u = it * kThreads + tid;
-        const int kp = (u & 15) + 16 * ((u >> 6) & 3);
-        const int d0 = ((u >> 4) & 3) + 4 * ((u >> 8) & 3);
-        const int s0 = min(j * kBlock + 2 * kp, p.S_k - 1);
-        const int s1 = min(j * kBlock + 2 * kp + 1, p.S_k - 1);
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(vb + (size_t)s0 * row_stride + 8 * d0);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(vb + (size_t)s1 * row_stride + 8 * d0);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t a = (e & 1) ? (lo[e >> 1] >> 16) : (lo[e >> 1] & 0xFFFFu);
-          const uint32_t c2 = (e & 1) ? (hi[e >> 1] & 0xFFFF0000u) : (hi[e >> 1] << 16);
-          vt[((8 * d0 + e) * kVStride + 2 * kp) >> 1] = a | c2;
-        }
-      }
-    }
+    load_kv_tile(p, b, g, j, ktile, vt, tid);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const bool mine = (selm >> j) & 1;
     if (__builtin_amdgcn_ballot_w64(mine) == 0) continue;  // uniform: no row of this wave takes j
-
-    // S^T = K Q^T as in the partial kernel; a row that does not take j has
-    // every key masked, its own block the keys past t.
+    // A row that does not take j has every key masked, its own block the
+    // keys past t.
     const bool need_mask = __builtin_amdgcn_ballot_w64(!mine || j * kBlock + kBlock - 1 > t) != 0;
-    const int lim = mine ? t - j * kBlock - 4 * h : -1;
     f32x16 sacc[4];
-    auto mask_chunk = [&](auto MT) {
-      constexpr int mt = decltype(MT)::value;
-      if (need_mask) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (mt * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[mt][r] = neg_inf();
-      }
-    };
-    float mx = neg_inf();
-    auto max2 = [&](auto MT, auto R) {
-      constexpr int mt = decltype(MT)::value, r = decltype(R)::value;
-      mx = max3f(sacc[mt][r], sacc[mt][r + 1], mx);
-    };
-    const u32x4* klane = ktile + n * 16;
-    auto kfrag = [&](int st) { return klane[(st >> 3) * 512 + ((2 * (st & 7) + h) ^ (n & 15))]; };
-    u32x4 ring[4];
-    static_for<0, 3>([&](auto P) { ring[P] = kfrag(P); });
-    static_for<0, 32>([&](auto S) {
-      constexpr int st = decltype(S)::value, mt = st / 8, ks = st % 8;
-      if constexpr (st + 3 < 32) ring[(st + 3) % 4] = kfrag(st + 3);
-      sacc[mt] = mfma32x32x16(ring[st % 4], qb[ks], ks == 0 ? zero16() : sacc[mt]);
-      if constexpr (mt >= 1 && ks == 0) mask_chunk(std::integral_constant<int, mt - 1>{});
-      if constexpr (mt >= 1) max2(std::integral_constant<int, mt - 1>{}, std::integral_constant<int, 2 * ks>{});
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    mask_chunk(std::integral_constant<int, 3>{});
-    static_for<0, 8>([&](auto K) { max2(std::integral_constant<int, 3>{}, std::integral_constant<int, 2 * K>{}); });
-    mx = halves_max(mx);
+    const float mx = s_block(ktile, qb, n, h, need_mask, mine ? t - j * kBlock - 4 * h : -1, sacc);
     // Online softmax: rescale what the earlier blocks left by 2^((m - m') c).
     const float m_new = __builtin_fmaxf(m, mx);
     const bool none = m_new == neg_inf();  // nothing visible yet for this row
     const float alpha = none ? 1.f : __builtin_amdgcn_exp2f((m - m_new) * c);
-    const float bias = none ? 0.f : -m_new * c;
     m = m_new;
     l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-    u32x4 pb[4][2];
-    auto exp2v = [&](auto MT, auto R) {
-      constexpr int mt = decltype(MT)::value, r = decltype(R)::value;
-      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][r], c, bias));
-      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][r + 1], c, bias));
-      l += e0;
-      l += e1;
-      pb[mt][r / 8][(r % 8) / 2] = pack_bf16x2(e0, e1);
-    };
-    static_for<0, 8>([&](auto K) { exp2v(std::integral_constant<int, 0>{}, std::integral_constant<int, 2 * K>{}); });
-    const uint32_t* vlane = vt + n * (kVStride / 2) + 2 * h;
-    auto vfrag = [&](int st) {
-      const uint32_t* va = vlane + (st & 3) * 16 * kVStride + (st >> 3) * 16 + 8 * ((st >> 2) & 1);
-      const uint2 a0 = *reinterpret_cast<const uint2*>(va);
-      const uint2 a1 = *reinterpret_cast<const uint2*>(va + 4);
-      return u32x4{a0.x, a0.y, a1.x, a1.y};
-    };
-    static_for<0, 3>([&](auto P) { ring[P] = vfrag(P); });
-    static_for<0, 32>([&](auto S) {
-      constexpr int st = decltype(S)::value, mt = st / 8, qq = (st / 4) % 2, dt = st % 4;
-      if constexpr (st + 3 < 32) ring[(st + 3) % 4] = vfrag(st + 3);
-      oacc[dt] = mfma32x32x16(ring[st % 4], pb[mt][qq], oacc[dt]);
-      if constexpr (mt < 3) exp2v(std::integral_constant<int, mt + 1>{}, std::integral_constant<int, 2 * (st % 8)>{});
-      __builtin_amdgcn_sched_barrier(0);
-    });
+    pv_block<false>(vt, sacc, c, none ? 0.f : -m_new * c, n, h, l, oacc);
   }
   l = halves_sum(l);
   if (!row_ok) return;
@@ -466,37 +498,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p, int
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
 
   for (int x = tid; x < n_here; x += kThreads) s_slot[x] = p.edges[ebase + x];
-  // K_j, V_j of group g into LDS (V transposed to [d][key]).
-  {
-    const size_t row_stride = (size_t)p.H_kv * kD;
-    const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
-    const uint16_t* vb = p.v + ((size_t)b * p.S_k * p.H_kv + g) * kD;
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int qd = it * kThreads + tid;
-      const int row = qd >> 4, c = qd & 15;
-      // Keys past S_k are causally masked for every query (their weight is
-      // exactly 0), so a clamped row is read instead of branching.
-      const int s = min(j * kBlock + row, p.S_k - 1);
-      ktile[row * 16 + (c ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * c);
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int u = it * kThreads + tid;
-      const int kp = (u & 15) + 16 * ((u >> 6) & 3);
-      const int d0 = ((u >> 4) & 3) + 4 * ((u >> 8) & 3);
-      const int s0 = min(j * kBlock + 2 * kp, p.S_k - 1);
-      const int s1 = min(j * kBlock + 2 * kp + 1, p.S_k - 1);
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(vb + (size_t)s0 * row_stride + 8 * d0);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(vb + (size_t)s1 * row_stride + 8 * d0);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t a = (e & 1) ? (lo[e >> 1] >> 16) : (lo[e >> 1] & 0xFFFFu);
-        const uint32_t c2 = (e & 1) ? (hi[e >> 1] & 0xFFFF0000u) : (hi[e >> 1] << 16);
-        vt[((8 * d0 + e) * kVStride + 2 * kp) >> 1] = a | c2;
-      }
-    }
-  }
+  load_kv_tile(p, b, g, j, ktile, vt, tid);  // K_j, V_j of group g
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -526,88 +528,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p, int
     load_q(qn, i_n);
     asm volatile("" ::: "memory");
 
-    // The two matrix phases are software pipelines, one MFMA per step with a
-    // scheduling barrier between steps: every operand fragment is read from
-    // LDS three steps ahead into a ring of four, and the vector work of one
-    // 32-key chunk runs two values a step during the next chunk's MFMAs.
+    // The two matrix phases are the software pipelines of s_block and
+    // pv_block.  Causal mask only where the block reaches past some row's
+    // position (the query's own block); raw scores are ranked, the scale is
+    // applied inside the exponent: p = 2^(s * c - m * c) with
+    // c = scale * log2(e).
     const int t = i + off;
-    // Causal mask only where the block reaches past some row's position (the
-    // query's own block); raw scores are ranked, the scale is applied inside
-    // the exponent: p = 2^(s * c - m * c) with c = scale * log2(e).
-    // A finished 32-key chunk is masked (one wave-uniform branch) before its
-    // values enter the row max.
     const bool need_mask = __builtin_amdgcn_ballot_w64(j * kBlock + kBlock - 1 > t) != 0;
-    // Register r of this lane holds key 32 mt + 8 (r / 4) + 4 h + r % 4 of the
-    // block; keys past t - 128 j are masked for this lane's row.
-    const int lim = t - j * kBlock - 4 * h;
     f32x16 sacc[4];
-    auto mask_chunk = [&](auto MT) {
-      constexpr int mt = decltype(MT)::value;
-      if (need_mask) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (mt * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[mt][r] = neg_inf();
-      }
-    };
-    float mx = neg_inf();
-    // Values r, r + 1 of chunk mt into the row max.
-    auto max2 = [&](auto MT, auto R) {
-      constexpr int mt = decltype(MT)::value, r = decltype(R)::value;
-      mx = max3f(sacc[mt][r], sacc[mt][r + 1], mx);
-    };
-    // S^T = K Q^T, step st = 8 mt + ks: K rows 32 mt + n, k-step ks.  Row
-    // 32 mt + n keeps its 16-byte chunks swizzled by n & 15.
-    const u32x4* klane = ktile + n * 16;
-    auto kfrag = [&](int st) { return klane[(st >> 3) * 512 + ((2 * (st & 7) + h) ^ (n & 15))]; };
-    u32x4 ring[4];
-    static_for<0, 3>([&](auto P) { ring[P] = kfrag(P); });
-    static_for<0, 32>([&](auto S) {
-      constexpr int st = decltype(S)::value, mt = st / 8, ks = st % 8;
-      if constexpr (st + 3 < 32) ring[(st + 3) % 4] = kfrag(st + 3);
-      sacc[mt] = mfma32x32x16(ring[st % 4], qb[ks], ks == 0 ? zero16() : sacc[mt]);
-      if constexpr (mt >= 1 && ks == 0) mask_chunk(std::integral_constant<int, mt - 1>{});
-      if constexpr (mt >= 1) max2(std::integral_constant<int, mt - 1>{}, std::integral_constant<int, 2 * ks>{});
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    mask_chunk(std::integral_constant<int, 3>{});
-    static_for<0, 8>([&](auto K) { max2(std::integral_constant<int, 3>{}, std::integral_constant<int, 2 * K>{}); });
-    mx = halves_max(mx);
+    const float mx = s_block(ktile, qb, n, h, need_mask, t - j * kBlock - 4 * h, sacc);
     const float c = p.scale_log2;
-    const float bias = -mx * c;
     // l sums the fp32 weights: the LSE it gives feeds the alignment loss,
     // whose teacher probabilities need it to a few 1e-6.
     float l = 0.f;
-    u32x4 pb[4][2];  // P in bf16, packed as the B operand of O^T = V^T P^T
-    // Weights of values r, r + 1 of chunk mt, packed into pb.
-    auto exp2v = [&](auto MT, auto R) {
-      constexpr int mt = decltype(MT)::value, r = decltype(R)::value;
-      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][r], c, bias));
-      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][r + 1], c, bias));
-      l += e0;
-      l += e1;
-      pb[mt][r / 8][(r % 8) / 2] = pack_bf16x2(e0, e1);
-    };
-    static_for<0, 8>([&](auto K) { exp2v(std::integral_constant<int, 0>{}, std::integral_constant<int, 2 * K>{}); });
-
-    // O^T = V^T P^T, step st = 8 mt + 4 qq + dt: V^T[d][key] with
-    // d = 32 dt + n, keys 32 mt + 16 qq + 4 h + 0..3 and + 8..11, from one
-    // lane base plus compile-time offsets (in dwords).
     f32x16 oacc[4];
-    const uint32_t* vlane = vt + n * (kVStride / 2) + 2 * h;
-    auto vfrag = [&](int st) {
-      const uint32_t* va = vlane + (st & 3) * 16 * kVStride + (st >> 3) * 16 + 8 * ((st >> 2) & 1);
-      const uint2 a0 = *reinterpret_cast<const uint2*>(va);
-      const uint2 a1 = *reinterpret_cast<const uint2*>(va + 4);
-      return u32x4{a0.x, a0.y, a1.x, a1.y};
-    };
-    static_for<0, 3>([&](auto P) { ring[P] = vfrag(P); });
-    static_for<0, 32>([&](auto S) {
-      constexpr int st = decltype(S)::value, mt = st / 8, qq = (st / 4) % 2, dt = st % 4;
-      if constexpr (st + 3 < 32) ring[(st + 3) % 4] = vfrag(st + 3);
-      oacc[dt] = mfma32x32x16(ring[st % 4], pb[mt][qq], mt == 0 && qq == 0 ? zero16() : oacc[dt]);
-      if constexpr (mt < 3) exp2v(std::integral_constant<int, mt + 1>{}, std::integral_constant<int, 2 * (st % 8)>{});
-      __builtin_amdgcn_sched_barrier(0);
-    });
+    pv_block<true>(vt, sacc, c, -mx * c, n, h, l, oacc);
     l = halves_sum(l);
     float amax = 0.f;
 #pragma unroll
