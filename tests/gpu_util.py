@@ -217,3 +217,53 @@ def parity(w, rows=None, threads=0, label=None):
     h = host_inputs(t)
     ref = oracle.forward(p, h["q"], h["k"], h["v"], h["q_idx"], h["k_idx"], rows=rows, threads=threads)
     return compare(w, dev, ref, rows, label=label)
+
+
+def prepare_backward(w, t):
+    """Forward, loss forward and a seeded upstream gradient (t["dout"]) for
+    the backward entry points; returns (out, lse, idx, lse_idx)."""
+    t["dout"] = torch.empty_like(t["q"])
+    synth.fill_device(w, "dout", t["dout"])
+    out, lse, idx = msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk,
+                                    **forward_outputs(w))
+    _, lse_idx = msa.msa_kl_loss_fwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, return_lse_idx=True)
+    return out, lse, idx, lse_idx
+
+
+def fused_backward(w, t, out, lse, idx, lse_idx, grad=1.0, ws_bytes=None):
+    """msa_backward on poisoned gradients and workspace; returns
+    (dq, dk, dv, dq_idx, dk_idx)."""
+    d = msa.dims_of(t["q"], t["k"], t["q_idx"], t["k_idx"], topk=w.topk)
+    nbytes = msa.msa_workspace_bytes(d, msa.ENTRY_BACKWARD) if ws_bytes is None else ws_bytes
+    res = msa.msa_backward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], idx, out, lse, lse_idx, t["dout"],
+                           grad, workspace=poisoned_workspace(nbytes),
+                           dq=poisoned(t["q"].shape, torch.bfloat16), dk=poisoned(t["k"].shape, torch.bfloat16),
+                           dv=poisoned(t["v"].shape, torch.bfloat16),
+                           dq_idx=poisoned(t["q_idx"].shape, torch.bfloat16),
+                           dk_idx=poisoned(t["k_idx"].shape, torch.bfloat16))
+    torch.cuda.synchronize()
+    return res
+
+
+def backward_against_oracle(w, t, grads, idx, label):
+    """Every row's dq, dq_idx and every key's dk, dv, dk_idx against the
+    oracle's gradients (the loss's scaled by 1 / (B S_q H_kv)), by the
+    tolerance rule above; the selection is checked bit-exact first."""
+    dq, dk, dv, dqi, dki = grads
+    p = oracle.Problem.of(w)
+    rows = p.all_rows()
+    h = {n: to_u16(x) for n, x in t.items()}
+    ref = oracle.forward(p, h["q"], h["k"], h["v"], h["q_idx"], h["k_idx"], rows=rows)
+    assert (idx.cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]] == ref["sel"]).all(), f"{label}: selection differs"
+    rdq, rdk, rdv = oracle.attention_bwd(p, h["q"], h["k"], h["v"], h["dout"], ref["sel"], rows)
+    rdqi, rdki, _ = oracle.kl_bwd(p, h["q"], h["k"], h["q_idx"], h["k_idx"], ref["sel"], rows)
+    c = 1.0 / (w.batch * w.seqlen_q * w.heads_kv)
+    G = w.group
+    dqn = dq.float().cpu().numpy()
+    gdq = np.stack([dqn[bb, ii, gg * G:(gg + 1) * G] for bb, ii, gg in rows])
+    for name, got, r in (("dq", gdq, rdq), ("dk", dk.float().cpu().numpy(), rdk),
+                         ("dv", dv.float().cpu().numpy(), rdv)):
+        check_close(f"{label} {name}", got, r, grad_scale(r))
+    dqin = dqi.float().cpu().numpy()
+    check_close(f"{label} dq_idx", dqin[rows[:, 0], rows[:, 1], rows[:, 2]], rdqi * c, float(np.abs(rdqi * c).max()))
+    check_close(f"{label} dk_idx", dki.float().cpu().numpy(), rdki * c, float(np.abs(rdki * c).max()))

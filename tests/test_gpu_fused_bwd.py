@@ -10,44 +10,19 @@ outputs are compared with the oracle's gradients on every row and key, by
 the one tolerance rule of gpu_util.check_close.  Outputs and workspaces are
 poisoned before every call.
 """
-import numpy as np
 import pytest
 import torch
 
 import block_sparse_gqa_scores_amd as msa
-import oracle
 import synth
-from gpu_util import (check_close, forward_outputs, inputs_for, poisoned, poisoned_workspace,
-                      spread_index_queries, to_u16)
+from gpu_util import (backward_against_oracle, fused_backward as fused, inputs_for, poisoned_workspace,
+                      prepare_backward as prepare, spread_index_queries)
 
 pytestmark = pytest.mark.gpu
 
 
 def W(name, B, Sq, Sk, Hq, Hkv, Didx=128, topk=16, **kw):
     return synth.Workload(name, B, Sq, Sk, Hq, Hkv, index_dim=Didx, topk=topk, **kw)
-
-
-def prepare(w, t):
-    """Forward, loss forward and a seeded upstream gradient."""
-    t["dout"] = torch.empty_like(t["q"])
-    synth.fill_device(w, "dout", t["dout"])
-    out, lse, idx = msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk,
-                                    **forward_outputs(w))
-    _, lse_idx = msa.msa_kl_loss_fwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, return_lse_idx=True)
-    return out, lse, idx, lse_idx
-
-
-def fused(w, t, out, lse, idx, lse_idx, grad=1.0, ws_bytes=None):
-    d = msa.dims_of(t["q"], t["k"], t["q_idx"], t["k_idx"], topk=w.topk)
-    nbytes = msa.msa_workspace_bytes(d, msa.ENTRY_BACKWARD) if ws_bytes is None else ws_bytes
-    res = msa.msa_backward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], idx, out, lse, lse_idx, t["dout"],
-                           grad, workspace=poisoned_workspace(nbytes),
-                           dq=poisoned(t["q"].shape, torch.bfloat16), dk=poisoned(t["k"].shape, torch.bfloat16),
-                           dv=poisoned(t["v"].shape, torch.bfloat16),
-                           dq_idx=poisoned(t["q_idx"].shape, torch.bfloat16),
-                           dk_idx=poisoned(t["k_idx"].shape, torch.bfloat16))
-    torch.cuda.synchronize()
-    return res
 
 
 def separate(w, t, out, lse, idx, lse_idx, grad=1.0):
@@ -115,25 +90,8 @@ def test_fused_chunked_against_oracle(chunks):
     nbytes = next(b for b in range(lo, hi + 1, max(1, (hi - lo) // 4096))
                   if msa.msa_attn_chunks(d, msa.ENTRY_BACKWARD, b) <= chunks)
     assert msa.msa_attn_chunks(d, msa.ENTRY_BACKWARD, nbytes) == chunks
-    dq, dk, dv, dqi, dki = fused(w, t, out, lse, idx, lse_idx, ws_bytes=nbytes)
-    p = oracle.Problem.of(w)
-    rows = p.all_rows()
-    h = {n: to_u16(x) for n, x in t.items()}
-    ref = oracle.forward(p, h["q"], h["k"], h["v"], h["q_idx"], h["k_idx"], rows=rows)
-    assert (idx.cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]] == ref["sel"]).all(), "selection differs"
-    rdq, rdk, rdv = oracle.attention_bwd(p, h["q"], h["k"], h["v"], h["dout"], ref["sel"], rows)
-    rdqi, rdki, _ = oracle.kl_bwd(p, h["q"], h["k"], h["q_idx"], h["k_idx"], ref["sel"], rows)
-    c = 1.0 / (w.batch * w.seqlen_q * w.heads_kv)
-    G = w.group
-    dqn = dq.float().cpu().numpy()
-    gdq = np.stack([dqn[bb, ii, gg * G:(gg + 1) * G] for bb, ii, gg in rows])
-    for name, got, r in (("dq", gdq, rdq), ("dk", dk.float().cpu().numpy(), rdk),
-                         ("dv", dv.float().cpu().numpy(), rdv)):
-        check_close(f"{chunks} chunks {name}", got, r, max(1.0, float(np.abs(r).max())))
-    dqin = dqi.float().cpu().numpy()
-    check_close(f"{chunks} chunks dq_idx", dqin[rows[:, 0], rows[:, 1], rows[:, 2]], rdqi * c,
-                float(np.abs(rdqi * c).max()))
-    check_close(f"{chunks} chunks dk_idx", dki.float().cpu().numpy(), rdki * c, float(np.abs(rdki * c).max()))
+    grads = fused(w, t, out, lse, idx, lse_idx, ws_bytes=nbytes)
+    backward_against_oracle(w, t, grads, idx, f"{chunks} chunks")
 
 
 def test_fused_without_queries_writes_zero_key_gradients():
