@@ -13,7 +13,7 @@ import synth
 # outputs and gradients alike), applied by check_close and compare:
 #   excess = max(|err| - (half the bf16 spacing at the exact value), 0),
 #   max(excess) <= 1e-2 * s and mean(excess) <= 1e-3 * s,
-# with s = 1 for the forward output (the benchmark spec's absolute figures; |o| is
+# with s = 1 for the forward output (the absolute bounds 1e-2 and 1e-3; |o| is
 # bounded by max |v|) and s = max |ref| of the tensor for gradients, whose
 # size is set by the problem (it grows with the rows that meet at a key and
 # shrinks with the loss's 1 / (B S_q H_kv)).  The bound is on the arithmetic,
