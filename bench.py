@@ -215,11 +215,12 @@ def backward_rates(w, t, steps):
     """The backward on the forward's selection (next to the forward, not part
     of its step): msa_sparse_attn_bwd (dq, dk, dv from a seeded dO),
     msa_kl_loss_bwd (gradients of the alignment loss into q_idx, k_idx) and
-    msa_backward (both in one pass).  Algorithmic FLOPs per call: the main
-    branch recomputes S and forms dP, dV, dK and dq, five products of
-    2 D H_q sum|T_i| each; the loss backward recomputes the main logits
-    (2 D H_q sum|T_i|) and forms z, dk_idx and dq_idx (2 D_idx H_kv sum|T_i|
-    each); the fused pass forms S once for both."""
+    msa_backward (both in one call, sharing each query chunk's edge buckets).
+    Algorithmic FLOPs per call: the main branch recomputes S and forms dP,
+    dV, dK and dq, five products of 2 D H_q sum|T_i| each; the loss backward
+    recomputes the main logits (2 D H_q sum|T_i|) and forms z, dk_idx and
+    dq_idx (2 D_idx H_kv sum|T_i| each); the combined call's count takes S
+    once, although its loss kernels form S again on their own."""
     import torch
 
     import block_sparse_gqa_scores_amd as msa
@@ -245,7 +246,7 @@ def backward_rates(w, t, steps):
         "kl_loss_bwd": (lambda: msa.msa_kl_loss_bwd(t["q"], t["k"], t["q_idx"], t["k_idx"], idx, lse, lse_idx,
                                                      1.0, workspace=ws),
                         loss_fl),
-        "fused": (lambda: msa.msa_backward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], idx, out, lse, lse_idx,
+        "msa_backward": (lambda: msa.msa_backward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], idx, out, lse, lse_idx,
                                            dout, 1.0, workspace=ws),
                   main_fl + loss_fl - 2.0 * w.head_dim * w.heads_q * tok),
     }

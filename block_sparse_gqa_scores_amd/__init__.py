@@ -437,9 +437,9 @@ def msa_sparse_attn_bwd(q, k, v, block_idx, out, lse, dout, *, block_size=128, s
 
 def msa_backward(q, k, v, q_idx, k_idx, block_idx, out, lse, lse_idx, dout, grad_loss=1.0, *, block_size=128,
                  softmax_scale=0.0, dq=None, dk=None, dv=None, dq_idx=None, dk_idx=None, workspace=None):
-    """Both backward passes in one (the fused backward): returns (dq, dk, dv,
-    dq_idx, dk_idx), bf16, equal to msa_sparse_attn_bwd's and
-    msa_kl_loss_bwd's outputs."""
+    """Both backward passes in one call: returns (dq, dk, dv, dq_idx, dk_idx),
+    bf16, equal bit for bit to msa_sparse_attn_bwd's and msa_kl_loss_bwd's
+    outputs when each call runs in one query chunk."""
     import torch
     _rank("block_idx", block_idx, 4)
     d = dims_of(q, k, q_idx, k_idx, topk=block_idx.shape[-1], block_size=block_size,

@@ -90,21 +90,9 @@ __global__ __launch_bounds__(256) void bucket_sort_kernel(Params p) {
   for (int x = threadIdx.x; x < n; x += 256) e[x] = v[x];
 }
 
-// DIDX = 0: the main branch alone.  DIDX = D_idx: the fused pass, which also
-// forms the alignment loss's gradients (kl_bwd.hip states them) from the same
-// S, P, staged Q rows and edge walk: the teacher is the head mean of P, z and
-// g = coef (P_idx - teacher) are formed per sub-tile, dk_idx accumulates per
-// group in registers and dq_idx leaves per-edge records, in the loss
-// backward's formats and orders (so both gradients equal the separate
-// passes' bit for bit).
-template <int G, int DIDX>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlBwdParams kp) {
+template <int G>
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
   constexpr int QW = 32 / G;                // queries per sub-tile
-  constexpr bool KL = DIDX > 0;
-  constexpr int ICH = KL ? DIDX / 8 : 1;    // 16-byte chunks per index row
-  constexpr int NDT = KL ? DIDX / 32 : 1;   // 32-dim tiles of the index dims
-  constexpr int RPS = G >= 8 ? G / 2 : G;   // registers of one query in a lane
-  constexpr int NL = 16 / RPS;              // queries per lane
   const Params& p = bp.e;
   __shared__ u32x4 ktile[kBlock * 16];      // K_j [key][16 chunks], swizzled
   __shared__ u32x4 vtile[kBlock * 16];      // V_j, same
@@ -114,12 +102,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
   __shared__ __align__(16) float2 s_stat[32];  // (LSE log2, delta) of each row
   __shared__ int s_t[QW];                   // position of each query (-1: no edge)
   __shared__ int s_slot[QW];
-  // Fused pass only: k_idx of the block, the rows' index queries, g, and each
-  // query's index-score LSE.
-  __shared__ u32x4 itile[KL ? kBlock * ICH : 1];  // chunk c at c ^ (key & (ICH - 1))
-  __shared__ u32x4 sqi[KL ? 32 * ICH : 1];        // chunk c at c ^ (rsw(row) & (ICH - 1))
-  __shared__ __align__(16) uint16_t sg[KL ? 32 * kGStride : 8];  // g [row][key] bf16
-  __shared__ float s_lsez[KL ? QW : 1];
 
   const int BG = p.B * p.H_kv;
   const int j = blockIdx.x / BG;            // early (busier) blocks first
@@ -129,17 +111,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int n = lane & 31;
   const int off = p.S_k - p.S_q;
-  constexpr float kLog2e = 1.4426950408889634f;
   const float c = p.scale_log2;
 
 
   f32x16 dk_acc[4], dv_acc[4];  // [key row][d tile]: this wave's 32 keys x 128 dims
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) dk_acc[dt] = dv_acc[dt] = zero16();
-  f32x16 ki_acc[NDT];  // fused pass: dk_idx of this wave's keys [key row][index-dim tile]
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) ki_acc[dt] = zero16();
-  const float invG = 1.f / G;
 
   const int key0 = 32 * wave;          // this wave's keys within the block
   const int key_abs = j * kBlock + key0 + n;
@@ -195,8 +172,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
     u32x4 qa[2], da[2];
     float2 st;
     Ids id;
-    u32x4 qi[2];  // fused pass: the rows' index-query chunks (cc % ICH)
-    float lsez;   // fused pass: the row's query's index-score LSE
   };
   auto fetch = [&](const Ids& d, Fetched& f) {
 #pragma unroll
@@ -206,15 +181,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
       const size_t rowoff = (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + 8 * cc;
       f.qa[y] = *reinterpret_cast<const u32x4*>(p.q + rowoff);
       f.da[y] = *reinterpret_cast<const u32x4*>(bp.dout + rowoff);
-      if constexpr (KL)
-        f.qi[y] = *reinterpret_cast<const u32x4*>(p.q_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX +
-                                                  8 * (cc % ICH));
     }
     if (tid < 32) {  // (loading it in every thread costs registers)
       const int hh = tid % G;
       const int i = slot_query(p, bg, d.e2);
       f.st = bp.stat[((size_t)bg * p.S_q + i) * G + hh];
-      if constexpr (KL) f.lsez = kp.lse_idx[((size_t)b * p.H_kv + g) * p.S_q + i];
     }
     f.id = d;
   };
@@ -233,29 +204,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
     const float s = m > 0.f ? 2047.f * __builtin_amdgcn_rcpf(m) : 0.f;
     store_piece<G, false>(bp.dq_rec + slot * (kRecBytes<G> / 16), (wave * G + hh) * 2 + h, qacc, s);
     bp.dq_sc[(slot * 4 + wave) * G + hh] = m * bp.scale * (1.f / 2047.f);  // both halves store the same value
-  };
-  // Fused pass: the dq_idx record of each query of a sub-tile, as the loss
-  // backward writes it, by the lanes of the query's first row (the other
-  // rows hold the same values); every other lane writes the sink.
-  auto store_kl_records = [&](const f32x16& qacc, bool dummy) {
-    const int q = n / G, hh = n - (n / G) * G;
-    const int sl = dummy ? -1 : s_slot[q];
-    const long slot = hh == 0 && sl >= 0 ? sl : kp.sink;
-    float m = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) m = max3abs(qacc[r], qacc[r], m);
-    m = __builtin_fmaxf(m, swap_halves(m));
-    const float inv = m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
-    u32x4* rec = reinterpret_cast<u32x4*>(kp.rec + (slot * NDT + wave) * 32 + 16 * h);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x4 v4;
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-        v4[x] = pack_f16x2(qacc[8 * half + 2 * x] * inv, qacc[8 * half + 2 * x + 1] * inv);
-      rec[half] = v4;
-    }
-    kp.rec_sc[slot * NDT + wave] = m;  // both halves store the same m
   };
   // Pipeline, in issue order: sub-tile n stages rows fetched during n - 2,
   // requests the ids of n + 3 and then the rows of n + 2, computes, and
@@ -279,25 +227,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
       ktile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * cc);
       vtile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(vb + (size_t)s * row_stride + 8 * cc);
     }
-    if constexpr (KL) {
-      const uint16_t* ib = p.k_idx + (size_t)b * p.S_k * DIDX;
-#pragma unroll
-      for (int it = 0; it < kBlock * ICH / kThreads; ++it) {
-        const int qd = it * kThreads + tid;
-        const int row = qd / ICH, cc = qd % ICH;
-        const int s = min(j * kBlock + row, p.S_k - 1);
-        itile[row * ICH + (cc ^ (row & (ICH - 1)))] = *reinterpret_cast<const u32x4*>(ib + (size_t)s * DIDX + 8 * cc);
-      }
-    }
   };
   bool h0 = next(cur), h1 = false, h2 = false;
   const bool any = h0;   // some edge of this chunk selects the block
   if (h0) load_tiles();  // uniform
-  // Fused pass: whether this group's dk_idx part of the block already holds
-  // an earlier chunk's sums; read before the loop's barriers, written after.
-  const long flag_at = (long)bg * p.n_blk + j;
-  bool had = false;
-  if constexpr (KL) had = !kp.first && kp.dk_flag[flag_at] != 0;
   Fetched fx, fy;
   Ids ide, ido;  // ids of the even and of the odd sub-tiles
   if (h0) {
@@ -307,83 +240,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
     load_ids(cur, ido);
     fetch(i0, fx);
     store_records(zero16(), true);
-    if constexpr (KL) if (wave < NDT) store_kl_records(zero16(), true);
     h2 = h1 && next(cur);
     load_ids(cur, ide);
     fetch(ido, fy);
     store_records(zero16(), true);
-    if constexpr (KL) if (wave < NDT) store_kl_records(zero16(), true);
   }
 
-  // Operands that are the same for every sub-tile can stay in registers
-  // once loaded instead of being read from LDS each sub-tile: the K_j and V_j
-  // rows of the wave's keys (S, dP), K^T of the wave's head dims (dq), and in
-  // the fused pass the k_idx rows (z) and k_idx^T (dq_idx).  Which ones do
-  // is bounded by the register file (one wave per SIMD: 512 registers).
-  constexpr bool FKV = !(KL && G == 1), FKT = !KL, FZ = false, FQ = KL && (DIDX == 64 || G >= 8);
-  constexpr int NZ = !KL ? 1 : G >= 8 ? 2 * (DIDX / 32) : DIDX / 16;
-  u32x4 kf[FKV ? 8 : 1], vf[FKV ? 8 : 1], ktf[FKT ? 8 : 1], zf[FZ ? NZ : 1], qf[FQ ? 8 : 1];
+  // Operands that are the same for every sub-tile stay in registers once
+  // loaded instead of being read from LDS each sub-tile: the K_j and V_j rows
+  // of the wave's keys (S, dP) and K^T of the wave's head dims (dq), 96
+  // registers (one wave per SIMD leaves room).
+  u32x4 kf[8], vf[8], ktf[8];
   auto load_frags = [&]() {
     const int krow = key0 + n;
-    if constexpr (FKV) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        kf[ks] = ktile[krow * 16 + ((2 * ks + h) ^ (krow & 15))];
-        vf[ks] = vtile[krow * 16 + ((2 * ks + h) ^ (krow & 15))];
-      }
+    for (int ks = 0; ks < 8; ++ks) {
+      kf[ks] = ktile[krow * 16 + ((2 * ks + h) ^ (krow & 15))];
+      vf[ks] = vtile[krow * 16 + ((2 * ks + h) ^ (krow & 15))];
     }
     const int lr = lane & 15;
-    if constexpr (FKT) {
-      const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
+    const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
-        const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + lds_tile_off(k0, c0, k0 & 15));
-        const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + lds_tile_off(k1, c0, k1 & 15));
-        ktf[ks] = u32x4{a0.x, a0.y, a1.x, a1.y};
-      }
-    }
-    if constexpr (FZ) {
-      if constexpr (G >= 8) {
-        const int k0 = key0 + (lane & 15), k1 = k0 + 16;
-#pragma unroll
-        for (int ks = 0; ks < DIDX / 32; ++ks) {
-          const int ch = 4 * ks + (lane >> 4);
-          zf[2 * ks] = itile[k0 * ICH + (ch ^ (k0 & (ICH - 1)))];
-          zf[2 * ks + 1] = itile[k1 * ICH + (ch ^ (k1 & (ICH - 1)))];
-        }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < DIDX / 16; ++ks) {
-          const int ch = 2 * ks + h;
-          zf[ks] = itile[krow * ICH + (ch ^ (krow & (ICH - 1)))];
-        }
-      }
-    }
-    if constexpr (FQ) {
-      if (wave < NDT) {
-        const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
-          const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k0, c0, k0 & (ICH - 1)));
-          const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k1, c0, k1 & (ICH - 1)));
-          qf[ks] = u32x4{a0.x, a0.y, a1.x, a1.y};
-        }
-      }
+    for (int ks = 0; ks < 8; ++ks) {
+      const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
+      const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + lds_tile_off(k0, c0, k0 & 15));
+      const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + lds_tile_off(k1, c0, k1 & 15));
+      ktf[ks] = u32x4{a0.x, a0.y, a1.x, a1.y};
     }
   };
 
-  auto step = [&](Fetched& f_, const Ids& use, Ids& load) {
-    Fetched& f = f_;
-    // The fused pass holds three sets of accumulators: there the lane
-    // coordinates are re-derived from an opaque copy each sub-tile, so the
-    // compiler recomputes the LDS addresses built from them instead of
-    // keeping them all live across the loop.
-    int tid_l = tid;
-    if constexpr (KL) asm volatile("" : "+v"(tid_l));
-    const int lane = tid_l & 63, h = lane >> 5, n = lane & 31;
-    const int key_abs = j * kBlock + key0 + n;
+  auto step = [&](Fetched& f, const Ids& use, Ids& load) {
     __syncthreads();  // the previous sub-tile's LDS reads are done
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
@@ -391,8 +277,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
       const u32x4 z = {0u, 0u, 0u, 0u};
       sq[r * 16 + (cc ^ rsw(r))] = f.qa[y];
       sdo[r * 16 + (cc ^ rsw(r))] = (f.id.valid >> (y % NI)) & 1 ? f.da[y] : z;
-      if constexpr (KL)
-        if (cc < ICH) sqi[r * ICH + (cc ^ (rsw(r) & (ICH - 1)))] = f.qi[y];
     }
     if (tid < 32) {
       const int x = f.id.e2;
@@ -401,7 +285,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
       if (tid % G == 0) {
         s_t[tid / G] = valid ? slot_query(p, bg, x) + off : -1;
         s_slot[tid / G] = valid ? x : -1;
-        if constexpr (KL) s_lsez[tid / G] = valid ? f.lsez * kLog2e : __builtin_inff();
       }
     }
     __syncthreads();
@@ -420,10 +303,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const int ch = 2 * ks + h;
-        const u32x4 kb = FKV ? kf[FKV ? ks : 0] : ktile[krow * 16 + (ch ^ (krow & 15))];
-        const u32x4 vb = FKV ? vf[FKV ? ks : 0] : vtile[krow * 16 + (ch ^ (krow & 15))];
-        sacc = mfma32x32x16(sq[n * 16 + (ch ^ rsw(n))], kb, sacc);
-        pacc = mfma32x32x16(sdo[n * 16 + (ch ^ rsw(n))], vb, pacc);
+        sacc = mfma32x32x16(sq[n * 16 + (ch ^ rsw(n))], kf[ks], sacc);
+        pacc = mfma32x32x16(sdo[n * 16 + (ch ^ rsw(n))], vf[ks], pacc);
       }
       // P and dS; rows r -> 8 (r / 4) + 4 h + r % 4.
       float lse4[16], del4[16];
@@ -442,82 +323,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
         const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse4[r]));
         pv[r] = vis ? e2 : 0.f;
         dsv[r] = pv[r] * (pacc[r] - del4[r]);
-      }
-      if constexpr (KL) {
-        // z of query slot l at key key0 + n.  With G >= 8 a sub-tile has at
-        // most 4 queries: 16x16x32 tiles whose A row m is query m % 4 (the
-        // last one repeated past QW), keys key0 .. + 15 and key0 + 16 .. + 31;
-        // lane n takes the tile holding its key, and register l is query l.
-        // Otherwise z repeats each query's index row on its heads' rows.
-        float zv[NL];
-        if constexpr (G >= 8) {
-          const int qr = min(lane & 3, QW - 1) * G;  // a row of query qr / G in sqi
-          const int k0 = key0 + (lane & 15), k1 = k0 + 16;
-          f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < DIDX / 32; ++ks) {
-            const int ch = 4 * ks + (lane >> 4);
-            const u32x4 a = sqi[qr * ICH + (ch ^ (rsw(qr) & (ICH - 1)))];
-            z0 = mfma16x16x32(a, FZ ? zf[FZ ? 2 * ks : 0] : itile[k0 * ICH + (ch ^ (k0 & (ICH - 1)))], z0);
-            z1 = mfma16x16x32(a, FZ ? zf[FZ ? 2 * ks + 1 : 0] : itile[k1 * ICH + (ch ^ (k1 & (ICH - 1)))], z1);
-          }
-          const bool upper = (lane >> 4) & 1;
-#pragma unroll
-          for (int l = 0; l < NL; ++l) zv[l] = upper ? z1[l] : z0[l];
-        } else {
-          f32x16 zacc = zero16();
-#pragma unroll
-          for (int ks = 0; ks < DIDX / 16; ++ks) {
-            const int ch = 2 * ks + h;
-            zacc = mfma32x32x16(sqi[n * ICH + (ch ^ (rsw(n) & (ICH - 1)))],
-                                FZ ? zf[FZ ? ks : 0] : itile[krow * ICH + (ch ^ (krow & (ICH - 1)))], zacc);
-          }
-#pragma unroll
-          for (int l = 0; l < NL; ++l) zv[l] = zacc[l * RPS];
-        }
-        // g per (query slot l, key): the teacher is the mean of P over the
-        // query's heads (an in-lane sum, and the other half's heads for G >= 8).
-        float gq[NL];
-#pragma unroll
-        for (int l = 0; l < NL; ++l) {
-          float acc = 0.f;
-#pragma unroll
-          for (int rr = 0; rr < RPS; ++rr) acc += pv[l * RPS + rr];
-          if constexpr (G >= 8) acc += swap_halves(acc);
-          const int q = mfma32_row(l * RPS, lane) / G;
-          const bool vis = key_abs <= s_t[q];
-          const float pidx = __builtin_amdgcn_exp2f(__builtin_fmaf(zv[l], kLog2e, -s_lsez[q]));
-          gq[l] = vis ? kp.coef * (pidx - acc * invG) : 0.f;
-        }
-        // dk_idx += g^T q_idx: A = g of each register's row (its query's
-        // value on each of its G rows, times 1/G), B = the rows' index rows,
-        // transposed.
-        {
-          const int lr = lane & 15;
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            u32x4 ga;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              const int r0 = 8 * kk + 2 * x;
-              ga[x] = pack_bf16x2(gq[r0 / RPS] * invG, gq[(r0 + 1) / RPS] * invG);
-            }
-            const int rbase = 16 * kk + 4 * h;
-            const int ra = rbase + (lr >> 2), rb = rbase + 8 + (lr >> 2);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-              const int c0 = 32 * dt + 16 * (n >> 4) + 4 * (lr & 3);
-              const uint2 b0 = lds_read_tr16(reinterpret_cast<const char*>(sqi) + lds_tile_off<ICH>(ra, c0, rsw(ra) & (ICH - 1)));
-              const uint2 b1 = lds_read_tr16(reinterpret_cast<const char*>(sqi) + lds_tile_off<ICH>(rb, c0, rsw(rb) & (ICH - 1)));
-              const u32x4 bb = {b0.x, b0.y, b1.x, b1.y};
-              ki_acc[dt] = mfma32x32x16(ga, bb, ki_acc[dt]);
-            }
-          }
-        }
-        // g to LDS as [row][key] for dq_idx (each row carries its query's g).
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sg[mfma32_row(r, lane) * kGStride + key0 + n] = (uint16_t)(pack_bf16x2(gq[r / RPS], 0.f) & 0xFFFFu);
       }
       // dV += P^T dO and dK += dS^T Q: A = this lane's P / dS (row = key,
       // k = the 8 rows of registers 8 kk .. 8 kk + 7), B = dO^T / Q^T rows of
@@ -567,47 +372,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
       f32x16 qacc = zero16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        // K^T operand: keys 16 ks + 8 h .. + 7 of column 32 wave + n, as two
-        // transposing reads of the row-major K tile.
-        const int lr = lane & 15;
-        const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
-        const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
-        u32x4 ka;
-        if constexpr (FKT) {
-          ka = ktf[ks];
-        } else {
-          const uint2 ka0 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + lds_tile_off(k0, c0, k0 & 15));
-          const uint2 ka1 = lds_read_tr16(reinterpret_cast<const char*>(ktile) + lds_tile_off(k1, c0, k1 & 15));
-          ka = u32x4{ka0.x, ka0.y, ka1.x, ka1.y};
-        }
+        // K^T operand (keys 16 ks + 8 h .. + 7 of column 32 wave + n): ktf.
         const u32x4 sb = *reinterpret_cast<const u32x4*>(&sds[n * kSStride + 16 * ks + 8 * h]);
-        qacc = mfma32x32x16(ka, sb, qacc);
+        qacc = mfma32x32x16(ktf[ks], sb, qacc);
       }
       store_records(qacc, false);
-      // Fused pass: dq_idx^T[c'][row] = sum_key k_idx^T[c'][key] g[row][key]
-      // for index dims 32 wave .. 32 wave + 31 (waves past D_idx / 32 idle).
-      if constexpr (KL) {
-        if (wave < NDT) {
-          f32x16 iacc = zero16();
-          const int lr = lane & 15;
-          const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks) {
-            const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
-            u32x4 ka;
-            if constexpr (FQ) {
-              ka = qf[ks];
-            } else {
-              const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k0, c0, k0 & (ICH - 1)));
-              const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k1, c0, k1 & (ICH - 1)));
-              ka = u32x4{a0.x, a0.y, a1.x, a1.y};
-            }
-            const u32x4 gb = *reinterpret_cast<const u32x4*>(&sg[n * kGStride + 16 * ks + 8 * h]);
-            iacc = mfma32x32x16(ka, gb, iacc);
-          }
-          store_kl_records(iacc, false);
-        }
-      }
   };
   if (h0) {  // uniform
     __syncthreads();  // the tiles are in LDS
@@ -623,25 +392,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp, KlB
     step(fy, ido, ide);
     h0 = h1;
     h1 = hb;
-  }
-
-  // Fused pass: this group's dk_idx for the wave's keys (fp32, summed over
-  // chunks), as the loss backward stores it, and the block's flag.
-  if constexpr (KL) {
-    if (any) {  // uniform
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int dcol = 32 * dt + n;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j * kBlock + key0 + mfma32_row(r, lane);
-          if (key >= p.S_k) continue;
-          float* o = kp.dk_part + (((size_t)b * p.H_kv + g) * p.S_k + key) * DIDX + dcol;
-          *o = had ? *o + ki_acc[dt][r] : ki_acc[dt][r];
-        }
-      }
-    }
-    if (tid == 0 && (kp.first || any)) kp.dk_flag[flag_at] = had || any;
   }
 
   // A block that no edge of the chunk selects adds nothing: in a middle chunk
@@ -768,6 +518,14 @@ void launch_bucket_sort(const Layout& L, const Params& p, hipStream_t st) {
 
 namespace {
 
+// The main backward of one chunk, after the chunk's bucket build and sort.
+template <int G>
+void launch_main_chunk(const AttnShape& s, const Layout& L, const BwdParams& bp, hipStream_t st) {
+  hipLaunchKernelGGL((attn_bwd_kernel<G>), dim3((unsigned)(s.batch * s.H_kv * s.n_blk)), dim3(kThreads), 0, st, bp);
+  const long mrows = (long)s.batch * s.H_kv * L.Qc;
+  hipLaunchKernelGGL(dq_merge_kernel<G>, dim3((unsigned)((mrows + 3) / 4)), dim3(256), 0, st, bp);
+}
+
 template <int G>
 hipError_t launch_bwd_g(const AttnShape& s, const BwdLayout& BL, BwdParams bp, hipStream_t st) {
   const Layout& L = BL.L;
@@ -779,19 +537,18 @@ hipError_t launch_bwd_g(const AttnShape& s, const BwdLayout& BL, BwdParams bp, h
     bp.last = q0 + L.Qc >= s.S_q;
     launch_build(s, L, bp.e, st);
     launch_bucket_sort(L, bp.e, st);
-    hipLaunchKernelGGL((attn_bwd_kernel<G, 0>), dim3((unsigned)(s.batch * s.H_kv * s.n_blk)), dim3(kThreads), 0, st, bp,
-                       KlBwdParams{});
-    const long mrows = (long)s.batch * s.H_kv * L.Qc;
-    hipLaunchKernelGGL(dq_merge_kernel<G>, dim3((unsigned)((mrows + 3) / 4)), dim3(256), 0, st, bp);
+    launch_main_chunk<G>(s, L, bp, st);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
 }
 
-template <int G, int DIDX>
-hipError_t launch_fused_g(const AttnShape& s, const FusedBwdLayout& FL, BwdParams bp, KlBwdParams kp,
-                          hipStream_t st) {
+// Both backward passes on the same query chunks: one bucket build and sort
+// per chunk serves the main-branch kernels and the loss backward's.
+template <int G>
+hipError_t launch_both_g(const AttnShape& s, const FusedBwdLayout& FL, BwdParams bp, KlBwdParams kp,
+                         hipStream_t st) {
   const Layout& L = FL.B.L;
   const long rows = (long)s.batch * s.S_q * s.H_q;
   hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, st, bp);
@@ -802,29 +559,12 @@ hipError_t launch_fused_g(const AttnShape& s, const FusedBwdLayout& FL, BwdParam
     kp.first = ci == 0;
     launch_build(s, L, bp.e, st);
     launch_bucket_sort(L, bp.e, st);
+    launch_main_chunk<G>(s, L, bp, st);
     kp.e = bp.e;
-    hipLaunchKernelGGL((attn_bwd_kernel<G, DIDX>), dim3((unsigned)(s.batch * s.H_kv * s.n_blk)), dim3(kThreads), 0,
-                       st, bp, kp);
-    const long mrows = (long)s.batch * s.H_kv * L.Qc;
-    hipLaunchKernelGGL(dq_merge_kernel<G>, dim3((unsigned)((mrows + 3) / 4)), dim3(256), 0, st, bp);
-    const hipError_t err = launch_kl_dq_merge(kp, DIDX, mrows, st);
+    const hipError_t err = launch_kl_chunk(s, L, kp, st);
     if (err != hipSuccess) return err;
   }
-  return launch_kl_dk_reduce(kp, DIDX, (long)s.batch * s.n_blk, st);
-}
-
-template <int DIDX>
-hipError_t launch_fused_d(const AttnShape& s, const FusedBwdLayout& FL, const BwdParams& bp,
-                          const KlBwdParams& kp, hipStream_t st) {
-  switch (bp.e.G) {
-    case 1: return launch_fused_g<1, DIDX>(s, FL, bp, kp, st);
-    case 2: return launch_fused_g<2, DIDX>(s, FL, bp, kp, st);
-    case 4: return launch_fused_g<4, DIDX>(s, FL, bp, kp, st);
-    case 8: return launch_fused_g<8, DIDX>(s, FL, bp, kp, st);
-    case 16: return launch_fused_g<16, DIDX>(s, FL, bp, kp, st);
-    case 32: return launch_fused_g<32, DIDX>(s, FL, bp, kp, st);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_kl_dk_reduce(kp, kp.D_idx, (long)s.batch * s.n_blk, st);
 }
 
 }  // namespace
@@ -852,18 +592,26 @@ hipError_t launch_backward(const AttnShape& s, int D_idx, const uint16_t* q, con
   bp.dv_acc = reinterpret_cast<float*>(base + BL.dv_acc);
   bp.dq = dq; bp.dk = dk; bp.dv = dv;
   bp.scale = s.scale;
+  float* lse_t = reinterpret_cast<float*>(base + FL.lse_t);
+  bp.e.lse_t = lse_t;
+  launch_lse_group(s, lse, lse_t, stream);
   KlBwdParams kp{};
   kp.e = bp.e;
   kp.lse_idx = lse_idx; kp.coef = coef;
   kp.rec = reinterpret_cast<uint16_t*>(base + FL.rec);
   kp.rec_sc = reinterpret_cast<float*>(base + FL.rec_sc);
+  kp.g_rec = reinterpret_cast<uint16_t*>(base + FL.g_rec);
   kp.sink = BL.L.E;
   kp.dk_part = reinterpret_cast<float*>(base + FL.dk_part);
   kp.dk_flag = reinterpret_cast<int32_t*>(base + FL.dk_flag);
   kp.dq_idx = dq_idx; kp.dk_idx = dk_idx; kp.D_idx = D_idx;
-  switch (D_idx) {
-    case 64: return launch_fused_d<64>(s, FL, bp, kp, stream);
-    case 128: return launch_fused_d<128>(s, FL, bp, kp, stream);
+  switch (bp.e.G) {
+    case 1: return launch_both_g<1>(s, FL, bp, kp, stream);
+    case 2: return launch_both_g<2>(s, FL, bp, kp, stream);
+    case 4: return launch_both_g<4>(s, FL, bp, kp, stream);
+    case 8: return launch_both_g<8>(s, FL, bp, kp, stream);
+    case 16: return launch_both_g<16>(s, FL, bp, kp, stream);
+    case 32: return launch_both_g<32>(s, FL, bp, kp, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,6 +1,7 @@
 // Parameters shared by the backward kernels: the main branch's
-// (attn_bwd.hip), the alignment loss's (kl_bwd.hip), and the fused pass that
-// computes both gradients over one walk of the edges (attn_bwd.hip).
+// (attn_bwd.hip) and the alignment loss's (kl_bwd.hip).  The combined
+// backward (launch_backward, attn_bwd.hip) runs both on the same query chunks,
+// one bucket build and sort per chunk serving the two.
 #pragma once
 
 #include "edge_buckets.h"
@@ -34,6 +35,7 @@ struct KlBwdParams {
   float coef;            // gradient of the loss / (B * S_q * H_kv)
   uint16_t* rec;         // [slot][D_idx / 32][32] fp16 (rec_dim order) / scale
   float* rec_sc;         // [slot][D_idx / 32]
+  uint16_t* g_rec;       // [slot][128] bf16: g of each (edge, key) (kl_grad_kernel), read by kl_dk_kernel
   long sink;             // record slot written by padding rows (never read)
   float* dk_part;        // [B][H_kv][S_k][D_idx] fp32, per group
   int32_t* dk_flag;      // [B][H_kv][n_blk]: 1 if the group's dk_part rows of the block hold data
@@ -43,9 +45,11 @@ struct KlBwdParams {
   int first;             // this chunk is the first (dk_part is stored, not added)
 };
 
-// The loss backward's per-row dq_idx merge (rows of the chunk at p.q0) and
-// its per-group dk_idx reduce, for D_idx = 64 or 128 (kl_bwd.hip).
-hipError_t launch_kl_dq_merge(const KlBwdParams& kp, int D_idx, long rows, hipStream_t st);
+// The loss backward's kernels of one query chunk (kp.e.q0; its bucket build
+// and sort done): g rows and dq_idx records, their per-row merge, and the
+// per-group dk_idx parts; then, after the last chunk, the reduce of the
+// groups' parts (kl_bwd.hip; D_idx = 64 or 128).
+hipError_t launch_kl_chunk(const AttnShape& s, const Layout& L, const KlBwdParams& kp, hipStream_t st);
 hipError_t launch_kl_dk_reduce(const KlBwdParams& kp, int D_idx, long blocks, hipStream_t st);
 
 }  // namespace edges

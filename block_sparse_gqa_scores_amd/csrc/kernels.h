@@ -79,7 +79,8 @@ hipError_t launch_kl_loss_bwd(const AttnShape& s, int D_idx, const uint16_t* q, 
                               const float* lse, const float* lse_idx, float coef, uint16_t* dq_idx,
                               uint16_t* dk_idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
-// Both backward passes over one walk of the edges (the fused backward).
+// Both backward passes in one call: per query chunk, one bucket build and sort,
+// then the main backward's kernels and the loss backward's.
 size_t backward_workspace(const AttnShape& s, int D_idx);
 size_t backward_workspace_min(const AttnShape& s, int D_idx);
 int backward_chunks(const AttnShape& s, int D_idx, size_t ws_bytes);

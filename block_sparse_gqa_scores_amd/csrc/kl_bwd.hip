@@ -11,17 +11,15 @@
 // c is the caller's gradient of the loss divided by B * S_q * H_kv (the loss
 // is the mean of the row terms).
 //
-// Schedule: as the main-branch backward (attn_bwd.hip).  One workgroup per
-// (batch, group, block) runs every edge of the block in sorted order; its four
-// waves split the block's keys.  Per 32-row sub-tile (32 / G queries x G
-// heads) it recomputes the teacher from S = Q K^T and the forward's LSE (the
-// head mean is an in-lane sum plus one half-wave exchange), the index scores
-// z (16x16x32 tiles with the sub-tile's queries on every 16-lane group for
-// G >= 8, else the query's index row repeated on its heads' rows), then g.  The
-// block's dk_idx accumulates in registers (per group; the groups are added in
-// a fixed order at the end, since all groups share one index key head);
-// dq_idx of each edge goes through LDS and a per-edge fp16 record, added per
-// row by a merge.
+// Schedule, per query chunk, on the attention's edge buckets: kl_grad_kernel
+// runs the work items (a bucket's K_j and index keys loaded once, up to QT
+// of its edges, two workgroups per CU) and leaves per edge g as a bf16 row
+// and dq_idx as an fp16 record (added per row by kl_dq_merge_kernel);
+// kl_dk_kernel then reduces each (batch, group, block)'s dk_idx over the
+// block's edges in sorted order from those g rows, and after the last chunk
+// kl_dk_reduce_kernel adds the groups (all share one index key head) in a
+// fixed order.  Splitting the two sums this way lets the heavy pass run on
+// independent work items instead of one long walk per block.
 #include "bwd_common.h"
 
 namespace msa {
@@ -30,382 +28,424 @@ namespace {
 
 
 
+// Per-edge gradients on the attention's work items (the loss forward's
+// schedule, kl_loss.hip: a work item loads K_j and the index keys of block j
+// once and runs up to QT of its edges, two workgroups per CU): per edge the
+// teacher P (head mean of the main branch's probabilities, from S = Q K^T and
+// the forward's LSE), the index scores z and P_idx = 2^(z log2(e) - LSE_z),
+// then g = c (P_idx - P) on the visible keys.  g leaves as a bf16 row per
+// edge (for the dk_idx reduction, kl_dk_kernel) and, through this wave's LDS
+// rows, gives dq_idx = sum_key g k_idx, one fp16 record per edge (per 32-dim
+// quarter scaled by its largest magnitude, in the order the merge reads).
 template <int G, int DIDX>
-__global__ __launch_bounds__(kThreads, 1) void kl_bwd_kernel(KlBwdParams kp) {
-  constexpr int QW = 32 / G;
-  constexpr int ICH = DIDX / 8;             // 16-byte chunks per index row
-  constexpr int NDT = DIDX / 32;            // 32-dim tiles of the index dims
-  constexpr int RPS = G >= 8 ? G / 2 : G;   // registers of one query in a lane
-  constexpr int NL = 16 / RPS;              // queries per lane
+__global__ __launch_bounds__(kThreads, 2) void kl_grad_kernel(KlBwdParams kp) {
   const Params& p = kp.e;
-  __shared__ u32x4 ktile[kBlock * 16];      // K_j rows, chunk c at c ^ (key & 15)
-  __shared__ u32x4 itile[kBlock * ICH];     // k_idx rows, chunk c at c ^ (key & (ICH - 1))
-  __shared__ u32x4 sq[32 * 16];             // Q rows of the sub-tile, chunk c at c ^ rsw(row)
-  __shared__ u32x4 sqi[32 * ICH];           // q_idx row of each row's query, chunk c at c ^ (rsw(row) & (ICH - 1))
-  __shared__ __align__(16) uint16_t sg[32 * kGStride];  // g [row][key] bf16
-  __shared__ __align__(16) float s_lse[32];
-  __shared__ float s_lsez[QW];
-  __shared__ int s_t[QW];
-  __shared__ int s_slot[QW];
+  constexpr int QW = 32 / G;                 // queries per wave sub-tile
+  constexpr int QT = kSubTiles * 4 * QW;     // edges per work item
+  constexpr int ICH = DIDX / 8;              // 16-byte chunks per index key
+  constexpr int RPS = G >= 8 ? G / 2 : G;    // registers per (query, key) in a lane
+  constexpr int NL = 16 / RPS;               // queries per lane
+  __shared__ u32x4 ktile[kBlock * 16];       // [key][16 chunks], swizzled
+  __shared__ u32x4 itile[kBlock * ICH];      // [key][ICH chunks], swizzled
+  __shared__ __align__(16) float s_lse[QT * G];  // log2(e) * lse of (edge, head)
+  __shared__ int32_t s_slot[QT];
+  __shared__ int32_t s_i[QT];
+  __shared__ float s_lsez[QT];                   // log2(e) * index-score LSE of the edge's row
+  constexpr int GS = kBlock + 8;                 // bf16 per g row (padded)
+  __shared__ __align__(16) uint16_t sg[4][QW][GS];  // per wave: g of its sub-tile [query][key]
 
-  const int BG = p.B * p.H_kv;
-  const int j = blockIdx.x / BG;
-  const int bg = blockIdx.x - j * BG;
+  const int w = blockIdx.x;
+  if (w >= p.tile_off[p.NB]) return;  // uniform: past the last work item
+  const int2 item = p.work[w];
+  const int bucket = item.x;
+  const int start = item.y;
+  const int n_here = min(p.QT, p.counts[bucket] - start);
+  const int ebase = p.offsets[bucket] + start;
+  const int bgw = bucket / p.n_blk;
+  const int j = bucket - bgw * p.n_blk;
+  const int bg = bgw / p.n_win;
   const int b = bg / p.H_kv;
   const int g = bg - b * p.H_kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-  const int n = lane & 31;
-  const int off = p.S_k - p.S_q;
   constexpr float kLog2e = 1.4426950408889634f;
-  const float c = p.scale_log2;
-  const float invG = 1.f / G;
 
-
-  f32x16 dk_acc[NDT];  // [key row][index-dim tile]: this wave's 32 keys
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) dk_acc[dt] = zero16();
-  const int key0 = 32 * wave;
-  const int key_abs = j * kBlock + key0 + n;
-
-  struct Cursor {
-    int w, base, cnt;
-    const int32_t* ed;
-  };
-  // Advances to the next sub-tile; past the last one it returns false and
-  // leaves the cursor on the last sub-tile, so its addresses stay valid.
-  auto next = [&](Cursor& cu) {  // uniform
-    Cursor t = cu;
-    t.base += QW;
-    while (t.base >= t.cnt) {
-      if (++t.w >= p.n_win) return false;
-      const long bucket = ((long)bg * p.n_win + t.w) * p.n_blk + j;
-      t.cnt = __builtin_amdgcn_readfirstlane(p.counts[bucket]);
-      t.ed = p.edges + __builtin_amdgcn_readfirstlane(p.offsets[bucket]);
-      t.base = 0;
-    }
-    cu = t;
-    return true;
-  };
-  const int pr = tid & 15, cc = tid >> 4;  // staging role: rows (2 pr, 2 pr + 1), chunk cc
-  // Edge ids one sub-tile ahead of the rows: e for this thread's staging
-  // rows (one query unless G = 1), e2 for the statistics of row tid % 32;
-  // validity flags come from the cursor alone.
-  constexpr int NI = G >= 2 ? 1 : 2;
-  struct Ids {
-    int e[NI];
-    int e2;
-    int valid;  // bit y: e[y]; bit 2: e2
-  };
-  auto load_ids = [&](const Cursor& cu, Ids& d) {
-    int v = 0;
-#pragma unroll
-    for (int y = 0; y < NI; ++y) {
-      const int q = (2 * pr + y) / G;
-      d.e[y] = cu.ed[min(cu.base + q, cu.cnt - 1)];
-      v |= (cu.base + q < cu.cnt) << y;
-    }
-    const int q2 = (tid & 31) / G;
-    d.e2 = cu.ed[min(cu.base + q2, cu.cnt - 1)];
-    d.valid = v | (cu.base + q2 < cu.cnt) << 2;
-  };
-  // The rows of one sub-tile as fetched by this thread (two sets alternate):
-  // Q rows, the query's index row (chunk cc % ICH; threads past ICH repeat
-  // a chunk and do not stage it), and for the first 32 threads the row's
-  // main-branch LSE and its query's index-score LSE.
-  struct Fetched {
-    u32x4 qa[2], qi[2];
-    float lse, lsez;
-    Ids id;
-  };
-  auto fetch = [&](const Ids& d, Fetched& f) {
-#pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      const int r = 2 * pr + y, hh = r % G;
-      const int i = slot_query(p, bg, d.e[y % NI]);
-      f.qa[y] = *reinterpret_cast<const u32x4*>(p.q + (((size_t)b * p.S_q + i) * p.H_q + g * G + hh) * kD + 8 * cc);
-      f.qi[y] = *reinterpret_cast<const u32x4*>(p.q_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX +
-                                                8 * (cc % ICH));
-    }
-    if (tid < 32) {
-      const int hh = tid % G;
-      const int i = slot_query(p, bg, d.e2);
-      f.lse = p.lse_t[((size_t)bg * p.S_q + i) * G + hh];
-      f.lsez = kp.lse_idx[((size_t)b * p.H_kv + g) * p.S_q + i];
-    }
-    f.id = d;
-  };
-  // Pipeline, in issue order: sub-tile n stages rows fetched during n - 2,
-  // requests the ids of n + 3 and then the rows of n + 2, computes, and
-  // stores its dq_idx records.  Every request but the statistics is
-  // unconditional (past the end the cursor repeats the last sub-tile, and
-  // rows that store no record write the sink), so the memory counter's
-  // order is the same on every iteration and its waits stay tight.
-  Cursor cur{-1, -QW, 0, nullptr};
-  // The block's tiles, loaded only when some edge selects the block (a
-  // workgroup without edges just writes zero gradients).
-  auto load_tiles = [&]() {  // K_j and k_idx of block j (rows past S_k clamped: never visible)
+  // Edges past n_here repeat the last one (same inputs, same record).
+  for (int x = tid; x < QT; x += kThreads) {
+    const int sl = p.edges[ebase + min(x, n_here - 1)];
+    s_slot[x] = sl;
+    s_i[x] = p.q0 + (int)((sl / p.topk) % p.Qc);
+  }
+  __syncthreads();
+  {  // each edge's G head LSEs are one contiguous run of lse_t
+    const float* lq = p.lse_t + (size_t)bg * p.S_q * G;
+    for (int x = tid; x < QT * G; x += kThreads) s_lse[x] = lq[(size_t)s_i[x / G] * G + x % G];
+    const float* lz = kp.lse_idx + (size_t)bg * p.S_q;
+    for (int x = tid; x < QT; x += kThreads) s_lsez[x] = lz[s_i[x]] * kLog2e;
+  }
+  {
     const size_t row_stride = (size_t)p.H_kv * kD;
     const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int qd = it * kThreads + tid;
-      const int row = qd >> 4, cc = qd & 15;
+      const int row = qd >> 4, c = qd & 15;
+      // Keys past S_k are masked for every query; a clamped row is read.
       const int s = min(j * kBlock + row, p.S_k - 1);
-      ktile[row * 16 + (cc ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * cc);
+      ktile[row * 16 + (c ^ (row & 15))] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * c);
     }
     const uint16_t* ib = p.k_idx + (size_t)b * p.S_k * DIDX;
 #pragma unroll
     for (int it = 0; it < kBlock * ICH / kThreads; ++it) {
       const int qd = it * kThreads + tid;
-      const int row = qd / ICH, cc = qd % ICH;
+      const int row = qd / ICH, c = qd % ICH;
       const int s = min(j * kBlock + row, p.S_k - 1);
-      itile[row * ICH + (cc ^ (row & (ICH - 1)))] = *reinterpret_cast<const u32x4*>(ib + (size_t)s * DIDX + 8 * cc);
+      itile[row * ICH + (c ^ (row & (ICH - 1)))] = *reinterpret_cast<const u32x4*>(ib + (size_t)s * DIDX + 8 * c);
     }
-  };
-  bool h0 = next(cur), h1 = false, h2 = false;
-  if (h0) load_tiles();  // uniform
-  // Whether this group's dk_part rows of the block already hold an earlier
-  // chunk's sums; read before the loop's barriers, written after them.
-  const bool any = h0;
-  const long flag_at = (long)bg * p.n_blk + j;
-  const bool had = !kp.first && kp.dk_flag[flag_at] != 0;
-  Fetched fx, fy;
-  Ids ide, ido;  // ids of the even and of the odd sub-tiles
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
-  // The dq_idx record of each query of a sub-tile, written by the lanes of
-  // its first row (the other rows hold the same values); every other lane,
-  // and the dummy stores of the prologue, write the sink.
-  auto store_records = [&](const f32x16& qacc, bool dummy) {
-    const int q = n / G, hh = n - (n / G) * G;
-    const int sl = dummy ? -1 : s_slot[q];
-    const long slot = hh == 0 && sl >= 0 ? sl : kp.sink;
-    float m = 0.f;
+  const int off = p.S_k - p.S_q;
+  const int n = lane & 31;                       // key column of this lane / A row
+  const int qm = n / G, hm = n - (n / G) * G;    // A row: query qm of the sub-tile, head hm
+  const float c = p.scale_log2;
+  const float invG = 1.f / G;
+
+  // Query (within the sub-tile) of query slot l of this lane: the D rows
+  // 8 (r / 4) + 4 h + r % 4 for r = l RPS .. l RPS + RPS - 1.
+  auto q_of = [&](int l) {
+    const int r0 = l * RPS;
+    return (8 * (r0 >> 2) + 4 * h + (r0 & 3)) / G;
+  };
+  auto load_q = [&](u32x4* dq, int i) {
+    const uint16_t* qrow = p.q + (((size_t)b * p.S_q + i) * p.H_q + g * G + hm) * kD + 8 * h;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) m = max3abs(qacc[r], qacc[r], m);
-    m = __builtin_fmaxf(m, swap_halves(m));
-    const float inv = m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
-    u32x4* rec = reinterpret_cast<u32x4*>(kp.rec + (slot * NDT + wave) * 32 + 16 * h);
+    for (int ks = 0; ks < 8; ++ks) dq[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
+  };
+  auto load_qi = [&](u32x4* di, int i) {
+    const uint16_t* irow = p.q_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX + 8 * h;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x4 v4;
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-        v4[x] = pack_f16x2(qacc[8 * half + 2 * x] * inv, qacc[8 * half + 2 * x + 1] * inv);
-      rec[half] = v4;
-    }
-    kp.rec_sc[slot * NDT + wave] = m;  // both halves store the same m
+    for (int ks = 0; ks < DIDX / 16; ++ks) di[ks] = *reinterpret_cast<const u32x4*>(irow + 16 * ks);
   };
 
-  // The block's operands that are the same for every sub-tile stay in
-  // registers once loaded (K_j rows of the wave's keys for S, their k_idx
-  // rows for z, k_idx^T of the wave's index dims for dq_idx), which takes
-  // three quarters of the LDS reads of a sub-tile off the LDS.
-  constexpr int NZ = G >= 8 ? 2 * (DIDX / 32) : DIDX / 16;
-  u32x4 kf[8], zf[NZ], qf[8];
-  auto load_frags = [&]() {
-    const int krow = key0 + n;
+  // With G >= 8 a sub-tile has at most 4 queries, and z (one value per query
+  // and key) takes 16x16x32 instructions whose A row m carries query m % 4
+  // (the last query repeated past QW): every 16-lane group of the result then
+  // holds all the queries, in register order, for its 16 keys.
+  constexpr bool kZ16 = G >= 8;
+  constexpr int ZKS = DIDX / 32;
+  const int qz = min(lane & 3, QW - 1);
+  auto load_qz = [&](u32x4* dz, int i) {
+    const uint16_t* irow = p.q_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX + 8 * (lane >> 4);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kf[ks] = ktile[krow * 16 + ((2 * ks + h) ^ (krow & 15))];
-    if constexpr (G >= 8) {
-      const int k0 = key0 + (lane & 15), k1 = k0 + 16;
-#pragma unroll
-      for (int ks = 0; ks < DIDX / 32; ++ks) {
-        const int ch = 4 * ks + (lane >> 4);
-        zf[2 * ks] = itile[k0 * ICH + (ch ^ (k0 & (ICH - 1)))];
-        zf[2 * ks + 1] = itile[k1 * ICH + (ch ^ (k1 & (ICH - 1)))];
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < DIDX / 16; ++ks) {
-        const int ch = 2 * ks + h;
-        zf[ks] = itile[krow * ICH + (ch ^ (krow & (ICH - 1)))];
-      }
-    }
-    if (wave < NDT) {
-      const int lr = lane & 15;
-      const int c0 = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int k0 = 16 * ks + 8 * h + (lr >> 2), k1 = k0 + 4;
-        const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k0, c0, k0 & (ICH - 1)));
-        const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(k1, c0, k1 & (ICH - 1)));
-        qf[ks] = u32x4{a0.x, a0.y, a1.x, a1.y};
-      }
-    }
+    for (int ks = 0; ks < ZKS; ++ks) dz[ks] = *reinterpret_cast<const u32x4*>(irow + 32 * ks);
   };
 
-  auto step = [&](Fetched& f, const Ids& use, Ids& load) {
-    __syncthreads();  // the previous sub-tile's LDS reads are done
-#pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      const int r = 2 * pr + y;
-      sq[r * 16 + (cc ^ rsw(r))] = f.qa[y];
-      if (cc < ICH) sqi[r * ICH + (cc ^ (rsw(r) & (ICH - 1)))] = f.qi[y];
-    }
-    if (tid < 32) {
-      const int x = f.id.e2;
-      const bool valid = (f.id.valid >> 2) & 1;
-      s_lse[tid] = valid ? f.lse : __builtin_inff();
-      if (tid % G == 0) {
-        const int i = slot_query(p, bg, x);
-        s_lsez[tid / G] = valid ? f.lsez * kLog2e : __builtin_inff();
-        s_t[tid / G] = valid ? i + off : -1;
-        s_slot[tid / G] = valid ? x : -1;
-      }
-    }
-    __syncthreads();
-    {
-      const bool h3 = h2 && next(cur);
-      load_ids(cur, load);
-      fetch(use, f);
-      h2 = h3;
-    }
-    asm volatile("" ::: "memory");
+  u32x4 qb[8], ib[kZ16 ? 1 : DIDX / 16], iz[kZ16 ? ZKS : 1];
+  load_q(qb, s_i[wave * QW + qm]);
+  if constexpr (kZ16) load_qz(iz, s_i[wave * QW + qz]);
+  else load_qi(ib, s_i[wave * QW + qm]);
+  for (int sub = 0; sub < n_here; sub += 4 * QW) {
+    const int e0 = sub + wave * QW;  // first edge of this wave's sub-tile
+    if (e0 >= n_here) break;         // wave-uniform
+    const int i_next = s_i[min(e0 + 4 * QW, QT - QW) + qm];
+    const int iz_next = s_i[min(e0 + 4 * QW, QT - QW) + qz];
 
-    // S and z for this wave's 32 keys: rows on registers, keys on lanes.
-    f32x16 sacc = zero16();
-    const int krow = key0 + n;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int ch = 2 * ks + h;
-      sacc = mfma32x32x16(sq[n * 16 + (ch ^ rsw(n))], kf[ks], sacc);
-    }
-    // z of query slot l at key key0 + n.  With G >= 8 a sub-tile has at most
-    // 4 queries: 16x16x32 tiles whose A row m is query m % 4 (the last one
-    // repeated past QW), keys key0 .. + 15 and key0 + 16 .. + 31; lane n takes
-    // the tile holding its key, and register l is query l (= the query of
-    // slot l).  Otherwise z repeats each query's index row on its heads' rows.
-    float zv[NL];
-    if constexpr (G >= 8) {
-      const int qr = min(lane & 3, QW - 1) * G;  // a row of query qr / G in sqi
-      const int k0 = key0 + (lane & 15), k1 = k0 + 16;
-      f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < DIDX / 32; ++ks) {
-        const int ch = 4 * ks + (lane >> 4);
-        const u32x4 a = sqi[qr * ICH + (ch ^ (rsw(qr) & (ICH - 1)))];
-        z0 = mfma16x16x32(a, zf[2 * ks], z0);
-        z1 = mfma16x16x32(a, zf[2 * ks + 1], z1);
-      }
-      const bool upper = (lane >> 4) & 1;
-#pragma unroll
-      for (int l = 0; l < NL; ++l) zv[l] = upper ? z1[l] : z0[l];
-    } else {
-      f32x16 zacc = zero16();
-#pragma unroll
-      for (int ks = 0; ks < DIDX / 16; ++ks) {
-        const int ch = 2 * ks + h;
-        zacc = mfma32x32x16(sqi[n * ICH + (ch ^ (rsw(n) & (ICH - 1)))], zf[ks], zacc);
-      }
-#pragma unroll
-      for (int l = 0; l < NL; ++l) zv[l] = zacc[l * RPS];
-    }
-    // Teacher per (query slot l, key): the mean over the query's heads.
-    float lse4[16];
+    float lse2[16];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const float4 a = *reinterpret_cast<const float4*>(&s_lse[8 * r4 + 4 * h]);
-      lse4[4 * r4] = a.x; lse4[4 * r4 + 1] = a.y; lse4[4 * r4 + 2] = a.z; lse4[4 * r4 + 3] = a.w;
+      const float4 v = *reinterpret_cast<const float4*>(&s_lse[e0 * G + 8 * r4 + 4 * h]);
+      lse2[4 * r4 + 0] = v.x; lse2[4 * r4 + 1] = v.y; lse2[4 * r4 + 2] = v.z; lse2[4 * r4 + 3] = v.w;
     }
-    float gq[NL];
+    int tq[NL];
+#pragma unroll
+    for (int l = 0; l < NL; ++l) tq[l] = s_i[e0 + q_of(l)] + off;
+
+    // Index scores first; the index rows of the next sub-tile load meanwhile.
+    float pt[4][NL], zv[4][NL];
+    if constexpr (kZ16) {
+      // Key tiles 2 nt and 2 nt + 1 (16 keys each); lane n (= lane % 32)
+      // takes key 32 nt + n from the first for n < 16, else from the second,
+      // and register l is query l (= q_of(l) for G >= 8).
+      const bool upper = (lane >> 4) & 1;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int k0 = nt * 32 + (lane & 15), k1 = k0 + 16;
+        f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < ZKS; ++ks) {
+          const int ch = 4 * ks + (lane >> 4);
+          z0 = mfma16x16x32(iz[ks], itile[k0 * ICH + (ch ^ (k0 & (ICH - 1)))], z0);
+          z1 = mfma16x16x32(iz[ks], itile[k1 * ICH + (ch ^ (k1 & (ICH - 1)))], z1);
+        }
+#pragma unroll
+        for (int l = 0; l < NL; ++l) zv[nt][l] = upper ? z1[l] : z0[l];
+      }
+      load_qz(iz, iz_next);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int krow = nt * 32 + n;
+        f32x16 za = zero16();
+#pragma unroll
+        for (int ks = 0; ks < DIDX / 16; ++ks)
+          za = mfma32x32x16(ib[ks], itile[krow * ICH + ((2 * ks + h) ^ (krow & (ICH - 1)))], za);
+#pragma unroll
+        for (int l = 0; l < NL; ++l) zv[nt][l] = za[l * RPS];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      load_qi(ib, i_next);
+    }
+    // S = Q K^T as a software pipeline, one MFMA per step (step st = 8 nt +
+    // ks, key tile nt) with a scheduling barrier between steps: each K
+    // fragment is read three steps ahead into a ring of four, and the
+    // teacher sums of tile nt - 1 run two values a step during tile nt's
+    // MFMAs (in the same order as one pass would add them).  Keys past a
+    // query are dropped after the head sum (the same keys for every head of
+    // the query), where vis is applied.  G = 1 keeps 64 teacher values per
+    // lane and has no registers for the ring: one tile at a time there.
+    if constexpr (G == 1) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int krow = nt * 32 + n;
+        f32x16 sa = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          sa = mfma32x32x16(qb[ks], ktile[krow * 16 + ((2 * ks + h) ^ (krow & 15))], sa);
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+          float acc = 0.f;
+#pragma unroll
+          for (int rr = 0; rr < RPS; ++rr) {
+            const int r = l * RPS + rr;
+            acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sa[r], c, -lse2[r]));
+          }
+          pt[nt][l] = acc;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      const u32x4* klane = ktile + n * 16;  // row 32 nt + n keeps its chunks swizzled by n & 15
+      auto kfrag = [&](int st) { return klane[(st >> 3) * 512 + ((2 * (st & 7) + h) ^ (n & 15))]; };
+      f32x16 sa[2];
+      // Values r, r + 1 of tile NT (accumulator sa[NT & 1]) into pt[NT].
+      auto teach2 = [&](auto NT, auto R) {
+        constexpr int nt = decltype(NT)::value, r = decltype(R)::value;
+#pragma unroll
+        for (int x = r; x < r + 2; ++x) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[nt & 1][x], c, -lse2[x]));
+          if (x % RPS == 0) pt[nt][x / RPS] = 0.f;
+          pt[nt][x / RPS] += e;
+        }
+      };
+      u32x4 ring[4];
+      static_for<0, 3>([&](auto P) { ring[P] = kfrag(P); });
+      static_for<0, 32>([&](auto S) {
+        constexpr int st = decltype(S)::value, nt = st / 8, ks = st % 8;
+        if constexpr (st + 3 < 32) ring[(st + 3) % 4] = kfrag(st + 3);
+        sa[nt & 1] = mfma32x32x16(qb[ks], ring[st % 4], ks == 0 ? zero16() : sa[nt & 1]);
+        if constexpr (nt >= 1) teach2(std::integral_constant<int, nt - 1>{}, std::integral_constant<int, 2 * ks>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      static_for<0, 8>([&](auto K) { teach2(std::integral_constant<int, 3>{}, std::integral_constant<int, 2 * K>{}); });
+    }
+    // Teacher and index score of each (query slot l, key tile u) of this
+    // lane.  For G >= 8 the halves hold head partial sums of the same queries:
+    // one swap32 per pair of key tiles completes the head sums and leaves
+    // tiles 0, 1 in half 0 and tiles 2, 3 in half 1 (sums then run over all 64
+    // lanes); for G <= 4 each half has its own queries and all four tiles.
+    constexpr int NT = G >= 8 ? 2 : 4;
+    float P[NL][NT], Z[NL][NT];
+    bool vis[NL][NT];
+#pragma unroll
+    for (int l = 0; l < NL; ++l)
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        float pv;
+        if constexpr (G >= 8) {
+          float a = pt[u][l], bq = pt[2 + u][l];
+          swap32(a, bq);
+          pv = (a + bq) * invG;
+          float za = zv[u][l], zb = zv[2 + u][l];
+          swap32(za, zb);
+          Z[l][u] = za;
+        } else {
+          pv = pt[u][l] * invG;
+          Z[l][u] = zv[u][l];
+        }
+        const int nt = G >= 8 ? 2 * h + u : u;
+        vis[l][u] = j * kBlock + nt * 32 + n <= tq[l];
+        P[l][u] = vis[l][u] ? pv : 0.f;
+      }
+    load_q(qb, i_next);  // lands while the statistics below are reduced
+
+    // g = c (P_idx - P) on visible keys, P_idx = 2^(z log2(e) - LSE_z).
+    // Stored as bf16 per (edge, key) for the dk_idx reduction and into this
+    // wave's LDS rows for dq_idx; each (query, key) is held by one lane.
+    const int wg = wave;
+    float lsz[NL];
+#pragma unroll
+    for (int l = 0; l < NL; ++l) lsz[l] = s_lsez[e0 + q_of(l)];
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
-      float acc = 0.f;
+      const int q = q_of(l);
+      uint16_t* grow = kp.g_rec + (size_t)s_slot[e0 + q] * kBlock;
 #pragma unroll
-      for (int rr = 0; rr < RPS; ++rr) {
-        const int r = l * RPS + rr;
-        acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c, -lse4[r]));
+      for (int u = 0; u < NT; ++u) {
+        const float pidx = __builtin_amdgcn_exp2f(__builtin_fmaf(Z[l][u], kLog2e, -lsz[l]));
+        const float gv = vis[l][u] ? kp.coef * (pidx - P[l][u]) : 0.f;
+        const uint16_t gb = (uint16_t)(pack_bf16x2(gv, 0.f) & 0xFFFFu);
+        const int key = (G >= 8 ? 2 * h + u : u) * 32 + n;
+        grow[key] = gb;
+        sg[wg][q][key] = gb;
       }
-      if constexpr (G >= 8) acc += swap_halves(acc);
-      const int q = mfma32_row(l * RPS, lane) / G;
-      const bool vis = key_abs <= s_t[q];
-      const float pidx = __builtin_amdgcn_exp2f(__builtin_fmaf(zv[l], kLog2e, -s_lsez[q]));
-      gq[l] = vis ? kp.coef * (pidx - acc * invG) : 0.f;
     }
-    // dk_idx += g^T q_idx: A = g of each register's row (a query's value on
-    // each of its G rows, times 1/G), B = the rows' index rows, transposed.
-    {
-      const int lr = lane & 15;
+
+    // dq_idx^T[d][q] = sum_key k_idx^T[d][key] g[q][key], 16x16x32 tiles: A
+    // = k_idx^T (transposing reads of the row-major index tile: lane i of
+    // each 16-lane group takes dim 16 t + i, keys 32 ks + 8 (lane / 16) + 0..7),
+    // B = g rows of the wave's queries (query 16 qg + lane % 16, clamped past
+    // QW).  Lane L then holds dims 16 t + 4 (L / 16) + 0..3 of that query.
+    constexpr int NDQ = DIDX / 16;
+    const int i16 = lane & 15, g16 = lane >> 4;
+    // Queries 16 qg + i16 (a 16-column MFMA per 16 queries of the sub-tile).
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4 ga;
+    for (int qg = 0; qg < (QW + 15) / 16; ++qg) {
+      f32x4 dqa[NDQ];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int r0 = 8 * kk + 2 * x;
-          ga[x] = pack_bf16x2(gq[r0 / RPS] * invG, gq[(r0 + 1) / RPS] * invG);
+      for (int t = 0; t < NDQ; ++t) dqa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int qcol = 16 * qg + i16;
+      const uint16_t* gq = &sg[wg][min(qcol, QW - 1)][0];
+#pragma unroll
+      for (int ks = 0; ks < kBlock / 32; ++ks) {
+        const u32x4 gbv = *reinterpret_cast<const u32x4*>(gq + 32 * ks + 8 * g16);
+        const int ra = 32 * ks + 8 * g16 + (i16 >> 2), rb = ra + 4;
+#pragma unroll
+        for (int t = 0; t < NDQ; ++t) {
+          const int c0 = 16 * t + 4 * (i16 & 3);
+          const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(ra, c0, ra & (ICH - 1)));
+          const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(itile) + lds_tile_off<ICH>(rb, c0, rb & (ICH - 1)));
+          dqa[t] = mfma16x16x32(u32x4{a0.x, a0.y, a1.x, a1.y}, gbv, dqa[t]);
         }
-        const int rbase = 16 * kk + 4 * h;
-        const int ra = rbase + (lr >> 2), rb = rbase + 8 + (lr >> 2);
+      }
+      // The record of query qcol (lanes with qcol < QW): per 32-dim quarter
+      // the largest magnitude m (over the quarter's two tiles and the four
+      // lanes of the query), the values / m as fp16 at the record positions
+      // the merge reads (rec_dim order: dim 16 (t % 2) + 4 g16 + x of the
+      // quarter at 16 (g16 % 2) + 8 (t % 2) + 4 (g16 / 2) + x).
+      const long slot = s_slot[e0 + min(qcol, QW - 1)];
+#pragma unroll
+      for (int qq = 0; qq < DIDX / 32; ++qq) {
+        float m = 0.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) m = max3abs(dqa[2 * qq][x], dqa[2 * qq + 1][x], m);
+        m = __builtin_fmaxf(m, __shfl_xor(m, 16, 64));
+        m = __builtin_fmaxf(m, __shfl_xor(m, 32, 64));
+        const float inv = m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
+        if (qcol < QW) {
+          uint16_t* rec = kp.rec + slot * DIDX + 32 * qq;
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2) {
+            const f32x4 v = dqa[2 * qq + t2];
+            uint2 w2;
+            w2.x = pack_f16x2(v[0] * inv, v[1] * inv);
+            w2.y = pack_f16x2(v[2] * inv, v[3] * inv);
+            *reinterpret_cast<uint2*>(rec + 16 * (g16 & 1) + 8 * t2 + 4 * (g16 >> 1)) = w2;
+          }
+          if (g16 == 0) kp.rec_sc[slot * (DIDX / 32) + qq] = m;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// dk_idx of block j for group (b, g): the sum over the block's edges (every
+// query window of the chunk, each bucket in its sorted order) of
+// g_e[key] q_idx[query(e)][g][:], with g from kl_grad_kernel.  Edges go
+// through LDS 32 at a time (g rows and index-query rows, row-swizzled);
+// wave w takes keys 32 w .. 32 w + 31 and all index dims, A = g^T and
+// B = q_idx^T both from transposing reads (lane (n, h) takes edges
+// 16 kk + 4 h + 0..3 and + 8..11 of step kk), the sums in registers.  This
+// group's part is stored (fp32, added across chunks) and
+// kl_dk_reduce_kernel adds the groups in a fixed order.
+template <int DIDX>
+__global__ __launch_bounds__(kThreads) void kl_dk_kernel(KlBwdParams kp) {
+  const Params& p = kp.e;
+  constexpr int ICH = DIDX / 8;   // 16-byte chunks per index row
+  constexpr int NDT = DIDX / 32;  // 32-dim tiles
+  constexpr int EB = 32;          // edges per batch
+  __shared__ u32x4 sgb[EB * 16];  // g rows [edge][128 keys], chunk c at c ^ rsw(edge)
+  __shared__ u32x4 sqb[EB * ICH]; // index-query rows [edge][DIDX], chunk c at c ^ (rsw(edge) & (ICH - 1))
+  const int BG = p.B * p.H_kv;
+  const int j = blockIdx.x / BG;  // early (busier) blocks first
+  const int bg = blockIdx.x - j * BG;
+  const int b = bg / p.H_kv;
+  const int g = bg - b * p.H_kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, n = lane & 31;
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = zero16();
+  const long flag_at = (long)bg * p.n_blk + j;
+  const bool had = !kp.first && kp.dk_flag[flag_at] != 0;
+  bool any = false;
+  const int lr = lane & 15;
+  for (int w = 0; w < p.n_win; ++w) {
+    const long bucket = ((long)bg * p.n_win + w) * p.n_blk + j;
+    const int cnt = __builtin_amdgcn_readfirstlane(p.counts[bucket]);
+    const int32_t* ed = p.edges + __builtin_amdgcn_readfirstlane(p.offsets[bucket]);
+    any |= cnt > 0;
+    for (int e0 = 0; e0 < cnt; e0 += EB) {  // uniform
+      __syncthreads();  // the previous batch's LDS reads are done
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {  // g: 32 rows x 16 chunks, two per thread
+        const int x = tid + kThreads * y, r = x >> 4, cc = x & 15;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (e0 + r < cnt) v = *reinterpret_cast<const u32x4*>(kp.g_rec + (size_t)ed[e0 + r] * kBlock + 8 * cc);
+        sgb[r * 16 + (cc ^ rsw(r))] = v;
+      }
+#pragma unroll
+      for (int y = 0; y < EB * ICH / kThreads; ++y) {  // index-query rows
+        const int x = tid + kThreads * y, r = x / ICH, cc = x % ICH;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (e0 + r < cnt) {
+          const int i = slot_query(p, bg, ed[e0 + r]);
+          v = *reinterpret_cast<const u32x4*>(p.q_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX + 8 * cc);
+        }
+        sqb[r * ICH + (cc ^ (rsw(r) & (ICH - 1)))] = v;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < EB / 16; ++kk) {
+        const int r0 = 16 * kk + 4 * h;
+        const int ra = r0 + (lr >> 2), rb = r0 + 8 + (lr >> 2);
+        const int ck = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
+        const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(sgb) + lds_tile_off(ra, ck, rsw(ra)));
+        const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(sgb) + lds_tile_off(rb, ck, rsw(rb)));
+        const u32x4 ga = {a0.x, a0.y, a1.x, a1.y};
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const int c0 = 32 * dt + 16 * (n >> 4) + 4 * (lr & 3);
-          const uint2 b0 = lds_read_tr16(reinterpret_cast<const char*>(sqi) + lds_tile_off<ICH>(ra, c0, rsw(ra) & (ICH - 1)));
-          const uint2 b1 = lds_read_tr16(reinterpret_cast<const char*>(sqi) + lds_tile_off<ICH>(rb, c0, rsw(rb) & (ICH - 1)));
-          const u32x4 bb = {b0.x, b0.y, b1.x, b1.y};
-          dk_acc[dt] = mfma32x32x16(ga, bb, dk_acc[dt]);
+          const int cd = 32 * dt + 16 * (n >> 4) + 4 * (lr & 3);
+          const uint2 b0 = lds_read_tr16(reinterpret_cast<const char*>(sqb) + lds_tile_off<ICH>(ra, cd, rsw(ra) & (ICH - 1)));
+          const uint2 b1 = lds_read_tr16(reinterpret_cast<const char*>(sqb) + lds_tile_off<ICH>(rb, cd, rsw(rb) & (ICH - 1)));
+          acc[dt] = mfma32x32x16(ga, u32x4{b0.x, b0.y, b1.x, b1.y}, acc[dt]);
         }
       }
     }
-    // g to LDS as [row][key] for dq_idx (each row carries its query's g).
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      sg[mfma32_row(r, lane) * kGStride + key0 + n] = (uint16_t)(pack_bf16x2(gq[r / RPS], 0.f) & 0xFFFFu);
-    __syncthreads();
-
-    // dq_idx^T[c'][row] = sum_key k_idx^T[c'][key] g[row][key] for index dims
-    // 32 wave .. 32 wave + 31 (waves past D_idx / 32 idle); one record per query.
-    if (wave < NDT) {
-      f32x16 qacc = zero16();
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const u32x4 gb = *reinterpret_cast<const u32x4*>(&sg[n * kGStride + 16 * ks + 8 * h]);
-        qacc = mfma32x32x16(qf[ks], gb, qacc);
-      }
-      store_records(qacc, false);
-    }
-  };
-  if (h0) {  // uniform
-    Ids i0;
-    load_ids(cur, i0);
-    h1 = next(cur);
-    load_ids(cur, ido);
-    fetch(i0, fx);
-    if (wave < NDT) store_records(zero16(), true);
-    h2 = h1 && next(cur);
-    load_ids(cur, ide);
-    fetch(ido, fy);
-    if (wave < NDT) store_records(zero16(), true);
   }
-  if (h0) {  // uniform
-    __syncthreads();  // the tiles are in LDS
-    load_frags();
-  }
-  while (h0) {  // uniform
-    bool hb = h2;
-    step(fx, ide, ido);
-    h0 = h1;
-    h1 = hb;
-    if (!h0) break;
-    hb = h2;
-    step(fy, ido, ide);
-    h0 = h1;
-    h1 = hb;
-  }
-
-  // This group's dk_idx for the wave's keys (fp32, summed over chunks).  A
-  // block that no edge of the chunk selects stores nothing: its flag tells
-  // the reduce whether the rows hold anything (on a decode-shaped problem
-  // nearly every block is such a block).
+  // This group's part of the wave's keys (fp32, summed over chunks); a block
+  // no edge of the chunk selects stores nothing, and its flag tells the
+  // reduce whether the rows hold anything.
   if (any) {  // uniform
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const int dcol = 32 * dt + n;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = j * kBlock + key0 + mfma32_row(r, lane);
+        const int key = j * kBlock + 32 * wave + mfma32_row(r, lane);
         if (key >= p.S_k) continue;
         float* o = kp.dk_part + (((size_t)b * p.H_kv + g) * p.S_k + key) * DIDX + dcol;
-        *o = had ? *o + dk_acc[dt][r] : dk_acc[dt][r];
+        *o = had ? *o + acc[dt][r] : acc[dt][r];
       }
     }
   }
@@ -480,14 +520,37 @@ __global__ __launch_bounds__(256) void kl_dk_reduce_kernel(KlBwdParams kp) {
   }
 }
 
+template <int G, int DIDX>
+void launch_kl_chunk_g(const AttnShape& s, const Layout& L, const KlBwdParams& kp, hipStream_t st) {
+  hipLaunchKernelGGL((kl_grad_kernel<G, DIDX>), dim3((unsigned)L.T), dim3(kThreads), 0, st, kp);
+  const long rows = (long)s.batch * s.H_kv * L.Qc;
+  hipLaunchKernelGGL(kl_dq_merge_kernel<DIDX>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, st, kp);
+  hipLaunchKernelGGL(kl_dk_kernel<DIDX>, dim3((unsigned)(s.batch * s.H_kv * s.n_blk)), dim3(kThreads), 0, st, kp);
+}
+
+template <int DIDX>
+hipError_t launch_kl_chunk_d(const AttnShape& s, const Layout& L, const KlBwdParams& kp, hipStream_t st) {
+  switch (kp.e.G) {
+    case 1: launch_kl_chunk_g<1, DIDX>(s, L, kp, st); break;
+    case 2: launch_kl_chunk_g<2, DIDX>(s, L, kp, st); break;
+    case 4: launch_kl_chunk_g<4, DIDX>(s, L, kp, st); break;
+    case 8: launch_kl_chunk_g<8, DIDX>(s, L, kp, st); break;
+    case 16: launch_kl_chunk_g<16, DIDX>(s, L, kp, st); break;
+    case 32: launch_kl_chunk_g<32, DIDX>(s, L, kp, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 namespace edges {
-hipError_t launch_kl_dq_merge(const KlBwdParams& kp, int D_idx, long rows, hipStream_t st) {
-  const dim3 grid((unsigned)((rows * 16 + 255) / 256));
-  if (D_idx == 64) hipLaunchKernelGGL(kl_dq_merge_kernel<64>, grid, dim3(256), 0, st, kp);
-  else hipLaunchKernelGGL(kl_dq_merge_kernel<128>, grid, dim3(256), 0, st, kp);
-  return hipGetLastError();
+hipError_t launch_kl_chunk(const AttnShape& s, const Layout& L, const KlBwdParams& kp, hipStream_t st) {
+  switch (kp.D_idx) {
+    case 64: return launch_kl_chunk_d<64>(s, L, kp, st);
+    case 128: return launch_kl_chunk_d<128>(s, L, kp, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_kl_dk_reduce(const KlBwdParams& kp, int D_idx, long blocks, hipStream_t st) {
@@ -496,41 +559,6 @@ hipError_t launch_kl_dk_reduce(const KlBwdParams& kp, int D_idx, long blocks, hi
   return hipGetLastError();
 }
 }  // namespace edges
-
-namespace {
-
-template <int G, int DIDX>
-hipError_t launch_kl_bwd_g(const AttnShape& s, const KlBwdLayout& K, KlBwdParams kp, hipStream_t st) {
-  const Layout& L = K.L;
-  for (int q0 = 0, ci = 0; q0 < s.S_q; q0 += L.Qc, ++ci) {
-    kp.e.q0 = q0;
-    kp.first = ci == 0;
-    launch_build(s, L, kp.e, st);
-    launch_bucket_sort(L, kp.e, st);
-    hipLaunchKernelGGL((kl_bwd_kernel<G, DIDX>), dim3((unsigned)(s.batch * s.H_kv * s.n_blk)), dim3(kThreads), 0, st, kp);
-    const long rows = (long)s.batch * s.H_kv * L.Qc;
-    hipLaunchKernelGGL(kl_dq_merge_kernel<DIDX>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, st, kp);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  hipLaunchKernelGGL(kl_dk_reduce_kernel<DIDX>, dim3((unsigned)((long)s.batch * s.n_blk)), dim3(256), 0, st, kp);
-  return hipGetLastError();
-}
-
-template <int DIDX>
-hipError_t launch_kl_bwd_d(const AttnShape& s, const KlBwdLayout& K, const KlBwdParams& kp, hipStream_t st) {
-  switch (kp.e.G) {
-    case 1: return launch_kl_bwd_g<1, DIDX>(s, K, kp, st);
-    case 2: return launch_kl_bwd_g<2, DIDX>(s, K, kp, st);
-    case 4: return launch_kl_bwd_g<4, DIDX>(s, K, kp, st);
-    case 8: return launch_kl_bwd_g<8, DIDX>(s, K, kp, st);
-    case 16: return launch_kl_bwd_g<16, DIDX>(s, K, kp, st);
-    case 32: return launch_kl_bwd_g<32, DIDX>(s, K, kp, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-}  // namespace
 
 hipError_t launch_kl_loss_bwd(const AttnShape& s, int D_idx, const uint16_t* q, const uint16_t* k,
                               const uint16_t* q_idx, const uint16_t* k_idx, const int32_t* idx,
@@ -549,15 +577,21 @@ hipError_t launch_kl_loss_bwd(const AttnShape& s, int D_idx, const uint16_t* q, 
   launch_lse_group(s, lse, lse_t, stream);
   kp.rec = reinterpret_cast<uint16_t*>(base + K.rec);
   kp.rec_sc = reinterpret_cast<float*>(base + K.rec_sc);
+  kp.g_rec = reinterpret_cast<uint16_t*>(base + K.g_rec);
   kp.sink = K.L.E;
   kp.dk_part = reinterpret_cast<float*>(base + K.dk_part);
   kp.dk_flag = reinterpret_cast<int32_t*>(base + K.dk_flag);
   kp.dq_idx = dq_idx; kp.dk_idx = dk_idx; kp.D_idx = D_idx;
-  switch (D_idx) {
-    case 64: return launch_kl_bwd_d<64>(s, K, kp, stream);
-    case 128: return launch_kl_bwd_d<128>(s, K, kp, stream);
-    default: return hipErrorInvalidValue;
+  const Layout& L = K.L;
+  for (int q0 = 0, ci = 0; q0 < s.S_q; q0 += L.Qc, ++ci) {
+    kp.e.q0 = q0;
+    kp.first = ci == 0;
+    launch_build(s, L, kp.e, stream);
+    launch_bucket_sort(L, kp.e, stream);
+    const hipError_t err = launch_kl_chunk(s, L, kp, stream);
+    if (err != hipSuccess) return err;
   }
+  return launch_kl_dk_reduce(kp, D_idx, (long)s.batch * s.n_blk, stream);
 }
 
 }  // namespace msa

@@ -131,7 +131,7 @@ int sparse_attn_bwd_chunks(const AttnShape& s, size_t ws_bytes) {
   return qc > 0 ? (s.S_q + qc - 1) / qc : 0;
 }
 
-// ---------------------------------------------------------------- fused backward
+// ---------------------------------------------------------------- both backward passes
 static size_t kl_bwd_per_query(const AttnShape& s, int D_idx);
 
 // Bytes of per-edge records per query: the main backward's and the loss
@@ -148,8 +148,10 @@ FusedBwdLayout make_fused_bwd_layout(const AttnShape& s, int D_idx, int Qc) {
   // One record past the chunk's edges takes the stores of padding rows.
   F.rec = o;     o = align256(o + (size_t)(L.E + 1) * D_idx * 2);
   F.rec_sc = o;  o = align256(o + (size_t)(L.E + 1) * (D_idx / 32) * 4);
+  F.g_rec = o;   o = align256(o + (size_t)(L.E + 1) * kBlock * 2);
   F.dk_part = o; o = align256(o + (size_t)s.batch * s.H_kv * s.S_k * D_idx * 4);
   F.dk_flag = o; o = align256(o + (size_t)s.batch * s.H_kv * s.n_blk * 4);
+  F.lse_t = o;   o = align256(o + (size_t)s.batch * s.H_q * s.S_q * 4);
   F.total = o;
   return F;
 }
@@ -193,9 +195,10 @@ Layout make_kl_layout(const AttnShape& s) {
 size_t kl_loss_workspace(const AttnShape& s) { return make_kl_layout(s).total; }
 
 // Bytes of per-edge records per query: each (b, g) row's topk dq_idx records
-// (D_idx fp16 values and one scale per 32 dims) and edge slots.
+// (D_idx fp16 values and one scale per 32 dims), g rows (128 bf16) and edge
+// slots.
 static size_t kl_bwd_per_query(const AttnShape& s, int D_idx) {
-  return (size_t)s.batch * s.H_kv * s.topk * ((size_t)D_idx * 2 + 16 + 4);
+  return (size_t)s.batch * s.H_kv * s.topk * ((size_t)D_idx * 2 + 16 + kBlock * 2 + 4);
 }
 
 // Workspace layout for query chunks of Qc queries.
@@ -209,6 +212,7 @@ KlBwdLayout make_kl_bwd_layout(const AttnShape& s, int D_idx, int Qc) {
   // One record past the chunk's edges takes the stores of padding rows.
   K.rec = o;     o = align256(o + (size_t)(L.E + 1) * D_idx * 2);
   K.rec_sc = o;  o = align256(o + (size_t)(L.E + 1) * (D_idx / 32) * 4);
+  K.g_rec = o;   o = align256(o + (size_t)(L.E + 1) * kBlock * 2);
   K.dk_part = o; o = align256(o + (size_t)s.batch * s.H_kv * s.S_k * D_idx * 4);
   K.dk_flag = o; o = align256(o + (size_t)s.batch * s.H_kv * s.n_blk * 4);
   K.lse_t = o;   o = align256(o + (size_t)s.batch * s.H_q * s.S_q * 4);

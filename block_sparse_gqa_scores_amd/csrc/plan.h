@@ -97,21 +97,22 @@ struct BwdLayout {
 BwdLayout make_bwd_layout(const AttnShape& s, int Qc);
 int bwd_chunk(const AttnShape& s, size_t ws_bytes);
 
-// Alignment-loss backward: bucket arrays, per-edge dq_idx records, per-group
-// fp32 dk_idx parts and their flags, grouped main-branch LSE.
+// Alignment-loss backward: bucket arrays, per-edge dq_idx records and g rows,
+// per-group fp32 dk_idx parts and their flags, grouped main-branch LSE.
 struct KlBwdLayout {
   edges::Layout L;
-  size_t rec, rec_sc, dk_part, dk_flag, lse_t, total;
+  size_t rec, rec_sc, g_rec, dk_part, dk_flag, lse_t, total;
 };
 KlBwdLayout make_kl_bwd_layout(const AttnShape& s, int D_idx, int Qc);
 int kl_bwd_chunk(const AttnShape& s, int D_idx, size_t ws_bytes);
 
-// Fused backward (both gradients over one walk of the edges): the main
-// backward's layout, then the loss backward's dq_idx records, per-group fp32
-// dk_idx parts and their flags.
+// Both backward passes in one call (msa_backward), on the same query chunks
+// and edge buckets: the main backward's layout, then the loss backward's
+// dq_idx records, g rows, per-group fp32 dk_idx parts and their flags, and
+// the grouped main-branch LSE.
 struct FusedBwdLayout {
   BwdLayout B;
-  size_t rec, rec_sc, dk_part, dk_flag, total;
+  size_t rec, rec_sc, g_rec, dk_part, dk_flag, lse_t, total;
 };
 FusedBwdLayout make_fused_bwd_layout(const AttnShape& s, int D_idx, int Qc);
 int fused_bwd_chunk(const AttnShape& s, int D_idx, size_t ws_bytes);

@@ -326,20 +326,21 @@ msa_status msa_kl_loss_bwd(const msa_dims* dims, const void* q, const void* k,
                            void* dk_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * The fused backward: msa_sparse_attn_bwd and msa_kl_loss_bwd in one pass
- * over the selected blocks (the MSA kernel notes fuse the proxy backward with
- * the main backward because the proxy's signal needs both probability sets
- * at once, The Architecture of Infinity, baystreetwire.com; Sparse Attention
- * Part II, section 3.2 for the loss).  One walk of the edges forms S = Q K^T
- * and P once for both: dq, dk, dv as msa_sparse_attn_bwd defines them, and
- * dq_idx, dk_idx (the gradient of grad_loss * loss) as msa_kl_loss_bwd does.
- * Inputs: q, k, v, q_idx, k_idx, block_idx as msa_forward; out and lse as the
- * forward returned them; lse_idx as msa_kl_loss_fwd wrote it for the same
- * selection; dout [B][S_q][H_q][D] bf16.  Outputs bf16, written in full:
- * dq like q, dk and dv like k and v, dq_idx like q_idx, dk_idx like k_idx;
- * each equals the separate entry point's output bit for bit at the same
- * ws_bytes (same arithmetic, same summation orders).  `ws` holds at least
- * msa_workspace_min_bytes(dims, MSA_ENTRY_BACKWARD) bytes (both passes'
+ * The whole backward in one call: msa_sparse_attn_bwd and msa_kl_loss_bwd
+ * over the same selection (the MSA kernel notes pair the proxy's backward
+ * with the main backward because the proxy's signal needs both probability
+ * sets, The Architecture of Infinity, baystreetwire.com; Sparse Attention
+ * Part II, section 3.2 for the loss).  Each query chunk's edge buckets are
+ * built and sorted once and serve both passes: dq, dk, dv as
+ * msa_sparse_attn_bwd defines them, and dq_idx, dk_idx (the gradient of
+ * grad_loss * loss) as msa_kl_loss_bwd does.  Inputs: q, k, v, q_idx, k_idx,
+ * block_idx as msa_forward; out and lse as the forward returned them; lse_idx
+ * as msa_kl_loss_fwd wrote it for the same selection; dout [B][S_q][H_q][D]
+ * bf16.  Outputs bf16, written in full: dq like q, dk and dv like k and v,
+ * dq_idx like q_idx, dk_idx like k_idx; when this call and the separate ones
+ * each run in one query chunk, every output equals the separate entry
+ * point's bit for bit (same kernels, same summation orders).  `ws` holds at
+ * least msa_workspace_min_bytes(dims, MSA_ENTRY_BACKWARD) bytes (both passes'
  * per-edge records); contents on entry do not matter.  Errors as the two
  * separate calls.
  */

@@ -1,11 +1,11 @@
-"""GPU parity of the fused backward (msa_backward through the C ABI): both
-gradients from one walk of the edges.
+"""GPU parity of the combined backward (msa_backward through the C ABI):
+both gradients in one call, the two passes sharing each query chunk's edge
+buckets.
 
-The fused pass forms dq, dk, dv with the main backward's arithmetic and
-dq_idx, dk_idx with the loss backward's, in the same summation orders, so at
-one query chunk each output must equal the separate entry point's bit for
-bit (msa_sparse_attn_bwd, msa_kl_loss_bwd), on every shape those tests
-cover.  With several query chunks (forced through a small workspace) the
+The combined call runs the main backward's kernels and the loss backward's,
+in the same summation orders, so at one query chunk each output must equal
+the separate entry point's bit for bit (msa_sparse_attn_bwd,
+msa_kl_loss_bwd), on every shape those tests cover.  With several query chunks (forced through a small workspace) the
 outputs are compared with the oracle's gradients on every row and key, by
 the one tolerance rule of gpu_util.check_close.  Outputs and workspaces are
 poisoned before every call.
@@ -67,7 +67,7 @@ def test_fused_equals_separate(w):
 
 def test_fused_spread_student_equals_separate():
     """With a spread student (two +-1 channels per index row) every token's
-    P_idx enters g; the fused pass still equals the separate ones."""
+    P_idx enters g; the combined call still equals the separate ones."""
     w = W("fb_spread_g8", 1, 700, 3000, 64, 8, topk=12)
     t = spread_index_queries(w, inputs_for(w))
     out, lse, idx, lse_idx = prepare(w, t)
@@ -79,7 +79,7 @@ def test_fused_spread_student_equals_separate():
 
 @pytest.mark.parametrize("chunks", [2, 3])
 def test_fused_chunked_against_oracle(chunks):
-    """A workspace that fits only part of the queries runs the fused pass in
+    """A workspace that fits only part of the queries runs the combined call in
     several chunks (dk, dv and dk_idx carry fp32 sums across them); every
     row's dq, dq_idx and every key's dk, dv, dk_idx against the oracle."""
     w = W("fb_chunks", 1, 1024, 1536, 16, 2, Didx=64, topk=6)
