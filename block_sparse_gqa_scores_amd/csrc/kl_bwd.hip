@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 2) void kl_grad_kernel(KlBwdParams kp) {
 // group's part is stored (fp32, added across chunks) and
 // kl_dk_reduce_kernel adds the groups in a fixed order.
 template <int DIDX>
-__global__ __launch_bounds__(kThreads) void kl_dk_kernel(KlBwdParams kp) {
+__global__ __launch_bounds__(kThreads, 2) void kl_dk_kernel(KlBwdParams kp) {
   const Params& p = kp.e;
   constexpr int ICH = DIDX / 8;   // 16-byte chunks per index row
   constexpr int NDT = DIDX / 32;  // 32-dim tiles
@@ -388,50 +388,136 @@ __global__ __launch_bounds__(kThreads) void kl_dk_kernel(KlBwdParams kp) {
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = zero16();
   const long flag_at = (long)bg * p.n_blk + j;
   const bool had = !kp.first && kp.dk_flag[flag_at] != 0;
-  bool any = false;
   const int lr = lane & 15;
-  for (int w = 0; w < p.n_win; ++w) {
-    const long bucket = ((long)bg * p.n_win + w) * p.n_blk + j;
-    const int cnt = __builtin_amdgcn_readfirstlane(p.counts[bucket]);
-    const int32_t* ed = p.edges + __builtin_amdgcn_readfirstlane(p.offsets[bucket]);
-    any |= cnt > 0;
-    for (int e0 = 0; e0 < cnt; e0 += EB) {  // uniform
-      __syncthreads();  // the previous batch's LDS reads are done
+  // Batches of up to EB edges of one window's bucket, windows ascending.
+  // Advances to the next batch; past the last one it returns false and
+  // leaves the cursor on the last batch, so its addresses stay valid.
+  struct Cursor {
+    int w, e0, cnt;
+    const int32_t* ed;
+  };
+  auto next = [&](Cursor& cu) {  // uniform
+    Cursor t = cu;
+    t.e0 += EB;
+    while (t.e0 >= t.cnt) {
+      if (++t.w >= p.n_win) return false;
+      const long bucket = ((long)bg * p.n_win + t.w) * p.n_blk + j;
+      t.cnt = __builtin_amdgcn_readfirstlane(p.counts[bucket]);
+      t.ed = p.edges + __builtin_amdgcn_readfirstlane(p.offsets[bucket]);
+      t.e0 = 0;
+    }
+    cu = t;
+    return true;
+  };
+  // This thread's rows of a batch: g rows r = tid / 16 + 16 y (chunk
+  // tid % 16) and index-query rows (tid + 256 y) / ICH.  A row past the
+  // bucket's end repeats its last edge (loaded, in bounds) and is flagged
+  // invalid, so it is staged as zeros.
+  constexpr int NQ = EB * ICH / kThreads;
+  struct Ids {
+    int eg[2], eq[NQ];
+    int valid;  // bit y: g row y; bit 2 + y: index-query row y
+  };
+  auto load_ids = [&](const Cursor& cu, Ids& d) {
+    int v = 0;
 #pragma unroll
-      for (int y = 0; y < 2; ++y) {  // g: 32 rows x 16 chunks, two per thread
-        const int x = tid + kThreads * y, r = x >> 4, cc = x & 15;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (e0 + r < cnt) v = *reinterpret_cast<const u32x4*>(kp.g_rec + (size_t)ed[e0 + r] * kBlock + 8 * cc);
-        sgb[r * 16 + (cc ^ rsw(r))] = v;
-      }
+    for (int y = 0; y < 2; ++y) {
+      const int r = (tid >> 4) + 16 * y;
+      d.eg[y] = cu.ed[min(cu.e0 + r, cu.cnt - 1)];
+      v |= (cu.e0 + r < cu.cnt) << y;
+    }
 #pragma unroll
-      for (int y = 0; y < EB * ICH / kThreads; ++y) {  // index-query rows
-        const int x = tid + kThreads * y, r = x / ICH, cc = x % ICH;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (e0 + r < cnt) {
-          const int i = slot_query(p, bg, ed[e0 + r]);
-          v = *reinterpret_cast<const u32x4*>(p.q_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX + 8 * cc);
-        }
-        sqb[r * ICH + (cc ^ (rsw(r) & (ICH - 1)))] = v;
-      }
-      __syncthreads();
+    for (int y = 0; y < NQ; ++y) {
+      const int r = (tid + kThreads * y) / ICH;
+      d.eq[y] = cu.ed[min(cu.e0 + r, cu.cnt - 1)];
+      v |= (cu.e0 + r < cu.cnt) << (2 + y);
+    }
+    d.valid = v;
+  };
+  struct Rows {
+    u32x4 g[2], q[NQ];
+    int valid;
+  };
+  auto fetch = [&](const Ids& d, Rows& f) {
 #pragma unroll
-      for (int kk = 0; kk < EB / 16; ++kk) {
-        const int r0 = 16 * kk + 4 * h;
-        const int ra = r0 + (lr >> 2), rb = r0 + 8 + (lr >> 2);
-        const int ck = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
-        const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(sgb) + lds_tile_off(ra, ck, rsw(ra)));
-        const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(sgb) + lds_tile_off(rb, ck, rsw(rb)));
-        const u32x4 ga = {a0.x, a0.y, a1.x, a1.y};
+    for (int y = 0; y < 2; ++y) f.g[y] = *reinterpret_cast<const u32x4*>(kp.g_rec + (size_t)d.eg[y] * kBlock + 8 * (tid & 15));
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int cd = 32 * dt + 16 * (n >> 4) + 4 * (lr & 3);
-          const uint2 b0 = lds_read_tr16(reinterpret_cast<const char*>(sqb) + lds_tile_off<ICH>(ra, cd, rsw(ra) & (ICH - 1)));
-          const uint2 b1 = lds_read_tr16(reinterpret_cast<const char*>(sqb) + lds_tile_off<ICH>(rb, cd, rsw(rb) & (ICH - 1)));
-          acc[dt] = mfma32x32x16(ga, u32x4{b0.x, b0.y, b1.x, b1.y}, acc[dt]);
-        }
+    for (int y = 0; y < NQ; ++y) {
+      const int i = slot_query(p, bg, d.eq[y]);
+      const int cc = (tid + kThreads * y) % ICH;
+      f.q[y] = *reinterpret_cast<const u32x4*>(p.q_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX + 8 * cc);
+    }
+    f.valid = d.valid;
+  };
+  auto stage = [&](const Rows& f) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int r = (tid >> 4) + 16 * y, cc = tid & 15;
+      sgb[r * 16 + (cc ^ rsw(r))] = (f.valid >> y) & 1 ? f.g[y] : z;
+    }
+#pragma unroll
+    for (int y = 0; y < NQ; ++y) {
+      const int x = tid + kThreads * y, r = x / ICH, cc = x % ICH;
+      sqb[r * ICH + (cc ^ (rsw(r) & (ICH - 1)))] = (f.valid >> (2 + y)) & 1 ? f.q[y] : z;
+    }
+  };
+  // Pipeline: batch n stages the rows fetched during n - 2, then requests
+  // the ids of n + 3 and the rows of n + 2 before its products, so two
+  // batches of loads are in flight behind each batch's barrier and MFMAs
+  // (a block chosen by most queries walks thousands of batches).
+  Cursor cur{-1, -EB, 0, nullptr};
+  bool h0 = next(cur), h1 = false, h2 = false;
+  const bool any = h0;  // some edge of this chunk selects the block
+  Rows fx, fy;
+  Ids ide, ido;  // ids of the even and of the odd batches
+  if (h0) {
+    Ids i0;
+    load_ids(cur, i0);
+    h1 = next(cur);
+    load_ids(cur, ido);
+    fetch(i0, fx);
+    h2 = h1 && next(cur);
+    load_ids(cur, ide);
+    fetch(ido, fy);
+  }
+  auto step = [&](Rows& f, const Ids& use, Ids& load) {
+    __syncthreads();  // the previous batch's LDS reads are done
+    stage(f);
+    __syncthreads();
+    {
+      const bool h3 = h2 && next(cur);
+      load_ids(cur, load);
+      fetch(use, f);
+      h2 = h3;
+    }
+#pragma unroll
+    for (int kk = 0; kk < EB / 16; ++kk) {
+      const int r0 = 16 * kk + 4 * h;
+      const int ra = r0 + (lr >> 2), rb = r0 + 8 + (lr >> 2);
+      const int ck = 32 * wave + 16 * (n >> 4) + 4 * (lr & 3);
+      const uint2 a0 = lds_read_tr16(reinterpret_cast<const char*>(sgb) + lds_tile_off(ra, ck, rsw(ra)));
+      const uint2 a1 = lds_read_tr16(reinterpret_cast<const char*>(sgb) + lds_tile_off(rb, ck, rsw(rb)));
+      const u32x4 ga = {a0.x, a0.y, a1.x, a1.y};
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int cd = 32 * dt + 16 * (n >> 4) + 4 * (lr & 3);
+        const uint2 b0 = lds_read_tr16(reinterpret_cast<const char*>(sqb) + lds_tile_off<ICH>(ra, cd, rsw(ra) & (ICH - 1)));
+        const uint2 b1 = lds_read_tr16(reinterpret_cast<const char*>(sqb) + lds_tile_off<ICH>(rb, cd, rsw(rb) & (ICH - 1)));
+        acc[dt] = mfma32x32x16(ga, u32x4{b0.x, b0.y, b1.x, b1.y}, acc[dt]);
       }
     }
+  };
+  while (h0) {  // uniform
+    bool hb = h2;
+    step(fx, ide, ido);
+    h0 = h1;
+    h1 = hb;
+    if (!h0) break;
+    hb = h2;
+    step(fy, ido, ide);
+    h0 = h1;
+    h1 = hb;
   }
   // This group's part of the wave's keys (fp32, summed over chunks); a block
   // no edge of the chunk selects stores nothing, and its flag tells the
