@@ -104,10 +104,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
   __shared__ int s_slot[QW];
 
   const int BG = p.B * p.H_kv;
-  const int j = blockIdx.x / BG;            // early (busier) blocks first
-  const int bg = blockIdx.x - j * BG;
+  const long nblk = (long)BG * p.n_blk;
+  if ((long)blockIdx.x >= bp.blk_item[nblk]) return;  // uniform: past the last work item
+  // Work item: segment sg of the sub-tiles of (j, bg), early (busier) blocks
+  // first; a block with one segment is walked whole.
+  const int2 item = bp.items[blockIdx.x];
+  const int x = item.x, sg = item.y;
+  const int j = x / BG;
+  const int bg = x - j * BG;
   const int b = bg / p.H_kv;
   const int g = bg - b * p.H_kv;
+  const int nseg = bp.blk_item[x + 1] - bp.blk_item[x];
+  const int n_tiles = bp.blk_t[x];
+  const int seg_len = (n_tiles + nseg - 1) / nseg;
+  const int first_tile = sg * seg_len;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int n = lane & 31;
   const int off = p.S_k - p.S_q;
@@ -127,11 +137,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
   struct Cursor {
     int w, base, cnt;
     const int32_t* ed;
+    int left;  // sub-tiles of the segment still to come
   };
-  // Advances to the next sub-tile; past the last one it returns false and
-  // leaves the cursor on the last sub-tile, so its addresses stay valid.
+  // Advances to the next sub-tile; past the segment's last one it returns
+  // false and leaves the cursor on that sub-tile, so its addresses stay valid.
   auto next = [&](Cursor& cu) {  // uniform
+    if (cu.left <= 0) return false;
     Cursor t = cu;
+    --t.left;
     t.base += QW;
     while (t.base >= t.cnt) {
       if (++t.w >= p.n_win) return false;
@@ -212,7 +225,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
   // the same on every iteration and the waits stay exact: the rows of n + 1
   // and the records of n - 1 stay in flight while n stages.  The prologue
   // issues the same sequence, with two dummy record stores.
-  Cursor cur{-1, -QW, 0, nullptr};
+  Cursor cur{-1, -QW, 0, nullptr, max(0, min(seg_len, n_tiles - first_tile))};
+  if (first_tile > 0) {  // uniform: start at the segment's first sub-tile
+    int skip = first_tile;
+    for (int w = 0; w < p.n_win; ++w) {
+      const long bucket = ((long)bg * p.n_win + w) * p.n_blk + j;
+      const int cnt = __builtin_amdgcn_readfirstlane(p.counts[bucket]);
+      const int t = (cnt + QW - 1) / QW;
+      if (skip < t) {
+        cur.w = w;
+        cur.base = (skip - 1) * QW;  // next() moves to sub-tile `skip` of this bucket
+        cur.cnt = cnt;
+        cur.ed = p.edges + __builtin_amdgcn_readfirstlane(p.offsets[bucket]);
+        break;
+      }
+      skip -= t;
+    }
+  }
   // The block's tiles, loaded only when some edge selects the block (a
   // workgroup without edges just writes zero gradients).
   auto load_tiles = [&]() {  // K_j, V_j row-major into LDS (rows past S_k clamped: masked for every query)
@@ -394,6 +423,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
     h1 = hb;
   }
 
+  // A segment of a split block leaves its fp32 part, summed in segment order
+  // with the other segments' by seg_reduce_kernel.
+  if (nseg > 1) {  // uniform
+    float* pk = bp.part + (size_t)(bp.blk_part[x] + sg) * 2 * kBlock * kD;
+    float* pv = pk + kBlock * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int o = (key0 + mfma32_row(r, lane)) * kD + 32 * dt + n;
+        pk[o] = dk_acc[dt][r] * bp.scale;
+        pv[o] = dv_acc[dt][r];
+      }
+    }
+    return;
+  }
+
   // A block that no edge of the chunk selects adds nothing: in a middle chunk
   // the running sums stay as they are, and a one-chunk problem writes zero
   // rows 16 bytes at a time (on a decode-shaped problem nearly every block is
@@ -507,6 +553,105 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdParams bp) {
   }
 }
 
+// Sub-tiles of each (group, block) in the chunk, and its number of work
+// items: max(1, ceil(T / seg)), kept in blk_item until the scan.
+__global__ __launch_bounds__(256) void seg_count_kernel(BwdParams bp, int QW) {
+  const Params& p = bp.e;
+  const int BG = p.B * p.H_kv;
+  const long x = (long)blockIdx.x * 256 + threadIdx.x;
+  if (x >= (long)BG * p.n_blk) return;
+  const int j = (int)(x / BG), bg = (int)(x % BG);
+  int T = 0;
+  for (int w = 0; w < p.n_win; ++w) T += (p.counts[((long)bg * p.n_win + w) * p.n_blk + j] + QW - 1) / QW;
+  bp.blk_t[x] = T;
+  bp.blk_item[x] = T > bp.seg ? (T + bp.seg - 1) / bp.seg : 1;
+}
+
+// One workgroup: exclusive scans of the work items and of the partial slots
+// (split blocks only) in x order, the totals at blk_item[nblk], and the
+// work-item list: the segments of split blocks first (the longest items, so
+// none of them starts last), then the other blocks in x order.  Each thread
+// takes a contiguous run of x.
+__global__ __launch_bounds__(256) void seg_scan_kernel(BwdParams bp, long nblk) {
+  __shared__ int32_t sa[256], sb[256];
+  const int tid = threadIdx.x;
+  const long per = (nblk + 255) / 256;
+  const long x0 = min(nblk, tid * per), x1 = min(nblk, x0 + per);
+  int na = 0, nb = 0;
+  for (long x = x0; x < x1; ++x) {
+    const int k = bp.blk_item[x];
+    na += k;
+    nb += k > 1 ? k : 0;
+  }
+  sa[tid] = na;
+  sb[tid] = nb;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {  // Hillis-Steele inclusive scan
+    const int a = tid >= d ? sa[tid - d] : 0;
+    const int c = tid >= d ? sb[tid - d] : 0;
+    __syncthreads();
+    sa[tid] += a;
+    sb[tid] += c;
+    __syncthreads();
+  }
+  int oa = sa[tid] - na, ob = sb[tid] - nb;
+  const int n_split = sb[255];  // work items of split blocks
+  for (long x = x0; x < x1; ++x) {
+    const int k = bp.blk_item[x];
+    bp.blk_item[x] = oa;
+    bp.blk_part[x] = ob;
+    if (k > 1) {
+      for (int u = 0; u < k; ++u) bp.items[ob + u] = make_int2((int)x, u);
+    } else {
+      bp.items[n_split + oa - ob] = make_int2((int)x, 0);  // oa - ob: unsplit blocks before x
+    }
+    oa += k;
+    ob += k > 1 ? k : 0;
+  }
+  if (tid == 255) bp.blk_item[nblk] = sa[255];
+}
+
+// dK, dV of each split (group, block): its segments' fp32 parts added in
+// segment order, then what the unsplit path does (the earlier chunks' sums
+// added, bf16 out after the last chunk, fp32 sums kept before it).
+__global__ __launch_bounds__(256) void seg_reduce_kernel(BwdParams bp) {
+  const Params& p = bp.e;
+  const int BG = p.B * p.H_kv;
+  const long x = blockIdx.x;
+  const int nseg = bp.blk_item[x + 1] - bp.blk_item[x];
+  if (nseg <= 1) return;  // uniform
+  const int j = (int)(x / BG), bg = (int)(x % BG);
+  const int b = bg / p.H_kv, g = bg - (bg / p.H_kv) * p.H_kv;
+  const float* base = bp.part + (size_t)bp.blk_part[x] * 2 * kBlock * kD;
+  constexpr int kSlot = 2 * kBlock * kD;
+  for (int c = threadIdx.x; c < kBlock * kD / 4; c += 256) {  // 4 values of one key row
+    const int key = j * kBlock + c / (kD / 4);
+    if (key >= p.S_k) break;  // rows past S_k come last
+    float4 sk = *reinterpret_cast<const float4*>(base + 4 * c);
+    float4 sv = *reinterpret_cast<const float4*>(base + kBlock * kD + 4 * c);
+    for (int u = 1; u < nseg; ++u) {
+      const float4 ak = *reinterpret_cast<const float4*>(base + (size_t)u * kSlot + 4 * c);
+      const float4 av = *reinterpret_cast<const float4*>(base + (size_t)u * kSlot + kBlock * kD + 4 * c);
+      sk.x += ak.x; sk.y += ak.y; sk.z += ak.z; sk.w += ak.w;
+      sv.x += av.x; sv.y += av.y; sv.z += av.z; sv.w += av.w;
+    }
+    const size_t o = (((size_t)b * p.S_k + key) * p.H_kv + g) * kD + 4 * (c % (kD / 4));
+    if (!bp.first) {
+      const float4 ak = *reinterpret_cast<const float4*>(bp.dk_acc + o);
+      const float4 av = *reinterpret_cast<const float4*>(bp.dv_acc + o);
+      sk.x += ak.x; sk.y += ak.y; sk.z += ak.z; sk.w += ak.w;
+      sv.x += av.x; sv.y += av.y; sv.z += av.z; sv.w += av.w;
+    }
+    if (bp.last) {
+      *reinterpret_cast<uint2*>(bp.dk + o) = make_uint2(pack_bf16x2(sk.x, sk.y), pack_bf16x2(sk.z, sk.w));
+      *reinterpret_cast<uint2*>(bp.dv + o) = make_uint2(pack_bf16x2(sv.x, sv.y), pack_bf16x2(sv.z, sv.w));
+    } else {
+      *reinterpret_cast<float4*>(bp.dk_acc + o) = sk;
+      *reinterpret_cast<float4*>(bp.dv_acc + o) = sv;
+    }
+  }
+}
+
 }  // namespace
 
 namespace edges {
@@ -520,8 +665,12 @@ namespace {
 
 // The main backward of one chunk, after the chunk's bucket build and sort.
 template <int G>
-void launch_main_chunk(const AttnShape& s, const Layout& L, const BwdParams& bp, hipStream_t st) {
-  hipLaunchKernelGGL((attn_bwd_kernel<G>), dim3((unsigned)(s.batch * s.H_kv * s.n_blk)), dim3(kThreads), 0, st, bp);
+void launch_main_chunk(const AttnShape& s, const Layout& L, const BwdParams& bp, long n_items, hipStream_t st) {
+  const long nblk = (long)s.batch * s.H_kv * s.n_blk;
+  hipLaunchKernelGGL(seg_count_kernel, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, st, bp, 32 / G);
+  hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(256), 0, st, bp, nblk);
+  hipLaunchKernelGGL((attn_bwd_kernel<G>), dim3((unsigned)n_items), dim3(kThreads), 0, st, bp);
+  hipLaunchKernelGGL(seg_reduce_kernel, dim3((unsigned)nblk), dim3(256), 0, st, bp);
   const long mrows = (long)s.batch * s.H_kv * L.Qc;
   hipLaunchKernelGGL(dq_merge_kernel<G>, dim3((unsigned)((mrows + 3) / 4)), dim3(256), 0, st, bp);
 }
@@ -537,7 +686,7 @@ hipError_t launch_bwd_g(const AttnShape& s, const BwdLayout& BL, BwdParams bp, h
     bp.last = q0 + L.Qc >= s.S_q;
     launch_build(s, L, bp.e, st);
     launch_bucket_sort(L, bp.e, st);
-    launch_main_chunk<G>(s, L, bp, st);
+    launch_main_chunk<G>(s, L, bp, BL.n_items, st);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -559,7 +708,7 @@ hipError_t launch_both_g(const AttnShape& s, const FusedBwdLayout& FL, BwdParams
     kp.first = ci == 0;
     launch_build(s, L, bp.e, st);
     launch_bucket_sort(L, bp.e, st);
-    launch_main_chunk<G>(s, L, bp, st);
+    launch_main_chunk<G>(s, L, bp, FL.B.n_items, st);
     kp.e = bp.e;
     const hipError_t err = launch_kl_chunk(s, L, kp, st);
     if (err != hipSuccess) return err;
@@ -568,6 +717,16 @@ hipError_t launch_both_g(const AttnShape& s, const FusedBwdLayout& FL, BwdParams
 }
 
 }  // namespace
+
+// The work-item arrays of the main backward in a workspace laid out by BL.
+static void set_segments(BwdParams& bp, const BwdLayout& BL, char* base) {
+  bp.seg = BL.seg;
+  bp.blk_t = reinterpret_cast<int32_t*>(base + BL.blk_t);
+  bp.blk_item = reinterpret_cast<int32_t*>(base + BL.blk_item);
+  bp.blk_part = reinterpret_cast<int32_t*>(base + BL.blk_part);
+  bp.items = reinterpret_cast<int2*>(base + BL.items);
+  bp.part = reinterpret_cast<float*>(base + BL.part);
+}
 
 hipError_t launch_backward(const AttnShape& s, int D_idx, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, const uint16_t* q_idx, const uint16_t* k_idx,
@@ -590,6 +749,7 @@ hipError_t launch_backward(const AttnShape& s, int D_idx, const uint16_t* q, con
   bp.dq_sc = reinterpret_cast<float*>(base + BL.dq_sc);
   bp.dk_acc = reinterpret_cast<float*>(base + BL.dk_acc);
   bp.dv_acc = reinterpret_cast<float*>(base + BL.dv_acc);
+  set_segments(bp, BL, base);
   bp.dq = dq; bp.dk = dk; bp.dv = dv;
   bp.scale = s.scale;
   float* lse_t = reinterpret_cast<float*>(base + FL.lse_t);
@@ -635,6 +795,7 @@ hipError_t launch_sparse_attn_bwd(const AttnShape& s, const uint16_t* q, const u
   bp.dq_sc = reinterpret_cast<float*>(base + BL.dq_sc);
   bp.dk_acc = reinterpret_cast<float*>(base + BL.dk_acc);
   bp.dv_acc = reinterpret_cast<float*>(base + BL.dv_acc);
+  set_segments(bp, BL, base);
   bp.dq = dq; bp.dk = dk; bp.dv = dv;
   bp.scale = s.scale;
   switch (bp.e.G) {

@@ -27,6 +27,15 @@ struct BwdParams {
   float* dv_acc;
   float scale;           // softmax scale
   int first, last;       // this chunk is the first / the last
+  // Work items of attn_bwd_kernel: the sub-tiles of a (group, block) in
+  // segments of about `seg`, so that a block most queries select spreads
+  // over several workgroups.  Index x = j * B * H_kv + b * H_kv + g.
+  int seg;               // sub-tiles per segment; a block with more is split
+  int32_t* blk_t;        // [x]: the block's sub-tiles in this chunk
+  int32_t* blk_item;     // [x]: first work item of x (NBLK + 1, total at the end)
+  int32_t* blk_part;     // [x]: first partial slot of a split x
+  int2* items;           // (x, segment)
+  float* part;           // [slot][2][kBlock][kD]: one segment's fp32 dK (times scale), dV
 };
 
 struct KlBwdParams {

@@ -105,6 +105,21 @@ BwdLayout make_bwd_layout(const AttnShape& s, int Qc) {
   const size_t kv = (size_t)s.batch * s.S_k * s.H_kv * kD * 4;
   B.dk_acc = o; o = align256(o + (B.chunks > 1 ? kv : 0));
   B.dv_acc = o; o = align256(o + (B.chunks > 1 ? kv : 0));
+  // Segments: `sub` bounds the chunk's sub-tiles (a bucket adds at most one
+  // partial one).  A block of T sub-tiles takes max(1, ceil(T / seg)) work
+  // items, at most 1 + T / seg, and when split (T > seg) at most 2 T / seg
+  // partial slots.
+  const int QW = 32 / G;
+  const long nblk = (long)s.batch * s.H_kv * s.n_blk;
+  const long sub = (L.E + QW - 1) / QW + std::min(L.NB, L.E);
+  B.seg = (int)std::max(kSegMin, (L.E / QW + kSegSpread - 1) / kSegSpread);
+  B.n_items = nblk + sub / B.seg + 1;
+  B.n_part = 2 * sub / B.seg + 1;
+  B.blk_t = o;    o = align256(o + (size_t)nblk * 4);
+  B.blk_item = o; o = align256(o + (size_t)(nblk + 1) * 4);
+  B.blk_part = o; o = align256(o + (size_t)nblk * 4);
+  B.items = o;    o = align256(o + (size_t)B.n_items * 8);
+  B.part = o;     o = align256(o + (size_t)B.n_part * 2 * kBlock * kD * 4);
   B.total = o;
   L.total = o;
   return B;

@@ -89,10 +89,17 @@ int fwd_chunk(const AttnShape& s, size_t ws_bytes);
 
 // Main backward: bucket arrays, per-row statistics, per-edge dq records, and
 // fp32 dk / dv sums when there is more than one chunk.
+// A (group, block) with more than `seg` sub-tiles in a chunk is split into
+// segments whose fp32 dK / dV parts are summed afterwards: seg is the
+// chunk's expected sub-tiles spread over kSegSpread work items, at least
+// kSegMin.
+constexpr long kSegSpread = 4096;
+constexpr long kSegMin = 512;
 struct BwdLayout {
   edges::Layout L;
-  size_t stat, dq_rec, dq_sc, dk_acc, dv_acc, total;
-  int chunks;
+  size_t stat, dq_rec, dq_sc, dk_acc, dv_acc, blk_t, blk_item, blk_part, items, part, total;
+  int chunks, seg;
+  long n_items, n_part;  // bounds on work items and on partial slots
 };
 BwdLayout make_bwd_layout(const AttnShape& s, int Qc);
 int bwd_chunk(const AttnShape& s, size_t ws_bytes);

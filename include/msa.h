@@ -288,8 +288,10 @@ msa_status msa_kl_loss_fwd(const msa_dims* dims, const void* q, const void* k,
  * Sums run in a fixed order: results are identical
  * from run to run for the same ws_bytes.  `ws` holds at least
  * msa_workspace_min_bytes(dims, MSA_ENTRY_SPARSE_ATTN_BWD) bytes (edge lists,
- * per-edge dq records of G * (2 D + 16) bytes per chunk, and fp32 dk / dv
- * sums when the queries run in several chunks); contents on entry do not
+ * per-edge dq records of G * (3 D / 2 + 16) bytes per chunk, fp32 dk / dv
+ * parts of the key blocks so many queries select that their gradient is
+ * split over several workgroups, 128 KiB per part, and fp32 dk / dv sums
+ * when the queries run in several chunks); contents on entry do not
  * matter.  Uses the main-branch fields of
  * dims (index_dim is ignored).
  */

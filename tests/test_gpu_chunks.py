@@ -11,7 +11,8 @@ row and every key:
     arithmetic does not depend on which chunk it falls in);
   - main backward: dq of every row, dk and dv of every key, including keys
     selected by queries of several chunks (the first / middle / last chunk
-    sums), against the oracle's fp64 gradients;
+    sums) and a key block whose gradient is split over several workgroups
+    in every chunk, against the oracle's fp64 gradients;
   - alignment-loss backward: dq_idx of every row and dk_idx of every key.
 
 Outputs and workspaces are poisoned before every call.
@@ -146,6 +147,44 @@ def test_backward_chunked_every_key():
     print(f"blocks selected from the first and the last chunk: {shared.tolist()}", flush=True)
     assert len(shared) > 0
     for n, ws in zip((2, 3), chunk_sizes(w, msa.ENTRY_SPARSE_ATTN_BWD, (2, 3))):
+        dq, dk, dv = _bwd(w, t, idx, out, lse, ws)
+        dqn = dq.float().cpu().numpy()
+        check_close(f"{n} chunks dq", np.stack([dqn[b, i, g * G:(g + 1) * G] for b, i, g in rows]), rdq,
+                    float(np.abs(rdq).max()))
+        check_close(f"{n} chunks dk", dk.float().cpu().numpy(), rdk, float(np.abs(rdk).max()))
+        check_close(f"{n} chunks dv", dv.float().cpu().numpy(), rdv, float(np.abs(rdv).max()))
+
+
+# G = 32 (one query per 32-row sub-tile) with block 0 chosen by nearly every
+# query: its dK, dV walk ~2000 sub-tiles in one chunk and ~1000 / ~700 per
+# chunk in two / three, each more than the 512 sub-tiles after which a
+# block's gradient is split over several workgroups and its fp32 parts are
+# summed (first, middle and last chunk).
+SPLIT = W("chunked_split", 1, 2048, 2048, 32, 1, Didx=64, topk=3, gain=True)
+
+
+def test_backward_split_blocks_every_key():
+    w = SPLIT
+    t = inputs_for(w)
+    t["dout"] = torch.empty_like(t["q"])
+    synth.fill_device(w, "dout", t["dout"])
+    o = forward_outputs(w)
+    out, lse, idx = msa.msa_forward(t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], topk=w.topk, **o)
+    p = oracle.Problem.of(w)
+    h = host_inputs(t)
+    h["dout"] = to_u16(t["dout"])
+    rows = p.all_rows()
+    ref = oracle.forward(p, h["q"], h["k"], h["v"], h["q_idx"], h["k_idx"], rows=rows)
+    assert (idx.cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]] == ref["sel"]).all()
+    sel = ref["sel"]
+    for a, b in ((0, 768), (768, 1536), (1536, 2048)):  # the rows of every chunk below
+        m = (rows[:, 1] >= a) & (rows[:, 1] < b)
+        assert (sel[m] == 0).any(axis=1).sum() > 0.95 * (b - a), f"block 0 not chosen by rows {a}..{b}"
+    rdq, rdk, rdv = oracle.attention_bwd(p, h["q"], h["k"], h["v"], h["dout"], sel, rows)
+    G = w.group
+    d = dims(w)
+    for n in (1, 2, 3):
+        ws = msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_BWD) if n == 1 else chunk_sizes(w, msa.ENTRY_SPARSE_ATTN_BWD, (n,))[0]
         dq, dk, dv = _bwd(w, t, idx, out, lse, ws)
         dqn = dq.float().cpu().numpy()
         check_close(f"{n} chunks dq", np.stack([dqn[b, i, g * G:(g + 1) * G] for b, i, g in rows]), rdq,
