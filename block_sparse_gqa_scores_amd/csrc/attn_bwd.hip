@@ -60,16 +60,78 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams bp) {
 // order that depends on scheduling).  Bitonic network in LDS over the next
 // power of two of the bucket's size; SIZE bounds the buckets this instance
 // takes (the other instance skips them).
+//
+// Large buckets first try a counting sort: slot = row * topk + e with row =
+// bg * Qc + il, and a bucket (bg, window w, block j) holds at most one entry
+// per query of the window unless a row repeats a block.  One bit per query
+// of the window marks the bucket's rows and the entry index e is kept
+// beside it; the set bits, taken in order, give the slots in ascending
+// order.  A repeated row (a bit found set) leaves the bucket to the network.
 template <int SIZE, bool LARGE>
 __global__ __launch_bounds__(256) void bucket_sort_kernel(Params p) {
   __shared__ int32_t v[SIZE];
+  __shared__ int32_t scan[256];
+  __shared__ int dup;
   const long bucket = blockIdx.x;
   const int n = p.counts[bucket];
   if (n <= 1 || (LARGE ? n <= kSortSmall : n > kSortSmall)) return;  // uniform
+  int32_t* e = p.edges + p.offsets[bucket];
+  const int tid = threadIdx.x;
+  if constexpr (LARGE) {
+    static_assert(SIZE >= kMaxWindow / 32 + kMaxWindow / 4, "bit set and entry bytes must fit in v");
+    const int w = (int)((bucket / p.n_blk) % p.n_win);
+    const int bg = (int)(bucket / ((long)p.n_win * p.n_blk));
+    const int row0 = bg * p.Qc + w * p.W;  // the window's first row
+    const int nw = (p.W + 31) / 32;        // words of the bit set (W <= kMaxWindow)
+    uint32_t* bits = reinterpret_cast<uint32_t*>(v);
+    uint8_t* ent = reinterpret_cast<uint8_t*>(v + kMaxWindow / 32);
+    for (int x = tid; x < nw; x += 256) bits[x] = 0u;
+    if (tid == 0) dup = 0;
+    __syncthreads();
+    for (int x = tid; x < n; x += 256) {
+      const int slot = e[x];
+      const int row = slot_row(p, slot);
+      const int r = row - row0;  // 0 <= r < W for every slot of the bucket
+      if ((unsigned)r >= (unsigned)p.W) {
+        dup = 1;
+        continue;
+      }
+      const uint32_t bit = 1u << (r & 31);
+      if (atomicOr(&bits[r >> 5], bit) & bit) dup = 1;
+      ent[r] = (uint8_t)(slot - row * p.topk);  // topk <= 64
+    }
+    __syncthreads();
+    if (!dup) {  // uniform
+      // Exclusive prefix of the words' popcounts: thread t holds words 2t, 2t + 1.
+      const int w0 = 2 * tid;
+      const int c0 = w0 < nw ? __popc(bits[w0]) : 0;
+      const int c1 = w0 + 1 < nw ? __popc(bits[w0 + 1]) : 0;
+      scan[tid] = c0 + c1;
+      __syncthreads();
+      for (int d = 1; d < 256; d <<= 1) {  // Hillis-Steele inclusive scan
+        const int a = tid >= d ? scan[tid - d] : 0;
+        __syncthreads();
+        scan[tid] += a;
+        __syncthreads();
+      }
+      int pos = scan[tid] - c0 - c1;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (w0 + k >= nw) break;
+        uint32_t m = bits[w0 + k];
+        while (m) {
+          const int r = 32 * (w0 + k) + __builtin_ctz(m);
+          m &= m - 1u;
+          e[pos++] = (row0 + r) * p.topk + ent[r];
+        }
+      }
+      return;
+    }
+    __syncthreads();  // v is reused below
+  }
   if (n > SIZE) return;  // more edges than queries in a window: repeated blocks in a row
   int P = 2;
   while (P < n) P <<= 1;
-  int32_t* e = p.edges + p.offsets[bucket];
   for (int x = threadIdx.x; x < P; x += 256) v[x] = x < n ? e[x] : 0x7FFFFFFF;
   __syncthreads();
   for (int k = 2; k <= P; k <<= 1)
