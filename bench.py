@@ -512,6 +512,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-kl", action="store_true", help="skip the alignment-loss measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--backward-extra", default="prefill_128k_gain",
+                    help="comma-separated workloads whose backward is reported beside the legs workload's "
+                         "('' for none)")
     ap.add_argument("--no-mask", action="store_true", help="skip the selection-mask measurement")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="run one plain device copy of this many bytes first (counter calibration)")
@@ -578,6 +581,15 @@ def main():
             res["backward"] = backward_rates(legs, tl, max(2, args.steps // 2))
         del tl
         release()
+    if not args.no_backward:
+        res["backward_workloads"] = {}
+        for name in [x for x in args.backward_extra.split(",") if x and x != legs.name]:
+            wb = synth.WORKLOADS[name]
+            print(f"[bench] backward {name} ...", file=sys.stderr, flush=True)
+            tb = synth.device_tensors(wb, torch.device("cuda", 0))
+            res["backward_workloads"][name] = backward_rates(wb, tb, max(2, args.steps // 4))
+            del tb
+            release()
     if not args.no_decode:
         wd = synth.WORKLOADS["decode_64x256k"]
         print(f"[bench] decode workload {wd.name}", file=sys.stderr, flush=True)
