@@ -340,11 +340,11 @@ def roofline(w, stage_ms, chunks):
 # valid while the sha256 of the listed sources matches the measured code.
 TRAFFIC_FILES = {
     ("prefill_32k", "attn_partial"): ("attn_partial_prefill_32k_traffic.txt",
-                                      ("sparse_attn.hip", "edge_buckets.h", "device_common.h")),
+                                      ("sparse_attn.hip", "edge_buckets.h", "device_common.h", "plan.h")),
     ("chunk_16k_of_1m", "index_scores"): ("index_scan_chunk_16k_of_1m_traffic.txt", ("index_scan.hip", "device_common.h")),
     ("decode_64x256k", "index_scores"): ("index_scan_decode_64x256k_traffic.txt", ("index_scan.hip", "device_common.h")),
     ("prefill_128k_gain", "attn_partial"): ("attn_partial_prefill_128k_gain_traffic.txt",
-                                            ("sparse_attn.hip", "edge_buckets.h", "device_common.h")),
+                                            ("sparse_attn.hip", "edge_buckets.h", "device_common.h", "plan.h")),
 }
 
 

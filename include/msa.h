@@ -396,7 +396,7 @@ int msa_attn_chunks(const msa_dims* dims, int entry, size_t ws_bytes);
 /*
  * Bytes of caller-provided workspace the given entry point is designed for
  * with these dims (0 for entries that need none): its query chunks keep at
- * most 16 GiB of per-edge records.  Returns (size_t)-1 when the dims are not
+ * most 48 GiB of per-edge records.  Returns (size_t)-1 when the dims are not
  * valid for that entry point.
  */
 size_t msa_workspace_bytes(const msa_dims* dims, int entry);

@@ -319,8 +319,8 @@ def test_attn_chunks():
     assert msa.msa_attn_chunks(dims()) == 1
     assert msa.msa_attn_chunks(dims(causal=0)) == 0
     assert msa.msa_attn_chunks(dims(batch=0)) == 0
-    # partials of 131072 queries x 8 groups x 16 blocks exceed one chunk's budget
-    big = dims(seqlen_q=131072, seqlen_k=131072, num_heads_q=64, num_heads_kv=8)
+    # partials of 262144 queries x 8 groups x 16 blocks exceed one chunk's budget
+    big = dims(seqlen_q=262144, seqlen_k=262144, num_heads_q=64, num_heads_kv=8)
     assert msa.msa_attn_chunks(big) >= 2
     assert msa.msa_attn_chunks(dims(), msa.ENTRY_INDEX_SCORES, 1 << 30) == 0
     assert msa.msa_attn_chunks(dims(), msa.ENTRY_KL_LOSS_FWD) == 1

@@ -146,8 +146,8 @@ def release():
 def test_bwd_workload(name):
     """Full size, in the configuration a training step would call: sampled dq
     rows, the last two key blocks' dk and dv (complete from the last 256
-    queries' rows, 32K only), and the sum identities on every group (128K runs
-    in several query chunks)."""
+    queries' rows, 32K only), and the sum identities on every group; the
+    several-chunk paths are checked on every key in test_gpu_chunks.py)."""
     w = synth.WORKLOADS[name]
     print(f"[{name}] inputs, forward, backward", flush=True)
     t = inputs_for(w)
