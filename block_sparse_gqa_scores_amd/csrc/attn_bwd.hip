@@ -167,18 +167,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
 
   const int BG = p.B * p.H_kv;
   const long nblk = (long)BG * p.n_blk;
-  if ((long)blockIdx.x >= bp.blk_item[nblk]) return;  // uniform: past the last work item
-  // Work item: segment sg of the sub-tiles of (j, bg), early (busier) blocks
-  // first; a block with one segment is walked whole.
-  const int2 item = bp.items[blockIdx.x];
-  const int x = item.x, sg = item.y;
+  // Work item: segment sg of the sub-tiles of block x = (j, bg), early
+  // (busier) blocks first; a block with one segment is walked whole.  When
+  // no block can be split, work item x is block x.
+  int x = blockIdx.x, sg = 0, nseg = 1, n_tiles = 0x7FFFFFFF;
+  if (bp.seg_on) {  // uniform
+    if ((long)blockIdx.x >= bp.blk_item[nblk]) return;  // past the last work item
+    const int2 item = bp.items[blockIdx.x];
+    x = item.x;
+    sg = item.y;
+    nseg = bp.blk_item[x + 1] - bp.blk_item[x];
+    n_tiles = bp.blk_t[x];
+  }
   const int j = x / BG;
   const int bg = x - j * BG;
   const int b = bg / p.H_kv;
   const int g = bg - b * p.H_kv;
-  const int nseg = bp.blk_item[x + 1] - bp.blk_item[x];
-  const int n_tiles = bp.blk_t[x];
-  const int seg_len = (n_tiles + nseg - 1) / nseg;
+  const int seg_len = nseg == 1 ? n_tiles : (n_tiles + nseg - 1) / nseg;
   const int first_tile = sg * seg_len;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int n = lane & 31;
@@ -287,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
   // the same on every iteration and the waits stay exact: the rows of n + 1
   // and the records of n - 1 stay in flight while n stages.  The prologue
   // issues the same sequence, with two dummy record stores.
-  Cursor cur{-1, -QW, 0, nullptr, max(0, min(seg_len, n_tiles - first_tile))};
+  Cursor cur{-1, -QW, 0, nullptr, nseg == 1 ? n_tiles : max(0, min(seg_len, n_tiles - first_tile))};
   if (first_tile > 0) {  // uniform: start at the segment's first sub-tile
     int skip = first_tile;
     for (int w = 0; w < p.n_win; ++w) {
@@ -640,10 +645,15 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(BwdParams bp, long nblk) 
   const long per = (nblk + 255) / 256;
   const long x0 = min(nblk, tid * per), x1 = min(nblk, x0 + per);
   int na = 0, nb = 0;
-  for (long x = x0; x < x1; ++x) {
-    const int k = bp.blk_item[x];
-    na += k;
-    nb += k > 1 ? k : 0;
+  for (long x = x0; x < x1; x += 8) {  // eight independent loads in flight
+    int k[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) k[u] = x + u < x1 ? bp.blk_item[x + u] : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      na += k[u];
+      nb += k[u] > 1 ? k[u] : 0;
+    }
   }
   sa[tid] = na;
   sb[tid] = nb;
@@ -729,10 +739,14 @@ namespace {
 template <int G>
 void launch_main_chunk(const AttnShape& s, const Layout& L, const BwdParams& bp, long n_items, hipStream_t st) {
   const long nblk = (long)s.batch * s.H_kv * s.n_blk;
-  hipLaunchKernelGGL(seg_count_kernel, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, st, bp, 32 / G);
-  hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(256), 0, st, bp, nblk);
-  hipLaunchKernelGGL((attn_bwd_kernel<G>), dim3((unsigned)n_items), dim3(kThreads), 0, st, bp);
-  hipLaunchKernelGGL(seg_reduce_kernel, dim3((unsigned)nblk), dim3(256), 0, st, bp);
+  if (bp.seg_on) {
+    hipLaunchKernelGGL(seg_count_kernel, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, st, bp, 32 / G);
+    hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(256), 0, st, bp, nblk);
+    hipLaunchKernelGGL((attn_bwd_kernel<G>), dim3((unsigned)n_items), dim3(kThreads), 0, st, bp);
+    hipLaunchKernelGGL(seg_reduce_kernel, dim3((unsigned)nblk), dim3(256), 0, st, bp);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_kernel<G>), dim3((unsigned)nblk), dim3(kThreads), 0, st, bp);
+  }
   const long mrows = (long)s.batch * s.H_kv * L.Qc;
   hipLaunchKernelGGL(dq_merge_kernel<G>, dim3((unsigned)((mrows + 3) / 4)), dim3(256), 0, st, bp);
 }
@@ -783,6 +797,7 @@ hipError_t launch_both_g(const AttnShape& s, const FusedBwdLayout& FL, BwdParams
 // The work-item arrays of the main backward in a workspace laid out by BL.
 static void set_segments(BwdParams& bp, const BwdLayout& BL, char* base) {
   bp.seg = BL.seg;
+  bp.seg_on = BL.seg_on;
   bp.blk_t = reinterpret_cast<int32_t*>(base + BL.blk_t);
   bp.blk_item = reinterpret_cast<int32_t*>(base + BL.blk_item);
   bp.blk_part = reinterpret_cast<int32_t*>(base + BL.blk_part);

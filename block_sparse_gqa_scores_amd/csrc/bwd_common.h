@@ -31,6 +31,7 @@ struct BwdParams {
   // segments of about `seg`, so that a block most queries select spreads
   // over several workgroups.  Index x = j * B * H_kv + b * H_kv + g.
   int seg;               // sub-tiles per segment; a block with more is split
+  int seg_on;            // 0: no block of the chunk can exceed seg (one work item per block)
   int32_t* blk_t;        // [x]: the block's sub-tiles in this chunk
   int32_t* blk_item;     // [x]: first work item of x (NBLK + 1, total at the end)
   int32_t* blk_part;     // [x]: first partial slot of a split x

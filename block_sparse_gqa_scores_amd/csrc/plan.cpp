@@ -113,6 +113,9 @@ BwdLayout make_bwd_layout(const AttnShape& s, int Qc) {
   const long nblk = (long)s.batch * s.H_kv * s.n_blk;
   const long sub = (L.E + QW - 1) / QW + std::min(L.NB, L.E);
   B.seg = (int)std::max(kSegMin, (L.E / QW + kSegSpread - 1) / kSegSpread);
+  // A block holds at most one edge per query of the chunk (selections are
+  // distinct), so at most Qc / QW + n_win sub-tiles.
+  B.seg_on = (long)L.Qc / QW + L.n_win > B.seg;
   B.n_items = nblk + sub / B.seg + 1;
   B.n_part = 2 * sub / B.seg + 1;
   B.blk_t = o;    o = align256(o + (size_t)nblk * 4);

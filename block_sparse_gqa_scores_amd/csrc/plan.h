@@ -103,6 +103,7 @@ struct BwdLayout {
   edges::Layout L;
   size_t stat, dq_rec, dq_sc, dk_acc, dv_acc, blk_t, blk_item, blk_part, items, part, total;
   int chunks, seg;
+  bool seg_on;           // some block of a chunk can hold more than seg sub-tiles
   long n_items, n_part;  // bounds on work items and on partial slots
 };
 BwdLayout make_bwd_layout(const AttnShape& s, int Qc);
