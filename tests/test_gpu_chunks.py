@@ -161,10 +161,13 @@ def test_backward_chunked_every_key():
 # block's gradient is split over several workgroups and its fp32 parts are
 # summed (first, middle and last chunk).
 SPLIT = W("chunked_split", 1, 2048, 2048, 32, 1, Didx=64, topk=3, gain=True)
+# Two sequences and two groups (G = 16): block 0 of every (b, g) takes ~1020
+# sub-tiles in one chunk and is split; the work items span all four rows.
+SPLIT_B2 = W("split_b2", 2, 2048, 2048, 32, 2, Didx=64, topk=3, gain=True)
 
 
-def test_backward_split_blocks_every_key():
-    w = SPLIT
+@pytest.mark.parametrize("w,counts", [(SPLIT, (1, 2, 3)), (SPLIT_B2, (1,))], ids=["one_group", "b2_g2"])
+def test_backward_split_blocks_every_key(w, counts):
     t = inputs_for(w)
     t["dout"] = torch.empty_like(t["q"])
     synth.fill_device(w, "dout", t["dout"])
@@ -183,7 +186,7 @@ def test_backward_split_blocks_every_key():
     rdq, rdk, rdv = oracle.attention_bwd(p, h["q"], h["k"], h["v"], h["dout"], sel, rows)
     G = w.group
     d = dims(w)
-    for n in (1, 2, 3):
+    for n in counts:
         ws = msa.msa_workspace_bytes(d, msa.ENTRY_SPARSE_ATTN_BWD) if n == 1 else chunk_sizes(w, msa.ENTRY_SPARSE_ATTN_BWD, (n,))[0]
         dq, dk, dv = _bwd(w, t, idx, out, lse, ws)
         dqn = dq.float().cpu().numpy()
