@@ -12,7 +12,10 @@
 // MoBA): the forward's edge buckets, walked KV-stationary.  One workgroup owns
 // one (batch, group, block): it loads K_j and V_j into LDS once and
 // runs every edge of the block (all query windows of the chunk), so dK_j and
-// dV_j accumulate in registers and are written once, with no atomics.  Its
+// dV_j accumulate in registers and are written once, with no atomics.  A
+// block that far more queries select than the rest is cut into segments of
+// its sub-tiles, one workgroup each, whose fp32 parts are added afterwards in
+// segment order (seg_count / seg_scan / seg_reduce below).  Its
 // four waves split the block's 128 keys; the edges go through in sub-tiles of
 // 32 MFMA rows (32 / G queries x G heads) staged in LDS, in a fixed order
 // (windows ascending, slots sorted inside each bucket), so the sums and the
