@@ -332,7 +332,7 @@ def roofline(w, stage_ms, chunks):
     per_launch_ms = stage_ms[dom] / n
     ach, unit, peak = rate(bound, amount / n, per_launch_ms)
     return {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
-            "traffic": measured_traffic(w, dom), "kernel": kernel_of_stage(w, dom), "launches_per_step": n,
+            "traffic": measured_traffic(w, dom, chunks), "kernel": kernel_of_stage(w, dom), "launches_per_step": n,
             "avg_launch_ms": per_launch_ms, "work_per_launch": amount / n}
 
 
@@ -340,11 +340,11 @@ def roofline(w, stage_ms, chunks):
 # valid while the sha256 of the listed sources matches the measured code.
 TRAFFIC_FILES = {
     ("prefill_32k", "attn_partial"): ("attn_partial_prefill_32k_traffic.txt",
-                                      ("sparse_attn.hip", "edge_buckets.h", "device_common.h", "plan.h")),
+                                      ("sparse_attn.hip", "edge_buckets.h", "device_common.h")),
     ("chunk_16k_of_1m", "index_scores"): ("index_scan_chunk_16k_of_1m_traffic.txt", ("index_scan.hip", "device_common.h")),
     ("decode_64x256k", "index_scores"): ("index_scan_decode_64x256k_traffic.txt", ("index_scan.hip", "device_common.h")),
     ("prefill_128k_gain", "attn_partial"): ("attn_partial_prefill_128k_gain_traffic.txt",
-                                            ("sparse_attn.hip", "edge_buckets.h", "device_common.h", "plan.h")),
+                                            ("sparse_attn.hip", "edge_buckets.h", "device_common.h")),
 }
 
 
@@ -354,10 +354,12 @@ def source_digest(files):
     return hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in files)).hexdigest()
 
 
-def measured_traffic(w, stage):
+def measured_traffic(w, stage, chunks):
     """HBM bytes per launch from the committed counter summary of this kernel
     (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel calibration), or
-    None when there is none or the kernel's source changed since."""
+    None when there is none, the kernel's source changed since, or the
+    attention ran in another number of query chunks than when it was
+    measured (a launch then covers another share of the edges)."""
     key = TRAFFIC_FILES.get((w.name, stage))
     if key is None:
         return None
@@ -370,6 +372,8 @@ def measured_traffic(w, stage):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
     if source_digest(key[1]) != fields.get("source_sha256"):
+        return None
+    if "attn_chunks" in fields and int(fields["attn_chunks"]) != chunks:
         return None
     return float(fields["hbm_bytes_per_launch"])
 

@@ -105,3 +105,15 @@ def test_decode_stages_are_rated_in_bytes():
                                "attn_partial": 0.11, "attn_merge": 0.01}, 1)
     assert st["index_scores"]["bound"] == "hbm" and st["attn_partial"]["bound"] == "hbm"
     assert 0 < st["index_scores"]["frac"] < 1 and 0 < st["attn_partial"]["frac"] < 1
+
+
+def test_partial_traffic_needs_the_measured_chunk_count():
+    """A committed traffic figure of the partial kernel is bytes per launch at
+    the chunk count it was measured with; another count (a launch covering
+    another share of the edges) reports none."""
+    w = synth.WORKLOADS["prefill_32k"]
+    measured = bench.measured_traffic(w, "attn_partial", 1)
+    if measured is None:
+        pytest.skip("the committed summary does not match the current kernel sources")
+    assert measured > 0
+    assert bench.measured_traffic(w, "attn_partial", 2) is None
