@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kernel(BwdParams bp) {
 #pragma unroll
     for (int r = 0; r < 16; r += 2) m = max3abs(qacc[r], qacc[r + 1], m);
     m = halves_max(m);
-    const float s = m > 0.f ? 2047.f * __builtin_amdgcn_rcpf(m) : 0.f;
+    const float s = 2047.f * rec_inv(m);
     store_piece<G, false>(bp.dq_rec + slot * (kRecBytes<G> / 16), (wave * G + hh) * 2 + h, qacc, s);
     bp.dq_sc[(slot * 4 + wave) * G + hh] = m * bp.scale * (1.f / 2047.f);  // both halves store the same value
   };

@@ -80,6 +80,13 @@ __device__ __forceinline__ float max16(float m, const f32x16& x) {
 }
 
 // max(|a|, |b|, c): one v_max3_f32 with abs source modifiers (see max3f).
+// Reciprocal of a record's scale m (its largest magnitude): the values are
+// stored as fractions or codes of m.  Below 2^-100 they are stored as zero:
+// 1 / m of a subnormal m overflows fp32 (and 2047 / m even earlier), which
+// would turn the record into inf or NaN, and values this small vanish next to
+// any other contribution to a bf16 result.
+__device__ __forceinline__ float rec_inv(float m) { return m >= 0x1p-100f ? __builtin_amdgcn_rcpf(m) : 0.f; }
+
 __device__ __forceinline__ float max3abs(float a, float b, float c) {
   return __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(a), __builtin_fabsf(b)), c);
 }

@@ -341,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 2) void kl_grad_kernel(KlBwdParams kp) {
         for (int x = 0; x < 4; ++x) m = max3abs(dqa[2 * qq][x], dqa[2 * qq + 1][x], m);
         m = __builtin_fmaxf(m, __shfl_xor(m, 16, 64));
         m = __builtin_fmaxf(m, __shfl_xor(m, 32, 64));
-        const float inv = m > 0.f ? __builtin_amdgcn_rcpf(m) : 0.f;
+        const float inv = rec_inv(m);
         if (qcol < QW) {
           uint16_t* rec = kp.rec + slot * DIDX + 32 * qq;
 #pragma unroll

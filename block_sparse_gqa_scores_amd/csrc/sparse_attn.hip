@@ -551,7 +551,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p, int
       for (int r = 0; r < 16; r += 2) amax = max3abs(oacc[dt][r], oacc[dt][r + 1], amax);
     amax = halves_max(amax);
     {
-      const float s = amax > 0.f ? 2047.f * __builtin_amdgcn_rcpf(amax) : 0.f;
+      const float s = 2047.f * rec_inv(amax);
       u32x4* rec = p.part_o + (size_t)slot * (kRecBytes<G> / 16);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) store_piece<G, true>(rec, piece_of(G, dt, hh, h), oacc[dt], s);
@@ -685,7 +685,7 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(Params p) {
   __syncthreads();
   amax = __builtin_fmaxf(__builtin_fmaxf(s_a[0][n], s_a[1][n]), __builtin_fmaxf(s_a[2][n], s_a[3][n]));
   if (n < G) {
-    const float s = amax > 0.f ? 2047.f * __builtin_amdgcn_rcpf(amax) : 0.f;
+    const float s = 2047.f * rec_inv(amax);
     store_piece<G, true>(p.part_o + (size_t)slot * (kRecBytes<G> / 16), piece_of(G, wave, n, h), oacc, s);
     if (wave == 0 && h == 0) {
       p.part_stat[(size_t)slot * G + n] = f32x2{mx * c + __builtin_amdgcn_logf(l), amax * __builtin_amdgcn_rcpf(2047.f * l)};

@@ -105,3 +105,23 @@ def test_fused_without_queries_writes_zero_key_gradients():
                                 dk.data_ptr(), dv.data_ptr(), None, dki.data_ptr(), None, 0, None)
     torch.cuda.synchronize()
     assert rc == 0 and not dk.float().any() and not dv.float().any() and not dki.float().any()
+
+
+SHARP = [W("fb_sharp_mha", 2, 700, 1100, 4, 4, Didx=64, topk=5),
+         W("fb_sharp_g8", 1, 1500, 2600, 64, 8, topk=8)]
+
+
+@pytest.mark.parametrize("w", SHARP, ids=lambda w: w.name)
+def test_sharp_softmax_against_oracle(w):
+    """Sharp main and index softmaxes (q and k scaled by 6, the integer q_idx
+    by 4): a block that holds almost none of a row's mass in both gives
+    gradient records whose largest magnitude is subnormal, which must encode
+    as zeros rather than inf or NaN.  Every row and key against the oracle."""
+    t = inputs_for(w)
+    with torch.no_grad():
+        t["q"].mul_(6)
+        t["k"].mul_(6)
+        t["q_idx"].mul_(4)
+    out, lse, idx, lse_idx = prepare(w, t)
+    grads = fused(w, t, out, lse, idx, lse_idx)
+    backward_against_oracle(w, t, grads, idx, w.name)

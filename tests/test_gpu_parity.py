@@ -94,6 +94,29 @@ def test_explicit_softmax_scale():
     assert np.abs(l - ref["lse"]).max() < 1e-3
 
 
+@pytest.mark.parametrize("shape", [(2, 700, 1100, 4, 4, 64, 5), (1, 1500, 2600, 64, 8, 128, 8)],
+                         ids=["mha", "g8"])
+def test_sharp_softmax_forward(shape):
+    """q and k scaled by 6 (logits with a standard deviation near 36, nearly
+    one-hot rows) and the integer q_idx by 4: block scores and selections
+    bit-exact, out and lse within the tolerance rule, on every row."""
+    B, Sq, Sk, Hq, Hkv, Didx, k = shape
+    w = W(f"sharp_{Hq}x{Hkv}", B, Sq, Sk, Hq, Hkv, Didx=Didx, topk=k)
+    t = inputs_for(w)
+    with torch.no_grad():
+        t["q"].mul_(6)
+        t["k"].mul_(6)
+        t["q_idx"].mul_(4)
+    dev = run_device(w, t)
+    p = oracle.Problem.of(w)
+    rows = p.all_rows()
+    h = host_inputs(t)
+    ref = oracle.forward(p, h["q"], h["k"], h["v"], h["q_idx"], h["k_idx"], rows=rows)
+    msgs, stats = compare(w, dev, ref, rows, label=w.name)
+    print(w.name, stats, flush=True)
+    assert not msgs, "\n".join(msgs)
+
+
 def test_massive_ties_take_the_exact_path():
     """k_idx = 0: every block score is 0, so the tie rule alone decides
     (blocks 0..k-2 plus the local block), on rows wider than the survivor
