@@ -125,3 +125,30 @@ def test_sharp_softmax_against_oracle(w):
     out, lse, idx, lse_idx = prepare(w, t)
     grads = fused(w, t, out, lse, idx, lse_idx)
     backward_against_oracle(w, t, grads, idx, w.name)
+
+
+def test_zero_upstream_gradient():
+    """dO = 0: dq, dk, dv are exactly zero, and dq_idx, dk_idx (which do not
+    depend on dO) equal the call with the seeded dO bit for bit."""
+    w = W("fb_zero_dout", 1, 1300, 2300, 64, 8, topk=8)
+    t = inputs_for(w)
+    out, lse, idx, lse_idx = prepare(w, t)
+    ref = fused(w, t, out, lse, idx, lse_idx)
+    t["dout"].zero_()
+    got = fused(w, t, out, lse, idx, lse_idx)
+    for name, g in zip(NAMES[:3], got[:3]):
+        assert not g.float().abs().max().item(), f"{name} is not zero"
+    for name, a, b in zip(NAMES[3:], got[3:], ref[3:]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name} depends on dO"
+
+
+def test_uniform_attention_against_oracle():
+    """q = 0: every visible token gets the same weight (the main scores are
+    all zero) while the selection still follows the index branch; forward
+    selection and every gradient against the oracle."""
+    w = W("fb_uniform", 2, 600, 1000, 4, 4, Didx=64, topk=5)
+    t = inputs_for(w)
+    t["q"].zero_()
+    out, lse, idx, lse_idx = prepare(w, t)
+    grads = fused(w, t, out, lse, idx, lse_idx)
+    backward_against_oracle(w, t, grads, idx, w.name)
