@@ -574,9 +574,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partial_kernel(Params p, int
 // Decode form of the partial (one query per (b, g) row, S_q = 1): every
 // selected block is its own work item, so no bucket build is needed; one
 // workgroup per (b, g, entry e) writes the record of slot (b H_kv + g) k + e,
-// in the layout of attn_partial_kernel's records.  K rows go from memory
-// straight into the MFMA A operand; V goes through LDS row-major and comes
-// back transposed (ds_read_b64_tr_b16).  S^T = K q^T puts this wave's 32 keys
+// in the layout of attn_partial_kernel's records.  K and V are both read with
+// whole 256-byte rows per 16 lanes and staged through one LDS tile in turn:
+// K first, read back as the MFMA A operand (loading the operand fragments
+// straight from memory touches 32 bytes of 32 rows per instruction, 0.116
+// against 0.094 ms on 64 x 256K), then V, read back transposed
+// (ds_read_b64_tr_b16).  S^T = K q^T puts this wave's 32 keys
 // on registers and the heads on lanes; the block's per-head max and sum are
 // exchanged across the four waves in LDS; P goes to LDS as [head][key]; wave w
 // then forms O^T for head dims 32 w .. 32 w + 31 over all 128 keys.
@@ -584,7 +587,7 @@ constexpr int kPStride = kBlock + 8;  // bf16 per head row of P
 
 template <int G>
 __global__ __launch_bounds__(kThreads) void attn_decode_kernel(Params p) {
-  __shared__ u32x4 vtile[kBlock * 16];                  // V_j [key][chunk ^ rsw(key)]
+  __shared__ u32x4 vtile[kBlock * 16];                  // K_j, then V_j [key][chunk ^ rsw(key)]
   __shared__ __align__(16) uint16_t sp[G * kPStride];   // P [head][key] bf16
   __shared__ float s_m[4][32], s_l[4][32], s_a[4][32];  // per-wave max, sum, max |O|
 
@@ -598,35 +601,38 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(Params p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, n = lane & 31;
   const float c = p.scale_log2;
 
-  // Every load first: V tile pieces, this lane's K row (key 32 w + n), q of
-  // head n (the last head repeated past G).  The V pieces are read once and
-  // only staged through LDS, so they are loaded non-temporally (0.12 ->
-  // 0.11 ms on 64 x 256K); the same hint on the K rows, which feed the
-  // matrix operands directly, measured slower.
+  // Every load first: the K and V tile pieces (row qd / 16, chunk qd % 16),
+  // and q of head n (the last head repeated past G).  Both tiles are read
+  // once and only staged through LDS, so they are loaded non-temporally
+  // (0.12 -> 0.11 ms on 64 x 256K for V).
   const size_t row_stride = (size_t)p.H_kv * kD;
   const uint16_t* kb = p.k + ((size_t)b * p.S_k * p.H_kv + g) * kD;
   const uint16_t* vb = p.v + ((size_t)b * p.S_k * p.H_kv + g) * kD;
-  u32x4 vr[8], kr[8], qr[8];
+  u32x4 vr[8], kq[8], qr[8];
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int qd = it * kThreads + tid;
     const int s = min(jj * kBlock + (qd >> 4), p.S_k - 1);  // rows past S_k: masked below
+    kq[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 8 * (qd & 15)));
     vr[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (size_t)s * row_stride + 8 * (qd & 15)));
   }
   {
-    const int s = min(jj * kBlock + 32 * wave + n, p.S_k - 1);
     const uint16_t* qrow = p.q + ((size_t)b * p.H_q + g * G + min(n, G - 1)) * kD + 8 * h;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      kr[ks] = *reinterpret_cast<const u32x4*>(kb + (size_t)s * row_stride + 16 * ks + 8 * h);
-      qr[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
-    }
+    for (int ks = 0; ks < 8; ++ks) qr[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
   }
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int qd = it * kThreads + tid;
     const int row = qd >> 4;
-    vtile[row * 16 + ((qd & 15) ^ rsw(row))] = vr[it];
+    vtile[row * 16 + ((qd & 15) ^ rsw(row))] = kq[it];
+  }
+  __syncthreads();  // the K tile
+  u32x4 kr[8];  // this lane's K row (key 32 w + n), chunks 2 ks + h
+  {
+    const int krow = 32 * wave + n;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kr[ks] = vtile[krow * 16 + ((2 * ks + h) ^ rsw(krow))];
   }
 
   // S^T[key 32 w + 8 (r / 4) + 4 h + r % 4][head n].
@@ -639,7 +645,13 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(Params p) {
   float mx = max16(neg_inf(), sacc);
   mx = __builtin_fmaxf(mx, swap_halves(mx));
   if (h == 0) s_m[wave][n] = mx;
-  __syncthreads();  // also the V tile
+  __syncthreads();  // every wave has its K operands: the tile takes V now
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int qd = it * kThreads + tid;
+    const int row = qd >> 4;
+    vtile[row * 16 + ((qd & 15) ^ rsw(row))] = vr[it];
+  }
   mx = __builtin_fmaxf(__builtin_fmaxf(s_m[0][n], s_m[1][n]), __builtin_fmaxf(s_m[2][n], s_m[3][n]));
   const float bias = -mx * c;
   float l = 0.f;
