@@ -539,7 +539,12 @@ __global__ __launch_bounds__(kThreads, 2) void kl_dk_kernel(KlBwdParams kp) {
 }
 
 // dq_idx of each row: the sum of its edges' records; 16 lanes per row, 8
-// index dims each.
+// index dims each.  Every entry's selection, scale and record piece of a
+// batch are requested before any is used (an entry that does not count
+// reads its own slot, which lies inside the record array, and is skipped),
+// and the sums still run in entry order.  Records are read once and dq_idx
+// is written once, both non-temporal (32K loss backward: 3.56 -> 3.46 ms
+// against one entry's loads at a time).
 template <int DIDX>
 __global__ __launch_bounds__(256) void kl_dq_merge_kernel(KlBwdParams kp) {
   constexpr int NDT = DIDX / 32;
@@ -557,16 +562,27 @@ __global__ __launch_bounds__(256) void kl_dq_merge_kernel(KlBwdParams kp) {
   const int local = (i + p.S_k - p.S_q) / kBlock;
   const long slot0 = ((long)bg * p.Qc + il) * p.topk;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int e = 0; e < p.topk; ++e) {
-    const int jj = sel[e];
-    if (jj < 0 || jj > local) continue;
-    const long slot = slot0 + e;
-    const float sc = kp.rec_sc[slot * NDT + f / 4];
-    const u32x4 x = *reinterpret_cast<const u32x4*>(kp.rec + slot * DIDX + 8 * f);
+  constexpr int kB = 16;
+  for (int e0 = 0; e0 < p.topk; e0 += kB) {
+    u32x4 xs[kB];
+    float scs[kB];
+    int js[kB];
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      acc[2 * y] += sc * f16_lo(x[y]);
-      acc[2 * y + 1] += sc * f16_hi(x[y]);
+    for (int k = 0; k < kB; ++k) {
+      const int e = min(e0 + k, p.topk - 1);
+      const long slot = slot0 + e;
+      js[k] = sel[e];
+      scs[k] = kp.rec_sc[slot * NDT + f / 4];
+      xs[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp.rec + slot * DIDX + 8 * f));
+    }
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      if (e0 + k >= p.topk || js[k] < 0 || js[k] > local) continue;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        acc[2 * y] += scs[k] * f16_lo(xs[k][y]);
+        acc[2 * y + 1] += scs[k] * f16_hi(xs[k][y]);
+      }
     }
   }
   uint16_t* o = kp.dq_idx + (((size_t)b * p.S_q + i) * p.H_kv + g) * DIDX;
@@ -576,8 +592,8 @@ __global__ __launch_bounds__(256) void kl_dq_merge_kernel(KlBwdParams kp) {
   lo.y = pack_bf16x2(acc[2], acc[3]);
   hi.x = pack_bf16x2(acc[4], acc[5]);
   hi.y = pack_bf16x2(acc[6], acc[7]);
-  *reinterpret_cast<uint2*>(o + rec_dim(quarter, pos)) = lo;
-  *reinterpret_cast<uint2*>(o + rec_dim(quarter, pos + 4)) = hi;
+  __builtin_nontemporal_store(((uint64_t)lo.y << 32) | lo.x, reinterpret_cast<uint64_t*>(o + rec_dim(quarter, pos)));
+  __builtin_nontemporal_store(((uint64_t)hi.y << 32) | hi.x, reinterpret_cast<uint64_t*>(o + rec_dim(quarter, pos + 4)));
 }
 
 // dk_idx = the sum of the groups' parts, in group order, over the groups
