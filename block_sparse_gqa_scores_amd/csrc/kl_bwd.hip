@@ -597,28 +597,43 @@ __global__ __launch_bounds__(256) void kl_dq_merge_kernel(KlBwdParams kp) {
 }
 
 // dk_idx = the sum of the groups' parts, in group order, over the groups
-// whose part of the key's block holds data (the others are zero).  One
-// workgroup per (batch, key block); four index dims per thread and step.
+// whose part of the key's block holds data (the others are zero).  Four
+// workgroups per (batch, key block); four index dims per thread and step.
+// Eight groups' flags and parts are requested before any is added (a part
+// whose flag is clear is read, inside its buffer, and skipped).  Each part
+// is read once and dk_idx written once, both non-temporal (32K loss
+// backward: 3.56 -> 3.43 ms against one workgroup per block and one group's
+// loads at a time).
 template <int DIDX>
 __global__ __launch_bounds__(256) void kl_dk_reduce_kernel(KlBwdParams kp) {
   const Params& p = kp.e;
-  const int b = blockIdx.x / p.n_blk;
-  const int j = blockIdx.x - b * p.n_blk;
+  constexpr int kSplit = 4;
+  const int bj = blockIdx.x / kSplit;
+  const int part = blockIdx.x - bj * kSplit;
+  const int b = bj / p.n_blk;
+  const int j = bj - b * p.n_blk;
   const int keys = min(kBlock, p.S_k - j * kBlock);
   const int n4 = keys * DIDX / 4;
   const size_t row0 = (size_t)j * kBlock * DIDX;  // the block's first element in a [S_k][D_idx] plane
-  for (int x = threadIdx.x; x < n4; x += 256) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int g = 0; g < p.H_kv; ++g) {
-      const long bg = (long)b * p.H_kv + g;
-      if (kp.dk_flag[bg * p.n_blk + j] == 0) continue;  // uniform
-      const float4 v = *reinterpret_cast<const float4*>(kp.dk_part + bg * p.S_k * DIDX + row0 + 4 * x);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  for (int x = part * 256 + threadIdx.x; x < n4; x += 256 * kSplit) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int g0 = 0; g0 < p.H_kv; g0 += 8) {
+      f32x4 v[8];
+      int fl[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const long bg = (long)b * p.H_kv + min(g0 + k, p.H_kv - 1);
+        fl[k] = kp.dk_flag[bg * p.n_blk + j];
+        v[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(kp.dk_part + bg * p.S_k * DIDX + row0 + 4 * x));
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (g0 + k >= p.H_kv || fl[k] == 0) continue;  // uniform
+        acc.x += v[k].x; acc.y += v[k].y; acc.z += v[k].z; acc.w += v[k].w;
+      }
     }
-    uint2 o;
-    o.x = pack_bf16x2(acc.x, acc.y);
-    o.y = pack_bf16x2(acc.z, acc.w);
-    *reinterpret_cast<uint2*>(kp.dk_idx + (size_t)b * p.S_k * DIDX + row0 + 4 * x) = o;
+    const uint64_t o = ((uint64_t)pack_bf16x2(acc.z, acc.w) << 32) | pack_bf16x2(acc.x, acc.y);
+    __builtin_nontemporal_store(o, reinterpret_cast<uint64_t*>(kp.dk_idx + (size_t)b * p.S_k * DIDX + row0 + 4 * x));
   }
 }
 
@@ -656,8 +671,8 @@ hipError_t launch_kl_chunk(const AttnShape& s, const Layout& L, const KlBwdParam
 }
 
 hipError_t launch_kl_dk_reduce(const KlBwdParams& kp, int D_idx, long blocks, hipStream_t st) {
-  if (D_idx == 64) hipLaunchKernelGGL(kl_dk_reduce_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, kp);
-  else hipLaunchKernelGGL(kl_dk_reduce_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, st, kp);
+  if (D_idx == 64) hipLaunchKernelGGL(kl_dk_reduce_kernel<64>, dim3((unsigned)(4 * blocks)), dim3(256), 0, st, kp);
+  else hipLaunchKernelGGL(kl_dk_reduce_kernel<128>, dim3((unsigned)(4 * blocks)), dim3(256), 0, st, kp);
   return hipGetLastError();
 }
 }  // namespace edges

@@ -352,7 +352,10 @@ __global__ __launch_bounds__(kThreads, 2) void kl_partial_kernel(Params p) {
 }
 
 // Row terms and the loss.  One thread per row (b, g, i); the records of its
-// selected blocks are combined online:
+// selected blocks are requested 16 at a time (an entry that does not count
+// reads its own slot, inside the record array, and is skipped; 32K:
+// 2.20 -> 2.12 ms for the loss against one entry's loads at a time) and
+// combined online, in entry order:
 //   M running max of m_j, L = sum L_j e^(m_j - M), U = sum S_j (m_j - M),
 //   KL_row = sum (A_j - C_j) - U + (sum S_j) ln L.
 // Each workgroup leaves the sum of its rows' terms; kl_total_kernel adds those
@@ -368,23 +371,36 @@ __global__ __launch_bounds__(256) void kl_merge_kernel(Params p) {
     const int32_t* sel = p.idx + r * p.topk;
     float M = neg_inf(), L = 0.f, U = 0.f, S = 0.f, AC = 0.f;
     constexpr float kLog2e = 1.4426950408889634f;
-    for (int e = 0; e < p.topk; ++e) {
-      const int jj = sel[e];
-      if (jj < 0 || jj > local) continue;
-      const float4 rec = *reinterpret_cast<const float4*>(p.kl_rec + (r * p.topk + e) * 8);
-      const float mj = p.kl_rec[(r * p.topk + e) * 8 + 4];
-      if (mj > M) {  // rescale what was summed against the old maximum
-        if (M != neg_inf()) {
-          L *= __builtin_amdgcn_exp2f((M - mj) * kLog2e);
-          U += S * (M - mj);
-        }
-        M = mj;
+    constexpr int kB = 16;
+    for (int e0 = 0; e0 < p.topk; e0 += kB) {
+      float4 recs[kB];
+      float mjs[kB];
+      int js[kB];
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const long e = r * p.topk + min(e0 + k, p.topk - 1);
+        js[k] = sel[min(e0 + k, p.topk - 1)];
+        recs[k] = *reinterpret_cast<const float4*>(p.kl_rec + e * 8);
+        mjs[k] = p.kl_rec[e * 8 + 4];
       }
-      const float dm = mj - M;
-      L += rec.w * __builtin_amdgcn_exp2f(dm * kLog2e);
-      U += rec.x * dm;
-      S += rec.x;
-      AC += rec.y - rec.z;
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        if (e0 + k >= p.topk || js[k] < 0 || js[k] > local) continue;
+        const float4 rec = recs[k];
+        const float mj = mjs[k];
+        if (mj > M) {  // rescale what was summed against the old maximum
+          if (M != neg_inf()) {
+            L *= __builtin_amdgcn_exp2f((M - mj) * kLog2e);
+            U += S * (M - mj);
+          }
+          M = mj;
+        }
+        const float dm = mj - M;
+        L += rec.w * __builtin_amdgcn_exp2f(dm * kLog2e);
+        U += rec.x * dm;
+        S += rec.x;
+        AC += rec.y - rec.z;
+      }
     }
     const float lnL = __builtin_amdgcn_logf(L) * 0.69314718055994530942f;
     kl = AC - U + S * lnL;
