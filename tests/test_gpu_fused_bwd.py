@@ -49,6 +49,7 @@ CASES = [
     W("fb_g32", 2, 300, 300, 32, 1, Didx=64, topk=4),          # G = 32
     W("fb_decode", 3, 1, 5000, 16, 2, Didx=64),                # S_q = 1
     W("fb_gain", 1, 1500, 3000, 16, 2, gain=True, topk=6),     # uneven blocks
+    W("fb_hkv10", 1, 400, 900, 20, 10, topk=4),                # H_kv = 10 (G = 2): groups past the first eight
     W("fb_split", 1, 2048, 2048, 32, 1, Didx=64, topk=3, gain=True),  # block 0's dK, dV split over workgroups
 ]
 

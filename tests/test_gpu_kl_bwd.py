@@ -76,6 +76,7 @@ CASES = [
     W("klb_decode", 3, 1, 5000, 16, 2, Didx=64),               # S_q = 1
     W("klb_k64", 1, 130, 9000, 4, 1, topk=64),                 # the largest topk
     W("klb_gain", 1, 1500, 3000, 16, 2, gain=True, topk=6),    # uneven blocks
+    W("klb_hkv12", 1, 400, 900, 12, 12, Didx=64, topk=4),     # H_kv = 12: dk_idx sums groups in two batches
 ]
 
 

@@ -44,6 +44,7 @@ SMALL = [
     W("g16", 1, 500, 640, 32, 2, topk=2),                               # G = 16
     W("g32", 2, 300, 300, 32, 1, Didx=64, topk=4),                      # G = 32, one group
     W("topk1", 1, 400, 900, 8, 2, topk=1),                              # local block only
+    W("hkv12", 1, 400, 900, 12, 12, Didx=64, topk=4),                   # H_kv = 12, not a power of two
     W("decode_small", 3, 1, 5000, 16, 2, Didx=64),                      # S_q = 1: decode kernels
     W("decode_mha", 2, 1, 3000, 4, 4, topk=8),                          # decode, G = 1
     W("decode_g2", 2, 1, 2500, 8, 4, Didx=64, topk=5),                  # decode, G = 2
